@@ -1,0 +1,210 @@
+"""Thin Python binding of libbitlinear (include/bitlinear.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  Importing this module fails loudly when libbitlinear.so has not been
+built -- there is no CPU fallback.
+
+The functions keep the names of the C entry points (ternarize_pack,
+quant_act, gemv_w2a8, gemm_w2a8, ffn_chain); ``raw`` exposes the ctypes
+handle for callers that want the C signatures directly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_SEGMENTS, BL_ERR_WORKSPACE, BL_ERR_HIP = range(8)
+BL_F32, BL_BF16, BL_I8, BL_I32 = range(4)
+MAX_SEGMENTS = 8
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libbitlinear.so not found at {LIB_PATH}; build it first "
+        "(python -m bit_ternary_weight_amd.build or __graft_entry__.build())")
+
+raw = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_S = ctypes.c_size_t
+_F = ctypes.c_float
+
+
+class FfnDebug(ctypes.Structure):
+    _fields_ = [("q1", _P), ("a1", _P), ("p", _P), ("q2", _P), ("a2", _P)]
+
+
+_SIGS = {
+    "bl_abi_version": (_I, []),
+    "bl_status_string": (ctypes.c_char_p, [_I]),
+    "bl_last_error": (ctypes.c_char_p, []),
+    "bl_ternarize_workspace_bytes": (_S, [_L, _L]),
+    "bl_ternarize_pack": (_I, [_P, _I, _I, _P, _P, _P, _S, _P]),
+    "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "bl_gemv_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_gemv_w2a8": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
+    "bl_gemm_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_gemm_w2a8": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
+    "bl_ffn_chain_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_ffn_chain": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _I, _P, _S,
+                          ctypes.POINTER(FfnDebug), _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(raw, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{raw.bl_status_string(status).decode()}: {msg}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != BL_OK:
+        raise BitLinearError(status, raw.bl_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_DT = {torch.float32: BL_F32, torch.bfloat16: BL_BF16, torch.int8: BL_I8, torch.int32: BL_I32}
+_TORCH = {v: k for k, v in _DT.items()}
+
+
+def _dt(t) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on a HIP device")
+    return ts[0].device
+
+
+# ---------------------------------------------------------------------------
+# Workspace: one zero-initialised buffer per device, grown on demand.  The
+# library keeps its zero prefix zero across calls, so the buffer is cleared
+# only when it is (re)allocated.
+# ---------------------------------------------------------------------------
+_ws_lock = threading.Lock()
+_ws: dict = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    with _ws_lock:
+        buf = _ws.get(key)
+        if buf is None or buf.numel() < nbytes:
+            size = max(int(nbytes), 16 << 20)
+            buf = torch.zeros(size, dtype=torch.uint8, device=device)
+            _ws[key] = buf
+        return buf
+
+
+def _segs(seg_n, N):
+    if seg_n is None:
+        return 1, None
+    seg = (ctypes.c_int * len(seg_n))(*[int(v) for v in seg_n])
+    return len(seg_n), seg
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+def ternarize_pack(W: torch.Tensor, packed: torch.Tensor = None, w_mean: torch.Tensor = None):
+    """W fp32 [N,K] -> (packed uint8 [N/4,K], w_mean fp32 [1])."""
+    dev = _dev(W)
+    N, K = W.shape
+    if packed is None:
+        packed = torch.empty((N // 4, K), dtype=torch.uint8, device=dev)
+    if w_mean is None:
+        w_mean = torch.empty(1, dtype=torch.float32, device=dev)
+    nbytes = raw.bl_ternarize_workspace_bytes(N, K)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(raw.bl_ternarize_pack(_ptr(W), N, K, _ptr(packed), _ptr(w_mean), _ptr(ws), ws.numel(), _stream(dev)))
+    return packed, w_mean
+
+
+def quant_act(x: torch.Tensor, q: torch.Tensor = None, a: torch.Tensor = None):
+    """x [M,K] fp32/bf16 (row stride may exceed K) -> (q int8 [M,K], a fp32 [M])."""
+    dev = _dev(x)
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    if a is None:
+        a = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(raw.bl_quant_act(_ptr(x), _dt(x), M, K, x.stride(0), _ptr(q), _ptr(a), _stream(dev)))
+    return q, a
+
+
+def _contract(fn_name, ws_query, x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):
+    dev = _dev(x, packed, w_mean)
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    N = packed.shape[0] * 4
+    n_seg, seg = _segs(seg_n, N)
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=dev)
+    nbytes = ws_query(M, N, K)
+    ws = workspace(dev, nbytes)
+    fn = getattr(raw, fn_name)
+    _check(fn(_ptr(x), _dt(x), x.stride(0), _ptr(a), M, K, _ptr(packed), N, n_seg, seg, _ptr(w_mean),
+              _ptr(y), _dt(y), _ptr(ws), ws.numel(), _stream(dev)))
+    return y
+
+
+def gemv_w2a8(x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):
+    """Decode BitLinear (M <= 64): y = rescale(quant(x) @ unpack(packed)^T)."""
+    return _contract("bl_gemv_w2a8", raw.bl_gemv_workspace_bytes, x, packed, w_mean, seg_n, y_dtype, a, y)
+
+
+def gemm_w2a8(x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):
+    """Prefill BitLinear (any M), same arithmetic as gemv_w2a8."""
+    return _contract("bl_gemm_w2a8", raw.bl_gemm_workspace_bytes, x, packed, w_mean, seg_n, y_dtype, a, y)
+
+
+def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g_ffn=None, eps=1e-5,
+              y_dtype=torch.float32, debug=False, y=None):
+    """FFN half of a layer.  Returns y, or (y, dict of stage outputs) with debug=True."""
+    dev = _dev(h, packed_gu, packed_down)
+    M, H = h.shape
+    I = packed_gu.shape[0] * 2
+    if y is None:
+        y = torch.empty((M, H), dtype=y_dtype, device=dev)
+    stages = None
+    dbg = None
+    if debug:
+        stages = dict(q1=torch.empty((M, H), dtype=torch.int8, device=dev),
+                      a1=torch.empty(M, dtype=torch.float32, device=dev),
+                      p=torch.empty((M, I), dtype=torch.float32, device=dev),
+                      q2=torch.empty((M, I), dtype=torch.int8, device=dev),
+                      a2=torch.empty(M, dtype=torch.float32, device=dev))
+        dbg = FfnDebug(*[stages[k].data_ptr() for k in ("q1", "a1", "p", "q2", "a2")])
+    nbytes = raw.bl_ffn_chain_workspace_bytes(M, H, I)
+    ws = workspace(dev, nbytes)
+    _check(raw.bl_ffn_chain(_ptr(h), _dt(h), M, H, I, _ptr(g_subln), _ptr(g_ffn), float(eps),
+                            _ptr(packed_gu), _ptr(w_mean_gu), _ptr(packed_down), _ptr(w_mean_down),
+                            _ptr(y), _dt(y), _ptr(ws), ws.numel(),
+                            ctypes.byref(dbg) if dbg is not None else None, _stream(dev)))
+    return (y, stages) if debug else y

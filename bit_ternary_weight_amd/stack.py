@@ -1,0 +1,148 @@
+"""Linear path of a BitNet b1.58 2B4T-shaped decoder stack, attention excluded.
+
+Per layer (shapes from the "BitNetConfig" section of the BitNet model
+documentation pages: hidden 2560, intermediate 6912, 20 query / 5 key-value
+heads of 128):
+  x -> fused q|k|v BitLinear (three segments, one launch)
+    -> o BitLinear fed with q's output (stand-in for attention: a convention,
+       the pages give no such wiring)
+    -> FFN chain: subln RMSNorm -> quantize -> gate|up -> ReLU^2(gate)*up ->
+       ffn_sub_norm RMSNorm -> quantize -> down          (bl_ffn_chain)
+  and down's output is the next layer's input (no residual additions).
+
+Every step runs in libbitlinear through the binding; this module only holds
+weights and orders calls.  Weights are ternarized on the device from seeded
+fp32 masters (bl_ternarize_pack), so the packed bytes match what the oracle
+packs from the same masters.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as bl
+from . import synth
+
+H = synth.HIDDEN
+I = synth.INTERMEDIATE
+KV = synth.KV_DIM
+QKV_SEGS = (H, KV, KV)
+DECODE_MAX_M = 64
+
+
+@dataclass
+class LayerWeights:
+    packed_qkv: torch.Tensor    # [(H+2KV)/4, H]
+    w_qkv: torch.Tensor         # [3]
+    packed_o: torch.Tensor      # [H/4, H]
+    w_o: torch.Tensor           # [1]
+    packed_gu: torch.Tensor     # [2I/4, H]
+    w_gu: torch.Tensor          # [2]
+    packed_down: torch.Tensor   # [H/4, I]
+    w_down: torch.Tensor        # [1]
+
+    def nbytes_packed(self) -> int:
+        return sum(t.numel() for t in (self.packed_qkv, self.packed_o, self.packed_gu, self.packed_down))
+
+
+def _alloc_layer(device) -> LayerWeights:
+    u8, f32 = torch.uint8, torch.float32
+    return LayerWeights(
+        packed_qkv=torch.empty(((H + 2 * KV) // 4, H), dtype=u8, device=device),
+        w_qkv=torch.empty(3, dtype=f32, device=device),
+        packed_o=torch.empty((H // 4, H), dtype=u8, device=device),
+        w_o=torch.empty(1, dtype=f32, device=device),
+        packed_gu=torch.empty((2 * I // 4, H), dtype=u8, device=device),
+        w_gu=torch.empty(2, dtype=f32, device=device),
+        packed_down=torch.empty((H // 4, I), dtype=u8, device=device),
+        w_down=torch.empty(1, dtype=f32, device=device),
+    )
+
+
+def _dest(lw: LayerWeights, proj: str):
+    """(packed rows view, w_mean view) where projection `proj` lives."""
+    r_h, r_kv, r_i = H // 4, KV // 4, I // 4
+    return {
+        "q": (lw.packed_qkv[0:r_h], lw.w_qkv[0:1]),
+        "k": (lw.packed_qkv[r_h:r_h + r_kv], lw.w_qkv[1:2]),
+        "v": (lw.packed_qkv[r_h + r_kv:r_h + 2 * r_kv], lw.w_qkv[2:3]),
+        "o": (lw.packed_o, lw.w_o),
+        "gate": (lw.packed_gu[0:r_i], lw.w_gu[0:1]),
+        "up": (lw.packed_gu[r_i:2 * r_i], lw.w_gu[1:2]),
+        "down": (lw.packed_down, lw.w_down),
+    }[proj]
+
+
+def build_layers(n_layers: int, device, masters=None, workers: int = 8):
+    """Ternarize and pack `n_layers` seeded layers on the device.
+
+    masters: optional callable (layer, proj) -> fp32 numpy [N,K]; defaults to
+    the seeded generator.  Masters are drawn on host threads and ternarized
+    one projection at a time, so at most a few projections sit in memory.
+    """
+    gen = masters or synth.layer_weight
+    layers = [_alloc_layer(device) for _ in range(n_layers)]
+    jobs = [(l, p) for l in range(n_layers) for p, _, _ in synth.PROJECTIONS]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(gen, l, p) for l, p in jobs[: 2 * workers]]
+        nxt = len(futs)
+        for i, (l, p) in enumerate(jobs):
+            W = futs[i].result()
+            futs[i] = None
+            if nxt < len(jobs):
+                futs.append(ex.submit(gen, *jobs[nxt]))
+                nxt += 1
+            Wd = torch.from_numpy(W).to(device, non_blocking=False)
+            packed, wm = _dest(layers[l], p)
+            bl.ternarize_pack(Wd, packed=packed, w_mean=wm)
+            del Wd
+    torch.cuda.synchronize(device)
+    return layers
+
+
+def _contract(M):
+    return bl.gemv_w2a8 if M <= DECODE_MAX_M else bl.gemm_w2a8
+
+
+def layer_forward(x: torch.Tensor, lw: LayerWeights, eps: float = 1e-5, out: torch.Tensor = None,
+                  bufs: dict = None):
+    """One layer's linear path.  x [M,H] fp32 or bf16 -> y [M,H] fp32.
+
+    bufs: optional dict of preallocated intermediates (y_qkv, y_o) reused
+    across calls (keeps the allocator out of timed loops).
+    """
+    M = x.shape[0]
+    fn = _contract(M)
+    dev = x.device
+    if bufs is None:
+        bufs = {}
+    y_qkv = bufs.get("y_qkv")
+    if y_qkv is None or y_qkv.shape[0] != M:
+        y_qkv = torch.empty((M, sum(QKV_SEGS)), dtype=torch.float32, device=dev)
+        bufs["y_qkv"] = y_qkv
+    y_o = bufs.get("y_o")
+    if y_o is None or y_o.shape[0] != M:
+        y_o = torch.empty((M, H), dtype=torch.float32, device=dev)
+        bufs["y_o"] = y_o
+    fn(x, lw.packed_qkv, lw.w_qkv, seg_n=QKV_SEGS, y=y_qkv)
+    fn(y_qkv[:, :H], lw.packed_o, lw.w_o, y=y_o)
+    return bl.ffn_chain(y_o, lw.packed_gu, lw.w_gu, lw.packed_down, lw.w_down, eps=eps, y=out)
+
+
+def stack_forward(x: torch.Tensor, layers, eps: float = 1e-5, bufs: dict = None):
+    """All layers in sequence; returns the last layer's output [M,H] fp32."""
+    if bufs is None:
+        bufs = {}
+    M = x.shape[0]
+    outs = bufs.get("outs")
+    if outs is None or outs[0].shape[0] != M:
+        outs = [torch.empty((M, H), dtype=torch.float32, device=x.device) for _ in range(2)]
+        bufs["outs"] = outs
+    cur = x
+    for i, lw in enumerate(layers):
+        cur = layer_forward(cur, lw, eps, out=outs[i & 1], bufs=bufs)
+    return cur
+

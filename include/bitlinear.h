@@ -1,0 +1,188 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear: the BitNet b1.58 BitLinear forward
+ * (1.58-bit ternary weights, 8-bit activations) on AMD Instinct MI355X
+ * (gfx950), hand-written HIP kernels.
+ *
+ * Sources (page title, then the section on it):
+ *  [Q] "BitNet", Transformers quantization guide (Portuguese edition):
+ *      numbered list of the three quantization steps; "Kernels".
+ *  [T] "Transformers 实战 BitNet 1.58 位量化：BitLinear 原理、量化流程与推理加载全指南":
+ *      "BitLinear 的三步量化" (steps 1-3); "推理侧 BitLinear：打包权重、解包与缩放"
+ *      (pack, unpack and the inference forward) and the subln paragraph after it.
+ *  [M] "BitNet" model documentation (Chinese and Portuguese editions):
+ *      "模型详情" / "Detalhes do Modelo" (W1.58A8, ReLU squared, subln, no
+ *      bias) and "BitNetConfig" (rms_norm_eps 1e-5, layer shapes).
+ *
+ * Numerics (what every call computes, bit for bit):
+ *  - weight scale  w_mean = max(float(sum|W| / count), 1e-5), sum in fp64;
+ *  - weight code   c = clip(round_half_even(W / w_mean), -1, 1), fp32 division;
+ *  - packed weight P[r,k] = sum_i (c[i*N/4 + r, k] + 1) << 2i  (plane order);
+ *  - act scale     a_m = 127 / max(max_k |x[m,k]|, 1e-5), fp32 division;
+ *  - act code      q = clip(round_half_even(x * a_m), -128, 127), fp32 multiply;
+ *  - accumulator   A[m,n] = sum_k q[m,k] * c[n,k]  (exact int32);
+ *  - output        y = float(A) * (w_mean_s / a_m), fp32; bf16 = RNE(y);
+ *  - RMSNorm       r = float(1/sqrt(sum h^2 / K + eps)) (fp64), out = (h*r)*g.
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns
+ *    every buffer; the library keeps no device memory between calls.
+ *  - Row-major, contiguous.  Device buffers must be 16-byte aligned.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *    null stream) and returns without synchronizing.
+ *  - Argument checks run on the host before anything is enqueued.  A failed
+ *    check returns a non-zero bl_status, stores a message retrievable with
+ *    bl_last_error() (per host thread) and enqueues nothing.  After
+ *    launching, a launch error returns BL_ERR_HIP.  Faults inside kernels
+ *    surface at the caller's next synchronization.  No C++ exception ever
+ *    crosses this interface.
+ *  - Inputs must be finite (NaN/Inf are outside the contract).
+ *  - Segments: a weight may be several tensors, each ternarized with its own
+ *    scale and packed on its own, concatenated along the packed rows (fused
+ *    q|k|v, gate|up).  seg_n (host) lists their output widths, each a
+ *    multiple of 4, summing to N; w_mean (device) holds one scale per
+ *    segment.  n_seg = 1 with seg_n = NULL means one tensor.  At most
+ *    BL_MAX_SEGMENTS segments.
+ *  - Workspace (ws): device scratch of at least the queried size.  Its first
+ *    BL_WS_ZERO_PREFIX-queried bytes must be zero before the first call that
+ *    uses it (allocate it zero-filled once); every call leaves them zero
+ *    again when it completes.  Calls that share a workspace must not run
+ *    concurrently.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BL_ABI_VERSION 1
+#define BL_MAX_SEGMENTS 8
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    BL_ERR_SHAPE = 2,     /* a size is out of range or not a multiple it must be */
+    BL_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned             */
+    BL_ERR_DTYPE = 4,     /* a dtype code is not allowed for that argument       */
+    BL_ERR_SEGMENTS = 5,  /* bad segment count or widths                         */
+    BL_ERR_WORKSPACE = 6, /* workspace missing or smaller than required          */
+    BL_ERR_HIP = 7        /* the HIP runtime reported an error at launch         */
+} bl_status;
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1, BL_I8 = 2, BL_I32 = 3 } bl_dtype;
+
+typedef void *bl_stream; /* hipStream_t */
+
+/* Version of this interface (BL_ABI_VERSION). */
+int bl_abi_version(void);
+/* Static name of a status code; never NULL. */
+const char *bl_status_string(int status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char *bl_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * bl_ternarize_pack -- absmean ternarization and 2-bit packing of one weight
+ * tensor.  [Q] steps 1-2; [T] "BitLinear 的三步量化" steps 1-2 (scale = mean
+ * |W| over the whole tensor, floored at 1e-5; codes = W / scale rounded and
+ * clipped to [-1,1]) and "推理侧 BitLinear" (codes + 1 stored 2 bits each,
+ * four per byte, a quarter of the rows; field i under mask 3 << 2i).
+ *   W       [N,K] fp32 master weight.
+ *   packed  out [N/4,K] uint8; packed row r, bits 2i..2i+1 hold code+1 of
+ *           weight row i*N/4 + r (plane order).
+ *   w_mean  out, one fp32.
+ *   ws      scratch of bl_ternarize_workspace_bytes(N,K) bytes (no zero
+ *           requirement).
+ * N >= 4, N % 4 == 0, K >= 1, N*K < 2^40.  Deterministic: the fp64 sum runs
+ * in a fixed order for a given (N, K).
+ * ------------------------------------------------------------------------ */
+size_t bl_ternarize_workspace_bytes(int64_t N, int64_t K);
+int bl_ternarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_mean,
+                      void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * bl_quant_act -- per-token absmax int8 activation quantization.  [Q] step 3;
+ * [T] "BitLinear 的三步量化" step 3; [M] "模型详情" (per token).
+ *   x       [M,K] (row stride ldx elements; ldx = 0 means K), dtype BL_F32 or
+ *           BL_BF16.
+ *   q       out [M,K] int8, contiguous.
+ *   a       out [M] fp32 scales a_m = 127 / max(absmax, 1e-5).
+ * M >= 1, K >= 1.
+ * ------------------------------------------------------------------------ */
+int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx,
+                 int8_t *q, float *a, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * bl_gemv_w2a8 / bl_gemm_w2a8 -- the BitLinear contraction with rescale.
+ * [T] "推理侧 BitLinear" forward bullet: quantize the activations, multiply
+ * with the unpacked ternary weight, rescale by the activation and weight
+ * scales.  bl_gemv_w2a8 is the decode path (1 <= M <= 64, weights streamed
+ * from HBM once); bl_gemm_w2a8 is the prefill path (any M >= 1, int8 MFMA
+ * tiles).  Both compute the same bits.
+ *   x       [M,K], row stride ldx elements (0 = K).  x_dtype BL_F32/BL_BF16:
+ *           quantized inside the call (bl_quant_act's arithmetic).  BL_I8:
+ *           already quantized codes, with their scales in `a`.
+ *   a       [M] fp32 activation scales, read when x_dtype == BL_I8, else
+ *           ignored (may be NULL).
+ *   packed  [N/4,K] uint8 packed weight (segments stacked).
+ *   N       total output width; n_seg, seg_n (host), w_mean [n_seg] as above.
+ *   y       out [M,N]; y_dtype BL_F32, BL_BF16, or BL_I32 (the exact int32
+ *           accumulators A, no rescale).
+ *   ws      scratch of bl_gemv_workspace_bytes / bl_gemm_workspace_bytes
+ *           bytes; zero prefix as described above.
+ * K >= 1, K < 2^19 (bounds the int32 partial sums); N % 4 == 0.
+ * ------------------------------------------------------------------------ */
+size_t bl_gemv_workspace_bytes(int M, int N, int K);
+int bl_gemv_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K,
+                 const uint8_t *packed, int N, int n_seg, const int *seg_n,
+                 const float *w_mean, void *y, int y_dtype,
+                 void *ws, size_t ws_bytes, bl_stream stream);
+
+size_t bl_gemm_workspace_bytes(int M, int N, int K);
+int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K,
+                 const uint8_t *packed, int N, int n_seg, const int *seg_n,
+                 const float *w_mean, void *y, int y_dtype,
+                 void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * bl_ffn_chain -- the feed-forward half of a BitNet layer, fused:
+ *   subln RMSNorm(h) -> quantize -> gate|up -> ReLU^2(gate)*up ->
+ *   ffn_sub_norm RMSNorm -> quantize -> down.
+ * [T] subln paragraph after "推理侧 BitLinear" (normalize before the next
+ * projection); [M] "模型详情" (ReLU squared in the FFN, subln, no bias) and
+ * "BitNetConfig" (rms_norm_eps).
+ *   h          [M,H] BL_F32 or BL_BF16.
+ *   g_subln    [H] fp32 gain or NULL (unit gain); g_ffn [I] or NULL.
+ *   eps        RMSNorm epsilon (the model uses 1e-5).
+ *   packed_gu  [2I/4,H] uint8: gate tensor packed, then up tensor packed.
+ *   w_mean_gu  [2] device: gate scale, up scale.
+ *   packed_down [H/4,I] uint8; w_mean_down [1] device.
+ *   y          out [M,H], BL_F32 or BL_BF16.
+ *   dbg        (host struct, may be NULL) optional device buffers receiving
+ *              the stage outputs for stage-wise checks; any member may be NULL.
+ *   ws         scratch of bl_ffn_chain_workspace_bytes(M,H,I); zero prefix.
+ * H % 4 == 0, I % 4 == 0, M >= 1.  M <= 64 runs the decode kernels, larger
+ * M the prefill kernels.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int8_t *q1; /* [M,H] codes after subln            */
+    float *a1;  /* [M]   their scales                 */
+    float *p;   /* [M,I] ReLU^2(gate) * up            */
+    int8_t *q2; /* [M,I] codes after ffn_sub_norm     */
+    float *a2;  /* [M]   their scales                 */
+} bl_ffn_debug;
+
+size_t bl_ffn_chain_workspace_bytes(int M, int H, int I);
+int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I,
+                 const float *g_subln, const float *g_ffn, float eps,
+                 const uint8_t *packed_gu, const float *w_mean_gu,
+                 const uint8_t *packed_down, const float *w_mean_down,
+                 void *y, int y_dtype, void *ws, size_t ws_bytes,
+                 const bl_ffn_debug *dbg, bl_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

@@ -1,0 +1,71 @@
+"""Shared helpers of the GPU parity tests: device transfer and the acceptance rules.
+
+Acceptance (from the method's integer/float split):
+  * int8 codes, scales, packed bytes, weight scales and int32 accumulators:
+    bit-exact;
+  * fp32 outputs: for every token row, max |y - y_ref| <= 1e-5 * max |y_ref|,
+    and rows whose reference is all zero must be exactly zero;
+  * bf16 outputs: the same rule with 8e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_ternary_weight_amd import synth
+
+F32_TOL = 1e-5
+BF16_TOL = 8e-3
+
+requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no HIP device")
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev()).view(torch.bfloat16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def f32_of_bf16(bits: np.ndarray) -> np.ndarray:
+    return synth.bf16_to_f32(bits)
+
+
+def assert_rows_close(y: np.ndarray, ref: np.ndarray, tol: float, what: str = "y"):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    rmax = np.abs(ref).max(axis=1)
+    err = np.abs(y - ref).max(axis=1)
+    zero = rmax == 0
+    assert (err[zero] == 0).all(), f"{what}: rows with all-zero reference are not exactly zero"
+    bad = np.nonzero(err[~zero] > tol * rmax[~zero])[0]
+    assert bad.size == 0, f"{what}: {bad.size} rows out of tolerance, worst rel {np.max(err[~zero] / rmax[~zero]):.3e}"
+
+
+def max_ulp_diff(y: np.ndarray, ref: np.ndarray) -> int:
+    a = np.ascontiguousarray(y, np.float32).view(np.int32).astype(np.int64)
+    b = np.ascontiguousarray(ref, np.float32).view(np.int32).astype(np.int64)
+    a = np.where(a < 0, -(a & 0x7FFFFFFF), a)
+    b = np.where(b < 0, -(b & 0x7FFFFFFF), b)
+    return int(np.abs(a - b).max()) if a.size else 0
+
+
+def assert_exact(got: np.ndarray, ref: np.ndarray, what: str):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if not np.array_equal(got, ref):
+        idx = np.argwhere(got != ref)
+        raise AssertionError(f"{what}: {idx.shape[0]} mismatches, first at {idx[0].tolist()}: "
+                             f"got {got[tuple(idx[0])]} want {ref[tuple(idx[0])]}")

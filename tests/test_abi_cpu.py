@@ -1,0 +1,161 @@
+"""C-ABI contract of libbitlinear, checked without a GPU.
+
+Every call here fails argument validation on the host, before anything is
+enqueued, so no kernel is ever launched (the pointers are fake).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+LIB = os.path.join(ROOT, "bit_ternary_weight_amd", "libbitlinear.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bl_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libbitlinear.so is not built (run __graft_entry__.build())")
+    from bit_ternary_weight_amd import binding
+    return binding
+
+
+def test_header_declares_the_five_calls():
+    fns = declared_functions()
+    for name in ("bl_ternarize_pack", "bl_quant_act", "bl_gemv_w2a8", "bl_gemm_w2a8", "bl_ffn_chain"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    handle = ctypes.CDLL(LIB)
+    missing = [f for f in declared_functions() if not hasattr(handle, f)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    raw = lib.raw
+    assert raw.bl_abi_version() == 1
+    names = [raw.bl_status_string(i).decode() for i in range(8)]
+    assert names == ["BL_OK", "BL_ERR_NULL", "BL_ERR_SHAPE", "BL_ERR_ALIGN", "BL_ERR_DTYPE",
+                     "BL_ERR_SEGMENTS", "BL_ERR_WORKSPACE", "BL_ERR_HIP"]
+    assert raw.bl_status_string(99).decode() == "BL_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x10004)   # 4-byte aligned only
+BIG = 1 << 40
+
+
+def _gemv(raw, fn="bl_gemv_w2a8", x=FAKE, x_dt=1, ldx=0, a=None, M=1, K=256, packed=FAKE, N=256,
+          n_seg=1, seg=None, w_mean=FAKE, y=FAKE, y_dt=0, ws=FAKE, ws_bytes=BIG):
+    return getattr(raw, fn)(x, x_dt, ldx, a, M, K, packed, N, n_seg, seg, w_mean, y, y_dt, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["bl_gemv_w2a8", "bl_gemm_w2a8"])
+def test_contract_validation(lib, fn):
+    raw = lib.raw
+    segs = lambda *v: (ctypes.c_int * len(v))(*v)
+    cases = [
+        (dict(x=None), lib.BL_ERR_NULL),
+        (dict(packed=None), lib.BL_ERR_NULL),
+        (dict(w_mean=None), lib.BL_ERR_NULL),
+        (dict(y=None), lib.BL_ERR_NULL),
+        (dict(ws=None), lib.BL_ERR_NULL),
+        (dict(x_dt=2, a=None), lib.BL_ERR_NULL),          # int8 codes need scales
+        (dict(x_dt=3), lib.BL_ERR_DTYPE),
+        (dict(y_dt=2), lib.BL_ERR_DTYPE),
+        (dict(M=0), lib.BL_ERR_SHAPE),
+        (dict(K=0), lib.BL_ERR_SHAPE),
+        (dict(N=254), lib.BL_ERR_SHAPE),
+        (dict(K=1 << 19), lib.BL_ERR_SHAPE),
+        (dict(ldx=100), lib.BL_ERR_SHAPE),
+        (dict(x=FAKE_MIS), lib.BL_ERR_ALIGN),
+        (dict(packed=FAKE_MIS), lib.BL_ERR_ALIGN),
+        (dict(y=FAKE_MIS), lib.BL_ERR_ALIGN),
+        (dict(n_seg=0), lib.BL_ERR_SEGMENTS),
+        (dict(n_seg=9, seg=segs(*([32] * 8 + [0]))), lib.BL_ERR_SEGMENTS),
+        (dict(n_seg=2, seg=None), lib.BL_ERR_SEGMENTS),
+        (dict(n_seg=2, seg=segs(128, 64)), lib.BL_ERR_SEGMENTS),   # sums to 192
+        (dict(n_seg=2, seg=segs(126, 130)), lib.BL_ERR_SEGMENTS),  # not multiples of 4
+        (dict(ws_bytes=1024), lib.BL_ERR_WORKSPACE),
+    ]
+    if fn == "bl_gemv_w2a8":
+        cases.append((dict(M=65), lib.BL_ERR_SHAPE))
+    for kw, want in cases:
+        st = _gemv(raw, fn=fn, **kw)
+        assert st == want, (kw, st, raw.bl_last_error())
+        assert raw.bl_last_error().decode() != ""
+
+
+def test_workspace_queries(lib):
+    raw = lib.raw
+    zero = 64 * 1024 + 8 * 1024 * 1024
+    assert raw.bl_gemv_workspace_bytes(1, 2560, 2560) >= zero + 2560
+    assert raw.bl_gemm_workspace_bytes(2048, 13824, 2560) >= zero + 2048 * 2560 + 4 * 2048
+    assert raw.bl_ffn_chain_workspace_bytes(4, 2560, 6912) >= zero + 4 * (2560 + 6912 + 4 * 6912)
+    assert raw.bl_ternarize_workspace_bytes(2560, 2560) >= 8
+    assert raw.bl_ternarize_workspace_bytes(2560, 2560) % 256 == 0
+
+
+def test_ternarize_and_quant_validation(lib):
+    raw = lib.raw
+    B = lib
+    assert raw.bl_ternarize_pack(None, 8, 8, FAKE, FAKE, FAKE, BIG, None) == B.BL_ERR_NULL
+    assert raw.bl_ternarize_pack(FAKE, 6, 8, FAKE, FAKE, FAKE, BIG, None) == B.BL_ERR_SHAPE
+    assert raw.bl_ternarize_pack(FAKE, 8, 0, FAKE, FAKE, FAKE, BIG, None) == B.BL_ERR_SHAPE
+    assert raw.bl_ternarize_pack(FAKE_MIS, 8, 8, FAKE, FAKE, FAKE, BIG, None) == B.BL_ERR_ALIGN
+    assert raw.bl_ternarize_pack(FAKE, 2560, 2560, FAKE, FAKE, FAKE, 8, None) == B.BL_ERR_WORKSPACE
+    assert raw.bl_quant_act(None, 0, 4, 8, 0, FAKE, FAKE, None) == B.BL_ERR_NULL
+    assert raw.bl_quant_act(FAKE, 2, 4, 8, 0, FAKE, FAKE, None) == B.BL_ERR_DTYPE
+    assert raw.bl_quant_act(FAKE, 0, 0, 8, 0, FAKE, FAKE, None) == B.BL_ERR_SHAPE
+    assert raw.bl_quant_act(FAKE, 0, 4, 8, 4, FAKE, FAKE, None) == B.BL_ERR_SHAPE
+    assert raw.bl_quant_act(FAKE_MIS, 0, 4, 8, 0, FAKE, FAKE, None) == B.BL_ERR_ALIGN
+
+
+def test_ffn_chain_validation(lib):
+    raw = lib.raw
+    B = lib
+
+    def call(h=FAKE, h_dt=0, M=1, H=256, I=512, eps=1e-5, gu=FAKE, wgu=FAKE, dn=FAKE, wd=FAKE, y=FAKE,
+             y_dt=0, ws=FAKE, ws_bytes=BIG):
+        return raw.bl_ffn_chain(h, h_dt, M, H, I, None, None, eps, gu, wgu, dn, wd, y, y_dt, ws, ws_bytes,
+                                None, None)
+
+    assert call(h=None) == B.BL_ERR_NULL
+    assert call(gu=None) == B.BL_ERR_NULL
+    assert call(h_dt=2) == B.BL_ERR_DTYPE
+    assert call(y_dt=3) == B.BL_ERR_DTYPE
+    assert call(H=254) == B.BL_ERR_SHAPE
+    assert call(I=0) == B.BL_ERR_SHAPE
+    assert call(M=0) == B.BL_ERR_SHAPE
+    assert call(eps=-1.0) == B.BL_ERR_SHAPE
+    assert call(y=FAKE_MIS) == B.BL_ERR_ALIGN
+    assert call(ws_bytes=4096) == B.BL_ERR_WORKSPACE
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+    raw = lib.raw
+    assert _gemv(raw, M=0) == lib.BL_ERR_SHAPE
+    msg_main = raw.bl_last_error().decode()
+    seen = {}
+
+    def worker():
+        seen["before"] = raw.bl_last_error().decode()
+        _gemv(raw, x=None)
+        seen["after"] = raw.bl_last_error().decode()
+
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert seen["before"] == ""
+    assert "NULL" in seen["after"]
+    assert raw.bl_last_error().decode() == msg_main

@@ -1,0 +1,224 @@
+"""GPU parity: bl_gemv_w2a8 (decode) and bl_gemm_w2a8 (prefill) against the oracle.
+
+Weights are always packed by the oracle (its bytes go to the device), so the
+contraction is checked on its own.  int32 accumulators (y dtype int32) are
+compared bit-exactly; fp32 / bf16 outputs by the per-row tolerance, and the
+fp32 path is additionally expected to be bit-identical (it replays the same
+fp32 operations).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_ternary_weight_amd import synth
+from gpu_helpers import (BF16_TOL, F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16, host,
+                         max_ulp_diff, requires_gpu, to_dev)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _bl():
+    from bit_ternary_weight_amd import binding
+    return binding
+
+
+def _weights(seed, seg_n, K):
+    """Oracle-packed segmented weight: (packed [N/4,K], w_means [S], codes [N,K])."""
+    packs, wms, codes = [], [], []
+    for i, n in enumerate(seg_n):
+        p, wm, c = oracle.ternarize_pack(synth.master_weight(seed + 17 * i, n, K))
+        packs.append(p)
+        wms.append(wm)
+        codes.append(c)
+    return np.concatenate(packs), np.array(wms, np.float32), np.concatenate(codes)
+
+
+def _run(fn, x_dev, packed, wms, seg_n, y_dtype, a=None):
+    f = getattr(_bl(), fn)
+    return f(x_dev, to_dev(packed), to_dev(wms), seg_n=list(seg_n) if len(seg_n) > 1 else None,
+             y_dtype=y_dtype, a=a)
+
+
+def _check(fn, M, K, seg_n, x_kind="bf16", seed=0, check_all_dtypes=True):
+    packed, wms, codes = _weights(1000 + seed, seg_n, K)
+    if x_kind == "bf16":
+        bits = synth.act_outliers_bf16(seed, M, K)
+        x_host = f32_of_bf16(bits)
+        x_dev = bf16_dev(bits)
+    else:
+        x_host = synth.act_normal_f32(seed, M, K)
+        x_dev = to_dev(x_host)
+    q, a, A, y = oracle.bitlinear(x_host, codes, seg_n, wms)
+    a_dev = None
+    if x_kind == "i8":
+        x_dev = to_dev(q)
+        a_dev = to_dev(a)
+        x_dev_used = x_dev
+    # raw accumulators
+    Ag = _run(fn, x_dev, packed, wms, seg_n, torch.int32, a=a_dev)
+    assert_exact(host(Ag), A, f"{fn} int32 accumulators")
+    if not check_all_dtypes:
+        return
+    yg = host(_run(fn, x_dev, packed, wms, seg_n, torch.float32, a=a_dev))
+    assert_rows_close(yg, y, F32_TOL, "fp32 y")
+    assert max_ulp_diff(yg, y) == 0, "fp32 output differs from the oracle's bits"
+    yb = host(_run(fn, x_dev, packed, wms, seg_n, torch.bfloat16, a=a_dev))
+    assert_rows_close(f32_of_bf16(yb), y, BF16_TOL, "bf16 y")
+    assert_exact(yb, oracle.to_bf16(y), "bf16 bits")
+
+
+# ----------------------------------------------------------------------------- decode path
+GEMV_SHAPES = [  # (M, K, seg_n)
+    (1, 64, (4,)), (1, 256, (256,)), (2, 256, (64,)), (3, 128, (12,)), (4, 256, (256,)),
+    (5, 320, (36,)), (16, 512, (128,)), (17, 256, (68,)), (33, 192, (64,)), (64, 256, (256,)),
+    (1, 2560, (2560, 640, 640)), (4, 2560, (64, 16, 16)), (64, 1024, (128, 32, 32)),
+    (1, 6912, (2560,)), (1, 6912, (64,)), (2, 4096, (16,)), (64, 6912, (32,)),
+]
+
+
+@pytest.mark.parametrize("M,K,seg_n", GEMV_SHAPES)
+def test_gemv_parity(M, K, seg_n):
+    _check("gemv_w2a8", M, K, seg_n, seed=M + K)
+
+
+@pytest.mark.parametrize("M,K,seg_n", [(1, 17, (8,)), (3, 100, (16,)), (2, 4, (4,)), (4, 33, (12, 4))])
+def test_gemv_ragged_k(M, K, seg_n):
+    _check("gemv_w2a8", M, K, seg_n, seed=3)
+
+
+@pytest.mark.parametrize("x_kind", ["f32", "i8"])
+def test_gemv_input_kinds(x_kind):
+    _check("gemv_w2a8", 4, 2560, (640, 160), x_kind=x_kind, seed=9)
+
+
+def test_gemv_split_path_twice():
+    """A tile split over many workgroups (long K, one tile) uses the atomic
+    scratch; a second call on the same workspace must see it zeroed."""
+    for seed in (1, 2):
+        _check("gemv_w2a8", 1, 6912, (64,), seed=seed, check_all_dtypes=False)
+        _check("gemv_w2a8", 2, 6912, (128,), seed=seed + 5, check_all_dtypes=False)
+
+
+# ----------------------------------------------------------------------------- prefill path
+GEMM_SHAPES = [
+    (1, 64, (4,)), (7, 256, (256,)), (64, 256, (128,)), (65, 256, (128,)), (128, 512, (64,)),
+    (129, 320, (36,)), (200, 1024, (256, 64, 64)), (300, 2560, (160,)), (256, 6912, (128,)),
+]
+
+
+@pytest.mark.parametrize("M,K,seg_n", GEMM_SHAPES)
+def test_gemm_parity(M, K, seg_n):
+    _check("gemm_w2a8", M, K, seg_n, seed=2 * M + K)
+
+
+@pytest.mark.parametrize("M,K,seg_n", [(130, 17, (8,)), (70, 100, (16,))])
+def test_gemm_ragged_k(M, K, seg_n):
+    _check("gemm_w2a8", M, K, seg_n, seed=4)
+
+
+@pytest.mark.parametrize("x_kind", ["f32", "i8"])
+def test_gemm_input_kinds(x_kind):
+    _check("gemm_w2a8", 150, 2560, (256, 64), x_kind=x_kind, seed=10)
+
+
+# ----------------------------------------------------------------------------- properties
+@pytest.mark.parametrize("fn,M", [("gemv_w2a8", 4), ("gemm_w2a8", 130)])
+def test_identity_weight_pins_orientation(fn, M):
+    K = 256
+    packed, wm, codes = oracle.ternarize_pack(np.eye(K, dtype=np.float32))
+    x = synth.act_normal_f32(6, M, K)
+    q, a = oracle.quant_act(x)
+    A = host(getattr(_bl(), fn)(to_dev(x), to_dev(packed), to_dev(np.array([wm])), y_dtype=torch.int32))
+    assert_exact(A, q.astype(np.int32), "identity weight accumulators")
+
+
+@pytest.mark.parametrize("fn,M", [("gemv_w2a8", 64), ("gemm_w2a8", 300)])
+def test_row_permutation_and_determinism(fn, M):
+    K, seg_n = 2560, (256,)
+    packed, wms, _ = _weights(5, seg_n, K)
+    bits = synth.act_heavy_tail_bf16(8, M, K)
+    x = bf16_dev(bits)
+    y1 = _run(fn, x, packed, wms, seg_n, torch.float32)
+    y2 = _run(fn, x, packed, wms, seg_n, torch.float32)
+    assert torch.equal(y1, y2)
+    perm = torch.randperm(M, generator=torch.Generator().manual_seed(1)).to(x.device)
+    y3 = _run(fn, x[perm].contiguous(), packed, wms, seg_n, torch.float32)
+    assert torch.equal(y3, y1[perm])
+
+
+def test_gemv_equals_gemm():
+    K, seg_n = 2560, (2560, 640, 640)
+    packed, wms, _ = _weights(6, seg_n, K)
+    bits = synth.act_outliers_bf16(13, 64, K)
+    x = bf16_dev(bits)
+    yv = _run("gemv_w2a8", x, packed, wms, seg_n, torch.int32)
+    ym = _run("gemm_w2a8", x, packed, wms, seg_n, torch.int32)
+    assert torch.equal(yv, ym)
+
+
+def test_extreme_accumulators():
+    K = 6912
+    M = 2
+    x = np.full((M, K), 1.0, np.float32)
+    x[1] = -1.0
+    W = np.ones((8, K), np.float32)
+    W[1::2] = -1.0
+    packed, wm, codes = oracle.ternarize_pack(W)
+    for fn in ("gemv_w2a8", "gemm_w2a8"):
+        A = host(getattr(_bl(), fn)(to_dev(x), to_dev(packed), to_dev(np.array([wm])), y_dtype=torch.int32))
+        exp = np.array([[127 * K, -127 * K] * 4, [-127 * K, 127 * K] * 4], np.int64)
+        # plane order: output column n is weight row n
+        assert_exact(A, exp.astype(np.int32), fn)
+
+
+# ----------------------------------------------------------------------------- full-size shapes
+@pytest.mark.parametrize("proj", [p for p, _, _ in synth.PROJECTIONS])
+def test_config2_decode_projection(proj):
+    """M=1 decode over each projection of one 2B4T layer, oracle-packed weights."""
+    _, N, K = synth.PROJECTIONS[synth.PROJ_INDEX[proj]]
+    packed, wm, codes = oracle.ternarize_pack(synth.layer_weight(0, proj))
+    bits = synth.act_outliers_bf16(0, 1, K)
+    q, a, A, y = oracle.bitlinear(f32_of_bf16(bits), codes, None, wm)
+    yg = host(_bl().gemv_w2a8(bf16_dev(bits), to_dev(packed), to_dev(np.array([wm]))))
+    assert_rows_close(yg, y, F32_TOL)
+    assert max_ulp_diff(yg, y) == 0
+
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_config3_batched_decode(M):
+    """M=16/64 with Student-t rows over the fused q|k|v and gate|up shapes and down."""
+    bits = synth.act_heavy_tail_bf16(0, M, 2560)
+    for projs in (("q", "k", "v"), ("gate", "up")):
+        packs, wms, codes = [], [], []
+        for p in projs:
+            pk, wm, c = oracle.ternarize_pack(synth.layer_weight(0, p))
+            packs.append(pk); wms.append(wm); codes.append(c)
+        seg_n = [c.shape[0] for c in codes]
+        rows = [0, M // 8, M // 2, M - 1]   # sample rows incl. Student-t rows
+        q, a, A, y = oracle.bitlinear(f32_of_bf16(bits[rows]), np.concatenate(codes), seg_n, np.array(wms))
+        yg = host(_bl().gemv_w2a8(bf16_dev(bits), to_dev(np.concatenate(packs)), to_dev(np.array(wms)),
+                                  seg_n=seg_n))
+        assert_rows_close(yg[rows], y, F32_TOL)
+        assert max_ulp_diff(yg[rows], y) == 0
+
+
+def test_config4_prefill_sampled_rows():
+    """M=2048 prefill: fused gate|up (K=2560 -> 2x6912) and down (6912 -> 2560)."""
+    M = 2048
+    rows = [0, 1, 127, 128, 1000, 2047]
+    pg, wg, cg = oracle.ternarize_pack(synth.layer_weight(0, "gate"))
+    pu, wu, cu = oracle.ternarize_pack(synth.layer_weight(0, "up"))
+    bits = synth.act_normal_bf16(0, M, 2560)
+    wms = np.array([wg, wu], np.float32)
+    yg = host(_bl().gemm_w2a8(bf16_dev(bits), to_dev(np.concatenate([pg, pu])), to_dev(wms),
+                              seg_n=[6912, 6912]))
+    _, _, _, y = oracle.bitlinear(f32_of_bf16(bits[rows]), np.concatenate([cg, cu]), [6912, 6912], wms)
+    assert_rows_close(yg[rows], y, F32_TOL)
+    assert max_ulp_diff(yg[rows], y) == 0
+    pd, wd, cd = oracle.ternarize_pack(synth.layer_weight(0, "down"))
+    bits2 = synth.act_normal_bf16(1, M, 6912)
+    yd = host(_bl().gemm_w2a8(bf16_dev(bits2), to_dev(pd), to_dev(np.array([wd]))))
+    _, _, _, y2 = oracle.bitlinear(f32_of_bf16(bits2[rows]), cd, None, wd)
+    assert_rows_close(yd[rows], y2, F32_TOL)
+    assert max_ulp_diff(yd[rows], y2) == 0
