@@ -42,6 +42,15 @@ class FfnDebug(ctypes.Structure):
     _fields_ = [("q1", _P), ("a1", _P), ("p", _P), ("q2", _P), ("a2", _P)]
 
 
+class GemvProblem(ctypes.Structure):
+    _fields_ = [("x", _P), ("x_dtype", _I), ("ldx", _I), ("a", _P), ("M", _I), ("K", _I),
+                ("packed", _P), ("N", _I), ("n_seg", _I), ("seg_n", ctypes.POINTER(_I)), ("w_mean", _P),
+                ("y", _P), ("y_dtype", _I)]
+
+
+MAX_PROBLEMS = 8
+
+
 _SIGS = {
     "bl_abi_version": (_I, []),
     "bl_status_string": (ctypes.c_char_p, [_I]),
@@ -51,6 +60,8 @@ _SIGS = {
     "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "bl_gemv_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_gemv_w2a8": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
+    "bl_gemv_batched_workspace_bytes": (_S, [_I, ctypes.POINTER(GemvProblem)]),
+    "bl_gemv_w2a8_batched": (_I, [_I, ctypes.POINTER(GemvProblem), _P, _S, _P]),
     "bl_gemm_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_gemm_w2a8": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_ffn_chain_workspace_bytes": (_S, [_I, _I, _I]),
@@ -100,9 +111,8 @@ def _dev(*ts):
 
 
 # ---------------------------------------------------------------------------
-# Workspace: one zero-initialised buffer per device, grown on demand.  The
-# library keeps its zero prefix zero across calls, so the buffer is cleared
-# only when it is (re)allocated.
+# Workspace: one scratch buffer per device, grown on demand.  Calls never read
+# what an earlier call left in it.
 # ---------------------------------------------------------------------------
 _ws_lock = threading.Lock()
 _ws: dict = {}
@@ -114,7 +124,7 @@ def workspace(device, nbytes: int) -> torch.Tensor:
         buf = _ws.get(key)
         if buf is None or buf.numel() < nbytes:
             size = max(int(nbytes), 16 << 20)
-            buf = torch.zeros(size, dtype=torch.uint8, device=device)
+            buf = torch.empty(size, dtype=torch.uint8, device=device)
             _ws[key] = buf
         return buf
 
@@ -177,6 +187,38 @@ def _contract(fn_name, ws_query, x, packed, w_mean, seg_n=None, y_dtype=torch.fl
 def gemv_w2a8(x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):
     """Decode BitLinear (M <= 64): y = rescale(quant(x) @ unpack(packed)^T)."""
     return _contract("bl_gemv_w2a8", raw.bl_gemv_workspace_bytes, x, packed, w_mean, seg_n, y_dtype, a, y)
+
+
+def gemv_w2a8_batched(problems):
+    """Up to 8 independent decode contractions in one launch.
+
+    problems: list of dicts with keys x, packed, w_mean and optional seg_n,
+    a, y, y_dtype.  Returns the list of outputs (allocated when y is absent).
+    """
+    if not 1 <= len(problems) <= MAX_PROBLEMS:
+        raise ValueError(f"1..{MAX_PROBLEMS} problems per launch")
+    arr = (GemvProblem * len(problems))()
+    keep, outs = [], []
+    dev = None
+    for i, pr in enumerate(problems):
+        x, packed, w_mean = pr["x"], pr["packed"], pr["w_mean"]
+        dev = _dev(x, packed, w_mean)
+        if x.stride(1) != 1:
+            raise ValueError("x rows must be contiguous")
+        M, K = x.shape
+        N = packed.shape[0] * 4
+        y = pr.get("y")
+        if y is None:
+            y = torch.empty((M, N), dtype=pr.get("y_dtype", torch.float32), device=dev)
+        n_seg, seg = _segs(pr.get("seg_n"), N)
+        keep.append(seg)
+        a = pr.get("a")
+        arr[i] = GemvProblem(x.data_ptr(), _dt(x), x.stride(0), a.data_ptr() if a is not None else None, M, K,
+                             packed.data_ptr(), N, n_seg, seg, w_mean.data_ptr(), y.data_ptr(), _dt(y))
+        outs.append(y)
+    ws = workspace(dev, raw.bl_gemv_batched_workspace_bytes(len(problems), arr))
+    _check(raw.bl_gemv_w2a8_batched(len(problems), arr, _ptr(ws), ws.numel(), _stream(dev)))
+    return outs
 
 
 def gemm_w2a8(x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):

@@ -2,14 +2,14 @@
 // argument checks, workspace layout and kernel dispatch.  Every check runs on
 // the host before anything is enqueued; nothing here synchronizes.
 //
-// Workspace layout of the contraction calls (gemv, gemm, ffn_chain):
-//   [0, 64 KiB)              tickets of the split decode kernel (u32), zero
-//   [64 KiB, 64 KiB + 8 MiB) int32 accumulators of the split decode kernel, zero
-//   [kZeroBytes, ...)        per-call scratch: activation codes and scales,
-//                            intermediate chain tensors (overwritten each call)
-// The zero prefix sits at the same place for every call, so one workspace
-// can serve calls of any shape in sequence; the decode kernel returns every
-// word it touches there to zero before the call completes.
+// Dispatch of the contraction:
+//   decode (bl_gemv_w2a8*, M <= 64): the batched decode kernel; activations
+//     quantized in its prologue when M <= 4 and the rows fit in LDS, else by
+//     the row kernel into the workspace first;
+//   prefill (bl_gemm_w2a8): the row kernel, then the MFMA GEMM;
+//   any K that is not a multiple of 16: the plain kernel.
+// The workspace only holds per-call scratch (activation codes and scales,
+// intermediate chain tensors); nothing in it survives a call.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -18,10 +18,6 @@
 
 namespace {
 
-constexpr size_t kTicketBytes = 64 * 1024;
-constexpr int kTicketCap = (int)(kTicketBytes / sizeof(unsigned));
-constexpr size_t kAccBytes = 8u * 1024 * 1024;
-constexpr size_t kZeroBytes = kTicketBytes + kAccBytes;
 constexpr int kMaxK = 1 << 19;
 constexpr int kMaxGemvM = 64;
 
@@ -44,17 +40,10 @@ int check_hip(hipError_t e, const char *what) {
     return BL_OK;
 }
 
-// Scratch of a contraction call beyond the zero prefix.
-struct ContractScratch {
-    size_t q_off, a_off, end;
-};
+size_t quant_scratch(int M, int K) { return align256((size_t)M * K) + align256((size_t)M * sizeof(float)); }
 
-ContractScratch contract_scratch(int M, int K) {
-    ContractScratch s;
-    s.q_off = kZeroBytes;
-    s.a_off = s.q_off + align256((size_t)M * K);
-    s.end = s.a_off + align256((size_t)M * sizeof(float));
-    return s;
+bool fusable(int M, int K) {
+    return M <= bl::kFuseMaxM && (size_t)M * K <= (size_t)bl::kFuseMaxBytes && K % 16 == 0;
 }
 
 struct ChainScratch {
@@ -63,7 +52,7 @@ struct ChainScratch {
 
 ChainScratch chain_scratch(int M, int H, int I) {
     ChainScratch s;
-    s.q1 = kZeroBytes;
+    s.q1 = 0;
     s.a1 = s.q1 + align256((size_t)M * H);
     s.p = s.a1 + align256((size_t)M * sizeof(float));
     s.q2 = s.p + align256((size_t)M * I * sizeof(float));
@@ -93,70 +82,191 @@ int make_segtab(int N, int n_seg, const int *seg_n, bl::SegTab &t) {
     return BL_OK;
 }
 
-int check_act_dtype(int dt, bool allow_i8, const char *name) {
-    if (dt == BL_F32 || dt == BL_BF16 || (allow_i8 && dt == BL_I8)) return BL_OK;
-    return fail(BL_ERR_DTYPE, "%s dtype %d not allowed", name, dt);
+// Validated view of one contraction call.
+struct Call {
+    const void *x;
+    int x_dt, ldx;
+    const float *a;
+    int M, K;
+    const uint8_t *packed;
+    int N;
+    bl::SegTab seg;
+    const float *w_mean;
+    void *y;
+    int y_dt;
+};
+
+int validate(const char *fn, bool decode, const bl_gemv_problem &pr, Call &c) {
+    if (!pr.x || !pr.packed || !pr.w_mean || !pr.y) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (pr.x_dtype != BL_F32 && pr.x_dtype != BL_BF16 && pr.x_dtype != BL_I8)
+        return fail(BL_ERR_DTYPE, "%s: x dtype %d not allowed", fn, pr.x_dtype);
+    if (pr.x_dtype == BL_I8 && !pr.a) return fail(BL_ERR_NULL, "%s: x is int8 codes but a is NULL", fn);
+    if (pr.y_dtype != BL_F32 && pr.y_dtype != BL_BF16 && pr.y_dtype != BL_I32)
+        return fail(BL_ERR_DTYPE, "%s: y dtype %d not allowed", fn, pr.y_dtype);
+    if (pr.M < 1 || pr.K < 1 || pr.N < 4)
+        return fail(BL_ERR_SHAPE, "%s: M=%d K=%d N=%d out of range", fn, pr.M, pr.K, pr.N);
+    if (decode && pr.M > kMaxGemvM) return fail(BL_ERR_SHAPE, "%s: M=%d exceeds %d", fn, pr.M, kMaxGemvM);
+    if (pr.K >= kMaxK) return fail(BL_ERR_SHAPE, "%s: K=%d must be below %d", fn, pr.K, kMaxK);
+    if (pr.N % 4 != 0) return fail(BL_ERR_SHAPE, "%s: N=%d is not a multiple of 4", fn, pr.N);
+    const int ldx = pr.ldx == 0 ? pr.K : pr.ldx;
+    if (ldx < pr.K) return fail(BL_ERR_SHAPE, "%s: ldx=%d < K=%d", fn, ldx, pr.K);
+    if (!aligned(pr.x, 16) || !aligned(pr.packed, 16) || !aligned(pr.y, 16) || !aligned(pr.w_mean, 4) ||
+        (pr.a && !aligned(pr.a, 4)))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (int st = make_segtab(pr.N, pr.n_seg, pr.seg_n, c.seg)) return st;
+    c.x = pr.x;
+    c.x_dt = pr.x_dtype;
+    c.ldx = ldx;
+    c.a = pr.a;
+    c.M = pr.M;
+    c.K = pr.K;
+    c.packed = pr.packed;
+    c.N = pr.N;
+    c.w_mean = pr.w_mean;
+    c.y = pr.y;
+    c.y_dt = pr.y_dtype;
+    return BL_OK;
 }
 
-// Shared validation and dispatch of bl_gemv_w2a8 / bl_gemm_w2a8.
-int contract_call(bool decode, const void *x, int x_dt, int ldx, const float *a, int M, int K,
-                  const uint8_t *packed, int N, int n_seg, const int *seg_n, const float *w_mean,
-                  void *y, int y_dt, void *ws, size_t ws_bytes, hipStream_t s) {
-    const char *fn = decode ? "bl_gemv_w2a8" : "bl_gemm_w2a8";
-    if (!x || !packed || !w_mean || !y || !ws) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
-    if (int st = check_act_dtype(x_dt, true, "x")) return st;
-    if (x_dt == BL_I8 && !a) return fail(BL_ERR_NULL, "%s: x is int8 codes but a is NULL", fn);
-    if (y_dt != BL_F32 && y_dt != BL_BF16 && y_dt != BL_I32)
-        return fail(BL_ERR_DTYPE, "%s: y dtype %d not allowed", fn, y_dt);
-    if (M < 1 || K < 1 || N < 4) return fail(BL_ERR_SHAPE, "%s: M=%d K=%d N=%d out of range", fn, M, K, N);
-    if (decode && M > kMaxGemvM) return fail(BL_ERR_SHAPE, "%s: M=%d exceeds %d", fn, M, kMaxGemvM);
-    if (K >= kMaxK) return fail(BL_ERR_SHAPE, "%s: K=%d must be below %d", fn, K, kMaxK);
-    if (N % 4 != 0) return fail(BL_ERR_SHAPE, "%s: N=%d is not a multiple of 4", fn, N);
-    if (ldx == 0) ldx = K;
-    if (ldx < K) return fail(BL_ERR_SHAPE, "%s: ldx=%d < K=%d", fn, ldx, K);
-    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 16) || !aligned(ws, 16) ||
-        !aligned(w_mean, 4) || (a && !aligned(a, 4)))
-        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
-    bl::SegTab seg;
-    if (int st = make_segtab(N, n_seg, seg_n, seg)) return st;
-    const ContractScratch sc = contract_scratch(M, K);
-    if (ws_bytes < sc.end)
-        return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, sc.end);
+bool is_fast(const Call &c) { return c.K % 16 == 0; }
 
-    char *wsb = (char *)ws;
-    bl::Contract c;
-    if (x_dt == BL_I8) {
-        c.q = (const int8_t *)x;
-        c.ldq = ldx;
-        c.a = a;
-    } else {
-        int8_t *q = (int8_t *)(wsb + sc.q_off);
-        float *aw = (float *)(wsb + sc.a_off);
-        if (int st = check_hip(bl::launch_quant_act(x, x_dt, M, K, ldx, q, aw, s), "quant_act launch"))
-            return st;
-        c.q = q;
-        c.ldq = K;
-        c.a = aw;
+// Decode calls are quantized inside the contraction kernel (fused prologue)
+// when every fast call of the launch has raw activations that fit;
+// otherwise the raw ones are quantized by one batched row-kernel launch into
+// the workspace.  Calls with K % 16 != 0 use the plain kernel.
+bool decode_all_fused(int n, const Call *calls) {
+    bool any = false;
+    for (int i = 0; i < n; ++i) {
+        if (!is_fast(calls[i])) continue;
+        if (calls[i].x_dt == BL_I8 || !fusable(calls[i].M, calls[i].K)) return false;
+        any = true;
     }
-    c.M = M;
-    c.K = K;
-    c.P = packed;
-    c.seg = seg;
-    c.R = N / 4;
-    c.w_mean = w_mean;
-    c.y = y;
-    c.y_dt = y_dt;
-    c.ldy = N;
-    c.pair = false;
-    hipError_t e;
-    const bool fast = (K % 16 == 0) && (c.ldq % 16 == 0);
-    if (!fast)
-        e = bl::launch_generic(c, s);
-    else if (decode)
-        e = bl::launch_gemv(c, (int32_t *)(wsb + kTicketBytes), kAccBytes, (unsigned *)wsb, kTicketCap, s);
-    else
-        e = bl::launch_gemm(c, s);
-    return check_hip(e, fn);
+    return any;
+}
+
+size_t decode_scratch(int n, const Call *calls) {
+    const bool fused = decode_all_fused(n, calls);
+    size_t need = 0;
+    for (int i = 0; i < n; ++i) {
+        const Call &c = calls[i];
+        if (c.x_dt == BL_I8) continue;
+        if (is_fast(c) && fused) continue;
+        need += quant_scratch(c.M, c.K);
+    }
+    return need;
+}
+
+size_t prefill_scratch(const Call &c) { return c.x_dt == BL_I8 ? 0 : quant_scratch(c.M, c.K); }
+
+bl::Contract contract_of(const Call &c, const int8_t *q, int ldq, const float *a) {
+    bl::Contract k;
+    k.q = q;
+    k.ldq = ldq;
+    k.a = a;
+    k.M = c.M;
+    k.K = c.K;
+    k.P = c.packed;
+    k.seg = c.seg;
+    k.R = c.N / 4;
+    k.w_mean = c.w_mean;
+    k.y = c.y;
+    k.y_dt = c.y_dt;
+    k.ldy = c.N;
+    k.pair = false;
+    return k;
+}
+
+bl::GemvProblem gemv_of(const Call &c, int mode, const void *x, int ldx, const float *a) {
+    bl::GemvProblem p;
+    memset(&p, 0, sizeof(p));
+    p.x = x;
+    p.a = a;
+    p.P = c.packed;
+    p.w_mean = c.w_mean;
+    p.y = c.y;
+    p.seg = c.seg;
+    p.x_dt = c.x_dt;
+    p.ldx = ldx;
+    p.M = c.M;
+    p.K = c.K;
+    p.R = c.N / 4;
+    p.y_dt = c.y_dt;
+    p.ldy = c.N;
+    p.mode = mode;
+    return p;
+}
+
+// Enqueues a set of validated decode calls (n <= kMaxProblems).
+int run_decode(const char *fn, int n, const Call *calls, char *ws, hipStream_t s) {
+    const bool fused = decode_all_fused(n, calls);
+    bl::GemvBatch b;
+    b.n = 0;
+    bl::QuantBatch qb;
+    qb.n = 0;
+    size_t off = 0;
+    // codes / scales of every call that is not quantized in a fused prologue
+    const int8_t *qv[BL_MAX_PROBLEMS];
+    const float *av[BL_MAX_PROBLEMS];
+    int ldq[BL_MAX_PROBLEMS];
+    for (int i = 0; i < n; ++i) {
+        const Call &c = calls[i];
+        qv[i] = (const int8_t *)c.x;
+        av[i] = c.a;
+        ldq[i] = c.ldx;
+        if (c.x_dt != BL_I8 && !(is_fast(c) && fused)) {
+            int8_t *qw = (int8_t *)(ws + off);
+            float *aw = (float *)(ws + off + align256((size_t)c.M * c.K));
+            off += quant_scratch(c.M, c.K);
+            bl::QuantProblem &qp = qb.p[qb.n++];
+            qp.x = c.x; qp.q = qw; qp.a = aw; qp.x_dt = c.x_dt; qp.M = c.M; qp.K = c.K; qp.ldx = c.ldx;
+            qv[i] = qw;
+            av[i] = aw;
+            ldq[i] = c.K;
+        }
+    }
+    if (qb.n > 0)
+        if (int st = check_hip(bl::launch_quant_batch(qb, s), fn)) return st;
+    for (int i = 0; i < n; ++i) {
+        const Call &c = calls[i];
+        if (!is_fast(c) || ldq[i] % 16 != 0) {
+            if (int st = check_hip(bl::launch_generic(contract_of(c, qv[i], ldq[i], av[i]), s), fn)) return st;
+        } else if (fused) {
+            b.p[b.n++] = gemv_of(c, 1, c.x, c.ldx, nullptr);
+        } else {
+            bl::GemvProblem p = gemv_of(c, 0, qv[i], ldq[i], av[i]);
+            p.x_dt = BL_I8;
+            b.p[b.n++] = p;
+        }
+    }
+    if (b.n == 0) return BL_OK;
+    return check_hip(bl::launch_gemv_batch(b, s), fn);
+}
+
+int check_ws(const char *fn, const void *ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return BL_OK;
+    if (!ws) return fail(BL_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got NULL", fn, need);
+    if (!aligned(ws, 16)) return fail(BL_ERR_ALIGN, "%s: misaligned workspace", fn);
+    if (ws_bytes < need) return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    return BL_OK;
+}
+
+bl_gemv_problem as_problem(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const uint8_t *packed,
+                           int N, int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype) {
+    bl_gemv_problem p;
+    p.x = x;
+    p.x_dtype = x_dtype;
+    p.ldx = ldx;
+    p.a = a;
+    p.M = M;
+    p.K = K;
+    p.packed = packed;
+    p.N = N;
+    p.n_seg = n_seg;
+    p.seg_n = seg_n;
+    p.w_mean = w_mean;
+    p.y = y;
+    p.y_dtype = y_dtype;
+    return p;
 }
 
 } // namespace
@@ -186,8 +296,8 @@ size_t bl_ternarize_workspace_bytes(int64_t N, int64_t K) {
     return align256((size_t)bl::absmean_parts(N * K) * sizeof(double));
 }
 
-int bl_ternarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_mean, void *ws,
-                      size_t ws_bytes, bl_stream stream) {
+int bl_ternarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_mean, void *ws, size_t ws_bytes,
+                      bl_stream stream) {
     g_err[0] = 0;
     if (!W || !packed || !w_mean || !ws) return fail(BL_ERR_NULL, "bl_ternarize_pack: NULL pointer argument");
     if (N < 4 || K < 1 || N % 4 != 0)
@@ -209,7 +319,7 @@ int bl_ternarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_me
 int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx, int8_t *q, float *a, bl_stream stream) {
     g_err[0] = 0;
     if (!x || !q || !a) return fail(BL_ERR_NULL, "bl_quant_act: NULL pointer argument");
-    if (int st = check_act_dtype(x_dtype, false, "x")) return st;
+    if (x_dtype != BL_F32 && x_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "bl_quant_act: x dtype %d not allowed", x_dtype);
     if (M < 1 || K < 1) return fail(BL_ERR_SHAPE, "bl_quant_act: M=%d K=%d out of range", M, K);
     if (ldx == 0) ldx = K;
     if (ldx < K) return fail(BL_ERR_SHAPE, "bl_quant_act: ldx=%d < K=%d", ldx, K);
@@ -220,58 +330,98 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx, int8_t *q, f
 
 size_t bl_gemv_workspace_bytes(int M, int N, int K) {
     (void)N;
-    if (M < 1 || K < 1) return kZeroBytes;
-    return contract_scratch(M, K).end;
+    if (M < 1 || K < 1) return 0;
+    return quant_scratch(M, K);
 }
 
 size_t bl_gemm_workspace_bytes(int M, int N, int K) { return bl_gemv_workspace_bytes(M, N, K); }
 
-int bl_gemv_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const uint8_t *packed,
-                 int N, int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype, void *ws,
-                 size_t ws_bytes, bl_stream stream) {
+int bl_gemv_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const uint8_t *packed, int N,
+                 int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype, void *ws, size_t ws_bytes,
+                 bl_stream stream) {
     g_err[0] = 0;
-    return contract_call(true, x, x_dtype, ldx, a, M, K, packed, N, n_seg, seg_n, w_mean, y, y_dtype, ws,
-                         ws_bytes, (hipStream_t)stream);
+    const char *fn = "bl_gemv_w2a8";
+    const bl_gemv_problem pr = as_problem(x, x_dtype, ldx, a, M, K, packed, N, n_seg, seg_n, w_mean, y, y_dtype);
+    Call c;
+    if (int st = validate(fn, true, pr, c)) return st;
+    if (int st = check_ws(fn, ws, ws_bytes, decode_scratch(1, &c))) return st;
+    return run_decode(fn, 1, &c, (char *)ws, (hipStream_t)stream);
 }
 
-int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const uint8_t *packed,
-                 int N, int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype, void *ws,
-                 size_t ws_bytes, bl_stream stream) {
+size_t bl_gemv_batched_workspace_bytes(int n, const bl_gemv_problem *problems) {
+    size_t need = 0;
+    if (!problems || n < 1) return 0;
+    for (int i = 0; i < n && i < BL_MAX_PROBLEMS; ++i)
+        if (problems[i].M > 0 && problems[i].K > 0) need += quant_scratch(problems[i].M, problems[i].K);
+    return need;
+}
+
+int bl_gemv_w2a8_batched(int n, const bl_gemv_problem *problems, void *ws, size_t ws_bytes, bl_stream stream) {
     g_err[0] = 0;
-    return contract_call(false, x, x_dtype, ldx, a, M, K, packed, N, n_seg, seg_n, w_mean, y, y_dtype, ws,
-                         ws_bytes, (hipStream_t)stream);
+    const char *fn = "bl_gemv_w2a8_batched";
+    if (!problems) return fail(BL_ERR_NULL, "%s: problems is NULL", fn);
+    if (n < 1 || n > BL_MAX_PROBLEMS) return fail(BL_ERR_SHAPE, "%s: n=%d must be in [1,%d]", fn, n, BL_MAX_PROBLEMS);
+    Call calls[BL_MAX_PROBLEMS];
+    for (int i = 0; i < n; ++i)
+        if (int st = validate(fn, true, problems[i], calls[i])) return st;
+    if (int st = check_ws(fn, ws, ws_bytes, decode_scratch(n, calls))) return st;
+    return run_decode(fn, n, calls, (char *)ws, (hipStream_t)stream);
+}
+
+int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const uint8_t *packed, int N,
+                 int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype, void *ws, size_t ws_bytes,
+                 bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_gemm_w2a8";
+    const bl_gemv_problem pr = as_problem(x, x_dtype, ldx, a, M, K, packed, N, n_seg, seg_n, w_mean, y, y_dtype);
+    Call c;
+    if (int st = validate(fn, false, pr, c)) return st;
+    if (int st = check_ws(fn, ws, ws_bytes, prefill_scratch(c))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int8_t *q = (const int8_t *)c.x;
+    int ldq = c.ldx;
+    const float *aq = c.a;
+    if (c.x_dt != BL_I8) {
+        int8_t *qw = (int8_t *)ws;
+        float *aw = (float *)((char *)ws + align256((size_t)c.M * c.K));
+        if (int st = check_hip(bl::launch_quant_act(c.x, c.x_dt, c.M, c.K, c.ldx, qw, aw, s), fn)) return st;
+        q = qw;
+        ldq = c.K;
+        aq = aw;
+    }
+    const bl::Contract k = contract_of(c, q, ldq, aq);
+    return check_hip((is_fast(c) && ldq % 16 == 0) ? bl::launch_gemm(k, s) : bl::launch_generic(k, s), fn);
 }
 
 size_t bl_ffn_chain_workspace_bytes(int M, int H, int I) {
-    if (M < 1 || H < 1 || I < 1) return kZeroBytes;
+    if (M < 1 || H < 1 || I < 1) return 0;
     return chain_scratch(M, H, I).end;
 }
 
-int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g_subln, const float *g_ffn,
-                 float eps, const uint8_t *packed_gu, const float *w_mean_gu, const uint8_t *packed_down,
-                 const float *w_mean_down, void *y, int y_dtype, void *ws, size_t ws_bytes,
-                 const bl_ffn_debug *dbg, bl_stream stream) {
+int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g_subln, const float *g_ffn, float eps,
+                 const uint8_t *packed_gu, const float *w_mean_gu, const uint8_t *packed_down,
+                 const float *w_mean_down, void *y, int y_dtype, void *ws, size_t ws_bytes, const bl_ffn_debug *dbg,
+                 bl_stream stream) {
     g_err[0] = 0;
     const char *fn = "bl_ffn_chain";
-    if (!h || !packed_gu || !w_mean_gu || !packed_down || !w_mean_down || !y || !ws)
+    if (!h || !packed_gu || !w_mean_gu || !packed_down || !w_mean_down || !y)
         return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
-    if (int st = check_act_dtype(h_dtype, false, "h")) return st;
+    if (h_dtype != BL_F32 && h_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "%s: h dtype %d not allowed", fn, h_dtype);
     if (y_dtype != BL_F32 && y_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "%s: y dtype %d not allowed", fn, y_dtype);
     if (M < 1 || H < 4 || I < 4 || H % 4 != 0 || I % 4 != 0)
         return fail(BL_ERR_SHAPE, "%s: M=%d H=%d I=%d (H, I must be positive multiples of 4)", fn, M, H, I);
     if (H >= kMaxK || I >= kMaxK) return fail(BL_ERR_SHAPE, "%s: H or I too large", fn);
     if (!(eps >= 0.0f)) return fail(BL_ERR_SHAPE, "%s: eps must be >= 0", fn);
     if (!aligned(h, 16) || !aligned(packed_gu, 16) || !aligned(packed_down, 16) || !aligned(y, 16) ||
-        !aligned(ws, 16) || !aligned(w_mean_gu, 4) || !aligned(w_mean_down, 4) ||
-        (g_subln && !aligned(g_subln, 4)) || (g_ffn && !aligned(g_ffn, 4)))
+        !aligned(w_mean_gu, 4) || !aligned(w_mean_down, 4) || (g_subln && !aligned(g_subln, 4)) ||
+        (g_ffn && !aligned(g_ffn, 4)))
         return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
     if (dbg && ((dbg->q1 && !aligned(dbg->q1, 16)) || (dbg->q2 && !aligned(dbg->q2, 16)) ||
                 (dbg->p && !aligned(dbg->p, 16)) || (dbg->a1 && !aligned(dbg->a1, 4)) ||
                 (dbg->a2 && !aligned(dbg->a2, 4))))
         return fail(BL_ERR_ALIGN, "%s: misaligned debug pointer", fn);
     const ChainScratch sc = chain_scratch(M, H, I);
-    if (ws_bytes < sc.end)
-        return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, sc.end);
+    if (int st = check_ws(fn, ws, ws_bytes, sc.end)) return st;
 
     hipStream_t s = (hipStream_t)stream;
     char *wsb = (char *)ws;
@@ -280,52 +430,76 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
     float *p = dbg && dbg->p ? dbg->p : (float *)(wsb + sc.p);
     int8_t *q2 = dbg && dbg->q2 ? dbg->q2 : (int8_t *)(wsb + sc.q2);
     float *a2 = dbg && dbg->a2 ? dbg->a2 : (float *)(wsb + sc.a2);
-    int32_t *acc = (int32_t *)(wsb + kTicketBytes);
-    unsigned *tickets = (unsigned *)wsb;
     const bool decode = M <= kMaxGemvM;
+    const bool fuse = decode && fusable(M, H) && fusable(M, I);
+
+    bl::SegTab seg_i, seg_h;
+    make_segtab(I, 1, nullptr, seg_i);
+    make_segtab(H, 1, nullptr, seg_h);
+
+    if (fuse) {
+        // Two launches: each decode kernel normalizes and quantizes its own
+        // input rows in the prologue (stage codes go to the debug buffers).
+        bl::GemvBatch b;
+        memset(&b, 0, sizeof(b));
+        b.n = 1;
+        bl::GemvProblem &g = b.p[0];
+        g.x = h; g.x_dt = h_dtype; g.ldx = H; g.gain = g_subln; g.eps = eps; g.mode = 2;
+        g.M = M; g.K = H; g.R = I / 4; g.P = packed_gu; g.seg = seg_i; g.w_mean = w_mean_gu;
+        g.y = p; g.y_dt = BL_F32; g.ldy = I; g.pair = 1;
+        g.dbg_q = dbg ? dbg->q1 : nullptr; g.dbg_a = dbg ? dbg->a1 : nullptr;
+        if (int st = check_hip(bl::launch_gemv_batch(b, s), "gate|up launch")) return st;
+        memset(&b, 0, sizeof(b));
+        b.n = 1;
+        bl::GemvProblem &d = b.p[0];
+        d.x = p; d.x_dt = BL_F32; d.ldx = I; d.gain = g_ffn; d.eps = eps; d.mode = 2;
+        d.M = M; d.K = I; d.R = H / 4; d.P = packed_down; d.seg = seg_h; d.w_mean = w_mean_down;
+        d.y = y; d.y_dt = y_dtype; d.ldy = H; d.pair = 0;
+        d.dbg_q = dbg ? dbg->q2 : nullptr; d.dbg_a = dbg ? dbg->a2 : nullptr;
+        return check_hip(bl::launch_gemv_batch(b, s), "down launch");
+    }
 
     // 1. subln RMSNorm + quantize
     if (int st = check_hip(bl::launch_rmsnorm_quant(h, h_dtype, M, H, g_subln, eps, q1, a1, s), "subln launch"))
         return st;
     // 2. gate|up with ReLU^2(gate)*up
     bl::Contract c;
-    c.q = q1;
-    c.ldq = H;
-    c.a = a1;
-    c.M = M;
-    c.K = H;
-    c.P = packed_gu;
-    make_segtab(I, 1, nullptr, c.seg);
-    c.R = I / 4;
-    c.w_mean = w_mean_gu;
-    c.y = p;
-    c.y_dt = BL_F32;
-    c.ldy = I;
-    c.pair = true;
+    c.q = q1; c.ldq = H; c.a = a1; c.M = M; c.K = H; c.P = packed_gu; c.seg = seg_i; c.R = I / 4;
+    c.w_mean = w_mean_gu; c.y = p; c.y_dt = BL_F32; c.ldy = I; c.pair = true;
     hipError_t e;
-    if (H % 16 != 0) e = bl::launch_generic(c, s);
-    else if (decode) e = bl::launch_gemv(c, acc, kAccBytes, tickets, kTicketCap, s);
-    else e = bl::launch_gemm(c, s);
+    if (H % 16 != 0) {
+        e = bl::launch_generic(c, s);
+    } else if (decode) {
+        bl::GemvBatch b;
+        memset(&b, 0, sizeof(b));
+        b.n = 1;
+        bl::GemvProblem &g = b.p[0];
+        g.x = q1; g.x_dt = BL_I8; g.ldx = H; g.a = a1; g.mode = 0; g.M = M; g.K = H; g.R = I / 4;
+        g.P = packed_gu; g.seg = seg_i; g.w_mean = w_mean_gu; g.y = p; g.y_dt = BL_F32; g.ldy = I; g.pair = 1;
+        e = bl::launch_gemv_batch(b, s);
+    } else {
+        e = bl::launch_gemm(c, s);
+    }
     if (int st = check_hip(e, "gate|up launch")) return st;
     // 3. ffn_sub_norm RMSNorm + quantize
     if (int st = check_hip(bl::launch_rmsnorm_quant(p, BL_F32, M, I, g_ffn, eps, q2, a2, s), "ffn_sub_norm launch"))
         return st;
     // 4. down
-    c.q = q2;
-    c.ldq = I;
-    c.a = a2;
-    c.K = I;
-    c.P = packed_down;
-    make_segtab(H, 1, nullptr, c.seg);
-    c.R = H / 4;
-    c.w_mean = w_mean_down;
-    c.y = y;
-    c.y_dt = y_dtype;
-    c.ldy = H;
-    c.pair = false;
-    if (I % 16 != 0) e = bl::launch_generic(c, s);
-    else if (decode) e = bl::launch_gemv(c, acc, kAccBytes, tickets, kTicketCap, s);
-    else e = bl::launch_gemm(c, s);
+    c.q = q2; c.ldq = I; c.a = a2; c.K = I; c.P = packed_down; c.seg = seg_h; c.R = H / 4;
+    c.w_mean = w_mean_down; c.y = y; c.y_dt = y_dtype; c.ldy = H; c.pair = false;
+    if (I % 16 != 0) {
+        e = bl::launch_generic(c, s);
+    } else if (decode) {
+        bl::GemvBatch b;
+        memset(&b, 0, sizeof(b));
+        b.n = 1;
+        bl::GemvProblem &d = b.p[0];
+        d.x = q2; d.x_dt = BL_I8; d.ldx = I; d.a = a2; d.mode = 0; d.M = M; d.K = I; d.R = H / 4;
+        d.P = packed_down; d.seg = seg_h; d.w_mean = w_mean_down; d.y = y; d.y_dt = y_dtype; d.ldy = H; d.pair = 0;
+        e = bl::launch_gemv_batch(b, s);
+    } else {
+        e = bl::launch_gemm(c, s);
+    }
     return check_hip(e, "down launch");
 }
 

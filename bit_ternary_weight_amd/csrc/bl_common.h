@@ -79,6 +79,71 @@ __device__ __forceinline__ float relu2_mul(float g, float u) {
 }
 
 // ---------------------------------------------------------------------------
+// int8 MFMA helpers shared by the contraction kernels.
+//
+// Expansion without the -1: for a packed dword b (four k's of one packed
+// row), b & 0x03030303, b & 0x0C0C0C0C, b & 0x30303030 and (b >> 2) &
+// 0x30303030 are four int8x4 operands holding v*1, v*4, v*16, v*16 with
+// v = code + 1 in {0,1,2} for fields 0..3.  The matrix core accumulates
+// sum_k q*v scaled by that power of two; an exact arithmetic shift undoes it,
+// and subtracting sum_k q (the row sum of the codes over the same k range)
+// gives the exact sum_k q*code.  With |q| <= 128 and K < 2^19 every partial
+// stays inside int32.
+//
+// Operand layout of v_mfma_i32_16x16x64_i8: lane l supplies row (l & 15) of
+// A and column (l & 15) of B, each as 16 int8 values of k-group (l >> 4); A
+// and B use the same k placement, so any consistent assignment of k to
+// (group, byte) gives the same dot products.  The 16x16 int32 result sits in
+// lane l as rows 4*(l >> 4) + j, column l & 15, for j = 0..3.
+// ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
+
+__device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void expand(v4i b, v4i f[4]) {
+    f[0] = b & 0x03030303;
+    f[1] = b & 0x0C0C0C0C;
+    f[2] = b & 0x30303030;
+    f[3] = (b >> 2) & 0x30303030;
+}
+
+__device__ __forceinline__ int rowsum16(v4i a) {
+    int s = __builtin_amdgcn_sdot4(a.x, 0x01010101, 0, false);
+    s = __builtin_amdgcn_sdot4(a.y, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(a.z, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(a.w, 0x01010101, s, false);
+    return s;
+}
+
+__device__ __forceinline__ int shift_field(int v, int f) {
+    return f == 0 ? v : (f == 1 ? (v >> 2) : (v >> 4));
+}
+
+// Output of one accumulator entry: packed row vr, field f, token row m with
+// activation scale a.  PAIR: A is the gate accumulator, U the up one, and the
+// output is ReLU^2(gate)*up at column f*R + vr.
+__device__ __forceinline__ void emit_out(void *y, int y_dt, int ldy, bool pair, const SegTab &seg, int R,
+                                         const float *w_mean, int m, int vr, int f, float a, int A, int U) {
+    if (pair) {
+        const float gv = (float)A * (w_mean[0] / a);
+        const float uv = (float)U * (w_mean[1] / a);
+        const float p = relu2_mul(gv, uv);
+        const size_t idx = (size_t)m * ldy + f * R + vr;
+        if (y_dt == BL_BF16)
+            ((uint16_t *)y)[idx] = f32_to_bf16(p);
+        else
+            ((float *)y)[idx] = p;
+    } else {
+        const ColOf cs = col_of(seg, vr, f);
+        store_out(y, y_dt, (size_t)m * ldy + cs.col, A, w_mean[cs.seg] / a);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (host side).  Each returns hipSuccess or the launch error.
 // ---------------------------------------------------------------------------
 hipError_t launch_absmean(const float *W, int64_t count, double *partials, int nparts,
@@ -89,6 +154,18 @@ hipError_t launch_ternarize_pack(const float *W, int N, int K, const float *w_me
 
 hipError_t launch_quant_act(const void *x, int x_dt, int M, int K, int ldx, int8_t *q, float *a,
                             hipStream_t s);
+// Several row quantizations in one launch (problems of the batched decode).
+struct QuantProblem {
+    const void *x;
+    int8_t *q;
+    float *a;
+    int x_dt, M, K, ldx, row0;
+};
+struct QuantBatch {
+    int n;
+    QuantProblem p[8];
+};
+hipError_t launch_quant_batch(QuantBatch &qb, hipStream_t s);
 hipError_t launch_rmsnorm_quant(const void *h, int h_dt, int M, int K, const float *g, float eps,
                                 int8_t *q, float *a, hipStream_t s);
 
@@ -108,9 +185,35 @@ struct Contract {
     bool pair;        // gate|up with ReLU^2(gate)*up epilogue; up rows at P + R*K
 };
 
-// Decode path (M <= 64).  acc/tickets: zero-initialised scratch, left zero.
-hipError_t launch_gemv(const Contract &c, int32_t *acc, size_t acc_cap, unsigned *tickets,
-                       int ticket_cap, hipStream_t s);
+// Decode path (M <= 64): one launch covers up to kMaxProblems independent
+// contractions.  Modes: 0 = int8 codes in (x, a); 1 = raw fp32/bf16 x,
+// quantized in the kernel's prologue; 2 = raw x, RMSNorm then quantized in
+// the prologue.  Modes 1-2 need M <= kFuseMaxM and M*K <= kFuseMaxBytes.
+constexpr int kMaxProblems = 8;
+constexpr int kFuseMaxM = 4;
+constexpr int kFuseMaxBytes = 48 * 1024;
+
+struct GemvProblem {
+    const void *x;      // mode 0: int8 codes; else fp32/bf16 activations
+    const float *a;     // mode 0: activation scales [M]
+    const float *gain;  // mode 2: RMSNorm gain [K] or null
+    const uint8_t *P;   // packed weight, row stride K (PAIR: gate rows then up rows)
+    const float *w_mean;
+    void *y;
+    int8_t *dbg_q;      // optional: the prologue's codes [M,K] (written once)
+    float *dbg_a;       // optional: their scales [M]
+    SegTab seg;
+    int x_dt, ldx, M, K, R, y_dt, ldy, tile0, mode, pair;
+    float eps;
+};
+
+struct GemvBatch {
+    int n;
+    GemvProblem p[kMaxProblems];
+};
+
+// Fills tile0 of every problem and launches; all problems must share `pair`.
+hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s);
 // Prefill path (any M).
 hipError_t launch_gemm(const Contract &c, hipStream_t s);
 // Any K (slow, simple): used when K is not a multiple of 16.

@@ -191,7 +191,45 @@ hipError_t launch_rows(const void *x, int dt, int M, int K, int ldx, const float
     return hipGetLastError();
 }
 
+// Several independent quantizations in one launch: block b quantizes row
+// b - row0 of the problem whose [row0, row0 + M) range holds b.
+__global__ __launch_bounds__(kThreads) void k_quant_batch(QuantBatch qb) {
+    __shared__ float redf[4];
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxProblems; ++i)
+        if (i < qb.n && (int)blockIdx.x >= qb.p[i].row0) pi = i;
+    const QuantProblem &p = qb.p[pi];
+    const int m = (int)blockIdx.x - p.row0;
+    const int K = p.K;
+    float amax = 0.0f;
+    for (int k = threadIdx.x; k < K; k += kThreads) {
+        const size_t i = (size_t)m * p.ldx + k;
+        const float v = p.x_dt == BL_BF16 ? bf16_to_f32(((const uint16_t *)p.x)[i]) : ((const float *)p.x)[i];
+        amax = fmaxf(amax, fabsf(v));
+    }
+    amax = block_max(amax, redf);
+    const float s = 127.0f / fmaxf(amax, kFloor);
+    if (threadIdx.x == 0) p.a[m] = s;
+    for (int k = threadIdx.x; k < K; k += kThreads) {
+        const size_t i = (size_t)m * p.ldx + k;
+        const float v = p.x_dt == BL_BF16 ? bf16_to_f32(((const uint16_t *)p.x)[i]) : ((const float *)p.x)[i];
+        p.q[(size_t)m * K + k] = (int8_t)quant1(v, s);
+    }
+}
+
 } // namespace
+
+hipError_t launch_quant_batch(QuantBatch &qb, hipStream_t s) {
+    int rows = 0;
+    for (int i = 0; i < qb.n; ++i) {
+        qb.p[i].row0 = rows;
+        rows += qb.p[i].M;
+    }
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quant_batch, dim3(rows), dim3(kThreads), 0, s, qb);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const void *x, int x_dt, int M, int K, int ldx, int8_t *q, float *a,
                             hipStream_t s) {

@@ -42,11 +42,10 @@
  *    multiple of 4, summing to N; w_mean (device) holds one scale per
  *    segment.  n_seg = 1 with seg_n = NULL means one tensor.  At most
  *    BL_MAX_SEGMENTS segments.
- *  - Workspace (ws): device scratch of at least the queried size.  Its first
- *    BL_WS_ZERO_PREFIX-queried bytes must be zero before the first call that
- *    uses it (allocate it zero-filled once); every call leaves them zero
- *    again when it completes.  Calls that share a workspace must not run
- *    concurrently.
+ *  - Workspace (ws): device scratch of at least the queried size (the query
+ *    is an upper bound; a call that needs none accepts NULL).  Contents are
+ *    per call and never read across calls; calls that share a workspace must
+ *    not run concurrently.
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -60,6 +59,7 @@ extern "C" {
 
 #define BL_ABI_VERSION 1
 #define BL_MAX_SEGMENTS 8
+#define BL_MAX_PROBLEMS 8
 
 typedef enum {
     BL_OK = 0,
@@ -131,7 +131,7 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx,
  *   y       out [M,N]; y_dtype BL_F32, BL_BF16, or BL_I32 (the exact int32
  *           accumulators A, no rescale).
  *   ws      scratch of bl_gemv_workspace_bytes / bl_gemm_workspace_bytes
- *           bytes; zero prefix as described above.
+ *           bytes (activation codes when the call quantizes x).
  * K >= 1, K < 2^19 (bounds the int32 partial sums); N % 4 == 0.
  * ------------------------------------------------------------------------ */
 size_t bl_gemv_workspace_bytes(int M, int N, int K);
@@ -139,6 +139,33 @@ int bl_gemv_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int
                  const uint8_t *packed, int N, int n_seg, const int *seg_n,
                  const float *w_mean, void *y, int y_dtype,
                  void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * bl_gemv_w2a8_batched -- up to BL_MAX_PROBLEMS independent decode
+ * contractions in one launch (for example the seven projections of a layer,
+ * each with its own activations).  Each problem has the arguments of
+ * bl_gemv_w2a8 and the same rules; the results are identical to n separate
+ * bl_gemv_w2a8 calls.  problems is a host array.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const void *x;
+    int x_dtype;
+    int ldx;
+    const float *a;
+    int M;
+    int K;
+    const uint8_t *packed;
+    int N;
+    int n_seg;
+    const int *seg_n; /* host */
+    const float *w_mean;
+    void *y;
+    int y_dtype;
+} bl_gemv_problem;
+
+size_t bl_gemv_batched_workspace_bytes(int n, const bl_gemv_problem *problems);
+int bl_gemv_w2a8_batched(int n, const bl_gemv_problem *problems, void *ws, size_t ws_bytes,
+                         bl_stream stream);
 
 size_t bl_gemm_workspace_bytes(int M, int N, int K);
 int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K,
@@ -162,7 +189,7 @@ int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int
  *   y          out [M,H], BL_F32 or BL_BF16.
  *   dbg        (host struct, may be NULL) optional device buffers receiving
  *              the stage outputs for stage-wise checks; any member may be NULL.
- *   ws         scratch of bl_ffn_chain_workspace_bytes(M,H,I); zero prefix.
+ *   ws         scratch of bl_ffn_chain_workspace_bytes(M,H,I).
  * H % 4 == 0, I % 4 == 0, M >= 1.  M <= 64 runs the decode kernels, larger
  * M the prefill kernels.
  * ------------------------------------------------------------------------ */

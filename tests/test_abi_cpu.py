@@ -68,7 +68,7 @@ def test_contract_validation(lib, fn):
         (dict(packed=None), lib.BL_ERR_NULL),
         (dict(w_mean=None), lib.BL_ERR_NULL),
         (dict(y=None), lib.BL_ERR_NULL),
-        (dict(ws=None), lib.BL_ERR_NULL),
+        (dict(ws=None, M=8), lib.BL_ERR_WORKSPACE),       # 8 bf16 rows need scratch
         (dict(x_dt=2, a=None), lib.BL_ERR_NULL),          # int8 codes need scales
         (dict(x_dt=3), lib.BL_ERR_DTYPE),
         (dict(y_dt=2), lib.BL_ERR_DTYPE),
@@ -85,22 +85,24 @@ def test_contract_validation(lib, fn):
         (dict(n_seg=2, seg=None), lib.BL_ERR_SEGMENTS),
         (dict(n_seg=2, seg=segs(128, 64)), lib.BL_ERR_SEGMENTS),   # sums to 192
         (dict(n_seg=2, seg=segs(126, 130)), lib.BL_ERR_SEGMENTS),  # not multiples of 4
-        (dict(ws_bytes=1024), lib.BL_ERR_WORKSPACE),
+        (dict(ws_bytes=1024, M=8), lib.BL_ERR_WORKSPACE),
     ]
     if fn == "bl_gemv_w2a8":
         cases.append((dict(M=65), lib.BL_ERR_SHAPE))
     for kw, want in cases:
         st = _gemv(raw, fn=fn, **kw)
+        # a case that passed validation would have reached a launch: never allowed here
+        assert st not in (lib.BL_OK, lib.BL_ERR_HIP), (kw, st)
         assert st == want, (kw, st, raw.bl_last_error())
         assert raw.bl_last_error().decode() != ""
 
 
 def test_workspace_queries(lib):
     raw = lib.raw
-    zero = 64 * 1024 + 8 * 1024 * 1024
-    assert raw.bl_gemv_workspace_bytes(1, 2560, 2560) >= zero + 2560
-    assert raw.bl_gemm_workspace_bytes(2048, 13824, 2560) >= zero + 2048 * 2560 + 4 * 2048
-    assert raw.bl_ffn_chain_workspace_bytes(4, 2560, 6912) >= zero + 4 * (2560 + 6912 + 4 * 6912)
+    assert raw.bl_gemv_workspace_bytes(1, 2560, 2560) >= 2560 + 4
+    assert raw.bl_gemm_workspace_bytes(2048, 13824, 2560) >= 2048 * 2560 + 4 * 2048
+    assert raw.bl_ffn_chain_workspace_bytes(4, 2560, 6912) >= 4 * (2560 + 6912 + 4 * 6912)
+    assert raw.bl_gemv_workspace_bytes(0, 4, 4) == 0
     assert raw.bl_ternarize_workspace_bytes(2560, 2560) >= 8
     assert raw.bl_ternarize_workspace_bytes(2560, 2560) % 256 == 0
 
@@ -138,7 +140,34 @@ def test_ffn_chain_validation(lib):
     assert call(M=0) == B.BL_ERR_SHAPE
     assert call(eps=-1.0) == B.BL_ERR_SHAPE
     assert call(y=FAKE_MIS) == B.BL_ERR_ALIGN
-    assert call(ws_bytes=4096) == B.BL_ERR_WORKSPACE
+    assert call(ws_bytes=16) == B.BL_ERR_WORKSPACE
+    assert call(ws=None) == B.BL_ERR_WORKSPACE
+
+
+def test_batched_validation(lib):
+    raw = lib.raw
+    P = lib.GemvProblem
+
+    def prob(**kw):
+        d = dict(x=0x10000, x_dtype=1, ldx=0, a=None, M=1, K=256, packed=0x20000, N=256, n_seg=1,
+                 seg_n=None, w_mean=0x30000, y=0x40000, y_dtype=0)
+        d.update(kw)
+        return P(**d)
+
+    arr = (P * 2)(prob(), prob(M=0))
+    assert raw.bl_gemv_w2a8_batched(2, arr, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    arr = (P * 2)(prob(), prob(x=None))
+    assert raw.bl_gemv_w2a8_batched(2, arr, FAKE, BIG, None) == lib.BL_ERR_NULL
+    arr = (P * 1)(prob(M=65))
+    assert raw.bl_gemv_w2a8_batched(1, arr, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    assert raw.bl_gemv_w2a8_batched(0, arr, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    assert raw.bl_gemv_w2a8_batched(9, arr, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    assert raw.bl_gemv_w2a8_batched(1, None, FAKE, BIG, None) == lib.BL_ERR_NULL
+    arr = (P * 2)(prob(M=8), prob(M=8, K=512))      # M > 4: codes go to the workspace
+    need = raw.bl_gemv_batched_workspace_bytes(2, arr)
+    assert need >= 8 * 256 + 8 * 512
+    assert raw.bl_gemv_w2a8_batched(2, arr, FAKE, need - 1, None) == lib.BL_ERR_WORKSPACE
+    assert raw.bl_gemv_w2a8_batched(2, arr, None, 0, None) == lib.BL_ERR_WORKSPACE
 
 
 def test_last_error_is_per_thread(lib):

@@ -54,7 +54,6 @@ def _check(fn, M, K, seg_n, x_kind="bf16", seed=0, check_all_dtypes=True):
     if x_kind == "i8":
         x_dev = to_dev(q)
         a_dev = to_dev(a)
-        x_dev_used = x_dev
     # raw accumulators
     Ag = _run(fn, x_dev, packed, wms, seg_n, torch.int32, a=a_dev)
     assert_exact(host(Ag), A, f"{fn} int32 accumulators")
@@ -92,9 +91,9 @@ def test_gemv_input_kinds(x_kind):
     _check("gemv_w2a8", 4, 2560, (640, 160), x_kind=x_kind, seed=9)
 
 
-def test_gemv_split_path_twice():
-    """A tile split over many workgroups (long K, one tile) uses the atomic
-    scratch; a second call on the same workspace must see it zeroed."""
+def test_gemv_long_k_repeated():
+    """Long K over a single tile (one workgroup streams all of it); repeated
+    calls on the same workspace stay exact."""
     for seed in (1, 2):
         _check("gemv_w2a8", 1, 6912, (64,), seed=seed, check_all_dtypes=False)
         _check("gemv_w2a8", 2, 6912, (128,), seed=seed + 5, check_all_dtypes=False)
@@ -222,3 +221,59 @@ def test_config4_prefill_sampled_rows():
     _, _, _, y2 = oracle.bitlinear(f32_of_bf16(bits2[rows]), cd, None, wd)
     assert_rows_close(yd[rows], y2, F32_TOL)
     assert max_ulp_diff(yd[rows], y2) == 0
+
+
+# ----------------------------------------------------------------------------- batched decode
+def _proj_case(layer, proj, M, seed, kind="outliers"):
+    _, N, K = synth.PROJECTIONS[synth.PROJ_INDEX[proj]]
+    packed, wm, codes = oracle.ternarize_pack(synth.layer_weight(layer, proj))
+    if kind == "heavy":
+        bits = synth.act_heavy_tail_bf16(seed, M, K)
+    else:
+        bits = synth.act_outliers_bf16(seed, M, K)
+    return packed, wm, codes, bits
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 64])
+def test_batched_seven_projections(M):
+    """The 7 projections of a layer, each with its own activations, in one call."""
+    cases = [_proj_case(0, p, M, 50 + j, "heavy" if M >= 16 else "outliers")
+             for j, (p, _, _) in enumerate(synth.PROJECTIONS)]
+    probs = [dict(x=bf16_dev(bits), packed=to_dev(pk), w_mean=to_dev(np.array([wm]))) for pk, wm, _, bits in cases]
+    outs = _bl().gemv_w2a8_batched(probs)
+    rows = list(range(M)) if M <= 4 else [0, M // 8, M - 1]
+    for (pk, wm, codes, bits), y in zip(cases, outs):
+        _, _, _, yr = oracle.bitlinear(f32_of_bf16(bits[rows]), codes, None, wm)
+        yh = host(y)[rows]
+        assert_rows_close(yh, yr, F32_TOL)
+        assert max_ulp_diff(yh, yr) == 0
+
+
+def test_batched_mixed_kinds():
+    """Fused-prologue, int8-input, larger-M and ragged-K problems in one call."""
+    specs = [(1, 2560, (64, 16, 16), "bf16"), (8, 512, (128,), "f32"), (3, 256, (32,), "i8"),
+             (2, 100, (16,), "bf16"), (1, 6912, (64,), "bf16")]
+    probs, refs = [], []
+    for i, (M, K, seg_n, kind) in enumerate(specs):
+        packed, wms, codes = _weights(300 + i, seg_n, K)
+        if kind == "bf16":
+            bits = synth.act_outliers_bf16(70 + i, M, K)
+            xh, xd = f32_of_bf16(bits), bf16_dev(bits)
+        else:
+            xh = synth.act_normal_f32(70 + i, M, K)
+            xd = to_dev(xh)
+        q, a, A, y = oracle.bitlinear(xh, codes, seg_n, wms)
+        pr = dict(x=xd, packed=to_dev(packed), w_mean=to_dev(wms), seg_n=list(seg_n) if len(seg_n) > 1 else None)
+        if kind == "i8":
+            pr.update(x=to_dev(q), a=to_dev(a))
+        probs.append(pr)
+        refs.append(y)
+    outs = _bl().gemv_w2a8_batched(probs)
+    for y, yr in zip(outs, refs):
+        assert_rows_close(host(y), yr, F32_TOL)
+        assert max_ulp_diff(host(y), yr) == 0
+    # each problem alone gives the same bits
+    for pr, y in zip(probs, outs):
+        kw = {k: v for k, v in pr.items() if k in ("seg_n", "a")}
+        y1 = _bl().gemv_w2a8(pr["x"], pr["packed"], pr["w_mean"], **kw)
+        assert torch.equal(y1, y)
