@@ -209,6 +209,7 @@ struct GemvProblem {
 
 struct GemvBatch {
     int n;
+    int ring_off;   // LDS offset of the weight ring (streaming variant)
     GemvProblem p[kMaxProblems];
 };
 
