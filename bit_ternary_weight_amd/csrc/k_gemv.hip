@@ -479,6 +479,28 @@ struct kWaitVm {
     static constexpr int value = (VM & 0xF) | (0x7 << 4) | (0xF << 8) | ((VM >> 4) << 14);
 };
 
+// s_waitcnt vmcnt(n) for a run-time n in [0, 2*kRing] (the counter field is an
+// immediate, so dispatch over the possible values).
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value); break;
+    case 1: __builtin_amdgcn_s_waitcnt(kWaitVm<1>::value); break;
+    case 2: __builtin_amdgcn_s_waitcnt(kWaitVm<2>::value); break;
+    case 3: __builtin_amdgcn_s_waitcnt(kWaitVm<3>::value); break;
+    case 4: __builtin_amdgcn_s_waitcnt(kWaitVm<4>::value); break;
+    case 5: __builtin_amdgcn_s_waitcnt(kWaitVm<5>::value); break;
+    case 6: __builtin_amdgcn_s_waitcnt(kWaitVm<6>::value); break;
+    case 7: __builtin_amdgcn_s_waitcnt(kWaitVm<7>::value); break;
+    case 8: __builtin_amdgcn_s_waitcnt(kWaitVm<8>::value); break;
+    case 9: __builtin_amdgcn_s_waitcnt(kWaitVm<9>::value); break;
+    case 10: __builtin_amdgcn_s_waitcnt(kWaitVm<10>::value); break;
+    case 11: __builtin_amdgcn_s_waitcnt(kWaitVm<11>::value); break;
+    case 12: __builtin_amdgcn_s_waitcnt(kWaitVm<12>::value); break;
+    case 13: __builtin_amdgcn_s_waitcnt(kWaitVm<13>::value); break;
+    default: __builtin_amdgcn_s_waitcnt(kWaitVm<14>::value); break;
+    }
+}
+
 __device__ __forceinline__ void dma16(const void *src, void *lds_slot) {
     __builtin_amdgcn_global_load_lds(src, lds_slot, 16, 0, 0);
 }
@@ -499,6 +521,7 @@ void k_gemv_lds(GemvBatch b) {
     __shared__ double rd[16];
     __shared__ float rf[16];
     __shared__ __attribute__((aligned(16))) int8_t q_s[kLdsQBytes];
+    __shared__ float wm_s[BL_MAX_SEGMENTS];
     extern __shared__ __attribute__((aligned(16))) unsigned char ring_lds[];
 
     int pi = 0;
@@ -550,12 +573,19 @@ void k_gemv_lds(GemvBatch b) {
         }
     }
 
-    // keep every activation / gain load ahead of the weight loads
-    asm volatile("" ::: "memory");
+    // the weight scales of the output segments, with the same early loads
+    const int nscale = PAIR ? 2 : p.seg.n;
+    const float wmv = (int)threadIdx.x < nscale ? p.w_mean[threadIdx.x] : 0.0f;
 
-    // 2. fill the ring with the first kRing steps.  Every lane issues every
-    // load (out-of-range lanes read a fixed valid address and their slot is
-    // masked on use), so exactly kRing*NB loads are in flight at each wait.
+    // Every wave issues its activation loads before any wave issues a weight
+    // load (the CU's memory pipeline is shared: a wave's activation loads
+    // must not queue behind the other waves' weight stream).
+    lds_barrier();
+
+    // 2. fill the ring with this wave's first min(ks, kRing) steps.  Every
+    // lane of a wave issues each load (lanes outside the tile or past K read
+    // a fixed valid address; their slot bytes are masked on use), so the
+    // wave's outstanding-load count is known exactly at every wait below.
     const uint8_t *pw[NB];
     pw[0] = p.P + (size_t)vr * K + 16 * g;
     if (PAIR) pw[NB - 1] = p.P + (size_t)(p.R + vr) * K + 16 * g;
@@ -564,14 +594,17 @@ void k_gemv_lds(GemvBatch b) {
         const bool ok = i < ks && st * 64 + 16 * g < K && row_ok;
         return ok ? (const void *)(pw[t] + st * 64) : (const void *)p.P;
     };
+    // The prefill is always kRing steps (steps past this wave's last read the
+    // fixed address), so the wait below has a constant count.
 #pragma unroll
     for (int i = 0; i < kRing; ++i)
 #pragma unroll
         for (int t = 0; t < NB; ++t) dma16(src_of(t, i), ring + (i * NB + t) * 1024);
 
-    // The activation and gain loads are older than the kRing*NB weight loads
-    // just issued: this wait retires them without waiting for any weight load.
+    // The activation, gain and scale loads are older than the kRing*NB weight
+    // loads just issued: this wait retires them without waiting for any of those.
     __builtin_amdgcn_s_waitcnt(kWaitVm<kRing * NB>::value);
+    if ((int)threadIdx.x < nscale) wm_s[threadIdx.x] = wmv;
 
     // 3. prologue: quantize the activation rows into LDS (uses only xr)
     for (int i = threadIdx.x; i < NB * NE; i += W * 64) red[i] = 0;
@@ -591,17 +624,22 @@ void k_gemv_lds(GemvBatch b) {
         const int st = wave + W * i;
         const int kk = st * 64 + 16 * g;
         const bool kok = kk < K;
-        // the oldest kRing-1 steps in flight are younger than step i
-        __builtin_amdgcn_s_waitcnt(kWaitVm<(kRing - 1) * NB>::value);
+        // slots issued so far: the kRing prefill plus one refill per earlier
+        // iteration that had a step kRing ahead; all issued after step i may
+        // stay outstanding
+        const int issued = kRing + (i < ks - kRing ? i : (ks > kRing ? ks - kRing : 0));
+        wait_vm((issued - i - 1) * NB);
         v4i bw[NB];
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
             bw[t] = *reinterpret_cast<const v4i *>(ring + (slot * NB + t) * 1024 + 16 * lane);
             if (!(kok && row_ok)) bw[t] = v4i{0, 0, 0, 0};
         }
-        // refill the slot (a fixed address once past this wave's last step)
+        // refill the slot with step i + kRing when this wave has one
+        if (i + kRing < ks) {
 #pragma unroll
-        for (int t = 0; t < NB; ++t) dma16(src_of(t, i + kRing), ring + (slot * NB + t) * 1024);
+            for (int t = 0; t < NB; ++t) dma16(src_of(t, i + kRing), ring + (slot * NB + t) * 1024);
+        }
         const v4i a_op = (kok && lr < M) ? *reinterpret_cast<const v4i *>(q_s + (size_t)lr * K + kk)
                                          : v4i{0, 0, 0, 0};
         qs += rowsum16(a_op);
@@ -648,7 +686,7 @@ void k_gemv_lds(GemvBatch b) {
         const int m = 4 * (ln >> 4) + j;
         const int vrr = r0 + (ln & 15);
         if (m >= M || vrr >= p.R) continue;
-        emit_out(p.y, p.y_dt, p.ldy, PAIR, p.seg, p.R, p.w_mean, m, vrr, f, a_s[m], red[e],
+        emit_out(p.y, p.y_dt, p.ldy, PAIR, p.seg, p.R, wm_s, m, vrr, f, a_s[m], red[e],
                  PAIR ? red[(NB - 1) * NE + e] : 0);
     }
 }
