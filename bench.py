@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel loop (for profiler runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
@@ -156,6 +158,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
+        return
     H, I, KV = synth.HIDDEN, synth.INTERMEDIATE, synth.KV_DIM
     timer = Timer(torch)
     t_build = time.perf_counter()

@@ -204,6 +204,7 @@ struct GemvProblem {
     float *dbg_a;       // optional: their scales [M]
     SegTab seg;
     int x_dt, ldx, M, K, R, y_dt, ldy, tile0, mode, pair;
+    int cs;             // streaming variant: column sets of 4 packed rows per workgroup
     float eps;
 };
 

@@ -328,27 +328,37 @@ __global__ __launch_bounds__(W * 64) void k_gemv(GemvBatch b) {
 }
 
 // ===========================================================================
-// Streaming variant for the fused path (M <= 4): the packed weights land in
-// LDS through the gfx950 direct global->LDS loads (global_load_lds_dwordx4),
-// so the bytes in flight cost no registers and two workgroups share a CU.
-// Each wave owns a ring of RING 1 KB slots per weight tensor; lane l's 16
-// bytes of a k-step land at slot + 16*l and only lane l reads them back, so a
-// wave needs no barrier to consume its own slots: it waits for its oldest
-// load (s_waitcnt vmcnt), reads the slot, and immediately refills it with the
-// step RING places ahead.  The raw activation rows are loaded into registers
-// before any weight load, so the quantization prologue (which needs only
-// them) never waits behind the weight stream.
+// Streaming variant for the fused path (M <= 4).  One 12-wave workgroup per
+// CU, with two roles:
+//   * 8 stream waves move the packed weights into LDS with the gfx950 direct
+//     global->LDS loads (global_load_lds_dwordx4) and run the MFMAs.  Each
+//     owns a ring of kRing 1 KB slots; lane l's 16 bytes land at slot + 16 l
+//     and only this wave reads the slot back, so consuming a slot needs only
+//     the wave's own s_waitcnt vmcnt, never a workgroup barrier.  They issue
+//     their first kRing loads at once, before anything else.
+//   * 4 quantizer waves (one per SIMD) load the activation rows and quantize
+//     them into LDS.  They synchronise among themselves through LDS flags,
+//     not s_barrier: a stream wave is stalled in the issue of its weight
+//     loads for microseconds while the memory system is saturated, and a
+//     workgroup barrier would hold the quantizer waves behind it.
+// The stream waves wait for the quantizer waves' flags before their first
+// MFMA.  Both roles meet at one barrier at the end, where the column sums are
+// reduced, rescaled and stored.
 // ===========================================================================
-constexpr int kRing = 7;
-constexpr int kLdsWaves = 8;
-constexpr int kLdsQBytes = 8192;   // static LDS for the activation codes (M*K)
-constexpr int kXChunks = 4;   // 16-byte activation chunks per lane (all rows); row_pass selects among 4
+constexpr int kStreamWaves = 8;
+constexpr int kQuantWaves = 4;
+constexpr int kLdsWaves = kStreamWaves + kQuantWaves;
+constexpr int kQuantLanes = kQuantWaves * 64;
+constexpr int kRing = 12;            // 1 KB ring slots per stream wave
+constexpr int kLdsQBytes = 12288;    // static LDS for the activation codes (M rows of pitch Kp)
+constexpr int kXRegs = 8;            // 16-byte activation chunks per quantizer lane (all rows)
+constexpr int kSpinMax = 1 << 22;    // bound of every flag wait (about 0.2 s)
 
 // Activation elements per 16-byte chunk.
 __host__ __device__ constexpr int x_per_chunk(int dt) { return dt == BL_BF16 ? 8 : 4; }
 
-// Chunks per row for K elements (every lane takes chunk c at element
-// (c * lanes + lane) * per_chunk).
+// Chunks per row for K elements (quantizer lane ql takes chunk c at element
+// (c * lanes + ql) * per_chunk).
 __host__ __device__ inline int x_chunks(int K, int dt, int lanes) {
     const int per = x_per_chunk(dt) * lanes;
     return (K + per - 1) / per;
@@ -364,111 +374,240 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int W>
-__device__ __forceinline__ float block_max_lds(float v, float *rf) {
-    v = wave_max(v);
-    if ((threadIdx.x & 63) == 0) rf[threadIdx.x >> 6] = v;
-    lds_barrier();
-    float r = rf[0];
-#pragma unroll
-    for (int i = 1; i < W; ++i) r = fmaxf(r, rf[i]);
-    lds_barrier();
-    return r;
+// Wave-wide reductions without LDS round trips: DPP within each 16-lane row
+// (xor 1, xor 2, rotate 4, rotate 8 leave every lane of a row holding the
+// row's result), then the four rows combined in order through readlane.  The
+// result is uniform and its summation order fixed.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
-template <int W>
-__device__ __forceinline__ double block_sum_lds(double v, double *rd) {
-    v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) rd[threadIdx.x >> 6] = v;
-    lds_barrier();
-    double r = rd[0];
-#pragma unroll
-    for (int i = 1; i < W; ++i) r += rd[i];
-    lds_barrier();
-    return r;
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+    v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_i<0x124>(v);   // row_ror:4
+    v += dpp_i<0x128>(v);   // row_ror:8
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-// Element i of a 16-byte activation chunk (static i after unrolling).
+__device__ __forceinline__ float fmax_dpp_step(float v, int b) { return fmaxf(v, __int_as_float(b)); }
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmax_dpp_step(v, dpp_i<0xB1>(__float_as_int(v)));
+    v = fmax_dpp_step(v, dpp_i<0x4E>(__float_as_int(v)));
+    v = fmax_dpp_step(v, dpp_i<0x124>(__float_as_int(v)));
+    v = fmax_dpp_step(v, dpp_i<0x128>(__float_as_int(v)));
+    const int iv = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 32)), __int_as_float(__builtin_amdgcn_readlane(iv, 48))));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp_i<CTRL>((int)(b & 0xFFFFFFFF));
+    const int hi = dpp_i<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+    v += dpp_d<0xB1>(v);
+    v += dpp_d<0x4E>(v);
+    v += dpp_d<0x124>(v);
+    v += dpp_d<0x128>(v);
+    return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
+}
+
+// The PER activation values of a 16-byte chunk as fp32 (bf16: 8, fp32: 4).
 template <int PER>
-__device__ __forceinline__ float chunk_elem(const v4i &c, int i) {
+__device__ __forceinline__ void chunk_f32(const v4i &c, float *v) {
     if (PER == 8) {
-        const uint32_t w = (uint32_t)c[i >> 1];
-        return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float((uint32_t)c[i] << 16);
+            v[2 * i + 1] = __uint_as_float((uint32_t)c[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float((uint32_t)c[i]);
     }
-    return __uint_as_float((uint32_t)c[i]);
 }
 
-// One pass of the prologue over the register chunks of row m:
-// OP 0 accumulates sum v^2 (fp64), OP 1 the max |v|, OP 2 quantizes into q_s.
-// Register j of an array of four, with static indices only (a dynamic index
-// would put the array in scratch memory).
-__device__ __forceinline__ v4i pick4(const v4i *a, int j) {
-    return j == 0 ? a[0] : (j == 1 ? a[1] : (j == 2 ? a[2] : a[3]));
+// Flags of the quantizer waves, in LDS: qflag[w] counts the steps wave w has
+// published.  A wave publishes after its LDS writes (the LDS executes one
+// wave's operations in order).  Waiters poll with plain loads behind a
+// compiler memory clobber (a volatile or atomic LDS load would make the
+// compiler wait for every weight load in flight first).
+__device__ __forceinline__ void publish(int *qflag, int w, int step) {
+    asm volatile("" ::: "memory");
+    if ((threadIdx.x & 63) == 0) qflag[w] = step;
+    asm volatile("" ::: "memory");
 }
 
-template <int PER, int OP>
-__device__ __forceinline__ void row_pass(const GemvProblem &p, const v4i *xr, const v4i *gr, int E, int m,
-                                         int lanes, float r, float s, bool norm, int8_t *q_s, double &ss,
-                                         float &amax) {
+// The poll is one LDS read and scalar compares; between polls the wave
+// sleeps SLEEP x 64 cycles, so that spinning waves leave the SIMD to the
+// waves sharing it (the stream waves' wait is long; the quantizer waves'
+// waits on each other are short).
+template <int SLEEP>
+__device__ __forceinline__ void wait_published(const int *qflag, int step) {
+    static_assert(kQuantWaves == 4, "one 16-byte read covers the flags");
+    for (int it = 0; it < kSpinMax; ++it) {
+        asm volatile("" ::: "memory");
+        const v4i f = *reinterpret_cast<const v4i *>(qflag);
+        const int lo = min(__builtin_amdgcn_readfirstlane(f[0]), __builtin_amdgcn_readfirstlane(f[1]));
+        const int hi = min(__builtin_amdgcn_readfirstlane(f[2]), __builtin_amdgcn_readfirstlane(f[3]));
+        if (min(lo, hi) >= step) break;
+        __builtin_amdgcn_s_sleep(SLEEP);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Element m of a 4-element per-row array, m uniform and run-time (selects,
+// not an indexed access: that would go through scratch memory).
+template <typename T>
+__device__ __forceinline__ T sel4(const T *a, int m) {
+    return m == 0 ? a[0] : (m == 1 ? a[1] : (m == 2 ? a[2] : a[3]));
+}
+
+// Per-row accumulator update with a uniform, run-time row index.
+template <typename T, typename F>
+__device__ __forceinline__ void row_update(T *acc, int m, T v, F op) {
+#pragma unroll
+    for (int r = 0; r < kFuseMaxM; ++r)
+        if (r == m) acc[r] = op(acc[r], v);
+}
+
+// Quantizer waves: quantize the M (<= 4) rows held in xr (register j holds
+// row j / E, chunk j % E of this lane) into q_s (row pitch `pitch`), with the
+// same arithmetic as prologue(): optional RMSNorm (fp64 sum of squares), then
+// per-row absmax, scale and codes.  With the norm, M is 1 (register j holds
+// chunk j, so the gains of chunk j sit in the static registers
+// gr[j*PER/4 ...], all ones when the norm has no gain).  Each wave leaves its
+// share of every row's code sum in sq_s[m * kQuantWaves + qw].  Global memory
+// is not touched.
+template <int PER, bool NORM>
+__device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, const v4i *gr, int E, int pitch, int qw, int ql,
+                           int8_t *q_s, float *a_s, int *sq_s, double *part_d, float *part_f,
+                           int *qflag) {
     const int K = p.K;
-    // fully unrolled (static bounds, predicated): a loop reading registers
-    // loaded before it would make the compiler wait for every load in flight
+    const int M = p.M;
+    auto elem0 = [&](int j) { return ((j % E) * kQuantLanes + ql) * PER; };
+    auto row_of = [&](int j) { return j / E; };
+    // the norm of register j's chunk (NORM: M == 1, so chunk j, static)
+    auto norm = [&](float *v, int j, float r) {
+        const v4i g0 = gr[(j * (PER / 4)) % kXRegs];
+        const v4i g1 = PER == 8 ? gr[(j * 2 + 1) % kXRegs] : g0;
 #pragma unroll
-    for (int c = 0; c < kXChunks; ++c) {
-        const int k0 = (c * lanes + (int)threadIdx.x) * PER;
-        if (c >= E || k0 >= K) continue;   // K % PER == 0: a chunk is all in or all out
-        const v4i xc = pick4(xr, m * E + c);
-        // gains of this chunk: PER floats = PER/4 registers starting at gr[c*PER/4]
-        const v4i g0 = pick4(gr, c * (PER / 4));
-        const v4i g1 = PER == 8 ? pick4(gr, c * 2 + 1) : g0;
-        uint32_t pk[2] = {0, 0};
+        for (int i = 0; i < PER; ++i)
+            v[i] = (v[i] * r) * __uint_as_float((uint32_t)(i < 4 ? g0[i & 3] : g1[i & 3]));
+    };
+    int step = 0;
+    float r[kFuseMaxM] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (NORM) {
+        double ss[kFuseMaxM] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            float t = chunk_elem<PER>(xc, i);
-            if (OP == 0) {
-                ss += (double)t * (double)t;
-                continue;
-            }
-            if (norm) {
-                t = t * r;
-                if (p.gain) t = t * __uint_as_float((uint32_t)(i < 4 ? g0[i & 3] : g1[i & 3]));
-            }
-            if (OP == 1) amax = fmaxf(amax, fabsf(t));
-            else pk[i >> 2] |= (uint32_t)(quant1(t, s) & 0xFF) << (8 * (i & 3));
+        for (int j = 0; j < kXRegs; ++j) {
+            if (j >= M * E || elem0(j) >= K) continue;   // K % PER == 0
+            float v[PER];
+            chunk_f32<PER>(xr[j], v);
+            double t = 0.0;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) t += (double)v[i] * (double)v[i];
+            row_update(ss, row_of(j), t, [](double a, double b) { return a + b; });
         }
-        if (OP == 2) {
-            int8_t *dst = q_s + (size_t)m * K + k0;
-            if (PER == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[1]);
-            else *reinterpret_cast<uint32_t *>(dst) = pk[0];
+#pragma unroll
+        for (int m = 0; m < kFuseMaxM; ++m) {
+            if (m >= M) break;
+            const double w = wave_sum_dpp(ss[m]);
+            if ((threadIdx.x & 63) == 0) part_d[m * kQuantWaves + qw] = w;
+        }
+        publish(qflag, qw, ++step);
+        wait_published<1>(qflag, step);
+#pragma unroll
+        for (int m = 0; m < kFuseMaxM; ++m) {
+            if (m >= M) break;
+            double t = part_d[m * kQuantWaves];
+#pragma unroll
+            for (int w = 1; w < kQuantWaves; ++w) t += part_d[m * kQuantWaves + w];
+            r[m] = (float)(1.0 / sqrt(t / (double)K + (double)p.eps));
         }
     }
-}
-
-// Quantize the M (<= 4) rows held in xr (row m, chunk c at xr[m*E + c]) into
-// q_s and a_s; same arithmetic as prologue().  Global memory is not touched
-// (no loads or stores may sit between the weight loads in flight).
-template <int W, int PER>
-__device__ void prologue_regs(const GemvProblem &p, const v4i *xr, const v4i *gr, int E, int8_t *q_s, float *a_s,
-                              double *rd, float *rf) {
-    const bool norm = p.mode == 2;
-    const int lanes = W * 64;
+    float amax[kFuseMaxM] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) {
+        if (j >= M * E || elem0(j) >= K) continue;
+        float v[PER];
+        chunk_f32<PER>(xr[j], v);
+        const int m = row_of(j);
+        if (NORM) norm(v, j, r[0]);
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) t = fmaxf(t, fabsf(v[i]));
+        row_update(amax, m, t, [](float a, float b) { return fmaxf(a, b); });
+    }
 #pragma unroll
     for (int m = 0; m < kFuseMaxM; ++m) {
-        if (m >= p.M) break;
-        double ss = 0.0;
-        float amax = 0.0f;
-        float r = 1.0f;
-        if (norm) {
-            row_pass<PER, 0>(p, xr, gr, E, m, lanes, 1.0f, 0.0f, norm, q_s, ss, amax);
-            ss = block_sum_lds<W>(ss, rd);
-            r = (float)(1.0 / sqrt(ss / (double)p.K + (double)p.eps));
-        }
-        row_pass<PER, 1>(p, xr, gr, E, m, lanes, r, 0.0f, norm, q_s, ss, amax);
-        amax = block_max_lds<W>(amax, rf);
-        const float s = 127.0f / fmaxf(amax, kFloor);   // IEEE fp32 division
-        if (threadIdx.x == 0) a_s[m] = s;
-        row_pass<PER, 2>(p, xr, gr, E, m, lanes, r, s, norm, q_s, ss, amax);
+        if (m >= M) break;
+        const float w = wave_max_dpp(amax[m]);
+        if ((threadIdx.x & 63) == 0) part_f[m * kQuantWaves + qw] = w;
     }
+    publish(qflag, qw, ++step);
+    wait_published<1>(qflag, step);
+    float s[kFuseMaxM] = {1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+    for (int m = 0; m < kFuseMaxM; ++m) {
+        if (m >= M) break;
+        float t = part_f[m * kQuantWaves];
+#pragma unroll
+        for (int w = 1; w < kQuantWaves; ++w) t = fmaxf(t, part_f[m * kQuantWaves + w]);
+        s[m] = 127.0f / fmaxf(t, kFloor);   // IEEE fp32 division
+        if (threadIdx.x == (unsigned)(kStreamWaves * 64)) a_s[m] = s[m];
+    }
+    int qsum[kFuseMaxM] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < kXRegs; ++j) {
+        const int k0 = elem0(j);
+        if (j >= M * E || k0 >= K) continue;
+        float v[PER];
+        chunk_f32<PER>(xr[j], v);
+        const int m = row_of(j);
+        if (NORM) norm(v, j, r[0]);
+        const float scale = sel4(s, m);
+        uint32_t pk[PER / 4];
+        int cs = 0;
+#pragma unroll
+        for (int h = 0; h < PER / 4; ++h) {
+            uint32_t u = 0;
+            // code + 128 is an integer in [0, 255]: the byte conversion is exact
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float q = __builtin_amdgcn_fmed3f(rintf(v[4 * h + jj] * scale), -128.0f, 127.0f);
+                u = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, jj, u);
+            }
+            pk[h] = u ^ 0x80808080u;   // offset binary -> two's complement bytes
+            cs = __builtin_amdgcn_sdot4((int)pk[h], 0x01010101, cs, false);
+        }
+        row_update(qsum, m, cs, [](int a, int b) { return a + b; });
+        int8_t *dst = q_s + (size_t)m * pitch + k0;
+        if (PER == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[PER / 4 - 1]);
+        else *reinterpret_cast<uint32_t *>(dst) = pk[0];
+    }
+#pragma unroll
+    for (int m = 0; m < kFuseMaxM; ++m) {
+        if (m >= M) break;
+        const int t = wave_sum_dpp(qsum[m]);
+        if ((threadIdx.x & 63) == 0) sq_s[m * kQuantWaves + qw] = t;
+    }
+    publish(qflag, qw, ++step);
 }
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt = VM, leaving expcnt and
@@ -479,47 +618,43 @@ struct kWaitVm {
     static constexpr int value = (VM & 0xF) | (0x7 << 4) | (0xF << 8) | ((VM >> 4) << 14);
 };
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 2*kRing] (the counter field is an
-// immediate, so dispatch over the possible values).
-__device__ __forceinline__ void wait_vm(int n) {
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value); break;
-    case 1: __builtin_amdgcn_s_waitcnt(kWaitVm<1>::value); break;
-    case 2: __builtin_amdgcn_s_waitcnt(kWaitVm<2>::value); break;
-    case 3: __builtin_amdgcn_s_waitcnt(kWaitVm<3>::value); break;
-    case 4: __builtin_amdgcn_s_waitcnt(kWaitVm<4>::value); break;
-    case 5: __builtin_amdgcn_s_waitcnt(kWaitVm<5>::value); break;
-    case 6: __builtin_amdgcn_s_waitcnt(kWaitVm<6>::value); break;
-    case 7: __builtin_amdgcn_s_waitcnt(kWaitVm<7>::value); break;
-    case 8: __builtin_amdgcn_s_waitcnt(kWaitVm<8>::value); break;
-    case 9: __builtin_amdgcn_s_waitcnt(kWaitVm<9>::value); break;
-    case 10: __builtin_amdgcn_s_waitcnt(kWaitVm<10>::value); break;
-    case 11: __builtin_amdgcn_s_waitcnt(kWaitVm<11>::value); break;
-    case 12: __builtin_amdgcn_s_waitcnt(kWaitVm<12>::value); break;
-    case 13: __builtin_amdgcn_s_waitcnt(kWaitVm<13>::value); break;
-    default: __builtin_amdgcn_s_waitcnt(kWaitVm<14>::value); break;
-    }
-}
 
 __device__ __forceinline__ void dma16(const void *src, void *lds_slot) {
     __builtin_amdgcn_global_load_lds(src, lds_slot, 16, 0, 0);
 }
 
-// Occupancy target: two 8-wave workgroups per CU (4 waves per SIMD, <= 128
-// VGPRs); the LDS ring (kRing KB per wave and tensor) bounds it as well.
+// A unit of the weight stream is 4 packed rows x kUnitK bytes (k values) of
+// one tensor: 1 KB, fetched by one wave with one 16-byte-per-lane direct load.
+// Lane L fetches row q = L >> 4 of the unit, 16-byte chunk (L & 15) ^ rr, where
+// rr is the row's index within its wave's row group, and the bytes land at
+// slot + 16 L.  Each row's 256 bytes thus arrive as two whole 128-byte lines,
+// and the xor puts the 16 rows that one MFMA operand read touches on distinct
+// LDS banks.
+constexpr int kUnitK = 256;
+constexpr int kMaxCS = 8;   // column sets (4 packed rows each) per workgroup
+constexpr int kMaxTileRows = 4 * kMaxCS;
+
+// A workgroup owns 4*CS packed rows of each of the NB tensors, over all of K.
+// Its stream waves split them into row groups of RW = min(4*CS, 16) rows: a
+// stream wave always works on the same row group and tensor and walks the
+// k-ranges kr0, kr0 + kstep, ...  The 16 MFMA columns of a wave are its RW
+// rows times 16/RW field slots: column n is row n % RW; MFMA i (of RW/4)
+// takes field i*(16/RW) + n/RW of it.  One 16-byte operand read of a row thus
+// feeds RW/4 MFMAs.
 template <bool PAIR>
-__global__ __launch_bounds__(kLdsWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(kLdsWaves * 64)
 void k_gemv_lds(GemvBatch b) {
-    constexpr int W = kLdsWaves;
     constexpr int NB = PAIR ? 2 : 1;
-    constexpr int NE = 1024;   // MT == 1
+    constexpr int SW = kStreamWaves;
     // Static LDS objects (distinct from the dynamic weight ring, so the
     // compiler can tell that writing them does not race the ring's loads);
     // the dynamic ring then starts after them, never at LDS address 0.
-    __shared__ int red[NB * NE];
-    __shared__ float a_s[64];
-    __shared__ double rd[16];
-    __shared__ float rf[16];
+    __shared__ int red[NB * kMaxTileRows * 4 * kFuseMaxM];   // [tensor][packed row][field][row of x]
+    __shared__ float a_s[kFuseMaxM];
+    __shared__ int sq_s[kFuseMaxM * kQuantWaves];      // per-wave code sums of each row
+    __shared__ double part_d[kFuseMaxM * kQuantWaves];
+    __shared__ float part_f[kFuseMaxM * kQuantWaves];
+    __shared__ __attribute__((aligned(16))) int qflag[kQuantWaves];
     __shared__ __attribute__((aligned(16))) int8_t q_s[kLdsQBytes];
     __shared__ float wm_s[BL_MAX_SEGMENTS];
     extern __shared__ __attribute__((aligned(16))) unsigned char ring_lds[];
@@ -530,164 +665,212 @@ void k_gemv_lds(GemvBatch b) {
         if (i < b.n && (int)blockIdx.x >= b.p[i].tile0) pi = i;
     const GemvProblem &p = b.p[pi];
 
+    const int CS = p.cs;                 // 1, 2, 4 or 8; CS * NB divides SW
     const int tile = (int)blockIdx.x - p.tile0;
+    const int r0 = tile * 4 * CS;        // first packed row of the tile
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int lr = lane & 15;
-    const int g = lane >> 4;
-    const int r0 = tile * 16;
-    const int vr = r0 + lr;
-    const bool row_ok = vr < p.R;
     const int K = p.K;
     const int M = p.M;
-    const int nsteps = (K + 63) >> 6;
-    const int ks = (nsteps + W - 1) / W;   // steps of this wave: wave + W*i, i < ks
-    unsigned char *ring = ring_lds + (size_t)wave * (kRing * NB * 1024);
+    const int Kp = (K + kUnitK - 1) / kUnitK * kUnitK;   // row pitch of q_s
 
-    // 1. the raw activation rows, into registers, before any weight load
-    const int E = x_chunks(K, p.x_dt, W * 64);
-    v4i xr[kXChunks];
-    v4i gr[kXChunks];
-    {
+    // LDS that is accumulated into or polled, and the zero tail of every code
+    // row (k in [K, Kp) multiplies weight bytes that lie past K or are not
+    // loaded at all), before any wave can touch it
+    for (int i = threadIdx.x; i < NB * kMaxTileRows * 4 * kFuseMaxM; i += kLdsWaves * 64) red[i] = 0;
+    if ((int)threadIdx.x < kQuantWaves) qflag[threadIdx.x] = 0;
+    if (Kp > K)
+        for (int i = threadIdx.x; i < M * (Kp - K); i += kLdsWaves * 64)
+            q_s[(i / (Kp - K)) * Kp + K + i % (Kp - K)] = 0;
+    lds_barrier();
+
+    if (wave >= SW) {
+        // ---------------- quantizer waves ----------------
+        const int qw = wave - SW;
+        const int ql = (int)threadIdx.x - SW * 64;
         const int per = x_per_chunk(p.x_dt);
         const int esz = p.x_dt == BL_BF16 ? 2 : 4;
-        // unconditional loads (out-of-range chunks read row 0, chunk 0 and are
-        // never used), so the wait counter sees straight-line code
+        const int E = x_chunks(K, p.x_dt, kQuantLanes);
+        // Registers past the rows are loaded too (straight-line code), each
+        // lane from its own chunk of row 0: every workgroup runs this at the
+        // same moment, and placeholder loads of one fixed address would all
+        // queue on the single L2 channel that holds it.
+        v4i xr[kXRegs];
+        v4i gr[kXRegs];
+        const size_t spread = ((size_t)ql * 16) % ((size_t)K * esz);
 #pragma unroll
-        for (int j = 0; j < kXChunks; ++j) {
-            const int m = j / (E > 0 ? E : 1);
+        for (int j = 0; j < kXRegs; ++j) {
+            const int m = j / E;
             const int c = j - m * E;
-            const int k0 = (c * W * 64 + (int)threadIdx.x) * per;
+            const int k0 = (c * kQuantLanes + ql) * per;
             const bool ok = j < M * E && k0 < K;
-            xr[j] = ld16((const unsigned char *)p.x + (ok ? ((size_t)m * p.ldx + k0) * esz : 0));
+            xr[j] = ld16((const unsigned char *)p.x + (ok ? ((size_t)m * p.ldx + k0) * esz : spread));
         }
         // RMSNorm gains of this lane's chunks (shared by the rows): register
-        // c*per/4 + h holds gain[k0(c) + 4h .. +3]; unused ones read x.
+        // c*per/4 + h holds gain[k0(c) + 4h .. +3]; all ones without gains
+        const bool gains = p.gain != nullptr && p.mode == 2;
+        if (gains) {
+            const int gspread = (ql * 4) % K;
 #pragma unroll
-        for (int j = 0; j < kXChunks; ++j) {
-            const int c = j / (per / 4);
-            const int h = j - c * (per / 4);
-            const int k0 = (c * W * 64 + (int)threadIdx.x) * per + 4 * h;
-            const bool ok = p.gain != nullptr && p.mode == 2 && c < E && k0 < K;
-            gr[j] = ok ? ld16(p.gain + k0) : ld16(p.x);
-        }
-    }
-
-    // the weight scales of the output segments, with the same early loads
-    const int nscale = PAIR ? 2 : p.seg.n;
-    const float wmv = (int)threadIdx.x < nscale ? p.w_mean[threadIdx.x] : 0.0f;
-
-    // Every wave issues its activation loads before any wave issues a weight
-    // load (the CU's memory pipeline is shared: a wave's activation loads
-    // must not queue behind the other waves' weight stream).
-    lds_barrier();
-
-    // 2. fill the ring with this wave's first min(ks, kRing) steps.  Every
-    // lane of a wave issues each load (lanes outside the tile or past K read
-    // a fixed valid address; their slot bytes are masked on use), so the
-    // wave's outstanding-load count is known exactly at every wait below.
-    const uint8_t *pw[NB];
-    pw[0] = p.P + (size_t)vr * K + 16 * g;
-    if (PAIR) pw[NB - 1] = p.P + (size_t)(p.R + vr) * K + 16 * g;
-    auto src_of = [&](int t, int i) -> const void * {
-        const int st = wave + W * i;
-        const bool ok = i < ks && st * 64 + 16 * g < K && row_ok;
-        return ok ? (const void *)(pw[t] + st * 64) : (const void *)p.P;
-    };
-    // The prefill is always kRing steps (steps past this wave's last read the
-    // fixed address), so the wait below has a constant count.
-#pragma unroll
-    for (int i = 0; i < kRing; ++i)
-#pragma unroll
-        for (int t = 0; t < NB; ++t) dma16(src_of(t, i), ring + (i * NB + t) * 1024);
-
-    // The activation, gain and scale loads are older than the kRing*NB weight
-    // loads just issued: this wait retires them without waiting for any of those.
-    __builtin_amdgcn_s_waitcnt(kWaitVm<kRing * NB>::value);
-    if ((int)threadIdx.x < nscale) wm_s[threadIdx.x] = wmv;
-
-    // 3. prologue: quantize the activation rows into LDS (uses only xr)
-    for (int i = threadIdx.x; i < NB * NE; i += W * 64) red[i] = 0;
-    if (p.x_dt == BL_BF16) prologue_regs<W, 8>(p, xr, gr, E, q_s, a_s, rd, rf);
-    else prologue_regs<W, 4>(p, xr, gr, E, q_s, a_s, rd, rf);
-    lds_barrier();
-
-    // 4. stream: consume step i from its slot, refill the slot with step i + kRing
-    v4i accv[NB][4];
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-#pragma unroll
-        for (int f = 0; f < 4; ++f) accv[t][f] = v4i{0, 0, 0, 0};
-    int qs = 0;
-    for (int i = 0; i < ks; ++i) {
-        const int slot = i % kRing;
-        const int st = wave + W * i;
-        const int kk = st * 64 + 16 * g;
-        const bool kok = kk < K;
-        // slots issued so far: the kRing prefill plus one refill per earlier
-        // iteration that had a step kRing ahead; all issued after step i may
-        // stay outstanding
-        const int issued = kRing + (i < ks - kRing ? i : (ks > kRing ? ks - kRing : 0));
-        wait_vm((issued - i - 1) * NB);
-        v4i bw[NB];
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            bw[t] = *reinterpret_cast<const v4i *>(ring + (slot * NB + t) * 1024 + 16 * lane);
-            if (!(kok && row_ok)) bw[t] = v4i{0, 0, 0, 0};
-        }
-        // refill the slot with step i + kRing when this wave has one
-        if (i + kRing < ks) {
-#pragma unroll
-            for (int t = 0; t < NB; ++t) dma16(src_of(t, i + kRing), ring + (slot * NB + t) * 1024);
-        }
-        const v4i a_op = (kok && lr < M) ? *reinterpret_cast<const v4i *>(q_s + (size_t)lr * K + kk)
-                                         : v4i{0, 0, 0, 0};
-        qs += rowsum16(a_op);
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            v4i fb[4];
-            expand(bw[t], fb);
-#pragma unroll
-            for (int f = 0; f < 4; ++f) accv[t][f] = mfma16(a_op, fb[f], accv[t][f]);
-        }
-    }
-
-    // No weight load may still be writing LDS once the workgroup ends (its
-    // LDS can be handed to the next workgroup): drain the ring.
-    __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value);
-
-    // The first tile's workgroup hands out its activation codes and scales
-    // (stage outputs for checks), now that no weight load is in flight.
-    if (tile == 0 && p.dbg_q != nullptr) {
-        for (int i = threadIdx.x; i < M * K; i += W * 64) p.dbg_q[i] = q_s[i];
-        if (p.dbg_a != nullptr && (int)threadIdx.x < M) p.dbg_a[threadIdx.x] = a_s[threadIdx.x];
-    }
-
-    // 5. reduce across waves, rescale, store
-    qs += __shfl_xor(qs, 16, 64);
-    qs += __shfl_xor(qs, 32, 64);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int qsum = __shfl(qs, 4 * g + j, 64);
-        if (4 * g + j >= M) continue;
-#pragma unroll
-        for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int v = shift_field(accv[t][f][j], f) - qsum;
-                atomicAdd(&red[t * NE + (f * 4 + j) * 64 + lane], v);
+            for (int j = 0; j < kXRegs; ++j) {
+                const int c = j / (per / 4);
+                const int h = j - c * (per / 4);
+                const int k0 = (c * kQuantLanes + ql) * per + 4 * h;
+                gr[j] = ld16(p.gain + (c < E && k0 < K ? k0 : gspread));
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kXRegs; ++j) gr[j] = v4i{0x3F800000, 0x3F800000, 0x3F800000, 0x3F800000};
+        }
+        const int nscale = PAIR ? 2 : p.seg.n;
+        const float wmv = ql < nscale ? p.w_mean[ql] : 0.0f;
+        __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value);
+        if (ql < nscale) wm_s[ql] = wmv;
+        if (p.mode == 2) {
+            if (p.x_dt == BL_BF16)
+                quant_rows<8, true>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
+            else
+                quant_rows<4, true>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
+        } else {
+            if (p.x_dt == BL_BF16)
+                quant_rows<8, false>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
+            else
+                quant_rows<4, false>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
+        }
+    } else {
+        // ---------------- stream waves ----------------
+        const int lr = lane & 15;
+        const int g = lane >> 4;
+        const int nkr = Kp / kUnitK;
+        const int RW = 4 * CS < 16 ? 4 * CS : 16;   // rows per row group
+        const int UPK = RW / 4;                      // units per k-range
+        const int grp = (4 * CS / RW) * NB;          // stream waves per k-range
+        const int tsel = wave % NB;                  // tensor of this wave
+        const int rg = (wave / NB) % (4 * CS / RW);  // row group of this wave
+        const int kr0 = wave / grp;
+        const int kstep = SW / grp;
+        const int ks = kr0 < nkr ? (nkr - kr0 + kstep - 1) / kstep : 0;   // k-ranges of this wave
+        const int kb = kRing / UPK;                  // k-ranges per batch
+        unsigned char *ring = ring_lds + (size_t)wave * (kRing * 1024);
+        const int row0 = r0 + rg * RW;               // first packed row of the row group
+
+        // this lane's share of a unit load: row q of the unit, swizzled chunk
+        const int dq = lane >> 4;
+        const int dpc = lane & 15;
+        // this lane's MFMA column: row rr of the group, field slot fs
+        const int rr = lr % RW;
+        const int fs = lr / RW;
+        const int8_t *qrow = q_s + (size_t)(lr < M ? lr : 0) * Kp + 16 * g;
+        v4i acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = v4i{0, 0, 0, 0};
+
+        // Batches of kb k-ranges: issue every unit of the batch, wait for all
+        // of them, then consume.  (Waiting for the oldest load while later
+        // direct loads are still in flight, and reading LDS meanwhile, slows
+        // the whole stream down on this hardware.)
+        for (int b0 = 0; b0 < ks; b0 += kb) {
+            const int nb = ks - b0 < kb ? ks - b0 : kb;
+            for (int t = 0; t < nb * UPK; ++t) {
+                const int kr = kr0 + kstep * (b0 + t / UPK);
+                const int u = t % UPK;
+                const int row = row0 + 4 * u + dq;
+                const int lc = dpc ^ ((4 * u + dq) & 15);
+                const bool ok = row < p.R && kr * kUnitK + 16 * lc < K;
+                const uint8_t *src = ok ? p.P + (size_t)(tsel * p.R + row) * K + (size_t)kr * kUnitK + 16 * lc
+                                        : p.P + 16 * dpc;
+                dma16(src, ring + t * 1024);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value);
+            // the activation codes (once; the quantizer waves publish once per
+            // reduction -- the norm's sum of squares, the absmax -- and once when done)
+            if (b0 == 0) wait_published<4>(qflag, p.mode == 2 ? 3 : 2);
+            for (int t = 0; t < nb; ++t) {
+                const int kr = kr0 + kstep * (b0 + t);
+                const unsigned char *slot = ring + (t * UPK + (rr >> 2)) * 1024 + 256 * (rr & 3);
+                // all operand reads of the k-range first: one LDS round trip
+                v4i bw[4], av[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    bw[j] = *reinterpret_cast<const v4i *>(slot + 16 * ((4 * j + g) ^ rr));
+                    av[j] = lr < M ? *reinterpret_cast<const v4i *>(qrow + kr * kUnitK + 64 * j) : v4i{0, 0, 0, 0};
+                }
+                if (RW == 16) {
+                    // all four fields of every byte: masked in place they
+                    // are the codes + 1 times 1, 4, 16 and (after >> 2) 16,
+                    // a scale the reduction divides out exactly
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v4i f0, f1, f2, f3;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const uint32_t w = (uint32_t)bw[j][d];
+                            f0[d] = (int)(w & 0x03030303u);
+                            f1[d] = (int)(w & 0x0C0C0C0Cu);
+                            f2[d] = (int)(w & 0x30303030u);
+                            f3[d] = (int)((w >> 2) & 0x30303030u);
+                        }
+                        acc[0] = mfma16(av[j], f0, acc[0]);
+                        acc[1] = mfma16(av[j], f1, acc[1]);
+                        acc[2] = mfma16(av[j], f2, acc[2]);
+                        acc[3] = mfma16(av[j], f3, acc[3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            if (i >= UPK) break;
+                            const int fsh = 2 * (i * (16 / RW) + fs);
+                            v4i fb;
+#pragma unroll
+                            for (int d = 0; d < 4; ++d) fb[d] = (int)(((uint32_t)bw[j][d] >> fsh) & 0x03030303u);
+                            acc[i] = mfma16(av[j], fb, acc[i]);
+                        }
+                    }
+                }
+            }
+        }
+
+        // 4. column sums across the waves of a row group.  Lanes 0-15 hold
+        // rows 0-3 of each 16 x 16 result (row j in element j), column = lane.
+        if (lane < 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i >= UPK) break;
+                const int prow = rg * RW + rr;          // packed row within the tile
+                const int f = i * (16 / RW) + fs;       // field
+                // undo the field scale of the masked path (exact: every
+                // product carries the factor)
+                const int sh = RW == 16 ? (i == 0 ? 0 : (i == 1 ? 2 : 4)) : 0;
+#pragma unroll
+                for (int j = 0; j < kFuseMaxM; ++j)
+                    if (j < M) atomicAdd(&red[((tsel * kMaxTileRows + prow) * 4 + f) * kFuseMaxM + j], acc[i][j] >> sh);
+            }
+        }
     }
     lds_barrier();
-    for (int e = threadIdx.x; e < NE; e += W * 64) {
-        const int ln = e & 63;
-        const int j = (e >> 6) & 3;
-        const int f = (e >> 8) & 3;
-        const int m = 4 * (ln >> 4) + j;
-        const int vrr = r0 + (ln & 15);
-        if (m >= M || vrr >= p.R) continue;
-        emit_out(p.y, p.y_dt, p.ldy, PAIR, p.seg, p.R, wm_s, m, vrr, f, a_s[m], red[e],
-                 PAIR ? red[(NB - 1) * NE + e] : 0);
+
+    // 5. rescale and store (both roles)
+    for (int e = threadIdx.x; e < 4 * CS * 4 * M; e += kLdsWaves * 64) {
+        const int m = e % M;
+        const int f = (e / M) & 3;
+        const int prow = e / (4 * M);
+        const int vr = r0 + prow;
+        if (vr >= p.R) continue;
+        // the codes were taken as c + 1: subtract the row's code sum once
+        int qsum = 0;
+#pragma unroll
+        for (int w = 0; w < kQuantWaves; ++w) qsum += sq_s[m * kQuantWaves + w];
+        const int A = red[((0 * kMaxTileRows + prow) * 4 + f) * kFuseMaxM + m] - qsum;
+        const int U = PAIR ? red[((1 * kMaxTileRows + prow) * 4 + f) * kFuseMaxM + m] - qsum : 0;
+        emit_out(p.y, p.y_dt, p.ldy, PAIR, p.seg, p.R, wm_s, m, vr, f, a_s[m], A, U);
+    }
+    // The first tile's workgroup hands out its activation codes and scales
+    // (stage outputs for checks).
+    if (tile == 0 && p.dbg_q != nullptr) {
+        for (int i = threadIdx.x; i < M * K; i += kLdsWaves * 64) p.dbg_q[i] = q_s[(i / K) * Kp + i % K];
+        if (p.dbg_a != nullptr && (int)threadIdx.x < M) p.dbg_a[threadIdx.x] = a_s[threadIdx.x];
     }
 }
 
@@ -737,9 +920,31 @@ int max_ksmax(int mt, bool pair, bool fused) {
 
 // Streaming variant (fused path, every problem's rows in kXChunks register
 // chunks): problems ordered by decreasing K so the longest tiles start first.
+// Even share of the batch's weight bytes per workgroup at one workgroup per
+// CU.  The launcher gives each problem the largest number of column sets (4
+// packed rows each) of 8, 4, 2, 1 whose tile (NB tensors x 4*CS rows x K
+// bytes) stays within 1.25x this share, so every workgroup of the launch is
+// resident at once and none streams much longer than the others.
+size_t even_share(const GemvBatch &b, int nb, int cus) {
+    size_t total = 0;
+    for (int i = 0; i < b.n; ++i) total += (size_t)nb * b.p[i].R * b.p[i].K;
+    return total / (size_t)cus;
+}
+
 template <bool PAIR>
 hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
     constexpr int NB = PAIR ? 2 : 1;
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus = n;
+    }
+    const size_t share = even_share(b, NB, cus) * 5 / 4;
     GemvBatch o = b;
     int order[kMaxProblems];
     for (int i = 0; i < b.n; ++i) order[i] = i;
@@ -751,14 +956,18 @@ hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
         }
     int tiles = 0;
     for (int i = 0; i < b.n; ++i) {
-        o.p[i] = b.p[order[i]];
-        o.p[i].tile0 = tiles;
-        tiles += (o.p[i].R + 15) / 16;
+        GemvProblem &q = o.p[i];
+        q = b.p[order[i]];
+        int cs = kStreamWaves / NB;   // CS * NB must divide the stream waves
+        while (cs > 1 && (size_t)NB * 4 * cs * q.K > share) cs >>= 1;
+        q.cs = cs;
+        q.tile0 = tiles;
+        tiles += (q.R + 4 * cs - 1) / (4 * cs);
     }
     o.ring_off = 0;
-    const size_t lds = (size_t)kLdsWaves * kRing * NB * 1024;   // dynamic part: the weight ring
+    const size_t lds = (size_t)kStreamWaves * kRing * 1024;   // dynamic part: the weight ring
     // Dynamic LDS above the default 64 KiB must be allowed per kernel (the
-    // static part, at most ~17 KiB, comes on top; both fit the 160 KiB).
+    // static part, about 17 KiB, comes on top; both fit the 160 KiB).
     static size_t attr_bytes = 0;
     if (attr_bytes < lds) {
         hipError_t e = hipFuncSetAttribute((const void *)k_gemv_lds<PAIR>,
@@ -779,9 +988,12 @@ hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s) {
         for (int i = 0; i < b.n; ++i) {
             const GemvProblem &p = b.p[i];
             const int per = x_per_chunk(p.x_dt);
-            if (p.mode == 0 || p.M > kFuseMaxM || p.M * x_chunks(p.K, p.x_dt, kLdsWaves * 64) > kXChunks ||
-                (size_t)p.M * p.K > (size_t)kLdsQBytes || ((uintptr_t)p.gain % 16) != 0 ||
-                p.K % per != 0 || p.ldx % per != 0 || (p.pair != 0) != (b.p[0].pair != 0))
+            const int E = x_chunks(p.K, p.x_dt, kQuantLanes);
+            if (p.mode == 0 || p.M > kFuseMaxM || p.M * E > kXRegs ||
+                (p.mode == 2 && (p.M != 1 || E * per / 4 > kXRegs)) ||
+                (size_t)p.M * ((p.K + kUnitK - 1) / kUnitK * kUnitK) > (size_t)kLdsQBytes ||
+                ((uintptr_t)p.gain % 16) != 0 || p.K % 16 != 0 || p.K % per != 0 || p.ldx % per != 0 ||
+                (p.pair != 0) != (b.p[0].pair != 0))
                 ok = false;
         }
         if (ok) return b.p[0].pair ? launch_lds<true>(b, s) : launch_lds<false>(b, s);
