@@ -328,7 +328,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv(GemvBatch b) {
 }
 
 // ===========================================================================
-// Streaming variant for the fused path (M <= 4).  One 12-wave workgroup per
+// Streaming variant for the fused path (M <= 4).  One 16-wave workgroup per
 // CU, with two roles:
 //   * 8 stream waves move the packed weights into LDS with the gfx950 direct
 //     global->LDS loads (global_load_lds_dwordx4) and run the MFMAs.  Each
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv(GemvBatch b) {
 //     and only this wave reads the slot back, so consuming a slot needs only
 //     the wave's own s_waitcnt vmcnt, never a workgroup barrier.  They issue
 //     their first kRing loads at once, before anything else.
-//   * 4 quantizer waves (one per SIMD) load the activation rows and quantize
+//   * 8 quantizer waves (two per SIMD) load the activation rows and quantize
 //     them into LDS.  They synchronise among themselves through LDS flags,
 //     not s_barrier: a stream wave is stalled in the issue of its weight
 //     loads for microseconds while the memory system is saturated, and a
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv(GemvBatch b) {
 // reduced, rescaled and stored.
 // ===========================================================================
 constexpr int kStreamWaves = 8;
-constexpr int kQuantWaves = 4;
+constexpr int kQuantWaves = 8;
 constexpr int kLdsWaves = kStreamWaves + kQuantWaves;
 constexpr int kQuantLanes = kQuantWaves * 64;
 constexpr int kRing = 12;            // 1 KB ring slots per stream wave
@@ -459,13 +459,16 @@ __device__ __forceinline__ void publish(int *qflag, int w, int step) {
 // waits on each other are short).
 template <int SLEEP>
 __device__ __forceinline__ void wait_published(const int *qflag, int step) {
-    static_assert(kQuantWaves == 4, "one 16-byte read covers the flags");
+    static_assert(kQuantWaves == 8, "two 16-byte reads cover the flags");
     for (int it = 0; it < kSpinMax; ++it) {
         asm volatile("" ::: "memory");
         const v4i f = *reinterpret_cast<const v4i *>(qflag);
-        const int lo = min(__builtin_amdgcn_readfirstlane(f[0]), __builtin_amdgcn_readfirstlane(f[1]));
-        const int hi = min(__builtin_amdgcn_readfirstlane(f[2]), __builtin_amdgcn_readfirstlane(f[3]));
-        if (min(lo, hi) >= step) break;
+        const v4i h = *reinterpret_cast<const v4i *>(qflag + 4);
+        int lo = step;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lo = min(lo, min(__builtin_amdgcn_readfirstlane(f[i]), __builtin_amdgcn_readfirstlane(h[i])));
+        if (lo >= step) break;
         __builtin_amdgcn_s_sleep(SLEEP);
     }
     asm volatile("" ::: "memory");
@@ -500,8 +503,22 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
                            int *qflag) {
     const int K = p.K;
     const int M = p.M;
-    auto elem0 = [&](int j) { return ((j % E) * kQuantLanes + ql) * PER; };
-    auto row_of = [&](int j) { return j / E; };
+    // row and chunk of each register (uniform; counted up once, no divisions)
+    int jrow[kXRegs], jchunk[kXRegs];
+    {
+        int m = 0, c = 0;
+#pragma unroll
+        for (int j = 0; j < kXRegs; ++j) {
+            jrow[j] = m;
+            jchunk[j] = c;
+            if (++c == E) {
+                c = 0;
+                ++m;
+            }
+        }
+    }
+    auto elem0 = [&](int j) { return (jchunk[j] * kQuantLanes + ql) * PER; };
+    auto row_of = [&](int j) { return jrow[j]; };
     // the norm of register j's chunk (NORM: M == 1, so chunk j, static)
     auto norm = [&](float *v, int j, float r) {
         const v4i g0 = gr[(j * (PER / 4)) % kXRegs];
@@ -698,13 +715,18 @@ void k_gemv_lds(GemvBatch b) {
         v4i xr[kXRegs];
         v4i gr[kXRegs];
         const size_t spread = ((size_t)ql * 16) % ((size_t)K * esz);
+        {
+            int m = 0, c = 0;   // row and chunk of register j (no divisions)
 #pragma unroll
-        for (int j = 0; j < kXRegs; ++j) {
-            const int m = j / E;
-            const int c = j - m * E;
-            const int k0 = (c * kQuantLanes + ql) * per;
-            const bool ok = j < M * E && k0 < K;
-            xr[j] = ld16((const unsigned char *)p.x + (ok ? ((size_t)m * p.ldx + k0) * esz : spread));
+            for (int j = 0; j < kXRegs; ++j) {
+                const int k0 = (c * kQuantLanes + ql) * per;
+                const bool ok = j < M * E && k0 < K;
+                xr[j] = ld16((const unsigned char *)p.x + (ok ? ((size_t)m * p.ldx + k0) * esz : spread));
+                if (++c == E) {
+                    c = 0;
+                    ++m;
+                }
+            }
         }
         // RMSNorm gains of this lane's chunks (shared by the rows): register
         // c*per/4 + h holds gain[k0(c) + 4h .. +3]; all ones without gains
@@ -742,15 +764,19 @@ void k_gemv_lds(GemvBatch b) {
         const int lr = lane & 15;
         const int g = lane >> 4;
         const int nkr = Kp / kUnitK;
-        const int RW = 4 * CS < 16 ? 4 * CS : 16;   // rows per row group
-        const int UPK = RW / 4;                      // units per k-range
-        const int grp = (4 * CS / RW) * NB;          // stream waves per k-range
-        const int tsel = wave % NB;                  // tensor of this wave
-        const int rg = (wave / NB) % (4 * CS / RW);  // row group of this wave
-        const int kr0 = wave / grp;
-        const int kstep = SW / grp;
-        const int ks = kr0 < nkr ? (nkr - kr0 + kstep - 1) / kstep : 0;   // k-ranges of this wave
-        const int kb = kRing / UPK;                  // k-ranges per batch
+        // every count here is a power of two: shifts and masks, no divisions
+        const int lcs = CS >= 8 ? 3 : (CS >= 4 ? 2 : (CS >= 2 ? 1 : 0));   // log2 CS
+        const int lrw = lcs + 2 < 4 ? lcs + 2 : 4;   // log2 of the rows per row group
+        const int RW = 1 << lrw;
+        const int lupk = lrw - 2;                    // log2 of the units per k-range
+        const int UPK = 1 << lupk;
+        const int lgrp = (lcs + 2 - lrw) + (NB == 2 ? 1 : 0);   // log2 of the stream waves per k-range
+        const int tsel = wave & (NB - 1);            // tensor of this wave
+        const int rg = (wave >> (NB == 2 ? 1 : 0)) & ((1 << (lcs + 2 - lrw)) - 1);   // row group of this wave
+        const int kr0 = wave >> lgrp;
+        const int kstep = SW >> lgrp;
+        const int ks = kr0 < nkr ? ((nkr - kr0 + kstep - 1) >> (3 - lgrp)) : 0;   // k-ranges of this wave
+        const int kb = kRing >> lupk;                // k-ranges per batch (kRing is a multiple of 4)
         unsigned char *ring = ring_lds + (size_t)wave * (kRing * 1024);
         const int row0 = r0 + rg * RW;               // first packed row of the row group
 
@@ -758,8 +784,8 @@ void k_gemv_lds(GemvBatch b) {
         const int dq = lane >> 4;
         const int dpc = lane & 15;
         // this lane's MFMA column: row rr of the group, field slot fs
-        const int rr = lr % RW;
-        const int fs = lr / RW;
+        const int rr = lr & (RW - 1);
+        const int fs = lr >> lrw;
         const int8_t *qrow = q_s + (size_t)(lr < M ? lr : 0) * Kp + 16 * g;
         v4i acc[4];
 #pragma unroll
@@ -772,8 +798,8 @@ void k_gemv_lds(GemvBatch b) {
         for (int b0 = 0; b0 < ks; b0 += kb) {
             const int nb = ks - b0 < kb ? ks - b0 : kb;
             for (int t = 0; t < nb * UPK; ++t) {
-                const int kr = kr0 + kstep * (b0 + t / UPK);
-                const int u = t % UPK;
+                const int kr = kr0 + kstep * (b0 + (t >> lupk));
+                const int u = t & (UPK - 1);
                 const int row = row0 + 4 * u + dq;
                 const int lc = dpc ^ ((4 * u + dq) & 15);
                 const bool ok = row < p.R && kr * kUnitK + 16 * lc < K;
@@ -851,13 +877,13 @@ void k_gemv_lds(GemvBatch b) {
     }
     lds_barrier();
 
-    // 5. rescale and store (both roles)
-    for (int e = threadIdx.x; e < 4 * CS * 4 * M; e += kLdsWaves * 64) {
-        const int m = e % M;
-        const int f = (e / M) & 3;
-        const int prow = e / (4 * M);
+    // 5. rescale and store (both roles): e = (packed row, field, row of x)
+    for (int e = threadIdx.x; e < 4 * CS * 4 * kFuseMaxM; e += kLdsWaves * 64) {
+        const int m = e & (kFuseMaxM - 1);
+        const int f = (e >> 2) & 3;
+        const int prow = e >> 4;
         const int vr = r0 + prow;
-        if (vr >= p.R) continue;
+        if (m >= M || vr >= p.R) continue;
         // the codes were taken as c + 1: subtract the row's code sum once
         int qsum = 0;
 #pragma unroll
