@@ -102,6 +102,30 @@ def capture(torch, fn):
     return g
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_lds_decode_config2_traffic.md")
+TRAFFIC_SOURCES = ("bit_ternary_weight_amd/csrc/k_gemv.hip", "bit_ternary_weight_amd/csrc/bl_common.h")
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the headline kernel from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when the kernel sources have
+    changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    h = re.search(r"^source_sha256: ([0-9a-f]+)$", text, re.M)
+    if not t or not h:
+        return None
+    d = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        d.update(open(os.path.join(ROOT, f), "rb").read())
+    return int(t.group(1)) if d.hexdigest() == h.group(1) else None
+
+
 def cpu_baseline(seconds: float = 12.0):
     """The oracle as it stands, single thread, M=1 layers on two distinct layers' codes."""
     import numpy as np
@@ -210,10 +234,12 @@ def main():
     # The headline kernel is the only launch of a step: its average launch
     # duration over the timed region is the step time (back-to-back launches
     # from a graph), so the roofline uses the same bytes and time.
+    traffic = profiled_traffic()
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gemv<16,1,8,false,true> (batched decode GEMV, fused per-token quantization)",
-                "bytes_per_launch": sb, "avg_launch_us": round(ms * 1e3, 3)}
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_gemv_lds<false> (batched decode GEMV, fused per-token quantization)",
+                "bytes_per_launch": sb, "avg_launch_us": round(ms * 1e3, 3),
+                "traffic_over_algorithmic": None if traffic is None else round(traffic / sb, 4)}
     if args.kernel_only:
         print(json.dumps({"roofline": roofline}), flush=True)
         return
