@@ -129,6 +129,29 @@ def workspace(device, nbytes: int) -> torch.Tensor:
         return buf
 
 
+def _need(t, shape, dtypes, name, contiguous=True):
+    """Host-side check of a tensor handed to the library: the C ABI takes bare
+    pointers, so a buffer of the wrong size would be read or written out of
+    bounds on the device instead of failing here."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_OUT_DT = (torch.float32, torch.bfloat16, torch.int32)
+
+
+def _check_weight(packed, w_mean, N4, K, n_seg, name="packed"):
+    _need(packed, (N4, K), (torch.uint8,), name)
+    if w_mean.dtype != torch.float32 or w_mean.numel() < n_seg:
+        raise ValueError(f"w_mean must be float32 with at least {n_seg} elements")
+
+
 def _segs(seg_n, N):
     if seg_n is None:
         return 1, None
@@ -143,10 +166,13 @@ def ternarize_pack(W: torch.Tensor, packed: torch.Tensor = None, w_mean: torch.T
     """W fp32 [N,K] -> (packed uint8 [N/4,K], w_mean fp32 [1])."""
     dev = _dev(W)
     N, K = W.shape
+    _need(W, (N, K), (torch.float32,), "W")
     if packed is None:
         packed = torch.empty((N // 4, K), dtype=torch.uint8, device=dev)
     if w_mean is None:
         w_mean = torch.empty(1, dtype=torch.float32, device=dev)
+    _need(packed, (N // 4, K), (torch.uint8,), "packed")
+    _need(w_mean, (1,), (torch.float32,), "w_mean")
     nbytes = raw.bl_ternarize_workspace_bytes(N, K)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     _check(raw.bl_ternarize_pack(_ptr(W), N, K, _ptr(packed), _ptr(w_mean), _ptr(ws), ws.numel(), _stream(dev)))
@@ -163,6 +189,8 @@ def quant_act(x: torch.Tensor, q: torch.Tensor = None, a: torch.Tensor = None):
         q = torch.empty((M, K), dtype=torch.int8, device=dev)
     if a is None:
         a = torch.empty(M, dtype=torch.float32, device=dev)
+    _need(q, (M, K), (torch.int8,), "q")
+    _need(a, (M,), (torch.float32,), "a")
     _check(raw.bl_quant_act(_ptr(x), _dt(x), M, K, x.stride(0), _ptr(q), _ptr(a), _stream(dev)))
     return q, a
 
@@ -174,8 +202,12 @@ def _contract(fn_name, ws_query, x, packed, w_mean, seg_n=None, y_dtype=torch.fl
         raise ValueError("x rows must be contiguous")
     N = packed.shape[0] * 4
     n_seg, seg = _segs(seg_n, N)
+    _check_weight(packed, w_mean, N // 4, K, n_seg)
+    if a is not None and (a.dtype != torch.float32 or a.numel() < M):
+        raise ValueError("a must be float32 with at least M elements")
     if y is None:
         y = torch.empty((M, N), dtype=y_dtype, device=dev)
+    _need(y, (M, N), _OUT_DT, "y")
     nbytes = ws_query(M, N, K)
     ws = workspace(dev, nbytes)
     fn = getattr(raw, fn_name)
@@ -211,8 +243,12 @@ def gemv_w2a8_batched(problems):
         if y is None:
             y = torch.empty((M, N), dtype=pr.get("y_dtype", torch.float32), device=dev)
         n_seg, seg = _segs(pr.get("seg_n"), N)
+        _check_weight(packed, w_mean, N // 4, K, n_seg)
+        _need(y, (M, N), _OUT_DT, "y")
         keep.append(seg)
         a = pr.get("a")
+        if a is not None and (a.dtype != torch.float32 or a.numel() < M):
+            raise ValueError("a must be float32 with at least M elements")
         arr[i] = GemvProblem(x.data_ptr(), _dt(x), x.stride(0), a.data_ptr() if a is not None else None, M, K,
                              packed.data_ptr(), N, n_seg, seg, w_mean.data_ptr(), y.data_ptr(), _dt(y))
         outs.append(y)
@@ -232,8 +268,16 @@ def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g
     dev = _dev(h, packed_gu, packed_down)
     M, H = h.shape
     I = packed_gu.shape[0] * 2
+    if h.stride(1) != 1 or h.stride(0) != H:
+        raise ValueError("h must be contiguous")
+    _check_weight(packed_gu, w_mean_gu, I // 2, H, 2, "packed_gu")
+    _check_weight(packed_down, w_mean_down, H // 4, I, 1, "packed_down")
+    for g, n, name in ((g_subln, H, "g_subln"), (g_ffn, I, "g_ffn")):
+        if g is not None:
+            _need(g, (n,), (torch.float32,), name)
     if y is None:
         y = torch.empty((M, H), dtype=y_dtype, device=dev)
+    _need(y, (M, H), (torch.float32, torch.bfloat16), "y")
     stages = None
     dbg = None
     if debug:

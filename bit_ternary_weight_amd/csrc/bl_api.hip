@@ -47,7 +47,7 @@ bool fusable(int M, int K) {
 }
 
 struct ChainScratch {
-    size_t q1, a1, p, q2, a2, end;
+    size_t q1, a1, p, q2, a2, qs, end;
 };
 
 ChainScratch chain_scratch(int M, int H, int I) {
@@ -57,7 +57,8 @@ ChainScratch chain_scratch(int M, int H, int I) {
     s.p = s.a1 + align256((size_t)M * sizeof(float));
     s.q2 = s.p + align256((size_t)M * I * sizeof(float));
     s.a2 = s.q2 + align256((size_t)M * I);
-    s.end = s.a2 + align256((size_t)M * sizeof(float));
+    s.qs = s.a2 + align256((size_t)M * sizeof(float));   // code sums, reused by both contractions
+    s.end = s.qs + align256((size_t)M * sizeof(int));
     return s;
 }
 
@@ -156,7 +157,11 @@ size_t decode_scratch(int n, const Call *calls) {
     return need;
 }
 
-size_t prefill_scratch(const Call &c) { return c.x_dt == BL_I8 ? 0 : quant_scratch(c.M, c.K); }
+// Prefill scratch: the codes and scales when x is not int8, then the rows'
+// code sums (M ints) that the large-tile GEMM reads.
+size_t prefill_scratch(const Call &c) {
+    return (c.x_dt == BL_I8 ? 0 : quant_scratch(c.M, c.K)) + align256((size_t)c.M * sizeof(int));
+}
 
 bl::Contract contract_of(const Call &c, const int8_t *q, int ldq, const float *a) {
     bl::Contract k;
@@ -334,7 +339,11 @@ size_t bl_gemv_workspace_bytes(int M, int N, int K) {
     return quant_scratch(M, K);
 }
 
-size_t bl_gemm_workspace_bytes(int M, int N, int K) { return bl_gemv_workspace_bytes(M, N, K); }
+size_t bl_gemm_workspace_bytes(int M, int N, int K) {
+    (void)N;
+    if (M < 1 || K < 1) return 0;
+    return quant_scratch(M, K) + align256((size_t)M * sizeof(int));
+}
 
 int bl_gemv_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const uint8_t *packed, int N,
                  int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype, void *ws, size_t ws_bytes,
@@ -390,7 +399,8 @@ int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int
         aq = aw;
     }
     const bl::Contract k = contract_of(c, q, ldq, aq);
-    return check_hip((is_fast(c) && ldq % 16 == 0) ? bl::launch_gemm(k, s) : bl::launch_generic(k, s), fn);
+    int *qsum = (int *)((char *)ws + (c.x_dt == BL_I8 ? 0 : quant_scratch(c.M, c.K)));
+    return check_hip((is_fast(c) && ldq % 16 == 0) ? bl::launch_gemm(k, qsum, s) : bl::launch_generic(k, s), fn);
 }
 
 size_t bl_ffn_chain_workspace_bytes(int M, int H, int I) {
@@ -478,7 +488,7 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
         g.P = packed_gu; g.seg = seg_i; g.w_mean = w_mean_gu; g.y = p; g.y_dt = BL_F32; g.ldy = I; g.pair = 1;
         e = bl::launch_gemv_batch(b, s);
     } else {
-        e = bl::launch_gemm(c, s);
+        e = bl::launch_gemm(c, (int *)(wsb + sc.qs), s);
     }
     if (int st = check_hip(e, "gate|up launch")) return st;
     // 3. ffn_sub_norm RMSNorm + quantize
@@ -498,7 +508,7 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
         d.P = packed_down; d.seg = seg_h; d.w_mean = w_mean_down; d.y = y; d.y_dt = y_dtype; d.ldy = H; d.pair = 0;
         e = bl::launch_gemv_batch(b, s);
     } else {
-        e = bl::launch_gemm(c, s);
+        e = bl::launch_gemm(c, (int *)(wsb + sc.qs), s);
     }
     return check_hip(e, "down launch");
 }

@@ -24,14 +24,18 @@ struct ColOf {
     int col;
 };
 
+// Static indices only (selects): a run-time index into the table would make
+// the compiler copy a kernel argument into scratch memory.
 __device__ __forceinline__ ColOf col_of(const SegTab &t, int rr, int f) {
-    int s = 0;
+    int s = 0, r0 = t.roff[0], r1 = t.roff[1];
 #pragma unroll
     for (int i = 1; i < BL_MAX_SEGMENTS; ++i)
-        if (i < t.n && rr >= t.roff[i]) s = i;
-    int r0 = t.roff[s];
-    int Rs = t.roff[s + 1] - r0;
-    return ColOf{s, 4 * r0 + f * Rs + (rr - r0)};
+        if (i < t.n && rr >= t.roff[i]) {
+            s = i;
+            r0 = t.roff[i];
+            r1 = t.roff[i + 1];
+        }
+    return ColOf{s, 4 * r0 + f * (r1 - r0) + (rr - r0)};
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -183,6 +187,7 @@ struct Contract {
     int y_dt;
     int ldy;
     bool pair;        // gate|up with ReLU^2(gate)*up epilogue; up rows at P + R*K
+    const int *qsum = nullptr;   // [M] code sums of the rows of q (filled by launch_gemm)
 };
 
 // Decode path (M <= 64): one launch covers up to kMaxProblems independent
@@ -217,7 +222,10 @@ struct GemvBatch {
 // Fills tile0 of every problem and launches; all problems must share `pair`.
 hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s);
 // Prefill path (any M).
-hipError_t launch_gemm(const Contract &c, hipStream_t s);
+// Prefill GEMM.  qsum_ws: device scratch for M ints (the rows' code sums,
+// which the large-tile kernel reads instead of recomputing them per tile);
+// without it the small-tile kernel runs.
+hipError_t launch_gemm(const Contract &c, int *qsum_ws, hipStream_t s);
 // Any K (slow, simple): used when K is not a multiple of 16.
 hipError_t launch_generic(const Contract &c, hipStream_t s);
 

@@ -157,6 +157,292 @@ __global__ __launch_bounds__(256) void k_gemm(Contract c, int ntm) {
 }
 
 // ===========================================================================
+// Code sums: s[m] = sum_k q[m,k], one workgroup per row (K a multiple of 16).
+// The contraction takes codes + 1 from the packed fields and subtracts this
+// sum once per output.
+// ===========================================================================
+__global__ __launch_bounds__(256) void k_code_sums(const int8_t *q, int ldq, int M, int K, int *out) {
+    __shared__ int part[4];
+    const int m = blockIdx.x;
+    const int8_t *row = q + (size_t)m * ldq;
+    int acc = 0;
+    for (int k = threadIdx.x * 16; k < K; k += 256 * 16) acc += rowsum16(ld16(row + k));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) out[m] = part[0] + part[1] + part[2] + part[3];
+}
+
+// ===========================================================================
+// Prefill kernel, large tiles (K a multiple of 256).
+// Workgroup: 4 waves in a 2 x 2 grid over a TM-token x TR-packed-row tile
+// (PAIR: TR/2 gate rows and the same TR/2 up rows).  Wave (wm, wn) owns TM/2
+// tokens (NA = TM/32 MFMA row tiles) and NBW 16-row B fragments; each packed
+// fragment is unpacked in registers into its four fields, so one fragment
+// feeds 4 * NA MFMAs (v_mfma_i32_16x16x64_i8) per 64-k step.
+// K advances in stages of 256 bytes per row, brought into a 3-stage LDS ring
+// with direct global->LDS loads (one 1 KB load = 4 rows x 256 bytes, whole
+// cache lines).  One workgroup barrier per stage: every wave waits for its own
+// loads of stage s, the barrier then publishes stage s and also certifies that
+// every wave is done with stage s-1, whose slot the loads of stage s+2 reuse.
+// Within a stage the operands of the next 64-k step are read from LDS while
+// the MFMAs of the current one run.  In LDS the 16-byte chunk c of tile row r
+// sits at position c ^ (r & 15), so a fragment read (16 rows, one chunk)
+// touches 16 distinct bank groups.
+// ===========================================================================
+constexpr int kGK = 128;     // k bytes per stage
+constexpr int kGStages = 3;
+
+template <bool PAIR, int TM, int NBW>
+struct GemmShape {
+    static constexpr int NA = TM / 32;               // 16-token tiles per wave
+    static constexpr int BR = 32 * NBW;              // packed rows staged per stage
+    static constexpr int A_BYTES = TM * kGK;
+    static constexpr int B_BYTES = BR * kGK;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int DPA = TM * kGK / 4096;      // 1 KB loads of A per wave per stage
+    static constexpr int DPB = BR * kGK / 4096;
+    static constexpr int DPW = DPA + DPB;            // 1 KB loads per wave per stage
+    static constexpr int ROWS = PAIR ? BR / 2 : BR;  // packed rows of the output tile
+    static_assert(!PAIR || NBW == 2, "a gate|up tile holds one gate and one up fragment per wave");
+    static_assert(kGStages * DPW < 64, "vmcnt holds at most 63 loads");
+};
+
+template <int VM>
+__device__ __forceinline__ void g_wait_vm() {
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | (0x7 << 4) | (0xF << 8) | ((VM >> 4) << 14));
+}
+
+// Direct global->LDS load of 16 bytes per lane (lane l lands at lds + 16 l).
+// (Target builtins stay inside device functions: used directly in a kernel
+// template's body they would keep the host side from emitting its stub.)
+__device__ __forceinline__ void g_dma16(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void g_lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <bool PAIR, int TM, int NBW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gemm_big(Contract c, int ntm) {
+    using S = GemmShape<PAIR, TM, NBW>;
+    constexpr int NA = S::NA;
+    // a static LDS object first: the dynamic ring must not start at address 0
+    __shared__ int qs_s[4];
+    extern __shared__ __attribute__((aligned(16))) unsigned char g_lds[];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int lr = lane & 15;
+    const int g = lane >> 4;
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    const int bm = blockIdx.x % ntm;
+    const int bn = blockIdx.x / ntm;
+    const int m0 = bm * TM;
+    const int r0 = bn * S::ROWS;
+    const int K = c.K;
+    const int nst = K / kGK;
+    if (tid < 4) qs_s[tid] = 0;
+    // Swizzle of a tile row: the 16-byte chunk c of row r sits at position
+    // c ^ swz(r).  With 256-byte rows a row spans all 64 banks, so the 16 rows
+    // of a fragment need 16 distinct positions (r & 15); with 128-byte rows
+    // two rows share the banks, so rows r and r + 1 need the same positions
+    // offset by half a row: ((r >> 1) & 7).
+    auto swz = [](int r) { return kGK == 256 ? (r & 15) : ((r >> 1) & 7); };
+
+    // this lane's part of every 1 KB load: row L / CPR of the 1024 / kGK, chunk slot L % CPR
+    constexpr int CPR = kGK / 16;                             // 16-byte chunks per row
+    constexpr int RPL = 1024 / kGK;                           // rows per 1 KB load
+    const int lrow = lane / CPR;
+    const int lpos = lane % CPR;
+    const int8_t *a_src[S::DPA];
+#pragma unroll
+    for (int i = 0; i < S::DPA; ++i) {
+        const int row = (wave * S::DPA + i) * RPL + lrow;    // tile row 0 .. TM-1
+        const int ch = lpos ^ swz(row);
+        const int m = m0 + row < c.M ? m0 + row : 0;         // rows past M compute garbage never stored
+        a_src[i] = c.q + (size_t)m * c.ldq + 16 * ch;
+    }
+    const uint8_t *b_src[S::DPB];
+#pragma unroll
+    for (int i = 0; i < S::DPB; ++i) {
+        const int row = (wave * S::DPB + i) * RPL + lrow;    // B stage row 0 .. BR-1
+        const int ch = lpos ^ swz(row);
+        const int trow = PAIR ? (row < S::BR / 2 ? row : row - S::BR / 2) : row;   // row within its tensor's tile
+        const int prow = (PAIR && row >= S::BR / 2 ? c.R : 0) + r0 + trow;
+        const bool ok = r0 + trow < c.R;
+        b_src[i] = c.P + (size_t)(ok ? prow : 0) * K + 16 * ch;
+    }
+    auto issue = [&](int st) {
+        unsigned char *base = g_lds + (st % kGStages) * S::STAGE;
+        const size_t k0 = (size_t)st * kGK;
+#pragma unroll
+        for (int i = 0; i < S::DPA; ++i) g_dma16(a_src[i] + k0, base + (wave * S::DPA + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < S::DPB; ++i) g_dma16(b_src[i] + k0, base + S::A_BYTES + (wave * S::DPB + i) * 1024);
+    };
+
+    v4i acc[NA][NBW][4];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[i][b][f] = v4i{0, 0, 0, 0};
+    // LDS byte offsets of this lane's fragment rows (chunk 0 excluded)
+    int aoff[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) aoff[i] = (wm * (TM / 2) + i * 16 + lr) * kGK;
+    int boff[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+        boff[b] = S::A_BYTES + (PAIR ? (b == 0 ? wn * 16 + lr : S::BR / 2 + wn * 16 + lr) : (wn * NBW + b) * 16 + lr) * kGK;
+    // the swizzled position of chunk ch for this lane's rows: rows of a fragment
+    // are 16 consecutive tile rows starting at a multiple of 16, so their
+    // swizzle is swz(lr)
+    const int lsw = swz(lr);
+    auto chunk = [&](int ch) { return 16 * (ch ^ lsw); };
+
+    g_lds_barrier();   // qs_s initialised; no LDS load below can race it
+    issue(0);
+    if (nst > 1) issue(1);
+    v4i af[NA], bw[NBW];
+    for (int st = 0; st < nst; ++st) {
+        // this wave's loads of stage st are done once at most those of stage
+        // st + 1 are outstanding
+        if (st + 1 < nst) g_wait_vm<S::DPW>();
+        else g_wait_vm<0>();
+        g_lds_barrier();
+        if (st + 2 < nst) issue(st + 2);
+        const unsigned char *base = g_lds + (st % kGStages) * S::STAGE;
+        // operands of k-step 0
+#pragma unroll
+        for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const v4i *>(base + aoff[i] + chunk(g));
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) bw[b] = *reinterpret_cast<const v4i *>(base + boff[b] + chunk(g));
+#pragma unroll
+        for (int ks = 0; ks < kGK / 64; ++ks) {
+            v4i an[NA], bn[NBW];
+            if (ks + 1 < kGK / 64) {
+                const int ch = 4 * (ks + 1) + g;
+#pragma unroll
+                for (int i = 0; i < NA; ++i) an[i] = *reinterpret_cast<const v4i *>(base + aoff[i] + chunk(ch));
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) bn[b] = *reinterpret_cast<const v4i *>(base + boff[b] + chunk(ch));
+            }
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                // the four fields, masked in place: codes + 1 times 1, 4, 16, 16
+                v4i f0, f1, f2, f3;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t w = (uint32_t)bw[b][d];
+                    f0[d] = (int)(w & 0x03030303u);
+                    f1[d] = (int)(w & 0x0C0C0C0Cu);
+                    f2[d] = (int)(w & 0x30303030u);
+                    f3[d] = (int)((w >> 2) & 0x30303030u);
+                }
+#pragma unroll
+                for (int i = 0; i < NA; ++i) {
+                    acc[i][b][0] = mfma16(af[i], f0, acc[i][b][0]);
+                    acc[i][b][1] = mfma16(af[i], f1, acc[i][b][1]);
+                    acc[i][b][2] = mfma16(af[i], f2, acc[i][b][2]);
+                    acc[i][b][3] = mfma16(af[i], f3, acc[i][b][3]);
+                }
+            }
+            if (ks + 1 < kGK / 64) {
+#pragma unroll
+                for (int i = 0; i < NA; ++i) af[i] = an[i];
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) bw[b] = bn[b];
+            }
+        }
+    }
+
+    // Epilogue.  A lane's packed rows -- hence its output columns, segments
+    // and weight scales -- do not depend on the token row, so they are looked
+    // up once; the factor w_mean / a is formed once per token row (IEEE fp32
+    // division, as the oracle), and each accumulator then costs a shift, a
+    // subtraction, a conversion and a multiply: float(A) * (w_mean / a).
+    int colb[NBW][4];
+    float wmb[NBW];
+    bool okb[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+        const int vr = r0 + (PAIR ? wn * 16 : (wn * NBW + b) * 16) + lr;
+        okb[b] = vr < c.R;
+        const int vrc = okb[b] ? vr : 0;
+        if (PAIR) {
+            // gate (b = 0) and up (b = 1) share the row; p goes to column f*R + vr
+#pragma unroll
+            for (int f = 0; f < 4; ++f) colb[b][f] = f * c.R + vrc;
+            wmb[b] = c.w_mean[b];
+        } else {
+            int sg = 0;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const ColOf co = col_of(c.seg, vrc, f);
+                colb[b][f] = co.col;
+                sg = co.seg;
+            }
+            wmb[b] = c.w_mean[sg];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        // the code sums of this lane's four token rows (computed once per row
+        // by k_code_sums, not per tile)
+        int qsr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
+            qsr[j] = m < c.M ? c.qsum[m] : 0;
+        }
+        // undo the unpack's field scale, subtract the rows' code sums
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int sh = f == 0 ? 0 : (f == 1 ? 2 : 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][b][f][j] = (acc[i][b][f][j] >> sh) - qsr[j];
+            }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
+            if (m >= c.M) continue;
+            const float am = c.a[m];
+            const size_t rowo = (size_t)m * c.ldy;
+            if (PAIR) {
+                if (!okb[0]) continue;
+                const float s0 = wmb[0] / am;
+                const float s1 = wmb[1] / am;
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const float pv = relu2_mul((float)acc[i][0][f][j] * s0, (float)acc[i][1][f][j] * s1);
+                    if (c.y_dt == BL_BF16) ((uint16_t *)c.y)[rowo + colb[0][f]] = f32_to_bf16(pv);
+                    else ((float *)c.y)[rowo + colb[0][f]] = pv;
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) {
+                    if (!okb[b]) continue;
+                    const float sc = wmb[b] / am;
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) store_out(c.y, c.y_dt, rowo + colb[b][f], acc[i][b][f][j], sc);
+                }
+            }
+        }
+    }
+}
+
+// ===========================================================================
 // Generic kernel: one lane per (token row, packed row), byte loads, any K.
 // ===========================================================================
 __global__ __launch_bounds__(256) void k_generic(Contract c) {
@@ -186,7 +472,43 @@ __global__ __launch_bounds__(256) void k_generic(Contract c) {
 
 } // namespace
 
-hipError_t launch_gemm(const Contract &c, hipStream_t s) {
+template <bool PAIR, int TM, int NBW>
+hipError_t go_big(const Contract &c, hipStream_t s) {
+    using S = GemmShape<PAIR, TM, NBW>;
+    const int ntm = (c.M + TM - 1) / TM;
+    const int ntn = (c.R + S::ROWS - 1) / S::ROWS;
+    const size_t lds = (size_t)kGStages * S::STAGE;
+    static bool attr = false;   // the dynamic LDS above 64 KiB must be allowed once
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_gemm_big<PAIR, TM, NBW>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e;
+        }
+        attr = true;
+    }
+    hipLaunchKernelGGL((k_gemm_big<PAIR, TM, NBW>), dim3(ntm * ntn), dim3(256), lds, s, c, ntm);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const Contract &c0, int *qsum_ws, hipStream_t s) {
+    Contract c = c0;
+    // Large tiles when K fits whole 128-byte stages and the grid still fills
+    // the chip; the field scale of the masked unpack (x16) must not overflow.
+    // (A 256-token tile needs 256 accumulator registers per lane, which the
+    // compiler does not keep in the accumulator file: it copies them around
+    // every MFMA.  128-token tiles keep all 128 in place.)
+    if (qsum_ws != nullptr && c.K % kGK == 0 && c.ldq % 16 == 0 && c.K <= (1 << 18)) {
+        hipLaunchKernelGGL(k_code_sums, dim3(c.M), dim3(256), 0, s, c.q, c.ldq, c.M, c.K, qsum_ws);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        c.qsum = qsum_ws;
+        const int cus = 256;
+        if (c.pair) return go_big<true, 128, 2>(c, s);
+        const int mid = ((c.M + 127) / 128) * ((c.R + 63) / 64);
+        if (mid >= cus) return go_big<false, 128, 2>(c, s);
+        return go_big<false, 128, 1>(c, s);
+    }
     const int ntm = (c.M + kBM - 1) / kBM;
     const int ntn = (c.R + kVR - 1) / kVR;
     if (c.pair)
