@@ -223,6 +223,7 @@ int run_decode(const char *fn, int n, const Call *calls, char *ws, hipStream_t s
             float *aw = (float *)(ws + off + align256((size_t)c.M * c.K));
             off += quant_scratch(c.M, c.K);
             bl::QuantProblem &qp = qb.p[qb.n++];
+            qp = bl::QuantProblem{};
             qp.x = c.x; qp.q = qw; qp.a = aw; qp.x_dt = c.x_dt; qp.M = c.M; qp.K = c.K; qp.ldx = c.ldx;
             qv[i] = qw;
             av[i] = aw;
@@ -330,7 +331,7 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx, int8_t *q, f
     if (ldx < K) return fail(BL_ERR_SHAPE, "bl_quant_act: ldx=%d < K=%d", ldx, K);
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(a, 4))
         return fail(BL_ERR_ALIGN, "bl_quant_act: misaligned pointer");
-    return check_hip(bl::launch_quant_act(x, x_dtype, M, K, ldx, q, a, (hipStream_t)stream), "bl_quant_act");
+    return check_hip(bl::launch_quant_act(x, x_dtype, M, K, ldx, q, a, nullptr, (hipStream_t)stream), "bl_quant_act");
 }
 
 size_t bl_gemv_workspace_bytes(int M, int N, int K) {
@@ -390,17 +391,24 @@ int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int
     const int8_t *q = (const int8_t *)c.x;
     int ldq = c.ldx;
     const float *aq = c.a;
+    int *qsum = (int *)((char *)ws + (c.x_dt == BL_I8 ? 0 : quant_scratch(c.M, c.K)));
+    const bool fast = is_fast(c);
     if (c.x_dt != BL_I8) {
         int8_t *qw = (int8_t *)ws;
         float *aw = (float *)((char *)ws + align256((size_t)c.M * c.K));
-        if (int st = check_hip(bl::launch_quant_act(c.x, c.x_dt, c.M, c.K, c.ldx, qw, aw, s), fn)) return st;
+        if (int st = check_hip(bl::launch_quant_act(c.x, c.x_dt, c.M, c.K, c.ldx, qw, aw, fast ? qsum : nullptr, s), fn))
+            return st;
         q = qw;
         ldq = c.K;
         aq = aw;
     }
-    const bl::Contract k = contract_of(c, q, ldq, aq);
-    int *qsum = (int *)((char *)ws + (c.x_dt == BL_I8 ? 0 : quant_scratch(c.M, c.K)));
-    return check_hip((is_fast(c) && ldq % 16 == 0) ? bl::launch_gemm(k, qsum, s) : bl::launch_generic(k, s), fn);
+    bl::Contract k = contract_of(c, q, ldq, aq);
+    if (fast && ldq % 16 == 0) {
+        // codes quantized here come with their row sums
+        if (c.x_dt != BL_I8) k.qsum = qsum;
+        return check_hip(bl::launch_gemm(k, qsum, s), fn);
+    }
+    return check_hip(bl::launch_generic(k, s), fn);
 }
 
 size_t bl_ffn_chain_workspace_bytes(int M, int H, int I) {
@@ -470,7 +478,9 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
     }
 
     // 1. subln RMSNorm + quantize
-    if (int st = check_hip(bl::launch_rmsnorm_quant(h, h_dtype, M, H, g_subln, eps, q1, a1, s), "subln launch"))
+    int *qs = (int *)(wsb + sc.qs);
+    if (int st = check_hip(bl::launch_rmsnorm_quant(h, h_dtype, M, H, g_subln, eps, q1, a1, decode ? nullptr : qs, s),
+                           "subln launch"))
         return st;
     // 2. gate|up with ReLU^2(gate)*up
     bl::Contract c;
@@ -488,11 +498,13 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
         g.P = packed_gu; g.seg = seg_i; g.w_mean = w_mean_gu; g.y = p; g.y_dt = BL_F32; g.ldy = I; g.pair = 1;
         e = bl::launch_gemv_batch(b, s);
     } else {
-        e = bl::launch_gemm(c, (int *)(wsb + sc.qs), s);
+        c.qsum = qs;
+        e = bl::launch_gemm(c, qs, s);
     }
     if (int st = check_hip(e, "gate|up launch")) return st;
     // 3. ffn_sub_norm RMSNorm + quantize
-    if (int st = check_hip(bl::launch_rmsnorm_quant(p, BL_F32, M, I, g_ffn, eps, q2, a2, s), "ffn_sub_norm launch"))
+    if (int st = check_hip(bl::launch_rmsnorm_quant(p, BL_F32, M, I, g_ffn, eps, q2, a2, decode ? nullptr : qs, s),
+                           "ffn_sub_norm launch"))
         return st;
     // 4. down
     c.q = q2; c.ldq = I; c.a = a2; c.K = I; c.P = packed_down; c.seg = seg_h; c.R = H / 4;
@@ -508,7 +520,8 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
         d.P = packed_down; d.seg = seg_h; d.w_mean = w_mean_down; d.y = y; d.y_dt = y_dtype; d.ldy = H; d.pair = 0;
         e = bl::launch_gemv_batch(b, s);
     } else {
-        e = bl::launch_gemm(c, (int *)(wsb + sc.qs), s);
+        c.qsum = qs;
+        e = bl::launch_gemm(c, qs, s);
     }
     return check_hip(e, "down launch");
 }

@@ -157,21 +157,28 @@ hipError_t launch_ternarize_pack(const float *W, int N, int K, const float *w_me
                                  uint8_t *packed, hipStream_t s);
 
 hipError_t launch_quant_act(const void *x, int x_dt, int M, int K, int ldx, int8_t *q, float *a,
-                            hipStream_t s);
-// Several row quantizations in one launch (problems of the batched decode).
+                            int *qsum, hipStream_t s);
+// One per-token quantization (optionally preceded by RMSNorm): rows
+// [0, M) of x (stride ldx) -> codes q (stride K), scales a, and, when qsum is
+// not null, each row's code sum.
 struct QuantProblem {
     const void *x;
     int8_t *q;
     float *a;
+    int *qsum;          // [M] sum of the row's codes, or nullptr
+    const float *gain;  // RMSNorm gain (nullptr: none)
+    float eps;
+    int norm;           // 1: RMSNorm before quantizing
     int x_dt, M, K, ldx, row0;
 };
+// Several row quantizations in one launch (the problems of a batched decode).
 struct QuantBatch {
     int n;
     QuantProblem p[8];
 };
 hipError_t launch_quant_batch(QuantBatch &qb, hipStream_t s);
 hipError_t launch_rmsnorm_quant(const void *h, int h_dt, int M, int K, const float *g, float eps,
-                                int8_t *q, float *a, hipStream_t s);
+                                int8_t *q, float *a, int *qsum, hipStream_t s);
 
 // Contraction arguments common to the decode and prefill kernels.
 struct Contract {
@@ -187,7 +194,7 @@ struct Contract {
     int y_dt;
     int ldy;
     bool pair;        // gate|up with ReLU^2(gate)*up epilogue; up rows at P + R*K
-    const int *qsum = nullptr;   // [M] code sums of the rows of q (filled by launch_gemm)
+    const int *qsum = nullptr;   // [M] code sums of the rows of q (nullptr: launch_gemm computes them)
 };
 
 // Decode path (M <= 64): one launch covers up to kMaxProblems independent
@@ -221,10 +228,10 @@ struct GemvBatch {
 
 // Fills tile0 of every problem and launches; all problems must share `pair`.
 hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s);
-// Prefill path (any M).
-// Prefill GEMM.  qsum_ws: device scratch for M ints (the rows' code sums,
-// which the large-tile kernel reads instead of recomputing them per tile);
-// without it the small-tile kernel runs.
+// Prefill GEMM (any M).  The large-tile kernel reads the rows' code sums
+// instead of recomputing them per tile: from c.qsum when the caller has them,
+// else computed into qsum_ws (device scratch for M ints); with neither the
+// small-tile kernel runs.
 hipError_t launch_gemm(const Contract &c, int *qsum_ws, hipStream_t s);
 // Any K (slow, simple): used when K is not a multiple of 16.
 hipError_t launch_generic(const Contract &c, hipStream_t s);

@@ -499,10 +499,13 @@ hipError_t launch_gemm(const Contract &c0, int *qsum_ws, hipStream_t s) {
     // (A 256-token tile needs 256 accumulator registers per lane, which the
     // compiler does not keep in the accumulator file: it copies them around
     // every MFMA.  128-token tiles keep all 128 in place.)
-    if (qsum_ws != nullptr && c.K % kGK == 0 && c.ldq % 16 == 0 && c.K <= (1 << 18)) {
-        hipLaunchKernelGGL(k_code_sums, dim3(c.M), dim3(256), 0, s, c.q, c.ldq, c.M, c.K, qsum_ws);
-        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-        c.qsum = qsum_ws;
+    // c.qsum already set: the quantizer wrote the row code sums.
+    if ((c.qsum != nullptr || qsum_ws != nullptr) && c.K % kGK == 0 && c.ldq % 16 == 0 && c.K <= (1 << 18)) {
+        if (c.qsum == nullptr) {
+            hipLaunchKernelGGL(k_code_sums, dim3(c.M), dim3(256), 0, s, c.q, c.ldq, c.M, c.K, qsum_ws);
+            if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+            c.qsum = qsum_ws;
+        }
         const int cus = 256;
         if (c.pair) return go_big<true, 128, 2>(c, s);
         const int mid = ((c.M + 127) / 128) * ((c.R + 63) / 64);

@@ -52,6 +52,15 @@ def test_quant_ragged_fp32_and_bf16(M, K):
     _check_quant_bf16(synth.act_outliers_bf16(12, M, K))
 
 
+# Row lengths at and just past what the register-resident kernel holds
+# (8 loads of 16 bytes per lane: 16384 bf16 or 8192 fp32 elements), a last
+# load that only some lanes make, and lengths that take the re-reading kernel.
+@pytest.mark.parametrize("M,K", [(2, 16384), (2, 16392), (3, 2056), (3, 8192), (2, 8196), (1, 24)])
+def test_quant_register_kernel_bounds(M, K):
+    _check_quant_f32(synth.act_normal_f32(13 + K, M, K))
+    _check_quant_bf16(synth.act_outliers_bf16(14 + K, M, K))
+
+
 def test_quant_edge_rows():
     x = np.zeros((6, 64), np.float32)
     x[1, 3] = 1e-7                      # below the floor
