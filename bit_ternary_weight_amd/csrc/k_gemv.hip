@@ -29,6 +29,8 @@
 // the problems.
 #include "bl_common.h"
 
+#include <cstring>
+
 namespace bl {
 
 namespace {
@@ -335,7 +337,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv(GemvBatch b) {
 //     owns a ring of kRing 1 KB slots; lane l's 16 bytes land at slot + 16 l
 //     and only this wave reads the slot back, so consuming a slot needs only
 //     the wave's own s_waitcnt vmcnt, never a workgroup barrier.  They issue
-//     their first kRing loads at once, before anything else.
+//     their first kRing loads at once, as soon as the activation loads of
+//     the quantizer waves are out.
 //   * 8 quantizer waves (two per SIMD) load the activation rows and quantize
 //     them into LDS.  They synchronise among themselves through LDS flags,
 //     not s_barrier: a stream wave is stalled in the issue of its weight
@@ -353,6 +356,20 @@ constexpr int kRing = 12;            // 1 KB ring slots per stream wave
 constexpr int kLdsQBytes = 12288;    // static LDS for the activation codes (M rows of pitch Kp)
 constexpr int kXRegs = 8;            // 16-byte activation chunks per quantizer lane (all rows)
 constexpr int kSpinMax = 1 << 22;    // bound of every flag wait (about 0.2 s)
+
+// Input kind of a launch of the streaming kernel, shared by all its problems:
+// activation dtype, RMSNorm in the prologue or not, one activation row or up
+// to four.  Each kind is its own kernel: the quantizer code of the other
+// kinds is never fetched.  (The streaming kernel is launched cold, its code
+// evicted from L2 by the previous launch's weight stream, so every
+// instruction-cache line it runs is a miss; with all kinds in one kernel the
+// waves spent a fifth of their time waiting for instruction fetch.)
+constexpr int kXkF32 = 1;    // fp32 activations (else bf16)
+constexpr int kXkNorm = 2;   // RMSNorm before quantizing (one row)
+constexpr int kXkM1 = 4;     // every problem has one activation row
+__host__ __device__ constexpr bool xk_bf16(int xk) { return (xk & kXkF32) == 0; }
+__host__ __device__ constexpr bool xk_norm(int xk) { return (xk & kXkNorm) != 0; }
+__host__ __device__ constexpr bool xk_m1(int xk) { return (xk & (kXkM1 | kXkNorm)) != 0; }
 
 // Activation elements per 16-byte chunk.
 __host__ __device__ constexpr int x_per_chunk(int dt) { return dt == BL_BF16 ? 8 : 4; }
@@ -497,12 +514,12 @@ __device__ __forceinline__ void row_update(T *acc, int m, T v, F op) {
 // gr[j*PER/4 ...], all ones when the norm has no gain).  Each wave leaves its
 // share of every row's code sum in sq_s[m * kQuantWaves + qw].  Global memory
 // is not touched.
-template <int PER, bool NORM>
+template <int PER, bool NORM, bool M1>
 __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, const v4i *gr, int E, int pitch, int qw, int ql,
                            int8_t *q_s, float *a_s, int *sq_s, double *part_d, float *part_f,
                            int *qflag) {
     const int K = p.K;
-    const int M = p.M;
+    const int M = M1 ? 1 : p.M;
     // row and chunk of each register (uniform; counted up once, no divisions)
     int jrow[kXRegs], jchunk[kXRegs];
     {
@@ -636,8 +653,30 @@ struct kWaitVm {
 };
 
 
+// The weight stream is read once per launch: its loads carry the
+// non-temporal hint (cache policy bit nt), so that it does not evict the
+// kernel's code and the activations from L2.
 __device__ __forceinline__ void dma16(const void *src, void *lds_slot) {
-    __builtin_amdgcn_global_load_lds(src, lds_slot, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, lds_slot, 16, 0, 2);
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n < 12 (the loads of one batch).
+__device__ __forceinline__ void wait_vm_upto11(int n) {
+    switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 0: __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value); break;
+    case 1: __builtin_amdgcn_s_waitcnt(kWaitVm<1>::value); break;
+    case 2: __builtin_amdgcn_s_waitcnt(kWaitVm<2>::value); break;
+    case 3: __builtin_amdgcn_s_waitcnt(kWaitVm<3>::value); break;
+    case 4: __builtin_amdgcn_s_waitcnt(kWaitVm<4>::value); break;
+    case 5: __builtin_amdgcn_s_waitcnt(kWaitVm<5>::value); break;
+    case 6: __builtin_amdgcn_s_waitcnt(kWaitVm<6>::value); break;
+    case 7: __builtin_amdgcn_s_waitcnt(kWaitVm<7>::value); break;
+    case 8: __builtin_amdgcn_s_waitcnt(kWaitVm<8>::value); break;
+    case 9: __builtin_amdgcn_s_waitcnt(kWaitVm<9>::value); break;
+    case 10: __builtin_amdgcn_s_waitcnt(kWaitVm<10>::value); break;
+    case 11: __builtin_amdgcn_s_waitcnt(kWaitVm<11>::value); break;
+    default: __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value); break;
+    }
 }
 
 // A unit of the weight stream is 4 packed rows x kUnitK bytes (k values) of
@@ -658,11 +697,14 @@ constexpr int kMaxTileRows = 4 * kMaxCS;
 // rows times 16/RW field slots: column n is row n % RW; MFMA i (of RW/4)
 // takes field i*(16/RW) + n/RW of it.  One 16-byte operand read of a row thus
 // feeds RW/4 MFMAs.
-template <bool PAIR>
+template <bool PAIR, int XK>
 __global__ __launch_bounds__(kLdsWaves * 64)
 void k_gemv_lds(GemvBatch b) {
     constexpr int NB = PAIR ? 2 : 1;
     constexpr int SW = kStreamWaves;
+    constexpr bool BF = xk_bf16(XK);
+    constexpr bool NORM = xk_norm(XK);
+    constexpr bool M1 = xk_m1(XK);
     // Static LDS objects (distinct from the dynamic weight ring, so the
     // compiler can tell that writing them does not race the ring's loads);
     // the dynamic ring then starts after them, never at LDS address 0.
@@ -672,6 +714,7 @@ void k_gemv_lds(GemvBatch b) {
     __shared__ double part_d[kFuseMaxM * kQuantWaves];
     __shared__ float part_f[kFuseMaxM * kQuantWaves];
     __shared__ __attribute__((aligned(16))) int qflag[kQuantWaves];
+    __shared__ __attribute__((aligned(16))) int xgo[kQuantWaves];   // quantizer wave w has issued its loads
     __shared__ __attribute__((aligned(16))) int8_t q_s[kLdsQBytes];
     __shared__ float wm_s[BL_MAX_SEGMENTS];
     extern __shared__ __attribute__((aligned(16))) unsigned char ring_lds[];
@@ -688,14 +731,17 @@ void k_gemv_lds(GemvBatch b) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int K = p.K;
-    const int M = p.M;
+    const int M = M1 ? 1 : p.M;
     const int Kp = (K + kUnitK - 1) / kUnitK * kUnitK;   // row pitch of q_s
 
     // LDS that is accumulated into or polled, and the zero tail of every code
     // row (k in [K, Kp) multiplies weight bytes that lie past K or are not
     // loaded at all), before any wave can touch it
     for (int i = threadIdx.x; i < NB * kMaxTileRows * 4 * kFuseMaxM; i += kLdsWaves * 64) red[i] = 0;
-    if ((int)threadIdx.x < kQuantWaves) qflag[threadIdx.x] = 0;
+    if ((int)threadIdx.x < kQuantWaves) {
+        qflag[threadIdx.x] = 0;
+        xgo[threadIdx.x] = 0;
+    }
     if (Kp > K)
         for (int i = threadIdx.x; i < M * (Kp - K); i += kLdsWaves * 64)
             q_s[(i / (Kp - K)) * Kp + K + i % (Kp - K)] = 0;
@@ -705,9 +751,9 @@ void k_gemv_lds(GemvBatch b) {
         // ---------------- quantizer waves ----------------
         const int qw = wave - SW;
         const int ql = (int)threadIdx.x - SW * 64;
-        const int per = x_per_chunk(p.x_dt);
-        const int esz = p.x_dt == BL_BF16 ? 2 : 4;
-        const int E = x_chunks(K, p.x_dt, kQuantLanes);
+        constexpr int per = BF ? 8 : 4;
+        constexpr int esz = BF ? 2 : 4;
+        const int E = x_chunks(K, BF ? BL_BF16 : BL_F32, kQuantLanes);
         // Registers past the rows are loaded too (straight-line code), each
         // lane from its own chunk of row 0: every workgroup runs this at the
         // same moment, and placeholder loads of one fixed address would all
@@ -730,7 +776,7 @@ void k_gemv_lds(GemvBatch b) {
         }
         // RMSNorm gains of this lane's chunks (shared by the rows): register
         // c*per/4 + h holds gain[k0(c) + 4h .. +3]; all ones without gains
-        const bool gains = p.gain != nullptr && p.mode == 2;
+        const bool gains = NORM && p.gain != nullptr;
         if (gains) {
             const int gspread = (ql * 4) % K;
 #pragma unroll
@@ -746,19 +792,15 @@ void k_gemv_lds(GemvBatch b) {
         }
         const int nscale = PAIR ? 2 : p.seg.n;
         const float wmv = ql < nscale ? p.w_mean[ql] : 0.0f;
+        // The activation loads are now in the memory queues: the stream waves
+        // may start (issued behind the weight stream instead, they would
+        // return only after most of it).
+        asm volatile("" ::: "memory");
+        if ((threadIdx.x & 63) == 0) xgo[qw] = 1;
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value);
         if (ql < nscale) wm_s[ql] = wmv;
-        if (p.mode == 2) {
-            if (p.x_dt == BL_BF16)
-                quant_rows<8, true>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
-            else
-                quant_rows<4, true>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
-        } else {
-            if (p.x_dt == BL_BF16)
-                quant_rows<8, false>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
-            else
-                quant_rows<4, false>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
-        }
+        quant_rows<per, NORM, M1>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
     } else {
         // ---------------- stream waves ----------------
         const int lr = lane & 15;
@@ -791,10 +833,12 @@ void k_gemv_lds(GemvBatch b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = v4i{0, 0, 0, 0};
 
-        // Batches of kb k-ranges: issue every unit of the batch, wait for all
-        // of them, then consume.  (Waiting for the oldest load while later
-        // direct loads are still in flight, and reading LDS meanwhile, slows
-        // the whole stream down on this hardware.)
+        // Batches of kb k-ranges: issue every unit of the batch, then consume
+        // the k-ranges in order, each once its own units have landed.  (A
+        // wait per k-range of UPK units; waiting unit by unit slowed the whole
+        // stream down on this hardware.)  The first weight load goes out
+        // only after every quantizer wave has issued its activation loads.
+        wait_published<1>(xgo, 1);
         for (int b0 = 0; b0 < ks; b0 += kb) {
             const int nb = ks - b0 < kb ? ks - b0 : kb;
             for (int t = 0; t < nb * UPK; ++t) {
@@ -807,11 +851,12 @@ void k_gemv_lds(GemvBatch b) {
                                         : p.P + 16 * dpc;
                 dma16(src, ring + t * 1024);
             }
-            __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value);
-            // the activation codes (once; the quantizer waves publish once per
-            // reduction -- the norm's sum of squares, the absmax -- and once when done)
-            if (b0 == 0) wait_published<4>(qflag, p.mode == 2 ? 3 : 2);
             for (int t = 0; t < nb; ++t) {
+                // this k-range's units have landed (loads complete in order)
+                wait_vm_upto11((nb - 1 - t) << lupk);
+                // the activation codes (once; the quantizer waves publish once per
+                // reduction -- the norm's sum of squares, the absmax -- and once when done)
+                if (b0 == 0 && t == 0) wait_published<4>(qflag, NORM ? 3 : 2);
                 const int kr = kr0 + kstep * (b0 + t);
                 const unsigned char *slot = ring + (t * UPK + (rr >> 2)) * 1024 + 256 * (rr & 3);
                 // all operand reads of the k-range first: one LDS round trip
@@ -957,7 +1002,7 @@ size_t even_share(const GemvBatch &b, int nb, int cus) {
     return total / (size_t)cus;
 }
 
-template <bool PAIR>
+template <bool PAIR, int XK>
 hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
     constexpr int NB = PAIR ? 2 : 1;
     static int cus = 0;
@@ -996,7 +1041,7 @@ hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
     // static part, about 17 KiB, comes on top; both fit the 160 KiB).
     static size_t attr_bytes = 0;
     if (attr_bytes < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_gemv_lds<PAIR>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_gemv_lds<PAIR, XK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) {
             (void)hipGetLastError();   // do not leave the error to the next launch
@@ -1004,8 +1049,29 @@ hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
         }
         attr_bytes = lds;
     }
-    hipLaunchKernelGGL(k_gemv_lds<PAIR>, dim3(tiles), dim3(kLdsWaves * 64), lds, s, o);
+    hipLaunchKernelGGL((k_gemv_lds<PAIR, XK>), dim3(tiles), dim3(kLdsWaves * 64), lds, s, o);
     return hipGetLastError();
+}
+
+// Input kind of a problem of the fused path.
+int xkind_of(const GemvProblem &p) {
+    return (p.x_dt == BL_BF16 ? 0 : kXkF32) | (p.mode == 2 ? kXkNorm : 0) | (p.M == 1 ? kXkM1 : 0);
+}
+
+// Launches the problems of one input kind (norm kinds: M == 1; PAIR only
+// with the norm, as in the fused chain).
+hipError_t launch_lds_kind(GemvBatch &b, int xk, hipStream_t s) {
+    const bool pair = b.p[0].pair != 0;
+    switch (xk) {
+    case kXkNorm | kXkM1: return pair ? launch_lds<true, kXkNorm>(b, s) : launch_lds<false, kXkNorm>(b, s);
+    case kXkF32 | kXkNorm | kXkM1:
+        return pair ? launch_lds<true, kXkF32 | kXkNorm>(b, s) : launch_lds<false, kXkF32 | kXkNorm>(b, s);
+    case kXkM1: return pair ? hipErrorInvalidValue : launch_lds<false, kXkM1>(b, s);
+    case kXkF32 | kXkM1: return pair ? hipErrorInvalidValue : launch_lds<false, kXkF32 | kXkM1>(b, s);
+    case 0: return pair ? hipErrorInvalidValue : launch_lds<false, 0>(b, s);
+    case kXkF32: return pair ? hipErrorInvalidValue : launch_lds<false, kXkF32>(b, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s) {
@@ -1015,14 +1081,30 @@ hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s) {
             const GemvProblem &p = b.p[i];
             const int per = x_per_chunk(p.x_dt);
             const int E = x_chunks(p.K, p.x_dt, kQuantLanes);
-            if (p.mode == 0 || p.M > kFuseMaxM || p.M * E > kXRegs ||
+            if (p.mode == 0 || (p.x_dt != BL_BF16 && p.x_dt != BL_F32) || p.M > kFuseMaxM || p.M * E > kXRegs ||
                 (p.mode == 2 && (p.M != 1 || E * per / 4 > kXRegs)) ||
                 (size_t)p.M * ((p.K + kUnitK - 1) / kUnitK * kUnitK) > (size_t)kLdsQBytes ||
                 ((uintptr_t)p.gain % 16) != 0 || p.K % 16 != 0 || p.K % per != 0 || p.ldx % per != 0 ||
-                (p.pair != 0) != (b.p[0].pair != 0))
+                (p.pair != 0) != (b.p[0].pair != 0) || (p.pair != 0 && p.mode != 2))
                 ok = false;
         }
-        if (ok) return b.p[0].pair ? launch_lds<true>(b, s) : launch_lds<false>(b, s);
+        if (ok) {
+            // one launch per input kind present (output rows are disjoint)
+            bool done[kMaxProblems] = {};
+            for (int i = 0; i < b.n; ++i) {
+                if (done[i]) continue;
+                const int xk = xkind_of(b.p[i]);
+                GemvBatch g;
+                memset(&g, 0, sizeof(g));
+                for (int j = i; j < b.n; ++j)
+                    if (!done[j] && xkind_of(b.p[j]) == xk) {
+                        g.p[g.n++] = b.p[j];
+                        done[j] = true;
+                    }
+                if (hipError_t e = launch_lds_kind(g, xk, s); e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
     }
     int tiles = 0, max_m = 1, max_steps = 1;
     size_t qbytes = 0;
