@@ -536,6 +536,13 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
     }
     auto elem0 = [&](int j) { return (jchunk[j] * kQuantLanes + ql) * PER; };
     auto row_of = [&](int j) { return jrow[j]; };
+    // Registers in use: a uniform bound, so each pass leaves its unrolled
+    // loop with one branch (the code of the unused registers is never
+    // fetched).  Past the row end a lane's register reads as zeros, which
+    // leave the maximum, the sum of squares and the code sum unchanged and
+    // are not stored.
+    const int nreg = M * E;
+    auto reg = [&](int j) { return elem0(j) < K ? xr[j] : v4i{0, 0, 0, 0}; };
     // the norm of register j's chunk (NORM: M == 1, so chunk j, static)
     auto norm = [&](float *v, int j, float r) {
         const v4i g0 = gr[(j * (PER / 4)) % kXRegs];
@@ -550,9 +557,9 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
         double ss[kFuseMaxM] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int j = 0; j < kXRegs; ++j) {
-            if (j >= M * E || elem0(j) >= K) continue;   // K % PER == 0
+            if (j >= nreg) break;
             float v[PER];
-            chunk_f32<PER>(xr[j], v);
+            chunk_f32<PER>(reg(j), v);
             double t = 0.0;
 #pragma unroll
             for (int i = 0; i < PER; ++i) t += (double)v[i] * (double)v[i];
@@ -578,9 +585,9 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
     float amax[kFuseMaxM] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
-        if (j >= M * E || elem0(j) >= K) continue;
+        if (j >= nreg) break;
         float v[PER];
-        chunk_f32<PER>(xr[j], v);
+        chunk_f32<PER>(reg(j), v);
         const int m = row_of(j);
         if (NORM) norm(v, j, r[0]);
         float t = 0.0f;
@@ -610,9 +617,9 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
 #pragma unroll
     for (int j = 0; j < kXRegs; ++j) {
         const int k0 = elem0(j);
-        if (j >= M * E || k0 >= K) continue;
+        if (j >= nreg) break;
         float v[PER];
-        chunk_f32<PER>(xr[j], v);
+        chunk_f32<PER>(reg(j), v);
         const int m = row_of(j);
         if (NORM) norm(v, j, r[0]);
         const float scale = sel4(s, m);
@@ -632,8 +639,10 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
         }
         row_update(qsum, m, cs, [](int a, int b) { return a + b; });
         int8_t *dst = q_s + (size_t)m * pitch + k0;
-        if (PER == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[PER / 4 - 1]);
-        else *reinterpret_cast<uint32_t *>(dst) = pk[0];
+        if (k0 < K) {
+            if (PER == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[PER / 4 - 1]);
+            else *reinterpret_cast<uint32_t *>(dst) = pk[0];
+        }
     }
 #pragma unroll
     for (int m = 0; m < kFuseMaxM; ++m) {
@@ -760,7 +769,10 @@ void k_gemv_lds(GemvBatch b) {
         // queue on the single L2 channel that holds it.
         v4i xr[kXRegs];
         v4i gr[kXRegs];
-        const size_t spread = ((size_t)ql * 16) % ((size_t)K * esz);
+        // (lane offsets below the largest power of two in the row's bytes:
+        // a mask, no division; K % 16 == 0, so the row has at least 32 bytes)
+        const int rowb = K * esz;
+        const size_t spread = (size_t)((ql * 16) & ((1 << (31 - __builtin_clz(rowb))) - 1));
         {
             int m = 0, c = 0;   // row and chunk of register j (no divisions)
 #pragma unroll
@@ -778,7 +790,7 @@ void k_gemv_lds(GemvBatch b) {
         // c*per/4 + h holds gain[k0(c) + 4h .. +3]; all ones without gains
         const bool gains = NORM && p.gain != nullptr;
         if (gains) {
-            const int gspread = (ql * 4) % K;
+            const int gspread = (ql * 4) & ((1 << (31 - __builtin_clz(K))) - 1);
 #pragma unroll
             for (int j = 0; j < kXRegs; ++j) {
                 const int c = j / (per / 4);
@@ -1058,16 +1070,312 @@ int xkind_of(const GemvProblem &p) {
     return (p.x_dt == BL_BF16 ? 0 : kXkF32) | (p.mode == 2 ? kXkNorm : 0) | (p.M == 1 ? kXkM1 : 0);
 }
 
-// Launches the problems of one input kind (norm kinds: M == 1; PAIR only
-// with the norm, as in the fused chain).
+// ===========================================================================
+// One-row streaming kernel (M == 1): the fused decode path for a single
+// activation row.  One 16-wave workgroup per CU, with the two roles of
+// k_gemv_lds:
+//   * 8 quantizer waves load the row and quantize it into LDS (quant_rows:
+//     RMSNorm sum of squares, absmax, codes, synchronised among themselves
+//     through LDS flags).  They issue no weight load, so nothing holds them
+//     up: a wave that issues weight loads is stalled in the issue for
+//     microseconds while the CU's requests drain at its share of HBM.
+//   * 8 stream waves issue their weight units once the activation loads are
+//     out: a unit is 4 packed rows x 256 bytes of one tensor (two whole
+//     128-byte lines per row), 16 bytes per lane, loaded into registers with
+//     the non-temporal hint.  Once the codes are published they consume the
+//     units in order, each as soon as it has landed: lane L holds row L >> 4
+//     of the unit, bytes 16 (L & 15) .. +15 of the k-range; the four 2-bit
+//     fields of each byte, masked in place (codes + 1 times 1, 4, 16, 16), go
+//     through sdot4 with the matching activation codes.  Each row is then
+//     summed over its 16 lanes (DPP) into LDS.
+// Both roles meet at one barrier, after which the outputs are rescaled and
+// stored.  With one row, a 16 x 16 x 64 MFMA would waste 15/16 of its work;
+// the VALU dot products cost 9 operations per weight dword.
+// ===========================================================================
+constexpr int kV1MaxUnits = 16;   // weight units per stream wave, all in flight (4 VGPRs each)
+constexpr int kV1MaxRows = 32;    // packed rows per tensor per workgroup (4 * CS, NB * CS <= 8)
+
+__device__ __forceinline__ v4i ld16_nt(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
+// Sum over each 16-lane DPP row (every lane of the row gets the row's sum).
+__device__ __forceinline__ int row16_sum(int v) {
+    v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_i<0x124>(v);   // row_ror:4
+    v += dpp_i<0x128>(v);   // row_ror:8
+    return v;
+}
+
+template <bool PAIR, int XK, int NS>
+__global__ __launch_bounds__(kLdsWaves * 64)
+void k_gemv_v1(GemvBatch b) {
+    constexpr int NB = PAIR ? 2 : 1;
+    constexpr int SW = kStreamWaves;
+    constexpr bool BF = xk_bf16(XK);
+    constexpr bool NORM = xk_norm(XK);
+    static_assert(xk_m1(XK), "one activation row");
+    __shared__ int red[NB * kV1MaxRows * 4];          // [tensor][packed row][field]
+    __shared__ float a_s[kFuseMaxM];
+    __shared__ int sq_s[kFuseMaxM * kQuantWaves];     // per-wave code sums
+    __shared__ double part_d[kFuseMaxM * kQuantWaves];
+    __shared__ float part_f[kFuseMaxM * kQuantWaves];
+    __shared__ __attribute__((aligned(16))) int qflag[kQuantWaves];
+    __shared__ __attribute__((aligned(16))) int xgo[kQuantWaves];   // quantizer wave w has issued its loads
+    __shared__ float wm_s[BL_MAX_SEGMENTS];
+    __shared__ __attribute__((aligned(16))) int8_t q_s[kLdsQBytes];
+
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxProblems; ++i)
+        if (i < b.n && (int)blockIdx.x >= b.p[i].tile0) pi = i;
+    const GemvProblem &p = b.p[pi];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+    const int lane = tid & 63;
+    const int K = p.K;
+    const int R = p.R;
+    const int CS = p.cs;                 // 1 .. 8, NB * CS <= 8
+    const int r0 = ((int)blockIdx.x - p.tile0) * 4 * CS;
+    const int nkr = (K + kUnitK - 1) / kUnitK;
+    const int Kp = nkr * kUnitK;         // row pitch of q_s
+
+    // LDS that is accumulated into or polled, and the zero code tail (k in
+    // [K, Kp): weight bytes there are placeholders or past K and must meet
+    // code 0), before any wave can touch it
+    for (int i = tid; i < NB * kV1MaxRows * 4; i += kLdsWaves * 64) red[i] = 0;
+    if (tid < kQuantWaves) {
+        qflag[tid] = 0;
+        xgo[tid] = 0;
+    }
+    if (tid < Kp - K) q_s[K + tid] = 0;
+    lds_barrier();
+
+    if (wave >= SW) {
+        // ---------------- quantizer waves ----------------
+        constexpr int per = BF ? 8 : 4;
+        constexpr int esz = BF ? 2 : 4;
+        const int qw = wave - SW;
+        const int ql = tid - SW * 64;
+        const int E = x_chunks(K, BF ? BL_BF16 : BL_F32, kQuantLanes);
+        v4i xr[kXRegs];
+        v4i gr[kXRegs];
+        // registers past the row read an in-row chunk of this lane (below
+        // the largest power of two in the row's bytes; a mask, no division)
+        const size_t spread = (size_t)((ql * 16) & ((1 << (31 - __builtin_clz(K * esz))) - 1));
+#pragma unroll
+        for (int j = 0; j < kXRegs; ++j) {
+            const int k0 = (j * kQuantLanes + ql) * per;
+            xr[j] = ld16((const unsigned char *)p.x + (j < E && k0 < K ? (size_t)k0 * esz : spread));
+        }
+        if (NORM && p.gain != nullptr) {
+            const int gspread = (ql * 4) & ((1 << (31 - __builtin_clz(K))) - 1);
+#pragma unroll
+            for (int j = 0; j < kXRegs; ++j) {
+                const int c = j / (per / 4);
+                const int h = j - c * (per / 4);
+                const int k0 = (c * kQuantLanes + ql) * per + 4 * h;
+                gr[j] = ld16(p.gain + (c < E && k0 < K ? k0 : gspread));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kXRegs; ++j) gr[j] = v4i{0x3F800000, 0x3F800000, 0x3F800000, 0x3F800000};
+        }
+        const int nscale = PAIR ? 2 : p.seg.n;
+        const float wmv = ql < nscale ? p.w_mean[ql] : 0.0f;
+        // the activation loads are in the queue: the stream waves may start
+        asm volatile("" ::: "memory");
+        if (lane == 0) xgo[qw] = 1;
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVm<0>::value);
+        if (ql < nscale) wm_s[ql] = wmv;
+        quant_rows<per, NORM, true>(p, xr, gr, E, Kp, qw, ql, q_s, a_s, sq_s, part_d, part_f, qflag);
+    } else {
+        // ---------------- stream waves ----------------
+        // tensor tsel, row group rg (4 packed rows), k-ranges kr0, kr0 +
+        // kstep, ... (all counts powers of two)
+        const int groups = NB * CS;
+        const int lwpg = __builtin_ctz(SW / groups);   // log2 stream waves per row group
+        const int grp = wave >> lwpg;
+        const int tsel = NB == 2 ? (grp & 1) : 0;
+        const int rg = NB == 2 ? (grp >> 1) : grp;
+        const int kr0 = wave & ((1 << lwpg) - 1);
+        const int kstep = 1 << lwpg;
+        const int ks = kr0 < nkr ? (nkr - kr0 + kstep - 1) >> lwpg : 0;   // <= NS
+        // Unit t covers the wave's k-range (t + rot) mod ks: waves and
+        // workgroups start at different k-ranges, so the requests in flight at
+        // any moment do not all fall on the same offsets of their rows (and on
+        // the same memory channels).  The sum does not depend on the order.
+        const int rot = ks > 0 ? (int)(((unsigned)blockIdx.x * 7u + (unsigned)wave * 3u) % (unsigned)ks) : 0;
+        auto kr_of = [&](int t) {
+            const int j = t + rot;
+            return kr0 + kstep * (j >= ks ? j - ks : j);
+        };
+        const int lr = lane >> 4;                  // row of the unit
+        const int lc = lane & 15;                  // 16-byte chunk of the k-range
+        const int row = r0 + rg * 4 + lr;
+        const size_t tbytes = (size_t)R * K;       // one tensor
+        // placeholder offset inside the tensor (largest power of two <= its size)
+        const int lpw = 63 - __builtin_clzll((unsigned long long)tbytes);
+        const size_t spread = (size_t)(16 * lane) & ((((size_t)1) << lpw) - 1);
+        const uint8_t *wrow = p.P + ((size_t)tsel * R + (row < R ? row : 0)) * K;
+        const uint8_t *wbase = p.P + (size_t)tsel * tbytes;
+        auto unit_src = [&](int kr) {
+            const int kb = kr * kUnitK + 16 * lc;
+            return row < R && kb < K ? wrow + kb : wbase + spread;
+        };
+        // Every stream wave issues exactly NS unit loads (NS >= ks for every
+        // wave of the launch): the load count is then the same on every path,
+        // so the compiler's own waits for these registers are exact (a count
+        // that varied by path would make it wait for all loads before the
+        // first use).  Loads past ks re-read the lane's last unit (a cache hit).
+        wait_published<1>(xgo, 1);
+        v4i wv[NS];
+#pragma clang loop unroll(full)
+        for (int t = 0; t < NS; ++t) {
+            const int tt = t < ks ? t : ks - 1;
+            wv[t] = ld16_nt(tt >= 0 ? unit_src(kr_of(tt)) : wbase + spread);
+        }
+        // the activation codes (the quantizer waves publish once per
+        // reduction -- the norm's sum of squares, the absmax -- and once when done)
+        wait_published<4>(qflag, NORM ? 3 : 2);
+        int acc0 = 0, acc1 = 0, acc2 = 0, acc3 = 0;
+        // unit t is used once the t + 1 oldest unit loads have landed (the
+        // compiler's wait: vmcnt(NS - 1 - t), loads complete in order)
+#pragma clang loop unroll(full)
+        for (int t = 0; t < NS; ++t) {
+            if (t < ks) {
+                const v4i w = wv[t];
+                const v4i xq = *reinterpret_cast<const v4i *>(q_s + kr_of(t) * kUnitK + 16 * lc);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t u = (uint32_t)w[d];
+                    acc0 = __builtin_amdgcn_sdot4((int)(u & 0x03030303u), xq[d], acc0, false);
+                    acc1 = __builtin_amdgcn_sdot4((int)(u & 0x0C0C0C0Cu), xq[d], acc1, false);
+                    acc2 = __builtin_amdgcn_sdot4((int)(u & 0x30303030u), xq[d], acc2, false);
+                    acc3 = __builtin_amdgcn_sdot4((int)((u >> 2) & 0x30303030u), xq[d], acc3, false);
+                }
+            }
+        }
+        // row sums over the 16 lanes of each row; the field scale of the
+        // masked fields divides out exactly (every product carries it)
+        acc0 = row16_sum(acc0);
+        acc1 = row16_sum(acc1) >> 2;
+        acc2 = row16_sum(acc2) >> 4;
+        acc3 = row16_sum(acc3) >> 4;
+        if (lc == 0 && ks > 0) {
+            int *dst = red + (tsel * kV1MaxRows + rg * 4 + lr) * 4;
+            atomicAdd(dst + 0, acc0);
+            atomicAdd(dst + 1, acc1);
+            atomicAdd(dst + 2, acc2);
+            atomicAdd(dst + 3, acc3);
+        }
+    }
+    lds_barrier();
+
+    // rescale and store: e = (packed row, field); the codes were taken as
+    // c + 1, so the row's code sum comes off once
+    int qsum = 0;
+#pragma unroll
+    for (int w = 0; w < kQuantWaves; ++w) qsum += sq_s[w];
+    const float a = a_s[0];
+    for (int e = tid; e < 4 * CS * 4; e += kLdsWaves * 64) {
+        const int f = e & 3;
+        const int prow = e >> 2;
+        const int vr = r0 + prow;
+        if (vr >= R) continue;
+        const int A = red[(0 * kV1MaxRows + prow) * 4 + f] - qsum;
+        const int U = PAIR ? red[(1 * kV1MaxRows + prow) * 4 + f] - qsum : 0;
+        emit_out(p.y, p.y_dt, p.ldy, PAIR, p.seg, R, wm_s, 0, vr, f, a, A, U);
+    }
+    // The first tile's workgroup hands out the codes and scale (stage outputs
+    // for checks).
+    if ((int)blockIdx.x == p.tile0 && p.dbg_q != nullptr) {
+        for (int i = tid; i < K; i += kLdsWaves * 64) p.dbg_q[i] = q_s[i];
+        if (p.dbg_a != nullptr && tid == 0) p.dbg_a[0] = a;
+    }
+}
+
+template <bool PAIR, int XK, int NS>
+hipError_t go_v1(GemvBatch &o, int tiles, hipStream_t s) {
+    hipLaunchKernelGGL((k_gemv_v1<PAIR, XK, NS>), dim3(tiles), dim3(kLdsWaves * 64), 0, s, o);
+    return hipGetLastError();
+}
+
+template <bool PAIR, int XK>
+hipError_t launch_v1(GemvBatch &b, hipStream_t s) {
+    constexpr int NB = PAIR ? 2 : 1;
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus = n;
+    }
+    // as launch_lds: even share of the weight bytes per CU, longest K first,
+    // each problem's tile the largest 4 * CS rows (CS = 8 / NB, ..., 1) that
+    // stays within 1.25x the share; CS shrinks further until no stream wave
+    // has more than kV1MaxUnits units (a row group's k-ranges split over
+    // 8 / (NB * CS) waves)
+    const size_t share = even_share(b, NB, cus) * 5 / 4;
+    GemvBatch o = b;
+    int order[kMaxProblems];
+    for (int i = 0; i < b.n; ++i) order[i] = i;
+    for (int i = 1; i < b.n; ++i)
+        for (int j = i; j > 0 && b.p[order[j]].K > b.p[order[j - 1]].K; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    int tiles = 0, ns = 1;
+    for (int i = 0; i < b.n; ++i) {
+        GemvProblem &q = o.p[i];
+        q = b.p[order[i]];
+        const int nkr = (q.K + kUnitK - 1) / kUnitK;
+        auto units = [&](int cs) {
+            const int kstep = kStreamWaves / (NB * cs);
+            return (nkr + kstep - 1) / kstep;
+        };
+        int cs = kStreamWaves / NB;
+        while (cs > 1 && ((size_t)NB * 4 * cs * q.K > share || units(cs) > kV1MaxUnits)) cs >>= 1;
+        if (units(cs) > kV1MaxUnits) return hipErrorInvalidValue;   // K beyond the one-row kernel
+        q.cs = cs;
+        q.tile0 = tiles;
+        tiles += (q.R + 4 * cs - 1) / (4 * cs);
+        ns = units(cs) > ns ? units(cs) : ns;
+    }
+    o.ring_off = 0;
+    switch (ns) {
+    case 1: return go_v1<PAIR, XK, 1>(o, tiles, s);
+    case 2: return go_v1<PAIR, XK, 2>(o, tiles, s);
+    case 3: return go_v1<PAIR, XK, 3>(o, tiles, s);
+    case 4: return go_v1<PAIR, XK, 4>(o, tiles, s);
+    case 5: return go_v1<PAIR, XK, 5>(o, tiles, s);
+    case 6: return go_v1<PAIR, XK, 6>(o, tiles, s);
+    case 7: return go_v1<PAIR, XK, 7>(o, tiles, s);
+    case 8: return go_v1<PAIR, XK, 8>(o, tiles, s);
+    case 9: case 10: return go_v1<PAIR, XK, 10>(o, tiles, s);
+    case 11: case 12: return go_v1<PAIR, XK, 12>(o, tiles, s);
+    default: return go_v1<PAIR, XK, 16>(o, tiles, s);
+    }
+}
+
+// Launches the problems of one input kind: one activation row (the norm
+// kinds always) -> the one-row kernel; up to four rows -> the MFMA kernel.
+// PAIR only comes with the norm, as in the fused chain.
 hipError_t launch_lds_kind(GemvBatch &b, int xk, hipStream_t s) {
     const bool pair = b.p[0].pair != 0;
     switch (xk) {
-    case kXkNorm | kXkM1: return pair ? launch_lds<true, kXkNorm>(b, s) : launch_lds<false, kXkNorm>(b, s);
+    case kXkNorm | kXkM1: return pair ? launch_v1<true, kXkNorm>(b, s) : launch_v1<false, kXkNorm>(b, s);
     case kXkF32 | kXkNorm | kXkM1:
-        return pair ? launch_lds<true, kXkF32 | kXkNorm>(b, s) : launch_lds<false, kXkF32 | kXkNorm>(b, s);
-    case kXkM1: return pair ? hipErrorInvalidValue : launch_lds<false, kXkM1>(b, s);
-    case kXkF32 | kXkM1: return pair ? hipErrorInvalidValue : launch_lds<false, kXkF32 | kXkM1>(b, s);
+        return pair ? launch_v1<true, kXkF32 | kXkNorm>(b, s) : launch_v1<false, kXkF32 | kXkNorm>(b, s);
+    case kXkM1: return pair ? hipErrorInvalidValue : launch_v1<false, kXkM1>(b, s);
+    case kXkF32 | kXkM1: return pair ? hipErrorInvalidValue : launch_v1<false, kXkF32 | kXkM1>(b, s);
     case 0: return pair ? hipErrorInvalidValue : launch_lds<false, 0>(b, s);
     case kXkF32: return pair ? hipErrorInvalidValue : launch_lds<false, kXkF32>(b, s);
     default: return hipErrorInvalidValue;
