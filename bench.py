@@ -102,7 +102,7 @@ def capture(torch, fn):
     return g
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_lds_decode_config2_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_v1_decode_config2_traffic.md")
 TRAFFIC_SOURCES = ("bit_ternary_weight_amd/csrc/k_gemv.hip", "bit_ternary_weight_amd/csrc/bl_common.h")
 
 
@@ -237,7 +237,7 @@ def main():
     traffic = profiled_traffic()
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_gemv_lds<false> (batched decode GEMV, fused per-token quantization)",
+                "kernel": "k_gemv_v1<false, bf16 one row, 10 units> (batched one-row decode GEMV, fused per-token quantization)",
                 "bytes_per_launch": sb, "avg_launch_us": round(ms * 1e3, 3),
                 "traffic_over_algorithmic": None if traffic is None else round(traffic / sb, 4)}
     if args.kernel_only:
