@@ -277,9 +277,10 @@ def main():
             extra[f"decode_m{M}_us_per_layer"] = round(t * 1e3, 2)
             log(f"config 3 decode M={M}: {t * 1e3:.2f} us/layer, {extra[f'decode_m{M}_gbs']} GB/s")
             del g, pm
-        # one layer, weights resident in the Infinity Cache (warm), for contrast
-        g = capture(torch, lambda: bl.gemv_w2a8_batched(probs1[0]))
-        t = timer.run(g.replay, 200, 10)
+        # one layer, weights resident in the Infinity Cache (warm), for
+        # contrast: 30 back-to-back launches on the same layer per replay
+        g = capture(torch, lambda: [bl.gemv_w2a8_batched(probs1[0]) for _ in range(len(layers))])
+        t = timer.run(g.replay, 20, 2) / len(layers)
         extra["decode_m1_one_layer_warm_gbs"] = round(sb / (t * 1e-3) / 1e9, 1)
         del g
         # prefill GEMM (config 4): fused gate|up (2560 -> 2x6912) then down (6912 -> 2560), M=2048
