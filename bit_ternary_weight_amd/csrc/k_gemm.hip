@@ -226,7 +226,44 @@ __device__ __forceinline__ void g_lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <bool PAIR, int TM, int NBW>
+// 4 x 4 transpose across the lanes of a quad (lanes 4q .. 4q + 3, rq = lane
+// & 3): lane rq enters with v[j] = M[rq][j] and leaves with v[j] = M[j][rq].
+// Two exchange stages (partner rq ^ 1, then rq ^ 2) through DPP quad_perm.
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float v[4], int rq) {
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float t = quad_dpp<0xB1>(v[j ^ 1]);   // quad_perm [1,0,3,2]: lane rq ^ 1
+        a[j] = ((j ^ rq) & 1) ? t : v[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float t = quad_dpp<0x4E>(a[j ^ 2]);   // quad_perm [2,3,0,1]: lane rq ^ 2
+        v[j] = ((j ^ rq) & 2) ? t : a[j];
+    }
+}
+
+// Four consecutive outputs of one row from one lane (y 16-byte aligned for
+// fp32 / int32, 8-byte for bf16; the values of int32 output are the exact
+// accumulators carried as float bit patterns).
+__device__ __forceinline__ void store4(void *y, int y_dt, size_t idx, const float v[4]) {
+    if (y_dt == BL_F32) {
+        *reinterpret_cast<float4 *>((float *)y + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if (y_dt == BL_BF16) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2 *>((uint16_t *)y + idx) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<int4 *>((int32_t *)y + idx) =
+            make_int4(__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3]));
+    }
+}
+
+template <bool PAIR, int TM, int NBW, bool VOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_big(Contract c, int ntm) {
     using S = GemmShape<PAIR, TM, NBW>;
@@ -413,6 +450,56 @@ void k_gemm_big(Contract c, int ntm) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][b][f][j] = (acc[i][b][f][j] >> sh) - qsr[j];
             }
+        if (VOUT) {
+            // Vector stores: scale in place (lane: column lr, token rows
+            // 4g + j), transpose each quad so that lane 4q + rq holds columns
+            // 4q .. 4q + 3 of token row 4g + rq, and store them at once.
+            // (The quad's columns are consecutive and inside one segment and
+            // below R: the launcher checks the segment sizes.)
+            const int rq = lr & 3;
+            const int mrow = m0 + wm * (TM / 2) + i * 16 + 4 * g + rq;   // this lane's row after the transpose
+            float am[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
+                am[j] = m < c.M ? c.a[m] : 1.0f;
+            }
+            const size_t rowo = (size_t)(mrow < c.M ? mrow : 0) * c.ldy;
+            if (PAIR) {
+                float s0[4], s1[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s0[j] = wmb[0] / am[j];
+                    s1[j] = wmb[1] / am[j];
+                }
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        v[j] = relu2_mul((float)acc[i][0][f][j] * s0[j], (float)acc[i][1][f][j] * s1[j]);
+                    quad_transpose(v, rq);
+                    if (mrow < c.M && okb[0]) store4(c.y, c.y_dt, rowo + colb[0][f] - rq, v);
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < NBW; ++b) {
+                    float sc[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sc[j] = wmb[b] / am[j];
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        float v[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            v[j] = c.y_dt == BL_I32 ? __int_as_float(acc[i][b][f][j]) : (float)acc[i][b][f][j] * sc[j];
+                        quad_transpose(v, rq);
+                        if (mrow < c.M && okb[b]) store4(c.y, c.y_dt, rowo + colb[b][f] - rq, v);
+                    }
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
@@ -472,7 +559,7 @@ __global__ __launch_bounds__(256) void k_generic(Contract c) {
 
 } // namespace
 
-template <bool PAIR, int TM, int NBW>
+template <bool PAIR, int TM, int NBW, bool VOUT>
 hipError_t go_big(const Contract &c, hipStream_t s) {
     using S = GemmShape<PAIR, TM, NBW>;
     const int ntm = (c.M + TM - 1) / TM;
@@ -480,7 +567,7 @@ hipError_t go_big(const Contract &c, hipStream_t s) {
     const size_t lds = (size_t)kGStages * S::STAGE;
     static bool attr = false;   // the dynamic LDS above 64 KiB must be allowed once
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_gemm_big<PAIR, TM, NBW>,
+        hipError_t e = hipFuncSetAttribute((const void *)k_gemm_big<PAIR, TM, NBW, VOUT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -488,8 +575,27 @@ hipError_t go_big(const Contract &c, hipStream_t s) {
         }
         attr = true;
     }
-    hipLaunchKernelGGL((k_gemm_big<PAIR, TM, NBW>), dim3(ntm * ntn), dim3(256), lds, s, c, ntm);
+    hipLaunchKernelGGL((k_gemm_big<PAIR, TM, NBW, VOUT>), dim3(ntm * ntn), dim3(256), lds, s, c, ntm);
     return hipGetLastError();
+}
+
+// The vector-store epilogue writes 4 consecutive output columns per lane: every
+// group of 4 packed rows (the columns of one field) must lie in one segment
+// (segment sizes multiples of 4 packed rows), and the rows and base pointer
+// must be aligned for 16-byte (fp32, int32) or 8-byte (bf16) stores.
+static bool vout_ok(const Contract &c) {
+    if (c.R % 4 != 0 || c.ldy % 4 != 0) return false;
+    const size_t esz = c.y_dt == BL_BF16 ? 2 : 4;
+    if ((uintptr_t)c.y % (4 * esz) != 0) return false;
+    if (!c.pair)
+        for (int i = 0; i <= c.seg.n; ++i)
+            if (c.seg.roff[i] % 4 != 0) return false;
+    return true;
+}
+
+template <bool PAIR, int TM, int NBW>
+hipError_t go_big_v(const Contract &c, hipStream_t s) {
+    return vout_ok(c) ? go_big<PAIR, TM, NBW, true>(c, s) : go_big<PAIR, TM, NBW, false>(c, s);
 }
 
 hipError_t launch_gemm(const Contract &c0, int *qsum_ws, hipStream_t s) {
@@ -507,10 +613,10 @@ hipError_t launch_gemm(const Contract &c0, int *qsum_ws, hipStream_t s) {
             c.qsum = qsum_ws;
         }
         const int cus = 256;
-        if (c.pair) return go_big<true, 128, 2>(c, s);
+        if (c.pair) return go_big_v<true, 128, 2>(c, s);
         const int mid = ((c.M + 127) / 128) * ((c.R + 63) / 64);
-        if (mid >= cus) return go_big<false, 128, 2>(c, s);
-        return go_big<false, 128, 1>(c, s);
+        if (mid >= cus) return go_big_v<false, 128, 2>(c, s);
+        return go_big_v<false, 128, 1>(c, s);
     }
     const int ntm = (c.M + kBM - 1) / kBM;
     const int ntn = (c.R + kVR - 1) / kVR;

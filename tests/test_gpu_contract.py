@@ -103,6 +103,8 @@ def test_gemv_long_k_repeated():
 GEMM_SHAPES = [
     (1, 64, (4,)), (7, 256, (256,)), (64, 256, (128,)), (65, 256, (128,)), (128, 512, (64,)),
     (129, 320, (36,)), (200, 1024, (256, 64, 64)), (300, 2560, (160,)), (256, 6912, (128,)),
+    # segments of 3 and 2 packed rows: the large-tile kernel with per-column stores
+    (130, 512, (12, 8)),
 ]
 
 
