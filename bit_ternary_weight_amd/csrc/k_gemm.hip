@@ -263,15 +263,11 @@ __device__ __forceinline__ void store4(void *y, int y_dt, size_t idx, const floa
     }
 }
 
+// One output tile: TM tokens from m0 x the packed rows from r0 (ROWS of them).
 template <bool PAIR, int TM, int NBW, bool VOUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_gemm_big(Contract c, int ntm) {
+__device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const int r0, unsigned char *g_lds) {
     using S = GemmShape<PAIR, TM, NBW>;
     constexpr int NA = S::NA;
-    // a static LDS object first: the dynamic ring must not start at address 0
-    __shared__ int qs_s[4];
-    extern __shared__ __attribute__((aligned(16))) unsigned char g_lds[];
-
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -279,13 +275,8 @@ void k_gemm_big(Contract c, int ntm) {
     const int g = lane >> 4;
     const int wm = wave & 1;
     const int wn = wave >> 1;
-    const int bm = blockIdx.x % ntm;
-    const int bn = blockIdx.x / ntm;
-    const int m0 = bm * TM;
-    const int r0 = bn * S::ROWS;
     const int K = c.K;
     const int nst = K / kGK;
-    if (tid < 4) qs_s[tid] = 0;
     // Swizzle of a tile row: the 16-byte chunk c of row r sits at position
     // c ^ swz(r).  With 256-byte rows a row spans all 64 banks, so the 16 rows
     // of a fragment need 16 distinct positions (r & 15); with 128-byte rows
@@ -346,7 +337,7 @@ void k_gemm_big(Contract c, int ntm) {
     const int lsw = swz(lr);
     auto chunk = [&](int ch) { return 16 * (ch ^ lsw); };
 
-    g_lds_barrier();   // qs_s initialised; no LDS load below can race it
+    g_lds_barrier();   // the kernel's static LDS initialised; no LDS load below can race it
     issue(0);
     if (nst > 1) issue(1);
     v4i af[NA], bw[NBW];
@@ -529,6 +520,38 @@ void k_gemm_big(Contract c, int ntm) {
     }
 }
 
+// Workgroup b of the launch: the leading nA workgroups take full tiles 0 ..
+// nA - 1; the next nH take half tiles (TM / 2 tokens) covering full tiles nA
+// .. nA + nH / 2 - 1; the rest take the remaining full tiles in order.  The
+// device starts workgroups b and b + (number of CUs) on the same CU, so with
+// nA = nH = CUs each CU's second workgroup finishes its first tile about half
+// way through the first one's, and from then on the two run half a tile out
+// of phase: one's epilogue (bound by the chip-wide output writes) overlaps
+// the other's MFMA loop.  Tile t covers tokens (t % ntm) * TM and packed rows
+// (t / ntm) * ROWS.
+template <bool PAIR, int TM, int NBW, bool VOUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gemm_big(Contract c, int ntm, int nA, int nH) {
+    using S = GemmShape<PAIR, TM, NBW>;
+    // a static LDS object first: the dynamic ring must not start at address 0
+    __shared__ int qs_s[4];
+    extern __shared__ __attribute__((aligned(16))) unsigned char g_lds[];
+    if (threadIdx.x < 4) qs_s[threadIdx.x] = 0;
+    const int b = blockIdx.x;
+    if constexpr (TM % 64 == 0) {
+        if (b >= nA && b < nA + nH) {
+            const int h = b - nA;
+            const int t = nA + (h >> 1);
+            gemm_tile<PAIR, TM / 2, NBW, VOUT>(c, (t % ntm) * TM + (h & 1) * (TM / 2), (t / ntm) * S::ROWS, g_lds);
+            return;
+        }
+    }
+    {
+        const int t = b < nA ? b : b - (nH >> 1);
+        gemm_tile<PAIR, TM, NBW, VOUT>(c, (t % ntm) * TM, (t / ntm) * S::ROWS, g_lds);
+    }
+}
+
 // ===========================================================================
 // Generic kernel: one lane per (token row, packed row), byte loads, any K.
 // ===========================================================================
@@ -559,11 +582,32 @@ __global__ __launch_bounds__(256) void k_generic(Contract c) {
 
 } // namespace
 
+static int cu_count() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus = n;
+    }
+    return cus;
+}
+
 template <bool PAIR, int TM, int NBW, bool VOUT>
 hipError_t go_big(const Contract &c, hipStream_t s) {
     using S = GemmShape<PAIR, TM, NBW>;
     const int ntm = (c.M + TM - 1) / TM;
     const int ntn = (c.R + S::ROWS - 1) / S::ROWS;
+    const int tiles = ntm * ntn;
+    // Half tiles for the CUs' second workgroups when the grid holds at least
+    // 2.5 tiles per CU (otherwise all tiles are full).
+    const int cus = cu_count();
+    const bool shift = TM % 64 == 0 && 2 * tiles >= 5 * cus;
+    const int nA = shift ? cus : tiles;
+    const int nH = shift ? cus : 0;
     const size_t lds = (size_t)kGStages * S::STAGE;
     static bool attr = false;   // the dynamic LDS above 64 KiB must be allowed once
     if (!attr) {
@@ -575,7 +619,7 @@ hipError_t go_big(const Contract &c, hipStream_t s) {
         }
         attr = true;
     }
-    hipLaunchKernelGGL((k_gemm_big<PAIR, TM, NBW, VOUT>), dim3(ntm * ntn), dim3(256), lds, s, c, ntm);
+    hipLaunchKernelGGL((k_gemm_big<PAIR, TM, NBW, VOUT>), dim3(tiles + nH / 2), dim3(256), lds, s, c, ntm, nA, nH);
     return hipGetLastError();
 }
 
@@ -612,11 +656,34 @@ hipError_t launch_gemm(const Contract &c0, int *qsum_ws, hipStream_t s) {
             if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
             c.qsum = qsum_ws;
         }
-        const int cus = 256;
-        if (c.pair) return go_big_v<true, 128, 2>(c, s);
-        const int mid = ((c.M + 127) / 128) * ((c.R + 63) / 64);
-        if (mid >= cus) return go_big_v<false, 128, 2>(c, s);
-        return go_big_v<false, 128, 1>(c, s);
+        // Tile shape: 128 or 96 tokens x 64 or 32 packed rows (the gate|up
+        // pair: 32 + 32), whichever finishes first in a model of the launch:
+        // rounds of two workgroups per CU, each round costing its tile's
+        // work, a round with at most one workgroup per CU 0.6 of it, divided
+        // by the shape's relative MFMA efficiency (smaller tiles reuse each
+        // operand fragment fewer times).
+        const int cus = cu_count();
+        auto cost = [&](int tm, int rows, double eff) {
+            const long tiles = (long)((c.M + tm - 1) / tm) * ((c.R + rows - 1) / rows);
+            double t = 0.0;
+            for (long left = tiles; left > 0; left -= 2L * cus)
+                t += (double)tm * rows * (left > cus ? 1.0 : 0.6);
+            return t / eff;
+        };
+        if (c.pair) {
+            if (cost(96, 32, 0.95) < cost(128, 32, 1.0)) return go_big_v<true, 96, 2>(c, s);
+            return go_big_v<true, 128, 2>(c, s);
+        }
+        const double cand[4] = {cost(128, 64, 1.0), cost(128, 32, 0.9), cost(96, 64, 0.95), cost(96, 32, 0.85)};
+        int pick = 0;
+        for (int i = 1; i < 4; ++i)
+            if (cand[i] < cand[pick]) pick = i;
+        switch (pick) {
+        case 0: return go_big_v<false, 128, 2>(c, s);
+        case 1: return go_big_v<false, 128, 1>(c, s);
+        case 2: return go_big_v<false, 96, 2>(c, s);
+        default: return go_big_v<false, 96, 1>(c, s);
+        }
     }
     const int ntm = (c.M + kBM - 1) / kBM;
     const int ntn = (c.R + kVR - 1) / kVR;
