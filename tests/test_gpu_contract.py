@@ -91,6 +91,32 @@ def test_gemv_input_kinds(x_kind):
     _check("gemv_w2a8", 4, 2560, (640, 160), x_kind=x_kind, seed=9)
 
 
+# The one-row decode kernel stages the row's codes in a 12288-byte LDS buffer:
+# K at that limit takes it, one k-range more takes the register kernel; fp32
+# rows carry half as many elements per load.
+@pytest.mark.parametrize("K,x_kind", [(12288, "bf16"), (12544, "bf16"), (12288, "f32"), (8192, "f32")])
+def test_gemv_one_row_kernel_k_limits(K, x_kind):
+    _check("gemv_w2a8", 1, K, (256,), x_kind=x_kind, seed=K % 97, check_all_dtypes=False)
+
+
+# Large single problems: each stream wave of the one-row kernel then holds the
+# most weight units (12 and 16 in flight, the two largest instantiations).
+# Codes are drawn uniformly from {-1, 0, 1} and packed by the oracle.
+@pytest.mark.parametrize("N,K", [(13312, 6144), (13312, 8192)])
+def test_gemv_one_row_kernel_many_units(N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    packed = oracle.pack(codes)
+    wms = np.array([0.0173], np.float32)
+    bits = synth.act_outliers_bf16(5, 1, K)
+    x_host = f32_of_bf16(bits)
+    _, _, A, y = oracle.bitlinear(x_host, codes, (N,), wms)
+    Ag = _run("gemv_w2a8", bf16_dev(bits), packed, wms, (N,), torch.int32)
+    assert_exact(host(Ag), A, "int32 accumulators")
+    yg = host(_run("gemv_w2a8", bf16_dev(bits), packed, wms, (N,), torch.float32))
+    assert_rows_close(yg, y, F32_TOL, "fp32 y")
+
+
 def test_gemv_long_k_repeated():
     """Long K over a single tile (one workgroup streams all of it); repeated
     calls on the same workspace stay exact."""
