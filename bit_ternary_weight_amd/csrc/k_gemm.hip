@@ -175,21 +175,19 @@ __global__ __launch_bounds__(256) void k_code_sums(const int8_t *q, int ldq, int
 }
 
 // ===========================================================================
-// Prefill kernel, large tiles (K a multiple of 256).
+// Prefill kernel, large tiles (K a multiple of kGK).
 // Workgroup: 4 waves in a 2 x 2 grid over a TM-token x TR-packed-row tile
 // (PAIR: TR/2 gate rows and the same TR/2 up rows).  Wave (wm, wn) owns TM/2
-// tokens (NA = TM/32 MFMA row tiles) and NBW 16-row B fragments; each packed
-// fragment is unpacked in registers into its four fields, so one fragment
-// feeds 4 * NA MFMAs (v_mfma_i32_16x16x64_i8) per 64-k step.
-// K advances in stages of 256 bytes per row, brought into a 3-stage LDS ring
-// with direct global->LDS loads (one 1 KB load = 4 rows x 256 bytes, whole
-// cache lines).  One workgroup barrier per stage: every wave waits for its own
-// loads of stage s, the barrier then publishes stage s and also certifies that
-// every wave is done with stage s-1, whose slot the loads of stage s+2 reuse.
-// Within a stage the operands of the next 64-k step are read from LDS while
-// the MFMAs of the current one run.  In LDS the 16-byte chunk c of tile row r
-// sits at position c ^ (r & 15), so a fragment read (16 rows, one chunk)
-// touches 16 distinct bank groups.
+// tokens (NA = TM/32 MFMA token tiles) and NBW 16-row weight fragments; each
+// packed fragment is unpacked in registers into its four fields, so one
+// fragment feeds 4 * NA MFMAs (v_mfma_i32_16x16x64_i8) per 64-k step.
+// K advances in stages of kGK bytes per row, brought into a 3-stage LDS ring
+// with direct global->LDS loads (one 1 KB load = 1024 / kGK whole rows).  One
+// workgroup barrier per stage: every wave waits for its own loads of stage s,
+// the barrier then publishes stage s and also certifies that every wave is
+// done with stage s-1, whose slot the loads of stage s+2 reuse.  In LDS the
+// 16-byte chunks of each tile row are XOR-swizzled (swz below) so that a
+// fragment read (16 rows, one chunk each) spreads over all bank groups.
 // ===========================================================================
 constexpr int kGK = 128;     // k bytes per stage
 constexpr int kGStages = 3;
@@ -224,27 +222,6 @@ __device__ __forceinline__ void g_dma16(const void *src, void *lds) {
 __device__ __forceinline__ void g_lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
     asm volatile("s_barrier" ::: "memory");
-}
-
-// 4 x 4 transpose across the lanes of a quad (lanes 4q .. 4q + 3, rq = lane
-// & 3): lane rq enters with v[j] = M[rq][j] and leaves with v[j] = M[j][rq].
-// Two exchange stages (partner rq ^ 1, then rq ^ 2) through DPP quad_perm.
-template <int CTRL>
-__device__ __forceinline__ float quad_dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ void quad_transpose(float v[4], int rq) {
-    float a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float t = quad_dpp<0xB1>(v[j ^ 1]);   // quad_perm [1,0,3,2]: lane rq ^ 1
-        a[j] = ((j ^ rq) & 1) ? t : v[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float t = quad_dpp<0x4E>(a[j ^ 2]);   // quad_perm [2,3,0,1]: lane rq ^ 2
-        v[j] = ((j ^ rq) & 2) ? t : a[j];
-    }
 }
 
 // Four consecutive outputs of one row from one lane (y 16-byte aligned for
@@ -316,13 +293,28 @@ __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const
         for (int i = 0; i < S::DPB; ++i) g_dma16(b_src[i] + k0, base + S::A_BYTES + (wave * S::DPB + i) * 1024);
     };
 
+    // Operand order: the unpacked weight fragment is the MFMA's first operand
+    // and the activations the second, so lane (g, lr) accumulates packed rows
+    // 4g .. 4g + 3 of a fragment for token lr: four consecutive output columns
+    // of one token row.  The accumulators start at -(code sum of the token) x
+    // (field scale), which removes the +1 of every code, and the field scale
+    // (1, 4, 16, 16) divides out exactly at the end.
+    int mtok[NA];
+    float am[NA];
     v4i acc[NA][NBW][4];
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
+    for (int i = 0; i < NA; ++i) {
+        mtok[i] = m0 + wm * (TM / 2) + i * 16 + lr;
+        const bool okm = mtok[i] < c.M;
+        const int qs = okm ? c.qsum[mtok[i]] : 0;
+        am[i] = okm ? c.a[mtok[i]] : 1.0f;
 #pragma unroll
-        for (int b = 0; b < NBW; ++b)
+        for (int f = 0; f < 4; ++f) {
+            const int v = -qs * (f == 0 ? 1 : (f == 1 ? 4 : 16));
 #pragma unroll
-            for (int f = 0; f < 4; ++f) acc[i][b][f] = v4i{0, 0, 0, 0};
+            for (int b = 0; b < NBW; ++b) acc[i][b][f] = v4i{v, v, v, v};
+        }
+    }
     // LDS byte offsets of this lane's fragment rows (chunk 0 excluded)
     int aoff[NA];
 #pragma unroll
@@ -378,10 +370,10 @@ __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const
                 }
 #pragma unroll
                 for (int i = 0; i < NA; ++i) {
-                    acc[i][b][0] = mfma16(af[i], f0, acc[i][b][0]);
-                    acc[i][b][1] = mfma16(af[i], f1, acc[i][b][1]);
-                    acc[i][b][2] = mfma16(af[i], f2, acc[i][b][2]);
-                    acc[i][b][3] = mfma16(af[i], f3, acc[i][b][3]);
+                    acc[i][b][0] = mfma16(f0, af[i], acc[i][b][0]);
+                    acc[i][b][1] = mfma16(f1, af[i], acc[i][b][1]);
+                    acc[i][b][2] = mfma16(f2, af[i], acc[i][b][2]);
+                    acc[i][b][3] = mfma16(f3, af[i], acc[i][b][3]);
                 }
             }
             if (ks + 1 < kGK / 64) {
@@ -393,19 +385,21 @@ __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const
         }
     }
 
-    // Epilogue.  A lane's packed rows -- hence its output columns, segments
-    // and weight scales -- do not depend on the token row, so they are looked
-    // up once; the factor w_mean / a is formed once per token row (IEEE fp32
-    // division, as the oracle), and each accumulator then costs a shift, a
-    // subtraction, a conversion and a multiply: float(A) * (w_mean / a).
+    // Epilogue.  Lane (g, lr) holds, per token fragment i, weight fragment b
+    // and field f, packed rows vr0 .. vr0 + 3 (vr0 a multiple of 4) of token
+    // mtok[i]; they sit in consecutive output columns when the segment sizes
+    // are multiples of 4 (checked by the launcher for the vector path).  The
+    // factor w_mean / a is formed once per (token, segment) with IEEE fp32
+    // division, as the oracle does; each output then costs a shift, a
+    // conversion and a multiply: float(A) * (w_mean / a).
     int colb[NBW][4];
     float wmb[NBW];
-    bool okb[NBW];
+    int vrb[NBW];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
-        const int vr = r0 + (PAIR ? wn * 16 : (wn * NBW + b) * 16) + lr;
-        okb[b] = vr < c.R;
-        const int vrc = okb[b] ? vr : 0;
+        const int vr0 = r0 + (PAIR ? wn * 16 : (wn * NBW + b) * 16) + 4 * g;
+        vrb[b] = vr0;
+        const int vrc = vr0 < c.R ? vr0 : 0;
         if (PAIR) {
             // gate (b = 0) and up (b = 1) share the row; p goes to column f*R + vr
 #pragma unroll
@@ -424,96 +418,62 @@ __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        // the code sums of this lane's four token rows (computed once per row
-        // by k_code_sums, not per tile)
-        int qsr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
-            qsr[j] = m < c.M ? c.qsum[m] : 0;
-        }
-        // undo the unpack's field scale, subtract the rows' code sums
-#pragma unroll
-        for (int b = 0; b < NBW; ++b)
+        const int m = mtok[i];
+        if (m >= c.M) continue;
+        const size_t rowo = (size_t)m * c.ldy;
+        if (PAIR) {
+            if (vrb[0] >= c.R) continue;
+            const float s0 = wmb[0] / am[i];
+            const float s1 = wmb[1] / am[i];
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
                 const int sh = f == 0 ? 0 : (f == 1 ? 2 : 4);
+                float v[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][b][f][j] = (acc[i][b][f][j] >> sh) - qsr[j];
-            }
-        if (VOUT) {
-            // Vector stores: scale in place (lane: column lr, token rows
-            // 4g + j), transpose each quad so that lane 4q + rq holds columns
-            // 4q .. 4q + 3 of token row 4g + rq, and store them at once.
-            // (The quad's columns are consecutive and inside one segment and
-            // below R: the launcher checks the segment sizes.)
-            const int rq = lr & 3;
-            const int mrow = m0 + wm * (TM / 2) + i * 16 + 4 * g + rq;   // this lane's row after the transpose
-            float am[4];
+                for (int j = 0; j < 4; ++j)
+                    v[j] = relu2_mul((float)(acc[i][0][f][j] >> sh) * s0, (float)(acc[i][1][f][j] >> sh) * s1);
+                if (VOUT) {
+                    store4(c.y, c.y_dt, rowo + colb[0][f], v);
+                } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
-                am[j] = m < c.M ? c.a[m] : 1.0f;
-            }
-            const size_t rowo = (size_t)(mrow < c.M ? mrow : 0) * c.ldy;
-            if (PAIR) {
-                float s0[4], s1[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    s0[j] = wmb[0] / am[j];
-                    s1[j] = wmb[1] / am[j];
-                }
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    float v[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        v[j] = relu2_mul((float)acc[i][0][f][j] * s0[j], (float)acc[i][1][f][j] * s1[j]);
-                    quad_transpose(v, rq);
-                    if (mrow < c.M && okb[0]) store4(c.y, c.y_dt, rowo + colb[0][f] - rq, v);
-                }
-            } else {
-#pragma unroll
-                for (int b = 0; b < NBW; ++b) {
-                    float sc[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sc[j] = wmb[b] / am[j];
-#pragma unroll
-                    for (int f = 0; f < 4; ++f) {
-                        float v[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            v[j] = c.y_dt == BL_I32 ? __int_as_float(acc[i][b][f][j]) : (float)acc[i][b][f][j] * sc[j];
-                        quad_transpose(v, rq);
-                        if (mrow < c.M && okb[b]) store4(c.y, c.y_dt, rowo + colb[b][f] - rq, v);
+                    for (int j = 0; j < 4; ++j) {
+                        if (vrb[0] + j >= c.R) break;
+                        const size_t idx = rowo + colb[0][f] + j;
+                        if (c.y_dt == BL_BF16) ((uint16_t *)c.y)[idx] = f32_to_bf16(v[j]);
+                        else ((float *)c.y)[idx] = v[j];
                     }
                 }
             }
-            continue;
-        }
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + wm * (TM / 2) + i * 16 + 4 * g + j;
-            if (m >= c.M) continue;
-            const float am = c.a[m];
-            const size_t rowo = (size_t)m * c.ldy;
-            if (PAIR) {
-                if (!okb[0]) continue;
-                const float s0 = wmb[0] / am;
-                const float s1 = wmb[1] / am;
+            for (int b = 0; b < NBW; ++b) {
+                if (vrb[b] >= c.R) continue;
+                if (VOUT) {
+                    const float sc = wmb[b] / am[i];
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const float pv = relu2_mul((float)acc[i][0][f][j] * s0, (float)acc[i][1][f][j] * s1);
-                    if (c.y_dt == BL_BF16) ((uint16_t *)c.y)[rowo + colb[0][f]] = f32_to_bf16(pv);
-                    else ((float *)c.y)[rowo + colb[0][f]] = pv;
-                }
-            } else {
+                    for (int f = 0; f < 4; ++f) {
+                        const int sh = f == 0 ? 0 : (f == 1 ? 2 : 4);
+                        float v[4];
 #pragma unroll
-                for (int b = 0; b < NBW; ++b) {
-                    if (!okb[b]) continue;
-                    const float sc = wmb[b] / am;
+                        for (int j = 0; j < 4; ++j) {
+                            const int A = acc[i][b][f][j] >> sh;
+                            v[j] = c.y_dt == BL_I32 ? __int_as_float(A) : (float)A * sc;
+                        }
+                        store4(c.y, c.y_dt, rowo + colb[b][f], v);
+                    }
+                } else {
+                    // scalar stores; the four rows may straddle a segment boundary
 #pragma unroll
-                    for (int f = 0; f < 4; ++f) store_out(c.y, c.y_dt, rowo + colb[b][f], acc[i][b][f][j], sc);
+                    for (int j = 0; j < 4; ++j) {
+                        const int vr = vrb[b] + j;
+                        if (vr >= c.R) break;
+#pragma unroll
+                        for (int f = 0; f < 4; ++f) {
+                            const int sh = f == 0 ? 0 : (f == 1 ? 2 : 4);
+                            const ColOf co = col_of(c.seg, vr, f);
+                            store_out(c.y, c.y_dt, rowo + co.col, acc[i][b][f][j] >> sh, c.w_mean[co.seg] / am[i]);
+                        }
+                    }
                 }
             }
         }
