@@ -1083,14 +1083,19 @@ int xkind_of(const GemvProblem &p) {
 //     out: a unit is 4 packed rows x 256 bytes of one tensor (two whole
 //     128-byte lines per row), 16 bytes per lane, loaded into registers with
 //     the non-temporal hint.  Once the codes are published they consume the
-//     units in order, each as soon as it has landed: lane L holds row L >> 4
-//     of the unit, bytes 16 (L & 15) .. +15 of the k-range; the four 2-bit
-//     fields of each byte, masked in place (codes + 1 times 1, 4, 16, 16), go
-//     through sdot4 with the matching activation codes.  Each row is then
-//     summed over its 16 lanes (DPP) into LDS.
+//     units in order, each as soon as it has landed.  Lane (g, l) = (L >> 4,
+//     L & 15) holds row l >> 2 of the unit, 16-byte chunk (l & 3) + 4 g of the
+//     k-range, and reads the activation codes of the same chunk.  The four
+//     2-bit fields, masked in place (codes + 1 times 1, 4, 16, 16), each go
+//     through one v_mfma_i32_16x16x64_i8 with the weights as the first operand
+//     (MFMA row l = unit row l >> 2, k-slice l & 3) and the codes as the
+//     second (column j holds k-slice j): entry (4 r + s, s) of the product is
+//     row r's sum over k-slice s, and the four slices of a row sit in the
+//     four lanes of one quad, summed with DPP at the end.  Per weight dword
+//     that is 5 VALU operations (the masks) instead of 9 with dot4 products;
+//     the matrix core's unused 15/16 cost nothing, it is otherwise idle.
 // Both roles meet at one barrier, after which the outputs are rescaled and
-// stored.  With one row, a 16 x 16 x 64 MFMA would waste 15/16 of its work;
-// the VALU dot products cost 9 operations per weight dword.
+// stored.
 // ===========================================================================
 constexpr int kV1MaxUnits = 16;   // weight units per stream wave, all in flight (4 VGPRs each)
 constexpr int kV1MaxRows = 32;    // packed rows per tensor per workgroup (4 * CS, NB * CS <= 8)
@@ -1099,13 +1104,16 @@ __device__ __forceinline__ v4i ld16_nt(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
 }
 
-// Sum over each 16-lane DPP row (every lane of the row gets the row's sum).
-__device__ __forceinline__ int row16_sum(int v) {
+// Sum over each quad of lanes (every lane of the quad gets the sum).
+__device__ __forceinline__ int quad_sum(int v) {
     v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_i<0x124>(v);   // row_ror:4
-    v += dpp_i<0x128>(v);   // row_ror:8
     return v;
+}
+
+// Entry m (0 .. 3, per lane) of a 4-vector, with selects.
+__device__ __forceinline__ int sel4_v(const v4i &a, int m) {
+    return m == 0 ? a[0] : (m == 1 ? a[1] : (m == 2 ? a[2] : a[3]));
 }
 
 template <bool PAIR, int XK, int NS>
@@ -1213,8 +1221,8 @@ void k_gemv_v1(GemvBatch b) {
             const int j = t + rot;
             return kr0 + kstep * (j >= ks ? j - ks : j);
         };
-        const int lr = lane >> 4;                  // row of the unit
-        const int lc = lane & 15;                  // 16-byte chunk of the k-range
+        const int lr = (lane & 15) >> 2;           // row of the unit
+        const int lc = (lane & 3) + 4 * (lane >> 4);   // 16-byte chunk of the k-range
         const int row = r0 + rg * 4 + lr;
         const size_t tbytes = (size_t)R * K;       // one tensor
         // placeholder offset inside the tensor (largest power of two <= its size)
@@ -1241,7 +1249,9 @@ void k_gemv_v1(GemvBatch b) {
         // the activation codes (the quantizer waves publish once per
         // reduction -- the norm's sum of squares, the absmax -- and once when done)
         wait_published<4>(qflag, NORM ? 3 : 2);
-        int acc0 = 0, acc1 = 0, acc2 = 0, acc3 = 0;
+        v4i acc[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
         // unit t is used once the t + 1 oldest unit loads have landed (the
         // compiler's wait: vmcnt(NS - 1 - t), loads complete in order)
 #pragma clang loop unroll(full)
@@ -1249,24 +1259,31 @@ void k_gemv_v1(GemvBatch b) {
             if (t < ks) {
                 const v4i w = wv[t];
                 const v4i xq = *reinterpret_cast<const v4i *>(q_s + kr_of(t) * kUnitK + 16 * lc);
+                v4i f0, f1, f2, f3;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     const uint32_t u = (uint32_t)w[d];
-                    acc0 = __builtin_amdgcn_sdot4((int)(u & 0x03030303u), xq[d], acc0, false);
-                    acc1 = __builtin_amdgcn_sdot4((int)(u & 0x0C0C0C0Cu), xq[d], acc1, false);
-                    acc2 = __builtin_amdgcn_sdot4((int)(u & 0x30303030u), xq[d], acc2, false);
-                    acc3 = __builtin_amdgcn_sdot4((int)((u >> 2) & 0x30303030u), xq[d], acc3, false);
+                    f0[d] = (int)(u & 0x03030303u);
+                    f1[d] = (int)(u & 0x0C0C0C0Cu);
+                    f2[d] = (int)(u & 0x30303030u);
+                    f3[d] = (int)((u >> 2) & 0x30303030u);
                 }
+                acc[0] = mfma16(f0, xq, acc[0]);
+                acc[1] = mfma16(f1, xq, acc[1]);
+                acc[2] = mfma16(f2, xq, acc[2]);
+                acc[3] = mfma16(f3, xq, acc[3]);
             }
         }
-        // row sums over the 16 lanes of each row; the field scale of the
-        // masked fields divides out exactly (every product carries it)
-        acc0 = row16_sum(acc0);
-        acc1 = row16_sum(acc1) >> 2;
-        acc2 = row16_sum(acc2) >> 4;
-        acc3 = row16_sum(acc3) >> 4;
-        if (lc == 0 && ks > 0) {
-            int *dst = red + (tsel * kV1MaxRows + rg * 4 + lr) * 4;
+        // Lane 16 r + s holds row r's k-slice s in entry s of each field's
+        // product (s < 4): pick it, sum the quad (DPP), and divide the field
+        // scale out exactly (every product carries it).
+        const int s4 = lane & 3;
+        const int acc0 = quad_sum(sel4_v(acc[0], s4));
+        const int acc1 = quad_sum(sel4_v(acc[1], s4)) >> 2;
+        const int acc2 = quad_sum(sel4_v(acc[2], s4)) >> 4;
+        const int acc3 = quad_sum(sel4_v(acc[3], s4)) >> 4;
+        if ((lane & 15) == 0 && ks > 0) {
+            int *dst = red + (tsel * kV1MaxRows + rg * 4 + (lane >> 4)) * 4;
             atomicAdd(dst + 0, acc0);
             atomicAdd(dst + 1, acc1);
             atomicAdd(dst + 2, acc2);
