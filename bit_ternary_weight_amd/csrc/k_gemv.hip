@@ -1334,25 +1334,20 @@ hipError_t launch_v1(GemvBatch &b, hipStream_t s) {
         }
         cus = n;
     }
-    // as launch_lds: even share of the weight bytes per CU, longest K first,
-    // each problem's tile the largest 4 * CS rows (CS = 8 / NB, ..., 1) that
-    // stays within 1.25x the share; CS shrinks further until no stream wave
-    // has more than kV1MaxUnits units (a row group's k-ranges split over
-    // 8 / (NB * CS) waves)
+    // Even share of the weight bytes per CU; each problem's tile is the
+    // largest 4 * CS rows (CS = 8 / NB, ..., 1) that stays within 1.25x the
+    // share; CS shrinks further until no stream wave has more than
+    // kV1MaxUnits units (a row group's k-ranges split over 8 / (NB * CS)
+    // waves).  Problems with the largest tiles take the lowest workgroup
+    // numbers: the device dispatches those first, and the last-dispatched
+    // workgroups, which can start microseconds late, get the smallest tiles.
     const size_t share = even_share(b, NB, cus) * 5 / 4;
     GemvBatch o = b;
-    int order[kMaxProblems];
-    for (int i = 0; i < b.n; ++i) order[i] = i;
-    for (int i = 1; i < b.n; ++i)
-        for (int j = i; j > 0 && b.p[order[j]].K > b.p[order[j - 1]].K; --j) {
-            const int t = order[j];
-            order[j] = order[j - 1];
-            order[j - 1] = t;
-        }
-    int tiles = 0, ns = 1;
+    int csv[kMaxProblems];
+    size_t tb[kMaxProblems];
+    int ns = 1;
     for (int i = 0; i < b.n; ++i) {
-        GemvProblem &q = o.p[i];
-        q = b.p[order[i]];
+        const GemvProblem &q = b.p[i];
         const int nkr = (q.K + kUnitK - 1) / kUnitK;
         auto units = [&](int cs) {
             const int kstep = kStreamWaves / (NB * cs);
@@ -1361,10 +1356,25 @@ hipError_t launch_v1(GemvBatch &b, hipStream_t s) {
         int cs = kStreamWaves / NB;
         while (cs > 1 && ((size_t)NB * 4 * cs * q.K > share || units(cs) > kV1MaxUnits)) cs >>= 1;
         if (units(cs) > kV1MaxUnits) return hipErrorInvalidValue;   // K beyond the one-row kernel
-        q.cs = cs;
-        q.tile0 = tiles;
-        tiles += (q.R + 4 * cs - 1) / (4 * cs);
+        csv[i] = cs;
+        tb[i] = (size_t)NB * 4 * cs * q.K;
         ns = units(cs) > ns ? units(cs) : ns;
+    }
+    int order[kMaxProblems];
+    for (int i = 0; i < b.n; ++i) order[i] = i;
+    for (int i = 1; i < b.n; ++i)
+        for (int j = i; j > 0 && tb[order[j]] > tb[order[j - 1]]; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    int tiles = 0;
+    for (int i = 0; i < b.n; ++i) {
+        GemvProblem &q = o.p[i];
+        q = b.p[order[i]];
+        q.cs = csv[order[i]];
+        q.tile0 = tiles;
+        tiles += (q.R + 4 * q.cs - 1) / (4 * q.cs);
     }
     o.ring_off = 0;
     switch (ns) {
