@@ -42,6 +42,14 @@ int check_hip(hipError_t e, const char *what) {
 
 size_t quant_scratch(int M, int K) { return align256((size_t)M * K) + align256((size_t)M * sizeof(float)); }
 
+// Decode calls that quantize outside the contraction kernel: codes (token
+// rows padded to a multiple of 16 for the tiled layout of the batched
+// kernel), scales, then the rows' code sums.
+size_t decode_codes(int M, int K) { return align256((size_t)((M + 15) / 16 * 16) * K); }
+size_t decode_quant_scratch(int M, int K) {
+    return decode_codes(M, K) + align256((size_t)M * sizeof(float)) + align256((size_t)M * sizeof(int));
+}
+
 bool fusable(int M, int K) {
     return M <= bl::kFuseMaxM && (size_t)M * K <= (size_t)bl::kFuseMaxBytes && K % 16 == 0;
 }
@@ -152,7 +160,7 @@ size_t decode_scratch(int n, const Call *calls) {
         const Call &c = calls[i];
         if (c.x_dt == BL_I8) continue;
         if (is_fast(c) && fused) continue;
-        need += quant_scratch(c.M, c.K);
+        need += decode_quant_scratch(c.M, c.K);
     }
     return need;
 }
@@ -212,21 +220,37 @@ int run_decode(const char *fn, int n, const Call *calls, char *ws, hipStream_t s
     // codes / scales of every call that is not quantized in a fused prologue
     const int8_t *qv[BL_MAX_PROBLEMS];
     const float *av[BL_MAX_PROBLEMS];
+    const int *sv[BL_MAX_PROBLEMS];
     int ldq[BL_MAX_PROBLEMS];
+    // The batched streaming kernel takes every call when all are quantized
+    // here and fit it; its codes are written tiled (code_offset).
+    bool mt = !fused;
+    int Ms[BL_MAX_PROBLEMS], Ks[BL_MAX_PROBLEMS];
+    for (int i = 0; i < n; ++i) {
+        const Call &c = calls[i];
+        mt = mt && c.x_dt != BL_I8 && is_fast(c) && aligned(c.packed, 16);
+        Ms[i] = c.M;
+        Ks[i] = c.K;
+    }
+    mt = mt && bl::gemv_mt_plan_ok(n, Ms, Ks);
     for (int i = 0; i < n; ++i) {
         const Call &c = calls[i];
         qv[i] = (const int8_t *)c.x;
         av[i] = c.a;
+        sv[i] = nullptr;
         ldq[i] = c.ldx;
         if (c.x_dt != BL_I8 && !(is_fast(c) && fused)) {
             int8_t *qw = (int8_t *)(ws + off);
-            float *aw = (float *)(ws + off + align256((size_t)c.M * c.K));
-            off += quant_scratch(c.M, c.K);
+            float *aw = (float *)(ws + off + decode_codes(c.M, c.K));
+            int *sw = (int *)(ws + off + decode_codes(c.M, c.K) + align256((size_t)c.M * sizeof(float)));
+            off += decode_quant_scratch(c.M, c.K);
             bl::QuantProblem &qp = qb.p[qb.n++];
             qp = bl::QuantProblem{};
-            qp.x = c.x; qp.q = qw; qp.a = aw; qp.x_dt = c.x_dt; qp.M = c.M; qp.K = c.K; qp.ldx = c.ldx;
+            qp.x = c.x; qp.q = qw; qp.a = aw; qp.qsum = sw; qp.x_dt = c.x_dt; qp.M = c.M; qp.K = c.K; qp.ldx = c.ldx;
+            qp.tile_m = mt ? (c.M + 15) / 16 * 16 : 0;
             qv[i] = qw;
             av[i] = aw;
+            sv[i] = sw;
             ldq[i] = c.K;
         }
     }
@@ -241,6 +265,8 @@ int run_decode(const char *fn, int n, const Call *calls, char *ws, hipStream_t s
         } else {
             bl::GemvProblem p = gemv_of(c, 0, qv[i], ldq[i], av[i]);
             p.x_dt = BL_I8;
+            p.qsum = sv[i];
+            p.qtile = mt ? (c.M + 15) / 16 * 16 : 0;
             b.p[b.n++] = p;
         }
     }
@@ -337,7 +363,7 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx, int8_t *q, f
 size_t bl_gemv_workspace_bytes(int M, int N, int K) {
     (void)N;
     if (M < 1 || K < 1) return 0;
-    return quant_scratch(M, K);
+    return decode_quant_scratch(M, K);
 }
 
 size_t bl_gemm_workspace_bytes(int M, int N, int K) {
@@ -362,7 +388,7 @@ size_t bl_gemv_batched_workspace_bytes(int n, const bl_gemv_problem *problems) {
     size_t need = 0;
     if (!problems || n < 1) return 0;
     for (int i = 0; i < n && i < BL_MAX_PROBLEMS; ++i)
-        if (problems[i].M > 0 && problems[i].K > 0) need += quant_scratch(problems[i].M, problems[i].K);
+        if (problems[i].M > 0 && problems[i].K > 0) need += decode_quant_scratch(problems[i].M, problems[i].K);
     return need;
 }
 

@@ -75,6 +75,22 @@ __device__ __forceinline__ void store_out(void *y, int y_dt, size_t idx, int A, 
     }
 }
 
+// Four consecutive outputs of one row from one lane (y 16-byte aligned for
+// fp32 / int32, 8-byte for bf16; the values of int32 output are the exact
+// accumulators carried as float bit patterns).
+__device__ __forceinline__ void store4(void *y, int y_dt, size_t idx, const float v[4]) {
+    if (y_dt == BL_F32) {
+        *reinterpret_cast<float4 *>((float *)y + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if (y_dt == BL_BF16) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2 *>((uint16_t *)y + idx) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<int4 *>((int32_t *)y + idx) =
+            make_int4(__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3]));
+    }
+}
+
 // ReLU^2(gate) * up on already-rescaled fp32 values (two roundings, no FMA).
 __device__ __forceinline__ float relu2_mul(float g, float u) {
     float gp = g > 0.0f ? g : 0.0f;
@@ -170,7 +186,15 @@ struct QuantProblem {
     float eps;
     int norm;           // 1: RMSNorm before quantizing
     int x_dt, M, K, ldx, row0;
+    int tile_m;         // 0: codes row-major [M,K]; else tiled, code_offset() with this token pitch
 };
+// Byte offset of code (m, k) in a code buffer: row-major [M,K] when tile_m is
+// 0, else tiled by 64-byte pieces of K: piece k / 64 holds tile_m token rows
+// of 64 codes each, so 16 tokens' codes of one piece are 1 KB contiguous.
+__host__ __device__ inline size_t code_offset(int m, int k, int K, int tile_m) {
+    return tile_m == 0 ? (size_t)m * K + k : ((size_t)(k >> 6) * tile_m + m) * 64 + (k & 63);
+}
+
 // Several row quantizations in one launch (the problems of a batched decode).
 struct QuantBatch {
     int n;
@@ -216,8 +240,12 @@ struct GemvProblem {
     float *dbg_a;       // optional: their scales [M]
     SegTab seg;
     int x_dt, ldx, M, K, R, y_dt, ldy, tile0, mode, pair;
-    int cs;             // streaming variant: column sets of 4 packed rows per workgroup
+    int cs;             // streaming variants: row groups per workgroup (4 rows; 16 in k_gemv_mt)
     float eps;
+    const int *qsum;    // mode 0: the rows' code sums [M] when the quantizer wrote them, else null
+    int qtile;          // mode 0: 0 = codes row-major with stride ldx; else tiled (code_offset) with this pitch
+    int vout;           // k_gemv_mt: four consecutive packed rows land in four consecutive,
+                        // 16-byte aligned output columns (vector stores)
 };
 
 struct GemvBatch {
@@ -228,6 +256,9 @@ struct GemvBatch {
 
 // Fills tile0 of every problem and launches; all problems must share `pair`.
 hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s);
+// Host check: decode problems with these M and K can go to the batched
+// streaming kernel (k_gemv_mt), whose codes the quantizer then writes tiled.
+bool gemv_mt_plan_ok(int n, const int *Ms, const int *Ks);
 // Prefill GEMM (any M).  The large-tile kernel reads the rows' code sums
 // instead of recomputing them per tile: from c.qsum when the caller has them,
 // else computed into qsum_ws (device scratch for M ints); with neither the

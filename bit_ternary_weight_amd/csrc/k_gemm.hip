@@ -224,22 +224,6 @@ __device__ __forceinline__ void g_lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Four consecutive outputs of one row from one lane (y 16-byte aligned for
-// fp32 / int32, 8-byte for bf16; the values of int32 output are the exact
-// accumulators carried as float bit patterns).
-__device__ __forceinline__ void store4(void *y, int y_dt, size_t idx, const float v[4]) {
-    if (y_dt == BL_F32) {
-        *reinterpret_cast<float4 *>((float *)y + idx) = make_float4(v[0], v[1], v[2], v[3]);
-    } else if (y_dt == BL_BF16) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2 *>((uint16_t *)y + idx) = make_uint2(lo, hi);
-    } else {
-        *reinterpret_cast<int4 *>((int32_t *)y + idx) =
-            make_int4(__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3]));
-    }
-}
-
 // One output tile: TM tokens from m0 x the packed rows from r0 (ROWS of them).
 template <bool PAIR, int TM, int NBW, bool VOUT>
 __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const int r0, unsigned char *g_lds) {

@@ -1409,6 +1409,300 @@ hipError_t launch_lds_kind(GemvBatch &b, int xk, hipStream_t s) {
     }
 }
 
+// ===========================================================================
+// Batched decode with precomputed codes (5 <= M <= 64, the quantizer has
+// written the int8 codes tiled by 64-byte pieces of K -- code_offset -- with
+// their scales and row code sums): a streaming
+// kernel in the manner of k_gemv_v1, with the tokens in the MFMA's 16
+// columns.  One 8-wave workgroup per tile of 16 * G packed rows of one
+// problem over all of K (G = 1, 2, 4, 8, sized to the CU's share of the
+// batch's weight bytes); the 8 / G waves of a 16-row group split its K into
+// interleaved 64-byte pieces.  A unit is 16 rows x 64 bytes of weights: lane
+// (g, l) loads row l, bytes 16 g .. +15 of the piece (non-temporal), and the
+// matching 16 code bytes of tokens l, 16 + l, ... (T token tiles of 16; in
+// the tiled layout a token tile's codes of one piece are 1 KB contiguous).
+// Each field of the unit, masked in place, goes through one
+// v_mfma_i32_16x16x64_i8 per token tile with the weights as the first
+// operand, so lane (g, c) accumulates packed rows 4 g .. 4 g + 3 for token c:
+// four consecutive output columns.  Units go in chunks of C, two chunks in
+// flight, every wave issuing the same number of loads on every path (the
+// compiler's waits stay exact; past its pieces a wave re-reads its last one).
+// The waves of a row group add their partial sums through LDS at the end.
+// ===========================================================================
+constexpr int kMtWaves = 8;
+constexpr int kMtMaxChunks = 8;
+
+__host__ __device__ constexpr int mt_chunk(int T) { return T == 1 ? 4 : (T == 2 ? 3 : 2); }
+
+// Rescale and store four consecutive packed rows vr0 .. vr0 + 3 (vr0 a
+// multiple of 4) of field f for token m from their exact sums s (codes + 1,
+// times the field scale).
+__device__ __forceinline__ void mt_emit4(const GemvProblem &p, int vr0, int m, int f, v4i s) {
+    if (m >= p.M || vr0 >= p.R) return;
+    const int sh = f == 0 ? 0 : (f == 1 ? 2 : 4);
+    const int qs = p.qsum[m];
+    int A[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) A[j] = (s[j] >> sh) - qs;
+    const float am = p.a[m];
+    const size_t rowo = (size_t)m * p.ldy;
+    if (p.vout) {
+        const ColOf co = col_of(p.seg, vr0, f);
+        const float sc = p.w_mean[co.seg] / am;   // IEEE fp32 division, as the oracle
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = p.y_dt == BL_I32 ? __int_as_float(A[j]) : (float)A[j] * sc;
+        store4(p.y, p.y_dt, rowo + co.col, v);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (vr0 + j >= p.R) break;
+            const ColOf co = col_of(p.seg, vr0 + j, f);
+            store_out(p.y, p.y_dt, rowo + co.col, A[j], p.w_mean[co.seg] / am);
+        }
+    }
+}
+
+template <int T, int NC>
+__global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
+    constexpr int C = mt_chunk(T);
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    v4i *part = reinterpret_cast<v4i *>(smem);   // [wave][token tile][field][lane]
+
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxProblems; ++i)
+        if (i < b.n && (int)blockIdx.x >= b.p[i].tile0) pi = i;
+    const GemvProblem &p = b.p[pi];
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int lr = lane & 15;
+    const int K = p.K;
+    const int lw = 3 - __builtin_ctz(p.cs);       // log2 waves per 16-row group
+    const int grp = wave >> lw;
+    const int kr0 = wave & ((1 << lw) - 1);
+    const int kstep = 1 << lw;
+    const int nkp = K >> 6;                       // 64-byte pieces per row
+    const int ks = kr0 < nkp ? (nkp - kr0 + kstep - 1) >> lw : 0;   // <= NC * C
+    // Unit t covers the wave's piece (t + rot) mod ks: waves and workgroups
+    // start at different offsets of their rows (the sum is order-free).
+    const int rot = ks > 0 ? (int)(((unsigned)blockIdx.x * 7u + (unsigned)wave * 3u) % (unsigned)ks) : 0;
+    auto kp_of = [&](int t) {
+        const int j = t + rot;
+        return kr0 + kstep * (j >= ks ? j - ks : j);
+    };
+    const int r0 = ((int)blockIdx.x - p.tile0) * 16 * p.cs;
+    const int row = r0 + 16 * grp + lr;
+    // rows past R and tokens past M read row 0 (in bounds) and are never stored
+    const uint8_t *wrow = p.P + (size_t)(row < p.R ? row : 0) * K + 16 * g;
+    // token tiles past this problem's codes re-read its last tile (in bounds,
+    // never stored)
+    const int8_t *q = reinterpret_cast<const int8_t *>(p.x);
+    const int qt = p.qtile;
+    const int8_t *qrow[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        const int uu = 16 * u < qt ? u : qt / 16 - 1;
+        qrow[u] = q + (size_t)(16 * uu + lr) * 64 + 16 * g;
+    }
+
+    v4i wv[2][C];
+    v4i cv[2][C][T];
+    auto issue = [&](int c, int buf) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = c * C + i;
+            const int tt = t < ks ? t : ks - 1;
+            const int kp = tt >= 0 ? kp_of(tt) : 0;
+            wv[buf][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wrow + 64 * (size_t)kp));
+#pragma unroll
+            for (int u = 0; u < T; ++u) cv[buf][i][u] = *reinterpret_cast<const v4i *>(qrow[u] + (size_t)kp * qt * 64);
+        }
+    };
+    v4i acc[T][4];
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[u][f] = v4i{0, 0, 0, 0};
+    issue(0, 0);
+    if (NC > 1) issue(1, 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int buf = c & 1;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (c * C + i < ks) {
+                v4i f0, f1, f2, f3;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t w = (uint32_t)wv[buf][i][d];
+                    f0[d] = (int)(w & 0x03030303u);
+                    f1[d] = (int)(w & 0x0C0C0C0Cu);
+                    f2[d] = (int)(w & 0x30303030u);
+                    f3[d] = (int)((w >> 2) & 0x30303030u);
+                }
+#pragma unroll
+                for (int u = 0; u < T; ++u) {
+                    acc[u][0] = mfma16(f0, cv[buf][i][u], acc[u][0]);
+                    acc[u][1] = mfma16(f1, cv[buf][i][u], acc[u][1]);
+                    acc[u][2] = mfma16(f2, cv[buf][i][u], acc[u][2]);
+                    acc[u][3] = mfma16(f3, cv[buf][i][u], acc[u][3]);
+                }
+            }
+        }
+        if (c + 2 < NC) issue(c + 2, buf);
+    }
+
+    // lane (g, c): packed rows 16 grp + 4 g + j, token 16 u + c
+    const int vr0 = r0 + 16 * grp + 4 * g;
+    if (lw == 0) {
+        // one wave per row group: its sums are complete
+#pragma unroll
+        for (int u = 0; u < T; ++u)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) mt_emit4(p, vr0, 16 * u + lr, f, acc[u][f]);
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) part[((wave * T + u) * 4 + f) * 64 + lane] = acc[u][f];
+    __syncthreads();
+    const int items = p.cs * T * 4 * 64;
+    for (int e = threadIdx.x; e < items; e += kMtWaves * 64) {
+        const int ln = e & 63;
+        const int f = (e >> 6) & 3;
+        const int u = (e >> 8) % T;
+        const int ge = (e >> 8) / T;
+        v4i sum = v4i{0, 0, 0, 0};
+        for (int kr = 0; kr < kstep; ++kr) sum += part[((((ge << lw) + kr) * T + u) * 4 + f) * 64 + ln];
+        mt_emit4(p, r0 + 16 * ge + 4 * (ln >> 4), 16 * u + (ln & 15), f, sum);
+    }
+}
+
+template <int T, int NC>
+hipError_t go_gemv_mt(GemvBatch &o, int tiles, hipStream_t s) {
+    const size_t lds = (size_t)kMtWaves * T * 4 * 64 * sizeof(v4i);
+    static size_t attr = 0;
+    if (lds > 65536 && attr < lds) {
+        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_mt<T, NC>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            e != hipSuccess)
+            return e;
+        attr = lds;
+    }
+    hipLaunchKernelGGL((k_gemv_mt<T, NC>), dim3(tiles), dim3(kMtWaves * 64), lds, s, o);
+    return hipGetLastError();
+}
+
+template <int T>
+hipError_t go_gemv_mt_nc(int nc, GemvBatch &o, int tiles, hipStream_t s) {
+    switch (nc) {
+    case 1: return go_gemv_mt<T, 1>(o, tiles, s);
+    case 2: return go_gemv_mt<T, 2>(o, tiles, s);
+    case 3: return go_gemv_mt<T, 3>(o, tiles, s);
+    case 4: return go_gemv_mt<T, 4>(o, tiles, s);
+    case 5: case 6: return go_gemv_mt<T, 6>(o, tiles, s);
+    default: return go_gemv_mt<T, 8>(o, tiles, s);
+    }
+}
+
+// Every problem fits k_gemv_mt: tiled codes with their row sums, no
+// gate|up pairing, K a multiple of 64, aligned weights.
+bool gemv_mt_ok(const GemvBatch &b) {
+    for (int i = 0; i < b.n; ++i) {
+        const GemvProblem &p = b.p[i];
+        if (p.mode != 0 || p.pair != 0 || p.qsum == nullptr || p.a == nullptr || p.M < 1 || p.M > 64 ||
+            p.qtile < 16 || p.qtile % 16 != 0 || p.qtile < p.M || p.K < 64 || p.K % 64 != 0 ||
+            ((uintptr_t)p.x % 16) != 0 || ((uintptr_t)p.P % 16) != 0)
+            return false;
+    }
+    return true;
+}
+
+bool gemv_mt_plan_ok(int n, const int *Ms, const int *Ks) {
+    int maxm = 1;
+    for (int i = 0; i < n; ++i) {
+        if (Ms[i] < 1 || Ms[i] > 64 || Ks[i] < 64 || Ks[i] % 64 != 0) return false;
+        maxm = Ms[i] > maxm ? Ms[i] : maxm;
+    }
+    const int C = mt_chunk((maxm + 15) / 16);
+    for (int i = 0; i < n; ++i)
+        if ((Ks[i] / 64 + kMtWaves - 1) / kMtWaves > kMtMaxChunks * C) return false;
+    return true;
+}
+
+// Tiles as for k_gemv_v1: the largest 16 * G rows (G = 8, 4, 2, 1) within
+// 1.25x the CU's even share of the weight bytes whose waves need at most
+// kMtMaxChunks chunks; largest tiles on the lowest workgroup numbers.
+// Returns hipErrorNotSupported when some problem's K needs more units.
+hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus = n;
+    }
+    int maxm = 1;
+    for (int i = 0; i < b.n; ++i) maxm = b.p[i].M > maxm ? b.p[i].M : maxm;
+    const int T = (maxm + 15) / 16;
+    const int C = mt_chunk(T);
+    const size_t share = even_share(b, 1, cus) * 5 / 4;
+    int gv[kMaxProblems];
+    size_t tb[kMaxProblems];
+    int maxu = 1;
+    for (int i = 0; i < b.n; ++i) {
+        const GemvProblem &q = b.p[i];
+        const int nkp = q.K / 64;
+        auto units = [&](int G) {
+            const int kstep = kMtWaves / G;
+            return (nkp + kstep - 1) / kstep;
+        };
+        int G = kMtWaves;
+        while (G > 1 && ((size_t)16 * G * q.K > share || units(G) > kMtMaxChunks * C)) G >>= 1;
+        if (units(G) > kMtMaxChunks * C) return hipErrorNotSupported;
+        gv[i] = G;
+        tb[i] = (size_t)16 * G * q.K;
+        maxu = units(G) > maxu ? units(G) : maxu;
+    }
+    int order[kMaxProblems];
+    for (int i = 0; i < b.n; ++i) order[i] = i;
+    for (int i = 1; i < b.n; ++i)
+        for (int j = i; j > 0 && tb[order[j]] > tb[order[j - 1]]; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    GemvBatch o = b;
+    int tiles = 0;
+    for (int i = 0; i < b.n; ++i) {
+        GemvProblem &q = o.p[i];
+        q = b.p[order[i]];
+        q.cs = gv[order[i]];
+        q.tile0 = tiles;
+        tiles += (q.R + 16 * q.cs - 1) / (16 * q.cs);
+        const size_t esz = q.y_dt == BL_BF16 ? 2 : 4;
+        bool v = q.R % 4 == 0 && q.ldy % 4 == 0 && ((uintptr_t)q.y % (4 * esz)) == 0;
+        for (int j = 0; j <= q.seg.n; ++j)
+            if (q.seg.roff[j] % 4 != 0) v = false;
+        q.vout = v ? 1 : 0;
+    }
+    o.ring_off = 0;
+    const int nc = (maxu + C - 1) / C;
+    switch (T) {
+    case 1: return go_gemv_mt_nc<1>(nc, o, tiles, s);
+    case 2: return go_gemv_mt_nc<2>(nc, o, tiles, s);
+    case 3: return go_gemv_mt_nc<3>(nc, o, tiles, s);
+    default: return go_gemv_mt_nc<4>(nc, o, tiles, s);
+    }
+}
+
 hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s) {
     if (b.p[0].mode != 0) {
         bool ok = true;
@@ -1440,6 +1734,14 @@ hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s) {
             }
             return hipSuccess;
         }
+    }
+    bool tiled = false;
+    for (int i = 0; i < b.n; ++i) tiled = tiled || b.p[i].qtile != 0;
+    if (tiled) {
+        // tiled codes are read by k_gemv_mt only
+        if (!gemv_mt_ok(b)) return hipErrorInvalidValue;
+        const hipError_t e = launch_gemv_mt(b, s);
+        return e == hipErrorNotSupported ? hipErrorInvalidValue : e;
     }
     int tiles = 0, max_m = 1, max_steps = 1;
     size_t qbytes = 0;

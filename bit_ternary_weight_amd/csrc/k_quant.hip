@@ -109,14 +109,12 @@ template <typename T, bool NORM, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(const T *__restrict__ x, int K, int ldx,
                                                          const float *__restrict__ g, float eps,
                                                          int8_t *__restrict__ q, float *__restrict__ a,
-                                                         int *__restrict__ qsum) {
+                                                         int *__restrict__ qsum, int tile_m) {
     __shared__ float redf[4];
     __shared__ double redd[4];
     __shared__ int redi[4];
     const int m = blockIdx.x;
     const T *row = x + (int64_t)m * ldx;
-    int8_t *qrow = q + (int64_t)m * K;
-
     float r = 1.0f;
     if (NORM) {
         double ss = 0.0;
@@ -176,13 +174,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const T *__restrict__ x
                 c[i] = quant1(t, s);
                 csum += c[i];
             }
-            *reinterpret_cast<uint32_t *>(qrow + k) = pack4(c[0], c[1], c[2], c[3]);
+            *reinterpret_cast<uint32_t *>(q + code_offset(m, k, K, tile_m)) = pack4(c[0], c[1], c[2], c[3]);
         }
     } else {
         for (int k = threadIdx.x; k < K; k += kThreads) {
             const int c = quant1(elem<T, NORM>(row, k, r, g), s);
             csum += c;
-            qrow[k] = (int8_t)c;
+            q[code_offset(m, k, K, tile_m)] = (int8_t)c;
         }
     }
     if (qsum) {
@@ -286,7 +284,6 @@ __global__ __launch_bounds__(kThreads) void k_rowq(QuantBatch qb) {
     const float s = 127.0f / fmaxf(amax, kFloor);   // IEEE fp32 division
     if (t == 0) p.a[m] = s;
 
-    int8_t *qrow = p.q + (int64_t)m * K;
     int csum = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -301,8 +298,9 @@ __global__ __launch_bounds__(kThreads) void k_rowq(QuantBatch qb) {
             w[h] = pack4(cc[0], cc[1], cc[2], cc[3]);
         }
         if (k < K) {
-            if (E == 8) *reinterpret_cast<uint2 *>(qrow + k) = make_uint2(w[0], w[E / 4 - 1]);
-            else *reinterpret_cast<uint32_t *>(qrow + k) = w[0];
+            int8_t *dst = p.q + code_offset(m, k, K, p.tile_m);   // 8 codes never straddle a 64-code piece
+            if (E == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[E / 4 - 1]);
+            else *reinterpret_cast<uint32_t *>(dst) = w[0];
         }
     }
     if (p.qsum) {
@@ -352,7 +350,7 @@ hipError_t launch_rowq(QuantBatch &qb, hipStream_t s) {
 
 template <bool NORM>
 hipError_t launch_rows(const void *x, int dt, int M, int K, int ldx, const float *g, float eps,
-                       int8_t *q, float *a, int *qsum, hipStream_t s) {
+                       int8_t *q, float *a, int *qsum, hipStream_t s, int tile_m = 0) {
     // Vector path: 4 elements per access, every row start aligned for it.
     const int esz = dt == BL_BF16 ? 2 : 4;
     const bool vec = (K % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % (4 * esz) == 0) &&
@@ -361,15 +359,15 @@ hipError_t launch_rows(const void *x, int dt, int M, int K, int ldx, const float
     if (dt == BL_BF16) {
         const uint16_t *xp = (const uint16_t *)x;
         if (vec)
-            hipLaunchKernelGGL((k_quant_rows<uint16_t, NORM, true>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum);
+            hipLaunchKernelGGL((k_quant_rows<uint16_t, NORM, true>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum, tile_m);
         else
-            hipLaunchKernelGGL((k_quant_rows<uint16_t, NORM, false>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum);
+            hipLaunchKernelGGL((k_quant_rows<uint16_t, NORM, false>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum, tile_m);
     } else {
         const float *xp = (const float *)x;
         if (vec)
-            hipLaunchKernelGGL((k_quant_rows<float, NORM, true>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum);
+            hipLaunchKernelGGL((k_quant_rows<float, NORM, true>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum, tile_m);
         else
-            hipLaunchKernelGGL((k_quant_rows<float, NORM, false>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum);
+            hipLaunchKernelGGL((k_quant_rows<float, NORM, false>), grid, block, 0, s, xp, K, ldx, g, eps, q, a, qsum, tile_m);
     }
     return hipGetLastError();
 }
@@ -383,8 +381,8 @@ hipError_t launch_one(const QuantProblem &p, hipStream_t s) {
         qb.p[0] = p;
         return launch_rowq(qb, s);
     }
-    if (p.norm) return launch_rows<true>(p.x, p.x_dt, p.M, p.K, p.ldx, p.gain, p.eps, p.q, p.a, p.qsum, s);
-    return launch_rows<false>(p.x, p.x_dt, p.M, p.K, p.ldx, nullptr, 0.0f, p.q, p.a, p.qsum, s);
+    if (p.norm) return launch_rows<true>(p.x, p.x_dt, p.M, p.K, p.ldx, p.gain, p.eps, p.q, p.a, p.qsum, s, p.tile_m);
+    return launch_rows<false>(p.x, p.x_dt, p.M, p.K, p.ldx, nullptr, 0.0f, p.q, p.a, p.qsum, s, p.tile_m);
 }
 
 } // namespace

@@ -131,7 +131,8 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx,
  *   y       out [M,N]; y_dtype BL_F32, BL_BF16, or BL_I32 (the exact int32
  *           accumulators A, no rescale).
  *   ws      scratch of bl_gemv_workspace_bytes / bl_gemm_workspace_bytes
- *           bytes (activation codes when the call quantizes x).
+ *           bytes (activation codes, scales and row code sums when the call
+ *           quantizes x).
  * K >= 1, K < 2^19 (bounds the int32 partial sums); N % 4 == 0.
  * ------------------------------------------------------------------------ */
 size_t bl_gemv_workspace_bytes(int M, int N, int K);
