@@ -1412,27 +1412,34 @@ hipError_t launch_lds_kind(GemvBatch &b, int xk, hipStream_t s) {
 // ===========================================================================
 // Batched decode with precomputed codes (5 <= M <= 64, the quantizer has
 // written the int8 codes tiled by 64-byte pieces of K -- code_offset -- with
-// their scales and row code sums): a streaming
-// kernel in the manner of k_gemv_v1, with the tokens in the MFMA's 16
-// columns.  One 8-wave workgroup per tile of 16 * G packed rows of one
-// problem over all of K (G = 1, 2, 4, 8, sized to the CU's share of the
-// batch's weight bytes); the 8 / G waves of a 16-row group split its K into
-// interleaved 64-byte pieces.  A unit is 16 rows x 64 bytes of weights: lane
-// (g, l) loads row l, bytes 16 g .. +15 of the piece (non-temporal), and the
-// matching 16 code bytes of tokens l, 16 + l, ... (T token tiles of 16; in
-// the tiled layout a token tile's codes of one piece are 1 KB contiguous).
-// Each field of the unit, masked in place, goes through one
-// v_mfma_i32_16x16x64_i8 per token tile with the weights as the first
-// operand, so lane (g, c) accumulates packed rows 4 g .. 4 g + 3 for token c:
-// four consecutive output columns.  Units go in chunks of C, two chunks in
-// flight, every wave issuing the same number of loads on every path (the
-// compiler's waits stay exact; past its pieces a wave re-reads its last one).
-// The waves of a row group add their partial sums through LDS at the end.
+// their scales and row code sums): a streaming kernel in the manner of
+// k_gemv_v1, with the tokens in the MFMA's 16 columns.  One 8-wave workgroup
+// per tile of 16 * G packed rows of one problem over all of K (G = 1, 2, 4,
+// 8, sized to the CU's share of the batch's weight bytes); the 8 / G waves of
+// a 16-row group split its K into interleaved 256-byte blocks.
+//   * A block (16 rows x 256 bytes) arrives as four whole-line loads of 4
+//     rows x 256 bytes (lane L: row L >> 4, bytes 16 (L & 15) .. +15;
+//     non-temporal) and goes through a 4 KB LDS buffer of the wave (16-byte
+//     chunk c of row r at position c ^ r: conflict-free both ways), from
+//     which lane (g, l) reads row l, bytes 16 g .. +15 of each 64-byte piece:
+//     the MFMA operand layout.  (Loading that layout directly from HBM, 16
+//     rows x 16 bytes per quarter wave, was 30 % slower.)
+//   * The codes of tokens l, 16 + l, ... (T token tiles of 16) for the same
+//     piece are 1 KB contiguous in the tiled layout, loaded straight into
+//     registers.
+//   * Each field of a piece, masked in place, goes through one
+//     v_mfma_i32_16x16x64_i8 per token tile with the weights as the first
+//     operand, so lane (g, c) accumulates packed rows 4 g .. 4 g + 3 for
+//     token c: four consecutive output columns.
+// Blocks go two in flight, every wave issuing the same number of loads on
+// every path (the compiler's waits stay exact; past its blocks a wave
+// re-reads its last one).  The waves of a row group add their partial sums
+// through LDS at the end.
 // ===========================================================================
 constexpr int kMtWaves = 8;
-constexpr int kMtMaxChunks = 8;
-
-__host__ __device__ constexpr int mt_chunk(int T) { return T == 1 ? 4 : (T == 2 ? 3 : 2); }
+constexpr int kMtMaxBlocks = 8;   // 256-byte blocks per wave (4 with 64 tokens: registers)
+__host__ __device__ constexpr int mt_max_blocks(int T) { return T >= 4 ? 4 : kMtMaxBlocks; }
+constexpr int kMtBufBytes = 4096; // a wave's transpose buffer
 
 // Rescale and store four consecutive packed rows vr0 .. vr0 + 3 (vr0 a
 // multiple of 4) of field f for token m from their exact sums s (codes + 1,
@@ -1463,11 +1470,9 @@ __device__ __forceinline__ void mt_emit4(const GemvProblem &p, int vr0, int m, i
     }
 }
 
-template <int T, int NC>
+template <int T, int NB>
 __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
-    constexpr int C = mt_chunk(T);
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    v4i *part = reinterpret_cast<v4i *>(smem);   // [wave][token tile][field][lane]
 
     int pi = 0;
 #pragma unroll
@@ -1484,21 +1489,25 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
     const int grp = wave >> lw;
     const int kr0 = wave & ((1 << lw) - 1);
     const int kstep = 1 << lw;
-    const int nkp = K >> 6;                       // 64-byte pieces per row
-    const int ks = kr0 < nkp ? (nkp - kr0 + kstep - 1) >> lw : 0;   // <= NC * C
-    // Unit t covers the wave's piece (t + rot) mod ks: waves and workgroups
+    const int nkb = K >> 8;                       // 256-byte blocks per row
+    const int ks = kr0 < nkb ? (nkb - kr0 + kstep - 1) >> lw : 0;   // <= NB
+    // Block t covers the wave's block (t + rot) mod ks: waves and workgroups
     // start at different offsets of their rows (the sum is order-free).
     const int rot = ks > 0 ? (int)(((unsigned)blockIdx.x * 7u + (unsigned)wave * 3u) % (unsigned)ks) : 0;
-    auto kp_of = [&](int t) {
+    auto kb_of = [&](int t) {
         const int j = t + rot;
         return kr0 + kstep * (j >= ks ? j - ks : j);
     };
     const int r0 = ((int)blockIdx.x - p.tile0) * 16 * p.cs;
-    const int row = r0 + 16 * grp + lr;
-    // rows past R and tokens past M read row 0 (in bounds) and are never stored
-    const uint8_t *wrow = p.P + (size_t)(row < p.R ? row : 0) * K + 16 * g;
-    // token tiles past this problem's codes re-read its last tile (in bounds,
-    // never stored)
+    // this lane's rows of the four loads of a block (rows past R read row 0:
+    // in bounds, never stored)
+    const uint8_t *wsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = r0 + 16 * grp + 4 * j + (lane >> 4);
+        wsrc[j] = p.P + (size_t)(row < p.R ? row : 0) * K + 16 * lr;
+    }
+    // token tiles past this problem's codes re-read its last tile
     const int8_t *q = reinterpret_cast<const int8_t *>(p.x);
     const int qt = p.qtile;
     const int8_t *qrow[T];
@@ -1507,19 +1516,30 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
         const int uu = 16 * u < qt ? u : qt / 16 - 1;
         qrow[u] = q + (size_t)(16 * uu + lr) * 64 + 16 * g;
     }
+    unsigned char *buf = smem + wave * kMtBufBytes;
+    // LDS offsets: the block's load j lands at row 4 j + (lane >> 4), chunk
+    // lane & 15; piece k of the block is read at row lr, chunk 4 k + g
+    int woff[4], roff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        woff[j] = r * 256 + 16 * ((lane & 15) ^ r);
+        roff[j] = lr * 256 + 16 * ((4 * j + g) ^ lr);
+    }
 
-    v4i wv[2][C];
-    v4i cv[2][C][T];
-    auto issue = [&](int c, int buf) {
+    v4i wv[2][4];
+    v4i cv[2][4][T];
+    auto issue = [&](int t, int sl) {
+        const int tt = t < ks ? t : ks - 1;
+        const int kb = tt >= 0 ? kb_of(tt) : 0;
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int t = c * C + i;
-            const int tt = t < ks ? t : ks - 1;
-            const int kp = tt >= 0 ? kp_of(tt) : 0;
-            wv[buf][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wrow + 64 * (size_t)kp));
+        for (int j = 0; j < 4; ++j)
+            wv[sl][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wsrc[j] + 256 * (size_t)kb));
 #pragma unroll
-            for (int u = 0; u < T; ++u) cv[buf][i][u] = *reinterpret_cast<const v4i *>(qrow[u] + (size_t)kp * qt * 64);
-        }
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int u = 0; u < T; ++u)
+                cv[sl][k][u] = *reinterpret_cast<const v4i *>(qrow[u] + (size_t)(4 * kb + k) * qt * 64);
     };
     v4i acc[T][4];
 #pragma unroll
@@ -1527,32 +1547,37 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[u][f] = v4i{0, 0, 0, 0};
     issue(0, 0);
-    if (NC > 1) issue(1, 1);
+    if (NB > 1) issue(1, 1);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int buf = c & 1;
+    for (int t = 0; t < NB; ++t) {
+        const int sl = t & 1;
+        if (t < ks) {
+            // this wave's LDS operations run in order: the reads below see
+            // these writes, and the next block's writes come after them
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            if (c * C + i < ks) {
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i *>(buf + woff[j]) = wv[sl][j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const v4i w = *reinterpret_cast<const v4i *>(buf + roff[k]);
                 v4i f0, f1, f2, f3;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const uint32_t w = (uint32_t)wv[buf][i][d];
-                    f0[d] = (int)(w & 0x03030303u);
-                    f1[d] = (int)(w & 0x0C0C0C0Cu);
-                    f2[d] = (int)(w & 0x30303030u);
-                    f3[d] = (int)((w >> 2) & 0x30303030u);
+                    const uint32_t x = (uint32_t)w[d];
+                    f0[d] = (int)(x & 0x03030303u);
+                    f1[d] = (int)(x & 0x0C0C0C0Cu);
+                    f2[d] = (int)(x & 0x30303030u);
+                    f3[d] = (int)((x >> 2) & 0x30303030u);
                 }
 #pragma unroll
                 for (int u = 0; u < T; ++u) {
-                    acc[u][0] = mfma16(f0, cv[buf][i][u], acc[u][0]);
-                    acc[u][1] = mfma16(f1, cv[buf][i][u], acc[u][1]);
-                    acc[u][2] = mfma16(f2, cv[buf][i][u], acc[u][2]);
-                    acc[u][3] = mfma16(f3, cv[buf][i][u], acc[u][3]);
+                    acc[u][0] = mfma16(f0, cv[sl][k][u], acc[u][0]);
+                    acc[u][1] = mfma16(f1, cv[sl][k][u], acc[u][1]);
+                    acc[u][2] = mfma16(f2, cv[sl][k][u], acc[u][2]);
+                    acc[u][3] = mfma16(f3, cv[sl][k][u], acc[u][3]);
                 }
             }
         }
-        if (c + 2 < NC) issue(c + 2, buf);
+        if (t + 2 < NB) issue(t + 2, sl);
     }
 
     // lane (g, c): packed rows 16 grp + 4 g + j, token 16 u + c
@@ -1565,6 +1590,9 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
             for (int f = 0; f < 4; ++f) mt_emit4(p, vr0, 16 * u + lr, f, acc[u][f]);
         return;
     }
+    // the partial sums reuse the transpose buffers: every wave must be done
+    __syncthreads();
+    v4i *part = reinterpret_cast<v4i *>(smem);   // [wave][token tile][field][lane]
 #pragma unroll
     for (int u = 0; u < T; ++u)
 #pragma unroll
@@ -1582,30 +1610,32 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
     }
 }
 
-template <int T, int NC>
+template <int T, int NB>
 hipError_t go_gemv_mt(GemvBatch &o, int tiles, hipStream_t s) {
-    const size_t lds = (size_t)kMtWaves * T * 4 * 64 * sizeof(v4i);
+    const size_t part = (size_t)kMtWaves * T * 4 * 64 * sizeof(v4i);
+    const size_t lds = part > (size_t)kMtWaves * kMtBufBytes ? part : (size_t)kMtWaves * kMtBufBytes;
     static size_t attr = 0;
     if (lds > 65536 && attr < lds) {
-        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_mt<T, NC>),
+        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_mt<T, NB>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             e != hipSuccess)
             return e;
         attr = lds;
     }
-    hipLaunchKernelGGL((k_gemv_mt<T, NC>), dim3(tiles), dim3(kMtWaves * 64), lds, s, o);
+    hipLaunchKernelGGL((k_gemv_mt<T, NB>), dim3(tiles), dim3(kMtWaves * 64), lds, s, o);
     return hipGetLastError();
 }
 
 template <int T>
-hipError_t go_gemv_mt_nc(int nc, GemvBatch &o, int tiles, hipStream_t s) {
-    switch (nc) {
+hipError_t go_gemv_mt_nb(int nb, GemvBatch &o, int tiles, hipStream_t s) {
+    switch (nb) {
     case 1: return go_gemv_mt<T, 1>(o, tiles, s);
     case 2: return go_gemv_mt<T, 2>(o, tiles, s);
     case 3: return go_gemv_mt<T, 3>(o, tiles, s);
     case 4: return go_gemv_mt<T, 4>(o, tiles, s);
-    case 5: case 6: return go_gemv_mt<T, 6>(o, tiles, s);
-    default: return go_gemv_mt<T, 8>(o, tiles, s);
+    default:
+        if constexpr (mt_max_blocks(T) > 4) return nb <= 6 ? go_gemv_mt<T, 6>(o, tiles, s) : go_gemv_mt<T, 8>(o, tiles, s);
+        else return hipErrorNotSupported;
     }
 }
 
@@ -1615,7 +1645,7 @@ bool gemv_mt_ok(const GemvBatch &b) {
     for (int i = 0; i < b.n; ++i) {
         const GemvProblem &p = b.p[i];
         if (p.mode != 0 || p.pair != 0 || p.qsum == nullptr || p.a == nullptr || p.M < 1 || p.M > 64 ||
-            p.qtile < 16 || p.qtile % 16 != 0 || p.qtile < p.M || p.K < 64 || p.K % 64 != 0 ||
+            p.qtile < 16 || p.qtile % 16 != 0 || p.qtile < p.M || p.K < 256 || p.K % 256 != 0 ||
             ((uintptr_t)p.x % 16) != 0 || ((uintptr_t)p.P % 16) != 0)
             return false;
     }
@@ -1625,18 +1655,18 @@ bool gemv_mt_ok(const GemvBatch &b) {
 bool gemv_mt_plan_ok(int n, const int *Ms, const int *Ks) {
     int maxm = 1;
     for (int i = 0; i < n; ++i) {
-        if (Ms[i] < 1 || Ms[i] > 64 || Ks[i] < 64 || Ks[i] % 64 != 0) return false;
+        if (Ms[i] < 1 || Ms[i] > 64 || Ks[i] < 256 || Ks[i] % 256 != 0) return false;
         maxm = Ms[i] > maxm ? Ms[i] : maxm;
     }
-    const int C = mt_chunk((maxm + 15) / 16);
+    const int cap = mt_max_blocks((maxm + 15) / 16);
     for (int i = 0; i < n; ++i)
-        if ((Ks[i] / 64 + kMtWaves - 1) / kMtWaves > kMtMaxChunks * C) return false;
+        if ((Ks[i] / 256 + kMtWaves - 1) / kMtWaves > cap) return false;
     return true;
 }
 
 // Tiles as for k_gemv_v1: the largest 16 * G rows (G = 8, 4, 2, 1) within
 // 1.25x the CU's even share of the weight bytes whose waves need at most
-// kMtMaxChunks chunks; largest tiles on the lowest workgroup numbers.
+// mt_max_blocks blocks; largest tiles on the lowest workgroup numbers.
 // Returns hipErrorNotSupported when some problem's K needs more units.
 hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s) {
     static int cus = 0;
@@ -1652,21 +1682,20 @@ hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s) {
     int maxm = 1;
     for (int i = 0; i < b.n; ++i) maxm = b.p[i].M > maxm ? b.p[i].M : maxm;
     const int T = (maxm + 15) / 16;
-    const int C = mt_chunk(T);
     const size_t share = even_share(b, 1, cus) * 5 / 4;
     int gv[kMaxProblems];
     size_t tb[kMaxProblems];
     int maxu = 1;
     for (int i = 0; i < b.n; ++i) {
         const GemvProblem &q = b.p[i];
-        const int nkp = q.K / 64;
+        const int nkb = q.K / 256;
         auto units = [&](int G) {
             const int kstep = kMtWaves / G;
-            return (nkp + kstep - 1) / kstep;
+            return (nkb + kstep - 1) / kstep;
         };
         int G = kMtWaves;
-        while (G > 1 && ((size_t)16 * G * q.K > share || units(G) > kMtMaxChunks * C)) G >>= 1;
-        if (units(G) > kMtMaxChunks * C) return hipErrorNotSupported;
+        while (G > 1 && ((size_t)16 * G * q.K > share || units(G) > mt_max_blocks(T))) G >>= 1;
+        if (units(G) > mt_max_blocks(T)) return hipErrorNotSupported;
         gv[i] = G;
         tb[i] = (size_t)16 * G * q.K;
         maxu = units(G) > maxu ? units(G) : maxu;
@@ -1694,12 +1723,11 @@ hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s) {
         q.vout = v ? 1 : 0;
     }
     o.ring_off = 0;
-    const int nc = (maxu + C - 1) / C;
     switch (T) {
-    case 1: return go_gemv_mt_nc<1>(nc, o, tiles, s);
-    case 2: return go_gemv_mt_nc<2>(nc, o, tiles, s);
-    case 3: return go_gemv_mt_nc<3>(nc, o, tiles, s);
-    default: return go_gemv_mt_nc<4>(nc, o, tiles, s);
+    case 1: return go_gemv_mt_nb<1>(maxu, o, tiles, s);
+    case 2: return go_gemv_mt_nb<2>(maxu, o, tiles, s);
+    case 3: return go_gemv_mt_nb<3>(maxu, o, tiles, s);
+    default: return go_gemv_mt_nb<4>(maxu, o, tiles, s);
     }
 }
 

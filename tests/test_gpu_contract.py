@@ -73,9 +73,11 @@ GEMV_SHAPES = [  # (M, K, seg_n)
     (5, 320, (36,)), (16, 512, (128,)), (17, 256, (68,)), (33, 192, (64,)), (64, 256, (256,)),
     (1, 2560, (2560, 640, 640)), (4, 2560, (64, 16, 16)), (64, 1024, (128, 32, 32)),
     (1, 6912, (2560,)), (1, 6912, (64,)), (2, 4096, (16,)), (64, 6912, (32,)),
-    # batched-decode streaming kernel: one 64-byte piece (most waves idle), a
-    # 2-row tensor, 49..64 rows over fused q|k|v, K not a multiple of 64
-    (8, 64, (16,)), (20, 128, (8,)), (50, 2560, (2560, 640, 640)), (16, 272, (32,)),
+    # batched-decode streaming kernel: one 256-byte block (most waves idle), a
+    # 10-row tensor, 49..64 rows over fused q|k|v; K not a multiple of 256
+    # (the register kernel)
+    (8, 256, (16,)), (24, 768, (40,)), (50, 2560, (2560, 640, 640)), (8, 64, (16,)), (20, 128, (8,)),
+    (16, 272, (32,)),
 ]
 
 
