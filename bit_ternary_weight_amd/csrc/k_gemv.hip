@@ -1239,13 +1239,18 @@ void k_gemv_v1(GemvBatch b) {
         // so the compiler's own waits for these registers are exact (a count
         // that varied by path would make it wait for all loads before the
         // first use).  Loads past ks re-read the lane's last unit (a cache hit).
-        wait_published<1>(xgo, 1);
+        // The first unit goes out at once; the rest only after every
+        // quantizer wave has issued its activation loads (one unit ahead of
+        // them measured 0.1 us faster per step, two units slower).
         v4i wv[NS];
-#pragma clang loop unroll(full)
-        for (int t = 0; t < NS; ++t) {
+        auto load_unit = [&](int t) {
             const int tt = t < ks ? t : ks - 1;
             wv[t] = ld16_nt(tt >= 0 ? unit_src(kr_of(tt)) : wbase + spread);
-        }
+        };
+        load_unit(0);
+        wait_published<1>(xgo, 1);
+#pragma clang loop unroll(full)
+        for (int t = 1; t < NS; ++t) load_unit(t);
         // the activation codes (the quantizer waves publish once per
         // reduction -- the norm's sum of squares, the absmax -- and once when done)
         wait_published<4>(qflag, NORM ? 3 : 2);
