@@ -1161,6 +1161,12 @@ void k_gemv_v1(GemvBatch b) {
     if (tid < Kp - K) q_s[K + tid] = 0;
     lds_barrier();
 
+    // The epilogue's per-output constants (column, w_mean / a, the row's
+    // code sum), formed by the storing threads while their weight units are
+    // still arriving rather than after the final barrier.
+    int ep_col = 0, ep_qsum = 0;
+    float ep_s0 = 0.0f, ep_s1 = 0.0f;
+
     if (wave >= SW) {
         // ---------------- quantizer waves ----------------
         constexpr int per = BF ? 8 : 4;
@@ -1254,6 +1260,22 @@ void k_gemv_v1(GemvBatch b) {
         // the activation codes (the quantizer waves publish once per
         // reduction -- the norm's sum of squares, the absmax -- and once when done)
         wait_published<4>(qflag, NORM ? 3 : 2);
+        if (tid < 4 * CS * 4) {
+            const int f = tid & 3;
+            const int vr = r0 + (tid >> 2);
+#pragma unroll
+            for (int w = 0; w < kQuantWaves; ++w) ep_qsum += sq_s[w];
+            const float av = a_s[0];
+            if (PAIR) {
+                ep_col = f * R + vr;
+                ep_s0 = wm_s[0] / av;   // IEEE fp32 division, as the oracle
+                ep_s1 = wm_s[1] / av;
+            } else {
+                const ColOf co = col_of(p.seg, vr < R ? vr : 0, f);
+                ep_col = co.col;
+                ep_s0 = wm_s[co.seg] / av;
+            }
+        }
         v4i acc[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
@@ -1297,20 +1319,22 @@ void k_gemv_v1(GemvBatch b) {
     }
     lds_barrier();
 
-    // rescale and store: e = (packed row, field); the codes were taken as
-    // c + 1, so the row's code sum comes off once
-    int qsum = 0;
-#pragma unroll
-    for (int w = 0; w < kQuantWaves; ++w) qsum += sq_s[w];
+    // rescale and store: thread e < 4 CS * 4 (all in stream waves 0 and 1)
+    // owns output e = (packed row, field); the codes were taken as c + 1, so
+    // the row's code sum comes off once
     const float a = a_s[0];
-    for (int e = tid; e < 4 * CS * 4; e += kLdsWaves * 64) {
-        const int f = e & 3;
-        const int prow = e >> 2;
-        const int vr = r0 + prow;
-        if (vr >= R) continue;
-        const int A = red[(0 * kV1MaxRows + prow) * 4 + f] - qsum;
-        const int U = PAIR ? red[(1 * kV1MaxRows + prow) * 4 + f] - qsum : 0;
-        emit_out(p.y, p.y_dt, p.ldy, PAIR, p.seg, R, wm_s, 0, vr, f, a, A, U);
+    if (tid < 4 * CS * 4 && r0 + (tid >> 2) < R) {
+        const int f = tid & 3;
+        const int prow = tid >> 2;
+        const int A = red[(0 * kV1MaxRows + prow) * 4 + f] - ep_qsum;
+        if (PAIR) {
+            const int U = red[(1 * kV1MaxRows + prow) * 4 + f] - ep_qsum;
+            const float pv = relu2_mul((float)A * ep_s0, (float)U * ep_s1);
+            if (p.y_dt == BL_BF16) ((uint16_t *)p.y)[ep_col] = f32_to_bf16(pv);
+            else ((float *)p.y)[ep_col] = pv;
+        } else {
+            store_out(p.y, p.y_dt, ep_col, A, ep_s0);
+        }
     }
     // The first tile's workgroup hands out the codes and scale (stage outputs
     // for checks).
