@@ -1460,9 +1460,9 @@ hipError_t launch_lds_kind(GemvBatch &b, int xk, hipStream_t s) {
 //     v_mfma_i32_16x16x64_i8 per token tile with the weights as the first
 //     operand, so lane (g, c) accumulates packed rows 4 g .. 4 g + 3 for
 //     token c: four consecutive output columns.
-// Blocks go two in flight, every wave issuing the same number of loads on
-// every path (the compiler's waits stay exact; past its blocks a wave
-// re-reads its last one).  The waves of a row group add their partial sums
+// Blocks go two in flight (with 64 tokens the codes one block ahead), every
+// wave issuing the same number of loads on every path (the compiler's waits
+// stay exact; past its blocks a wave re-reads its last one).  The waves of a row group add their partial sums
 // through LDS at the end.
 // ===========================================================================
 constexpr int kMtWaves = 8;
@@ -1472,19 +1472,19 @@ constexpr int kMtBufBytes = 4096; // a wave's transpose buffer
 
 // Rescale and store four consecutive packed rows vr0 .. vr0 + 3 (vr0 a
 // multiple of 4) of field f for token m from their exact sums s (codes + 1,
-// times the field scale).
-__device__ __forceinline__ void mt_emit4(const GemvProblem &p, int vr0, int m, int f, v4i s) {
+// times the field scale); qs, am: the token's code sum and scale, wm: the
+// weight scale of row vr0's segment (all loaded before the weight stream).
+__device__ __forceinline__ void mt_emit4(const GemvProblem &p, int vr0, int m, int f, v4i s, int qs, float am,
+                                         float wm) {
     if (m >= p.M || vr0 >= p.R) return;
     const int sh = f == 0 ? 0 : (f == 1 ? 2 : 4);
-    const int qs = p.qsum[m];
     int A[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) A[j] = (s[j] >> sh) - qs;
-    const float am = p.a[m];
     const size_t rowo = (size_t)m * p.ldy;
     if (p.vout) {
         const ColOf co = col_of(p.seg, vr0, f);
-        const float sc = p.w_mean[co.seg] / am;   // IEEE fp32 division, as the oracle
+        const float sc = wm / am;   // IEEE fp32 division, as the oracle
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = p.y_dt == BL_I32 ? __int_as_float(A[j]) : (float)A[j] * sc;
@@ -1502,6 +1502,9 @@ __device__ __forceinline__ void mt_emit4(const GemvProblem &p, int vr0, int m, i
 template <int T, int NB>
 __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ int qs_tab[64];
+    __shared__ float am_tab[64];
+    __shared__ float wm_tab[BL_MAX_SEGMENTS];
 
     int pi = 0;
 #pragma unroll
@@ -1545,6 +1548,21 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
         const int uu = 16 * u < qt ? u : qt / 16 - 1;
         qrow[u] = q + (size_t)(16 * uu + lr) * 64 + 16 * g;
     }
+    // The epilogue's inputs (token code sums and scales, segment weight
+    // scales) are loaded right after the first block, so that their latency
+    // is hidden; every lane loads the same number (clamped indices), so the
+    // compiler's waits for the stream stay exact.  (With 64 tokens the
+    // launcher never makes a wave own whole rows, and the registers are
+    // needed elsewhere: only the shared tables are loaded, at the end.)
+    constexpr bool kOwn = T < 4;
+    const int M = p.M;
+    int qs_l[kOwn ? T : 1];
+    float am_l[kOwn ? T : 1];
+    float wm_l = 0.0f;
+    const int mt_ = (int)threadIdx.x < M ? (int)threadIdx.x : M - 1;
+    const int sg_ = (int)threadIdx.x < p.seg.n ? (int)threadIdx.x : p.seg.n - 1;
+    int qs_t = 0;
+    float am_t = 0.0f, wm_t = 0.0f;
     unsigned char *buf = smem + wave * kMtBufBytes;
     // LDS offsets: the block's load j lands at row 4 j + (lane >> 4), chunk
     // lane & 15; piece k of the block is read at row lr, chunk 4 k + g
@@ -1556,14 +1574,24 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
         roff[j] = lr * 256 + 16 * ((4 * j + g) ^ lr);
     }
 
+    // Two blocks of weights in flight; the codes of two blocks as well below
+    // 64 tokens, of one block (issued a block ahead) with 64, whose code
+    // registers would not fit twice.
+    constexpr int CB = kOwn ? 2 : 1;
     v4i wv[2][4];
-    v4i cv[2][4][T];
-    auto issue = [&](int t, int sl) {
+    v4i cv[CB][4][T];
+    auto block_of = [&](int t) {
         const int tt = t < ks ? t : ks - 1;
-        const int kb = tt >= 0 ? kb_of(tt) : 0;
+        return tt >= 0 ? kb_of(tt) : 0;
+    };
+    auto issue_w = [&](int t, int sl) {
+        const int kb = block_of(t);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             wv[sl][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wsrc[j] + 256 * (size_t)kb));
+    };
+    auto issue_c = [&](int t, int sl) {
+        const int kb = block_of(t);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -1575,11 +1603,29 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
     for (int u = 0; u < T; ++u)
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[u][f] = v4i{0, 0, 0, 0};
-    issue(0, 0);
-    if (NB > 1) issue(1, 1);
+    issue_w(0, 0);
+    issue_c(0, 0);
+    if constexpr (kOwn) {
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+            const int m = 16 * u + lr < M ? 16 * u + lr : M - 1;
+            qs_l[u] = p.qsum[m];
+            am_l[u] = p.a[m];
+        }
+        const int vr0l = r0 + 16 * grp + 4 * g;
+        wm_l = p.w_mean[col_of(p.seg, vr0l < p.R ? vr0l : p.R - 1, 0).seg];
+        qs_t = p.qsum[mt_];
+        am_t = p.a[mt_];
+        wm_t = p.w_mean[sg_];
+    }
+    if (NB > 1) {
+        issue_w(1, 1);
+        if (CB == 2) issue_c(1, 1);
+    }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
         const int sl = t & 1;
+        const int cs = CB == 2 ? sl : 0;
         if (t < ks) {
             // this wave's LDS operations run in order: the reads below see
             // these writes, and the next block's writes come after them
@@ -1599,25 +1645,51 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
                 }
 #pragma unroll
                 for (int u = 0; u < T; ++u) {
-                    acc[u][0] = mfma16(f0, cv[sl][k][u], acc[u][0]);
-                    acc[u][1] = mfma16(f1, cv[sl][k][u], acc[u][1]);
-                    acc[u][2] = mfma16(f2, cv[sl][k][u], acc[u][2]);
-                    acc[u][3] = mfma16(f3, cv[sl][k][u], acc[u][3]);
+                    acc[u][0] = mfma16(f0, cv[cs][k][u], acc[u][0]);
+                    acc[u][1] = mfma16(f1, cv[cs][k][u], acc[u][1]);
+                    acc[u][2] = mfma16(f2, cv[cs][k][u], acc[u][2]);
+                    acc[u][3] = mfma16(f3, cv[cs][k][u], acc[u][3]);
                 }
             }
         }
-        if (t + 2 < NB) issue(t + 2, sl);
+        if (CB == 2) {
+            if (t + 2 < NB) {
+                issue_w(t + 2, sl);
+                issue_c(t + 2, sl);
+            }
+        } else {
+            if (t + 1 < NB) issue_c(t + 1, 0);
+            if (t + 2 < NB) issue_w(t + 2, sl);
+        }
+        if (kOwn && t == 0) {
+            // the shared tables of the epilogue (their loads, the oldest of
+            // the wave, have landed by now); read after the final barrier
+            if (threadIdx.x < 64) {
+                qs_tab[threadIdx.x] = qs_t;
+                am_tab[threadIdx.x] = am_t;
+            }
+            if (threadIdx.x < BL_MAX_SEGMENTS) wm_tab[threadIdx.x] = wm_t;
+        }
     }
 
     // lane (g, c): packed rows 16 grp + 4 g + j, token 16 u + c
     const int vr0 = r0 + 16 * grp + 4 * g;
-    if (lw == 0) {
-        // one wave per row group: its sums are complete
+    if constexpr (kOwn) {
+        if (lw == 0) {
+            // one wave per row group: its sums are complete
 #pragma unroll
-        for (int u = 0; u < T; ++u)
+            for (int u = 0; u < T; ++u)
 #pragma unroll
-            for (int f = 0; f < 4; ++f) mt_emit4(p, vr0, 16 * u + lr, f, acc[u][f]);
-        return;
+                for (int f = 0; f < 4; ++f) mt_emit4(p, vr0, 16 * u + lr, f, acc[u][f], qs_l[u], am_l[u], wm_l);
+            return;
+        }
+    }
+    if constexpr (!kOwn) {
+        if (threadIdx.x < 64) {
+            qs_tab[threadIdx.x] = p.qsum[mt_];
+            am_tab[threadIdx.x] = p.a[mt_];
+        }
+        if (threadIdx.x < BL_MAX_SEGMENTS) wm_tab[threadIdx.x] = p.w_mean[sg_];
     }
     // the partial sums reuse the transpose buffers: every wave must be done
     __syncthreads();
@@ -1635,7 +1707,10 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
         const int ge = (e >> 8) / T;
         v4i sum = v4i{0, 0, 0, 0};
         for (int kr = 0; kr < kstep; ++kr) sum += part[((((ge << lw) + kr) * T + u) * 4 + f) * 64 + ln];
-        mt_emit4(p, r0 + 16 * ge + 4 * (ln >> 4), 16 * u + (ln & 15), f, sum);
+        const int m = 16 * u + (ln & 15);
+        const int ve = r0 + 16 * ge + 4 * (ln >> 4);
+        const int mc = m < M ? m : M - 1;
+        mt_emit4(p, ve, m, f, sum, qs_tab[mc], am_tab[mc], wm_tab[col_of(p.seg, ve < p.R ? ve : p.R - 1, 0).seg]);
     }
 }
 
@@ -1722,7 +1797,7 @@ hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s) {
             const int kstep = kMtWaves / G;
             return (nkb + kstep - 1) / kstep;
         };
-        int G = kMtWaves;
+        int G = T < 4 ? kMtWaves : kMtWaves / 2;   // 64 tokens: at least two waves per row group
         while (G > 1 && ((size_t)16 * G * q.K > share || units(G) > mt_max_blocks(T))) G >>= 1;
         if (units(G) > mt_max_blocks(T)) return hipErrorNotSupported;
         gv[i] = G;
