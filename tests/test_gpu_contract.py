@@ -96,6 +96,13 @@ def test_gemv_input_kinds(x_kind):
     _check("gemv_w2a8", 4, 2560, (640, 160), x_kind=x_kind, seed=9)
 
 
+@pytest.mark.parametrize("M,x_kind", [(16, "i8"), (50, "i8"), (33, "f32"), (64, "f32")])
+def test_gemv_batched_input_kinds(M, x_kind):
+    """More than 4 rows: int8 codes given row-major take the register kernel,
+    fp32 rows are quantized into the tiled layout of the streaming kernel."""
+    _check("gemv_w2a8", M, 2560, (640, 160), x_kind=x_kind, seed=10 + M)
+
+
 # The one-row decode kernel stages the row's codes in a 12288-byte LDS buffer:
 # K at that limit takes it, one k-range more takes the register kernel; fp32
 # rows carry half as many elements per load.
