@@ -170,8 +170,8 @@ def main():
                     help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
-              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library has no "
+              "multi-GPU path (each GPU would hold its own shard of the weight rows)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
