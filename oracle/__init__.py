@@ -65,6 +65,8 @@ def _load():
         "ora_relu2_mul": (None, [P, P, L, P]),
         "ora_bitlinear": (None, [P, I, I, P, I, I, P, P, P, P, P, P]),
         "ora_ffn_chain": (None, [P, I, I, I, P, P, F, P, P, P, P, P, P, P, P, P, P]),
+        "ora_rope_f64": (None, [P, I, I, I, ctypes.c_double, P]),
+        "ora_attn_decode": (None, [P, P, P, I, I, I, I, P, P, I, ctypes.c_double, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -259,3 +261,30 @@ def layer(x, codes, w_means, eps=1e-5):
     ch = ffn_chain(y_o, gu, np.array([w_means["gate"], w_means["up"]], np.float32),
                    codes["down"], w_means["down"], eps=eps)
     return dict(q_in=q0, a_in=a0, y_qkv=y_qkv, q_o=q_o, a_o=a_o, y_o=y_o, **ch)
+
+
+def rope(x, pos, base):
+    """RoPE (split-half pairing) of x [heads, D] at position pos, fp64."""
+    x = _c(x, np.float64)
+    nh, D = x.shape
+    y = np.empty((nh, D), np.float64)
+    _load().ora_rope_f64(_p(x), nh, D, int(pos), float(base), _p(y))
+    return y
+
+
+def attn_decode(q, k_new, v_new, pos, k_cache, v_cache, base, n_heads, n_kv_heads):
+    """fp64 attention output [n_heads, D] of one new token at position pos.
+
+    q [H*D], k_new / v_new [KVH*D] fp32 (before RoPE); k_cache / v_cache
+    [KVH, max_seq, D] fp32, positions < pos used (rotated keys)."""
+    q = _c(np.asarray(q).reshape(-1), np.float32)
+    k_new = _c(np.asarray(k_new).reshape(-1), np.float32)
+    v_new = _c(np.asarray(v_new).reshape(-1), np.float32)
+    k_cache = _c(k_cache, np.float32)
+    v_cache = _c(v_cache, np.float32)
+    KVH, S, D = k_cache.shape
+    assert KVH == n_kv_heads and q.size == n_heads * D and 0 <= pos < S
+    out = np.empty((n_heads, D), np.float64)
+    _load().ora_attn_decode(_p(q), _p(k_new), _p(v_new), int(pos), n_heads, n_kv_heads, D,
+                            _p(k_cache), _p(v_cache), S, float(base), _p(out))
+    return out

@@ -316,3 +316,85 @@ void ora_ffn_chain(const float *h, int M, int H, int I,
 
     free(hn); free(Agu); free(ygu); free(gate); free(up); free(pn); free(Ad);
 }
+
+/* ===========================================================================
+ * Attention side of a decoder layer, one new token (decode).
+ *  [M] "BitNet" model documentation, "模型详情": the architecture uses rotary
+ *      position embeddings (RoPE); "BitNetConfig": 20 attention heads, 5
+ *      key/value heads (grouped-query attention: each key/value head serves an
+ *      equal group of consecutive query heads), hidden size 2560 (so a head
+ *      has 2560 / 20 = 128 dimensions), at most 2048 positions; the RoPE base
+ *      (rope_theta) is a parameter whose value the pages do not print.
+ * Readings (also in the design notes): the rotation pairs dimension i with
+ * i + D/2 of a head (the split-half convention), at angle
+ * pos * base^(-2i/D); the new token attends to every cached position and to
+ * itself (positions 0 .. pos); scores are scaled by 1/sqrt(D); softmax with
+ * the maximum subtracted.  Everything here is fp64; inputs and the cached
+ * keys/values are fp32.
+ * ------------------------------------------------------------------------ */
+
+/* RoPE of nh heads of D dims at position pos, fp64 in, fp64 out. */
+void ora_rope_f64(const double *x, int nh, int D, int pos, double base, double *y)
+{
+    const int h2 = D / 2;
+    for (int h = 0; h < nh; ++h)
+        for (int i = 0; i < h2; ++i) {
+            const double ang = (double)pos * pow(base, -2.0 * (double)i / (double)D);
+            const double c = cos(ang), s = sin(ang);
+            const double a = x[(int64_t)h * D + i], b = x[(int64_t)h * D + h2 + i];
+            y[(int64_t)h * D + i] = a * c - b * s;
+            y[(int64_t)h * D + h2 + i] = b * c + a * s;
+        }
+}
+
+/* Decode attention for one token.
+ *   q [H*D], k_new [KVH*D], v_new [KVH*D]: the new token's projections (fp32,
+ *     before RoPE);
+ *   k_cache, v_cache [KVH][max_seq][D] fp32: positions 0 .. pos-1 hold the
+ *     earlier tokens' rotated keys and their values (position pos is the new
+ *     token's, taken from k_new / v_new here);
+ *   out [H*D] fp64: softmax(q' k'^T / sqrt(D)) v per query head h, with key /
+ *     value head h / (H / KVH). */
+void ora_attn_decode(const float *q, const float *k_new, const float *v_new, int pos,
+                     int H, int KVH, int D, const float *k_cache, const float *v_cache,
+                     int max_seq, double base, double *out)
+{
+    const int G = H / KVH;
+    double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *qr = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *kd = (double *)malloc(sizeof(double) * (size_t)KVH * D);
+    double *kr = (double *)malloc(sizeof(double) * (size_t)KVH * D);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(pos + 1));
+    for (int64_t i = 0; i < (int64_t)H * D; ++i) qd[i] = (double)q[i];
+    for (int64_t i = 0; i < (int64_t)KVH * D; ++i) kd[i] = (double)k_new[i];
+    ora_rope_f64(qd, H, D, pos, base, qr);
+    ora_rope_f64(kd, KVH, D, pos, base, kr);
+    const double scale = 1.0 / sqrt((double)D);
+    for (int h = 0; h < H; ++h) {
+        const int g = h / G;
+        double mx = -INFINITY;
+        for (int j = 0; j <= pos; ++j) {
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) {
+                const double kv = j < pos ? (double)k_cache[((int64_t)g * max_seq + j) * D + d] : kr[(int64_t)g * D + d];
+                s += qr[(int64_t)h * D + d] * kv;
+            }
+            sc[j] = s * scale;
+            if (sc[j] > mx) mx = sc[j];
+        }
+        double l = 0.0;
+        for (int j = 0; j <= pos; ++j) {
+            sc[j] = exp(sc[j] - mx);
+            l += sc[j];
+        }
+        for (int d = 0; d < D; ++d) {
+            double o = 0.0;
+            for (int j = 0; j <= pos; ++j) {
+                const double vv = j < pos ? (double)v_cache[((int64_t)g * max_seq + j) * D + d] : (double)v_new[(int64_t)g * D + d];
+                o += sc[j] * vv;
+            }
+            out[(int64_t)h * D + d] = o / l;
+        }
+    }
+    free(qd); free(qr); free(kd); free(kr); free(sc);
+}

@@ -394,3 +394,104 @@ def test_ffn_chain_random_stagewise_consistency():
     assert (p == out["p"]).all()
     q2, a2, _, y = oracle.bitlinear(oracle.rmsnorm(p), cd, None, wd)
     assert (q2 == out["q2"]).all() and (a2 == out["a2"]).all() and (y == out["y"]).all()
+
+
+# ----------------------------------------------------------------------------- attention (decode)
+def _attn_inputs(seed, H, KVH, D, S):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal(H * D).astype(np.float32)
+    kn = rng.standard_normal(KVH * D).astype(np.float32)
+    vn = rng.standard_normal(KVH * D).astype(np.float32)
+    kc = rng.standard_normal((KVH, S, D)).astype(np.float32)
+    vc = rng.standard_normal((KVH, S, D)).astype(np.float32)
+    return q, kn, vn, kc, vc
+
+
+def test_rope_position_zero_is_identity_and_d2_is_a_plane_rotation():
+    x = np.random.default_rng(1).standard_normal((3, 16))
+    assert np.array_equal(oracle.rope(x, 0, 10000.0), x)
+    # D = 2: one pair rotated by exactly pos radians (base^0 = 1)
+    v = np.array([[0.6, -0.8]])
+    for pos in (1, 5, 77):
+        c, s = math.cos(pos), math.sin(pos)
+        assert np.allclose(oracle.rope(v, pos, 500000.0), [[0.6 * c + 0.8 * s, -0.8 * c + 0.6 * s]], atol=1e-15)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(2)
+    D = 128
+    x = rng.standard_normal((4, D))
+    y = rng.standard_normal((4, D))
+    for base in (10000.0, 500000.0):
+        r = oracle.rope(x, 37, base)
+        # each (i, i + D/2) pair keeps its length
+        assert np.allclose(r[:, :D // 2] ** 2 + r[:, D // 2:] ** 2, x[:, :D // 2] ** 2 + x[:, D // 2:] ** 2, rtol=1e-12)
+        # angles add
+        assert np.allclose(oracle.rope(oracle.rope(x, 11, base), 26, base), r, atol=1e-12)
+        # the dot product of a rotated query and key depends on their distance only
+        d1 = np.sum(oracle.rope(x, 40, base) * oracle.rope(y, 13, base), axis=1)
+        d2 = np.sum(oracle.rope(x, 1040, base) * oracle.rope(y, 1013, base), axis=1)
+        assert np.allclose(d1, d2, rtol=1e-9, atol=1e-9)
+
+
+def test_attn_single_position_returns_the_value():
+    H, KVH, D = 8, 2, 16
+    q, kn, vn, kc, vc = _attn_inputs(3, H, KVH, D, 4)
+    out = oracle.attn_decode(q, kn, vn, 0, kc, vc, 10000.0, H, KVH)
+    for h in range(H):
+        assert np.allclose(out[h], vn.reshape(KVH, D)[h // (H // KVH)], rtol=1e-14)
+
+
+def test_attn_equal_keys_average_the_values():
+    H, KVH, D, pos = 4, 1, 8, 5
+    q, kn, vn, kc, vc = _attn_inputs(4, H, KVH, D, 8)
+    # every cached key equal to the new token's rotated key: uniform weights
+    kr = oracle.rope(kn.reshape(KVH, D).astype(np.float64), pos, 10000.0)
+    kc[:, :pos, :] = kr.astype(np.float32)[:, None, :]
+    out = oracle.attn_decode(q, kn, vn, pos, kc, vc, 10000.0, H, KVH)
+    mean_v = (vc[0, :pos].astype(np.float64).sum(0) + vn.astype(np.float64)) / (pos + 1)
+    # the cached keys are the new key's fp32 rounding (<= 1 ulp apart): the
+    # weights are equal to ~1e-6
+    assert np.allclose(out, mean_v[None, :], rtol=0, atol=1e-5 * np.abs(mean_v).max())
+
+
+def test_attn_scale_and_softmax_closed_form():
+    # one cached key of zeros (score 0) and the new key with q.k = sqrt(D) ln 3
+    # (RoPE rotates q and the new key by the same angle: their dot product is
+    # unchanged): weights 1/4, 3/4
+    H, KVH, D, pos = 1, 1, 16, 1
+    q = np.zeros(D, np.float32)
+    q[0] = 1.0
+    kn = np.zeros(D, np.float32)
+    kn[0] = np.float32(math.sqrt(D) * math.log(3.0))
+    vn = np.random.default_rng(5).standard_normal(D).astype(np.float32)
+    kc = np.zeros((1, 4, D), np.float32)
+    vc = np.random.default_rng(6).standard_normal((1, 4, D)).astype(np.float32)
+    out = oracle.attn_decode(q, kn, vn, pos, kc, vc, 10000.0, H, KVH)
+    w1 = math.exp(float(kn[0]) / math.sqrt(D))      # exp(score of the new key), ~3
+    exp = (vc[0, 0].astype(np.float64) + w1 * vn.astype(np.float64)) / (1.0 + w1)
+    assert abs(w1 - 3.0) < 1e-6
+    assert np.allclose(out[0], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_attn_grouped_query_equals_repeated_heads():
+    # GQA with H / KVH query heads per key/value head equals multi-head
+    # attention with each key/value head repeated for its group
+    H, KVH, D, S, pos = 8, 2, 16, 12, 9
+    q, kn, vn, kc, vc = _attn_inputs(7, H, KVH, D, S)
+    G = H // KVH
+    gqa = oracle.attn_decode(q, kn, vn, pos, kc, vc, 10000.0, H, KVH)
+    rep = lambda a: np.repeat(a, G, axis=0)
+    mha = oracle.attn_decode(q, rep(kn.reshape(KVH, D)).reshape(-1), rep(vn.reshape(KVH, D)).reshape(-1), pos,
+                             rep(kc), rep(vc), 10000.0, H, H)
+    assert np.array_equal(gqa, mha)
+    # and per head it is the textbook softmax attention (numpy, fp64)
+    qr = oracle.rope(q.reshape(H, D), pos, 10000.0)
+    kr = oracle.rope(kn.reshape(KVH, D), pos, 10000.0)
+    for h in range(H):
+        g = h // G
+        keys = np.concatenate([kc[g, :pos].astype(np.float64), kr[g:g + 1]], axis=0)
+        vals = np.concatenate([vc[g, :pos].astype(np.float64), vn.reshape(KVH, D)[g:g + 1].astype(np.float64)], axis=0)
+        s = keys @ qr[h] / math.sqrt(D)
+        p = np.exp(s - s.max())
+        assert np.allclose(gqa[h], p @ vals / p.sum(), rtol=1e-12, atol=1e-12)
