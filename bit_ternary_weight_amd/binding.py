@@ -67,6 +67,9 @@ _SIGS = {
     "bl_ffn_chain_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_ffn_chain": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _I, _P, _S,
                           ctypes.POINTER(FfnDebug), _P]),
+    "bl_rope_table": (_I, [_I, _I, ctypes.c_double, _P, _P]),
+    "bl_attn_decode_workspace_bytes": (_S, [_I, _I]),
+    "bl_attn_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _S, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(raw, _name)
@@ -294,3 +297,41 @@ def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g
                             _ptr(y), _dt(y), _ptr(ws), ws.numel(),
                             ctypes.byref(dbg) if dbg is not None else None, _stream(dev)))
     return (y, stages) if debug else y
+
+
+def rope_table(max_pos: int, head_dim: int, base: float, device=None):
+    """(cos, sin) [max_pos, head_dim/2] fp32 of the library's RoPE table, on
+    `device` (host arrays when None)."""
+    import numpy as np
+    c = np.empty((max_pos, head_dim // 2), np.float32)
+    sn = np.empty((max_pos, head_dim // 2), np.float32)
+    _check(raw.bl_rope_table(int(max_pos), int(head_dim), float(base), c.ctypes.data_as(_P), sn.ctypes.data_as(_P)))
+    if device is None:
+        return c, sn
+    return torch.from_numpy(c).to(device), torch.from_numpy(sn).to(device)
+
+
+def attn_decode(q, k_new, v_new, pos, k_cache, v_cache, rope_cos, rope_sin, n_heads, n_kv_heads, out=None):
+    """Decode attention of one token at position `pos` (see bl_attn_decode):
+    q [n_heads*128], k_new / v_new [n_kv_heads*128] fp32; k_cache / v_cache
+    [n_kv_heads, max_seq, 128] fp32 (updated at `pos`); returns out [n_heads*128]."""
+    dev = _dev(q, k_new, v_new, k_cache, v_cache, rope_cos, rope_sin)
+    D = 128
+    kvh, max_seq, d = k_cache.shape
+    if d != D or kvh != n_kv_heads or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [n_kv_heads, max_seq, 128]")
+    for t, n, name in ((q, n_heads * D, "q"), (k_new, n_kv_heads * D, "k_new"), (v_new, n_kv_heads * D, "v_new")):
+        if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} elements")
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32")
+    if rope_cos.shape[0] < max_seq or rope_cos.shape[-1] != D // 2 or rope_sin.shape != rope_cos.shape:
+        raise ValueError("rope tables must be [>= max_seq, 64]")
+    if out is None:
+        out = torch.empty(n_heads * D, dtype=torch.float32, device=dev)
+    ws = workspace(dev, raw.bl_attn_decode_workspace_bytes(int(n_heads), int(max_seq)))
+    _check(raw.bl_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), int(pos), int(n_heads), int(n_kv_heads), D,
+                              _ptr(k_cache), _ptr(v_cache), int(max_seq), _ptr(rope_cos), _ptr(rope_sin),
+                              _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out

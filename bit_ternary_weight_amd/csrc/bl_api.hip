@@ -10,6 +10,7 @@
 //   any K that is not a multiple of 16: the plain kernel.
 // The workspace only holds per-call scratch (activation codes and scales,
 // intermediate chain tensors); nothing in it survives a call.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -550,6 +551,49 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I, const float *g
         e = bl::launch_gemm(c, qs, s);
     }
     return check_hip(e, "down launch");
+}
+
+int bl_rope_table(int max_pos, int head_dim, double base, float *cos_out, float *sin_out) {
+    g_err[0] = 0;
+    const char *fn = "bl_rope_table";
+    if (!cos_out || !sin_out) return fail(BL_ERR_NULL, "%s: output array is NULL", fn);
+    if (max_pos < 1 || head_dim < 2 || head_dim % 2 != 0 || !(base > 0.0))
+        return fail(BL_ERR_SHAPE, "%s: max_pos=%d head_dim=%d base=%g", fn, max_pos, head_dim, base);
+    const int h2 = head_dim / 2;
+    for (int p = 0; p < max_pos; ++p)
+        for (int i = 0; i < h2; ++i) {
+            const double ang = (double)p * pow(base, -2.0 * (double)i / (double)head_dim);
+            cos_out[(size_t)p * h2 + i] = (float)cos(ang);
+            sin_out[(size_t)p * h2 + i] = (float)sin(ang);
+        }
+    return BL_OK;
+}
+
+size_t bl_attn_decode_workspace_bytes(int n_heads, int max_seq) {
+    if (n_heads < 1 || max_seq < 1) return 0;
+    return align256(bl::attn_decode_part_bytes(n_heads, max_seq));
+}
+
+int bl_attn_decode(const float *q, const float *k_new, const float *v_new, int pos, int n_heads, int n_kv_heads,
+                   int head_dim, float *k_cache, float *v_cache, int max_seq, const float *rope_cos,
+                   const float *rope_sin, float *out, void *ws, size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_attn_decode";
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !rope_cos || !rope_sin || !out)
+        return fail(BL_ERR_NULL, "%s: a device pointer is NULL", fn);
+    if (head_dim != 128) return fail(BL_ERR_SHAPE, "%s: head_dim=%d (only 128 is supported)", fn, head_dim);
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > 4)
+        return fail(BL_ERR_SHAPE, "%s: n_heads=%d n_kv_heads=%d (a multiple, at most 4 per key/value head)", fn,
+                    n_heads, n_kv_heads);
+    if (max_seq < 1 || pos < 0 || pos >= max_seq)
+        return fail(BL_ERR_SHAPE, "%s: pos=%d max_seq=%d", fn, pos, max_seq);
+    const void *ptrs[] = {q, k_new, v_new, k_cache, v_cache, rope_cos, rope_sin, out};
+    for (const void *p : ptrs)
+        if (!aligned(p, 16)) return fail(BL_ERR_ALIGN, "%s: misaligned device pointer", fn);
+    if (int st = check_ws(fn, ws, ws_bytes, bl_attn_decode_workspace_bytes(n_heads, max_seq))) return st;
+    return check_hip(bl::launch_attn_decode(q, k_new, v_new, pos, n_heads, n_kv_heads, k_cache, v_cache, max_seq,
+                                            rope_cos, rope_sin, out, (float *)ws, (hipStream_t)stream),
+                     fn);
 }
 
 } // extern "C"

@@ -210,6 +210,42 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I,
                  void *y, int y_dtype, void *ws, size_t ws_bytes,
                  const bl_ffn_debug *dbg, bl_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * bl_rope_table / bl_attn_decode -- the attention side of a decoder layer
+ * for one new token (decode).  "BitNet" model documentation, "模型详情"
+ * (rotary position embeddings) and "BitNetConfig" (20 attention heads, 5
+ * key/value heads: grouped-query attention, each key/value head serving
+ * n_heads / n_kv_heads consecutive query heads; 128 dimensions per head;
+ * rope_theta a parameter).
+ *
+ * bl_rope_table (host only): cos / sin of pos * base^(-2i/head_dim) for
+ *   pos < max_pos, i < head_dim/2, computed in fp64 and rounded to fp32, into
+ *   host arrays cos_out / sin_out [max_pos][head_dim/2].  Copy them to the
+ *   device for bl_attn_decode.  Returns BL_OK or BL_ERR_NULL / BL_ERR_SHAPE.
+ *
+ * bl_attn_decode: for the token at position pos,
+ *   q [n_heads*128], k_new, v_new [n_kv_heads*128] fp32 device (before RoPE);
+ *   k_cache, v_cache [n_kv_heads][max_seq][128] fp32 device: positions
+ *     0 .. pos-1 hold the earlier tokens' rotated keys and their values; the
+ *     call writes the token's rotated key and its value at position pos;
+ *   rope_cos, rope_sin [max_seq][64] device (bl_rope_table);
+ *   out [n_heads*128] fp32 device: per query head h,
+ *     softmax_j(q'_h . k'_j / sqrt(128)) summed with v_j over j = 0 .. pos,
+ *     with the key/value head h / (n_heads / n_kv_heads) and q', k' rotated
+ *     by RoPE (dimension i paired with i + 64);
+ *   ws scratch of bl_attn_decode_workspace_bytes(n_heads, max_seq) bytes.
+ * head_dim must be 128; n_heads a multiple of n_kv_heads with at most 4
+ * query heads per key/value head; 0 <= pos < max_seq; all device pointers
+ * 16-byte aligned.  Arithmetic in fp32 (scores, exponentials, sums).
+ * ------------------------------------------------------------------------ */
+int bl_rope_table(int max_pos, int head_dim, double base, float *cos_out, float *sin_out);
+size_t bl_attn_decode_workspace_bytes(int n_heads, int max_seq);
+int bl_attn_decode(const float *q, const float *k_new, const float *v_new, int pos,
+                   int n_heads, int n_kv_heads, int head_dim,
+                   float *k_cache, float *v_cache, int max_seq,
+                   const float *rope_cos, const float *rope_sin,
+                   float *out, void *ws, size_t ws_bytes, bl_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -188,3 +188,38 @@ def test_last_error_is_per_thread(lib):
     assert seen["before"] == ""
     assert "NULL" in seen["after"]
     assert raw.bl_last_error().decode() == msg_main
+
+
+def _attn(raw, q=FAKE, kn=FAKE, vn=FAKE, pos=5, H=20, KVH=5, D=128, kc=FAKE, vc=FAKE, S=2048,
+          rc=FAKE, rs=FAKE, out=FAKE, ws=FAKE, ws_bytes=BIG):
+    return raw.bl_attn_decode(q, kn, vn, pos, H, KVH, D, kc, vc, S, rc, rs, out, ws, ws_bytes, None)
+
+
+def test_attn_decode_validation(lib):
+    raw = lib.raw
+    assert _attn(raw, q=None) == lib.BL_ERR_NULL
+    assert _attn(raw, out=None) == lib.BL_ERR_NULL
+    assert _attn(raw, D=64) == lib.BL_ERR_SHAPE
+    assert _attn(raw, H=20, KVH=3) == lib.BL_ERR_SHAPE          # not a multiple
+    assert _attn(raw, H=20, KVH=2) == lib.BL_ERR_SHAPE          # 10 query heads per key/value head
+    assert _attn(raw, pos=2048) == lib.BL_ERR_SHAPE
+    assert _attn(raw, pos=-1) == lib.BL_ERR_SHAPE
+    assert _attn(raw, kc=FAKE_MIS) == lib.BL_ERR_ALIGN
+    need = raw.bl_attn_decode_workspace_bytes(20, 2048)
+    assert need >= 20 * 32 * 130 * 4
+    assert _attn(raw, ws_bytes=need - 1) == lib.BL_ERR_WORKSPACE
+    assert _attn(raw, ws=None, ws_bytes=0) == lib.BL_ERR_WORKSPACE
+    assert raw.bl_attn_decode_workspace_bytes(0, 2048) == 0
+
+
+def test_rope_table_values(lib):
+    import numpy as np
+    c, s = lib.rope_table(64, 128, 500000.0)
+    pos = np.arange(64, dtype=np.float64)[:, None]
+    inv = 500000.0 ** (-2.0 * np.arange(64, dtype=np.float64) / 128.0)
+    assert np.array_equal(c, np.cos(pos * inv).astype(np.float32))
+    assert np.array_equal(s, np.sin(pos * inv).astype(np.float32))
+    raw = lib.raw
+    assert raw.bl_rope_table(4, 7, 10000.0, FAKE, FAKE) == lib.BL_ERR_SHAPE
+    assert raw.bl_rope_table(4, 8, 0.0, FAKE, FAKE) == lib.BL_ERR_SHAPE
+    assert raw.bl_rope_table(4, 8, 10000.0, None, FAKE) == lib.BL_ERR_NULL
