@@ -10,14 +10,22 @@
 // pos * base^(-i/64); the scores are scaled by 1/sqrt(128).
 //
 // Two launches.  k_attn_partial: one workgroup per (key/value head, chunk of
-// 64 positions).  It brings the chunk's keys and values into LDS with whole-
-// row loads (the new token's row from its rotated key and its value, which
-// the workgroup owning that position also stores into the caches), rotates
-// the group's queries, and per query head (one wave each) forms the 64
-// scores (a lane per position), their maximum, the exponentials and their
-// sum, then the weighted value sum (a lane per two dimensions).  It writes
-// (max, sum, 128 partial outputs) per head and chunk.  k_attn_combine: one
-// wave per query head merges the chunks (rescaling each by exp(max_c - max)).
+// 64 positions); it reads each cached key and value of its chunk once, into
+// registers, for all query heads of the group:
+//   keys    thread (dg = t & 15, ps = t >> 4) holds dimensions 4dg..4dg+3 and
+//           64+4dg..64+4dg+3 of positions ps, ps+16, ps+32, ps+48 (a 16-lane
+//           row group reads a whole 512-byte row in two loads);
+//   values  thread (dp = t & 63, pq = t >> 6) holds dimensions 2dp, 2dp+1 of
+//           positions 16pq .. 16pq+15 (a wave reads a whole row per load).
+// The rotated queries go through LDS; each thread forms its dimensions' part
+// of the scores of its 4 positions for every head and the row group sums
+// them (DPP reduce-scatter); one wave per head takes the maximum, the exponentials and
+// their sum over the chunk; each thread accumulates its 16 positions'
+// weighted values for every head and the four position quarters meet in LDS.
+// The workgroup owning pos rotates the token's key, stores it and the value
+// into the caches and uses them in place of its row.  It writes (max, sum,
+// 128 partial outputs) per head and chunk.  k_attn_combine: one workgroup per
+// query head merges the chunks (rescaling each by exp(max_c - max)).
 // Everything is fp32.
 #include "bl_common.h"
 
@@ -28,7 +36,6 @@ namespace {
 constexpr int kAttnD = 128;
 constexpr int kAttnChunk = 64;
 constexpr int kAttnMaxGroup = 4;                 // query heads per key/value head
-constexpr int kAttnKStride = kAttnD + 4;         // padded key rows: float4 reads of 64 rows spread over the banks
 constexpr int kAttnPart = kAttnD + 2;            // per head and chunk: max, sum, 128 outputs
 
 struct AttnArgs {
@@ -41,125 +48,270 @@ struct AttnArgs {
     float scale;
 };
 
+// Lane exchanges within a 16-lane DPP row.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm(1,0,3,2): lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm(2,3,0,1): lane ^ 2
+constexpr int kDppHalfMirror = 0x141;   // lane ^ 7 within the row
+constexpr int kDppMirror = 0x140;       // lane ^ 15 within the row
+
+// Four per-lane values s[0..3] (one per query head) summed over the 16 lanes
+// of a row, scattered: lane i of the row returns the sum of s[i >> 2].  Two
+// halving exchanges (lane ^ 15, then lane ^ 7) each keep half the heads and
+// send the other half; the quad then sums its four lanes.
+__device__ __forceinline__ float row16_reduce_scatter4(const float s[4], int i) {
+    const bool hi = (i & 8) != 0, hq = (i & 4) != 0;
+    const float k0 = hi ? s[2] : s[0], k1 = hi ? s[3] : s[1];
+    const float t0 = hi ? s[0] : s[2], t1 = hi ? s[1] : s[3];
+    const float u0 = k0 + dpp_f<kDppMirror>(t0);
+    const float u1 = k1 + dpp_f<kDppMirror>(t1);
+    const float kk = hq ? u1 : u0, tt = hq ? u0 : u1;
+    float v = kk + dpp_f<kDppHalfMirror>(tt);
+    v = v + dpp_f<kDppQuadSwap1>(v);
+    v = v + dpp_f<kDppQuadSwap2>(v);
+    return v;
+}
+
+// Maximum and sum over a whole wave (every lane active): the row by DPP, the
+// four rows through lane reads.
+__device__ __forceinline__ float wave64_max(float v) {
+    v = fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    const int b = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ float wave64_sum(float v) {
+    v = v + dpp_f<kDppQuadSwap1>(v);
+    v = v + dpp_f<kDppQuadSwap2>(v);
+    v = v + dpp_f<kDppHalfMirror>(v);
+    v = v + dpp_f<kDppMirror>(v);
+    const int b = __float_as_int(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
 __global__ __launch_bounds__(256) void k_attn_partial(AttnArgs a) {
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    float *Ks = sm;                                   // [64][kAttnKStride]
-    float *Vs = Ks + kAttnChunk * kAttnKStride;       // [64][128]
-    float *qs = Vs + kAttnChunk * kAttnD;             // [G][128]
-    float *ps = qs + kAttnMaxGroup * kAttnD;          // [G][64]
+    __shared__ float qs[kAttnMaxGroup][kAttnD];      // rotated queries
+    __shared__ float sc[kAttnMaxGroup][kAttnChunk];  // scaled scores
+    __shared__ float4 pw[kAttnChunk];                // probabilities, [position][head]
+    __shared__ float2 red[4][kAttnMaxGroup][64];     // weighted values per position quarter
+    __shared__ float knew[kAttnD], vnew[kAttnD];     // the token's rotated key and its value
     const int g = blockIdx.x;
     const int c = blockIdx.y;
     const int t = threadIdx.x;
     const int j0 = c * kAttnChunk;
     const int n = a.pos + 1 - j0 < kAttnChunk ? a.pos + 1 - j0 : kAttnChunk;   // valid rows (>= 1)
+    const int jn = a.pos - j0;                                                  // the token's row, if < 64
     const float *cs = a.rcos + (size_t)a.pos * (kAttnD / 2);
     const float *sn = a.rsin + (size_t)a.pos * (kAttnD / 2);
+    const float *kc = a.k_cache + (size_t)g * a.max_seq * kAttnD;
+    const float *vc = a.v_cache + (size_t)g * a.max_seq * kAttnD;
+    // Rows at or past pos are read from row pos - 1 instead (row 0 for an
+    // empty cache): loaded, given no weight, and never the row this call writes.
+    const int jmax = a.pos > 0 ? a.pos - 1 : 0;
 
-    // the group's rotated queries
-    if (t < a.G * (kAttnD / 2)) {
-        const int h = t >> 6, i = t & 63;
-        const float *qh = a.q + (size_t)(g * a.G + h) * kAttnD;
-        const float x0 = qh[i], x1 = qh[i + 64], co = cs[i], si = sn[i];
-        qs[h * kAttnD + i] = x0 * co - x1 * si;
-        qs[h * kAttnD + i + 64] = x1 * co + x0 * si;
-    }
-    // the chunk's keys and values (whole 512-byte rows, 32 lanes per row)
-    float *kc = a.k_cache + (size_t)g * a.max_seq * kAttnD;
-    float *vc = a.v_cache + (size_t)g * a.max_seq * kAttnD;
+    // every load first: queries and rotation (threads past the group read the
+    // last head's), keys, values
+    const int hq = min(t >> 6, a.G - 1), iq = t & 63;
+    const float *qh = a.q + (size_t)(g * a.G + hq) * kAttnD;
+    const float x0 = qh[iq], x1 = qh[iq + 64], co = cs[iq], si = sn[iq];
+    const int dg = t & 15, ps = t >> 4;
+    float4 kr[4][2];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int idx = t + 256 * r;
-        const int row = idx >> 5, c4 = idx & 31;
-        const int j = j0 + row;
-        float4 kv = make_float4(0.0f, 0.0f, 0.0f, 0.0f), vv = kv;
-        if (j < a.pos) {
-            kv = *reinterpret_cast<const float4 *>(kc + (size_t)j * kAttnD + 4 * c4);
-            vv = *reinterpret_cast<const float4 *>(vc + (size_t)j * kAttnD + 4 * c4);
-        }
-        *reinterpret_cast<float4 *>(Ks + row * kAttnKStride + 4 * c4) = kv;
-        *reinterpret_cast<float4 *>(Vs + row * kAttnD + 4 * c4) = vv;
+    for (int i = 0; i < 4; ++i) {
+        const float *row = kc + (size_t)min(j0 + ps + 16 * i, jmax) * kAttnD;
+        kr[i][0] = *reinterpret_cast<const float4 *>(row + 4 * dg);
+        kr[i][1] = *reinterpret_cast<const float4 *>(row + 64 + 4 * dg);
     }
-    // the new token's row: its rotated key and its value, also into the caches
-    const int jn = a.pos - j0;
-    if (jn < kAttnChunk) {
-        __syncthreads();   // its row of the staging above is overwritten here
+    const int dp = t & 63, pq = t >> 6;
+    float2 vr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        vr[i] = *reinterpret_cast<const float2 *>(vc + (size_t)min(j0 + 16 * pq + i, jmax) * kAttnD + 2 * dp);
+
+    qs[t >> 6][iq] = x0 * co - x1 * si;   // rows past the group hold copies no head reads
+    qs[t >> 6][iq + 64] = x1 * co + x0 * si;
+    if (jn < kAttnChunk) {   // the owner of pos: the token's rotated key and its value, also into the caches
         if (t < kAttnD / 2) {
             const float *kh = a.k_new + (size_t)g * kAttnD;
-            const float x0 = kh[t], x1 = kh[t + 64], co = cs[t], si = sn[t];
-            const float y0 = x0 * co - x1 * si, y1 = x1 * co + x0 * si;
-            Ks[jn * kAttnKStride + t] = y0;
-            Ks[jn * kAttnKStride + t + 64] = y1;
-            kc[(size_t)a.pos * kAttnD + t] = y0;
-            kc[(size_t)a.pos * kAttnD + t + 64] = y1;
+            const float y0 = kh[t] * cs[t] - kh[t + 64] * sn[t];
+            const float y1 = kh[t + 64] * cs[t] + kh[t] * sn[t];
+            knew[t] = y0;
+            knew[t + 64] = y1;
+            float *kw = a.k_cache + ((size_t)g * a.max_seq + a.pos) * kAttnD;
+            kw[t] = y0;
+            kw[t + 64] = y1;
         } else if (t < kAttnD) {
             const int d = t - 64;
             const float *vh = a.v_new + (size_t)g * kAttnD;
-            Vs[jn * kAttnD + d] = vh[d];
-            Vs[jn * kAttnD + d + 64] = vh[d + 64];
-            vc[(size_t)a.pos * kAttnD + d] = vh[d];
-            vc[(size_t)a.pos * kAttnD + d + 64] = vh[d + 64];
+            vnew[d] = vh[d];
+            vnew[d + 64] = vh[d + 64];
+            float *vw = a.v_cache + ((size_t)g * a.max_seq + a.pos) * kAttnD;
+            vw[d] = vh[d];
+            vw[d + 64] = vh[d + 64];
         }
     }
     __syncthreads();
-
-    const int w = t >> 6, lane = t & 63;
-    if (w >= a.G) return;
-    // scores of head w: lane = position
-    float s = -INFINITY;
-    if (lane < n) {
-        const float4 *kr = reinterpret_cast<const float4 *>(Ks + lane * kAttnKStride);
-        const float4 *qr = reinterpret_cast<const float4 *>(qs + w * kAttnD);
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int d4 = 0; d4 < kAttnD / 4; ++d4) {
-            const float4 kk = kr[d4], qq = qr[d4];
-            acc = acc + qq.x * kk.x;
-            acc = acc + qq.y * kk.y;
-            acc = acc + qq.z * kk.z;
-            acc = acc + qq.w * kk.w;
-        }
-        s = acc * a.scale;
-    }
-    const float m = wave_max(s);
-    const float p = lane < n ? expf(s - m) : 0.0f;
-    float l = p;
+    if (jn < kAttnChunk) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    ps[w * kAttnChunk + lane] = p;   // read back by this wave only: LDS operations of a wave complete in order
-    __builtin_amdgcn_wave_barrier();
-    // weighted values: lane = dimensions 2 lane, 2 lane + 1
-    float o0 = 0.0f, o1 = 0.0f;
-    for (int j = 0; j < n; ++j) {
-        const float pj = ps[w * kAttnChunk + j];
-        const float2 vv = *reinterpret_cast<const float2 *>(Vs + j * kAttnD + 2 * lane);
-        o0 = o0 + pj * vv.x;
-        o1 = o1 + pj * vv.y;
+        for (int i = 0; i < 4; ++i)
+            if (ps + 16 * i == jn) {
+                kr[i][0] = *reinterpret_cast<const float4 *>(&knew[4 * dg]);
+                kr[i][1] = *reinterpret_cast<const float4 *>(&knew[64 + 4 * dg]);
+            }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (16 * pq + i == jn) vr[i] = *reinterpret_cast<const float2 *>(&vnew[2 * dp]);
     }
-    float *pr = a.part + ((size_t)(g * a.G + w) * a.nchunks + c) * kAttnPart;
-    if (lane == 0) {
-        pr[0] = m;
-        pr[1] = l;
+
+    // scores: this thread's 8 dimensions of its 4 positions for every head
+    // (fused multiply-adds), reduce-scattered over the row group so that lane
+    // dg holds head dg >> 2's score; lanes of one quad store the same value
+    float4 qa[kAttnMaxGroup][2];
+#pragma unroll
+    for (int h = 0; h < kAttnMaxGroup; ++h) {
+        qa[h][0] = *reinterpret_cast<const float4 *>(&qs[h][4 * dg]);
+        qa[h][1] = *reinterpret_cast<const float4 *>(&qs[h][64 + 4 * dg]);
     }
-    pr[2 + 2 * lane] = o0;
-    pr[3 + 2 * lane] = o1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float sh[kAttnMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kAttnMaxGroup; ++h) {
+            float d = qa[h][0].x * kr[i][0].x;
+            d = fmaf(qa[h][0].y, kr[i][0].y, d);
+            d = fmaf(qa[h][0].z, kr[i][0].z, d);
+            d = fmaf(qa[h][0].w, kr[i][0].w, d);
+            d = fmaf(qa[h][1].x, kr[i][1].x, d);
+            d = fmaf(qa[h][1].y, kr[i][1].y, d);
+            d = fmaf(qa[h][1].z, kr[i][1].z, d);
+            d = fmaf(qa[h][1].w, kr[i][1].w, d);
+            sh[h] = d;
+        }
+        sc[dg >> 2][ps + 16 * i] = row16_reduce_scatter4(sh, dg) * a.scale;
+    }
+    __syncthreads();
+
+    // softmax over the chunk: wave w for head w
+    const int w = t >> 6, lane = t & 63;
+    if (w < a.G) {
+        const float sv = lane < n ? sc[w][lane] : -INFINITY;
+        const float m = wave64_max(sv);
+        const float p = lane < n ? expf(sv - m) : 0.0f;
+        const float l = wave64_sum(p);
+        reinterpret_cast<float *>(pw)[lane * 4 + w] = p;
+        if (lane == 0) {
+            float *pr = a.part + ((size_t)(g * a.G + w) * a.nchunks + c) * kAttnPart;
+            pr[0] = m;
+            pr[1] = l;
+        }
+    } else {
+        reinterpret_cast<float *>(pw)[lane * 4 + w] = 0.0f;   // heads past the group
+    }
+    __syncthreads();
+
+    // weighted values of this thread's 16 positions, every head
+    float2 acc[kAttnMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kAttnMaxGroup; ++h) acc[h] = make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float4 pv = pw[16 * pq + i];
+        acc[0].x = fmaf(pv.x, vr[i].x, acc[0].x);
+        acc[0].y = fmaf(pv.x, vr[i].y, acc[0].y);
+        acc[1].x = fmaf(pv.y, vr[i].x, acc[1].x);
+        acc[1].y = fmaf(pv.y, vr[i].y, acc[1].y);
+        acc[2].x = fmaf(pv.z, vr[i].x, acc[2].x);
+        acc[2].y = fmaf(pv.z, vr[i].y, acc[2].y);
+        acc[3].x = fmaf(pv.w, vr[i].x, acc[3].x);
+        acc[3].y = fmaf(pv.w, vr[i].y, acc[3].y);
+    }
+#pragma unroll
+    for (int h = 0; h < kAttnMaxGroup; ++h) red[pq][h][dp] = acc[h];
+    __syncthreads();
+    if (w < a.G) {   // thread (head w, dimensions 2 lane, 2 lane + 1) sums the quarters
+        float2 o = red[0][w][lane];
+#pragma unroll
+        for (int q4 = 1; q4 < 4; ++q4) {
+            const float2 r = red[q4][w][lane];
+            o.x = o.x + r.x;
+            o.y = o.y + r.y;
+        }
+        float *pr = a.part + ((size_t)(g * a.G + w) * a.nchunks + c) * kAttnPart;
+        pr[2 + 2 * lane] = o.x;
+        pr[3 + 2 * lane] = o.y;
+    }
 }
 
-__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+constexpr int kCombWaves = 8;
+constexpr int kCombBatch = 8;   // chunks a wave loads before it consumes any
+
+// One workgroup per query head; wave w takes chunks w, w + 8, ... in batches
+// of eight whose loads (max, sum, two outputs a lane) are all issued first,
+// keeping a running maximum and rescaling what it holds when the maximum
+// grows.  The eight waves' (max, sum, outputs) then meet in LDS.
+__global__ __launch_bounds__(64 * kCombWaves) void k_attn_combine(AttnArgs a) {
+    __shared__ float red[kCombWaves][kAttnPart];
     const int h = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const float *pr = a.part + (size_t)h * a.nchunks * kAttnPart;
-    float M = -INFINITY;
-    for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, pr[(size_t)c * kAttnPart]);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int c = 0; c < a.nchunks; ++c) {
-        const float *pc = pr + (size_t)c * kAttnPart;
-        const float e = expf(pc[0] - M);
-        L = L + e * pc[1];
-        o0 = o0 + e * pc[2 + 2 * lane];
-        o1 = o1 + e * pc[3 + 2 * lane];
+    float Mw = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int c0 = w; c0 < a.nchunks; c0 += kCombBatch * kCombWaves) {
+        float mm[kCombBatch], ll[kCombBatch];
+        float2 ov[kCombBatch];
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) {
+            const int c = c0 + i * kCombWaves;
+            const float *pc = pr + (size_t)(c < a.nchunks ? c : c0) * kAttnPart;
+            mm[i] = pc[0];
+            ll[i] = pc[1];
+            ov[i] = *reinterpret_cast<const float2 *>(pc + 2 + 2 * lane);
+        }
+        float mb = Mw;
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) mb = fmaxf(mb, mm[i]);
+        const float r = expf(Mw - mb);   // 0 before the first batch
+        L = L * r;
+        o0 = o0 * r;
+        o1 = o1 * r;
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) {
+            // a slot past the last chunk re-read chunk c0: it leaves the
+            // maximum unchanged and gets no weight
+            const float e = c0 + i * kCombWaves < a.nchunks ? expf(mm[i] - mb) : 0.0f;
+            L = L + e * ll[i];
+            o0 = o0 + e * ov[i].x;
+            o1 = o1 + e * ov[i].y;
+        }
+        Mw = mb;
     }
-    a.out[(size_t)h * kAttnD + 2 * lane] = o0 / L;
-    a.out[(size_t)h * kAttnD + 2 * lane + 1] = o1 / L;
+    red[w][2 + 2 * lane] = o0;
+    red[w][3 + 2 * lane] = o1;
+    if (lane == 0) {
+        red[w][0] = Mw;
+        red[w][1] = L;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float M = red[0][0];
+#pragma unroll
+    for (int i = 1; i < kCombWaves; ++i) M = fmaxf(M, red[i][0]);
+    float sl = 0.0f, s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCombWaves; ++i) {
+        const float e = expf(red[i][0] - M);   // 0 for a wave without chunks
+        sl = sl + e * red[i][1];
+        s0 = s0 + e * red[i][2 + 2 * lane];
+        s1 = s1 + e * red[i][3 + 2 * lane];
+    }
+    a.out[(size_t)h * kAttnD + 2 * lane] = s0 / sl;
+    a.out[(size_t)h * kAttnD + 2 * lane + 1] = s1 / sl;
 }
 
 } // namespace
@@ -180,19 +332,9 @@ hipError_t launch_attn_decode(const float *q, const float *k_new, const float *v
     a.pos = pos; a.H = H; a.KVH = KVH; a.G = H / KVH; a.max_seq = max_seq;
     a.nchunks = (pos + 1 + kAttnChunk - 1) / kAttnChunk;
     a.scale = 1.0f / sqrtf((float)kAttnD);
-    const size_t lds = sizeof(float) * ((size_t)kAttnChunk * kAttnKStride + (size_t)kAttnChunk * kAttnD +
-                                        (size_t)kAttnMaxGroup * kAttnD + (size_t)kAttnMaxGroup * kAttnChunk);
-    static bool attr = false;
-    if (!attr) {
-        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_partial),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            e != hipSuccess)
-            return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL(k_attn_partial, dim3(KVH, a.nchunks), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(k_attn_partial, dim3(KVH, a.nchunks), dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_combine, dim3(H), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_attn_combine, dim3(H), dim3(64 * kCombWaves), 0, s, a);
     return hipGetLastError();
 }
 
