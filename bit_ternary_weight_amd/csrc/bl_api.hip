@@ -571,7 +571,7 @@ int bl_rope_table(int max_pos, int head_dim, double base, float *cos_out, float 
 
 size_t bl_attn_decode_workspace_bytes(int n_heads, int max_seq) {
     if (n_heads < 1 || max_seq < 1) return 0;
-    return align256(bl::attn_decode_part_bytes(n_heads, max_seq));
+    return align256(bl::attn_decode_workspace_bytes(n_heads, max_seq));
 }
 
 int bl_attn_decode(const float *q, const float *k_new, const float *v_new, int pos, int n_heads, int n_kv_heads,
@@ -585,14 +585,15 @@ int bl_attn_decode(const float *q, const float *k_new, const float *v_new, int p
     if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > 4)
         return fail(BL_ERR_SHAPE, "%s: n_heads=%d n_kv_heads=%d (a multiple, at most 4 per key/value head)", fn,
                     n_heads, n_kv_heads);
-    if (max_seq < 1 || pos < 0 || pos >= max_seq)
-        return fail(BL_ERR_SHAPE, "%s: pos=%d max_seq=%d", fn, pos, max_seq);
+    if (max_seq < 1 || max_seq > bl::attn_decode_max_seq() || pos < 0 || pos >= max_seq)
+        return fail(BL_ERR_SHAPE, "%s: pos=%d max_seq=%d (max_seq at most %d)", fn, pos, max_seq,
+                    bl::attn_decode_max_seq());
     const void *ptrs[] = {q, k_new, v_new, k_cache, v_cache, rope_cos, rope_sin, out};
     for (const void *p : ptrs)
         if (!aligned(p, 16)) return fail(BL_ERR_ALIGN, "%s: misaligned device pointer", fn);
     if (int st = check_ws(fn, ws, ws_bytes, bl_attn_decode_workspace_bytes(n_heads, max_seq))) return st;
     return check_hip(bl::launch_attn_decode(q, k_new, v_new, pos, n_heads, n_kv_heads, k_cache, v_cache, max_seq,
-                                            rope_cos, rope_sin, out, (float *)ws, (hipStream_t)stream),
+                                            rope_cos, rope_sin, out, ws, (hipStream_t)stream),
                      fn);
 }
 

@@ -259,12 +259,14 @@ hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s);
 // Host check: decode problems with these M and K can go to the batched
 // streaming kernel (k_gemv_mt), whose codes the quantizer then writes tiled.
 bool gemv_mt_plan_ok(int n, const int *Ms, const int *Ks);
-// Decode attention (k_attn.hip): bytes of the per-chunk partial results for
-// n_heads query heads over max_seq positions, and the two launches.
-size_t attn_decode_part_bytes(int n_heads, int max_seq);
+// Decode attention (k_attn.hip): workspace bytes (the per-chunk partial
+// results for n_heads query heads over max_seq positions), the largest
+// max_seq it serves, and the launches.
+size_t attn_decode_workspace_bytes(int n_heads, int max_seq);
+int attn_decode_max_seq();
 hipError_t launch_attn_decode(const float *q, const float *k_new, const float *v_new, int pos, int H, int KVH,
                               float *k_cache, float *v_cache, int max_seq, const float *rcos, const float *rsin,
-                              float *out, float *part, hipStream_t s);
+                              float *out, void *ws, hipStream_t s);
 // Prefill GEMM (any M).  The large-tile kernel reads the rows' code sums
 // instead of recomputing them per tile: from c.qsum when the caller has them,
 // else computed into qsum_ws (device scratch for M ints); with neither the

@@ -19,13 +19,15 @@
 //           positions 16pq .. 16pq+15 (a wave reads a whole row per load).
 // The rotated queries go through LDS; each thread forms its dimensions' part
 // of the scores of its 4 positions for every head and the row group sums
-// them (DPP reduce-scatter); one wave per head takes the maximum, the exponentials and
-// their sum over the chunk; each thread accumulates its 16 positions'
-// weighted values for every head and the four position quarters meet in LDS.
-// The workgroup owning pos rotates the token's key, stores it and the value
-// into the caches and uses them in place of its row.  It writes (max, sum,
-// 128 partial outputs) per head and chunk.  k_attn_combine: one workgroup per
-// query head merges the chunks (rescaling each by exp(max_c - max)).
+// them (DPP reduce-scatter); one wave per head takes the maximum, the
+// exponentials and their sum over the chunk; each thread accumulates its 16
+// positions' weighted values for every head and the four position quarters
+// meet in LDS.  The workgroup owning pos rotates the token's key, stores it
+// and the value into the caches and uses them in place of its row.  Each
+// chunk writes (max, sum, 128 partial outputs) per head to the workspace;
+// k_attn_combine, one workgroup per query head, merges the chunks (weights
+// exp(max_c - max)).  A single chunk (pos < 64) writes the output itself and
+// the second launch is skipped.
 // Everything is fp32.
 #include "bl_common.h"
 
@@ -36,7 +38,8 @@ namespace {
 constexpr int kAttnD = 128;
 constexpr int kAttnChunk = 64;
 constexpr int kAttnMaxGroup = 4;                 // query heads per key/value head
-constexpr int kAttnPart = kAttnD + 2;            // per head and chunk: max, sum, 128 outputs
+constexpr int kAttnPart = kAttnD + 4;            // per head and chunk: max, sum, 2 unused, 128 outputs
+constexpr int kAttnMaxChunks = 512;              // max_seq <= 32768
 
 struct AttnArgs {
     const float *q, *k_new, *v_new;
@@ -200,17 +203,13 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnArgs a) {
 
     // softmax over the chunk: wave w for head w
     const int w = t >> 6, lane = t & 63;
+    float mw = 0.0f, lw = 1.0f;   // wave w: head w's maximum and sum over the chunk
     if (w < a.G) {
         const float sv = lane < n ? sc[w][lane] : -INFINITY;
-        const float m = wave64_max(sv);
-        const float p = lane < n ? expf(sv - m) : 0.0f;
-        const float l = wave64_sum(p);
+        mw = wave64_max(sv);
+        const float p = lane < n ? expf(sv - mw) : 0.0f;
+        lw = wave64_sum(p);
         reinterpret_cast<float *>(pw)[lane * 4 + w] = p;
-        if (lane == 0) {
-            float *pr = a.part + ((size_t)(g * a.G + w) * a.nchunks + c) * kAttnPart;
-            pr[0] = m;
-            pr[1] = l;
-        }
     } else {
         reinterpret_cast<float *>(pw)[lane * 4 + w] = 0.0f;   // heads past the group
     }
@@ -243,9 +242,17 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnArgs a) {
             o.x = o.x + r.x;
             o.y = o.y + r.y;
         }
-        float *pr = a.part + ((size_t)(g * a.G + w) * a.nchunks + c) * kAttnPart;
-        pr[2 + 2 * lane] = o.x;
-        pr[3 + 2 * lane] = o.y;
+        if (a.nchunks == 1) {   // the only chunk: its normalized sum is the result
+            a.out[(size_t)(g * a.G + w) * kAttnD + 2 * lane] = o.x / lw;
+            a.out[(size_t)(g * a.G + w) * kAttnD + 2 * lane + 1] = o.y / lw;
+        } else {
+            float *pr = a.part + ((size_t)(g * a.G + w) * a.nchunks + c) * kAttnPart;
+            if (lane == 0) {
+                pr[0] = mw;
+                pr[1] = lw;
+            }
+            *reinterpret_cast<float2 *>(pr + 4 + 2 * lane) = o;
+        }
     }
 }
 
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(64 * kCombWaves) void k_attn_combine(AttnArgs a) {
             const float *pc = pr + (size_t)(c < a.nchunks ? c : c0) * kAttnPart;
             mm[i] = pc[0];
             ll[i] = pc[1];
-            ov[i] = *reinterpret_cast<const float2 *>(pc + 2 + 2 * lane);
+            ov[i] = *reinterpret_cast<const float2 *>(pc + 4 + 2 * lane);
         }
         float mb = Mw;
 #pragma unroll
@@ -316,24 +323,27 @@ __global__ __launch_bounds__(64 * kCombWaves) void k_attn_combine(AttnArgs a) {
 
 } // namespace
 
-size_t attn_decode_part_bytes(int n_heads, int max_seq) {
+size_t attn_decode_workspace_bytes(int n_heads, int max_seq) {
     const int nch = (max_seq + kAttnChunk - 1) / kAttnChunk;
     return (size_t)n_heads * nch * kAttnPart * sizeof(float);
 }
 
+int attn_decode_max_seq() { return kAttnMaxChunks * kAttnChunk; }
+
 hipError_t launch_attn_decode(const float *q, const float *k_new, const float *v_new, int pos, int H, int KVH,
                               float *k_cache, float *v_cache, int max_seq, const float *rcos, const float *rsin,
-                              float *out, float *part, hipStream_t s) {
+                              float *out, void *ws, hipStream_t s) {
     AttnArgs a;
     a.q = q; a.k_new = k_new; a.v_new = v_new;
     a.k_cache = k_cache; a.v_cache = v_cache;
     a.rcos = rcos; a.rsin = rsin;
-    a.part = part; a.out = out;
+    a.part = static_cast<float *>(ws);
+    a.out = out;
     a.pos = pos; a.H = H; a.KVH = KVH; a.G = H / KVH; a.max_seq = max_seq;
     a.nchunks = (pos + 1 + kAttnChunk - 1) / kAttnChunk;
     a.scale = 1.0f / sqrtf((float)kAttnD);
     hipLaunchKernelGGL(k_attn_partial, dim3(KVH, a.nchunks), dim3(256), 0, s, a);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (hipError_t e = hipGetLastError(); e != hipSuccess || a.nchunks == 1) return e;
     hipLaunchKernelGGL(k_attn_combine, dim3(H), dim3(64 * kCombWaves), 0, s, a);
     return hipGetLastError();
 }

@@ -233,10 +233,12 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I,
  *     softmax_j(q'_h . k'_j / sqrt(128)) summed with v_j over j = 0 .. pos,
  *     with the key/value head h / (n_heads / n_kv_heads) and q', k' rotated
  *     by RoPE (dimension i paired with i + 64);
- *   ws scratch of bl_attn_decode_workspace_bytes(n_heads, max_seq) bytes.
+ *   ws device scratch of bl_attn_decode_workspace_bytes(n_heads, max_seq)
+ *     bytes (per-chunk partial results); calls that share it must be
+ *     ordered on one stream.
  * head_dim must be 128; n_heads a multiple of n_kv_heads with at most 4
- * query heads per key/value head; 0 <= pos < max_seq; all device pointers
- * 16-byte aligned.  Arithmetic in fp32 (scores, exponentials, sums).
+ * query heads per key/value head; 0 <= pos < max_seq <= 32768; all device
+ * pointers 16-byte aligned.  Arithmetic in fp32 (scores, exponentials, sums).
  * ------------------------------------------------------------------------ */
 int bl_rope_table(int max_pos, int head_dim, double base, float *cos_out, float *sin_out);
 size_t bl_attn_decode_workspace_bytes(int n_heads, int max_seq);

@@ -205,8 +205,9 @@ def test_attn_decode_validation(lib):
     assert _attn(raw, pos=2048) == lib.BL_ERR_SHAPE
     assert _attn(raw, pos=-1) == lib.BL_ERR_SHAPE
     assert _attn(raw, kc=FAKE_MIS) == lib.BL_ERR_ALIGN
+    assert _attn(raw, S=32769, pos=5) == lib.BL_ERR_SHAPE      # beyond the longest cache
     need = raw.bl_attn_decode_workspace_bytes(20, 2048)
-    assert need >= 20 * 32 * 130 * 4
+    assert need >= 20 * 32 * 132 * 4                            # partial results per head and chunk
     assert _attn(raw, ws_bytes=need - 1) == lib.BL_ERR_WORKSPACE
     assert _attn(raw, ws=None, ws_bytes=0) == lib.BL_ERR_WORKSPACE
     assert raw.bl_attn_decode_workspace_bytes(0, 2048) == 0

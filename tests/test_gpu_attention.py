@@ -71,6 +71,13 @@ def test_attn_decode_model_shape():
     _check(12, 20, 5, 2048, [0, 700, 2047], base=500000.0)
 
 
+def test_attn_decode_many_chunks():
+    # 79 and 512 chunks of 64 positions: merges over several batches, and the
+    # longest cache the kernel serves
+    _check(15, 8, 2, 5000, [4999, 4160])
+    _check(16, 4, 1, 32768, [32767])
+
+
 def test_attn_decode_other_base_and_peaked_scores():
     H, KVH, S, pos = 20, 5, 300, 257
     q, kn, vn, kc, vc = _inputs(13, H, KVH, S)
