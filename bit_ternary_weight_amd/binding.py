@@ -58,6 +58,7 @@ _SIGS = {
     "bl_ternarize_workspace_bytes": (_S, [_L, _L]),
     "bl_ternarize_pack": (_I, [_P, _I, _I, _P, _P, _P, _S, _P]),
     "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "bl_rmsnorm_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _P, _P]),
     "bl_gemv_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_gemv_w2a8": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_gemv_batched_workspace_bytes": (_S, [_I, ctypes.POINTER(GemvProblem)]),
@@ -195,6 +196,27 @@ def quant_act(x: torch.Tensor, q: torch.Tensor = None, a: torch.Tensor = None):
     _need(q, (M, K), (torch.int8,), "q")
     _need(a, (M,), (torch.float32,), "a")
     _check(raw.bl_quant_act(_ptr(x), _dt(x), M, K, x.stride(0), _ptr(q), _ptr(a), _stream(dev)))
+    return q, a
+
+
+def rmsnorm_quant(h: torch.Tensor, gain: torch.Tensor = None, eps: float = 1e-5, q: torch.Tensor = None,
+                  a: torch.Tensor = None):
+    """RMSNorm of each row of h [M,K] (contiguous fp32/bf16, optional gain
+    [K]) then per-token int8 quantization -> (q int8 [M,K], a fp32 [M])."""
+    dev = _dev(h)
+    M, K = h.shape
+    if not h.is_contiguous():
+        raise ValueError("h must be contiguous")
+    if gain is not None:
+        _need(gain, (K,), (torch.float32,), "gain")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    if a is None:
+        a = torch.empty(M, dtype=torch.float32, device=dev)
+    _need(q, (M, K), (torch.int8,), "q")
+    _need(a, (M,), (torch.float32,), "a")
+    _check(raw.bl_rmsnorm_quant(_ptr(h), _dt(h), M, K, None if gain is None else _ptr(gain), float(eps),
+                                _ptr(q), _ptr(a), _stream(dev)))
     return q, a
 
 

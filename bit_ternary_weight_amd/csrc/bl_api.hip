@@ -361,6 +361,19 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx, int8_t *q, f
     return check_hip(bl::launch_quant_act(x, x_dtype, M, K, ldx, q, a, nullptr, (hipStream_t)stream), "bl_quant_act");
 }
 
+int bl_rmsnorm_quant(const void *h, int h_dtype, int M, int K, const float *gain, float eps, int8_t *q, float *a,
+                     bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_rmsnorm_quant";
+    if (!h || !q || !a) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (h_dtype != BL_F32 && h_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "%s: h dtype %d not allowed", fn, h_dtype);
+    if (M < 1 || K < 1) return fail(BL_ERR_SHAPE, "%s: M=%d K=%d out of range", fn, M, K);
+    if (!(eps >= 0.0f) || !isfinite(eps)) return fail(BL_ERR_SHAPE, "%s: eps=%g", fn, (double)eps);
+    if (!aligned(h, 16) || !aligned(q, 16) || !aligned(a, 4) || (gain && !aligned(gain, 4)))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    return check_hip(bl::launch_rmsnorm_quant(h, h_dtype, M, K, gain, eps, q, a, nullptr, (hipStream_t)stream), fn);
+}
+
 size_t bl_gemv_workspace_bytes(int M, int N, int K) {
     (void)N;
     if (M < 1 || K < 1) return 0;

@@ -1,14 +1,22 @@
-"""Linear path of a BitNet b1.58 2B4T-shaped decoder stack, attention excluded.
+"""Linear path of a BitNet b1.58 2B4T-shaped decoder stack.
 
 Per layer (shapes from the "BitNetConfig" section of the BitNet model
 documentation pages: hidden 2560, intermediate 6912, 20 query / 5 key-value
 heads of 128):
   x -> fused q|k|v BitLinear (three segments, one launch)
-    -> o BitLinear fed with q's output (stand-in for attention: a convention,
-       the pages give no such wiring)
+    -> o BitLinear fed with q's output (layer_forward: attention left out, a
+       convention the pages give no wiring for)
     -> FFN chain: subln RMSNorm -> quantize -> gate|up -> ReLU^2(gate)*up ->
        ffn_sub_norm RMSNorm -> quantize -> down          (bl_ffn_chain)
   and down's output is the next layer's input (no residual additions).
+
+decode_layer_attn is the same layer at one token with the attention side in
+place of the stand-in ("BitNet" model documentation, "模型详情": rotary
+position embeddings, grouped-query attention, subln before o_proj):
+  x -> q|k|v -> RoPE, key/value cache append and attention over positions
+    0..pos (bl_attn_decode) -> attn_sub_norm RMSNorm -> quantize
+    (bl_rmsnorm_quant) -> o BitLinear on the codes -> FFN chain.
+Input norms and residual additions stay out, as in layer_forward.
 
 Every step runs in libbitlinear through the binding; this module only holds
 weights and orders calls.  Weights are ternarized on the device from seeded
@@ -31,6 +39,10 @@ I = synth.INTERMEDIATE
 KV = synth.KV_DIM
 QKV_SEGS = (H, KV, KV)
 DECODE_MAX_M = 64
+HEAD_DIM = 128
+N_HEADS = H // HEAD_DIM
+N_KV_HEADS = KV // HEAD_DIM
+ROPE_BASE = 500000.0   # rope_theta: a parameter on the pages (no value given); any base works
 
 
 @dataclass
@@ -146,3 +158,64 @@ def stack_forward(x: torch.Tensor, layers, eps: float = 1e-5, bufs: dict = None)
         cur = layer_forward(cur, lw, eps, out=outs[i & 1], bufs=bufs)
     return cur
 
+
+
+@dataclass
+class KVCache:
+    """Per-layer fp32 key/value caches [N_KV_HEADS, max_seq, 128] and the
+    RoPE tables [max_seq, 64] they share."""
+    k: list
+    v: list
+    rope_cos: torch.Tensor
+    rope_sin: torch.Tensor
+    max_seq: int
+
+
+def alloc_kv(n_layers: int, max_seq: int, device, base: float = ROPE_BASE) -> KVCache:
+    rc, rs = bl.rope_table(max_seq, HEAD_DIM, base, device=device)
+    shape = (N_KV_HEADS, max_seq, HEAD_DIM)
+    return KVCache([torch.zeros(shape, dtype=torch.float32, device=device) for _ in range(n_layers)],
+                   [torch.zeros(shape, dtype=torch.float32, device=device) for _ in range(n_layers)],
+                   rc, rs, max_seq)
+
+
+def decode_layer_attn(x: torch.Tensor, lw: LayerWeights, cache: KVCache, layer: int, pos: int,
+                      eps: float = 1e-5, out: torch.Tensor = None, bufs: dict = None, debug: dict = None):
+    """One layer at one token with attention.  x [1,H] fp32 or bf16 -> [1,H]
+    fp32; the token's rotated key and its value go into the layer's cache at
+    pos.  debug: optional dict that receives the stage outputs."""
+    if x.shape[0] != 1:
+        raise ValueError("decode_layer_attn takes one token")
+    dev = x.device
+    if bufs is None:
+        bufs = {}
+    if "att" not in bufs:
+        bufs["a_qkv"] = torch.empty((1, sum(QKV_SEGS)), dtype=torch.float32, device=dev)
+        bufs["att"] = torch.empty(H, dtype=torch.float32, device=dev)
+        bufs["q_o"] = torch.empty((1, H), dtype=torch.int8, device=dev)
+        bufs["a_o"] = torch.empty(1, dtype=torch.float32, device=dev)
+        bufs["a_y_o"] = torch.empty((1, H), dtype=torch.float32, device=dev)
+    y_qkv, att, q_o, a_o, y_o = bufs["a_qkv"], bufs["att"], bufs["q_o"], bufs["a_o"], bufs["a_y_o"]
+    bl.gemv_w2a8(x, lw.packed_qkv, lw.w_qkv, seg_n=QKV_SEGS, y=y_qkv)
+    row = y_qkv[0]
+    bl.attn_decode(row[:H], row[H:H + KV], row[H + KV:], pos, cache.k[layer], cache.v[layer],
+                   cache.rope_cos, cache.rope_sin, N_HEADS, N_KV_HEADS, out=att)
+    bl.rmsnorm_quant(att.view(1, H), eps=eps, q=q_o, a=a_o)
+    bl.gemv_w2a8(q_o, lw.packed_o, lw.w_o, a=a_o, y=y_o)
+    if debug is not None:
+        debug.update(y_qkv=y_qkv.clone(), att=att.clone(), q_o=q_o.clone(), a_o=a_o.clone(), y_o=y_o.clone())
+    return bl.ffn_chain(y_o, lw.packed_gu, lw.w_gu, lw.packed_down, lw.w_down, eps=eps, y=out)
+
+
+def decode_step_attn(x: torch.Tensor, layers, cache: KVCache, pos: int, eps: float = 1e-5, bufs: dict = None):
+    """All layers at one token with attention; returns the last layer's output."""
+    if bufs is None:
+        bufs = {}
+    outs = bufs.get("outs1")
+    if outs is None:
+        outs = [torch.empty((1, H), dtype=torch.float32, device=x.device) for _ in range(2)]
+        bufs["outs1"] = outs
+    cur = x
+    for i, lw in enumerate(layers):
+        cur = decode_layer_attn(cur, lw, cache, i, pos, eps, out=outs[i & 1], bufs=bufs)
+    return cur

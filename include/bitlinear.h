@@ -115,6 +115,22 @@ int bl_quant_act(const void *x, int x_dtype, int M, int K, int ldx,
                  int8_t *q, float *a, bl_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * bl_rmsnorm_quant -- RMSNorm of each row, then bl_quant_act's per-token
+ * int8 quantization: the sub-norm in front of a projection (attn_sub_norm
+ * before o_proj, ffn_sub_norm before down_proj).  [M] "模型详情" (subln
+ * normalization) and "BitNetConfig" (rms_norm_eps); [T] the subln
+ * paragraph; the quantization as in bl_quant_act.
+ *   h       [M,K] contiguous, dtype BL_F32 or BL_BF16.
+ *   gain    [K] fp32 RMSNorm weight, or NULL for all ones.
+ *   eps     >= 0 (the model uses 1e-5).
+ *   q, a    out: codes [M,K] int8 and scales [M] fp32 of
+ *           r = fp32(h * (1/sqrt(sum(h^2)/K + eps))) * gain, the sum in fp64.
+ * M >= 1, K >= 1.
+ * ------------------------------------------------------------------------ */
+int bl_rmsnorm_quant(const void *h, int h_dtype, int M, int K, const float *gain, float eps,
+                     int8_t *q, float *a, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
  * bl_gemv_w2a8 / bl_gemm_w2a8 -- the BitLinear contraction with rescale.
  * [T] "推理侧 BitLinear" forward bullet: quantize the activations, multiply
  * with the unpacked ternary weight, rescale by the activation and weight

@@ -120,6 +120,11 @@ def test_ternarize_and_quant_validation(lib):
     assert raw.bl_quant_act(FAKE, 0, 0, 8, 0, FAKE, FAKE, None) == B.BL_ERR_SHAPE
     assert raw.bl_quant_act(FAKE, 0, 4, 8, 4, FAKE, FAKE, None) == B.BL_ERR_SHAPE
     assert raw.bl_quant_act(FAKE_MIS, 0, 4, 8, 0, FAKE, FAKE, None) == B.BL_ERR_ALIGN
+    assert raw.bl_rmsnorm_quant(None, 0, 4, 8, None, 1e-5, FAKE, FAKE, None) == B.BL_ERR_NULL
+    assert raw.bl_rmsnorm_quant(FAKE, 2, 4, 8, None, 1e-5, FAKE, FAKE, None) == B.BL_ERR_DTYPE
+    assert raw.bl_rmsnorm_quant(FAKE, 0, 0, 8, None, 1e-5, FAKE, FAKE, None) == B.BL_ERR_SHAPE
+    assert raw.bl_rmsnorm_quant(FAKE, 0, 4, 8, None, -1.0, FAKE, FAKE, None) == B.BL_ERR_SHAPE
+    assert raw.bl_rmsnorm_quant(FAKE_MIS, 0, 4, 8, None, 1e-5, FAKE, FAKE, None) == B.BL_ERR_ALIGN
 
 
 def test_ffn_chain_validation(lib):

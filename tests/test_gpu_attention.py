@@ -111,3 +111,77 @@ def test_attn_decode_sequence_from_empty_cache():
         assert np.abs(out - ref).max() <= ATTN_TOL * max(1.0, np.abs(ref).max()), pos
         kc_ref[:, pos] = oracle.rope(kn.reshape(KVH, 128), pos, base).astype(np.float32)
         vc_ref[:, pos] = vn.reshape(KVH, 128)
+
+
+# ----------------------------------------------------------------------------- sub-norm + quantization
+@pytest.mark.parametrize("M,K,kind,gain", [(1, 2560, "bf16", False), (4, 2560, "f32", True),
+                                           (65, 6912, "f32", False), (3, 100, "f32", True), (1, 20, "bf16", True)])
+def test_rmsnorm_quant(M, K, kind, gain):
+    from bit_ternary_weight_amd import synth
+    from gpu_helpers import assert_exact, bf16_dev, f32_of_bf16
+    bl = _bl()
+    if kind == "bf16":
+        bits = synth.act_outliers_bf16(20 + M, M, K)
+        h_host, h_dev = f32_of_bf16(bits), bf16_dev(bits)
+    else:
+        h_host = synth.act_normal_f32(20 + M, M, K)
+        h_dev = to_dev(h_host)
+    g = np.random.default_rng(K).uniform(0.5, 1.5, size=K).astype(np.float32) if gain else None
+    q, a = bl.rmsnorm_quant(h_dev, gain=None if g is None else to_dev(g), eps=1e-5)
+    rq, ra = oracle.quant_act(oracle.rmsnorm(h_host, g, 1e-5))
+    assert_exact(host(q), rq, "codes")
+    assert_exact(host(a), ra, "scales")
+
+
+# ----------------------------------------------------------------------------- one layer with attention
+def test_decode_layer_with_attention_stagewise():
+    """stack.decode_layer_attn over 3 layers and several positions, each stage
+    against the oracle on the GPU's own input to that stage (no cascade):
+    q|k|v, attention (and the cache rows it appends), attn_sub_norm +
+    quantization, o, the FFN chain."""
+    from bit_ternary_weight_amd import stack, synth
+    from gpu_helpers import F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16, max_ulp_diff
+    H, KV, S, L = synth.HIDDEN, synth.KV_DIM, 300, 3
+    layers = stack.build_layers(L, dev())
+    cache = stack.alloc_kv(L, S, dev())
+    rng = np.random.default_rng(21)
+    # earlier tokens: random rotated keys and values at positions < 257
+    for l in range(L):
+        cache.k[l][:, :257] = torch.from_numpy(rng.standard_normal((5, 257, 128)).astype(np.float32)).to(dev())
+        cache.v[l][:, :257] = torch.from_numpy(rng.standard_normal((5, 257, 128)).astype(np.float32)).to(dev())
+    codes_l = []
+    for l in range(L):
+        codes, wms = {}, {}
+        for p, _, _ in synth.PROJECTIONS:
+            _, wm, c = oracle.ternarize_pack(synth.layer_weight(l, p))
+            codes[p], wms[p] = c, wm
+        codes_l.append((codes, wms))
+    for step, pos in enumerate((257, 258, 259)):
+        bits = synth.act_outliers_bf16(30 + step, 1, H)
+        x, x_host = bf16_dev(bits), f32_of_bf16(bits)
+        for l, lw in enumerate(layers):
+            codes, wms = codes_l[l]
+            kc0, vc0 = host(cache.k[l]).copy(), host(cache.v[l]).copy()
+            dbg = {}
+            y = stack.decode_layer_attn(x, lw, cache, l, pos, debug=dbg)
+            qkv_codes = np.concatenate([codes["q"], codes["k"], codes["v"]])
+            wq = np.array([wms["q"], wms["k"], wms["v"]], np.float32)
+            _, _, _, r_qkv = oracle.bitlinear(x_host, qkv_codes, [H, KV, KV], wq)
+            g_qkv = host(dbg["y_qkv"])
+            assert_rows_close(g_qkv, r_qkv, F32_TOL, f"qkv {l}")
+            assert max_ulp_diff(g_qkv, r_qkv) == 0
+            r_att = oracle.attn_decode(g_qkv[0, :H], g_qkv[0, H:H + KV], g_qkv[0, H + KV:], pos, kc0, vc0,
+                                       stack.ROPE_BASE, 20, 5).reshape(-1)
+            g_att = host(dbg["att"])
+            assert np.abs(g_att - r_att).max() <= ATTN_TOL * max(1.0, np.abs(r_att).max()), (l, pos)
+            assert np.array_equal(host(cache.v[l])[:, pos], g_qkv[0, H + KV:].reshape(5, 128))
+            rq, ra = oracle.quant_act(oracle.rmsnorm(g_att.reshape(1, H), None, 1e-5))
+            assert_exact(host(dbg["q_o"]), rq, f"attn_sub_norm codes {l}")
+            assert_exact(host(dbg["a_o"]), ra, f"attn_sub_norm scale {l}")
+            r_o = oracle.rescale(oracle.contract(rq, codes["o"]), ra, None, wms["o"])
+            assert_exact(host(dbg["y_o"]).view(np.uint32), r_o.view(np.uint32), f"o {l}")
+            gu = np.concatenate([codes["gate"], codes["up"]])
+            ch = oracle.ffn_chain(r_o, gu, np.array([wms["gate"], wms["up"]], np.float32), codes["down"], wms["down"])
+            yh = host(y)
+            assert_rows_close(yh, ch["y"], F32_TOL, f"layer {l}")
+            x, x_host = y.clone(), yh
