@@ -15,8 +15,8 @@ Headline (one JSON line on stdout):
 The same line carries the kernel's roofline, the oracle's CPU baseline, and
 secondary figures under "extra": the chained 30-layer decode (quantize ->
 q|k|v -> o -> RMSNorm -> gate|up -> ReLU^2 -> RMSNorm -> down per layer),
-batched decode at M=16 and M=64, decode attention over a 4096-token cache,
-prefill int8 TOPS, ternarization.
+batched decode at M=16 and M=64, decode attention over a 4096-token cache and
+the whole decode step with attention, prefill int8 TOPS, ternarization.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -278,27 +278,42 @@ def main():
             extra[f"decode_m{M}_us_per_layer"] = round(t * 1e3, 2)
             log(f"config 3 decode M={M}: {t * 1e3:.2f} us/layer, {extra[f'decode_m{M}_gbs']} GB/s")
             del g, pm
-        # decode attention at the full 4096-token context (N1): 30 layers'
-        # fp32 caches (20 query / 5 key-value heads x 128), the token at
-        # position 4095; bytes = the caches read + q, k, v in + the row
-        # appended + the output
-        S, KVH, NH = 4096, KV // 128, H // 128
-        rc, rs = bl.rope_table(S, 128, 500000.0, device=dev)
+        # decode attention at the full 4096-token context: 30 layers' fp32
+        # caches (20 query / 5 key-value heads x 128), the token at position
+        # 4095; bytes = the caches read + q, k, v in + the row appended + the
+        # output.  Then the whole decode step with attention through the 30
+        # layers (q|k|v -> attention -> attn_sub_norm + quantize -> o -> FFN).
+        S, KVH, NH = 4096, stack.N_KV_HEADS, stack.N_HEADS
+        cache = stack.alloc_kv(len(layers), S, dev)
         gen = torch.Generator(device=dev).manual_seed(5)
-        caches = [(torch.randn((KVH, S, 128), generator=gen, device=dev),
-                   torch.randn((KVH, S, 128), generator=gen, device=dev)) for _ in layers]
+        for kc, vc in zip(cache.k, cache.v):
+            kc.normal_(generator=gen)
+            vc.normal_(generator=gen)
         qa = torch.randn(H, generator=gen, device=dev)
         ka = torch.randn(KV, generator=gen, device=dev)
         va = torch.randn(KV, generator=gen, device=dev)
         oa = torch.empty(H, device=dev)
-        g = capture(torch, lambda: [bl.attn_decode(qa, ka, va, S - 1, kc, vc, rc, rs, NH, KVH, out=oa)
-                                    for kc, vc in caches])
+        g = capture(torch, lambda: [bl.attn_decode(qa, ka, va, S - 1, kc, vc, cache.rope_cos, cache.rope_sin,
+                                                   NH, KVH, out=oa) for kc, vc in zip(cache.k, cache.v)])
         t = timer.run(g.replay, 5, 1) / len(layers)
         ab = 2 * KVH * (S - 1) * 128 * 4 + (H + 2 * KV) * 4 + 2 * KV * 4 + H * 4
         extra["attn_decode_ctx4096_gbs"] = round(ab / (t * 1e-3) / 1e9, 1)
         extra["attn_decode_ctx4096_us_per_layer"] = round(t * 1e3, 2)
         log(f"decode attention, context 4096: {t * 1e3:.2f} us/layer, {extra['attn_decode_ctx4096_gbs']} GB/s")
-        del g, caches
+        del g
+        bufs_a = {}
+        g = capture(torch, lambda: stack.decode_step_attn(x1, layers, cache, S - 1, bufs=bufs_a))
+        ref = stack.decode_step_attn(x1, layers, cache, S - 1, bufs={}).clone()
+        for _ in range(3):   # replays must reproduce the eager step bit for bit
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(bufs_a["outs1"][(len(layers) - 1) & 1], ref):
+                raise RuntimeError("graph replay differs from the eager decode step with attention")
+        t = timer.run(g.replay, 5, 1) / len(layers)
+        extra["decode_step_attn_ctx4096_us_per_layer"] = round(t * 1e3, 2)
+        extra["decode_step_attn_ctx4096_gbs"] = round((layer_bytes(1, 4, H, I, KV) + ab) / (t * 1e-3) / 1e9, 1)
+        log(f"decode step with attention, context 4096: {t * 1e3:.2f} us/layer")
+        del g, cache
         # one layer, weights resident in the Infinity Cache (warm), for
         # contrast: 30 back-to-back launches on the same layer per replay
         g = capture(torch, lambda: [bl.gemv_w2a8_batched(probs1[0]) for _ in range(len(layers))])
