@@ -157,6 +157,39 @@ def cpu_baseline(seconds: float = 12.0):
                       f"seeded layers' codes, {dt:.1f} s on one host thread (same bytes accounting as the GPU)"}
 
 
+ATTN_CTX = 4096
+
+
+def attn_bytes(S: int, H: int, KV: int) -> int:
+    """Algorithmic bytes of one decode attention call for the token at
+    position S - 1: the cached key and value rows read, q, k, v in, the
+    appended rows and the output written (fp32)."""
+    return 2 * KV * (S - 1) * 4 + (H + 2 * KV) * 4 + 2 * KV * 4 + H * 4
+
+
+def attn_decode_timing(torch, bl, stack, timer, dev, n_layers, H, KV, keep=False):
+    """Decode attention for the token at position 4095 over n_layers layers'
+    fp32 caches (N(0,1)), replayed from a graph; returns (ms per layer, GB/s)
+    and, with keep, the caches."""
+    S = ATTN_CTX
+    cache = stack.alloc_kv(n_layers, S, dev)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    for kc, vc in zip(cache.k, cache.v):
+        kc.normal_(generator=gen)
+        vc.normal_(generator=gen)
+    qa = torch.randn(H, generator=gen, device=dev)
+    ka = torch.randn(KV, generator=gen, device=dev)
+    va = torch.randn(KV, generator=gen, device=dev)
+    oa = torch.empty(H, device=dev)
+    g = capture(torch, lambda: [bl.attn_decode(qa, ka, va, S - 1, kc, vc, cache.rope_cos, cache.rope_sin,
+                                               stack.N_HEADS, stack.N_KV_HEADS, out=oa)
+                                for kc, vc in zip(cache.k, cache.v)])
+    t = timer.run(g.replay, 5, 1) / n_layers
+    del g
+    gbs = round(attn_bytes(S, H, KV) / (t * 1e-3) / 1e9, 1)
+    return (t, gbs, cache) if keep else (t, gbs)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +200,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel loop (for profiler runs)")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="only the decode attention loop at position 4095 over 30 layers' caches (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
@@ -194,6 +229,11 @@ def main():
         return
     H, I, KV = synth.HIDDEN, synth.INTERMEDIATE, synth.KV_DIM
     timer = Timer(torch)
+    if args.attn_only:
+        t, gbs = attn_decode_timing(torch, bl, stack, timer, dev, args.layers, H, KV)
+        print(json.dumps({"attn_decode_ctx4096_us_per_layer": round(t * 1e3, 3), "attn_decode_ctx4096_gbs": gbs}),
+              flush=True)
+        return
     t_build = time.perf_counter()
     layers = stack.build_layers(args.layers, dev, workers=16)
     log(f"built {args.layers} layers in {time.perf_counter() - t_build:.1f} s")
@@ -283,24 +323,12 @@ def main():
         # 4095; bytes = the caches read + q, k, v in + the row appended + the
         # output.  Then the whole decode step with attention through the 30
         # layers (q|k|v -> attention -> attn_sub_norm + quantize -> o -> FFN).
-        S, KVH, NH = 4096, stack.N_KV_HEADS, stack.N_HEADS
-        cache = stack.alloc_kv(len(layers), S, dev)
-        gen = torch.Generator(device=dev).manual_seed(5)
-        for kc, vc in zip(cache.k, cache.v):
-            kc.normal_(generator=gen)
-            vc.normal_(generator=gen)
-        qa = torch.randn(H, generator=gen, device=dev)
-        ka = torch.randn(KV, generator=gen, device=dev)
-        va = torch.randn(KV, generator=gen, device=dev)
-        oa = torch.empty(H, device=dev)
-        g = capture(torch, lambda: [bl.attn_decode(qa, ka, va, S - 1, kc, vc, cache.rope_cos, cache.rope_sin,
-                                                   NH, KVH, out=oa) for kc, vc in zip(cache.k, cache.v)])
-        t = timer.run(g.replay, 5, 1) / len(layers)
-        ab = 2 * KVH * (S - 1) * 128 * 4 + (H + 2 * KV) * 4 + 2 * KV * 4 + H * 4
-        extra["attn_decode_ctx4096_gbs"] = round(ab / (t * 1e-3) / 1e9, 1)
+        S = ATTN_CTX
+        t, gbs, cache = attn_decode_timing(torch, bl, stack, timer, dev, len(layers), H, KV, keep=True)
+        ab = attn_bytes(S, H, KV)
+        extra["attn_decode_ctx4096_gbs"] = gbs
         extra["attn_decode_ctx4096_us_per_layer"] = round(t * 1e3, 2)
-        log(f"decode attention, context 4096: {t * 1e3:.2f} us/layer, {extra['attn_decode_ctx4096_gbs']} GB/s")
-        del g
+        log(f"decode attention, context 4096: {t * 1e3:.2f} us/layer, {gbs} GB/s")
         bufs_a = {}
         g = capture(torch, lambda: stack.decode_step_attn(x1, layers, cache, S - 1, bufs=bufs_a))
         ref = stack.decode_step_attn(x1, layers, cache, S - 1, bufs={}).clone()
