@@ -59,6 +59,8 @@ _SIGS = {
     "bl_ternarize_pack": (_I, [_P, _I, _I, _P, _P, _P, _S, _P]),
     "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "bl_rmsnorm_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _P, _P]),
+    "bl_subln_gemv_workspace_bytes": (_S, [_I, _I]),
+    "bl_subln_gemv_w2a8": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
     "bl_gemv_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_gemv_w2a8": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_gemv_batched_workspace_bytes": (_S, [_I, ctypes.POINTER(GemvProblem)]),
@@ -218,6 +220,35 @@ def rmsnorm_quant(h: torch.Tensor, gain: torch.Tensor = None, eps: float = 1e-5,
     _check(raw.bl_rmsnorm_quant(_ptr(h), _dt(h), M, K, None if gain is None else _ptr(gain), float(eps),
                                 _ptr(q), _ptr(a), _stream(dev)))
     return q, a
+
+
+def subln_gemv_w2a8(h: torch.Tensor, packed: torch.Tensor, w_mean: torch.Tensor, gain: torch.Tensor = None,
+                    eps: float = 1e-5, y_dtype=torch.float32, y: torch.Tensor = None, q_out: torch.Tensor = None,
+                    a_out: torch.Tensor = None):
+    """y = BitLinear(RMSNorm(h)) for h [M,K] contiguous fp32/bf16, one weight
+    segment; q_out / a_out optionally receive the codes and scales."""
+    dev = _dev(h, packed, w_mean)
+    M, K = h.shape
+    if not h.is_contiguous():
+        raise ValueError("h must be contiguous")
+    N = packed.shape[0] * 4
+    _need(packed, (N // 4, K), (torch.uint8,), "packed")
+    _need(w_mean, (1,), (torch.float32,), "w_mean")
+    if gain is not None:
+        _need(gain, (K,), (torch.float32,), "gain")
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=dev)
+    _need(y, (M, N), (y_dtype,), "y")
+    if q_out is not None:
+        _need(q_out, (M, K), (torch.int8,), "q_out")
+    if a_out is not None:
+        _need(a_out, (M,), (torch.float32,), "a_out")
+    ws = workspace(dev, raw.bl_subln_gemv_workspace_bytes(M, K))
+    _check(raw.bl_subln_gemv_w2a8(_ptr(h), _dt(h), M, K, None if gain is None else _ptr(gain), float(eps),
+                                  _ptr(packed), N, _ptr(w_mean), _ptr(y), _dt(y),
+                                  None if q_out is None else _ptr(q_out), None if a_out is None else _ptr(a_out),
+                                  _ptr(ws), ws.numel(), _stream(dev)))
+    return y
 
 
 def _contract(fn_name, ws_query, x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):

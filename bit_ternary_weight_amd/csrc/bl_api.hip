@@ -451,6 +451,61 @@ int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int
     return check_hip(bl::launch_generic(k, s), fn);
 }
 
+size_t bl_subln_gemv_workspace_bytes(int M, int K) {
+    if (M < 1 || K < 1) return 0;
+    return quant_scratch(M, K) + align256((size_t)M * sizeof(int));
+}
+
+int bl_subln_gemv_w2a8(const void *h, int h_dtype, int M, int K, const float *gain, float eps, const uint8_t *packed,
+                       int N, const float *w_mean, void *y, int y_dtype, int8_t *q_out, float *a_out, void *ws,
+                       size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_subln_gemv_w2a8";
+    if (h_dtype != BL_F32 && h_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "%s: h dtype %d not allowed", fn, h_dtype);
+    const bl_gemv_problem pr = as_problem(h, h_dtype, 0, nullptr, M, K, packed, N, 1, nullptr, w_mean, y, y_dtype);
+    Call c;
+    if (int st = validate(fn, false, pr, c)) return st;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return fail(BL_ERR_SHAPE, "%s: eps=%g", fn, (double)eps);
+    if ((gain && !aligned(gain, 4)) || (q_out && !aligned(q_out, 16)) || (a_out && !aligned(a_out, 4)))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (int st = check_ws(fn, ws, ws_bytes, bl_subln_gemv_workspace_bytes(M, K))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const bool decode = M <= kMaxGemvM;
+    const bool fast = is_fast(c);
+    if (decode && fast && fusable(M, K)) {
+        // one launch: the decode kernel normalizes and quantizes its rows in
+        // the prologue (codes and scales also to q_out / a_out when given)
+        bl::GemvBatch b;
+        memset(&b, 0, sizeof(b));
+        b.n = 1;
+        b.p[0] = gemv_of(c, 2, h, K, nullptr);
+        b.p[0].gain = gain;
+        b.p[0].eps = eps;
+        b.p[0].dbg_q = q_out;
+        b.p[0].dbg_a = a_out;
+        return check_hip(bl::launch_gemv_batch(b, s), fn);
+    }
+    char *wsb = (char *)ws;
+    int8_t *q = q_out ? q_out : (int8_t *)wsb;
+    float *a = a_out ? a_out : (float *)(wsb + align256((size_t)M * K));
+    int *qsum = (int *)(wsb + quant_scratch(M, K));
+    if (int st = check_hip(
+            bl::launch_rmsnorm_quant(h, h_dtype, M, K, gain, eps, q, a, !decode && fast ? qsum : nullptr, s), fn))
+        return st;
+    Call ci = c;
+    ci.x = q;
+    ci.x_dt = BL_I8;
+    ci.ldx = K;
+    ci.a = a;
+    if (decode) return run_decode(fn, 1, &ci, wsb, s);
+    bl::Contract k = contract_of(ci, q, K, a);
+    if (fast) {
+        k.qsum = qsum;
+        return check_hip(bl::launch_gemm(k, qsum, s), fn);
+    }
+    return check_hip(bl::launch_generic(k, s), fn);
+}
+
 size_t bl_ffn_chain_workspace_bytes(int M, int H, int I) {
     if (M < 1 || H < 1 || I < 1) return 0;
     return chain_scratch(M, H, I).end;

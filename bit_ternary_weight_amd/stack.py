@@ -14,8 +14,8 @@ decode_layer_attn is the same layer at one token with the attention side in
 place of the stand-in ("BitNet" model documentation, "模型详情": rotary
 position embeddings, grouped-query attention, subln before o_proj):
   x -> q|k|v -> RoPE, key/value cache append and attention over positions
-    0..pos (bl_attn_decode) -> attn_sub_norm RMSNorm -> quantize
-    (bl_rmsnorm_quant) -> o BitLinear on the codes -> FFN chain.
+    0..pos (bl_attn_decode) -> attn_sub_norm RMSNorm -> quantize -> o
+    BitLinear (bl_subln_gemv_w2a8, one launch at decode size) -> FFN chain.
 Input norms and residual additions stay out, as in layer_forward.
 
 Every step runs in libbitlinear through the binding; this module only holds
@@ -200,8 +200,8 @@ def decode_layer_attn(x: torch.Tensor, lw: LayerWeights, cache: KVCache, layer: 
     row = y_qkv[0]
     bl.attn_decode(row[:H], row[H:H + KV], row[H + KV:], pos, cache.k[layer], cache.v[layer],
                    cache.rope_cos, cache.rope_sin, N_HEADS, N_KV_HEADS, out=att)
-    bl.rmsnorm_quant(att.view(1, H), eps=eps, q=q_o, a=a_o)
-    bl.gemv_w2a8(q_o, lw.packed_o, lw.w_o, a=a_o, y=y_o)
+    bl.subln_gemv_w2a8(att.view(1, H), lw.packed_o, lw.w_o, eps=eps, y=y_o,
+                       q_out=q_o if debug is not None else None, a_out=a_o if debug is not None else None)
     if debug is not None:
         debug.update(y_qkv=y_qkv.clone(), att=att.clone(), q_o=q_o.clone(), a_o=a_o.clone(), y_o=y_o.clone())
     return bl.ffn_chain(y_o, lw.packed_gu, lw.w_gu, lw.packed_down, lw.w_down, eps=eps, y=out)

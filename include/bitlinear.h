@@ -191,6 +191,26 @@ int bl_gemm_w2a8(const void *x, int x_dtype, int ldx, const float *a, int M, int
                  void *ws, size_t ws_bytes, bl_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * bl_subln_gemv_w2a8 -- a sub-norm and the projection behind it:
+ *   y = BitLinear(RMSNorm(h)), i.e. bl_rmsnorm_quant then bl_gemv_w2a8 /
+ *   bl_gemm_w2a8 on the codes (attn_sub_norm before o_proj).  [M] "模型详情"
+ *   (subln); [T] the subln paragraph and "推理侧 BitLinear".
+ *   h       [M,K] contiguous fp32 / bf16; gain [K] fp32 or NULL; eps >= 0.
+ *   packed  [N/4,K] one segment with scale w_mean[0].
+ *   y       out [M,N], y_dtype BL_F32 / BL_BF16 / BL_I32.
+ *   q_out, a_out  optional (NULL): the codes [M,K] and scales [M] computed.
+ *   ws      scratch of bl_subln_gemv_workspace_bytes(M, K) bytes.
+ * Any M >= 1.  Decode sizes (M <= 64, K a multiple of 16, M*K small enough
+ * for the fused prologue) run as one launch whose decode kernel normalizes
+ * and quantizes its own rows; others run the norm kernel, then the
+ * contraction.  Same bits either way.
+ * ------------------------------------------------------------------------ */
+size_t bl_subln_gemv_workspace_bytes(int M, int K);
+int bl_subln_gemv_w2a8(const void *h, int h_dtype, int M, int K, const float *gain, float eps,
+                       const uint8_t *packed, int N, const float *w_mean, void *y, int y_dtype,
+                       int8_t *q_out, float *a_out, void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
  * bl_ffn_chain -- the feed-forward half of a BitNet layer, fused:
  *   subln RMSNorm(h) -> quantize -> gate|up -> ReLU^2(gate)*up ->
  *   ffn_sub_norm RMSNorm -> quantize -> down.

@@ -125,6 +125,18 @@ def test_ternarize_and_quant_validation(lib):
     assert raw.bl_rmsnorm_quant(FAKE, 0, 0, 8, None, 1e-5, FAKE, FAKE, None) == B.BL_ERR_SHAPE
     assert raw.bl_rmsnorm_quant(FAKE, 0, 4, 8, None, -1.0, FAKE, FAKE, None) == B.BL_ERR_SHAPE
     assert raw.bl_rmsnorm_quant(FAKE_MIS, 0, 4, 8, None, 1e-5, FAKE, FAKE, None) == B.BL_ERR_ALIGN
+    sg = raw.bl_subln_gemv_w2a8
+    need = raw.bl_subln_gemv_workspace_bytes(4, 64)
+    assert need >= 4 * 64 + 16 and raw.bl_subln_gemv_workspace_bytes(0, 64) == 0
+    ok = dict(h=FAKE, dt=0, M=4, K=64, g=None, eps=1e-5, P=FAKE, N=16, w=FAKE, y=FAKE, ydt=0, q=None, a=None,
+              ws=FAKE, wsb=need)
+    call = lambda **kw: sg(*{**ok, **kw}.values(), None)
+    assert call(h=None) == B.BL_ERR_NULL
+    assert call(dt=2) == B.BL_ERR_DTYPE                       # int8 input has no norm to apply
+    assert call(N=18) == B.BL_ERR_SHAPE
+    assert call(eps=-1.0) == B.BL_ERR_SHAPE
+    assert call(q=FAKE_MIS) == B.BL_ERR_ALIGN
+    assert call(wsb=need - 1) == B.BL_ERR_WORKSPACE
 
 
 def test_ffn_chain_validation(lib):

@@ -185,3 +185,38 @@ def test_decode_layer_with_attention_stagewise():
             yh = host(y)
             assert_rows_close(yh, ch["y"], F32_TOL, f"layer {l}")
             x, x_host = y.clone(), yh
+
+
+@pytest.mark.parametrize("M,K,N,kind,gain,ydt", [(1, 2560, 2560, "f32", False, torch.float32),
+                                                 (4, 2560, 640, "bf16", True, torch.float32),
+                                                 (1, 6912, 2560, "f32", True, torch.bfloat16),
+                                                 (3, 100, 64, "f32", False, torch.float32),
+                                                 (70, 256, 128, "f32", True, torch.float32)])
+def test_subln_gemv(M, K, N, kind, gain, ydt):
+    """bl_subln_gemv_w2a8 = RMSNorm -> quantize -> BitLinear: the fused decode
+    launch, the two-launch fallback (K not a multiple of 16) and the prefill
+    path (M > 64), against the oracle's rmsnorm, quant_act, contract, rescale."""
+    from bit_ternary_weight_amd import synth
+    from gpu_helpers import BF16_TOL, F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16
+    bl = _bl()
+    if kind == "bf16":
+        bits = synth.act_outliers_bf16(40 + M, M, K)
+        h_host, h_dev = f32_of_bf16(bits), bf16_dev(bits)
+    else:
+        h_host = synth.act_normal_f32(40 + M, M, K)
+        h_dev = to_dev(h_host)
+    g = np.random.default_rng(K + 1).uniform(0.5, 1.5, size=K).astype(np.float32) if gain else None
+    packed, wm, codes = oracle.ternarize_pack(synth.master_weight(50 + K, N, K))
+    q = torch.empty((M, K), dtype=torch.int8, device=dev())
+    a = torch.empty(M, dtype=torch.float32, device=dev())
+    y = bl.subln_gemv_w2a8(h_dev, to_dev(packed), to_dev(np.array([wm], np.float32)),
+                           gain=None if g is None else to_dev(g), y_dtype=ydt, q_out=q, a_out=a)
+    rq, ra = oracle.quant_act(oracle.rmsnorm(h_host, g, 1e-5))
+    assert_exact(host(q), rq, "codes")
+    assert_exact(host(a), ra, "scales")
+    ref = oracle.rescale(oracle.contract(rq, codes), ra, None, wm)
+    if ydt == torch.float32:
+        assert_exact(host(y).view(np.uint32), ref.view(np.uint32), "y bits")
+    else:
+        yb = host(y.view(torch.int16)).view(np.uint16)
+        assert_exact(yb, oracle.to_bf16(ref), "bf16 y")
