@@ -59,6 +59,8 @@ _SIGS = {
     "bl_ternarize_pack": (_I, [_P, _I, _I, _P, _P, _P, _S, _P]),
     "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "bl_rmsnorm_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _P, _P]),
+    "bl_attn_prefill_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_subln_gemv_workspace_bytes": (_S, [_I, _I]),
     "bl_subln_gemv_w2a8": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
     "bl_gemv_workspace_bytes": (_S, [_I, _I, _I]),
@@ -387,4 +389,36 @@ def attn_decode(q, k_new, v_new, pos, k_cache, v_cache, rope_cos, rope_sin, n_he
     _check(raw.bl_attn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), int(pos), int(n_heads), int(n_kv_heads), D,
                               _ptr(k_cache), _ptr(v_cache), int(max_seq), _ptr(rope_cos), _ptr(rope_sin),
                               _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def attn_prefill(q, k, v, k_cache, v_cache, rope_cos, rope_sin, n_heads, n_kv_heads, out=None):
+    """Causal attention of a prompt at positions 0 .. M-1 (see bl_attn_prefill):
+    q [M, n_heads*128], k / v [M, n_kv_heads*128] fp32 with one row stride
+    (views into a q|k|v output are fine); k_cache / v_cache [n_kv_heads,
+    max_seq, 128] fp32 (positions < M written); returns out [M, n_heads*128]."""
+    dev = _dev(q, k, v, k_cache, v_cache, rope_cos, rope_sin)
+    D = 128
+    M = q.shape[0]
+    for t, w, name in ((q, n_heads * D, "q"), (k, n_kv_heads * D, "k"), (v, n_kv_heads * D, "v")):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape != (M, w) or t.stride(1) != 1:
+            raise ValueError(f"{name} must be fp32 [{M}, {w}] with contiguous rows")
+    if not (q.stride(0) == k.stride(0) == v.stride(0)):
+        raise ValueError("q, k and v must share one row stride")
+    kvh, max_seq, d = k_cache.shape
+    if d != D or kvh != n_kv_heads or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [n_kv_heads, max_seq, 128]")
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32")
+    if rope_cos.shape[0] < M or rope_cos.shape[-1] != D // 2 or rope_sin.shape != rope_cos.shape:
+        raise ValueError("rope tables must be [>= M, 64]")
+    if out is None:
+        out = torch.empty((M, n_heads * D), dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or out.shape != (M, n_heads * D) or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [M, n_heads*128] with contiguous rows")
+    ws = workspace(dev, raw.bl_attn_prefill_workspace_bytes(M, int(n_heads), int(n_kv_heads)))
+    _check(raw.bl_attn_prefill(_ptr(q), _ptr(k), _ptr(v), q.stride(0), M, int(n_heads), int(n_kv_heads), D,
+                               _ptr(k_cache), _ptr(v_cache), int(max_seq), _ptr(rope_cos), _ptr(rope_sin),
+                               _ptr(out), out.stride(0), _ptr(ws), ws.numel(), _stream(dev)))
     return out

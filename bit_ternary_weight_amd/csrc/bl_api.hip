@@ -15,6 +15,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "bl_attn.h"
 #include "bl_common.h"
 
 namespace {
@@ -662,6 +663,35 @@ int bl_attn_decode(const float *q, const float *k_new, const float *v_new, int p
     if (int st = check_ws(fn, ws, ws_bytes, bl_attn_decode_workspace_bytes(n_heads, max_seq))) return st;
     return check_hip(bl::launch_attn_decode(q, k_new, v_new, pos, n_heads, n_kv_heads, k_cache, v_cache, max_seq,
                                             rope_cos, rope_sin, out, ws, (hipStream_t)stream),
+                     fn);
+}
+
+size_t bl_attn_prefill_workspace_bytes(int M, int n_heads, int n_kv_heads) {
+    if (M < 1 || n_heads < 1 || n_kv_heads < 1) return 0;
+    return align256(bl::attn_prefill_workspace_bytes(M, n_heads, n_kv_heads));
+}
+
+int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int M, int n_heads, int n_kv_heads,
+                    int head_dim, float *k_cache, float *v_cache, int max_seq, const float *rope_cos,
+                    const float *rope_sin, float *out, int ldo, void *ws, size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_attn_prefill";
+    if (!q || !k || !v || !k_cache || !v_cache || !rope_cos || !rope_sin || !out)
+        return fail(BL_ERR_NULL, "%s: a device pointer is NULL", fn);
+    if (head_dim != 128) return fail(BL_ERR_SHAPE, "%s: head_dim=%d (only 128 is supported)", fn, head_dim);
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0)
+        return fail(BL_ERR_SHAPE, "%s: n_heads=%d n_kv_heads=%d (n_heads a multiple of n_kv_heads)", fn, n_heads,
+                    n_kv_heads);
+    if (M < 1 || M > max_seq) return fail(BL_ERR_SHAPE, "%s: M=%d max_seq=%d", fn, M, max_seq);
+    if (ldx < 128 * n_heads || ldo < 128 * n_heads || ldo % 4 != 0)
+        return fail(BL_ERR_SHAPE, "%s: ldx=%d ldo=%d (at least n_heads*128; ldo a multiple of 4)", fn, ldx, ldo);
+    const void *p4[] = {q, k, v, k_cache, v_cache, rope_cos, rope_sin};
+    for (const void *p : p4)
+        if (!aligned(p, 4)) return fail(BL_ERR_ALIGN, "%s: misaligned device pointer", fn);
+    if (!aligned(out, 16)) return fail(BL_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+    if (int st = check_ws(fn, ws, ws_bytes, bl_attn_prefill_workspace_bytes(M, n_heads, n_kv_heads))) return st;
+    return check_hip(bl::launch_attn_prefill(q, k, v, ldx, M, n_heads, n_kv_heads, k_cache, v_cache, max_seq,
+                                             rope_cos, rope_sin, out, ldo, ws, (hipStream_t)stream),
                      fn);
 }
 

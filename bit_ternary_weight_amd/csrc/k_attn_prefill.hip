@@ -1,0 +1,268 @@
+// k_attn_prefill.hip -- the attention side of a decoder layer for a prompt
+// of M tokens at positions 0 .. M-1 (prefill): RoPE on every token's query
+// and key, the keys and values stored into the caches (for the decode steps
+// that follow), and causal grouped-query softmax attention.
+//
+// "BitNet" model documentation, "模型详情" (rotary position embeddings) and
+// "BitNetConfig" (20 attention heads, 5 key/value heads, hidden size 2560 =
+// 20 heads x 128 dimensions, rope_theta a parameter).  The rotation pairs
+// dimension i of a head with i + 64 at angle pos * base^(-i/64); scores are
+// scaled by 1/sqrt(128); token p attends to positions 0 .. p.
+//
+// Two launches.
+//   k_attn_prep: per 64 tokens and one head slot, the rotated queries and
+//     keys rounded to bf16 (and the keys in fp32 into the cache), the values
+//     into the cache and, rounded to bf16, transposed to [dimension][token].
+//   k_attn_fwd: one workgroup per (query head, block of 64 queries), heaviest
+//     blocks first; wave w owns queries 16w .. 16w+15.  Per block of 64 keys
+//     (staged through LDS, the next block's loads in flight meanwhile):
+//       S^T = K Q^T  with v_mfma_f32_16x16x32_bf16 (keys the first operand,
+//         so lane (g, c) holds keys 4g..4g+3 of each 16-key tile for query c);
+//       online softmax in fp32 (base-2 exponentials of the pre-scaled
+//         scores), the maximum shared by the four lanes of a query;
+//       O^T += V^T P^T with the probabilities rounded to bf16 straight from
+//         the score registers: the k index of the product runs over the keys
+//         in the order the score layout holds them, and the transposed value
+//         block is read in the same order.
+//     The result O^T / l is stored with 16-byte fp32 stores (four consecutive
+//     dimensions of one query per lane).
+#include "bl_common.h"
+#include "bl_attn.h"
+
+namespace bl {
+
+namespace {
+
+constexpr int kPD = 128;                 // head dimension
+constexpr int kPB = 64;                  // tokens per query block and per key block
+constexpr int kKStride = kPD + 8;        // LDS key row, bf16 elements (272 bytes: rows 4 banks apart)
+constexpr int kVStride = kPB + 4;        // LDS transposed value row, bf16 elements (136 bytes)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct PrefArgs {
+    const float *q, *k, *v;   // token rows with stride ldx: q head h at h*128, k / v head g at g*128
+    int ldx;
+    float *k_cache, *v_cache; // [KVH][max_seq][128]
+    int max_seq;
+    const float *rcos, *rsin; // [>= M][64]
+    __bf16 *qb;               // [H][Mp][128] rotated queries
+    __bf16 *kb;               // [KVH][Mp][128] rotated keys
+    __bf16 *vt;               // [KVH][128][Mp] values, transposed
+    float *out;               // [M][ldo]: head h at h*128
+    int ldo;
+    int M, Mp, H, KVH, G;
+    float scale_log2;         // log2(e) / sqrt(128)
+};
+
+// bf16 of an fp32 value, rounded to nearest even (finite inputs).
+__device__ __forceinline__ __bf16 to_bf(float x) { return static_cast<__bf16>(x); }
+
+__global__ __launch_bounds__(256) void k_attn_prep(PrefArgs a) {
+    __shared__ float vtile[kPB][kPD + 1];
+    const int m0 = blockIdx.x * kPB;
+    const int slot = blockIdx.y;          // < H: query head; < H + KVH: key head; else value head
+    const int t = threadIdx.x;
+    if (slot < a.H + a.KVH) {
+        const bool isq = slot < a.H;
+        const int hh = isq ? slot : slot - a.H;
+        const float *src = (isq ? a.q : a.k) + hh * kPD;
+        __bf16 *dst = (isq ? a.qb : a.kb) + (size_t)hh * a.Mp * kPD;
+        const int i = t & 63;
+#pragma unroll 4
+        for (int r = 0; r < kPB / 4; ++r) {
+            const int m = m0 + (t >> 6) + 4 * r;
+            float y0 = 0.0f, y1 = 0.0f;
+            if (m < a.M) {
+                const float x0 = src[(size_t)m * a.ldx + i], x1 = src[(size_t)m * a.ldx + i + 64];
+                const float co = a.rcos[(size_t)m * 64 + i], si = a.rsin[(size_t)m * 64 + i];
+                y0 = x0 * co - x1 * si;
+                y1 = x1 * co + x0 * si;
+                if (!isq) {
+                    float *kw = a.k_cache + ((size_t)hh * a.max_seq + m) * kPD;
+                    kw[i] = y0;
+                    kw[i + 64] = y1;
+                }
+            }
+            dst[(size_t)m * kPD + i] = to_bf(y0);
+            dst[(size_t)m * kPD + i + 64] = to_bf(y1);
+        }
+        return;
+    }
+    const int g = slot - a.H - a.KVH;
+    const float *src = a.v + g * kPD;
+#pragma unroll 4
+    for (int r = 0; r < kPB / 2; ++r) {
+        const int tok = (t >> 7) + 2 * r, d = t & 127;
+        const int m = m0 + tok;
+        float x = 0.0f;
+        if (m < a.M) {
+            x = src[(size_t)m * a.ldx + d];
+            a.v_cache[((size_t)g * a.max_seq + m) * kPD + d] = x;
+        }
+        vtile[tok][d] = x;
+    }
+    __syncthreads();
+    // transposed: thread (d = t >> 1, half = t & 1) writes 32 tokens of row d
+    const int d = t >> 1, h0 = (t & 1) * 32;
+    __bf16 *row = a.vt + ((size_t)g * kPD + d) * a.Mp + m0 + h0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        bf16x8 v8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v8[j] = to_bf(vtile[h0 + 8 * c + j][d]);
+        *reinterpret_cast<bf16x8 *>(row + 8 * c) = v8;
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void k_attn_fwd(PrefArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 ks[kPB * kKStride];
+    __shared__ __attribute__((aligned(16))) __bf16 vs[kPD * kVStride];
+    const int nqb = a.Mp / kPB;
+    const int qblk = nqb - 1 - (int)blockIdx.x / a.H;   // heaviest (latest) query blocks first
+    const int h = (int)blockIdx.x % a.H;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, lr = lane & 15;
+    const int kvh = h / a.G;
+    const int qrow = qblk * kPB + 16 * w + lr;           // this lane's query (position)
+    const __bf16 *kbase = a.kb + (size_t)kvh * a.Mp * kPD;
+    const __bf16 *vbase = a.vt + (size_t)kvh * kPD * a.Mp;
+
+    // second operand of S^T = K Q^T: Q[query lr][dimensions 32s + 8g .. +7]
+    bf16x8 qf[4];
+    {
+        const __bf16 *qp = a.qb + ((size_t)h * a.Mp + qrow) * kPD + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+    }
+    // staging: 1024 16-byte pieces of keys (row c >> 4, piece c & 15) and of
+    // transposed values (row c >> 3, piece c & 7), four of each per thread
+    bf16x8 kr[4], vr[4];
+    auto fetch = [&](int kb0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = t + 256 * r;
+            kr[r] = *reinterpret_cast<const bf16x8 *>(kbase + (size_t)(kb0 + (c >> 4)) * kPD + 8 * (c & 15));
+            vr[r] = *reinterpret_cast<const bf16x8 *>(vbase + (size_t)(c >> 3) * a.Mp + kb0 + 8 * (c & 7));
+        }
+    };
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;   // l_run: this lane's part (its keys) of the sum
+    fetch(0);
+    for (int kblk = 0; kblk <= qblk; ++kblk) {
+        __syncthreads();   // every wave is done with the previous block
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = t + 256 * r;
+            *reinterpret_cast<bf16x8 *>(&ks[(c >> 4) * kKStride + 8 * (c & 15)]) = kr[r];
+            bf16x4 *vd = reinterpret_cast<bf16x4 *>(&vs[(c >> 3) * kVStride + 8 * (c & 7)]);
+            vd[0] = bf16x4{vr[r][0], vr[r][1], vr[r][2], vr[r][3]};
+            vd[1] = bf16x4{vr[r][4], vr[r][5], vr[r][6], vr[r][7]};
+        }
+        __syncthreads();
+        if (kblk < qblk) fetch((kblk + 1) * kPB);
+
+        // S^T for 4 tiles of 16 keys: lane (g, lr) gets keys 16c + 4g + i of query lr
+        f32x4 sc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            sc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                sc[c] = mfma_bf16(*reinterpret_cast<const bf16x8 *>(&ks[(16 * c + lr) * kKStride + 32 * s + 8 * g]),
+                                  qf[s], sc[c]);
+        }
+        // online softmax in base 2
+        const bool diag = kblk == qblk;
+        float bm = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = sc[c][i] * a.scale_log2;
+                if (diag && kblk * kPB + 16 * c + 4 * g + i > qrow) v = -INFINITY;
+                sc[c][i] = v;
+                bm = fmaxf(bm, v);
+            }
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float m_new = fmaxf(m_run, bm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        float ps = 0.0f;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(sc[c][i] - m_new);
+                ps += p;
+                pb[c >> 1][4 * (c & 1) + i] = to_bf(p);
+            }
+        l_run = l_run * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        // O^T += V^T P^T: k slot 8g + j of step s is key 32s + 4g + j (j < 4)
+        // or 32s + 16 + 4g + (j - 4)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const __bf16 *vrow = &vs[(16 * dt + lr) * kVStride + 32 * s + 4 * g];
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vrow);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vrow + 16);
+                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[dt] = mfma_bf16(va, pb[s], o[dt]);
+            }
+    }
+    float l = l_run + __shfl_xor(l_run, 16, 64);
+    l = l + __shfl_xor(l, 32, 64);
+    if (qrow >= a.M) return;
+    const float inv = 1.0f / l;
+    float *orow = a.out + (size_t)qrow * a.ldo + h * kPD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        float4 v;
+        v.x = o[dt][0] * inv;
+        v.y = o[dt][1] * inv;
+        v.z = o[dt][2] * inv;
+        v.w = o[dt][3] * inv;
+        *reinterpret_cast<float4 *>(orow + 16 * dt) = v;
+    }
+}
+
+} // namespace
+
+size_t attn_prefill_workspace_bytes(int M, int n_heads, int n_kv_heads) {
+    const size_t Mp = (size_t)(M + kPB - 1) / kPB * kPB;
+    return Mp * kPD * sizeof(__bf16) * ((size_t)n_heads + 2 * (size_t)n_kv_heads);
+}
+
+hipError_t launch_attn_prefill(const float *q, const float *k, const float *v, int ldx, int M, int H, int KVH,
+                               float *k_cache, float *v_cache, int max_seq, const float *rcos, const float *rsin,
+                               float *out, int ldo, void *ws, hipStream_t s) {
+    PrefArgs a;
+    a.q = q; a.k = k; a.v = v; a.ldx = ldx;
+    a.k_cache = k_cache; a.v_cache = v_cache; a.max_seq = max_seq;
+    a.rcos = rcos; a.rsin = rsin;
+    a.M = M; a.Mp = (M + kPB - 1) / kPB * kPB; a.H = H; a.KVH = KVH; a.G = H / KVH;
+    a.qb = static_cast<__bf16 *>(ws);
+    a.kb = a.qb + (size_t)H * a.Mp * kPD;
+    a.vt = a.kb + (size_t)KVH * a.Mp * kPD;
+    a.out = out; a.ldo = ldo;
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)kPD);
+    const int nqb = a.Mp / kPB;
+    hipLaunchKernelGGL(k_attn_prep, dim3(nqb, H + 2 * KVH), dim3(256), 0, s, a);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_fwd, dim3(nqb * H), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace bl

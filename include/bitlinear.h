@@ -284,6 +284,32 @@ int bl_attn_decode(const float *q, const float *k_new, const float *v_new, int p
                    const float *rope_cos, const float *rope_sin,
                    float *out, void *ws, size_t ws_bytes, bl_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * bl_attn_prefill -- the attention side of a decoder layer for a prompt of M
+ * tokens at positions 0 .. M-1.  Same pages and readings as bl_attn_decode;
+ * token p attends to positions 0 .. p (causal).
+ *   q [M rows][n_heads*128], k, v [M rows][n_kv_heads*128] fp32 device,
+ *     row stride ldx elements (views into one q|k|v row are fine), before RoPE;
+ *   k_cache, v_cache [n_kv_heads][max_seq][128] fp32 device: positions
+ *     0 .. M-1 receive the rotated keys and the values (for later
+ *     bl_attn_decode calls);
+ *   rope_cos, rope_sin [>= M][64] device (bl_rope_table);
+ *   out [M rows][ldo] fp32 device, head h at columns h*128 .. h*128+127;
+ *   ws device scratch of bl_attn_prefill_workspace_bytes(M, n_heads,
+ *     n_kv_heads) bytes.
+ * Precision: the rotated queries and keys, the values and the probabilities
+ * enter the two products as bf16 (round to nearest even), with fp32
+ * products' sums, fp32 softmax and an fp32 result; the caches get fp32.
+ * head_dim must be 128; n_heads a multiple of n_kv_heads; 1 <= M <= max_seq;
+ * ldx, ldo >= n_heads*128, ldo a multiple of 4; out 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t bl_attn_prefill_workspace_bytes(int M, int n_heads, int n_kv_heads);
+int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int M,
+                    int n_heads, int n_kv_heads, int head_dim,
+                    float *k_cache, float *v_cache, int max_seq,
+                    const float *rope_cos, const float *rope_sin,
+                    float *out, int ldo, void *ws, size_t ws_bytes, bl_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

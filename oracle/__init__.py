@@ -10,7 +10,8 @@ and marshals numpy arrays through ctypes.  Every function here takes and
 returns numpy arrays.
 
 Parity status: every function is pinned by tests under ``tests/`` (worked
-examples, closed forms, invariants, brute force).  The layer wiring used for
+examples, closed forms, invariants, brute force; the prefill attention rows
+against the separately written decode attention).  The layer wiring used for
 the 30-layer stack (q output feeding o in place of attention, no residual)
 is a convention with no passage behind it: parity unpinned for that wiring.
 """
@@ -287,4 +288,49 @@ def attn_decode(q, k_new, v_new, pos, k_cache, v_cache, base, n_heads, n_kv_head
     out = np.empty((n_heads, D), np.float64)
     _load().ora_attn_decode(_p(q), _p(k_new), _p(v_new), int(pos), n_heads, n_kv_heads, D,
                             _p(k_cache), _p(v_cache), S, float(base), _p(out))
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """fp32 values of x rounded to bf16 (nearest even), via to_bf16."""
+    b = to_bf16(np.asarray(x, np.float32))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def attn_prefill_rows(q, k, v, base, n_heads, n_kv_heads, rows, bf16_inputs=True):
+    """fp64 causal attention outputs [len(rows), n_heads*D] of a prompt whose
+    tokens sit at positions 0 .. M-1.
+
+    q [M, n_heads*D], k / v [M, n_kv_heads*D] fp32, before RoPE.  Queries and
+    keys are rotated (rope, fp64) and rounded to fp32; with bf16_inputs they
+    and the values are then rounded to bf16, the precision in which the
+    prefill products take them.  Row p attends to positions 0 .. p with scores
+    q'.k'/sqrt(D); query head h reads key/value head h // (n_heads/n_kv_heads).
+    A numpy matmul forms the scores and the weighted sums.
+    """
+    q = np.asarray(q, np.float32)
+    k = np.asarray(k, np.float32)
+    v = np.asarray(v, np.float32)
+    M = q.shape[0]
+    D = q.shape[1] // n_heads
+    G = n_heads // n_kv_heads
+    qh = q.reshape(M, n_heads, D)
+    kh = k.reshape(M, n_kv_heads, D)
+    kr = np.stack([rope(kh[p], p, base) for p in range(M)]).astype(np.float32)
+    vv = v.reshape(M, n_kv_heads, D)
+    if bf16_inputs:
+        kr = bf16_round(kr)
+        vv = bf16_round(vv)
+    kr = kr.astype(np.float64)
+    vv = vv.astype(np.float64)
+    out = np.empty((len(rows), n_heads * D), np.float64)
+    for n, p in enumerate(rows):
+        qr = rope(qh[p], p, base).astype(np.float32)
+        if bf16_inputs:
+            qr = bf16_round(qr)
+        qr = qr.astype(np.float64)
+        for h in range(n_heads):
+            s = kr[:p + 1, h // G, :] @ qr[h] / np.sqrt(float(D))
+            w = np.exp(s - s.max())
+            out[n, h * D:(h + 1) * D] = (w @ vv[:p + 1, h // G, :]) / w.sum()
     return out

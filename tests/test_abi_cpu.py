@@ -241,3 +241,22 @@ def test_rope_table_values(lib):
     assert raw.bl_rope_table(4, 7, 10000.0, FAKE, FAKE) == lib.BL_ERR_SHAPE
     assert raw.bl_rope_table(4, 8, 0.0, FAKE, FAKE) == lib.BL_ERR_SHAPE
     assert raw.bl_rope_table(4, 8, 10000.0, None, FAKE) == lib.BL_ERR_NULL
+
+
+def test_attn_prefill_validation(lib):
+    raw = lib.raw
+    pf = raw.bl_attn_prefill
+    need = raw.bl_attn_prefill_workspace_bytes(100, 20, 5)
+    assert need >= 128 * 128 * 2 * 30 and raw.bl_attn_prefill_workspace_bytes(0, 20, 5) == 0
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, ldx=3840, M=100, H=20, KVH=5, D=128, kc=FAKE, vc=FAKE, S=4096, rc=FAKE,
+              rs=FAKE, out=FAKE, ldo=2560, ws=FAKE, wsb=need)
+    call = lambda **kw: pf(*{**ok, **kw}.values(), None)
+    assert call(q=None) == lib.BL_ERR_NULL
+    assert call(D=64) == lib.BL_ERR_SHAPE
+    assert call(KVH=3) == lib.BL_ERR_SHAPE
+    assert call(M=4097) == lib.BL_ERR_SHAPE
+    assert call(M=0) == lib.BL_ERR_SHAPE
+    assert call(ldx=2000) == lib.BL_ERR_SHAPE
+    assert call(ldo=2562) == lib.BL_ERR_SHAPE
+    assert call(out=FAKE_MIS) == lib.BL_ERR_ALIGN
+    assert call(wsb=need - 1) == lib.BL_ERR_WORKSPACE

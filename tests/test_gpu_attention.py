@@ -220,3 +220,76 @@ def test_subln_gemv(M, K, N, kind, gain, ydt):
     else:
         yb = host(y.view(torch.int16)).view(np.uint16)
         assert_exact(yb, oracle.to_bf16(ref), "bf16 y")
+
+
+# ----------------------------------------------------------------------------- prefill attention
+# The kernel multiplies bf16 queries, keys, values and probabilities (fp32
+# sums, fp32 softmax); the oracle rounds its fp64 rotations to fp32 and bf16
+# the same way and keeps everything else in fp64.  What remains is the bf16
+# rounding of the probabilities (a relative 2^-9 on each weight of the
+# numerator) and fp32 sums: |out - ref| <= 2^-8 * max|v| bounds it twice over.
+def _prefill_check(seed, M, H, KVH, rows=None, S=None, base=500000.0):
+    bl = _bl()
+    S = S or M
+    rng = np.random.default_rng(seed)
+    qkv = rng.standard_normal((M, (H + 2 * KVH) * 128)).astype(np.float32)
+    q, k, v = qkv[:, :H * 128], qkv[:, H * 128:(H + KVH) * 128], qkv[:, (H + KVH) * 128:]
+    d_qkv = to_dev(qkv)
+    rc, rs = bl.rope_table(S, 128, base, device=dev())
+    kc = torch.full((KVH, S, 128), 7.0, dtype=torch.float32, device=dev())
+    vc = torch.full((KVH, S, 128), 7.0, dtype=torch.float32, device=dev())
+    out = bl.attn_prefill(d_qkv[:, :H * 128], d_qkv[:, H * 128:(H + KVH) * 128], d_qkv[:, (H + KVH) * 128:],
+                          kc, vc, rc, rs, H, KVH)
+    rows = list(range(M)) if rows is None else rows
+    ref = oracle.attn_prefill_rows(q, k, v, base, H, KVH, rows)
+    got = host(out)[rows]
+    err = np.abs(got - ref).max()
+    assert err <= 2.0 ** -8 * np.abs(v).max(), (M, H, KVH, err)
+    # caches: rotated fp32 keys and the values at positions < M, nothing else
+    kch, vch = host(kc), host(vc)
+    for p in sorted(set([0, M - 1] + [r for r in rows if r < M])):
+        kr = oracle.rope(k[p].reshape(KVH, 128), p, base)
+        assert np.abs(kch[:, p] - kr).max() <= 1e-6 * max(1.0, np.abs(kr).max()), p
+        assert np.array_equal(vch[:, p], v[p].reshape(KVH, 128)), p
+    assert np.all(kch[:, M:] == 7.0) and np.all(vch[:, M:] == 7.0)
+    return err
+
+
+@pytest.mark.parametrize("M,H,KVH", [(1, 4, 1), (5, 4, 1), (64, 8, 2), (70, 8, 2), (130, 4, 4), (200, 20, 5)])
+def test_attn_prefill_small(M, H, KVH):
+    _prefill_check(60 + M, M, H, KVH, S=M + 17)
+
+
+@pytest.mark.timeout(600)
+def test_attn_prefill_model_shape_sampled_rows():
+    # 4096 tokens, 20 query / 5 key-value heads: sampled rows at block edges
+    _prefill_check(61, 4096, 20, 5, rows=[0, 1, 63, 64, 65, 1000, 2047, 2048, 4094, 4095])
+
+
+def test_attn_prefill_then_decode():
+    """The caches a prefill writes carry on into decode steps: the token at
+    position M against the oracle's decode over its own fp32 rotations."""
+    bl = _bl()
+    M, H, KVH, S, base = 100, 20, 5, 160, 10000.0
+    rng = np.random.default_rng(62)
+    qkv = rng.standard_normal((M, (H + 2 * KVH) * 128)).astype(np.float32)
+    d_qkv = to_dev(qkv)
+    rc, rs = bl.rope_table(S, 128, base, device=dev())
+    kc = torch.zeros((KVH, S, 128), dtype=torch.float32, device=dev())
+    vc = torch.zeros_like(kc)
+    bl.attn_prefill(d_qkv[:, :H * 128], d_qkv[:, H * 128:(H + KVH) * 128], d_qkv[:, (H + KVH) * 128:],
+                    kc, vc, rc, rs, H, KVH)
+    kc_ref = np.zeros((KVH, S, 128), np.float32)
+    vc_ref = np.zeros((KVH, S, 128), np.float32)
+    for p in range(M):
+        kc_ref[:, p] = oracle.rope(qkv[p, H * 128:(H + KVH) * 128].reshape(KVH, 128), p, base).astype(np.float32)
+        vc_ref[:, p] = qkv[p, (H + KVH) * 128:].reshape(KVH, 128)
+    for pos in (M, M + 1):
+        qn = rng.standard_normal(H * 128).astype(np.float32)
+        kn = rng.standard_normal(KVH * 128).astype(np.float32)
+        vn = rng.standard_normal(KVH * 128).astype(np.float32)
+        o = host(bl.attn_decode(to_dev(qn), to_dev(kn), to_dev(vn), pos, kc, vc, rc, rs, H, KVH)).reshape(H, 128)
+        r = oracle.attn_decode(qn, kn, vn, pos, kc_ref, vc_ref, base, H, KVH)
+        assert np.abs(o - r).max() <= ATTN_TOL * max(1.0, np.abs(r).max()), pos
+        kc_ref[:, pos] = oracle.rope(kn.reshape(KVH, 128), pos, base).astype(np.float32)
+        vc_ref[:, pos] = vn.reshape(KVH, 128)

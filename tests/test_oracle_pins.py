@@ -495,3 +495,49 @@ def test_attn_grouped_query_equals_repeated_heads():
         s = keys @ qr[h] / math.sqrt(D)
         p = np.exp(s - s.max())
         assert np.allclose(gqa[h], p @ vals / p.sum(), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- prefill attention
+def _prefill_inputs(seed, M, H, KVH, D=128):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((M, H * D)).astype(np.float32),
+            rng.standard_normal((M, KVH * D)).astype(np.float32),
+            rng.standard_normal((M, KVH * D)).astype(np.float32))
+
+
+def test_attn_prefill_rows_match_the_decode_oracle():
+    """Row p of the prompt equals one decode step at position p over a cache of
+    the earlier tokens' rotated (fp32) keys: the numpy prefill oracle against
+    the C decode oracle, two separate writings of the same attention."""
+    M, H, KVH, D, base = 40, 8, 2, 128, 10000.0
+    q, k, v = _prefill_inputs(21, M, H, KVH)
+    rows = [0, 1, 17, 39]
+    got = oracle.attn_prefill_rows(q, k, v, base, H, KVH, rows, bf16_inputs=False)
+    kc = np.zeros((KVH, M, D), np.float32)
+    vc = np.zeros((KVH, M, D), np.float32)
+    for p in range(M):
+        kc[:, p] = oracle.rope(k[p].reshape(KVH, D), p, base).astype(np.float32)
+        vc[:, p] = v[p].reshape(KVH, D)
+    for n, p in enumerate(rows):
+        ref = oracle.attn_decode(q[p], k[p], v[p], p, kc, vc, base, H, KVH).reshape(-1)
+        assert np.abs(got[n] - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max()), p
+
+
+def test_attn_prefill_first_row_and_causality():
+    M, H, KVH, D = 12, 4, 1, 128
+    q, k, v = _prefill_inputs(22, M, H, KVH)
+    out = oracle.attn_prefill_rows(q, k, v, 500000.0, H, KVH, [0, 5])
+    # position 0 sees only itself: every head returns the (bf16-rounded) value
+    for h in range(H):
+        assert np.array_equal(out[0, h * D:(h + 1) * D], oracle.bf16_round(v[0]).astype(np.float64))
+    # later tokens do not change row 5
+    k2, v2 = k.copy(), v.copy()
+    k2[6:] += 3.0
+    v2[6:] -= 2.0
+    assert np.array_equal(oracle.attn_prefill_rows(q, k2, v2, 500000.0, H, KVH, [5]), out[1:2])
+
+
+def test_bf16_round_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -2.5, 3.0e-3], np.float32)
+    want = np.array([1.0, 1.0, 1.0 + 2.0 ** -6, 1.0, -2.5, 0.0030059814453125], np.float32)
+    assert np.array_equal(oracle.bf16_round(x), want)
