@@ -19,7 +19,8 @@
 //       S^T = K Q^T  with v_mfma_f32_16x16x32_bf16 (keys the first operand,
 //         so lane (g, c) holds keys 4g..4g+3 of each 16-key tile for query c);
 //       online softmax in fp32 (base-2 exponentials of the pre-scaled
-//         scores), the maximum shared by the four lanes of a query;
+//         scores), the maximum shared by the four lanes of a query and moved
+//         only when a block's exceeds it by more than 8;
 //       O^T += V^T P^T with the probabilities rounded to bf16 straight from
 //         the score registers: the k index of the product runs over the keys
 //         in the order the score layout holds them, and the transposed value
@@ -179,36 +180,49 @@ __global__ __launch_bounds__(256) void k_attn_fwd(PrefArgs a) {
                 sc[c] = mfma_bf16(*reinterpret_cast<const bf16x8 *>(&ks[(16 * c + lr) * kKStride + 32 * s + 8 * g]),
                                   qf[s], sc[c]);
         }
-        // online softmax in base 2
-        const bool diag = kblk == qblk;
+        // online softmax in base 2 (scores pre-scaled by log2(e)/sqrt(128))
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[c][i] *= a.scale_log2;
+        if (kblk == qblk) {   // the diagonal block: keys past the query get no weight
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kblk * kPB + 16 * c + 4 * g + i > qrow) sc[c][i] = -INFINITY;
+        }
         float bm = -INFINITY;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = sc[c][i] * a.scale_log2;
-                if (diag && kblk * kPB + 16 * c + 4 * g + i > qrow) v = -INFINITY;
-                sc[c][i] = v;
-                bm = fmaxf(bm, v);
-            }
+            for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[c][i]);
         bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const float m_new = fmaxf(m_run, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // The running maximum moves only when a block's exceeds it by more
+        // than 8 (so every weight stays below 2^8, well inside bf16 and fp32);
+        // the accumulators are rescaled only then, which after the first
+        // blocks is rare.
+        const bool upd = bm > m_run + 8.0f;
+        if (__any(upd)) {
+            const float m_new = upd ? bm : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 for the first block
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        }
         float ps = 0.0f;
         bf16x8 pb[2];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sc[c][i] - m_new);
+                const float p = __builtin_amdgcn_exp2f(sc[c][i] - m_run);
                 ps += p;
                 pb[c >> 1][4 * (c & 1) + i] = to_bf(p);
             }
-        l_run = l_run * alpha + ps;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        l_run += ps;
         // O^T += V^T P^T: k slot 8g + j of step s is key 32s + 4g + j (j < 4)
         // or 32s + 16 + 4g + (j - 4)
 #pragma unroll
