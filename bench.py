@@ -16,7 +16,8 @@ The same line carries the kernel's roofline, the oracle's CPU baseline, and
 secondary figures under "extra": the chained 30-layer decode (quantize ->
 q|k|v -> o -> RMSNorm -> gate|up -> ReLU^2 -> RMSNorm -> down per layer),
 batched decode at M=16 and M=64, decode attention over a 4096-token cache and
-the whole decode step with attention, prefill int8 TOPS, ternarization.
+the whole decode step with attention, prefill int8 TOPS, the prefill with
+attention and the prefill attention alone, ternarization.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -384,6 +385,23 @@ def main():
         extra["prefill_m4096_stack_ms"] = round(t, 2)
         log(f"config 5 prefill: {extra['prefill_m4096_stack_tops']} TOPS")
         del bp
+        # the same prompt with attention (positions 0 .. 4095, caches filled),
+        # and the prefill attention alone on one layer's q|k|v
+        cache = stack.alloc_kv(len(layers), M, dev)
+        bp = {}
+        t = timer.run(lambda: stack.prefill_attn(xp, layers, cache, bufs=bp), 3, 1)
+        extra["prefill_m4096_attn_stack_ms"] = round(t, 2)
+        qkv = bp["p_qkv"]
+        att = torch.empty((M, H), dtype=torch.float32, device=dev)
+        t = timer.run(lambda: bl.attn_prefill(qkv[:, :H], qkv[:, H:H + KV], qkv[:, H + KV:], cache.k[0], cache.v[0],
+                                              cache.rope_cos, cache.rope_sin, stack.N_HEADS, stack.N_KV_HEADS,
+                                              out=att), 10, 2)
+        flops = 4 * 128 * stack.N_HEADS * M * (M + 1) / 2
+        extra["attn_prefill_m4096_us"] = round(t * 1e3, 1)
+        extra["attn_prefill_m4096_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
+        log(f"prefill with attention, M=4096: {extra['prefill_m4096_attn_stack_ms']} ms; attention alone "
+            f"{t * 1e3:.1f} us/layer, {extra['attn_prefill_m4096_tflops']} TFLOPS (bf16 products, causal)")
+        del bp, cache, att
         # offline ternarization (absmean + pack) of one 6912 x 2560 master
         W = torch.from_numpy(synth.layer_weight(0, "gate")).to(dev)
         pk = torch.empty((I // 4, H), dtype=torch.uint8, device=dev)

@@ -16,7 +16,10 @@ position embeddings, grouped-query attention, subln before o_proj):
   x -> q|k|v -> RoPE, key/value cache append and attention over positions
     0..pos (bl_attn_decode) -> attn_sub_norm RMSNorm -> quantize -> o
     BitLinear (bl_subln_gemv_w2a8, one launch at decode size) -> FFN chain.
-Input norms and residual additions stay out, as in layer_forward.
+prefill_layer_attn is the same at M prompt tokens (positions 0 .. M-1): the
+causal attention of bl_attn_prefill, which also fills the caches that the
+decode steps then extend.  Input norms and residual additions stay out, as in
+layer_forward.
 
 Every step runs in libbitlinear through the binding; this module only holds
 weights and orders calls.  Weights are ternarized on the device from seeded
@@ -218,4 +221,49 @@ def decode_step_attn(x: torch.Tensor, layers, cache: KVCache, pos: int, eps: flo
     cur = x
     for i, lw in enumerate(layers):
         cur = decode_layer_attn(cur, lw, cache, i, pos, eps, out=outs[i & 1], bufs=bufs)
+    return cur
+
+
+def prefill_layer_attn(x: torch.Tensor, lw: LayerWeights, cache: KVCache, layer: int, eps: float = 1e-5,
+                       out: torch.Tensor = None, bufs: dict = None, debug: dict = None):
+    """One layer over a prompt of M tokens at positions 0 .. M-1 with
+    attention (the prefill counterpart of decode_layer_attn): x [M,H] ->
+    [M,H] fp32; the layer's caches receive positions 0 .. M-1."""
+    M = x.shape[0]
+    if M > cache.max_seq:
+        raise ValueError("the prompt is longer than the cache")
+    dev = x.device
+    if bufs is None:
+        bufs = {}
+    if bufs.get("p_m") != M:
+        bufs["p_m"] = M
+        bufs["p_qkv"] = torch.empty((M, sum(QKV_SEGS)), dtype=torch.float32, device=dev)
+        bufs["p_att"] = torch.empty((M, H), dtype=torch.float32, device=dev)
+        bufs["p_y_o"] = torch.empty((M, H), dtype=torch.float32, device=dev)
+    y_qkv, att, y_o = bufs["p_qkv"], bufs["p_att"], bufs["p_y_o"]
+    _contract(M)(x, lw.packed_qkv, lw.w_qkv, seg_n=QKV_SEGS, y=y_qkv)
+    bl.attn_prefill(y_qkv[:, :H], y_qkv[:, H:H + KV], y_qkv[:, H + KV:], cache.k[layer], cache.v[layer],
+                    cache.rope_cos, cache.rope_sin, N_HEADS, N_KV_HEADS, out=att)
+    q_o = a_o = None
+    if debug is not None:
+        q_o = torch.empty((M, H), dtype=torch.int8, device=dev)
+        a_o = torch.empty(M, dtype=torch.float32, device=dev)
+    bl.subln_gemv_w2a8(att, lw.packed_o, lw.w_o, eps=eps, y=y_o, q_out=q_o, a_out=a_o)
+    if debug is not None:
+        debug.update(y_qkv=y_qkv.clone(), att=att.clone(), q_o=q_o, a_o=a_o, y_o=y_o.clone())
+    return bl.ffn_chain(y_o, lw.packed_gu, lw.w_gu, lw.packed_down, lw.w_down, eps=eps, y=out)
+
+
+def prefill_attn(x: torch.Tensor, layers, cache: KVCache, eps: float = 1e-5, bufs: dict = None):
+    """All layers over a prompt with attention; returns the last layer's output."""
+    if bufs is None:
+        bufs = {}
+    M = x.shape[0]
+    outs = bufs.get("p_outs")
+    if outs is None or outs[0].shape[0] != M:
+        outs = [torch.empty((M, H), dtype=torch.float32, device=x.device) for _ in range(2)]
+        bufs["p_outs"] = outs
+    cur = x
+    for i, lw in enumerate(layers):
+        cur = prefill_layer_attn(cur, lw, cache, i, eps, out=outs[i & 1], bufs=bufs)
     return cur

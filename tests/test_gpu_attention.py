@@ -293,3 +293,49 @@ def test_attn_prefill_then_decode():
         assert np.abs(o - r).max() <= ATTN_TOL * max(1.0, np.abs(r).max()), pos
         kc_ref[:, pos] = oracle.rope(kn.reshape(KVH, 128), pos, base).astype(np.float32)
         vc_ref[:, pos] = vn.reshape(KVH, 128)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_layer_with_attention_stagewise():
+    """stack.prefill_layer_attn over 2 layers of a 130-token prompt, each stage
+    against the oracle on the GPU's own input to it; then one decode step
+    continues from the caches the prefill wrote."""
+    from bit_ternary_weight_amd import stack, synth
+    from gpu_helpers import F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16, max_ulp_diff
+    H, KV, M, L = synth.HIDDEN, synth.KV_DIM, 130, 2
+    layers = stack.build_layers(L, dev())
+    cache = stack.alloc_kv(L, 256, dev())
+    bits = synth.act_normal_bf16(70, M, H)
+    x, x_host = bf16_dev(bits), f32_of_bf16(bits)
+    rows = [0, 1, 63, 64, 129]
+    for l, lw in enumerate(layers):
+        codes, wms = {}, {}
+        for p, _, _ in synth.PROJECTIONS:
+            _, wm, c = oracle.ternarize_pack(synth.layer_weight(l, p))
+            codes[p], wms[p] = c, wm
+        dbg = {}
+        y = stack.prefill_layer_attn(x, lw, cache, l, debug=dbg)
+        qkv_codes = np.concatenate([codes["q"], codes["k"], codes["v"]])
+        wq = np.array([wms["q"], wms["k"], wms["v"]], np.float32)
+        _, _, _, r_qkv = oracle.bitlinear(x_host[rows], qkv_codes, [H, KV, KV], wq)
+        g_qkv = host(dbg["y_qkv"])
+        assert_rows_close(g_qkv[rows], r_qkv, F32_TOL, f"qkv {l}")
+        assert max_ulp_diff(g_qkv[rows], r_qkv) == 0
+        g_att = host(dbg["att"])
+        r_att = oracle.attn_prefill_rows(g_qkv[:, :H], g_qkv[:, H:H + KV], g_qkv[:, H + KV:], stack.ROPE_BASE,
+                                         20, 5, rows)
+        assert np.abs(g_att[rows] - r_att).max() <= 2.0 ** -8 * np.abs(g_qkv[:, H + KV:]).max(), l
+        rq, ra = oracle.quant_act(oracle.rmsnorm(g_att[rows], None, 1e-5))
+        assert_exact(host(dbg["q_o"])[rows], rq, f"attn_sub_norm codes {l}")
+        assert_exact(host(dbg["a_o"])[rows], ra, f"attn_sub_norm scales {l}")
+        r_o = oracle.rescale(oracle.contract(rq, codes["o"]), ra, None, wms["o"])
+        assert_exact(host(dbg["y_o"])[rows].view(np.uint32), r_o.view(np.uint32), f"o {l}")
+        gu = np.concatenate([codes["gate"], codes["up"]])
+        ch = oracle.ffn_chain(r_o, gu, np.array([wms["gate"], wms["up"]], np.float32), codes["down"], wms["down"])
+        yh = host(y)
+        assert_rows_close(yh[rows], ch["y"], F32_TOL, f"layer {l}")
+        x, x_host = y.clone(), yh
+    # a decode step at position M reads the caches the prefill wrote
+    dbg = {}
+    stack.decode_layer_attn(x[-1:].contiguous(), layers[0], cache, 0, M, debug=dbg)
+    assert np.isfinite(host(dbg["att"])).all()
