@@ -13,8 +13,10 @@
 //   k_attn_prep: per 64 tokens and one head slot, the rotated queries and
 //     keys rounded to bf16 (and the keys in fp32 into the cache), the values
 //     into the cache and, rounded to bf16, transposed to [dimension][token].
-//   k_attn_fwd: one workgroup per (query head, block of 64 queries), heaviest
-//     blocks first; wave w owns queries 16w .. 16w+15.  Per block of 64 keys
+//   k_attn_fwd: one workgroup per (query head, block of 128 queries),
+//     heaviest blocks first; wave w owns two tiles of 16 queries, so every
+//     key and value operand read from LDS feeds two products.  Per block of
+//     64 keys
 //     (staged through LDS, the next block's loads in flight meanwhile):
 //       S^T = K Q^T  with v_mfma_f32_16x16x32_bf16 (keys the first operand,
 //         so lane (g, c) holds keys 4g..4g+3 of each 16-key tile for query c);
@@ -35,7 +37,9 @@ namespace bl {
 namespace {
 
 constexpr int kPD = 128;                 // head dimension
-constexpr int kPB = 64;                  // tokens per query block and per key block
+constexpr int kPB = 64;                  // tokens per key block (and per block of the prep kernel)
+constexpr int kQT = 2;                   // 16-query tiles per wave
+constexpr int kPQ = 4 * 16 * kQT;        // queries per workgroup (4 waves)
 constexpr int kKStride = kPD + 8;        // LDS key row, bf16 elements (272 bytes: rows 4 banks apart)
 constexpr int kVStride = kPB + 4;        // LDS transposed value row, bf16 elements (136 bytes)
 
@@ -122,24 +126,28 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void k_attn_fwd(PrefArgs a) {
+// Two workgroups a CU: the register budget is held to 256 a lane (no spills).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(PrefArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 ks[kPB * kKStride];
     __shared__ __attribute__((aligned(16))) __bf16 vs[kPD * kVStride];
-    const int nqb = a.Mp / kPB;
+    const int nqb = a.Mp / kPQ;
     const int qblk = nqb - 1 - (int)blockIdx.x / a.H;   // heaviest (latest) query blocks first
     const int h = (int)blockIdx.x % a.H;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, lr = lane & 15;
     const int kvh = h / a.G;
-    const int qrow = qblk * kPB + 16 * w + lr;           // this lane's query (position)
+    int qrow[kQT];                                       // this lane's queries (positions), one per tile
+#pragma unroll
+    for (int u = 0; u < kQT; ++u) qrow[u] = qblk * kPQ + 16 * (kQT * w + u) + lr;
     const __bf16 *kbase = a.kb + (size_t)kvh * a.Mp * kPD;
     const __bf16 *vbase = a.vt + (size_t)kvh * kPD * a.Mp;
 
-    // second operand of S^T = K Q^T: Q[query lr][dimensions 32s + 8g .. +7]
-    bf16x8 qf[4];
-    {
-        const __bf16 *qp = a.qb + ((size_t)h * a.Mp + qrow) * kPD + 8 * g;
+    // second operands of S^T = K Q^T: Q[query lr of tile u][dimensions 32s + 8g .. +7]
+    bf16x8 qf[kQT][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+    for (int u = 0; u < kQT; ++u) {
+        const __bf16 *qp = a.qb + ((size_t)h * a.Mp + qrow[u]) * kPD + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[u][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
     }
     // staging: 1024 16-byte pieces of keys (row c >> 4, piece c & 15) and of
     // transposed values (row c >> 3, piece c & 7), four of each per thread
@@ -152,12 +160,19 @@ __global__ __launch_bounds__(256) void k_attn_fwd(PrefArgs a) {
             vr[r] = *reinterpret_cast<const bf16x8 *>(vbase + (size_t)(c >> 3) * a.Mp + kb0 + 8 * (c & 7));
         }
     };
-    f32x4 o[8];
+    f32x4 o[kQT][8];
+    float m_run[kQT], l_run[kQT];   // l_run: this lane's part (its keys) of the sum
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;   // l_run: this lane's part (its keys) of the sum
+    for (int u = 0; u < kQT; ++u) {
+        m_run[u] = -INFINITY;
+        l_run[u] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[u][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int nkb = (qblk + 1) * (kPQ / kPB);   // key blocks up to the last query of the block
+    const int kdiag = qblk * (kPQ / kPB);       // key blocks from here on can hold keys past a query
     fetch(0);
-    for (int kblk = 0; kblk <= qblk; ++kblk) {
+    for (int kblk = 0; kblk < nkb; ++kblk) {
         __syncthreads();   // every wave is done with the previous block
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -168,63 +183,71 @@ __global__ __launch_bounds__(256) void k_attn_fwd(PrefArgs a) {
             vd[1] = bf16x4{vr[r][4], vr[r][5], vr[r][6], vr[r][7]};
         }
         __syncthreads();
-        if (kblk < qblk) fetch((kblk + 1) * kPB);
+        if (kblk + 1 < nkb) fetch((kblk + 1) * kPB);
 
-        // S^T for 4 tiles of 16 keys: lane (g, lr) gets keys 16c + 4g + i of query lr
-        f32x4 sc[4];
+        // S^T for 4 tiles of 16 keys, each key operand read once for both
+        // query tiles: lane (g, lr) gets keys 16c + 4g + i of query lr
+        f32x4 sc[kQT][4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            sc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sc[c] = mfma_bf16(*reinterpret_cast<const bf16x8 *>(&ks[(16 * c + lr) * kKStride + 32 * s + 8 * g]),
-                                  qf[s], sc[c]);
+            for (int u = 0; u < kQT; ++u) sc[u][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[(16 * c + lr) * kKStride + 32 * s + 8 * g]);
+#pragma unroll
+                for (int u = 0; u < kQT; ++u) sc[u][c] = mfma_bf16(kf, qf[u][s], sc[u][c]);
+            }
         }
-        // online softmax in base 2 (scores pre-scaled by log2(e)/sqrt(128))
+        bf16x8 pb[kQT][2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[c][i] *= a.scale_log2;
-        if (kblk == qblk) {   // the diagonal block: keys past the query get no weight
+        for (int u = 0; u < kQT; ++u) {
+            // online softmax in base 2 (scores pre-scaled by log2(e)/sqrt(128))
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (kblk * kPB + 16 * c + 4 * g + i > qrow) sc[c][i] = -INFINITY;
-        }
-        float bm = -INFINITY;
+                for (int i = 0; i < 4; ++i) sc[u][c][i] *= a.scale_log2;
+            if (kblk >= kdiag) {   // blocks that reach past some query: those keys get no weight
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[c][i]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        // The running maximum moves only when a block's exceeds it by more
-        // than 8 (so every weight stays below 2^8, well inside bf16 and fp32);
-        // the accumulators are rescaled only then, which after the first
-        // blocks is rare.
-        const bool upd = bm > m_run + 8.0f;
-        if (__any(upd)) {
-            const float m_new = upd ? bm : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 for the first block
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-        }
-        float ps = 0.0f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sc[c][i] - m_run);
-                ps += p;
-                pb[c >> 1][4 * (c & 1) + i] = to_bf(p);
+                    for (int i = 0; i < 4; ++i)
+                        if (kblk * kPB + 16 * c + 4 * g + i > qrow[u]) sc[u][c][i] = -INFINITY;
             }
-        l_run += ps;
+            float bm = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[u][c][i]);
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            // The running maximum moves only when a block's exceeds it by more
+            // than 8 (so every weight stays below 2^8, well inside bf16 and
+            // fp32); the accumulators are rescaled only then, which after the
+            // first blocks is rare.  A block wholly past the query (-inf) never
+            // moves it: every query has seen key 0 in block 0.
+            const bool upd = bm > m_run[u] + 8.0f;
+            if (__any(upd)) {
+                const float m_new = upd ? bm : m_run[u];
+                const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);   // 0 for the first block
+                m_run[u] = m_new;
+                l_run[u] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[u][dt] *= alpha;
+            }
+            float ps = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(sc[u][c][i] - m_run[u]);
+                    ps += p;
+                    pb[u][c >> 1][4 * (c & 1) + i] = to_bf(p);
+                }
+            l_run[u] += ps;
+        }
         // O^T += V^T P^T: k slot 8g + j of step s is key 32s + 4g + j (j < 4)
-        // or 32s + 16 + 4g + (j - 4)
+        // or 32s + 16 + 4g + (j - 4); each value operand read once for both tiles
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -233,29 +256,33 @@ __global__ __launch_bounds__(256) void k_attn_fwd(PrefArgs a) {
                 const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vrow);
                 const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vrow + 16);
                 const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[dt] = mfma_bf16(va, pb[s], o[dt]);
+#pragma unroll
+                for (int u = 0; u < kQT; ++u) o[u][dt] = mfma_bf16(va, pb[u][s], o[u][dt]);
             }
     }
-    float l = l_run + __shfl_xor(l_run, 16, 64);
-    l = l + __shfl_xor(l, 32, 64);
-    if (qrow >= a.M) return;
-    const float inv = 1.0f / l;
-    float *orow = a.out + (size_t)qrow * a.ldo + h * kPD + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        float4 v;
-        v.x = o[dt][0] * inv;
-        v.y = o[dt][1] * inv;
-        v.z = o[dt][2] * inv;
-        v.w = o[dt][3] * inv;
-        *reinterpret_cast<float4 *>(orow + 16 * dt) = v;
+    for (int u = 0; u < kQT; ++u) {
+        float l = l_run[u] + __shfl_xor(l_run[u], 16, 64);
+        l = l + __shfl_xor(l, 32, 64);
+        if (qrow[u] >= a.M) continue;
+        const float inv = 1.0f / l;
+        float *orow = a.out + (size_t)qrow[u] * a.ldo + h * kPD + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            float4 v;
+            v.x = o[u][dt][0] * inv;
+            v.y = o[u][dt][1] * inv;
+            v.z = o[u][dt][2] * inv;
+            v.w = o[u][dt][3] * inv;
+            *reinterpret_cast<float4 *>(orow + 16 * dt) = v;
+        }
     }
 }
 
 } // namespace
 
 size_t attn_prefill_workspace_bytes(int M, int n_heads, int n_kv_heads) {
-    const size_t Mp = (size_t)(M + kPB - 1) / kPB * kPB;
+    const size_t Mp = (size_t)(M + kPQ - 1) / kPQ * kPQ;
     return Mp * kPD * sizeof(__bf16) * ((size_t)n_heads + 2 * (size_t)n_kv_heads);
 }
 
@@ -266,16 +293,15 @@ hipError_t launch_attn_prefill(const float *q, const float *k, const float *v, i
     a.q = q; a.k = k; a.v = v; a.ldx = ldx;
     a.k_cache = k_cache; a.v_cache = v_cache; a.max_seq = max_seq;
     a.rcos = rcos; a.rsin = rsin;
-    a.M = M; a.Mp = (M + kPB - 1) / kPB * kPB; a.H = H; a.KVH = KVH; a.G = H / KVH;
+    a.M = M; a.Mp = (M + kPQ - 1) / kPQ * kPQ; a.H = H; a.KVH = KVH; a.G = H / KVH;
     a.qb = static_cast<__bf16 *>(ws);
     a.kb = a.qb + (size_t)H * a.Mp * kPD;
     a.vt = a.kb + (size_t)KVH * a.Mp * kPD;
     a.out = out; a.ldo = ldo;
     a.scale_log2 = 1.4426950408889634f / sqrtf((float)kPD);
-    const int nqb = a.Mp / kPB;
-    hipLaunchKernelGGL(k_attn_prep, dim3(nqb, H + 2 * KVH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_prep, dim3(a.Mp / kPB, H + 2 * KVH), dim3(256), 0, s, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_fwd, dim3(nqb * H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_fwd, dim3(a.Mp / kPQ * H), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
