@@ -191,6 +191,22 @@ def attn_decode_timing(torch, bl, stack, timer, dev, n_layers, H, KV, keep=False
     return (t, gbs, cache) if keep else (t, gbs)
 
 
+def attn_prefill_timing(torch, bl, stack, timer, dev, H, KV, qkv=None, cache=None):
+    """Prefill attention over a 4096-token prompt (20 query / 5 key-value
+    heads): ms per call and causal TFLOPS.  qkv defaults to N(0,1)."""
+    M = ATTN_CTX
+    if qkv is None:
+        qkv = torch.randn((M, H + 2 * KV), generator=torch.Generator(device=dev).manual_seed(6), device=dev)
+    if cache is None:
+        cache = stack.alloc_kv(1, M, dev)
+    att = torch.empty((M, H), dtype=torch.float32, device=dev)
+    t = timer.run(lambda: bl.attn_prefill(qkv[:, :H], qkv[:, H:H + KV], qkv[:, H + KV:], cache.k[0], cache.v[0],
+                                          cache.rope_cos, cache.rope_sin, stack.N_HEADS, stack.N_KV_HEADS,
+                                          out=att), 10, 2)
+    flops = 4 * 128 * stack.N_HEADS * M * (M + 1) / 2
+    return t, round(flops / (t * 1e-3) / 1e12, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +219,8 @@ def main():
                     help="only the dominant-kernel loop (for profiler runs)")
     ap.add_argument("--attn-only", action="store_true",
                     help="only the decode attention loop at position 4095 over 30 layers' caches (for profiler runs)")
+    ap.add_argument("--attn-prefill-only", action="store_true",
+                    help="only the prefill attention over a 4096-token prompt (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
@@ -234,6 +252,10 @@ def main():
         t, gbs = attn_decode_timing(torch, bl, stack, timer, dev, args.layers, H, KV)
         print(json.dumps({"attn_decode_ctx4096_us_per_layer": round(t * 1e3, 3), "attn_decode_ctx4096_gbs": gbs}),
               flush=True)
+        return
+    if args.attn_prefill_only:
+        t, tf = attn_prefill_timing(torch, bl, stack, timer, dev, H, KV)
+        print(json.dumps({"attn_prefill_m4096_us": round(t * 1e3, 1), "attn_prefill_m4096_tflops": tf}), flush=True)
         return
     t_build = time.perf_counter()
     layers = stack.build_layers(args.layers, dev, workers=16)
@@ -391,17 +413,12 @@ def main():
         bp = {}
         t = timer.run(lambda: stack.prefill_attn(xp, layers, cache, bufs=bp), 3, 1)
         extra["prefill_m4096_attn_stack_ms"] = round(t, 2)
-        qkv = bp["p_qkv"]
-        att = torch.empty((M, H), dtype=torch.float32, device=dev)
-        t = timer.run(lambda: bl.attn_prefill(qkv[:, :H], qkv[:, H:H + KV], qkv[:, H + KV:], cache.k[0], cache.v[0],
-                                              cache.rope_cos, cache.rope_sin, stack.N_HEADS, stack.N_KV_HEADS,
-                                              out=att), 10, 2)
-        flops = 4 * 128 * stack.N_HEADS * M * (M + 1) / 2
+        t, tf = attn_prefill_timing(torch, bl, stack, timer, dev, H, KV, qkv=bp["p_qkv"], cache=cache)
         extra["attn_prefill_m4096_us"] = round(t * 1e3, 1)
-        extra["attn_prefill_m4096_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
+        extra["attn_prefill_m4096_tflops"] = tf
         log(f"prefill with attention, M=4096: {extra['prefill_m4096_attn_stack_ms']} ms; attention alone "
-            f"{t * 1e3:.1f} us/layer, {extra['attn_prefill_m4096_tflops']} TFLOPS (bf16 products, causal)")
-        del bp, cache, att
+            f"{t * 1e3:.1f} us/layer, {tf} TFLOPS (bf16 products, causal)")
+        del bp, cache
         # offline ternarization (absmean + pack) of one 6912 x 2560 master
         W = torch.from_numpy(synth.layer_weight(0, "gate")).to(dev)
         pk = torch.empty((I // 4, H), dtype=torch.uint8, device=dev)
