@@ -60,6 +60,10 @@ _SIGS = {
     "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "bl_rmsnorm_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _P, _P]),
     "bl_attn_prefill_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_ste_grad_input_workspace_bytes": (_S, [_I, _I]),
+    "bl_ste_grad_weight_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_ste_grad_input": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "bl_ste_grad_weight": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _S, _P]),
     "bl_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_subln_gemv_workspace_bytes": (_S, [_I, _I]),
     "bl_subln_gemv_w2a8": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
@@ -422,3 +426,40 @@ def attn_prefill(q, k, v, k_cache, v_cache, rope_cos, rope_sin, n_heads, n_kv_he
                                _ptr(k_cache), _ptr(v_cache), int(max_seq), _ptr(rope_cos), _ptr(rope_sin),
                                _ptr(out), out.stride(0), _ptr(ws), ws.numel(), _stream(dev)))
     return out
+
+
+def ste_grad_input(dy, packed, w_mean, dx=None):
+    """dX = dY . (codes * w_mean) for dy [M,N] bf16 and one packed weight
+    segment [N/4,K] (see bl_ste_grad_input); returns dx [M,K] fp32."""
+    dev = _dev(dy, packed, w_mean)
+    M, N = dy.shape
+    K = packed.shape[1]
+    _need(dy, (M, N), (torch.bfloat16,), "dy")
+    _need(packed, (N // 4, K), (torch.uint8,), "packed")
+    _need(w_mean, (1,), (torch.float32,), "w_mean")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=dev)
+    _need(dx, (M, K), (torch.float32,), "dx")
+    ws = workspace(dev, raw.bl_ste_grad_input_workspace_bytes(N, K))
+    _check(raw.bl_ste_grad_input(_ptr(dy), M, N, K, _ptr(packed), _ptr(w_mean), _ptr(dx), _ptr(ws), ws.numel(),
+                                 _stream(dev)))
+    return dx
+
+
+def ste_grad_weight(dy, q, a, dw=None):
+    """dW = sum_m bf16(dY[m] / a[m]) (x) q[m] for dy [M,N] bf16 and the
+    forward's activation codes q [M,K] int8 and scales a [M] (see
+    bl_ste_grad_weight); returns dw [N,K] fp32."""
+    dev = _dev(dy, q, a)
+    M, N = dy.shape
+    K = q.shape[1]
+    _need(dy, (M, N), (torch.bfloat16,), "dy")
+    _need(q, (M, K), (torch.int8,), "q")
+    _need(a, (M,), (torch.float32,), "a")
+    if dw is None:
+        dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    _need(dw, (N, K), (torch.float32,), "dw")
+    ws = workspace(dev, raw.bl_ste_grad_weight_workspace_bytes(M, N, K))
+    _check(raw.bl_ste_grad_weight(_ptr(dy), _ptr(q), _ptr(a), M, N, K, _ptr(dw), _ptr(ws), ws.numel(),
+                                  _stream(dev)))
+    return dw

@@ -17,6 +17,7 @@
 
 #include "bl_attn.h"
 #include "bl_common.h"
+#include "bl_ste.h"
 
 namespace {
 
@@ -693,6 +694,50 @@ int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int
     return check_hip(bl::launch_attn_prefill(q, k, v, ldx, M, n_heads, n_kv_heads, k_cache, v_cache, max_seq,
                                              rope_cos, rope_sin, out, ldo, ws, (hipStream_t)stream),
                      fn);
+}
+
+size_t bl_ste_grad_input_workspace_bytes(int N, int K) {
+    if (N < 1 || K < 1) return 0;
+    return align256(bl::ste_grad_input_ws_bytes(N, K));
+}
+
+size_t bl_ste_grad_weight_workspace_bytes(int M, int N, int K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return align256(bl::ste_grad_weight_ws_bytes(M, N, K));
+}
+
+static int ste_shape(const char *fn, int M, int N, int K) {
+    if (M < 128 || N < 128 || K < 128 || M % 128 || N % 128 || K % 128)
+        return fail(BL_ERR_SHAPE, "%s: M=%d N=%d K=%d (each a positive multiple of 128)", fn, M, N, K);
+    if ((size_t)M * N >= ((size_t)1 << 31) || (size_t)M * K >= ((size_t)1 << 31) || (size_t)N * K >= ((size_t)1 << 31))
+        return fail(BL_ERR_SHAPE, "%s: M=%d N=%d K=%d (each product below 2^31)", fn, M, N, K);
+    return BL_OK;
+}
+
+int bl_ste_grad_input(const void *dy, int M, int N, int K, const uint8_t *packed, const float *w_mean, float *dx,
+                      void *ws, size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_ste_grad_input";
+    if (!dy || !packed || !w_mean || !dx) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (int st = ste_shape(fn, M, N, K)) return st;
+    if (!aligned(dy, 16) || !aligned(packed, 16) || !aligned(dx, 16) || !aligned(w_mean, 4))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (int st = check_ws(fn, ws, ws_bytes, bl_ste_grad_input_workspace_bytes(N, K))) return st;
+    return check_hip(bl::launch_ste_grad_input((const __bf16 *)dy, M, N, K, packed, w_mean, dx, ws,
+                                               (hipStream_t)stream),
+                     fn);
+}
+
+int bl_ste_grad_weight(const void *dy, const int8_t *q, const float *a, int M, int N, int K, float *dw, void *ws,
+                       size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_ste_grad_weight";
+    if (!dy || !q || !a || !dw) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (int st = ste_shape(fn, M, N, K)) return st;
+    if (!aligned(dy, 16) || !aligned(q, 16) || !aligned(dw, 16) || !aligned(a, 4))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (int st = check_ws(fn, ws, ws_bytes, bl_ste_grad_weight_workspace_bytes(M, N, K))) return st;
+    return check_hip(bl::launch_ste_grad_weight((const __bf16 *)dy, M, N, K, q, a, dw, ws, (hipStream_t)stream), fn);
 }
 
 } // extern "C"

@@ -310,6 +310,33 @@ int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int
                     const float *rope_cos, const float *rope_sin,
                     float *out, int ldo, void *ws, size_t ws_bytes, bl_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * bl_ste_grad_input / bl_ste_grad_weight -- the backward pass of BitLinear in
+ * quantization-aware training.  [T] "BitLinear 的三步量化": the weight and
+ * activation quantizers of training pass the incoming gradient through
+ * unchanged (straight-through estimator), so with the fake-quantized
+ * W~ = codes * w_mean and x~ = q / a of the forward:
+ *   dX = dY . W~     (bl_ste_grad_input)
+ *   dW = dY^T . x~   (bl_ste_grad_weight; the gradient of the fp32 master W)
+ *   dy      [M][N] bf16 device, contiguous (the output gradient);
+ *   packed  [N/4][K] uint8 device, one weight segment; w_mean [1] fp32 device;
+ *   q, a    [M][K] int8 and [M] fp32 device: the forward's activation codes
+ *           and scales (bl_quant_act);
+ *   dx      out [M][K] fp32 device = (sum_n dy[m][n] code[n][k]) * w_mean;
+ *   dw      out [N][K] fp32 device = sum_m bf16(dy[m][n] / a[m]) q[m][k];
+ *   ws      scratch of bl_ste_grad_input_workspace_bytes(N, K) /
+ *           bl_ste_grad_weight_workspace_bytes(M, N, K) bytes.
+ * Precision: bf16 products (the codes and q exactly; dy / a rounded to
+ * nearest even) summed in fp32.  M, N, K positive multiples of 128, each
+ * product of two below 2^31; dy, packed, q, dx, dw 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t bl_ste_grad_input_workspace_bytes(int N, int K);
+size_t bl_ste_grad_weight_workspace_bytes(int M, int N, int K);
+int bl_ste_grad_input(const void *dy, int M, int N, int K, const uint8_t *packed, const float *w_mean,
+                      float *dx, void *ws, size_t ws_bytes, bl_stream stream);
+int bl_ste_grad_weight(const void *dy, const int8_t *q, const float *a, int M, int N, int K,
+                       float *dw, void *ws, size_t ws_bytes, bl_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -334,3 +334,22 @@ def attn_prefill_rows(q, k, v, base, n_heads, n_kv_heads, rows, bf16_inputs=True
             w = np.exp(s - s.max())
             out[n, h * D:(h + 1) * D] = (w @ vv[:p + 1, h // G, :]) / w.sum()
     return out
+
+
+def ste_grad_input(dy, codes, w_mean) -> np.ndarray:
+    """fp64 dX [M,K] = dY . W~ of BitLinear's straight-through backward, with
+    the fake-quantized weight W~ = codes * w_mean: (sum_n dy[m,n] codes[n,k])
+    * w_mean.  dy [M,N] (values, e.g. bf16 ones); codes [N,K] int8."""
+    dy = np.asarray(dy, np.float64)
+    return (dy @ np.asarray(codes, np.float64)) * float(np.float32(w_mean))
+
+
+def ste_grad_weight(dy, q, a) -> np.ndarray:
+    """fp64 dW [N,K] = dY^T . x~ of the straight-through backward, x~ = q / a,
+    with 1/a folded into the gradient first: sum_m bf16(fp32(dy[m,n] / a[m]))
+    q[m,k] (the rounding the bf16 product takes).  dy [M,N] fp32 values; q
+    [M,K] int8; a [M] fp32."""
+    dy = np.asarray(dy, np.float32)
+    a = np.asarray(a, np.float32)
+    s = bf16_round(dy / a[:, None])
+    return s.astype(np.float64).T @ np.asarray(q, np.float64)

@@ -260,3 +260,20 @@ def test_attn_prefill_validation(lib):
     assert call(ldo=2562) == lib.BL_ERR_SHAPE
     assert call(out=FAKE_MIS) == lib.BL_ERR_ALIGN
     assert call(wsb=need - 1) == lib.BL_ERR_WORKSPACE
+
+
+def test_ste_validation(lib):
+    raw = lib.raw
+    gi, gw = raw.bl_ste_grad_input, raw.bl_ste_grad_weight
+    ni = raw.bl_ste_grad_input_workspace_bytes(256, 384)
+    nw = raw.bl_ste_grad_weight_workspace_bytes(128, 256, 384)
+    assert ni >= 256 * 384 * 2 and nw >= (256 * 128 + 384 * 128) * 2
+    assert gi(None, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_NULL
+    assert gi(FAKE, 100, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_SHAPE
+    assert gi(FAKE, 128, 200, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_SHAPE
+    assert gi(FAKE_MIS, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_ALIGN
+    assert gi(FAKE, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni - 1, None) == lib.BL_ERR_WORKSPACE
+    assert gw(FAKE, None, FAKE, 128, 256, 384, FAKE, FAKE, nw, None) == lib.BL_ERR_NULL
+    assert gw(FAKE, FAKE, FAKE, 128, 256, 380, FAKE, FAKE, nw, None) == lib.BL_ERR_SHAPE
+    assert gw(FAKE, FAKE, FAKE, 128, 256, 384, FAKE_MIS, FAKE, nw, None) == lib.BL_ERR_ALIGN
+    assert gw(FAKE, FAKE, FAKE, 128, 256, 384, FAKE, FAKE, nw - 1, None) == lib.BL_ERR_WORKSPACE

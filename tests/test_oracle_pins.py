@@ -541,3 +541,38 @@ def test_bf16_round_is_nearest_even():
     x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -2.5, 3.0e-3], np.float32)
     want = np.array([1.0, 1.0, 1.0 + 2.0 ** -6, 1.0, -2.5, 0.0030059814453125], np.float32)
     assert np.array_equal(oracle.bf16_round(x), want)
+
+
+# ----------------------------------------------------------------------------- straight-through backward
+def test_ste_grad_input_is_the_gradient_through_the_fake_quantized_weight():
+    rng = np.random.default_rng(31)
+    W = rng.normal(0, 0.02, size=(12, 20)).astype(np.float32)
+    _, wm, codes = oracle.ternarize_pack(W)
+    dy = rng.standard_normal((3, 12)).astype(np.float32)
+    # against the matmul with the fake-quantized weight itself
+    Wq = oracle.fake_quant_weight(codes, wm).astype(np.float64)
+    assert np.allclose(oracle.ste_grad_input(dy, codes, wm), dy.astype(np.float64) @ Wq, rtol=1e-12, atol=1e-15)
+    # brute force, element by element
+    got = oracle.ste_grad_input(dy, codes, wm)
+    for m in range(3):
+        for k in range(20):
+            ref = sum(float(dy[m, n]) * int(codes[n, k]) for n in range(12)) * float(wm)
+            assert abs(got[m, k] - ref) <= 1e-12
+
+
+def test_ste_grad_weight_single_token_and_fake_quant_activations():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((1, 16)).astype(np.float32)
+    q, a = oracle.quant_act(x)
+    dy = np.array([[0.5, -1.25, 3.0]], np.float32)   # exact in bf16; dy / a then rounds
+    got = oracle.ste_grad_weight(dy, q, a)
+    # one token: an outer product of bf16(dy / a) and the codes
+    s = oracle.bf16_round(dy / a[:, None])[0].astype(np.float64)
+    assert np.array_equal(got, np.outer(s, q[0].astype(np.float64)))
+    # the same as dY^T . x~ with x~ = q / a, up to the bf16 rounding of dy / a
+    xs = oracle.quant_act(rng.standard_normal((40, 16)).astype(np.float32))
+    dy2 = rng.standard_normal((40, 3)).astype(np.float32)
+    xt = xs[0].astype(np.float64) / xs[1].astype(np.float64)[:, None]
+    ref = dy2.astype(np.float64).T @ xt
+    bound = 2.0 ** -8 * (np.abs(dy2).astype(np.float64).T @ np.abs(xt))
+    assert np.all(np.abs(oracle.ste_grad_weight(dy2, xs[0], xs[1]) - ref) <= bound)
