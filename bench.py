@@ -17,7 +17,8 @@ secondary figures under "extra": the chained 30-layer decode (quantize ->
 q|k|v -> o -> RMSNorm -> gate|up -> ReLU^2 -> RMSNorm -> down per layer),
 batched decode at M=16 and M=64, decode attention over a 4096-token cache and
 the whole decode step with attention, prefill int8 TOPS, the prefill with
-attention and the prefill attention alone, ternarization.
+attention and the prefill attention alone, the straight-through backward of
+quantization-aware training, ternarization.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -372,7 +373,7 @@ def main():
         extra["decode_m1_one_layer_warm_gbs"] = round(sb / (t * 1e-3) / 1e9, 1)
         del g
         # prefill GEMM (config 4): fused gate|up (2560 -> 2x6912) then down (6912 -> 2560), M=2048
-        M = 2048
+        M = M2 = 2048
         xg = torch.from_numpy(synth.act_normal_bf16(0, M, H).view(np.int16)).to(dev).view(torch.bfloat16)
         xd = torch.from_numpy(synth.act_normal_bf16(1, M, I).view(np.int16)).to(dev).view(torch.bfloat16)
         qg, ag = bl.quant_act(xg)
@@ -419,6 +420,20 @@ def main():
         log(f"prefill with attention, M=4096: {extra['prefill_m4096_attn_stack_ms']} ms; attention alone "
             f"{t * 1e3:.1f} us/layer, {tf} TFLOPS (bf16 products, causal)")
         del bp, cache
+        # the straight-through backward at M=2048 (quantization-aware
+        # training): dX and dW of the gate|up pair and of down
+        from bit_ternary_weight_amd import qat
+        for name, N, K in (("gateup", 2 * I, H), ("down", H, I)):
+            W = torch.randn((N, K), generator=torch.Generator(device=dev).manual_seed(7), device=dev) * 0.02
+            xb = torch.randn((M2, K), generator=torch.Generator(device=dev).manual_seed(8), device=dev)
+            _, saved = qat.forward(xb, W)
+            dy = torch.randn((M2, N), generator=torch.Generator(device=dev).manual_seed(9), device=dev).to(torch.bfloat16)
+            t = timer.run(lambda: qat.backward(dy, saved), 5, 2)
+            extra[f"ste_backward_m2048_{name}_tflops"] = round(2 * 2 * M2 * N * K / (t * 1e-3) / 1e12, 1)
+            extra[f"ste_backward_m2048_{name}_us"] = round(t * 1e3, 1)
+            del W, xb, saved, dy
+        log(f"straight-through backward M=2048: gate|up {extra['ste_backward_m2048_gateup_tflops']} TFLOPS, "
+            f"down {extra['ste_backward_m2048_down_tflops']} TFLOPS (bf16 products)")
         # offline ternarization (absmean + pack) of one 6912 x 2560 master
         W = torch.from_numpy(synth.layer_weight(0, "gate")).to(dev)
         pk = torch.empty((I // 4, H), dtype=torch.uint8, device=dev)

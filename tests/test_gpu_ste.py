@@ -59,3 +59,32 @@ def test_ste_shapes_rejected():
     with pytest.raises(RuntimeError):
         bl.ste_grad_input(dy, torch.zeros((32, 128), dtype=torch.uint8, device=dev()),
                           torch.ones(1, dtype=torch.float32, device=dev()))
+
+
+def test_qat_forward_backward_autograd():
+    """The online path end to end through torch.autograd: the forward equals
+    the oracle's BitLinear on W ternarized this step (bit-exact), the
+    gradients equal the straight-through oracle on the forward's own codes."""
+    from bit_ternary_weight_amd import qat
+    from gpu_helpers import F32_TOL, assert_exact, assert_rows_close
+    M, N, K = 256, 384, 640
+    W = synth.master_weight(95, N, K)
+    x = synth.act_normal_f32(96, M, K)
+    Wd = to_dev(W).requires_grad_(True)
+    xd = to_dev(x).requires_grad_(True)
+    y = qat.BitLinearFunction.apply(xd, Wd)
+    _, wm, codes = oracle.ternarize_pack(W)
+    q, a, A, ref = oracle.bitlinear(x, codes, None, wm)
+    yh = host(y.detach())
+    assert_rows_close(yh, ref, F32_TOL)
+    assert np.array_equal(yh.view(np.uint32), ref.view(np.uint32))
+    bits = synth.act_normal_bf16(97, M, N)
+    y.backward(bf16_dev(bits).float())
+    dy = f32_of_bf16(bits)
+    rx = oracle.ste_grad_input(dy, codes, wm)
+    rw = oracle.ste_grad_weight(dy, q, a)
+    bx = 2.0 ** -14 * (np.abs(dy).astype(np.float64) @ np.abs(codes).astype(np.float64)) * float(wm) + 2.0 ** -23 * np.abs(rx)
+    s = oracle.bf16_round(dy / a[:, None]).astype(np.float64)
+    bw = 2.0 ** -14 * (np.abs(s).T @ np.abs(q).astype(np.float64))
+    assert np.all(np.abs(host(xd.grad) - rx) <= bx)
+    assert np.all(np.abs(host(Wd.grad) - rw) <= bw)
