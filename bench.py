@@ -208,6 +208,23 @@ def attn_prefill_timing(torch, bl, stack, timer, dev, H, KV, qkv=None, cache=Non
     return t, round(flops / (t * 1e-3) / 1e12, 1)
 
 
+def ste_timing(torch, dev, timer, H, I, M=2048):
+    """The straight-through backward (dX and dW) of the gate|up pair and of
+    down at M tokens, bf16 output gradients: µs and TFLOPS per backward."""
+    from bit_ternary_weight_amd import qat
+    out = {}
+    for name, N, K in (("gateup", 2 * I, H), ("down", H, I)):
+        W = torch.randn((N, K), generator=torch.Generator(device=dev).manual_seed(7), device=dev) * 0.02
+        xb = torch.randn((M, K), generator=torch.Generator(device=dev).manual_seed(8), device=dev)
+        _, saved = qat.forward(xb, W)
+        dy = torch.randn((M, N), generator=torch.Generator(device=dev).manual_seed(9), device=dev).to(torch.bfloat16)
+        t = timer.run(lambda: qat.backward(dy, saved), 5, 2)
+        out[f"ste_backward_m{M}_{name}_tflops"] = round(2 * 2 * M * N * K / (t * 1e-3) / 1e12, 1)
+        out[f"ste_backward_m{M}_{name}_us"] = round(t * 1e3, 1)
+        del W, xb, saved, dy
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +239,8 @@ def main():
                     help="only the decode attention loop at position 4095 over 30 layers' caches (for profiler runs)")
     ap.add_argument("--attn-prefill-only", action="store_true",
                     help="only the prefill attention over a 4096-token prompt (for profiler runs)")
+    ap.add_argument("--ste-only", action="store_true",
+                    help="only the straight-through backward at M=2048 (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
@@ -253,6 +272,9 @@ def main():
         t, gbs = attn_decode_timing(torch, bl, stack, timer, dev, args.layers, H, KV)
         print(json.dumps({"attn_decode_ctx4096_us_per_layer": round(t * 1e3, 3), "attn_decode_ctx4096_gbs": gbs}),
               flush=True)
+        return
+    if args.ste_only:
+        print(json.dumps(ste_timing(torch, dev, timer, H, I)), flush=True)
         return
     if args.attn_prefill_only:
         t, tf = attn_prefill_timing(torch, bl, stack, timer, dev, H, KV)
@@ -422,16 +444,7 @@ def main():
         del bp, cache
         # the straight-through backward at M=2048 (quantization-aware
         # training): dX and dW of the gate|up pair and of down
-        from bit_ternary_weight_amd import qat
-        for name, N, K in (("gateup", 2 * I, H), ("down", H, I)):
-            W = torch.randn((N, K), generator=torch.Generator(device=dev).manual_seed(7), device=dev) * 0.02
-            xb = torch.randn((M2, K), generator=torch.Generator(device=dev).manual_seed(8), device=dev)
-            _, saved = qat.forward(xb, W)
-            dy = torch.randn((M2, N), generator=torch.Generator(device=dev).manual_seed(9), device=dev).to(torch.bfloat16)
-            t = timer.run(lambda: qat.backward(dy, saved), 5, 2)
-            extra[f"ste_backward_m2048_{name}_tflops"] = round(2 * 2 * M2 * N * K / (t * 1e-3) / 1e12, 1)
-            extra[f"ste_backward_m2048_{name}_us"] = round(t * 1e3, 1)
-            del W, xb, saved, dy
+        extra.update(ste_timing(torch, dev, timer, H, I))
         log(f"straight-through backward M=2048: gate|up {extra['ste_backward_m2048_gateup_tflops']} TFLOPS, "
             f"down {extra['ste_backward_m2048_down_tflops']} TFLOPS (bf16 products)")
         # offline ternarization (absmean + pack) of one 6912 x 2560 master
