@@ -255,7 +255,8 @@ def _prefill_check(seed, M, H, KVH, rows=None, S=None, base=500000.0):
     return err
 
 
-@pytest.mark.parametrize("M,H,KVH", [(1, 4, 1), (5, 4, 1), (64, 8, 2), (70, 8, 2), (130, 4, 4), (200, 20, 5)])
+@pytest.mark.parametrize("M,H,KVH", [(1, 4, 1), (5, 4, 1), (64, 8, 2), (70, 8, 2), (127, 2, 2), (128, 4, 1),
+                                     (129, 4, 1), (130, 4, 4), (200, 20, 5), (257, 6, 3)])
 def test_attn_prefill_small(M, H, KVH):
     _prefill_check(60 + M, M, H, KVH, S=M + 17)
 
