@@ -197,7 +197,7 @@ def test_subln_gemv(M, K, N, kind, gain, ydt):
     launch, the two-launch fallback (K not a multiple of 16) and the prefill
     path (M > 64), against the oracle's rmsnorm, quant_act, contract, rescale."""
     from bit_ternary_weight_amd import synth
-    from gpu_helpers import BF16_TOL, F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16
+    from gpu_helpers import assert_exact, bf16_dev, f32_of_bf16
     bl = _bl()
     if kind == "bf16":
         bits = synth.act_outliers_bf16(40 + M, M, K)

@@ -66,7 +66,7 @@ def test_qat_forward_backward_autograd():
     the oracle's BitLinear on W ternarized this step (bit-exact), the
     gradients equal the straight-through oracle on the forward's own codes."""
     from bit_ternary_weight_amd import qat
-    from gpu_helpers import F32_TOL, assert_exact, assert_rows_close
+    from gpu_helpers import F32_TOL, assert_rows_close
     M, N, K = 256, 384, 640
     W = synth.master_weight(95, N, K)
     x = synth.act_normal_f32(96, M, K)
