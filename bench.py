@@ -105,7 +105,7 @@ def capture(torch, fn):
     return g
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_v1_decode_config2_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_v1_decode_m1_7proj_traffic.md")
 TRAFFIC_SOURCES = ("bit_ternary_weight_amd/csrc/k_gemv.hip", "bit_ternary_weight_amd/csrc/bl_common.h")
 
 
@@ -285,7 +285,7 @@ def main():
     log(f"built {args.layers} layers in {time.perf_counter() - t_build:.1f} s")
     packed_total = sum(lw.nbytes_packed() for lw in layers)
 
-    # ---------------------------------------------------------------- headline: config 2, batched decode
+    # ---------------------------------------------------------------- headline: one-row decode, 7 projections a launch
     def seven_problems(M, layer_list, kind):
         probs = []
         for l, lw in enumerate(layer_list):
@@ -316,7 +316,7 @@ def main():
     ms = ms_pass / len(layers)
     sb = step_bytes7(1)
     value = sb / (ms * 1e-3) / 1e9
-    log(f"config 2 decode: {ms * 1e3:.2f} us/step, {value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak)")
+    log(f"decode M=1, 7 projections: {ms * 1e3:.2f} us/step, {value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak)")
 
     # The headline kernel is the only launch of a step: its average launch
     # duration over the timed region is the step time (back-to-back launches
@@ -355,14 +355,14 @@ def main():
     del graph
 
     if not args.no_extras:
-        # batched decode (config 3): M=16 and M=64, 7 projections per launch
+        # batched decode: M=16 and M=64, 7 projections per launch
         for M in (16, 64):
             pm = seven_problems(M, layers, "heavy")
             g = capture(torch, lambda pm=pm: [bl.gemv_w2a8_batched(pl) for pl in pm])
             t = timer.run(g.replay, 3, 1) / len(layers)
             extra[f"decode_m{M}_gbs"] = round(step_bytes7(M) / (t * 1e-3) / 1e9, 1)
             extra[f"decode_m{M}_us_per_layer"] = round(t * 1e3, 2)
-            log(f"config 3 decode M={M}: {t * 1e3:.2f} us/layer, {extra[f'decode_m{M}_gbs']} GB/s")
+            log(f"batched decode M={M}: {t * 1e3:.2f} us/layer, {extra[f'decode_m{M}_gbs']} GB/s")
             del g, pm
         # decode attention at the full 4096-token context: 30 layers' fp32
         # caches (20 query / 5 key-value heads x 128), the token at position
@@ -394,7 +394,7 @@ def main():
         t = timer.run(g.replay, 20, 2) / len(layers)
         extra["decode_m1_one_layer_warm_gbs"] = round(sb / (t * 1e-3) / 1e9, 1)
         del g
-        # prefill GEMM (config 4): fused gate|up (2560 -> 2x6912) then down (6912 -> 2560), M=2048
+        # prefill GEMMs: fused gate|up (2560 -> 2x6912) then down (6912 -> 2560), M=2048
         M = M2 = 2048
         xg = torch.from_numpy(synth.act_normal_bf16(0, M, H).view(np.int16)).to(dev).view(torch.bfloat16)
         xd = torch.from_numpy(synth.act_normal_bf16(1, M, I).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -418,8 +418,8 @@ def main():
         extra["prefill_m2048_gateup_gemm_tops"] = round(ops_gu / (t_gu * 1e-3) / 1e12, 1)
         extra["prefill_m2048_down_gemm_tops"] = round(ops_dn / (t_dn * 1e-3) / 1e12, 1)
         extra["prefill_m2048_ffn_us"] = round(t_all * 1e3, 1)
-        log(f"config 4 prefill: {tops:.1f} TOPS ({tops / INT8_PEAK_TOPS:.1%} of int8 peak)")
-        # prefill through the 30-layer stack, M=4096 (config 5)
+        log(f"prefill FFN M=2048: {tops:.1f} TOPS ({tops / INT8_PEAK_TOPS:.1%} of int8 peak)")
+        # prefill through the 30-layer stack, M=4096
         M = 4096
         xp = torch.from_numpy(synth.act_normal_bf16(0, M, H).view(np.int16)).to(dev).view(torch.bfloat16)
         bp = {}
@@ -428,7 +428,7 @@ def main():
         extra["prefill_m4096_stack_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
         extra["prefill_m4096_stack_frac_of_int8_peak"] = round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
         extra["prefill_m4096_stack_ms"] = round(t, 2)
-        log(f"config 5 prefill: {extra['prefill_m4096_stack_tops']} TOPS")
+        log(f"30-layer prefill M=4096: {extra['prefill_m4096_stack_tops']} TOPS")
         del bp
         # the same prompt with attention (positions 0 .. 4095, caches filled),
         # and the prefill attention alone on one layer's q|k|v

@@ -149,7 +149,7 @@ CONFIGS = (
 
 
 def config1():
-    """Config 1 inputs: (W fp32 [256,256], x fp32 [4,256])."""
+    """The small parity case's inputs: (W fp32 [256,256], x fp32 [4,256])."""
     W = master_weight(0, 256, 256)
     x = act_normal_f32(0, 4, 256)
     return W, x
