@@ -14,7 +14,7 @@
 //   dW: A = bf16(dY[m][n] / a[m]) transposed [N][M], B = q transposed [K][M]
 //       (bf16, exact), s = 1.
 // The GEMM: 128 x 128 output tiles, 4 waves of 64 x 64, 64-deep stages
-// through LDS (rows padded to 144 bytes, the next stage's loads in flight in
+// through LDS (pieces of a row permuted, the next stage's loads in flight in
 // registers), v_mfma_f32_16x16x32_bf16 with the B fragment as the first
 // operand so each lane ends with four consecutive outputs of one row
 // (16-byte stores).
@@ -30,7 +30,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 128;            // output tile (both dimensions)
 constexpr int kL = 64;             // contraction depth per stage
-constexpr int kLS = kL + 8;        // LDS row, bf16 elements (144 bytes: rows 36 banks apart)
+// LDS rows of 64 bf16 (128 bytes, 8 pieces of 16), unpadded: piece p of row r
+// sits at position p ^ ((r >> 1) & 7).  Lane group g of a k-step ks reads
+// piece (g & 1) | (g >> 1) << 2 | ks << 1 (a permutation of the k order that
+// the two operands share), so the 16 lanes of a group, and lanes 0-7 with
+// 32-39, touch distinct banks.
+__device__ __forceinline__ int lds_pos(int r, int p) { return r * kL + 8 * (p ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int k_piece(int g, int ks) { return (g & 1) | ((g >> 1) << 2) | (ks << 1); }
 
 __device__ __forceinline__ __bf16 to_bf(float x) { return static_cast<__bf16>(x); }
 
@@ -91,8 +97,8 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __bf16 *B, float *C, int I, int J,
                                                        int L, const float *s_ptr) {
     const float s = s_ptr ? *s_ptr : 1.0f;
-    __shared__ __attribute__((aligned(16))) __bf16 as[kT * kLS];
-    __shared__ __attribute__((aligned(16))) __bf16 bs[kT * kLS];
+    __shared__ __attribute__((aligned(16))) __bf16 as[kT * kL];
+    __shared__ __attribute__((aligned(16))) __bf16 bs[kT * kL];
     const int nj = J / kT;
     const int i0 = (int)(blockIdx.x / nj) * kT, j0 = (int)(blockIdx.x % nj) * kT;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, lr = lane & 15;
@@ -119,8 +125,8 @@ __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __b
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = t + 256 * r;
-            *reinterpret_cast<bf16x8 *>(&as[(e >> 3) * kLS + 8 * (e & 7)]) = ar[r];
-            *reinterpret_cast<bf16x8 *>(&bs[(e >> 3) * kLS + 8 * (e & 7)]) = br[r];
+            *reinterpret_cast<bf16x8 *>(&as[lds_pos(e >> 3, e & 7)]) = ar[r];
+            *reinterpret_cast<bf16x8 *>(&bs[lds_pos(e >> 3, e & 7)]) = br[r];
         }
         __syncthreads();
         if (st + 1 < nst) fetch((st + 1) * kL);
@@ -129,10 +135,10 @@ __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __b
             bf16x8 af[4], bf[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                af[x] = *reinterpret_cast<const bf16x8 *>(&as[(wi + 16 * x + lr) * kLS + 32 * ks + 8 * g]);
+                af[x] = *reinterpret_cast<const bf16x8 *>(&as[lds_pos(wi + 16 * x + lr, k_piece(g, ks))]);
 #pragma unroll
             for (int y = 0; y < 4; ++y)
-                bf[y] = *reinterpret_cast<const bf16x8 *>(&bs[(wj + 16 * y + lr) * kLS + 32 * ks + 8 * g]);
+                bf[y] = *reinterpret_cast<const bf16x8 *>(&bs[lds_pos(wj + 16 * y + lr, k_piece(g, ks))]);
             // B first: lane (g, lr) accumulates C[i = 16x + lr][j = 16y + 4g + 0..3]
 #pragma unroll
             for (int x = 0; x < 4; ++x)
