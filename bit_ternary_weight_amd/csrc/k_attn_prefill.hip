@@ -21,7 +21,8 @@
 //       S^T = K Q^T  with v_mfma_f32_16x16x32_bf16 (keys the first operand,
 //         so lane (g, c) holds keys 4g..4g+3 of each 16-key tile for query c);
 //       online softmax in fp32 (base-2 exponentials of the pre-scaled
-//         scores), the maximum shared by the four lanes of a query and moved
+//         scores), the maximum shared by the four lanes of a query (lane
+//         swaps) and moved
 //         only when a block's exceeds it by more than 8;
 //       O^T += V^T P^T with the probabilities rounded to bf16 straight from
 //         the score registers: the k index of the product runs over the keys
@@ -122,6 +123,23 @@ __global__ __launch_bounds__(256) void k_attn_prep(PrefArgs a) {
     }
 }
 
+// Maximum / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (a query's four
+// lane groups), through the lane-swap instructions: swapping a register with
+// itself returns the values of lanes l & ~16 and l | 16 (then l & ~32 and
+// l | 32) in every lane.
+__device__ __forceinline__ float group4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -219,8 +237,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[u][c][i]);
-            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            bm = group4_max(bm);
             // The running maximum moves only when a block's exceeds it by more
             // than 8 (so every weight stays below 2^8, well inside bf16 and
             // fp32); the accumulators are rescaled only then, which after the
@@ -262,8 +279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 #pragma unroll
     for (int u = 0; u < kQT; ++u) {
-        float l = l_run[u] + __shfl_xor(l_run[u], 16, 64);
-        l = l + __shfl_xor(l, 32, 64);
+        const float l = group4_sum(l_run[u]);
         if (qrow[u] >= a.M) continue;
         const float inv = 1.0f / l;
         float *orow = a.out + (size_t)qrow[u] * a.ldo + h * kPD + 4 * g;
