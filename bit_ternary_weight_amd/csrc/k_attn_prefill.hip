@@ -140,6 +140,15 @@ __device__ __forceinline__ float group4_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Row of the transposed value block that staging piece c (8 pieces a row)
+// belongs to.  The 32 pieces c = 32k .. 32k+31 cover rows a, a+1, a+16, a+17
+// (a from k), whose 8-byte halves, 136 bytes a row, fill all 32 bank pairs
+// once: the LDS writes of lanes 0-31 do not conflict.
+__device__ __forceinline__ int v_row(int c) {
+    const int k = c >> 5, rs = (c >> 3) & 3;
+    return (rs & 1) | ((rs >> 1) << 4) | ((k & 7) << 1) | ((k >> 3) << 5);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -168,14 +177,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int s = 0; s < 4; ++s) qf[u][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
     }
     // staging: 1024 16-byte pieces of keys (row c >> 4, piece c & 15) and of
-    // transposed values (row c >> 3, piece c & 7), four of each per thread
+    // transposed values (row v_row(c), piece c & 7), four of each per thread
     bf16x8 kr[4], vr[4];
     auto fetch = [&](int kb0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = t + 256 * r;
             kr[r] = *reinterpret_cast<const bf16x8 *>(kbase + (size_t)(kb0 + (c >> 4)) * kPD + 8 * (c & 15));
-            vr[r] = *reinterpret_cast<const bf16x8 *>(vbase + (size_t)(c >> 3) * a.Mp + kb0 + 8 * (c & 7));
+            vr[r] = *reinterpret_cast<const bf16x8 *>(vbase + (size_t)v_row(c) * a.Mp + kb0 + 8 * (c & 7));
         }
     };
     f32x4 o[kQT][8];
@@ -196,7 +205,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 4; ++r) {
             const int c = t + 256 * r;
             *reinterpret_cast<bf16x8 *>(&ks[(c >> 4) * kKStride + 8 * (c & 15)]) = kr[r];
-            bf16x4 *vd = reinterpret_cast<bf16x4 *>(&vs[(c >> 3) * kVStride + 8 * (c & 7)]);
+            bf16x4 *vd = reinterpret_cast<bf16x4 *>(&vs[v_row(c) * kVStride + 8 * (c & 7)]);
             vd[0] = bf16x4{vr[r][0], vr[r][1], vr[r][2], vr[r][3]};
             vd[1] = bf16x4{vr[r][4], vr[r][5], vr[r][6], vr[r][7]};
         }
