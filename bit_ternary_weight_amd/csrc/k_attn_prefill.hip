@@ -41,7 +41,12 @@ constexpr int kPD = 128;                 // head dimension
 constexpr int kPB = 64;                  // tokens per key block (and per block of the prep kernel)
 constexpr int kQT = 2;                   // 16-query tiles per wave
 constexpr int kPQ = 4 * 16 * kQT;        // queries per workgroup (4 waves)
-constexpr int kKStride = kPD + 8;        // LDS key row, bf16 elements (272 bytes: rows 4 banks apart)
+// LDS key rows of 128 bf16 (256 bytes, 16 pieces of 16), unpadded: piece p of
+// row r sits at position p ^ (r & 15).  Lane group g of k-step s takes the
+// dimensions of piece (g & 1) | s << 1 | (g >> 1) << 3 (a permutation of the
+// dimension order that the queries share), so the 16 lanes of a group, and
+// lanes l and l + 32, read distinct banks.
+__device__ __forceinline__ int q_piece(int g, int s) { return (g & 1) | (s << 1) | ((g >> 1) << 3); }
 constexpr int kVStride = kPB + 4;        // LDS transposed value row, bf16 elements (136 bytes)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -155,7 +160,7 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 // Two workgroups a CU: the register budget is held to 256 a lane (no spills).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(PrefArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 ks[kPB * kKStride];
+    __shared__ __attribute__((aligned(16))) __bf16 ks[kPB * kPD];
     __shared__ __attribute__((aligned(16))) __bf16 vs[kPD * kVStride];
     const int nqb = a.Mp / kPQ;
     const int qblk = nqb - 1 - (int)blockIdx.x / a.H;   // heaviest (latest) query blocks first
@@ -168,13 +173,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const __bf16 *kbase = a.kb + (size_t)kvh * a.Mp * kPD;
     const __bf16 *vbase = a.vt + (size_t)kvh * kPD * a.Mp;
 
-    // second operands of S^T = K Q^T: Q[query lr of tile u][dimensions 32s + 8g .. +7]
+    // second operands of S^T = K Q^T: Q[query lr of tile u][the 8 dimensions
+    // of piece q_piece(g, s)]
     bf16x8 qf[kQT][4];
 #pragma unroll
     for (int u = 0; u < kQT; ++u) {
-        const __bf16 *qp = a.qb + ((size_t)h * a.Mp + qrow[u]) * kPD + 8 * g;
+        const __bf16 *qp = a.qb + ((size_t)h * a.Mp + qrow[u]) * kPD;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[u][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+        for (int s = 0; s < 4; ++s) qf[u][s] = *reinterpret_cast<const bf16x8 *>(qp + 8 * q_piece(g, s));
     }
     // staging: 1024 16-byte pieces of keys (row c >> 4, piece c & 15) and of
     // transposed values (row v_row(c), piece c & 7), four of each per thread
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = t + 256 * r;
-            *reinterpret_cast<bf16x8 *>(&ks[(c >> 4) * kKStride + 8 * (c & 15)]) = kr[r];
+            *reinterpret_cast<bf16x8 *>(&ks[(c >> 4) * kPD + 8 * ((c & 15) ^ ((c >> 4) & 15))]) = kr[r];
             bf16x4 *vd = reinterpret_cast<bf16x4 *>(&vs[v_row(c) * kVStride + 8 * (c & 7)]);
             vd[0] = bf16x4{vr[r][0], vr[r][1], vr[r][2], vr[r][3]};
             vd[1] = bf16x4{vr[r][4], vr[r][5], vr[r][6], vr[r][7]};
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int u = 0; u < kQT; ++u) sc[u][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[(16 * c + lr) * kKStride + 32 * s + 8 * g]);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&ks[(16 * c + lr) * kPD + 8 * (q_piece(g, s) ^ lr)]);
 #pragma unroll
                 for (int u = 0; u < kQT; ++u) sc[u][c] = mfma_bf16(kf, qf[u][s], sc[u][c]);
             }
