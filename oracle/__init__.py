@@ -9,11 +9,19 @@ function citing the page passage it follows); this module builds it with gcc
 and marshals numpy arrays through ctypes.  Every function here takes and
 returns numpy arrays.
 
+One step is evaluated by a library routine: ``contract_f64`` forms the
+integer contraction with numpy's fp64 matrix product.  Every product and
+every partial sum there is an integer below 2^53 in magnitude, so the result
+is exact in any summation order; it is pinned against the C loop
+(``ora_contract``) and brute force.  It serves the full-size parity checks,
+where the C loop would take minutes.
+
 Parity status: every function is pinned by tests under ``tests/`` (worked
-examples, closed forms, invariants, brute force; the prefill attention rows
-against the separately written decode attention).  The layer wiring used for
-the 30-layer stack (q output feeding o in place of attention, no residual)
-is a convention with no passage behind it: parity unpinned for that wiring.
+examples, closed forms, exact rationals, invariants, brute force; the prefill
+attention rows against the separately written decode attention).  The layer
+wiring used for the 30-layer stack (q output feeding o in place of
+attention, no residual) is a convention with no passage behind it: parity
+unpinned for that wiring.
 """
 from __future__ import annotations
 
@@ -68,6 +76,9 @@ def _load():
         "ora_ffn_chain": (None, [P, I, I, I, P, P, F, P, P, P, P, P, P, P, P, P, P]),
         "ora_rope_f64": (None, [P, I, I, I, ctypes.c_double, P]),
         "ora_attn_decode": (None, [P, P, P, I, I, I, I, P, P, I, ctypes.c_double, P]),
+        "ora_attn_prefill_f64": (None, [P, P, P, I, I, I, I, ctypes.c_double, P, I, P]),
+        "ora_ste_grad_input_rows": (None, [P, I, I, P, I, F, P, I, P]),
+        "ora_ste_grad_weight_rows": (None, [P, I, I, P, P, I, P, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -148,6 +159,28 @@ def contract(q, codes) -> np.ndarray:
     ovf = _load().ora_contract(_p(q), M, K, _p(codes), N, _p(A))
     assert ovf == 0, "int32 overflow in the contraction"
     return A
+
+
+def contract_f64(q, codes) -> np.ndarray:
+    """The same integer contraction as ``contract`` (sum_k q[m,k] c[n,k]),
+    evaluated by numpy's fp64 matrix product.  |q| <= 128 and |c| <= 1, so
+    every partial sum is an integer of magnitude <= 128 K < 2^53 for K < 2^45:
+    each addition is exact and the order the library takes does not matter."""
+    q = np.asarray(q, np.int8)
+    codes = np.asarray(codes, np.int8)
+    assert q.shape[1] == codes.shape[1] and q.shape[1] < (1 << 45)
+    A = q.astype(np.float64) @ codes.astype(np.float64).T
+    assert np.abs(A).max(initial=0) < 2.0 ** 31, "int32 overflow in the contraction"
+    return A.astype(np.int32)
+
+
+def bitlinear_f64gemm(x, codes, seg_n=None, w_mean=None):
+    """``bitlinear`` with the contraction taken by ``contract_f64``: the C
+    quantizer, the exact integer product, the C rescale.  Returns (q, a, A, y)."""
+    q, a = quant_act(x)
+    A = contract_f64(q, codes)
+    N = codes.shape[0]
+    return q, a, A, rescale(A, a, seg_n if seg_n is not None else [N], w_mean)
 
 
 def _segs(seg_n, N):
@@ -297,59 +330,59 @@ def bf16_round(x) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def attn_prefill_rows(q, k, v, base, n_heads, n_kv_heads, rows, bf16_inputs=True):
+def attn_prefill_rows(q, k, v, base, n_heads, n_kv_heads, rows):
     """fp64 causal attention outputs [len(rows), n_heads*D] of a prompt whose
-    tokens sit at positions 0 .. M-1.
+    tokens sit at positions 0 .. M-1: the plain definition, nothing rounded.
 
-    q [M, n_heads*D], k / v [M, n_kv_heads*D] fp32, before RoPE.  Queries and
-    keys are rotated (rope, fp64) and rounded to fp32; with bf16_inputs they
-    and the values are then rounded to bf16, the precision in which the
-    prefill products take them.  Row p attends to positions 0 .. p with scores
-    q'.k'/sqrt(D); query head h reads key/value head h // (n_heads/n_kv_heads).
-    A numpy matmul forms the scores and the weighted sums.
-    """
-    q = np.asarray(q, np.float32)
-    k = np.asarray(k, np.float32)
-    v = np.asarray(v, np.float32)
+    q [M, n_heads*D], k / v [M, n_kv_heads*D] fp32, before RoPE.  Row p
+    attends to positions 0 .. p with scores q'.k'/sqrt(D) of the fp64
+    rotations; query head h reads key/value head h // (n_heads/n_kv_heads)."""
+    q = _c(q, np.float32)
+    k = _c(k, np.float32)
+    v = _c(v, np.float32)
     M = q.shape[0]
     D = q.shape[1] // n_heads
-    G = n_heads // n_kv_heads
-    qh = q.reshape(M, n_heads, D)
-    kh = k.reshape(M, n_kv_heads, D)
-    kr = np.stack([rope(kh[p], p, base) for p in range(M)]).astype(np.float32)
-    vv = v.reshape(M, n_kv_heads, D)
-    if bf16_inputs:
-        kr = bf16_round(kr)
-        vv = bf16_round(vv)
-    kr = kr.astype(np.float64)
-    vv = vv.astype(np.float64)
-    out = np.empty((len(rows), n_heads * D), np.float64)
-    for n, p in enumerate(rows):
-        qr = rope(qh[p], p, base).astype(np.float32)
-        if bf16_inputs:
-            qr = bf16_round(qr)
-        qr = qr.astype(np.float64)
-        for h in range(n_heads):
-            s = kr[:p + 1, h // G, :] @ qr[h] / np.sqrt(float(D))
-            w = np.exp(s - s.max())
-            out[n, h * D:(h + 1) * D] = (w @ vv[:p + 1, h // G, :]) / w.sum()
+    assert k.shape == (M, n_kv_heads * D) and v.shape == k.shape and n_heads % n_kv_heads == 0
+    r = _c(np.asarray(rows).reshape(-1), np.int32)
+    assert r.size and r.min() >= 0 and r.max() < M
+    out = np.empty((r.size, n_heads * D), np.float64)
+    _load().ora_attn_prefill_f64(_p(q), _p(k), _p(v), M, n_heads, n_kv_heads, D, float(base), _p(r), r.size,
+                                 _p(out))
     return out
 
 
-def ste_grad_input(dy, codes, w_mean) -> np.ndarray:
-    """fp64 dX [M,K] = dY . W~ of BitLinear's straight-through backward, with
-    the fake-quantized weight W~ = codes * w_mean: (sum_n dy[m,n] codes[n,k])
-    * w_mean.  dy [M,N] (values, e.g. bf16 ones); codes [N,K] int8."""
-    dy = np.asarray(dy, np.float64)
-    return (dy @ np.asarray(codes, np.float64)) * float(np.float32(w_mean))
+def _rows(rows, n):
+    r = np.arange(n, dtype=np.int32) if rows is None else _c(np.asarray(rows).reshape(-1), np.int32)
+    assert r.size == 0 or (r.min() >= 0 and r.max() < n)
+    return r
 
 
-def ste_grad_weight(dy, q, a) -> np.ndarray:
-    """fp64 dW [N,K] = dY^T . x~ of the straight-through backward, x~ = q / a,
-    with 1/a folded into the gradient first: sum_m bf16(fp32(dy[m,n] / a[m]))
-    q[m,k] (the rounding the bf16 product takes).  dy [M,N] fp32 values; q
-    [M,K] int8; a [M] fp32."""
-    dy = np.asarray(dy, np.float32)
-    a = np.asarray(a, np.float32)
-    s = bf16_round(dy / a[:, None])
-    return s.astype(np.float64).T @ np.asarray(q, np.float64)
+def ste_grad_input(dy, codes, w_mean, rows=None) -> np.ndarray:
+    """fp64 rows of dX = dY . W~ of BitLinear's straight-through backward,
+    W~ = codes * w_mean: dx[m,k] = sum_n dy[m,n] (codes[n,k] w_mean) for the
+    token rows m in `rows` (all when None).  dy [M,N] fp32; codes [N,K]."""
+    dy = _c(dy, np.float32)
+    codes = _c(codes, np.int8)
+    M, N = dy.shape
+    N2, K = codes.shape
+    assert N == N2
+    r = _rows(rows, M)
+    out = np.empty((r.size, K), np.float64)
+    _load().ora_ste_grad_input_rows(_p(dy), M, N, _p(codes), K, float(np.float32(w_mean)), _p(r), r.size, _p(out))
+    return out
+
+
+def ste_grad_weight(dy, q, a, rows=None) -> np.ndarray:
+    """fp64 rows of dW = dY^T . x~ of the straight-through backward,
+    x~ = q / a: dw[n,k] = sum_m dy[m,n] (q[m,k] / a[m]) for the weight rows n
+    in `rows` (all when None).  dy [M,N] fp32; q [M,K] int8; a [M] fp32."""
+    dy = _c(dy, np.float32)
+    q = _c(q, np.int8)
+    a = _c(a, np.float32)
+    M, N = dy.shape
+    M2, K = q.shape
+    assert M == M2 and a.shape == (M,)
+    r = _rows(rows, N)
+    out = np.empty((r.size, K), np.float64)
+    _load().ora_ste_grad_weight_rows(_p(dy), M, N, _p(q), _p(a), K, _p(r), r.size, _p(out))
+    return out

@@ -398,3 +398,113 @@ void ora_attn_decode(const float *q, const float *k_new, const float *v_new, int
     }
     free(qd); free(qr); free(kd); free(kr); free(sc);
 }
+
+/* ===========================================================================
+ * Attention side of a decoder layer over a prompt (prefill): the tokens sit
+ * at positions 0 .. M-1 and token p attends to positions 0 .. p (causal).
+ * Same pages and readings as ora_attn_decode: RoPE with dimension i paired
+ * with i + D/2 at angle pos * base^(-2i/D) on queries and keys, scores scaled
+ * by 1/sqrt(D), softmax with the maximum subtracted, query head h reading
+ * key/value head h / (H / KVH).  The plain definition in fp64 throughout: the
+ * rotated queries and keys are never rounded, the values are the fp32 inputs.
+ *   q [M][H*D], k [M][KVH*D], v [M][KVH*D] fp32 (before RoPE), contiguous;
+ *   rows[nrows]: the token positions whose outputs are wanted;
+ *   out [nrows][H*D] fp64.
+ * ------------------------------------------------------------------------ */
+void ora_attn_prefill_f64(const float *q, const float *k, const float *v, int M, int H, int KVH, int D,
+                          double base, const int *rows, int nrows, double *out)
+{
+    const int G = H / KVH;
+    int pmax = 0;
+    for (int r = 0; r < nrows; ++r)
+        if (rows[r] > pmax) pmax = rows[r];
+    if (pmax >= M) pmax = M - 1;
+    const int64_t kw = (int64_t)KVH * D;
+    double *kd = (double *)malloc(sizeof(double) * (size_t)kw);
+    double *kr = (double *)malloc(sizeof(double) * (size_t)(pmax + 1) * kw);
+    double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *qr = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(pmax + 1));
+    for (int j = 0; j <= pmax; ++j) {
+        for (int64_t i = 0; i < kw; ++i) kd[i] = (double)k[(int64_t)j * kw + i];
+        ora_rope_f64(kd, KVH, D, j, base, kr + (int64_t)j * kw);
+    }
+    const double scale = 1.0 / sqrt((double)D);
+    for (int r = 0; r < nrows; ++r) {
+        const int p = rows[r];
+        for (int64_t i = 0; i < (int64_t)H * D; ++i) qd[i] = (double)q[(int64_t)p * H * D + i];
+        ora_rope_f64(qd, H, D, p, base, qr);
+        for (int h = 0; h < H; ++h) {
+            const int g = h / G;
+            double mx = -INFINITY;
+            for (int j = 0; j <= p; ++j) {
+                double s = 0.0;
+                for (int d = 0; d < D; ++d)
+                    s += qr[(int64_t)h * D + d] * kr[(int64_t)j * kw + (int64_t)g * D + d];
+                sc[j] = s * scale;
+                if (sc[j] > mx) mx = sc[j];
+            }
+            double l = 0.0;
+            for (int j = 0; j <= p; ++j) {
+                sc[j] = exp(sc[j] - mx);
+                l += sc[j];
+            }
+            for (int d = 0; d < D; ++d) {
+                double o = 0.0;
+                for (int j = 0; j <= p; ++j)
+                    o += sc[j] * (double)v[(int64_t)j * kw + (int64_t)g * D + d];
+                out[(int64_t)r * H * D + (int64_t)h * D + d] = o / l;
+            }
+        }
+    }
+    free(kd); free(kr); free(qd); free(qr); free(sc);
+}
+
+/* ===========================================================================
+ * Backward of BitLinear in quantization-aware training.  [T] "BitLinear 的三步
+ * 量化": in training both quantizers hand the incoming gradient through
+ * unchanged (straight-through estimator), so the layer's gradients are those
+ * of a plain linear layer evaluated at the fake-quantized tensors
+ *   W~ = codes * w_mean           (the ternary weight mapped back to its range)
+ *   x~ = q / a                    (the int8 activation mapped back)
+ *   dX = dY . W~,   dW = dY^T . x~.
+ * The plain definitions in fp64; dy is the fp32 output gradient.  Only the
+ * requested rows are formed (whole products are large).
+ * ------------------------------------------------------------------------ */
+
+/* dx[r][k] = sum_n dy[m][n] * (codes[n][k] * w_mean), m = rows[r].
+ * dy [M][N] fp32; codes [N][K] int8; dx [nrows][K] fp64. */
+void ora_ste_grad_input_rows(const float *dy, int M, int N, const int8_t *codes, int K, float w_mean,
+                             const int *rows, int nrows, double *dx)
+{
+    (void)M;
+    for (int r = 0; r < nrows; ++r) {
+        const int m = rows[r];
+        double *o = dx + (int64_t)r * K;
+        for (int kk = 0; kk < K; ++kk) o[kk] = 0.0;
+        for (int n = 0; n < N; ++n) {
+            const double g = (double)dy[(int64_t)m * N + n];
+            const int8_t *c = codes + (int64_t)n * K;
+            for (int kk = 0; kk < K; ++kk)
+                o[kk] += g * ((double)c[kk] * (double)w_mean);
+        }
+    }
+}
+
+/* dw[r][k] = sum_m dy[m][n] * (q[m][k] / a[m]), n = rows[r].
+ * dy [M][N] fp32; q [M][K] int8; a [M] fp32; dw [nrows][K] fp64. */
+void ora_ste_grad_weight_rows(const float *dy, int M, int N, const int8_t *q, const float *a, int K,
+                              const int *rows, int nrows, double *dw)
+{
+    for (int r = 0; r < nrows; ++r) {
+        const int n = rows[r];
+        double *o = dw + (int64_t)r * K;
+        for (int kk = 0; kk < K; ++kk) o[kk] = 0.0;
+        for (int m = 0; m < M; ++m) {
+            const double g = (double)dy[(int64_t)m * N + n];
+            const int8_t *qm = q + (int64_t)m * K;
+            for (int kk = 0; kk < K; ++kk)
+                o[kk] += g * ((double)qm[kk] / (double)a[m]);
+        }
+    }
+}

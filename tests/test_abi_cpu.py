@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     raw = lib.raw
-    assert raw.bl_abi_version() == 1
+    assert raw.bl_abi_version() == 2
     names = [raw.bl_status_string(i).decode() for i in range(8)]
     assert names == ["BL_OK", "BL_ERR_NULL", "BL_ERR_SHAPE", "BL_ERR_ALIGN", "BL_ERR_DTYPE",
                      "BL_ERR_SEGMENTS", "BL_ERR_WORKSPACE", "BL_ERR_HIP"]
@@ -232,11 +232,15 @@ def test_attn_decode_validation(lib):
 
 def test_rope_table_values(lib):
     import numpy as np
-    c, s = lib.rope_table(64, 128, 500000.0)
-    pos = np.arange(64, dtype=np.float64)[:, None]
-    inv = 500000.0 ** (-2.0 * np.arange(64, dtype=np.float64) / 128.0)
-    assert np.array_equal(c, np.cos(pos * inv).astype(np.float32))
-    assert np.array_equal(s, np.sin(pos * inv).astype(np.float32))
+    import math
+    # closed form: head_dim 8, base 100 -> pair i turns by 100^(-2i/8) = 1,
+    # 10^-0.5, 0.1, 10^-1.5 radians per position
+    c, s = lib.rope_table(4, 8, 100.0)
+    assert c.shape == (4, 4) and (c[0] == 1).all() and (s[0] == 0).all()
+    for p in range(1, 4):
+        for i, t in enumerate([1.0, 10 ** -0.5, 0.1, 10 ** -1.5]):
+            for got, want in ((c[p, i], math.cos(p * t)), (s[p, i], math.sin(p * t))):
+                assert abs(float(got) - want) <= float(np.spacing(np.float32(abs(want)))), (p, i)
     raw = lib.raw
     assert raw.bl_rope_table(4, 7, 10000.0, FAKE, FAKE) == lib.BL_ERR_SHAPE
     assert raw.bl_rope_table(4, 8, 0.0, FAKE, FAKE) == lib.BL_ERR_SHAPE
@@ -265,15 +269,24 @@ def test_attn_prefill_validation(lib):
 def test_ste_validation(lib):
     raw = lib.raw
     gi, gw = raw.bl_ste_grad_input, raw.bl_ste_grad_weight
-    ni = raw.bl_ste_grad_input_workspace_bytes(256, 384)
+    BF, F = lib.BL_BF16, lib.BL_F32
+    ni = raw.bl_ste_grad_input_workspace_bytes(128, 256, 384, BF)
     nw = raw.bl_ste_grad_weight_workspace_bytes(128, 256, 384)
     assert ni >= 256 * 384 * 2 and nw >= (256 * 128 + 384 * 128) * 2
-    assert gi(None, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_NULL
-    assert gi(FAKE, 100, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_SHAPE
-    assert gi(FAKE, 128, 200, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_SHAPE
-    assert gi(FAKE_MIS, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_ALIGN
-    assert gi(FAKE, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni - 1, None) == lib.BL_ERR_WORKSPACE
-    assert gw(FAKE, None, FAKE, 128, 256, 384, FAKE, FAKE, nw, None) == lib.BL_ERR_NULL
-    assert gw(FAKE, FAKE, FAKE, 128, 256, 380, FAKE, FAKE, nw, None) == lib.BL_ERR_SHAPE
-    assert gw(FAKE, FAKE, FAKE, 128, 256, 384, FAKE_MIS, FAKE, nw, None) == lib.BL_ERR_ALIGN
-    assert gw(FAKE, FAKE, FAKE, 128, 256, 384, FAKE, FAKE, nw - 1, None) == lib.BL_ERR_WORKSPACE
+    # whole tiles of a bf16 gradient are used in place; fp32 or ragged ones get a padded bf16 copy
+    assert raw.bl_ste_grad_input_workspace_bytes(128, 256, 384, F) >= ni + 128 * 256 * 2
+    assert raw.bl_ste_grad_input_workspace_bytes(100, 256, 384, BF) >= ni + 128 * 256 * 2
+    assert raw.bl_ste_grad_input_workspace_bytes(128, 256, 384, 2) == 0
+    ni100 = raw.bl_ste_grad_input_workspace_bytes(100, 200, 300, F)
+    assert gi(None, BF, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_NULL
+    assert gi(FAKE, BF, 0, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_SHAPE
+    assert gi(FAKE, F, 100, 202, 300, FAKE, FAKE, FAKE, FAKE, ni100, None) == lib.BL_ERR_SHAPE   # N % 4
+    assert gi(FAKE, 2, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_DTYPE
+    assert gi(FAKE_MIS, BF, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_ALIGN
+    assert gi(FAKE, BF, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni - 1, None) == lib.BL_ERR_WORKSPACE
+    assert gi(FAKE, BF, 1 << 16, 1 << 16, 128, FAKE, FAKE, FAKE, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    assert gw(FAKE, BF, None, FAKE, 128, 256, 384, FAKE, FAKE, nw, None) == lib.BL_ERR_NULL
+    assert gw(FAKE, BF, FAKE, FAKE, 128, 256, -1, FAKE, FAKE, nw, None) == lib.BL_ERR_SHAPE
+    assert gw(FAKE, BF, FAKE, FAKE, 128, 256, 384, FAKE_MIS, FAKE, nw, None) == lib.BL_ERR_ALIGN
+    assert gw(FAKE, BF, FAKE, FAKE, 128, 256, 384, FAKE, FAKE, nw - 1, None) == lib.BL_ERR_WORKSPACE
+    assert gw(FAKE, 3, FAKE, FAKE, 128, 256, 384, FAKE, FAKE, nw, None) == lib.BL_ERR_DTYPE

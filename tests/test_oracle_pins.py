@@ -268,7 +268,29 @@ def test_contract_extremes_and_identity():
 
 
 # ----------------------------------------------------------------------------- rescale
+def _rne32(fr: Fraction) -> float:
+    """Exact rational -> nearest fp32 (ties to even), by exact comparison with
+    the two fp32 neighbours; independent of any floating-point evaluation."""
+    if fr == 0:
+        return 0.0
+    sign = -1.0 if fr < 0 else 1.0
+    fr = abs(fr)
+    lo = np.float32(float(fr))                      # within an ulp of fr
+    while Fraction(float(lo)) > fr:
+        lo = np.nextafter(lo, np.float32(0))
+    while Fraction(float(np.nextafter(lo, np.float32(np.inf)))) <= fr:
+        lo = np.nextafter(lo, np.float32(np.inf))
+    hi = np.nextafter(lo, np.float32(np.inf))
+    dl, dh = fr - Fraction(float(lo)), Fraction(float(hi)) - fr
+    if dl < dh or (dl == dh and (int(np.array(lo).view(np.uint32)) & 1) == 0):
+        return sign * float(lo)
+    return sign * float(hi)
+
+
 def test_rescale_against_exact_rationals_segments():
+    """y = fl32(float(A) * fl32(w_mean / a)): the scale is the correctly rounded
+    quotient, then one rounding of the product (exact rationals, no float
+    evaluation of the formula)."""
     rng = np.random.default_rng(31)
     M, segs = 5, [8, 4, 12]
     N = sum(segs)
@@ -279,9 +301,28 @@ def test_rescale_against_exact_rationals_segments():
     seg_of = np.repeat(np.arange(3), segs)
     for m in range(M):
         for n in range(N):
-            exact = Fraction(int(A[m, n])) * Fraction(float(wm[seg_of[n]])) / Fraction(float(a[m]))
-            # two fp32 roundings: the scale, then the product
-            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(_ulp(float(exact))) * Fraction(3, 2)
+            sc = _rne32(Fraction(float(wm[seg_of[n]])) / Fraction(float(a[m])))
+            assert float(y[m, n]) == _rne32(Fraction(int(A[m, n])) * Fraction(sc)), (m, n)
+
+
+def test_rescale_divides_once_not_by_reciprocal():
+    """A pair (w_mean, a) for which fl(w_mean / a) and w_mean * fl(1 / a) are
+    different fp32 numbers: with A = 1 the output is the scale itself and must
+    be the correctly rounded quotient."""
+    rng = np.random.default_rng(77)
+    found = 0
+    for _ in range(20000):
+        w = np.float32(rng.uniform(0.01, 0.03))
+        a = np.float32(rng.uniform(1.0, 300.0))
+        quot = _rne32(Fraction(float(w)) / Fraction(float(a)))
+        recip = _rne32(Fraction(float(w)) * Fraction(_rne32(1 / Fraction(float(a)))))
+        if quot != recip:
+            y = oracle.rescale(np.ones((1, 4), np.int32), np.array([a]), None, np.float32(w))
+            assert (y == np.float32(quot)).all() and (y != np.float32(recip)).all()
+            found += 1
+            if found == 5:
+                break
+    assert found == 5
 
 
 def test_rescale_vs_dequant_f64():
@@ -326,6 +367,29 @@ def test_rmsnorm_closed_forms():
     assert np.allclose(og, o1 * g, rtol=1e-6, atol=0)
     # zero row stays zero
     assert (oracle.rmsnorm(np.zeros((1, 16), np.float32)) == 0).all()
+
+
+def test_rmsnorm_sum_of_squares_is_exact_fp64():
+    """A row of one 4096 followed by 4096 ones: sum h^2 = 4096^2 + 4096 =
+    4096 * 4097 exactly, so the mean square over K = 4097 is exactly 4096.
+    Summed in fp32 the ones vanish (2^24 + 1 is not representable), which
+    would give a mean of 2^24 / 4097 instead.  r = fl32(1 / sqrt(4096 + eps))
+    to within rounding of the exact value."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    K = 4097
+    h = np.ones((1, K), np.float32)
+    h[0, 0] = 4096.0
+    out = oracle.rmsnorm(h)
+    eps = Decimal(float(np.float32(1e-5)))
+    r_exact = Decimal(1) / (Decimal(4096) + eps).sqrt()
+    r = Fraction(float(out[0, 1]))                  # h = 1 there: out = fl32(r)
+    # one fp32 rounding of a value computed in fp64: within 0.5 ulp + 1e-15
+    assert abs(r - Fraction(r_exact)) <= Fraction(_ulp(float(r_exact))) / 2 + Fraction(1, 10 ** 15)
+    assert float(out[0, 0]) == float(np.float32(np.float32(4096.0) * np.float32(out[0, 1])))
+    # the fp32 sum's answer is far outside that
+    r_f32sum = 1 / math.sqrt(2.0 ** 24 / K + 1e-5)
+    assert abs(float(r) - r_f32sum) > 1000 * _ulp(r_f32sum)
 
 
 def test_relu2_mul_closed_forms():
@@ -417,6 +481,24 @@ def test_rope_position_zero_is_identity_and_d2_is_a_plane_rotation():
         assert np.allclose(oracle.rope(v, pos, 500000.0), [[0.6 * c + 0.8 * s, -0.8 * c + 0.6 * s]], atol=1e-15)
 
 
+def test_rope_angle_schedule_closed_form():
+    """D = 8, base = 100, position 1: the four pairs turn by 100^(-2i/8) =
+    1, 10^-0.5, 0.1, 10^-1.5 radians.  Unit vectors e_i and e_(i+4) give the
+    cosines and sines of exactly those angles."""
+    D, base = 8, 100.0
+    angles = [1.0, 10 ** -0.5, 0.1, 10 ** -1.5]
+    eye = np.eye(D)
+    r = oracle.rope(eye, 1, base)
+    for i, t in enumerate(angles):
+        # e_i -> cos t at i, sin t at i + 4;  e_(i+4) -> -sin t at i, cos t at i + 4
+        assert abs(r[i, i] - math.cos(t)) < 1e-15 and abs(r[i, i + 4] - math.sin(t)) < 1e-15
+        assert abs(r[i + 4, i] + math.sin(t)) < 1e-15 and abs(r[i + 4, i + 4] - math.cos(t)) < 1e-15
+    # position 3: three times the angles
+    r3 = oracle.rope(eye, 3, base)
+    for i, t in enumerate(angles):
+        assert abs(r3[i, i + 4] - math.sin(3 * t)) < 1e-14
+
+
 def test_rope_invariants():
     rng = np.random.default_rng(2)
     D = 128
@@ -506,13 +588,14 @@ def _prefill_inputs(seed, M, H, KVH, D=128):
 
 
 def test_attn_prefill_rows_match_the_decode_oracle():
-    """Row p of the prompt equals one decode step at position p over a cache of
-    the earlier tokens' rotated (fp32) keys: the numpy prefill oracle against
-    the C decode oracle, two separate writings of the same attention."""
+    """Row p of the prompt against one decode step at position p over a cache
+    of the earlier tokens' rotated keys: two separate writings of the same
+    attention.  The decode cache holds fp32 keys (rounded once), the prefill
+    definition none, hence the 1e-6."""
     M, H, KVH, D, base = 40, 8, 2, 128, 10000.0
     q, k, v = _prefill_inputs(21, M, H, KVH)
     rows = [0, 1, 17, 39]
-    got = oracle.attn_prefill_rows(q, k, v, base, H, KVH, rows, bf16_inputs=False)
+    got = oracle.attn_prefill_rows(q, k, v, base, H, KVH, rows)
     kc = np.zeros((KVH, M, D), np.float32)
     vc = np.zeros((KVH, M, D), np.float32)
     for p in range(M):
@@ -527,14 +610,40 @@ def test_attn_prefill_first_row_and_causality():
     M, H, KVH, D = 12, 4, 1, 128
     q, k, v = _prefill_inputs(22, M, H, KVH)
     out = oracle.attn_prefill_rows(q, k, v, 500000.0, H, KVH, [0, 5])
-    # position 0 sees only itself: every head returns the (bf16-rounded) value
+    # position 0 sees only itself: every head returns the value, unrounded
     for h in range(H):
-        assert np.array_equal(out[0, h * D:(h + 1) * D], oracle.bf16_round(v[0]).astype(np.float64))
+        assert np.array_equal(out[0, h * D:(h + 1) * D], v[0].astype(np.float64))
     # later tokens do not change row 5
     k2, v2 = k.copy(), v.copy()
     k2[6:] += 3.0
     v2[6:] -= 2.0
     assert np.array_equal(oracle.attn_prefill_rows(q, k2, v2, 500000.0, H, KVH, [5]), out[1:2])
+
+
+def test_attn_prefill_zero_query_averages_the_values():
+    """q = 0 gives every score 0, whatever the rotation: token p returns the
+    plain mean of the values of positions 0 .. p (its key/value head's)."""
+    M, H, KVH, D = 30, 4, 2, 128
+    _, k, v = _prefill_inputs(23, M, H, KVH)
+    q = np.zeros((M, H * D), np.float32)
+    rows = [0, 7, 29]
+    out = oracle.attn_prefill_rows(q, k, v, 10000.0, H, KVH, rows)
+    vh = v.astype(np.float64).reshape(M, KVH, D)
+    for n, p in enumerate(rows):
+        for h in range(H):
+            mean = vh[:p + 1, h // (H // KVH)].sum(axis=0) / (p + 1)
+            assert np.allclose(out[n, h * D:(h + 1) * D], mean, rtol=0, atol=1e-14)
+
+
+def test_attn_prefill_grouped_query_equals_repeated_heads():
+    M, H, KVH, D = 20, 6, 3, 128
+    q, k, v = _prefill_inputs(24, M, H, KVH)
+    G = H // KVH
+    rep = lambda a: np.repeat(a.reshape(M, KVH, D), G, axis=1).reshape(M, H * D)
+    rows = [3, 19]
+    gqa = oracle.attn_prefill_rows(q, k, v, 10000.0, H, KVH, rows)
+    mha = oracle.attn_prefill_rows(q, rep(k), rep(v), 10000.0, H, H, rows)
+    assert np.array_equal(gqa, mha)
 
 
 def test_bf16_round_is_nearest_even():
@@ -552,27 +661,60 @@ def test_ste_grad_input_is_the_gradient_through_the_fake_quantized_weight():
     # against the matmul with the fake-quantized weight itself
     Wq = oracle.fake_quant_weight(codes, wm).astype(np.float64)
     assert np.allclose(oracle.ste_grad_input(dy, codes, wm), dy.astype(np.float64) @ Wq, rtol=1e-12, atol=1e-15)
-    # brute force, element by element
+    # brute force in exact rationals, element by element
     got = oracle.ste_grad_input(dy, codes, wm)
     for m in range(3):
         for k in range(20):
-            ref = sum(float(dy[m, n]) * int(codes[n, k]) for n in range(12)) * float(wm)
-            assert abs(got[m, k] - ref) <= 1e-12
+            ref = sum(Fraction(float(dy[m, n])) * int(codes[n, k]) for n in range(12)) * Fraction(float(wm))
+            assert abs(Fraction(float(got[m, k])) - ref) <= Fraction(1, 2 ** 48) * (abs(ref) + 1)
+    # a row subset gives the same rows
+    assert np.array_equal(oracle.ste_grad_input(dy, codes, wm, rows=[2, 0]), got[[2, 0]])
 
 
-def test_ste_grad_weight_single_token_and_fake_quant_activations():
+def test_ste_grad_weight_is_dy_transposed_times_fake_quant_activations():
     rng = np.random.default_rng(32)
+    # one token: an outer product of dy and x~ = q / a
     x = rng.standard_normal((1, 16)).astype(np.float32)
     q, a = oracle.quant_act(x)
-    dy = np.array([[0.5, -1.25, 3.0]], np.float32)   # exact in bf16; dy / a then rounds
+    dy = np.array([[0.5, -1.25, 3.0]], np.float32)
     got = oracle.ste_grad_weight(dy, q, a)
-    # one token: an outer product of bf16(dy / a) and the codes
-    s = oracle.bf16_round(dy / a[:, None])[0].astype(np.float64)
-    assert np.array_equal(got, np.outer(s, q[0].astype(np.float64)))
-    # the same as dY^T . x~ with x~ = q / a, up to the bf16 rounding of dy / a
-    xs = oracle.quant_act(rng.standard_normal((40, 16)).astype(np.float32))
-    dy2 = rng.standard_normal((40, 3)).astype(np.float32)
-    xt = xs[0].astype(np.float64) / xs[1].astype(np.float64)[:, None]
-    ref = dy2.astype(np.float64).T @ xt
-    bound = 2.0 ** -8 * (np.abs(dy2).astype(np.float64).T @ np.abs(xt))
-    assert np.all(np.abs(oracle.ste_grad_weight(dy2, xs[0], xs[1]) - ref) <= bound)
+    for n in range(3):
+        for k in range(16):
+            exact = Fraction(float(dy[0, n])) * Fraction(int(q[0, k])) / Fraction(float(a[0]))
+            assert abs(Fraction(float(got[n, k])) - exact) <= Fraction(1, 2 ** 50) * abs(exact)
+    # several tokens, brute force in exact rationals: dW[n,k] = sum_m dy[m,n] q[m,k] / a[m]
+    xs = rng.standard_normal((7, 5)).astype(np.float32)
+    q2, a2 = oracle.quant_act(xs)
+    dy2 = rng.standard_normal((7, 4)).astype(np.float32)
+    got2 = oracle.ste_grad_weight(dy2, q2, a2)
+    assert got2.shape == (4, 5)
+    for n in range(4):
+        for k in range(5):
+            exact = sum(Fraction(float(dy2[m, n])) * int(q2[m, k]) / Fraction(float(a2[m])) for m in range(7))
+            assert abs(Fraction(float(got2[n, k])) - exact) <= Fraction(1, 2 ** 48) * (abs(exact) + 1)
+    assert np.array_equal(oracle.ste_grad_weight(dy2, q2, a2, rows=[3, 1]), got2[[3, 1]])
+
+
+# ----------------------------------------------------------------------------- exact contraction by fp64 product
+def test_contract_f64_equals_the_integer_loop():
+    rng = np.random.default_rng(55)
+    for M, K, N in ((3, 7, 8), (17, 300, 12), (64, 2560, 40)):
+        q = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        c = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        assert np.array_equal(oracle.contract_f64(q, c), oracle.contract(q, c))
+    # the extremes: |A| = 127 K and -128 K at K = 6912
+    K = 6912
+    q = np.full((2, K), 127, np.int8)
+    q[1] = -128
+    c = np.ones((4, K), np.int8)
+    c[1] = -1
+    A = oracle.contract_f64(q, c)
+    assert A[0, 0] == 127 * K and A[0, 1] == -127 * K and A[1, 0] == -128 * K and A[1, 1] == 128 * K
+    # and the whole forward agrees with the C forward bit for bit
+    W = synth.master_weight(9, 48, 256)
+    _, wm, codes = oracle.ternarize_pack(W)
+    x = synth.act_normal_f32(9, 5, 256)
+    r1 = oracle.bitlinear(x, codes, None, wm)
+    r2 = oracle.bitlinear_f64gemm(x, codes, None, wm)
+    for u, w in zip(r1, r2):
+        assert np.array_equal(u, w)
