@@ -62,6 +62,26 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
+    def trials(self, fn, min_trials=5, min_total_ms=50.0, max_trials=2000):
+        """Times whole calls of fn (each one timed region between two events)
+        until at least min_trials calls and min_total_ms of timed work; returns
+        (median ms per call, number of calls timed)."""
+        torch = self.torch
+        times = []
+        total = 0.0
+        while len(times) < max_trials and (len(times) < min_trials or total < min_total_ms):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            t = s.elapsed_time(e)
+            times.append(t)
+            total += t
+        times.sort()
+        return times[len(times) // 2], len(times)
+
     def run(self, fn, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -129,34 +149,135 @@ def profiled_traffic():
     return int(t.group(1)) if d.hexdigest() == h.group(1) else None
 
 
-def cpu_baseline(seconds: float = 12.0):
-    """The oracle as it stands, single thread, M=1 layers on two distinct layers' codes."""
+TRACE_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_v1_decode_m1_7proj_kernel_trace.md")
+
+
+def profiled_duration_us():
+    """Average duration of the headline kernel in the committed rocprofv3
+    kernel trace of this command, or None when the kernel sources have
+    changed since it was taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRACE_PROFILE).read()
+    except OSError:
+        return None
+    t = re.search(r"^headline_kernel_avg_us: ([0-9.]+)$", text, re.M)
+    h = re.search(r"^source_sha256: ([0-9a-f]+)$", text, re.M)
+    if not t or not h:
+        return None
+    d = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        d.update(open(os.path.join(ROOT, f), "rb").read())
+    return float(t.group(1)) if d.hexdigest() == h.group(1) else None
+
+
+def cpu_baseline():
+    """The oracle as it stands (plain single-threaded C), pinned to one host
+    core, on bounded samples of each workload; tokens are independent after
+    ternarization, so a row sample's rate is the workload's rate.  Returns the
+    cpu_baseline object: the headline (M=1, 7 projections of a layer) in
+    GB/s, the other workloads under per_config."""
     import numpy as np
 
     import oracle
     from bit_ternary_weight_amd import synth
     H, I, KV = synth.HIDDEN, synth.INTERMEDIATE, synth.KV_DIM
-    layers = []
-    for l in range(2):
-        codes, wms = {}, {}
-        for p, _, _ in synth.PROJECTIONS:
-            _, wm, c = oracle.ternarize_pack(synth.layer_weight(l, p))
-            codes[p], wms[p] = c, wm
-        layers.append((codes, wms))
-    x = synth.bf16_to_f32(synth.act_outliers_bf16(0, 1, H))
-    n = 0
-    nbytes = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        codes, wms = layers[n % 2]
-        out = oracle.layer(x, codes, wms)
-        nbytes += layer_bytes(1, 2 if n == 0 else 4, H, I, KV)
-        x = out["y"]
-        n += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} single-token (M=1) layer forwards of the 2B4T layer shape, alternating two "
-                      f"seeded layers' codes, {dt:.1f} s on one host thread (same bytes accounting as the GPU)"}
+    try:
+        allowed = os.sched_getaffinity(0)
+        core = min(allowed)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        allowed, core = None, None
+    try:
+        layers = []
+        for l in range(2):
+            codes, wms = {}, {}
+            for p, _, _ in synth.PROJECTIONS:
+                _, wm, c = oracle.ternarize_pack(synth.layer_weight(l, p))
+                codes[p], wms[p] = c, wm
+            layers.append((codes, wms))
+
+        def seven(M, kind, reps):
+            """M tokens through the 7 projections, each with its own input."""
+            xs = {}
+            for j, (p, N, K) in enumerate(synth.PROJECTIONS):
+                b = synth.act_heavy_tail_bf16(100 + j, M, K) if kind == "heavy" else synth.act_outliers_bf16(100 + j, M, K)
+                xs[p] = synth.bf16_to_f32(b)
+            t0 = time.perf_counter()
+            for r in range(reps):
+                codes, wms = layers[r % 2]
+                for p, N, K in synth.PROJECTIONS:
+                    oracle.bitlinear(xs[p], codes[p], None, wms[p])
+            dt = time.perf_counter() - t0
+            nbytes = reps * sum(N * K // 4 + M * K * 2 + M * N * 4 for _, N, K in synth.PROJECTIONS)
+            return nbytes / dt / 1e9, dt
+
+        out = {}
+        W1, x1 = synth.config1()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            _, wm1, c1 = oracle.ternarize_pack(W1)
+            oracle.bitlinear(x1, c1, None, wm1)
+        t1 = (time.perf_counter() - t0) / 20
+        out["config1_us_per_forward"] = round(t1 * 1e6, 1)
+        g2, t2 = seven(1, "outliers", 40)
+        out["config2_decode_m1_gbs"] = round(g2, 4)
+        g16, t16 = seven(16, "heavy", 2)
+        out["config3_decode_m16_gbs"] = round(g16, 4)
+        g64, t64 = seven(64, "heavy", 1)
+        out["config3_decode_m64_gbs"] = round(g64, 4)
+        # config 4 on 16 of its 2048 rows (gate|up then down)
+        rows4 = 16
+        codes, wms = layers[0]
+        cgu = np.concatenate([codes["gate"], codes["up"]])
+        wgu = np.array([wms["gate"], wms["up"]], np.float32)
+        xg = synth.bf16_to_f32(synth.act_normal_bf16(0, rows4, H))
+        xd = synth.bf16_to_f32(synth.act_normal_bf16(1, rows4, I))
+        t0 = time.perf_counter()
+        oracle.bitlinear(xg, cgu, [I, I], wgu)
+        oracle.bitlinear(xd, codes["down"], None, wms["down"])
+        t4 = time.perf_counter() - t0
+        out["config4_prefill_tops"] = round(2 * rows4 * (2 * I * H + H * I) / t4 / 1e12, 6)
+        # config 5: the chained decode through 30 layers (two layers' codes
+        # alternating) and the prefill on 4 of 4096 rows through 30 layers
+        x = synth.bf16_to_f32(synth.act_outliers_bf16(0, 1, H))
+        t0 = time.perf_counter()
+        for l in range(30):
+            codes, wms = layers[l % 2]
+            x = oracle.layer(x, codes, wms)["y"]
+        t5d = time.perf_counter() - t0
+        out["config5_decode_m1_gbs"] = round((layer_bytes(1, 2, H, I, KV) + 29 * layer_bytes(1, 4, H, I, KV))
+                                             / t5d / 1e9, 4)
+        rows5 = 4
+        x = synth.bf16_to_f32(synth.act_normal_bf16(0, rows5, H))
+        t0 = time.perf_counter()
+        for l in range(30):
+            codes, wms = layers[l % 2]
+            x = oracle.layer(x, codes, wms)["y"]
+        t5p = time.perf_counter() - t0
+        out["config5_prefill_tops"] = round(30 * layer_ops(rows5, H, I, KV) / t5p / 1e12, 6)
+        total = t2 + t16 + t64 + t4 + t5d + t5p
+    finally:
+        if allowed is not None:
+            os.sched_setaffinity(0, allowed)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": out["config2_decode_m1_gbs"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"oracle (gcc {' '.join(oracle.CFLAGS[:4])}), one thread pinned to core {core}: "
+                       f"config 1 in full (ternarize + forward, 20 times), config 2 in full (40 single-token passes over the 7 projections, two seeded layers' "
+                       f"codes alternating), config 3 in full (M=16 twice, M=64 once), config 4 on 16 of "
+                       f"2048 rows, config 5 decode in full (30 chained layers), config 5 prefill on 4 of 4096 "
+                       f"rows through 30 layers; rates scale with the rows (tokens are independent); "
+                       f"{total:.1f} s of CPU work"),
+            "per_config": out, "cpu_model": model, "host_cpus": os.cpu_count(),
+            "flags": " ".join(oracle.CFLAGS)}
 
 
 ATTN_CTX = 4096
@@ -229,7 +350,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -250,6 +371,15 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    # the oracle's CPU baseline first, before anything touches the GPU (its
+    # core is pinned and nothing else runs meanwhile)
+    run_cpu = not (args.no_cpu or args.copy_probe or args.kernel_only or args.attn_only or args.ste_only
+                   or args.attn_prefill_only)
+    cpu = cpu_baseline() if run_cpu else None
+    if cpu is not None:
+        log(f"cpu baseline (oracle, 1 core): {cpu['value']} GB/s decode; {cpu['per_config']}")
+
     import torch
 
     from bit_ternary_weight_amd import binding as bl
@@ -308,25 +438,39 @@ def main():
         return sum(N * K // 4 + M * K * 2 + M * N * 4 for _, N, K in synth.PROJECTIONS)
 
     probs1 = seven_problems(1, layers, "outliers")
-    one_pass = lambda: [bl.gemv_w2a8_batched(pl) for pl in probs1]
-    g1 = capture(torch, one_pass)
-    passes = max(1, args.steps // len(layers))
-    steps = passes * len(layers)
-    ms_pass = timer.run(g1.replay, passes, max(1, args.warmup // len(layers) + 1))
-    ms = ms_pass / len(layers)
+    # One step = one layer's 7 projections in one launch; step i uses layer
+    # i mod 30, so consecutive steps read different weights.  The timed region
+    # is a graph of exactly K steps (after W untimed steps); it is replayed
+    # until at least 5 regions and 50 ms have been timed, and the median
+    # region gives the step time.
+    steps = max(1, args.steps)
+    nl = len(layers)
+    warm_fn = lambda: [bl.gemv_w2a8_batched(probs1[i % nl]) for i in range(max(0, args.warmup))]
+    timed_fn = lambda: [bl.gemv_w2a8_batched(probs1[i % nl]) for i in range(steps)]
+    warm_fn()
+    g1 = capture(torch, timed_fn)
+    g1.replay()
+    ms_region, n_regions = timer.trials(g1.replay)
+    ms = ms_region / steps
     sb = step_bytes7(1)
     value = sb / (ms * 1e-3) / 1e9
-    log(f"decode M=1, 7 projections: {ms * 1e3:.2f} us/step, {value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak)")
+    log(f"decode M=1, 7 projections: {ms * 1e3:.2f} us/step, {value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak); "
+        f"median of {n_regions} timed regions of {steps} steps")
 
     # The headline kernel is the only launch of a step: its average launch
     # duration over the timed region is the step time (back-to-back launches
-    # from a graph), so the roofline uses the same bytes and time.
+    # from a graph, gaps included), so the roofline uses the same bytes and
+    # time.  The committed kernel trace of this command gives the kernel's
+    # duration under the tracer; both are reported.
     traffic = profiled_traffic()
+    prof_us = profiled_duration_us()
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_gemv_v1<false, bf16 one row, 10 units> (batched one-row decode GEMV, fused per-token quantization)",
-                "bytes_per_launch": sb, "avg_launch_us": round(ms * 1e3, 3),
-                "traffic_over_algorithmic": None if traffic is None else round(traffic / sb, 4)}
+                "bytes_per_launch": sb, "avg_launch_us": round(ms * 1e3, 3), "timing": "hip events, graph replay",
+                "traffic_over_algorithmic": None if traffic is None else round(traffic / sb, 4),
+                "rocprof_avg_us": prof_us,
+                "rocprof_frac": None if prof_us is None else round(sb / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if args.kernel_only:
         print(json.dumps({"roofline": roofline}), flush=True)
         return
@@ -455,7 +599,6 @@ def main():
         extra["ternarize_pack_gbs"] = round((W.numel() * 4 + pk.numel()) / (t * 1e-3) / 1e9, 1)
         del W
 
-    cpu = None if args.no_cpu else cpu_baseline()
     line = {
         "metric": "W1.58A8 BitLinear decode GEMV HBM GB/s (M=1, 7 projections of a 2B4T layer per step)",
         "value": round(value, 2),

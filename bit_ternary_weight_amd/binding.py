@@ -53,6 +53,7 @@ MAX_PROBLEMS = 8
 
 _SIGS = {
     "bl_abi_version": (_I, []),
+    "bl_device_errors": (_I, [ctypes.POINTER(ctypes.c_uint), _I]),
     "bl_status_string": (ctypes.c_char_p, [_I]),
     "bl_last_error": (ctypes.c_char_p, []),
     "bl_ternarize_workspace_bytes": (_S, [_L, _L]),
@@ -60,10 +61,10 @@ _SIGS = {
     "bl_quant_act": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "bl_rmsnorm_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _P, _P]),
     "bl_attn_prefill_workspace_bytes": (_S, [_I, _I, _I]),
-    "bl_ste_grad_input_workspace_bytes": (_S, [_I, _I]),
+    "bl_ste_grad_input_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "bl_ste_grad_weight_workspace_bytes": (_S, [_I, _I, _I]),
-    "bl_ste_grad_input": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
-    "bl_ste_grad_weight": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _S, _P]),
+    "bl_ste_grad_input": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "bl_ste_grad_weight": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P, _S, _P]),
     "bl_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_subln_gemv_workspace_bytes": (_S, [_I, _I]),
     "bl_subln_gemv_w2a8": (_I, [_P, _I, _I, _I, _P, ctypes.c_float, _P, _I, _P, _P, _I, _P, _P, _P, _S, _P]),
@@ -174,6 +175,14 @@ def _segs(seg_n, N):
 # ---------------------------------------------------------------------------
 # Entry points
 # ---------------------------------------------------------------------------
+def device_errors(reset: bool = True) -> int:
+    """Expired bounded waits counted by the kernels on the current device
+    since the last reset (synchronizes the device; see bl_device_errors)."""
+    n = ctypes.c_uint(0)
+    _check(raw.bl_device_errors(ctypes.byref(n), int(reset)))
+    return int(n.value)
+
+
 def ternarize_pack(W: torch.Tensor, packed: torch.Tensor = None, w_mean: torch.Tensor = None):
     """W fp32 [N,K] -> (packed uint8 [N/4,K], w_mean fp32 [1])."""
     dev = _dev(W)
@@ -326,7 +335,9 @@ def gemm_w2a8(x, packed, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=No
 
 def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g_ffn=None, eps=1e-5,
               y_dtype=torch.float32, debug=False, y=None):
-    """FFN half of a layer.  Returns y, or (y, dict of stage outputs) with debug=True."""
+    """FFN half of a layer.  Returns y, or (y, dict of stage outputs) with
+    debug=True; debug may also be a dict of preallocated stage buffers (q1,
+    a1, p, q2, a2; missing ones are allocated)."""
     dev = _dev(h, packed_gu, packed_down)
     M, H = h.shape
     I = packed_gu.shape[0] * 2
@@ -343,11 +354,16 @@ def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g
     stages = None
     dbg = None
     if debug:
-        stages = dict(q1=torch.empty((M, H), dtype=torch.int8, device=dev),
-                      a1=torch.empty(M, dtype=torch.float32, device=dev),
-                      p=torch.empty((M, I), dtype=torch.float32, device=dev),
-                      q2=torch.empty((M, I), dtype=torch.int8, device=dev),
-                      a2=torch.empty(M, dtype=torch.float32, device=dev))
+        shapes = dict(q1=((M, H), torch.int8), a1=((M,), torch.float32), p=((M, I), torch.float32),
+                      q2=((M, I), torch.int8), a2=((M,), torch.float32))
+        given = debug if isinstance(debug, dict) else {}
+        stages = {}
+        for k, (shp, dt) in shapes.items():
+            t = given.get(k)
+            if t is None:
+                t = torch.empty(shp, dtype=dt, device=dev)
+            _need(t, shp, (dt,), k)
+            stages[k] = t
         dbg = FfnDebug(*[stages[k].data_ptr() for k in ("q1", "a1", "p", "q2", "a2")])
     nbytes = raw.bl_ffn_chain_workspace_bytes(M, H, I)
     ws = workspace(dev, nbytes)
@@ -429,37 +445,38 @@ def attn_prefill(q, k, v, k_cache, v_cache, rope_cos, rope_sin, n_heads, n_kv_he
 
 
 def ste_grad_input(dy, packed, w_mean, dx=None):
-    """dX = dY . (codes * w_mean) for dy [M,N] bf16 and one packed weight
-    segment [N/4,K] (see bl_ste_grad_input); returns dx [M,K] fp32."""
+    """dX = dY . (codes * w_mean) for dy [M,N] bf16 or fp32 (rounded to bf16
+    on the device) and one packed weight segment [N/4,K] (see
+    bl_ste_grad_input); returns dx [M,K] fp32."""
     dev = _dev(dy, packed, w_mean)
     M, N = dy.shape
     K = packed.shape[1]
-    _need(dy, (M, N), (torch.bfloat16,), "dy")
+    _need(dy, (M, N), (torch.bfloat16, torch.float32), "dy")
     _need(packed, (N // 4, K), (torch.uint8,), "packed")
     _need(w_mean, (1,), (torch.float32,), "w_mean")
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.float32, device=dev)
     _need(dx, (M, K), (torch.float32,), "dx")
-    ws = workspace(dev, raw.bl_ste_grad_input_workspace_bytes(N, K))
-    _check(raw.bl_ste_grad_input(_ptr(dy), M, N, K, _ptr(packed), _ptr(w_mean), _ptr(dx), _ptr(ws), ws.numel(),
-                                 _stream(dev)))
+    ws = workspace(dev, raw.bl_ste_grad_input_workspace_bytes(M, N, K, _dt(dy)))
+    _check(raw.bl_ste_grad_input(_ptr(dy), _dt(dy), M, N, K, _ptr(packed), _ptr(w_mean), _ptr(dx), _ptr(ws),
+                                 ws.numel(), _stream(dev)))
     return dx
 
 
 def ste_grad_weight(dy, q, a, dw=None):
-    """dW = sum_m bf16(dY[m] / a[m]) (x) q[m] for dy [M,N] bf16 and the
+    """dW = sum_m bf16(dY[m] / a[m]) (x) q[m] for dy [M,N] bf16 or fp32 and the
     forward's activation codes q [M,K] int8 and scales a [M] (see
     bl_ste_grad_weight); returns dw [N,K] fp32."""
     dev = _dev(dy, q, a)
     M, N = dy.shape
     K = q.shape[1]
-    _need(dy, (M, N), (torch.bfloat16,), "dy")
+    _need(dy, (M, N), (torch.bfloat16, torch.float32), "dy")
     _need(q, (M, K), (torch.int8,), "q")
     _need(a, (M,), (torch.float32,), "a")
     if dw is None:
         dw = torch.empty((N, K), dtype=torch.float32, device=dev)
     _need(dw, (N, K), (torch.float32,), "dw")
     ws = workspace(dev, raw.bl_ste_grad_weight_workspace_bytes(M, N, K))
-    _check(raw.bl_ste_grad_weight(_ptr(dy), _ptr(q), _ptr(a), M, N, K, _ptr(dw), _ptr(ws), ws.numel(),
+    _check(raw.bl_ste_grad_weight(_ptr(dy), _dt(dy), _ptr(q), _ptr(a), M, N, K, _ptr(dw), _ptr(ws), ws.numel(),
                                   _stream(dev)))
     return dw

@@ -5,9 +5,58 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "bitlinear.h"
 
 namespace bl {
+
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).  Thread-safe.
+inline int device_cu_count() {
+    static std::mutex mu;
+    static std::map<int, int> cus;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cus.find(dev);
+    if (it != cus.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cus[dev] = n;
+    return n;
+}
+
+// Allows `bytes` of dynamic LDS for `kernel` on the current device (needed
+// above 64 KiB): set once per (device, kernel) and raised when a launch needs
+// more.  Thread-safe; a failure is returned and not left pending.
+inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, size_t> allowed;
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) {
+        (void)hipGetLastError();
+        return e;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    size_t &have = allowed[{dev, kernel}];
+    if (have >= bytes) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return e;
+    }
+    have = bytes;
+    return hipSuccess;
+}
 
 // Packed-row layout of a (possibly segmented) packed weight.  Segment s owns
 // packed rows [roff[s], roff[s+1]); its output columns start at 4*roff[s] and
@@ -272,6 +321,10 @@ hipError_t launch_attn_decode(const float *q, const float *k_new, const float *v
 // else computed into qsum_ws (device scratch for M ints); with neither the
 // small-tile kernel runs.
 hipError_t launch_gemm(const Contract &c, int *qsum_ws, hipStream_t s);
+
+// Expired bounded waits counted by the decode kernels on the current device
+// (synchronous read; reset clears the count).
+hipError_t gemv_wait_expired(unsigned int *count, bool reset);
 // Any K (slow, simple): used when K is not a multiple of 16.
 hipError_t launch_generic(const Contract &c, hipStream_t s);
 

@@ -526,19 +526,7 @@ __global__ __launch_bounds__(256) void k_generic(Contract c) {
 
 } // namespace
 
-static int cu_count() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-            (void)hipGetLastError();
-            n = 256;
-        }
-        cus = n;
-    }
-    return cus;
-}
+static int cu_count() { return device_cu_count(); }
 
 template <bool PAIR, int TM, int NBW, bool VOUT>
 hipError_t go_big(const Contract &c, hipStream_t s) {
@@ -552,19 +540,13 @@ hipError_t go_big(const Contract &c, hipStream_t s) {
     // 140 us against 128 us.
     const int cus = cu_count();
     const bool shift = !PAIR && TM % 64 == 0 && 2 * tiles >= 5 * cus;
+    // nH half tiles pair up into whole tiles: it must be even (an odd count
+    // would leave the second half of the last tile unwritten).
     const int nA = shift ? cus : tiles;
-    const int nH = shift ? cus : 0;
+    const int nH = shift ? (cus & ~1) : 0;
     const size_t lds = (size_t)kGStages * S::STAGE;
-    static bool attr = false;   // the dynamic LDS above 64 KiB must be allowed once
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_gemm_big<PAIR, TM, NBW, VOUT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return e;
-        }
-        attr = true;
-    }
+    if (hipError_t e = allow_dynamic_lds((const void *)k_gemm_big<PAIR, TM, NBW, VOUT>, lds); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((k_gemm_big<PAIR, TM, NBW, VOUT>), dim3(tiles + nH / 2), dim3(256), lds, s, c, ntm, nA, nH);
     return hipGetLastError();
 }

@@ -357,6 +357,10 @@ constexpr int kLdsQBytes = 12288;    // static LDS for the activation codes (M r
 constexpr int kXRegs = 8;            // 16-byte activation chunks per quantizer lane (all rows)
 constexpr int kSpinMax = 1 << 22;    // bound of every flag wait (about 0.2 s)
 
+// Count of bounded waits that expired in this file's kernels (one copy per
+// device); read and cleared by wait_expired_count().
+__device__ unsigned int g_wait_expired = 0;
+
 // Input kind of a launch of the streaming kernel, shared by all its problems:
 // activation dtype, RMSNorm in the prologue or not, one activation row or up
 // to four.  Each kind is its own kernel: the quantizer code of the other
@@ -474,20 +478,27 @@ __device__ __forceinline__ void publish(int *qflag, int w, int step) {
 // sleeps SLEEP x 64 cycles, so that spinning waves leave the SIMD to the
 // waves sharing it (the stream waves' wait is long; the quantizer waves'
 // waits on each other are short).
+// A wait that runs out of polls (which only a wave held off the CU for
+// about 0.2 s could cause) lets the kernel finish with whatever the flags
+// guard, and counts itself in g_wait_expired (a vector atomic) so that
+// bl_device_errors reports the call as unreliable instead of its output
+// passing silently.
 template <int SLEEP>
 __device__ __forceinline__ void wait_published(const int *qflag, int step) {
     static_assert(kQuantWaves == 8, "two 16-byte reads cover the flags");
+    int lo = 0;
     for (int it = 0; it < kSpinMax; ++it) {
         asm volatile("" ::: "memory");
         const v4i f = *reinterpret_cast<const v4i *>(qflag);
         const v4i h = *reinterpret_cast<const v4i *>(qflag + 4);
-        int lo = step;
+        lo = step;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             lo = min(lo, min(__builtin_amdgcn_readfirstlane(f[i]), __builtin_amdgcn_readfirstlane(h[i])));
         if (lo >= step) break;
         __builtin_amdgcn_s_sleep(SLEEP);
     }
+    if (lo < step && (threadIdx.x & 63) == 0) atomicAdd(&g_wait_expired, 1u);
     asm volatile("" ::: "memory");
 }
 
@@ -1017,16 +1028,7 @@ size_t even_share(const GemvBatch &b, int nb, int cus) {
 template <bool PAIR, int XK>
 hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
     constexpr int NB = PAIR ? 2 : 1;
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-            (void)hipGetLastError();
-            n = 256;
-        }
-        cus = n;
-    }
+    const int cus = device_cu_count();
     const size_t share = even_share(b, NB, cus) * 5 / 4;
     GemvBatch o = b;
     int order[kMaxProblems];
@@ -1051,16 +1053,7 @@ hipError_t launch_lds(GemvBatch &b, hipStream_t s) {
     const size_t lds = (size_t)kStreamWaves * kRing * 1024;   // dynamic part: the weight ring
     // Dynamic LDS above the default 64 KiB must be allowed per kernel (the
     // static part, about 17 KiB, comes on top; both fit the 160 KiB).
-    static size_t attr_bytes = 0;
-    if (attr_bytes < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_gemv_lds<PAIR, XK>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();   // do not leave the error to the next launch
-            return e;
-        }
-        attr_bytes = lds;
-    }
+    if (hipError_t e = allow_dynamic_lds((const void *)k_gemv_lds<PAIR, XK>, lds); e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemv_lds<PAIR, XK>), dim3(tiles), dim3(kLdsWaves * 64), lds, s, o);
     return hipGetLastError();
 }
@@ -1353,16 +1346,7 @@ hipError_t go_v1(GemvBatch &o, int tiles, hipStream_t s) {
 template <bool PAIR, int XK>
 hipError_t launch_v1(GemvBatch &b, hipStream_t s) {
     constexpr int NB = PAIR ? 2 : 1;
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-            (void)hipGetLastError();
-            n = 256;
-        }
-        cus = n;
-    }
+    const int cus = device_cu_count();
     // Even share of the weight bytes per CU; each problem's tile is the
     // largest 4 * CS rows (CS = 8 / NB, ..., 1) that stays within 1.25x the
     // share; CS shrinks further until no stream wave has more than
@@ -1718,14 +1702,9 @@ template <int T, int NB>
 hipError_t go_gemv_mt(GemvBatch &o, int tiles, hipStream_t s) {
     const size_t part = (size_t)kMtWaves * T * 4 * 64 * sizeof(v4i);
     const size_t lds = part > (size_t)kMtWaves * kMtBufBytes ? part : (size_t)kMtWaves * kMtBufBytes;
-    static size_t attr = 0;
-    if (lds > 65536 && attr < lds) {
-        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_mt<T, NB>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            e != hipSuccess)
+    if (lds > 65536)
+        if (hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&k_gemv_mt<T, NB>), lds); e != hipSuccess)
             return e;
-        attr = lds;
-    }
     hipLaunchKernelGGL((k_gemv_mt<T, NB>), dim3(tiles), dim3(kMtWaves * 64), lds, s, o);
     return hipGetLastError();
 }
@@ -1773,16 +1752,7 @@ bool gemv_mt_plan_ok(int n, const int *Ms, const int *Ks) {
 // mt_max_blocks blocks; largest tiles on the lowest workgroup numbers.
 // Returns hipErrorNotSupported when some problem's K needs more units.
 hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-            (void)hipGetLastError();
-            n = 256;
-        }
-        cus = n;
-    }
+    const int cus = device_cu_count();
     int maxm = 1;
     for (int i = 0; i < b.n; ++i) maxm = b.p[i].M > maxm ? b.p[i].M : maxm;
     const int T = (maxm + 15) / 16;
@@ -1899,6 +1869,18 @@ hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s) {
     const size_t lds = red_bytes(pair ? 2 : 1, mt) + kOffQ + ((qbytes + 15) & ~(size_t)15);
     if (pair) return fused ? go_mt<true, true>(mt, ksmax, b, tiles, lds, s) : go_mt<true, false>(mt, ksmax, b, tiles, lds, s);
     return fused ? go_mt<false, true>(mt, ksmax, b, tiles, lds, s) : go_mt<false, false>(mt, ksmax, b, tiles, lds, s);
+}
+
+hipError_t gemv_wait_expired(unsigned int *count, bool reset) {
+    unsigned int v = 0;
+    if (hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_wait_expired), sizeof(v)); e != hipSuccess) return e;
+    if (reset && v) {
+        const unsigned int zero = 0;
+        if (hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_wait_expired), &zero, sizeof(zero)); e != hipSuccess)
+            return e;
+    }
+    *count = v;
+    return hipSuccess;
 }
 
 } // namespace bl

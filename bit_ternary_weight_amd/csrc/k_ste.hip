@@ -8,11 +8,15 @@
 // backward that returns the incoming gradient unchanged).
 //
 // Both products run as one bf16 MFMA GEMM, C[i][j] = s * sum_l A[i][l] B[j][l]
-// with both operands contiguous along l, after a preparation launch:
-//   dX: A = dY [M][N] as given (bf16), B = codes transposed [K][N] (bf16,
-//       exact), s = w_mean;
-//   dW: A = bf16(dY[m][n] / a[m]) transposed [N][M], B = q transposed [K][M]
-//       (bf16, exact), s = 1.
+// with both operands contiguous along l, after preparation launches that
+// write the operands in bf16, zero-padded to whole tiles (rows to 128, the
+// contraction to 64):
+//   dX: A = dY [M][N] (used in place when it is bf16 and already whole tiles,
+//       else rounded / copied), B = codes transposed [K][N] (exact), s = w_mean;
+//   dW: A = bf16(fp32(dY[m][n] / a[m])) transposed [N][M], B = q transposed
+//       [K][M] (exact), s = 1.
+// The output gradient may be bf16 or fp32; an fp32 one is rounded to nearest
+// even here (for dW after the division by a, one rounding).
 // The GEMM: 128 x 128 output tiles, 4 waves of 64 x 64, 64-deep stages
 // through LDS (pieces of a row permuted, the next stage's loads in flight in
 // registers), v_mfma_f32_16x16x32_bf16 with the B fragment as the first
@@ -40,45 +44,81 @@ __device__ __forceinline__ int k_piece(int g, int ks) { return (g & 1) | ((g >> 
 
 __device__ __forceinline__ __bf16 to_bf(float x) { return static_cast<__bf16>(x); }
 
-// Codes of a plane-order packed weight, transposed: ct[k][n] = code(n, k) in
-// bf16 (-1, 0, 1).  Block: 32 packed rows x 64 columns; thread (k = t >> 2,
-// field f = t & 3) writes the 32 consecutive rows n = f*R + r0 .. +31.
-__global__ __launch_bounds__(256) void k_codes_t(const uint8_t *P, int R, int K, __bf16 *ct) {
+// Codes of a plane-order packed weight, transposed and zero-padded:
+// ct[k][n] = code(n, k) in bf16 (-1, 0, 1) for k < K, n < N = 4R, and 0 for
+// K <= k < J or N <= n < L (ct is [J][L]).  Block: 32 packed rows x 64
+// columns; thread (k = t >> 2, field f = t & 3) writes the rows n = f*R + r
+// of its 32 packed rows r that exist.  The first column of blocks also
+// clears the padding columns N .. L-1 of its 64 rows.
+__global__ __launch_bounds__(256) void k_codes_t(const uint8_t *P, int R, int K, int L, __bf16 *ct) {
     __shared__ uint8_t tile[32][64 + 4];
     const int r0 = blockIdx.x * 32, k0 = blockIdx.y * 64, t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int e = t + 256 * i, r = e >> 6, k = e & 63;
-        tile[r][k] = P[(size_t)(r0 + r) * K + k0 + k];
+        tile[r][k] = (r0 + r < R && k0 + k < K) ? P[(size_t)(r0 + r) * K + k0 + k] : (uint8_t)0x55;
     }
     __syncthreads();
     const int k = t >> 2, f = t & 3;
-    __bf16 *dst = ct + (size_t)(k0 + k) * (4 * R) + f * R + r0;
+    const bool krow = k0 + k < K;
+    __bf16 *dst = ct + (size_t)(k0 + k) * L + f * R + r0;
+    const bool vec = (R & 7) == 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         bf16x8 v;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = to_bf((float)(((tile[8 * c + j][k] >> (2 * f)) & 3) - 1));
-        *reinterpret_cast<bf16x8 *>(dst + 8 * c) = v;
+        for (int j = 0; j < 8; ++j)
+            v[j] = to_bf(krow ? (float)(((tile[8 * c + j][k] >> (2 * f)) & 3) - 1) : 0.0f);
+        if (vec && r0 + 8 * c + 8 <= R) {
+            *reinterpret_cast<bf16x8 *>(dst + 8 * c) = v;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (r0 + 8 * c + j < R) dst[8 * c + j] = v[j];
+        }
+    }
+    if (blockIdx.x == 0) {
+        __bf16 *row = ct + (size_t)(k0 + k) * L;
+        for (int n = 4 * R + f; n < L; n += 4) row[n] = to_bf(0.0f);
     }
 }
 
-// dst[c][r] = bf16(src[r][c] / a[r]) (bf16 src, SCALE) or bf16(src[r][c])
-// (int8 src) for a [rows][cols] source; 64 x 64 blocks through LDS.
+// dst[i][l] = bf16(src[i][l]) for i < rows, l < cols, 0 elsewhere in the
+// padded [I][L] destination (L a multiple of 8); 8 columns per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_pad_bf16(const T *src, int rows, int cols, __bf16 *dst, int I, int L) {
+    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int per_row = L / 8;
+    if (e >= (size_t)I * per_row) return;
+    const int i = (int)(e / per_row), l0 = (int)(e % per_row) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = to_bf((i < rows && l0 + j < cols) ? (float)src[(size_t)i * cols + l0 + j] : 0.0f);
+    *reinterpret_cast<bf16x8 *>(dst + (size_t)i * L + l0) = v;
+}
+
+// dst[c][r] = bf16(src[r][c] / a[r]) (SCALE) or bf16(src[r][c]) for a
+// [rows][cols] source, zero outside it; dst is [C][R] with C, R multiples of
+// 64 covering cols, rows.  64 x 64 blocks through LDS.
 template <typename T, bool SCALE>
-__global__ __launch_bounds__(256) void k_transpose(const T *src, int rows, int cols, const float *a, __bf16 *dst) {
+__global__ __launch_bounds__(256) void k_transpose(const T *src, int rows, int cols, const float *a, __bf16 *dst,
+                                                   int R) {
     __shared__ float tile[64][64 + 1];
     const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int e = t + 256 * i, r = e >> 6, c = e & 63;
-        float v = (float)src[(size_t)(r0 + r) * cols + c0 + c];
-        if (SCALE) v = v / a[r0 + r];
+        float v = 0.0f;
+        if (r0 + r < rows && c0 + c < cols) {
+            v = (float)src[(size_t)(r0 + r) * cols + c0 + c];
+            if (SCALE) v = v / a[r0 + r];
+        }
         tile[r][c] = v;
     }
     __syncthreads();
     const int c = t >> 2, q = (t & 3) * 16;
-    __bf16 *d = dst + (size_t)(c0 + c) * rows + r0 + q;
+    __bf16 *d = dst + (size_t)(c0 + c) * R + r0 + q;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         bf16x8 v;
@@ -92,10 +132,11 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// C[i][j] = s * sum_l A[i][l] B[j][l]; A [I][L], B [J][L] bf16, C [I][J] fp32;
-// I, J, L multiples of 128, 128, 64; s read from device memory (1 if null).
+// C[i][j] = s * sum_l A[i][l] B[j][l] for i < Ir, j < Jr; A [I][L], B [J][L]
+// bf16 (zero-padded), C [Ir][Jr] fp32 with row stride Jr; I, J, L multiples
+// of 128, 128, 64; s read from device memory (1 if null).
 __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __bf16 *B, float *C, int I, int J,
-                                                       int L, const float *s_ptr) {
+                                                       int L, int Ir, int Jr, const float *s_ptr) {
     const float s = s_ptr ? *s_ptr : 1.0f;
     __shared__ __attribute__((aligned(16))) __bf16 as[kT * kL];
     __shared__ __attribute__((aligned(16))) __bf16 bs[kT * kL];
@@ -146,9 +187,11 @@ __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __b
                 for (int y = 0; y < 4; ++y) acc[x][y] = mfma_bf16(bf[y], af[x], acc[x][y]);
         }
     }
+    const bool whole = i0 + kT <= Ir && j0 + kT <= Jr && (Jr & 3) == 0;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-        float *crow = C + (size_t)(i0 + wi + 16 * x + lr) * J + j0 + wj + 4 * g;
+        const int i = i0 + wi + 16 * x + lr;
+        float *crow = C + (size_t)i * Jr + j0 + wj + 4 * g;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
             float4 v;
@@ -156,35 +199,84 @@ __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __b
             v.y = acc[x][y][1] * s;
             v.z = acc[x][y][2] * s;
             v.w = acc[x][y][3] * s;
-            *reinterpret_cast<float4 *>(crow + 16 * y) = v;
+            if (whole) {
+                *reinterpret_cast<float4 *>(crow + 16 * y) = v;
+            } else if (i < Ir) {
+                const int j = j0 + wj + 4 * g + 16 * y;
+                if (j + 0 < Jr) crow[16 * y + 0] = v.x;
+                if (j + 1 < Jr) crow[16 * y + 1] = v.y;
+                if (j + 2 < Jr) crow[16 * y + 2] = v.z;
+                if (j + 3 < Jr) crow[16 * y + 3] = v.w;
+            }
         }
     }
 }
 
+inline int pad_to(int x, int m) { return (x + m - 1) / m * m; }
+
+// dX operand A is taken in place when it is already bf16 in whole tiles.
+bool dy_in_place(int M, int N, bool dy_bf16) { return dy_bf16 && M % kT == 0 && N % kL == 0; }
+
 } // namespace
 
-size_t ste_grad_input_ws_bytes(int N, int K) { return (size_t)K * N * sizeof(__bf16); }
-size_t ste_grad_weight_ws_bytes(int M, int N, int K) { return ((size_t)N * M + (size_t)K * M) * sizeof(__bf16); }
+size_t ste_grad_input_ws_bytes(int M, int N, int K, bool dy_bf16) {
+    const size_t L = pad_to(N, kL), I = pad_to(M, kT), J = pad_to(K, kT);
+    const size_t ct = (J * L * sizeof(__bf16) + 255) & ~(size_t)255;
+    return ct + (dy_in_place(M, N, dy_bf16) ? 0 : I * L * sizeof(__bf16));
+}
 
-hipError_t launch_ste_grad_input(const __bf16 *dY, int M, int N, int K, const uint8_t *packed, const float *w_mean,
-                                 float *dX, void *ws, hipStream_t s) {
+size_t ste_grad_weight_ws_bytes(int M, int N, int K) {
+    const size_t L = pad_to(M, kL), I = pad_to(N, kT), J = pad_to(K, kT);
+    return ((I * L * sizeof(__bf16) + 255) & ~(size_t)255) + J * L * sizeof(__bf16);
+}
+
+bool ste_dims_fit(int M, int N, int K) {
+    const size_t a = pad_to(M, kT), b = pad_to(N, kT), c = pad_to(K, kT);
+    const size_t lim = (size_t)1 << 31;
+    return a * b < lim && a * c < lim && b * c < lim;
+}
+
+hipError_t launch_ste_grad_input(const void *dY, bool dy_bf16, int M, int N, int K, const uint8_t *packed,
+                                 const float *w_mean, float *dX, void *ws, hipStream_t s) {
+    const int L = pad_to(N, kL), I = pad_to(M, kT), J = pad_to(K, kT), R = N / 4;
     __bf16 *ct = static_cast<__bf16 *>(ws);
-    const int R = N / 4;
-    hipLaunchKernelGGL(k_codes_t, dim3(R / 32, K / 64), dim3(256), 0, s, packed, R, K, ct);
+    hipLaunchKernelGGL(k_codes_t, dim3((R + 31) / 32, J / 64), dim3(256), 0, s, packed, R, K, L, ct);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_nt_bf16, dim3((M / kT) * (K / kT)), dim3(256), 0, s, dY, ct, dX, M, K, N, w_mean);
+    const __bf16 *A = static_cast<const __bf16 *>(dY);
+    if (!dy_in_place(M, N, dy_bf16)) {
+        __bf16 *dyb = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) +
+                                                 (((size_t)J * L * sizeof(__bf16) + 255) & ~(size_t)255));
+        const size_t threads = (size_t)I * (L / 8);
+        const dim3 grid((unsigned)((threads + 255) / 256));
+        if (dy_bf16)
+            hipLaunchKernelGGL(k_pad_bf16<__bf16>, grid, dim3(256), 0, s, static_cast<const __bf16 *>(dY), M, N, dyb,
+                               I, L);
+        else
+            hipLaunchKernelGGL(k_pad_bf16<float>, grid, dim3(256), 0, s, static_cast<const float *>(dY), M, N, dyb, I,
+                               L);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        A = dyb;
+    }
+    hipLaunchKernelGGL(k_gemm_nt_bf16, dim3((I / kT) * (J / kT)), dim3(256), 0, s, A, ct, dX, I, J, L, M, K, w_mean);
     return hipGetLastError();
 }
 
-hipError_t launch_ste_grad_weight(const __bf16 *dY, int M, int N, int K, const int8_t *q, const float *a, float *dW,
-                                  void *ws, hipStream_t s) {
-    __bf16 *at = static_cast<__bf16 *>(ws);          // [N][M]
-    __bf16 *qt = at + (size_t)N * M;                 // [K][M]
-    hipLaunchKernelGGL((k_transpose<__bf16, true>), dim3(N / 64, M / 64), dim3(256), 0, s, dY, M, N, a, at);
+hipError_t launch_ste_grad_weight(const void *dY, bool dy_bf16, int M, int N, int K, const int8_t *q, const float *a,
+                                  float *dW, void *ws, hipStream_t s) {
+    const int L = pad_to(M, kL), I = pad_to(N, kT), J = pad_to(K, kT);
+    __bf16 *at = static_cast<__bf16 *>(ws);                                        // [I][L]
+    __bf16 *qt = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) +
+                                            (((size_t)I * L * sizeof(__bf16) + 255) & ~(size_t)255));  // [J][L]
+    if (dy_bf16)
+        hipLaunchKernelGGL((k_transpose<__bf16, true>), dim3(I / 64, L / 64), dim3(256), 0, s,
+                           static_cast<const __bf16 *>(dY), M, N, a, at, L);
+    else
+        hipLaunchKernelGGL((k_transpose<float, true>), dim3(I / 64, L / 64), dim3(256), 0, s,
+                           static_cast<const float *>(dY), M, N, a, at, L);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_transpose<int8_t, false>), dim3(K / 64, M / 64), dim3(256), 0, s, q, M, K, nullptr, qt);
+    hipLaunchKernelGGL((k_transpose<int8_t, false>), dim3(J / 64, L / 64), dim3(256), 0, s, q, M, K, nullptr, qt, L);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_nt_bf16, dim3((N / kT) * (K / kT)), dim3(256), 0, s, at, qt, dW, N, K, M, nullptr);
+    hipLaunchKernelGGL(k_gemm_nt_bf16, dim3((I / kT) * (J / kT)), dim3(256), 0, s, at, qt, dW, I, J, L, N, K, nullptr);
     return hipGetLastError();
 }
 

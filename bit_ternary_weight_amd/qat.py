@@ -12,8 +12,8 @@ quantizers pass gradients straight through in the backward.  So:
 
 Every step runs in libbitlinear: bl_ternarize_pack, bl_quant_act,
 bl_gemv_w2a8 / bl_gemm_w2a8, bl_ste_grad_input, bl_ste_grad_weight.  The
-backward takes the output gradient in bf16 (the products' operand type); an
-fp32 gradient is rounded to bf16 first.
+backward takes the output gradient as it comes (bf16 or fp32); the library
+rounds an fp32 one to bf16, the products' operand type, on the device.
 """
 from __future__ import annotations
 
@@ -35,11 +35,10 @@ def forward(x: torch.Tensor, W: torch.Tensor):
 
 
 def backward(dy: torch.Tensor, saved):
-    """dy [M,N] (bf16, or fp32 rounded to bf16) -> (dx [M,K], dW [N,K]) fp32."""
+    """dy [M,N] bf16 or fp32 -> (dx [M,K], dW [N,K]) fp32."""
     packed, w_mean, q, a = saved
-    if dy.dtype != torch.bfloat16:
-        dy = dy.to(torch.bfloat16)
-    dy = dy.contiguous()
+    if not dy.is_contiguous():
+        raise ValueError("dy must be contiguous")
     return bl.ste_grad_input(dy, packed, w_mean), bl.ste_grad_weight(dy, q, a)
 
 

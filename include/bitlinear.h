@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BL_ABI_VERSION 1
+#define BL_ABI_VERSION 2
 #define BL_MAX_SEGMENTS 8
 #define BL_MAX_PROBLEMS 8
 
@@ -82,6 +82,18 @@ int bl_abi_version(void);
 const char *bl_status_string(int status);
 /* Message of the last failed call on this host thread ("" if none). */
 const char *bl_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * bl_device_errors -- faults the kernels detect themselves.  The decode
+ * kernels' waves wait on each other through flags with a bounded number of
+ * polls; a wait that runs out (only a wave held off its compute unit for
+ * about 0.2 s could cause it) lets the kernel finish normally and counts
+ * itself on the device, and the outputs of that call are then unreliable.
+ * This call synchronizes the current device, stores in *expired_waits (host)
+ * the number of expired waits since the last reset, and clears the count when
+ * reset is non-zero.  Returns BL_OK, BL_ERR_NULL or BL_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+int bl_device_errors(unsigned int *expired_waits, int reset);
 
 /* ---------------------------------------------------------------------------
  * bl_ternarize_pack -- absmean ternarization and 2-bit packing of one weight
@@ -318,23 +330,27 @@ int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int
  * W~ = codes * w_mean and x~ = q / a of the forward:
  *   dX = dY . W~     (bl_ste_grad_input)
  *   dW = dY^T . x~   (bl_ste_grad_weight; the gradient of the fp32 master W)
- *   dy      [M][N] bf16 device, contiguous (the output gradient);
+ *   dy      [M][N] device, contiguous: the output gradient, dy_dtype BL_BF16
+ *           or BL_F32 (an fp32 gradient is rounded to bf16 on the device);
  *   packed  [N/4][K] uint8 device, one weight segment; w_mean [1] fp32 device;
  *   q, a    [M][K] int8 and [M] fp32 device: the forward's activation codes
  *           and scales (bl_quant_act);
- *   dx      out [M][K] fp32 device = (sum_n dy[m][n] code[n][k]) * w_mean;
- *   dw      out [N][K] fp32 device = sum_m bf16(dy[m][n] / a[m]) q[m][k];
- *   ws      scratch of bl_ste_grad_input_workspace_bytes(N, K) /
- *           bl_ste_grad_weight_workspace_bytes(M, N, K) bytes.
- * Precision: bf16 products (the codes and q exactly; dy / a rounded to
- * nearest even) summed in fp32.  M, N, K positive multiples of 128, each
- * product of two below 2^31; dy, packed, q, dx, dw 16-byte aligned.
+ *   dx      out [M][K] fp32 device = (sum_n bf16(dy[m][n]) code[n][k]) * w_mean;
+ *   dw      out [N][K] fp32 device = sum_m bf16(fp32(dy[m][n] / a[m])) q[m][k];
+ *   ws      scratch of bl_ste_grad_input_workspace_bytes(M, N, K, dy_dtype) /
+ *           bl_ste_grad_weight_workspace_bytes(M, N, K) bytes (the operands
+ *           in bf16, padded to whole tiles).
+ * Precision: bf16 products (the codes and q exactly) summed in fp32; the
+ * plain fp64 definitions differ by at most the bf16 rounding of the gradient
+ * (relative 2^-8 per term) plus the fp32 sums.  Any M, N, K >= 1 (N a
+ * multiple of 4 for dx), each product of two of them, rounded up to 128,
+ * below 2^31; dx, dw 16-byte aligned; dy 16-byte aligned for dx.
  * ------------------------------------------------------------------------ */
-size_t bl_ste_grad_input_workspace_bytes(int N, int K);
+size_t bl_ste_grad_input_workspace_bytes(int M, int N, int K, int dy_dtype);
 size_t bl_ste_grad_weight_workspace_bytes(int M, int N, int K);
-int bl_ste_grad_input(const void *dy, int M, int N, int K, const uint8_t *packed, const float *w_mean,
-                      float *dx, void *ws, size_t ws_bytes, bl_stream stream);
-int bl_ste_grad_weight(const void *dy, const int8_t *q, const float *a, int M, int N, int K,
+int bl_ste_grad_input(const void *dy, int dy_dtype, int M, int N, int K, const uint8_t *packed,
+                      const float *w_mean, float *dx, void *ws, size_t ws_bytes, bl_stream stream);
+int bl_ste_grad_weight(const void *dy, int dy_dtype, const int8_t *q, const float *a, int M, int N, int K,
                        float *dw, void *ws, size_t ws_bytes, bl_stream stream);
 
 #ifdef __cplusplus

@@ -41,6 +41,57 @@ def f32_of_bf16(bits: np.ndarray) -> np.ndarray:
     return synth.bf16_to_f32(bits)
 
 
+# Output guards.  Every output buffer a GPU test hands to the library is
+# pre-filled with a byte pattern no correct result can hold, and is followed
+# by a canary tail.  After the call, no element may still hold the pattern
+# (an element never written) and the tail must be intact (no write past the
+# end).  The patterns: NaN for fp32 / bf16 (0xFF bytes); 0x80 bytes for int8
+# codes (-128 is unreachable: |x * a| < 127.5) and int32 accumulators
+# (0x80808080: |A| <= 127 K is far below it); 0xFF for packed bytes (field
+# value 3 is never produced).
+_FILL = {torch.float32: 0xFF, torch.bfloat16: 0xFF, torch.int8: 0x80, torch.int32: 0x80, torch.uint8: 0xFF}
+_TAIL = 512
+_CANARY = 0xA5
+
+
+class Guarded:
+    """A device tensor of `shape` / `dtype` inside a pre-filled buffer with a
+    canary tail (see above); .t is the tensor, .check() the assertions."""
+
+    def __init__(self, shape, dtype):
+        n = 1
+        for d in shape:
+            n *= int(d)
+        esz = torch.tensor([], dtype=dtype).element_size()
+        self.nbytes = n * esz
+        self.raw = torch.empty(self.nbytes + _TAIL, dtype=torch.uint8, device=dev())
+        self.raw[:self.nbytes].fill_(_FILL[dtype])
+        self.raw[self.nbytes:].fill_(_CANARY)
+        self.dtype = dtype
+        self.t = self.raw[:self.nbytes].view(dtype).view(*shape) if n else torch.empty(shape, dtype=dtype,
+                                                                                        device=dev())
+
+    def check(self, what="output"):
+        tail = self.raw[self.nbytes:]
+        assert bool((tail == _CANARY).all()), f"{what}: bytes written past the end of the buffer"
+        if self.nbytes == 0:
+            return
+        t = self.t
+        if self.dtype in (torch.float32, torch.bfloat16):
+            left = int(torch.isnan(t).sum())
+        elif self.dtype == torch.int8:
+            left = int((t == -128).sum())
+        elif self.dtype == torch.int32:
+            left = int((t == -2139062144).sum())
+        else:
+            left = int((t == 0xFF).sum())
+        assert left == 0, f"{what}: {left} elements never written"
+
+
+def guarded(shape, dtype=torch.float32) -> Guarded:
+    return Guarded(shape, dtype)
+
+
 def assert_rows_close(y: np.ndarray, ref: np.ndarray, tol: float, what: str = "y"):
     y = np.asarray(y, np.float64)
     ref = np.asarray(ref, np.float64)

@@ -47,6 +47,7 @@ def test_version_and_status_strings(lib):
     assert names == ["BL_OK", "BL_ERR_NULL", "BL_ERR_SHAPE", "BL_ERR_ALIGN", "BL_ERR_DTYPE",
                      "BL_ERR_SEGMENTS", "BL_ERR_WORKSPACE", "BL_ERR_HIP"]
     assert raw.bl_status_string(99).decode() == "BL_ERR_UNKNOWN"
+    assert raw.bl_device_errors(None, 0) == lib.BL_ERR_NULL
 
 
 FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced

@@ -5,6 +5,8 @@ ReLU^2(gate)*up tensor) are compared bit-exactly; final outputs by the fp32
 tolerance (and expected bit-identical).  The stack is checked layer by layer:
 each layer's GPU output is compared with the oracle's layer run on the same
 input (the GPU's input of that layer), so a difference cannot cascade.
+Every output and stage buffer is pre-filled with a pattern no result can
+hold and followed by a canary tail (gpu_helpers.Guarded).
 """
 import numpy as np
 import pytest
@@ -12,8 +14,8 @@ import torch
 
 import oracle
 from bit_ternary_weight_amd import synth
-from gpu_helpers import (F32_TOL, BF16_TOL, assert_exact, assert_rows_close, bf16_dev, dev, f32_of_bf16, host,
-                         max_ulp_diff, requires_gpu, to_dev)
+from gpu_helpers import (F32_TOL, BF16_TOL, assert_exact, assert_rows_close, bf16_dev, dev, f32_of_bf16, guarded,
+                         host, max_ulp_diff, requires_gpu, to_dev)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -44,11 +46,20 @@ def _check_chain(M, H, I, seed=0, gains=False, h_kind="f32", rows=None, y_dtype=
         rng = np.random.default_rng(seed)
         gs = rng.uniform(0.5, 1.5, size=H).astype(np.float32)
         gf = rng.uniform(0.5, 1.5, size=I).astype(np.float32)
+    gy = guarded((M, H), y_dtype)
+    gst = dict(q1=guarded((M, H), torch.int8), a1=guarded((M,)), p=guarded((M, I)), q2=guarded((M, I), torch.int8),
+               a2=guarded((M,)))
     y, st = _bl().ffn_chain(h_dev, to_dev(pgu), to_dev(wgu), to_dev(pd), to_dev(wd),
                             g_subln=None if gs is None else to_dev(gs), g_ffn=None if gf is None else to_dev(gf),
-                            debug=True, y_dtype=y_dtype)
+                            debug={k: g.t for k, g in gst.items()}, y_dtype=y_dtype, y=gy.t)
+    gy.check("y")
+    for k, g in gst.items():
+        g.check(k)
     rows = list(range(M)) if rows is None else rows
-    ref = oracle.ffn_chain(h_host[rows], cgu, wgu, cd, wd[0], g_subln=gs, g_ffn=gf)
+    if M * I > 4096 * 1024 and len(rows) > 8:
+        ref = oracle.ffn_chain_f64gemm(h_host[rows], cgu, wgu, cd, wd[0], g_subln=gs, g_ffn=gf)
+    else:
+        ref = oracle.ffn_chain(h_host[rows], cgu, wgu, cd, wd[0], g_subln=gs, g_ffn=gf)
     for k in ("q1", "a1", "q2", "a2"):
         assert_exact(host(st[k])[rows], ref[k], k)
     assert_exact(host(st["p"])[rows].view(np.uint32), ref["p"].view(np.uint32), "p bits")
@@ -78,11 +89,28 @@ def test_chain_ragged(M, H, I):
 
 @pytest.mark.parametrize("M", [1, 4, 64])
 def test_chain_full_size_decode(M):
-    _check_chain(M, 2560, 6912, seed=7, h_kind="bf16", rows=None if M <= 4 else [0, 31, 63])
+    _check_chain(M, 2560, 6912, seed=7, h_kind="bf16")
 
 
-def test_chain_full_size_prefill_sampled():
-    _check_chain(2048, 2560, 6912, seed=8, h_kind="bf16", rows=[0, 5, 1023, 2047])
+@pytest.mark.timeout(600)
+def test_chain_full_size_prefill_all_rows():
+    _check_chain(2048, 2560, 6912, seed=8, h_kind="bf16")
+
+
+def test_chain_zero_row():
+    """A zero row through both sub-norms and quantizers (decode and prefill
+    sizes): every stage is exactly zero for it, the other rows as usual."""
+    for M in (3, 130):
+        from bit_ternary_weight_amd import binding as bl
+        pgu, wgu, pd, wd, cgu, cd = _chain_weights(300 + M, 256, 512)
+        h = synth.act_normal_f32(60 + M, M, 256)
+        h[1] = 0.0
+        y, st = bl.ffn_chain(to_dev(h), to_dev(pgu), to_dev(wgu), to_dev(pd), to_dev(wd), debug=True)
+        ref = oracle.ffn_chain(h, cgu, wgu, cd, wd[0])
+        for k in ("q1", "a1", "q2", "a2"):
+            assert_exact(host(st[k]), ref[k], k)
+        assert (host(st["q1"])[1] == 0).all() and (host(y)[1] == 0).all()
+        assert_exact(host(y).view(np.uint32), ref["y"].view(np.uint32), "y bits")
 
 
 # ----------------------------------------------------------------------------- the stack
@@ -96,6 +124,9 @@ def _oracle_layer_codes(layer):
 
 
 def _check_stack(M, n_layers, rows):
+    """Each layer's stage outputs (q|k|v, o, the layer output) at `rows`
+    against the oracle's layer on the GPU's own input to that layer; every
+    buffer guarded over all M rows."""
     from bit_ternary_weight_amd import stack
     layers = stack.build_layers(n_layers, dev())
     if M == 1:
@@ -103,8 +134,9 @@ def _check_stack(M, n_layers, rows):
     else:
         bits = synth.act_normal_bf16(0, M, synth.HIDDEN)
     x = bf16_dev(bits)
-    bufs = {}
     x_host = f32_of_bf16(bits)
+    H = synth.HIDDEN
+    layer_ref = oracle.layer if len(rows) <= 4 else oracle.layer_f64gemm
     for l, lw in enumerate(layers):
         codes, wms = _oracle_layer_codes(l)
         # the device ternarization must reproduce the oracle's packing
@@ -112,13 +144,19 @@ def _check_stack(M, n_layers, rows):
             packed, wm = stack._dest(lw, p)
             assert host(wm)[0] == wms[p]
             assert_exact(host(packed), oracle.pack(codes[p]), f"layer {l} {p} packed")
-        y = stack.layer_forward(x, lw, bufs=bufs)
-        ref = oracle.layer(x_host[rows], codes, wms)
-        yh = host(y)
-        assert_rows_close(yh[rows], ref["y"], F32_TOL, f"layer {l}")
-        assert max_ulp_diff(yh[rows], ref["y"]) == 0, f"layer {l}"
+        g_qkv, g_o, g_y = guarded((M, H + 2 * synth.KV_DIM)), guarded((M, H)), guarded((M, H))
+        bufs = {"y_qkv": g_qkv.t, "y_o": g_o.t}
+        y = stack.layer_forward(x, lw, bufs=bufs, out=g_y.t)
+        for g, what in ((g_qkv, "q|k|v"), (g_o, "o"), (g_y, "layer output")):
+            g.check(f"layer {l} {what}")
+        ref = layer_ref(x_host[rows], codes, wms)
+        for key, t in (("y_qkv", g_qkv.t), ("y_o", g_o.t), ("y", y)):
+            got = host(t)[rows]
+            assert_rows_close(got, ref[key], F32_TOL, f"layer {l} {key}")
+            assert max_ulp_diff(got, ref[key]) == 0, f"layer {l} {key}"
         x = y.clone()
-        x_host = yh
+        x_host = host(y)
+        print(f"[stack M={M}] layer {l} matches the oracle on {len(rows)} rows", flush=True)
 
 
 @pytest.mark.timeout(900)
@@ -126,6 +164,11 @@ def test_stack_decode_30_layers():
     _check_stack(1, 30, [0])
 
 
-@pytest.mark.timeout(600)
-def test_stack_prefill_sampled_rows():
-    _check_stack(4096, 3, [0, 2049, 4095])
+@pytest.mark.timeout(1200)
+def test_stack_prefill_30_layers_one_row_per_token_tile():
+    """M=4096 through all 30 layers: one row in every 32-token block (so in
+    every 96- and 128-token tile of the prefill GEMM), at a different offset
+    in each block, plus the last row."""
+    M = 4096
+    rows = sorted(set([32 * t + (13 * t) % 32 for t in range(M // 32)] + [M - 1]))
+    _check_stack(M, 30, rows)

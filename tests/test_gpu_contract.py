@@ -4,7 +4,9 @@ Weights are always packed by the oracle (its bytes go to the device), so the
 contraction is checked on its own.  int32 accumulators (y dtype int32) are
 compared bit-exactly; fp32 / bf16 outputs by the per-row tolerance, and the
 fp32 path is additionally expected to be bit-identical (it replays the same
-fp32 operations).
+fp32 operations).  Every output buffer is pre-filled with a pattern no
+result can hold and followed by a canary tail (gpu_helpers.Guarded): no
+element may be left unwritten and nothing written past the end.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import torch
 
 import oracle
 from bit_ternary_weight_amd import synth
-from gpu_helpers import (BF16_TOL, F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16, host,
+from gpu_helpers import (BF16_TOL, F32_TOL, assert_exact, assert_rows_close, bf16_dev, f32_of_bf16, guarded, host,
                          max_ulp_diff, requires_gpu, to_dev)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -36,8 +38,12 @@ def _weights(seed, seg_n, K):
 
 def _run(fn, x_dev, packed, wms, seg_n, y_dtype, a=None):
     f = getattr(_bl(), fn)
-    return f(x_dev, to_dev(packed), to_dev(wms), seg_n=list(seg_n) if len(seg_n) > 1 else None,
-             y_dtype=y_dtype, a=a)
+    M, N = x_dev.shape[0], packed.shape[0] * 4
+    out = guarded((M, N), y_dtype)
+    f(x_dev, packed if isinstance(packed, torch.Tensor) else to_dev(packed), wms if isinstance(wms, torch.Tensor)
+      else to_dev(wms), seg_n=list(seg_n) if len(seg_n) > 1 else None, y_dtype=y_dtype, a=a, y=out.t)
+    out.check(f"{fn} y {y_dtype}")
+    return out.t
 
 
 def _check(fn, M, K, seg_n, x_kind="bf16", seed=0, check_all_dtypes=True):
@@ -242,25 +248,71 @@ def test_config3_batched_decode(M):
         assert max_ulp_diff(yg[rows], y) == 0
 
 
-def test_config4_prefill_sampled_rows():
-    """M=2048 prefill: fused gate|up (K=2560 -> 2x6912) and down (6912 -> 2560)."""
+@pytest.mark.timeout(600)
+def test_config4_prefill_all_rows():
+    """M=2048 prefill: fused gate|up (K=2560 -> 2x6912) and down (6912 -> 2560),
+    every row and column: the int32 accumulators bit-exact against the exact
+    integer product, the fp32 outputs bit-identical to the oracle's rescale."""
     M = 2048
-    rows = [0, 1, 127, 128, 1000, 2047]
     pg, wg, cg = oracle.ternarize_pack(synth.layer_weight(0, "gate"))
     pu, wu, cu = oracle.ternarize_pack(synth.layer_weight(0, "up"))
-    bits = synth.act_normal_bf16(0, M, 2560)
     wms = np.array([wg, wu], np.float32)
-    yg = host(_bl().gemm_w2a8(bf16_dev(bits), to_dev(np.concatenate([pg, pu])), to_dev(wms),
-                              seg_n=[6912, 6912]))
-    _, _, _, y = oracle.bitlinear(f32_of_bf16(bits[rows]), np.concatenate([cg, cu]), [6912, 6912], wms)
-    assert_rows_close(yg[rows], y, F32_TOL)
-    assert max_ulp_diff(yg[rows], y) == 0
+    cgu = np.concatenate([cg, cu])
+    pgu = to_dev(np.concatenate([pg, pu]))
+    bits = synth.act_normal_bf16(0, M, 2560)
+    q, a, A, y = oracle.bitlinear_f64gemm(f32_of_bf16(bits), cgu, [6912, 6912], wms)
+    Ag = _run("gemm_w2a8", bf16_dev(bits), pgu, to_dev(wms), (6912, 6912), torch.int32)
+    assert_exact(host(Ag), A, "gate|up accumulators")
+    yg = host(_run("gemm_w2a8", bf16_dev(bits), pgu, to_dev(wms), (6912, 6912), torch.float32))
+    assert_exact(yg.view(np.uint32), y.view(np.uint32), "gate|up fp32 bits")
+    del A, Ag, yg, y
     pd, wd, cd = oracle.ternarize_pack(synth.layer_weight(0, "down"))
     bits2 = synth.act_normal_bf16(1, M, 6912)
-    yd = host(_bl().gemm_w2a8(bf16_dev(bits2), to_dev(pd), to_dev(np.array([wd]))))
-    _, _, _, y2 = oracle.bitlinear(f32_of_bf16(bits2[rows]), cd, None, wd)
-    assert_rows_close(yd[rows], y2, F32_TOL)
-    assert max_ulp_diff(yd[rows], y2) == 0
+    _, _, A2, y2 = oracle.bitlinear_f64gemm(f32_of_bf16(bits2), cd, None, np.array([wd], np.float32))
+    Ad = _run("gemm_w2a8", bf16_dev(bits2), pd, np.array([wd], np.float32), (2560,), torch.int32)
+    assert_exact(host(Ad), A2, "down accumulators")
+    yd = host(_run("gemm_w2a8", bf16_dev(bits2), pd, np.array([wd], np.float32), (2560,), torch.float32))
+    assert_exact(yd.view(np.uint32), y2.view(np.uint32), "down fp32 bits")
+
+
+# ----------------------------------------------------------------------------- degenerate rows and ties
+def _zero_and_tie_rows(M, K):
+    """Rows of x: an all-zero row, a row whose codes hit the half-way ties
+    (max 127 so a = 1: +-63.5, 0.5, 1.5, 2.5, -2.5), a tiny row (max below the
+    1e-5 floor) and N(0,1) rows."""
+    x = synth.act_normal_f32(123 + K, M, K)
+    x[0] = 0.0
+    ties = np.array([127.0, 63.5, -63.5, 0.5, -0.5, 1.5, 2.5, -2.5, 3.5, -126.5], np.float32)
+    x[1] = 0.0
+    x[1, :min(K, ties.size)] = ties[:min(K, ties.size)]
+    x[2] = 0.0
+    x[2, ::7] = np.float32(3e-6)
+    x[M - 1] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("fn,M,K,seg_n,kind", [("gemv_w2a8", 4, 2560, (2560, 640, 640), "bf16"),
+                                               ("gemv_w2a8", 3, 2560, (64,), "f32"),
+                                               ("gemv_w2a8", 16, 2560, (128, 32), "bf16"),
+                                               ("gemm_w2a8", 130, 2560, (256, 64), "bf16"),
+                                               ("gemm_w2a8", 300, 6912, (128,), "f32")])
+def test_zero_rows_and_ties(fn, M, K, seg_n, kind):
+    """Zero rows, exact .5 ties and sub-floor rows through the quantizing
+    prologues (the decode kernel's fused quantizer, the row kernel before the
+    prefill GEMM): codes, accumulators and outputs exact; zero rows give +0."""
+    packed, wms, codes = _weights(900 + M, seg_n, K)
+    x = _zero_and_tie_rows(M, K)
+    if kind == "bf16":
+        bits = synth.bf16_bits(x)
+        x_host, x_dev = f32_of_bf16(bits), bf16_dev(bits)
+    else:
+        x_host, x_dev = x, to_dev(x)
+    q, a, A, y = oracle.bitlinear(x_host, codes, seg_n, wms)
+    assert (q[0] == 0).all() and (q[M - 1] == 0).all() and (A[0] == 0).all()
+    Ag = _run(fn, x_dev, packed, wms, seg_n, torch.int32)
+    assert_exact(host(Ag), A, "accumulators")
+    yg = host(_run(fn, x_dev, packed, wms, seg_n, torch.float32))
+    assert_exact(yg.view(np.uint32), y.view(np.uint32), "fp32 bits (zero rows +0)")
 
 
 # ----------------------------------------------------------------------------- batched decode

@@ -718,3 +718,26 @@ def test_contract_f64_equals_the_integer_loop():
     r2 = oracle.bitlinear_f64gemm(x, codes, None, wm)
     for u, w in zip(r1, r2):
         assert np.array_equal(u, w)
+
+
+def test_chain_and_layer_f64gemm_equal_the_c_composition():
+    """The fast compositions (contractions by the exact fp64 product) give the
+    C chain's and layer's bits at every stage."""
+    Wg, Wu, Wd = synth.master_weight(11, 48, 32), synth.master_weight(12, 48, 32), synth.master_weight(13, 32, 48)
+    _, wg, cg = oracle.ternarize_pack(Wg)
+    _, wu, cu = oracle.ternarize_pack(Wu)
+    _, wd, cd = oracle.ternarize_pack(Wd)
+    h = synth.act_normal_f32(14, 5, 32)
+    g1 = np.linspace(0.5, 1.5, 32).astype(np.float32)
+    a = oracle.ffn_chain(h, np.concatenate([cg, cu]), np.array([wg, wu]), cd, wd, g_subln=g1)
+    b = oracle.ffn_chain_f64gemm(h, np.concatenate([cg, cu]), np.array([wg, wu]), cd, wd, g_subln=g1)
+    for key in ("q1", "a1", "p", "q2", "a2", "y"):
+        assert np.array_equal(a[key], b[key]), key
+    codes, wms = {}, {}
+    for j, (p, n, k) in enumerate([("q", 32, 32), ("k", 8, 32), ("v", 8, 32), ("o", 32, 32), ("gate", 48, 32),
+                                   ("up", 48, 32), ("down", 32, 48)]):
+        _, wms[p], codes[p] = oracle.ternarize_pack(synth.master_weight(20 + j, n, k))
+    x = synth.act_normal_f32(15, 3, 32)
+    la, lb = oracle.layer(x, codes, wms), oracle.layer_f64gemm(x, codes, wms)
+    for key in la:
+        assert np.array_equal(la[key], lb[key]), key
