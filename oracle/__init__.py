@@ -277,6 +277,33 @@ def ffn_chain(h, codes_gu, w_mean_gu, codes_down, w_mean_down, g_subln=None, g_f
     return out
 
 
+def ffn_chain_f64gemm(h, codes_gu, w_mean_gu, codes_down, w_mean_down, g_subln=None, g_ffn=None, eps=1e-5):
+    """``ffn_chain`` composed from the C stage functions with the two
+    contractions taken by ``contract_f64`` (same stages, same order, the
+    exact integer products): dict(q1, a1, p, q2, a2, y)."""
+    h = _c(h, np.float32)
+    I = np.asarray(codes_gu).shape[0] // 2
+    wgu = _c(np.asarray(w_mean_gu).reshape(2), np.float32)
+    q1, a1, _, ygu = bitlinear_f64gemm(rmsnorm(h, g_subln, eps), codes_gu, [I, I], wgu)
+    p = relu2_mul(np.ascontiguousarray(ygu[:, :I]), np.ascontiguousarray(ygu[:, I:]))
+    q2, a2, _, y = bitlinear_f64gemm(rmsnorm(p, g_ffn, eps), codes_down, None, w_mean_down)
+    return dict(q1=q1, a1=a1, p=p, q2=q2, a2=a2, y=y)
+
+
+def layer_f64gemm(x, codes, w_means, eps=1e-5):
+    """``layer`` with every contraction taken by ``contract_f64``."""
+    qkv_codes = np.concatenate([codes["q"], codes["k"], codes["v"]], axis=0)
+    segs = [codes["q"].shape[0], codes["k"].shape[0], codes["v"].shape[0]]
+    wm = np.array([w_means["q"], w_means["k"], w_means["v"]], np.float32)
+    q0, a0, _, y_qkv = bitlinear_f64gemm(x, qkv_codes, segs, wm)
+    y_q = np.ascontiguousarray(y_qkv[:, :segs[0]])
+    q_o, a_o, _, y_o = bitlinear_f64gemm(y_q, codes["o"], None, w_means["o"])
+    gu = np.concatenate([codes["gate"], codes["up"]], axis=0)
+    ch = ffn_chain_f64gemm(y_o, gu, np.array([w_means["gate"], w_means["up"]], np.float32),
+                           codes["down"], w_means["down"], eps=eps)
+    return dict(q_in=q0, a_in=a0, y_qkv=y_qkv, q_o=q_o, a_o=a_o, y_o=y_o, **ch)
+
+
 def layer(x, codes, w_means, eps=1e-5):
     """One decoder layer's linear path (attention excluded), fp32 x [M,2560].
 
