@@ -77,6 +77,9 @@ _SIGS = {
     "bl_ffn_chain_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_ffn_chain": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _I, _P, _S,
                           ctypes.POINTER(FfnDebug), _P]),
+    "bl_ffn_chain_noalloc_max_bytes": (_S, []),
+    "bl_ffn_chain_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _I,
+                                  ctypes.POINTER(FfnDebug), _P]),
     "bl_rope_table": (_I, [_I, _I, ctypes.c_double, _P, _P]),
     "bl_attn_decode_workspace_bytes": (_S, [_I, _I]),
     "bl_attn_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _S, _P]),
@@ -372,6 +375,27 @@ def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g
                             _ptr(y), _dt(y), _ptr(ws), ws.numel(),
                             ctypes.byref(dbg) if dbg is not None else None, _stream(dev)))
     return (y, stages) if debug else y
+
+
+def ffn_chain_noalloc(h, packed_gu, w_mean_gu, packed_down, w_mean_down, y, g_subln=None, g_ffn=None, eps=1e-5):
+    """ffn_chain through the allocation-free entry point: the library's fixed
+    per-device scratch, no workspace; y [M,H] fp32/bf16 is the caller's.
+    Calls that overlap on one device race (they share the scratch)."""
+    dev = _dev(h, packed_gu, packed_down, y)
+    M, H = h.shape
+    I = packed_gu.shape[0] * 2
+    if h.stride(1) != 1 or h.stride(0) != H:
+        raise ValueError("h must be contiguous")
+    _check_weight(packed_gu, w_mean_gu, I // 2, H, 2, "packed_gu")
+    _check_weight(packed_down, w_mean_down, H // 4, I, 1, "packed_down")
+    for g, n, name in ((g_subln, H, "g_subln"), (g_ffn, I, "g_ffn")):
+        if g is not None:
+            _need(g, (n,), (torch.float32,), name)
+    _need(y, (M, H), (torch.float32, torch.bfloat16), "y")
+    _check(raw.bl_ffn_chain_noalloc(_ptr(h), _dt(h), M, H, I, _ptr(g_subln), _ptr(g_ffn), float(eps),
+                                    _ptr(packed_gu), _ptr(w_mean_gu), _ptr(packed_down), _ptr(w_mean_down),
+                                    _ptr(y), _dt(y), None, _stream(dev)))
+    return y
 
 
 def rope_table(max_pos: int, head_dim: int, base: float, device=None):

@@ -15,6 +15,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "bl_attn.h"
 #include "bl_common.h"
 #include "bl_ste.h"
@@ -513,6 +515,71 @@ int bl_subln_gemv_w2a8(const void *h, int h_dtype, int M, int K, const float *ga
         return check_hip(bl::launch_gemm(k, qsum, s), fn);
     }
     return check_hip(bl::launch_generic(k, s), fn);
+}
+
+} // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free variant of bl_ffn_chain: its scratch is this
+// file-scope device array (one copy per device, held until the process
+// ends).  Host code never passes the array's name to a kernel: it passes the
+// device address hipGetSymbolAddress returns for the current device, taken
+// once per device and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+
+} // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (BL_OK), looked up on the
+// device's first call.
+int scratch_address(const char *fn, void **out) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return check_hip(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(BL_ERR_HIP, "%s: device %d beyond the library's %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)); e != hipSuccess) {
+            (void)hipGetLastError();
+            return check_hip(e, fn);
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BL_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t bl_ffn_chain_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int bl_ffn_chain_noalloc(const void *h, int h_dtype, int M, int H, int I, const float *g_subln, const float *g_ffn,
+                         float eps, const uint8_t *packed_gu, const float *w_mean_gu, const uint8_t *packed_down,
+                         const float *w_mean_down, void *y, int y_dtype, const bl_ffn_debug *dbg, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_ffn_chain_noalloc";
+    if (M < 1 || H < 4 || I < 4 || H % 4 != 0 || I % 4 != 0)
+        return fail(BL_ERR_SHAPE, "%s: M=%d H=%d I=%d (H, I must be positive multiples of 4)", fn, M, H, I);
+    const size_t need = bl_ffn_chain_workspace_bytes(M, H, I);
+    if (need > kNoAllocScratchBytes)
+        return fail(BL_ERR_WORKSPACE, "%s: M=%d H=%d I=%d needs %zu bytes of scratch, beyond the fixed %zu", fn, M, H,
+                    I, need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (int st = scratch_address(fn, &ws)) return st;
+    return bl_ffn_chain(h, h_dtype, M, H, I, g_subln, g_ffn, eps, packed_gu, w_mean_gu, packed_down, w_mean_down, y,
+                        y_dtype, ws, kNoAllocScratchBytes, dbg, stream);
 }
 
 size_t bl_ffn_chain_workspace_bytes(int M, int H, int I) {

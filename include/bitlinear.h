@@ -259,6 +259,26 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I,
                  const bl_ffn_debug *dbg, bl_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * bl_ffn_chain_noalloc -- bl_ffn_chain for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments and results
+ * as bl_ffn_chain without ws / ws_bytes: its scratch is a fixed device array
+ * inside the library of bl_ffn_chain_noalloc_max_bytes() bytes (32 MiB), one
+ * per device, held until the process ends.  The call allocates nothing.
+ * Sizes whose scratch (bl_ffn_chain_workspace_bytes(M, H, I)) exceeds it are
+ * rejected with BL_ERR_WORKSPACE before anything is enqueued (at the
+ * BitNet-2B4T shape, H 2560 / I 6912, up to 903 rows).  All calls on one
+ * device share that array: calls that overlap in time on one device (other
+ * streams, other host threads) race and must be ordered by the caller.
+ * ------------------------------------------------------------------------ */
+size_t bl_ffn_chain_noalloc_max_bytes(void);
+int bl_ffn_chain_noalloc(const void *h, int h_dtype, int M, int H, int I,
+                         const float *g_subln, const float *g_ffn, float eps,
+                         const uint8_t *packed_gu, const float *w_mean_gu,
+                         const uint8_t *packed_down, const float *w_mean_down,
+                         void *y, int y_dtype, const bl_ffn_debug *dbg, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
  * bl_rope_table / bl_attn_decode -- the attention side of a decoder layer
  * for one new token (decode).  "BitNet" model documentation, "模型详情"
  * (rotary position embeddings) and "BitNetConfig" (20 attention heads, 5
