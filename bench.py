@@ -346,6 +346,55 @@ def ste_timing(torch, dev, timer, H, I, M=2048):
     return out
 
 
+def unpacked_timing(torch, bl, stack, synth, timer, dev, layers, probs1, H, I):
+    """The offline-unpacked baseline: the 30 layers' weights unpacked to bf16
+    codes (about 4.2 GB), decode M=1 over each layer's 7 projections (the
+    headline's inputs, one launch per projection, graph replay), and the
+    config-4 prefill (gate|up then down at M=2048, quantization included)."""
+    import numpy as np
+    out = {}
+    unp = []
+    for lw in layers:
+        d = {}
+        for name, N, K in synth.PROJECTIONS:
+            packed, _ = stack._dest(lw, name)
+            d[name] = bl.unpack_bf16(packed)        # one tensor each
+        unp.append(d)
+    torch.cuda.synchronize()
+    ys = [[torch.empty((1, N), dtype=torch.float32, device=dev) for _, N, _ in synth.PROJECTIONS] for _ in layers]
+
+    def one_pass():
+        for l, pl in enumerate(probs1):
+            for j, (name, N, K) in enumerate(synth.PROJECTIONS):
+                bl.gemm_unpacked(pl[j]["x"], unp[l][name], pl[j]["w_mean"], y=ys[l][j])
+
+    one_pass()
+    ok = all(torch.equal(ys[l][j], bl.gemv_w2a8(probs1[l][j]["x"], probs1[l][j]["packed"], probs1[l][j]["w_mean"]))
+             for l in (0, len(layers) - 1) for j in range(7))
+    if not ok:
+        raise RuntimeError("the unpacked path differs from the packed one")
+    g = capture(torch, one_pass)
+    t = timer.run(g.replay, 5, 1) / len(layers)
+    wbytes = sum(2 * N * K for _, N, K in synth.PROJECTIONS)
+    out["unpacked_decode_m1_us_per_layer"] = round(t * 1e3, 2)
+    out["unpacked_decode_m1_weight_gbs"] = round(wbytes / (t * 1e-3) / 1e9, 1)
+    del g
+    M = 2048
+    lw = layers[0]
+    gu = torch.cat([unp[0]["gate"], unp[0]["up"]])
+    dn = unp[0]["down"]
+    xg = torch.from_numpy(synth.act_normal_bf16(0, M, H).view(np.int16)).to(dev).view(torch.bfloat16)
+    xd = torch.from_numpy(synth.act_normal_bf16(1, M, I).view(np.int16)).to(dev).view(torch.bfloat16)
+    yg = torch.empty((M, 2 * I), dtype=torch.float32, device=dev)
+    yd = torch.empty((M, H), dtype=torch.float32, device=dev)
+    f = lambda: (bl.gemm_unpacked(xg, gu, lw.w_gu, seg_n=[I, I], y=yg), bl.gemm_unpacked(xd, dn, lw.w_down, y=yd))
+    t = timer.run(f, 10, 2)
+    out["unpacked_prefill_m2048_ffn_tops"] = round(2 * M * 3 * I * H / (t * 1e-3) / 1e12, 1)
+    out["unpacked_prefill_m2048_ffn_us"] = round(t * 1e3, 1)
+    del unp, gu
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +411,12 @@ def main():
                     help="only the prefill attention over a 4096-token prompt (for profiler runs)")
     ap.add_argument("--ste-only", action="store_true",
                     help="only the straight-through backward at M=2048 (for profiler runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the config-4 prefill GEMMs (gate|up, then down, int8 codes given) (for profiler runs)")
+    ap.add_argument("--chain-only", action="store_true",
+                    help="only the persistent 30-layer decode step (for profiler runs)")
+    ap.add_argument("--mt-only", type=int, default=0, metavar="M",
+                    help="only the batched decode at M rows, 7 projections per launch over 30 layers (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
@@ -375,7 +430,7 @@ def main():
     # the oracle's CPU baseline first, before anything touches the GPU (its
     # core is pinned and nothing else runs meanwhile)
     run_cpu = not (args.no_cpu or args.copy_probe or args.kernel_only or args.attn_only or args.ste_only
-                   or args.attn_prefill_only)
+                   or args.attn_prefill_only or args.prefill_only or args.mt_only or args.chain_only)
     cpu = cpu_baseline() if run_cpu else None
     if cpu is not None:
         log(f"cpu baseline (oracle, 1 core): {cpu['value']} GB/s decode; {cpu['per_config']}")
@@ -410,6 +465,19 @@ def main():
         t, tf = attn_prefill_timing(torch, bl, stack, timer, dev, H, KV)
         print(json.dumps({"attn_prefill_m4096_us": round(t * 1e3, 1), "attn_prefill_m4096_tflops": tf}), flush=True)
         return
+    if args.prefill_only:
+        lw = stack.build_layers(1, dev)[0]
+        M = 2048
+        qg, ag = bl.quant_act(torch.from_numpy(synth.act_normal_bf16(0, M, H).view(np.int16)).to(dev).view(torch.bfloat16))
+        qd, ad = bl.quant_act(torch.from_numpy(synth.act_normal_bf16(1, M, I).view(np.int16)).to(dev).view(torch.bfloat16))
+        yg = torch.empty((M, 2 * I), dtype=torch.float32, device=dev)
+        yd = torch.empty((M, H), dtype=torch.float32, device=dev)
+        f = lambda: (bl.gemm_w2a8(qg, lw.packed_gu, lw.w_gu, seg_n=[I, I], a=ag, y=yg),
+                     bl.gemm_w2a8(qd, lw.packed_down, lw.w_down, a=ad, y=yd))
+        t = timer.run(f, max(1, args.steps), 3)
+        print(json.dumps({"prefill_m2048_gateup_then_down_us": round(t * 1e3, 1),
+                          "tops": round((2 * M * 2 * I * H + 2 * M * H * I) / (t * 1e-3) / 1e12, 1)}), flush=True)
+        return
     t_build = time.perf_counter()
     layers = stack.build_layers(args.layers, dev, workers=16)
     log(f"built {args.layers} layers in {time.perf_counter() - t_build:.1f} s")
@@ -437,6 +505,23 @@ def main():
     def step_bytes7(M):
         return sum(N * K // 4 + M * K * 2 + M * N * 4 for _, N, K in synth.PROJECTIONS)
 
+    if args.chain_only:
+        x1 = torch.from_numpy(synth.act_outliers_bf16(0, 1, H).view(np.int16)).to(dev).view(torch.bfloat16)
+        yp = torch.empty((1, H), dtype=torch.float32, device=dev)
+        g = capture(torch, lambda: stack.stack_decode(x1, layers, out=yp))
+        t = timer.run(g.replay, max(1, args.steps), 2)
+        by = layer_bytes(1, 2, H, I, KV) + (len(layers) - 1) * layer_bytes(1, 4, H, I, KV)
+        print(json.dumps({"persistent_decode_us_per_layer": round(t * 1e3 / len(layers), 2),
+                          "persistent_decode_gbs": round(by / (t * 1e-3) / 1e9, 1)}), flush=True)
+        return
+    if args.mt_only:
+        M = args.mt_only
+        pm = seven_problems(M, layers, "heavy")
+        g = capture(torch, lambda: [bl.gemv_w2a8_batched(pl) for pl in pm])
+        t = timer.run(g.replay, max(1, args.steps // len(layers)), 1) / len(layers)
+        print(json.dumps({f"decode_m{M}_us_per_layer": round(t * 1e3, 2),
+                          f"decode_m{M}_gbs": round(step_bytes7(M) / (t * 1e-3) / 1e9, 1)}), flush=True)
+        return
     probs1 = seven_problems(1, layers, "outliers")
     # One step = one layer's 7 projections in one launch; step i uses layer
     # i mod 30, so consecutive steps read different weights.  The timed region
@@ -497,6 +582,26 @@ def main():
     extra["chained_decode_m1_eager_us_per_layer"] = round(eager_ms * 1e3 / len(layers), 2)
     log(f"chained decode M=1: {t * 1e3 / len(layers):.2f} us/layer, {extra['chained_decode_m1_gbs']} GB/s")
     del graph
+    # the same decode step as one persistent launch (bl_stack_decode): every
+    # replay checked against the eager launch chain's output
+    yp = torch.empty((1, H), dtype=torch.float32, device=dev)
+    pers = lambda: stack.stack_decode(x1, layers, out=yp)
+    pers()
+    torch.cuda.synchronize()
+    if not torch.equal(yp, ref):
+        log("persistent decode differs from the launch chain (RMSNorm fp64 sum order)")
+    gp = capture(torch, pers)
+    for _ in range(3):
+        gp.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(yp, ref):
+            raise RuntimeError("persistent decode graph replay differs from the eager decode pass")
+    t = timer.run(gp.replay, 20, 2)
+    extra["chained_decode_m1_persistent_gbs"] = round(by / (t * 1e-3) / 1e9, 1)
+    extra["chained_decode_m1_persistent_us_per_layer"] = round(t * 1e3 / len(layers), 2)
+    log(f"persistent chained decode M=1: {t * 1e3 / len(layers):.2f} us/layer, "
+        f"{extra['chained_decode_m1_persistent_gbs']} GB/s")
+    del gp
 
     if not args.no_extras:
         # batched decode: M=16 and M=64, 7 projections per launch
@@ -591,6 +696,14 @@ def main():
         extra.update(ste_timing(torch, dev, timer, H, I))
         log(f"straight-through backward M=2048: gate|up {extra['ste_backward_m2048_gateup_tflops']} TFLOPS, "
             f"down {extra['ste_backward_m2048_down_tflops']} TFLOPS (bf16 products)")
+        # the offline-unpacked path (weights expanded once to bf16 codes, dense
+        # bf16 products; the same output bits): decode M=1 over the 7
+        # projections of each of the 30 layers (one launch per projection),
+        # and the config-4 prefill
+        extra.update(unpacked_timing(torch, bl, stack, synth, timer, dev, layers, probs1, H, I))
+        log(f"offline-unpacked: decode M=1 {extra['unpacked_decode_m1_us_per_layer']} us/layer "
+            f"({extra['unpacked_decode_m1_weight_gbs']} GB/s of bf16 codes), prefill M=2048 "
+            f"{extra['unpacked_prefill_m2048_ffn_tops']} TOPS")
         # offline ternarization (absmean + pack) of one 6912 x 2560 master
         W = torch.from_numpy(synth.layer_weight(0, "gate")).to(dev)
         pk = torch.empty((I // 4, H), dtype=torch.uint8, device=dev)

@@ -42,6 +42,11 @@ class FfnDebug(ctypes.Structure):
     _fields_ = [("q1", _P), ("a1", _P), ("p", _P), ("q2", _P), ("a2", _P)]
 
 
+class Layer(ctypes.Structure):
+    _fields_ = [("packed_qkv", _P), ("w_qkv", _P), ("packed_o", _P), ("w_o", _P), ("packed_gu", _P), ("w_gu", _P),
+                ("packed_down", _P), ("w_down", _P), ("g_subln", _P), ("g_ffn", _P)]
+
+
 class GemvProblem(ctypes.Structure):
     _fields_ = [("x", _P), ("x_dtype", _I), ("ldx", _I), ("a", _P), ("M", _I), ("K", _I),
                 ("packed", _P), ("N", _I), ("n_seg", _I), ("seg_n", ctypes.POINTER(_I)), ("w_mean", _P),
@@ -77,6 +82,11 @@ _SIGS = {
     "bl_ffn_chain_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_ffn_chain": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _I, _P, _S,
                           ctypes.POINTER(FfnDebug), _P]),
+    "bl_unpack_bf16": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "bl_stack_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "bl_stack_decode": (_I, [_P, _I, _I, ctypes.POINTER(Layer), _I, _I, _I, _F, _P, _P, _P, _S, _P]),
+    "bl_gemm_unpacked_workspace_bytes": (_S, [_I, _I, _I]),
+    "bl_gemm_unpacked": (_I, [_P, _I, _I, _P, _I, _I, _P, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_ffn_chain_noalloc_max_bytes": (_S, []),
     "bl_ffn_chain_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _I,
                                   ctypes.POINTER(FfnDebug), _P]),
@@ -375,6 +385,92 @@ def ffn_chain(h, packed_gu, w_mean_gu, packed_down, w_mean_down, g_subln=None, g
                             _ptr(y), _dt(y), _ptr(ws), ws.numel(),
                             ctypes.byref(dbg) if dbg is not None else None, _stream(dev)))
     return (y, stages) if debug else y
+
+
+STACK_DECODE_MAX_LAYERS = 32
+
+
+def stack_decode(x, layers, H, KV, I, eps=1e-5, y=None, stages=None):
+    """The linear path of len(layers) <= 32 layers at one token in one
+    persistent launch (see bl_stack_decode).  x [H] or [1,H] fp32/bf16;
+    layers: objects with packed_qkv, w_qkv, packed_o, w_o, packed_gu, w_gu,
+    packed_down, w_down (and optional g_subln, g_ffn) device tensors.
+    Returns y [1,H] fp32; stages, when given, is [L, (H+2KV)+H+I+H] fp32 and
+    receives every stage's output."""
+    dev = _dev(x)
+    L = len(layers)
+    if not 1 <= L <= STACK_DECODE_MAX_LAYERS:
+        raise ValueError(f"1..{STACK_DECODE_MAX_LAYERS} layers per call")
+    if x.numel() != H or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous tensor of {H} elements")
+    arr = (Layer * L)()
+    for i, lw in enumerate(layers):
+        _need(lw.packed_qkv, ((H + 2 * KV) // 4, H), (torch.uint8,), "packed_qkv")
+        _need(lw.packed_o, (H // 4, H), (torch.uint8,), "packed_o")
+        _need(lw.packed_gu, (2 * I // 4, H), (torch.uint8,), "packed_gu")
+        _need(lw.packed_down, (H // 4, I), (torch.uint8,), "packed_down")
+        for t, n, name in ((lw.w_qkv, 3, "w_qkv"), (lw.w_o, 1, "w_o"), (lw.w_gu, 2, "w_gu"), (lw.w_down, 1, "w_down")):
+            if t.dtype != torch.float32 or t.numel() < n:
+                raise ValueError(f"{name} must be float32 with at least {n} elements")
+        gs, gf = getattr(lw, "g_subln", None), getattr(lw, "g_ffn", None)
+        if gs is not None:
+            _need(gs, (H,), (torch.float32,), "g_subln")
+        if gf is not None:
+            _need(gf, (I,), (torch.float32,), "g_ffn")
+        arr[i] = Layer(lw.packed_qkv.data_ptr(), lw.w_qkv.data_ptr(), lw.packed_o.data_ptr(), lw.w_o.data_ptr(),
+                       lw.packed_gu.data_ptr(), lw.w_gu.data_ptr(), lw.packed_down.data_ptr(), lw.w_down.data_ptr(),
+                       None if gs is None else gs.data_ptr(), None if gf is None else gf.data_ptr())
+    if y is None:
+        y = torch.empty((1, H), dtype=torch.float32, device=dev)
+    _need(y, tuple(y.shape), (torch.float32,), "y")
+    if y.numel() != H:
+        raise ValueError(f"y must hold {H} elements")
+    ws = None
+    if stages is not None:
+        _need(stages, (L, (H + 2 * KV) + H + I + H), (torch.float32,), "stages")
+    else:
+        ws = workspace(dev, raw.bl_stack_decode_workspace_bytes(L, H, KV, I))
+    _check(raw.bl_stack_decode(_ptr(x), _dt(x), L, arr, H, KV, I, float(eps), _ptr(y), _ptr(stages), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(dev)))
+    return y
+
+
+def unpack_bf16(packed, seg_n=None, w_codes=None):
+    """Offline unpack (see bl_unpack_bf16): packed uint8 [N/4,K] (segments
+    stacked, widths seg_n) -> bf16 codes [N,K] (-1, 0, +1) in output-column
+    order."""
+    dev = _dev(packed)
+    R, K = packed.shape
+    _need(packed, (R, K), (torch.uint8,), "packed")
+    n_seg, seg = _segs(seg_n, 4 * R)
+    if w_codes is None:
+        w_codes = torch.empty((4 * R, K), dtype=torch.bfloat16, device=dev)
+    _need(w_codes, (4 * R, K), (torch.bfloat16,), "w_codes")
+    _check(raw.bl_unpack_bf16(_ptr(packed), 4 * R, K, n_seg, seg, _ptr(w_codes), _stream(dev)))
+    return w_codes
+
+
+def gemm_unpacked(x, w_codes, w_mean, seg_n=None, y_dtype=torch.float32, a=None, y=None):
+    """BitLinear on offline-unpacked bf16 codes [N,K] (see bl_gemm_unpacked):
+    the same bits as gemm_w2a8 on the packed weight."""
+    dev = _dev(x, w_codes, w_mean)
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    N = w_codes.shape[0]
+    n_seg, seg = _segs(seg_n, N)
+    _need(w_codes, (N, K), (torch.bfloat16,), "w_codes")
+    if w_mean.dtype != torch.float32 or w_mean.numel() < n_seg:
+        raise ValueError(f"w_mean must be float32 with at least {n_seg} elements")
+    if a is not None and (a.dtype != torch.float32 or a.numel() < M):
+        raise ValueError("a must be float32 with at least M elements")
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=dev)
+    _need(y, (M, N), _OUT_DT, "y")
+    ws = workspace(dev, raw.bl_gemm_unpacked_workspace_bytes(M, N, K))
+    _check(raw.bl_gemm_unpacked(_ptr(x), _dt(x), x.stride(0), _ptr(a), M, K, _ptr(w_codes), N, n_seg, seg,
+                                _ptr(w_mean), _ptr(y), _dt(y), _ptr(ws), ws.numel(), _stream(dev)))
+    return y
 
 
 def ffn_chain_noalloc(h, packed_gu, w_mean_gu, packed_down, w_mean_down, y, g_subln=None, g_ffn=None, eps=1e-5):

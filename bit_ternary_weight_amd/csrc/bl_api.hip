@@ -316,7 +316,11 @@ int bl_device_errors(unsigned int *expired_waits, int reset) {
     g_err[0] = 0;
     if (!expired_waits) return fail(BL_ERR_NULL, "bl_device_errors: NULL pointer argument");
     if (hipError_t e = hipDeviceSynchronize(); e != hipSuccess) return check_hip(e, "bl_device_errors");
-    return check_hip(bl::gemv_wait_expired(expired_waits, reset != 0), "bl_device_errors");
+    unsigned int a = 0, b = 0;
+    if (int st = check_hip(bl::gemv_wait_expired(&a, reset != 0), "bl_device_errors")) return st;
+    if (int st = check_hip(bl::chain_wait_expired(&b, reset != 0), "bl_device_errors")) return st;
+    *expired_waits = a + b;
+    return BL_OK;
 }
 
 const char *bl_status_string(int status) {
@@ -767,6 +771,125 @@ int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int
     if (int st = check_ws(fn, ws, ws_bytes, bl_attn_prefill_workspace_bytes(M, n_heads, n_kv_heads))) return st;
     return check_hip(bl::launch_attn_prefill(q, k, v, ldx, M, n_heads, n_kv_heads, k_cache, v_cache, max_seq,
                                              rope_cos, rope_sin, out, ldo, ws, (hipStream_t)stream),
+                     fn);
+}
+
+size_t bl_stack_decode_workspace_bytes(int n_layers, int H, int KV, int I) {
+    if (n_layers < 1 || H < 1 || KV < 0 || I < 1) return 0;
+    return align256((size_t)n_layers * ((size_t)(H + 2 * KV) + H + I + H) * sizeof(float));
+}
+
+int bl_stack_decode(const void *x, int x_dtype, int n_layers, const bl_layer *layers, int H, int KV, int I, float eps,
+                    float *y, float *stages, void *ws, size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_stack_decode";
+    if (!x || !layers || !y) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (x_dtype != BL_F32 && x_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "%s: x dtype %d not allowed", fn, x_dtype);
+    if (n_layers < 1 || n_layers > bl::chain_max_layers())
+        return fail(BL_ERR_SHAPE, "%s: n_layers=%d (1..%d per call)", fn, n_layers, bl::chain_max_layers());
+    if (!(eps >= 0.0f)) return fail(BL_ERR_SHAPE, "%s: eps must be >= 0", fn);
+    const int G = bl::chain_workgroups();
+    if (G < 1) return fail(BL_ERR_SHAPE, "%s: the kernel does not fit one workgroup per compute unit here", fn);
+    if (!bl::chain_fits(H, KV, I, G))
+        return fail(BL_ERR_SHAPE, "%s: H=%d KV=%d I=%d outside the persistent kernel's capacity (H, I multiples of "
+                                  "256 up to 8192, KV of 16, the units per workgroup bounded)", fn, H, KV, I);
+    for (int l = 0; l < n_layers; ++l) {
+        const bl_layer &w = layers[l];
+        if (!w.packed_qkv || !w.w_qkv || !w.packed_o || !w.w_o || !w.packed_gu || !w.w_gu || !w.packed_down ||
+            !w.w_down)
+            return fail(BL_ERR_NULL, "%s: layer %d has a NULL weight pointer", fn, l);
+        if (!aligned(w.packed_qkv, 16) || !aligned(w.packed_o, 16) || !aligned(w.packed_gu, 16) ||
+            !aligned(w.packed_down, 16) || !aligned(w.w_qkv, 4) || !aligned(w.w_o, 4) || !aligned(w.w_gu, 4) ||
+            !aligned(w.w_down, 4) || (w.g_subln && !aligned(w.g_subln, 4)) || (w.g_ffn && !aligned(w.g_ffn, 4)))
+            return fail(BL_ERR_ALIGN, "%s: layer %d has a misaligned pointer", fn, l);
+    }
+    if (!aligned(x, x_dtype == BL_F32 ? 4 : 2) || !aligned(y, 4) || (stages && !aligned(stages, 4)))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    float *st = stages;
+    if (!st) {
+        if (int e = check_ws(fn, ws, ws_bytes, bl_stack_decode_workspace_bytes(n_layers, H, KV, I))) return e;
+        st = (float *)ws;
+    }
+    bl::ChainLayerPtrs lp[32];
+    for (int l = 0; l < n_layers; ++l) {
+        const bl_layer &w = layers[l];
+        lp[l] = bl::ChainLayerPtrs{w.packed_qkv, w.w_qkv, w.packed_o, w.w_o, w.packed_gu, w.w_gu, w.packed_down,
+                                   w.w_down, w.g_subln, w.g_ffn};
+    }
+    bl::ChainParams p{};
+    p.x = x; p.x_dt = x_dtype; p.L = n_layers; p.H = H; p.KV = KV; p.I = I; p.eps = eps; p.stages = st; p.y = y;
+    p.G = G; p.layers = lp;
+    const int segs[3] = {H, KV, KV};
+    if (int e = make_segtab(H + 2 * KV, 3, segs, p.seg_qkv)) return e;
+    return check_hip(bl::launch_chain_decode(p, (hipStream_t)stream), fn);
+}
+
+int bl_unpack_bf16(const uint8_t *packed, int N, int K, int n_seg, const int *seg_n, void *w_codes,
+                   bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_unpack_bf16";
+    if (!packed || !w_codes) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (N < 4 || N % 4 != 0 || K < 1) return fail(BL_ERR_SHAPE, "%s: N=%d K=%d (N a positive multiple of 4)", fn, N, K);
+    if ((size_t)N * K >= ((size_t)1 << 40)) return fail(BL_ERR_SHAPE, "%s: N*K too large", fn);
+    bl::SegTab seg;
+    if (int st = make_segtab(N, n_seg, seg_n, seg)) return st;
+    if (!aligned(w_codes, 2)) return fail(BL_ERR_ALIGN, "%s: w_codes must be 2-byte aligned", fn);
+    return check_hip(bl::launch_unpack_bf16(packed, N, K, seg, w_codes, (hipStream_t)stream), fn);
+}
+
+size_t bl_gemm_unpacked_workspace_bytes(int M, int N, int K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    (void)N;
+    return quant_scratch(M, K) + align256(bl::unpacked_gemm_ws_bytes(M, K));
+}
+
+int bl_gemm_unpacked(const void *x, int x_dtype, int ldx, const float *a, int M, int K, const void *w_codes, int N,
+                     int n_seg, const int *seg_n, const float *w_mean, void *y, int y_dtype, void *ws,
+                     size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_gemm_unpacked";
+    if (!x || !w_codes || !w_mean || !y) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (x_dtype != BL_F32 && x_dtype != BL_BF16 && x_dtype != BL_I8)
+        return fail(BL_ERR_DTYPE, "%s: x dtype %d not allowed", fn, x_dtype);
+    if (y_dtype != BL_F32 && y_dtype != BL_BF16 && y_dtype != BL_I32)
+        return fail(BL_ERR_DTYPE, "%s: y dtype %d not allowed", fn, y_dtype);
+    if (x_dtype == BL_I8 && !a) return fail(BL_ERR_NULL, "%s: a is required with int8 codes", fn);
+    if (M < 1 || K < 1 || N < 4 || N % 4 != 0)
+        return fail(BL_ERR_SHAPE, "%s: M=%d K=%d N=%d (N a positive multiple of 4)", fn, M, K, N);
+    if (ldx == 0) ldx = K;
+    if (ldx < K) return fail(BL_ERR_SHAPE, "%s: ldx=%d < K=%d", fn, ldx, K);
+    if (x_dtype == BL_I8 && ldx != K) return fail(BL_ERR_SHAPE, "%s: int8 codes must be contiguous rows", fn);
+    const bool gemv = M <= 4 && bl::unpacked_gemv_fits(K);
+    const bool gemm = bl::unpacked_gemm_fits(M, N, K);
+    if (!gemv && !gemm && !bl::unpacked_gemv_fits(K))
+        return fail(BL_ERR_SHAPE, "%s: M=%d N=%d K=%d: needs K a multiple of 8 up to 8192, or K a multiple of 64 "
+                                  "and N of 128", fn, M, N, K);
+    bl::SegTab seg;
+    if (int st = make_segtab(N, n_seg, seg_n, seg)) return st;
+    if (!aligned(x, x_dtype == BL_F32 ? 4 : (x_dtype == BL_BF16 ? 2 : 4)) || !aligned(w_codes, 16) ||
+        !aligned(y, 16) || !aligned(w_mean, 4) || (a && !aligned(a, 4)))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (int st = check_ws(fn, ws, ws_bytes, bl_gemm_unpacked_workspace_bytes(M, N, K))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char *wsb = (char *)ws;
+    const int8_t *q = (const int8_t *)x;
+    const float *av = a;
+    if (x_dtype != BL_I8) {
+        int8_t *qw = (int8_t *)wsb;
+        float *aw = (float *)(wsb + align256((size_t)M * K));
+        if (int st = check_hip(bl::launch_quant_act(x, x_dtype, M, K, ldx, qw, aw, nullptr, s), fn)) return st;
+        q = qw;
+        av = aw;
+    }
+    bl::GemmEpi e{};
+    e.a = av;
+    e.w_mean = w_mean;
+    e.nseg = seg.n;
+    for (int i = 0; i < BL_MAX_SEGMENTS; ++i) e.cend[i] = 4 * seg.roff[i < seg.n ? i + 1 : seg.n];
+    e.y_dt = y_dtype;
+    if (gemv || !gemm) return check_hip(bl::launch_unpacked_gemv(q, av, M, K, w_codes, N, e, y, s), fn);
+    return check_hip(bl::launch_unpacked_gemm(q, av, M, K, (const __bf16 *)w_codes, N, e, y, wsb + quant_scratch(M, K),
+                                              s),
                      fn);
 }
 

@@ -328,4 +328,39 @@ hipError_t gemv_wait_expired(unsigned int *count, bool reset);
 // Any K (slow, simple): used when K is not a multiple of 16.
 hipError_t launch_generic(const Contract &c, hipStream_t s);
 
+// The decode step of a stack of linear layers at one token in one
+// persistent launch (k_chain.hip).
+struct ChainLayerPtrs {
+    const uint8_t *P_qkv;
+    const float *w_qkv;
+    const uint8_t *P_o;
+    const float *w_o;
+    const uint8_t *P_gu;
+    const float *w_gu;
+    const uint8_t *P_dn;
+    const float *w_dn;
+    const float *g_sub;
+    const float *g_ffn;
+};
+struct ChainParams {
+    const void *x;
+    int x_dt;
+    int L, H, KV, I;
+    float eps;
+    float *stages;   // [L][(H + 2KV) + H + I + H] fp32, the exchange buffers
+    float *y;        // [H]
+    int G;           // workgroups (chain_workgroups())
+    SegTab seg_qkv;
+    const ChainLayerPtrs *layers;   // host array of L
+};
+int chain_max_layers();
+bool chain_fits(int H, int KV, int I, int G);
+int chain_workgroups();
+hipError_t launch_chain_decode(const ChainParams &p, hipStream_t s);
+hipError_t chain_wait_expired(unsigned int *count, bool reset);
+
+// Offline-unpacked weights (k_unpacked.hip): the packed weight expanded to
+// bf16 codes W [N][K], and the decode-size product against it.
+hipError_t launch_unpack_bf16(const uint8_t *packed, int N, int K, const SegTab &seg, void *w, hipStream_t s);
+
 } // namespace bl

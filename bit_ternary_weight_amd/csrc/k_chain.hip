@@ -1,0 +1,573 @@
+// k_chain.hip -- the decode step of a whole stack of linear layers at one
+// token (M = 1) in one persistent launch.
+//
+// Per layer (the BitNet model documentation, "模型详情" / "BitNetConfig":
+// subln before the projections that follow attention and the FFN's ReLU^2;
+// the article "Transformers 实战 BitNet 1.58 位量化", "推理侧 BitLinear" for
+// each BitLinear), with attention left out as in the layer driver:
+//   x -> quantize -> q|k|v            (three segments, one weight)
+//     -> q quantize -> o
+//     -> subln RMSNorm -> quantize -> gate|up -> ReLU^2(gate)*up
+//     -> ffn_sub_norm RMSNorm -> quantize -> down -> next layer's x.
+// Every BitLinear computes the same bits as the separate launches: per-token
+// absmax codes, the integer contraction of the packed codes (kept as code+1,
+// the code sum subtracted once), y = float(A) * (w_mean / a).
+//
+// Why one launch: each of the four stages needs the whole output vector of
+// the previous one (a row maximum, a norm), so a layer is four dependent
+// steps.  As separate launches every step paid a launch and a cold ramp of
+// its weight stream.  Here the weights of a step do not wait for its input:
+//
+//   * one workgroup per compute unit (all resident; the host checks the
+//     occupancy before launching), each owning a fixed set of 4-row groups of
+//     every stage's weight;
+//   * 12 stream waves hold the weight units (4 packed rows x 256 bytes) of two
+//     layers in registers: after a stage is consumed, the same registers are
+//     reloaded with that stage of the layer two ahead, so the HBM stream never
+//     waits for the chain of dependencies.  They issue no other global memory
+//     operation, so the compiler's waits on them stay exact;
+//   * 4 quantizer waves poll the previous stage's output, normalize and
+//     quantize it into LDS, and after the stream waves' products store this
+//     workgroup's part of the stage's output.
+//
+// Cross-workgroup exchange without flags or fences: every stage output lives
+// in a buffer that a fill launch sets to an all-ones word (a NaN no stage
+// produces from finite input) right before the persistent launch.  Outputs
+// are written with agent-scope stores and read with agent-scope loads (the
+// coherent cache policy), and a consumer polls each word until it is no
+// longer the fill pattern.  Each word is written once, so per-location
+// coherence is all the exchange needs.  Polls are bounded: an expired poll is
+// counted (bl_device_errors) and the kernel runs to its end.
+//
+// Within a workgroup the two roles meet at two barriers per stage (codes in
+// LDS; partial sums in LDS), both LDS-only so no wave waits for weight loads
+// in flight.
+#include "bl_common.h"
+
+namespace bl {
+
+namespace {
+
+constexpr int kCS = 12;                 // stream waves
+constexpr int kCQ = 4;                  // quantizer / epilogue waves
+constexpr int kCQL = kCQ * 64;
+constexpr int kCThreads = (kCS + kCQ) * 64;
+constexpr int kCMaxK = 8192;            // largest K: codes in LDS, polled words per lane
+constexpr int kCPoll = kCMaxK / kCQL;   // 32 polled words per quantizer lane, at most
+constexpr int kCUnit = 256;             // k bytes of a unit
+// Weight units per stream wave and stage (q|k|v, o, gate|up, down): a
+// workgroup owns at most 12 * kU units of a stage.
+constexpr int kUq = 1, kUo = 1, kUg = 4, kUd = 3;
+constexpr int kUMax = 4;
+constexpr int kCMaxUnits = kCS * kUMax;
+constexpr unsigned kFill = 0xFFFFFFFFu;  // stage words not yet written
+constexpr int kPollMax = 1 << 17;       // polls per wait (each at least a memory round trip)
+
+__device__ unsigned int g_chain_expired = 0;
+
+struct ChainLayer {
+    const uint8_t *P_qkv;
+    const float *w_qkv;
+    const uint8_t *P_o;
+    const float *w_o;
+    const uint8_t *P_gu;
+    const float *w_gu;
+    const uint8_t *P_dn;
+    const float *w_dn;
+    const float *g_sub;
+    const float *g_ffn;
+};
+
+constexpr int kChainMaxLayers = 32;
+
+struct ChainArgs {
+    const void *x;
+    int x_dt;
+    int L, H, KV, I;
+    float eps;
+    float *stages;   // [L][Sw]: q|k|v, o, p, y
+    int Sw;
+    float *y;        // [H]
+    int G;           // workgroups
+    SegTab seg_qkv;
+    ChainLayer layers[kChainMaxLayers];
+};
+
+// The launch's single argument, read through the kernel-argument pointer so
+// that a run-time layer index is a scalar load, not a copy of the table.
+__device__ __forceinline__ const ChainArgs &args() {
+    return *(const ChainArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Stage geometry of this workgroup, the same for every layer: computed once.
+struct Stage {
+    const uint8_t *P;  // packed weight (pair: gate rows, then up rows)
+    int K;             // input width (bytes of a packed row)
+    int R;             // packed rows of one tensor
+    int nt;            // tensors (2: gate|up)
+    int g0, ng;        // this workgroup's 4-row groups [g0, g0 + ng)
+    int ku;            // units along K
+    int nunits;        // nt * ng * ku
+};
+
+// The geometry is recomputed at each use from the kernel arguments (scalar
+// loads and scalar arithmetic on uniform values) rather than kept: a table
+// of it would be placed in scratch memory.
+struct Geo {};
+
+__device__ __forceinline__ Geo make_geo(const ChainArgs &) { return Geo{}; }
+
+__device__ __forceinline__ Stage stage_of(const ChainArgs &A, const Geo &, int l, int s) {
+    const ChainLayer &w = A.layers[l];
+    Stage st;
+    if (s == 0) { st.P = w.P_qkv; st.K = A.H; st.R = (A.H + 2 * A.KV) / 4; st.nt = 1; }
+    else if (s == 1) { st.P = w.P_o; st.K = A.H; st.R = A.H / 4; st.nt = 1; }
+    else if (s == 2) { st.P = w.P_gu; st.K = A.H; st.R = A.I / 4; st.nt = 2; }
+    else { st.P = w.P_dn; st.K = A.I; st.R = A.H / 4; st.nt = 1; }
+    const int groups = st.R / 4;
+    const int b = blockIdx.x;
+    st.g0 = b * groups / A.G;
+    st.ng = (b + 1) * groups / A.G - st.g0;
+    st.ku = st.K / kCUnit;
+    st.nunits = st.nt * st.ng * st.ku;
+    return st;
+}
+
+// Global address of this lane's 16 bytes of unit mu (clamped to a valid unit;
+// a workgroup with no group of this stage reads its neighbour's first unit).
+// The lanes of a wave cover 4 packed rows x 256 bytes: lane (g, l) holds row
+// l >> 2, chunk (l & 3) + 4g, the operand layout of the MFMA consumption.
+__device__ __forceinline__ const uint8_t *unit_addr(const Stage &st, int mu, int lane) {
+    int t = 0, gr = 0, k = 0;
+    if (st.nunits > 0) {
+        const int m = mu < st.nunits ? mu : st.nunits - 1;
+        k = m % st.ku;
+        const int rest = m / st.ku;
+        gr = st.g0 + rest % st.ng;
+        t = rest / st.ng;
+    } else {
+        gr = st.g0 < st.R / 4 ? st.g0 : st.R / 4 - 1;
+    }
+    const int row = t * st.R + 4 * gr + ((lane & 15) >> 2);
+    const int ch = (lane & 3) + 4 * (lane >> 4);
+    return st.P + (size_t)row * st.K + (size_t)k * kCUnit + 16 * ch;
+}
+
+template <int U>
+__device__ __forceinline__ void issue(const Stage &st, int ws, int lane, v4i (&r)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        r[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(unit_addr(st, ws + kCS * u, lane)));
+}
+
+// Consumes this wave's units of a stage: per unit, each field through one
+// v_mfma_i32_16x16x64_i8 (weights first, the codes of the same chunks
+// second), the k-slice sums of each row gathered from the quad that holds
+// them; lane 16r writes the unit's 4 fields of unit row r to part[mu].
+template <int U>
+__device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const v4i (&r)[U], const int8_t *q_s,
+                                        int *part) {
+    const int ch = (lane & 3) + 4 * (lane >> 4);
+    const int s = lane & 3;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int mu = ws + kCS * u;
+        if (mu >= st.nunits) break;
+        const int k = mu % st.ku;
+        const v4i b = *reinterpret_cast<const v4i *>(q_s + k * kCUnit + 16 * ch);
+        v4i f[4];
+        expand(r[u], f);
+        int tot[4];
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi) {
+            const v4i d = mfma16(f[fi], b, v4i{0, 0, 0, 0});
+            int v = s == 0 ? d[0] : (s == 1 ? d[1] : (s == 2 ? d[2] : d[3]));
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            tot[fi] = shift_field(v, fi);
+        }
+        if ((lane & 15) == 0) {
+            const int row = lane >> 4;
+            *reinterpret_cast<int4 *>(part + (mu * 4 + row) * 4) = int4{tot[0], tot[1], tot[2], tot[3]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Quantizer-wave helpers.  Flags in LDS order the four quantizer waves among
+// themselves (the barriers would also stop the stream waves).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void q_publish(int *qflag, int qw, int step) {
+    asm volatile("" ::: "memory");
+    if ((threadIdx.x & 63) == 0) qflag[qw] = step;
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void q_wait(const int *qflag, int step) {
+    int lo = 0;
+    for (int it = 0; it < (1 << 22); ++it) {
+        asm volatile("" ::: "memory");
+        const v4i f = *reinterpret_cast<const v4i *>(qflag);
+        lo = min(min(__builtin_amdgcn_readfirstlane(f[0]), __builtin_amdgcn_readfirstlane(f[1])),
+                 min(__builtin_amdgcn_readfirstlane(f[2]), __builtin_amdgcn_readfirstlane(f[3])));
+        if (lo >= step) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    if (lo < step && (threadIdx.x & 63) == 0) atomicAdd(&g_chain_expired, 1u);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Polls the K words of `in` this lane covers (element ql + 256 j) until none
+// holds the fill pattern; returns them in v.  `live` turns false after an
+// expired poll, after which later polls take what they find.
+__device__ __forceinline__ void poll(const float *in, int K, int ql, float (&v)[kCPoll], bool &live) {
+    const unsigned *p = reinterpret_cast<const unsigned *>(in);
+    for (int it = 0;; ++it) {
+        bool missing = false;
+#pragma unroll
+        for (int j = 0; j < kCPoll; ++j) {
+            const int k = ql + kCQL * j;
+            if (j * kCQL >= K) break;
+            unsigned u = 0;
+            if (k < K) u = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            missing |= (k < K) && (u == kFill);
+            v[j] = __uint_as_float(u);
+        }
+        if (!missing) return;
+        if (!live || it >= kPollMax) {
+            if (live) atomicAdd(&g_chain_expired, 1u);
+            live = false;
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// The layer input x (the caller's fp32 or bf16 row, plain loads).
+__device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float (&v)[kCPoll]) {
+#pragma unroll
+    for (int j = 0; j < kCPoll; ++j) {
+        const int k = ql + kCQL * j;
+        if (j * kCQL >= A.H) break;
+        float t = 0.0f;
+        if (k < A.H) {
+            if (A.x_dt == BL_BF16) t = bf16_to_f32(static_cast<const uint16_t *>(A.x)[k]);
+            else t = static_cast<const float *>(A.x)[k];
+        }
+        v[j] = t;
+    }
+}
+
+struct QState {
+    float a;      // this stage's activation scale
+    int step;     // quantizer-wave flag steps published so far
+    bool live;    // polls still wait
+};
+
+// Normalizes (optionally) and quantizes the K values in v: codes to q_s, the
+// scale to st.a, this wave's code sum to qs_part[qw] (summed after the first
+// barrier).  Same arithmetic as the row kernel: fp64 sum of squares,
+// r = float(1 / sqrt(ss / K + eps)), (h * r) * g, a = 127 / max(amax, 1e-5),
+// q = clamp(rint(x * a)).
+__device__ __forceinline__ void quantize(float (&v)[kCPoll], int K, const float *gain, bool norm, float eps, int qw,
+                                         int ql, int8_t *q_s, double *part_d, float *part_f, int *qs_part,
+                                         int *qflag, QState &qs) {
+    if (norm) {
+        double ss = 0.0;
+#pragma unroll
+        for (int j = 0; j < kCPoll; ++j) {
+            if (j * kCQL >= K) break;
+            if (ql + kCQL * j < K) ss += (double)v[j] * (double)v[j];
+        }
+        ss = wave_sum_d(ss);
+        if ((threadIdx.x & 63) == 0) part_d[qw] = ss;
+        q_publish(qflag, qw, ++qs.step);
+        q_wait(qflag, qs.step);
+        const double t = ((part_d[0] + part_d[1]) + part_d[2]) + part_d[3];
+        const float r = (float)(1.0 / sqrt(t / (double)K + (double)eps));
+        if (gain) {
+            float gv[kCPoll];
+#pragma unroll
+            for (int j = 0; j < kCPoll; ++j) {
+                const int k = ql + kCQL * j;
+                if (j * kCQL >= K) break;
+                gv[j] = k < K ? gain[k] : 1.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kCPoll; ++j) {
+                if (j * kCQL >= K) break;
+                v[j] = (v[j] * r) * gv[j];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kCPoll; ++j) {
+                if (j * kCQL >= K) break;
+                v[j] = v[j] * r;
+            }
+        }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCPoll; ++j) {
+        if (j * kCQL >= K) break;
+        if (ql + kCQL * j < K) am = fmaxf(am, fabsf(v[j]));
+    }
+    am = wave_max(am);
+    if ((threadIdx.x & 63) == 0) part_f[qw] = am;
+    q_publish(qflag, qw, ++qs.step);
+    q_wait(qflag, qs.step);
+    const float mx = fmaxf(fmaxf(part_f[0], part_f[1]), fmaxf(part_f[2], part_f[3]));
+    const float a = 127.0f / fmaxf(mx, 1e-5f);
+    qs.a = a;
+    int cs = 0;
+#pragma unroll
+    for (int j = 0; j < kCPoll; ++j) {
+        const int k = ql + kCQL * j;
+        if (j * kCQL >= K) break;
+        if (k < K) {
+            const float q = __builtin_amdgcn_fmed3f(rintf(v[j] * a), -128.0f, 127.0f);
+            const int qi = (int)q;
+            q_s[k] = (int8_t)qi;
+            cs += qi;
+        }
+    }
+    cs = wave_sum_i(cs);
+    if ((threadIdx.x & 63) == 0) qs_part[qw] = cs;
+}
+
+// This workgroup's outputs of a stage: quantizer lane ql < 16 ng takes group
+// ql / 16, row (ql / 4) % 4, field ql % 4; the unit partials of its row are
+// summed over K, the code sum subtracted, then the rescale (and ReLU^2 for
+// the pair).  Stores are agent-scope (the next stage polls them).
+__device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, int s, int l, int ql, const int *part,
+                                         int qsum, float a, float *out, float *y_last) {
+    if (ql >= 16 * st.ng) return;
+    const int grl = ql >> 4, row = (ql >> 2) & 3, f = ql & 3;
+    const ChainLayer &w = A.layers[l];
+    int acc[2] = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (t >= st.nt) break;
+        int sum = 0;
+        const int base = (t * st.ng + grl) * st.ku;
+        for (int k = 0; k < st.ku; ++k) sum += part[((base + k) * 4 + row) * 4 + f];
+        acc[t] = sum - qsum;
+    }
+    const int rr = 4 * (st.g0 + grl) + row;   // packed row within its tensor
+    float val;
+    int col;
+    if (s == 2) {
+        const float gv = (float)acc[0] * (w.w_gu[0] / a);
+        const float uv = (float)acc[1] * (w.w_gu[1] / a);
+        val = relu2_mul(gv, uv);
+        col = f * st.R + rr;
+    } else if (s == 0) {
+        const ColOf c = col_of(A.seg_qkv, rr, f);
+        val = (float)acc[0] * (w.w_qkv[c.seg] / a);
+        col = c.col;
+    } else {
+        val = (float)acc[0] * ((s == 1 ? w.w_o[0] : w.w_dn[0]) / a);
+        col = f * st.R + rr;
+    }
+    __hip_atomic_store(reinterpret_cast<unsigned *>(out) + col, __float_as_uint(val), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (y_last) y_last[col] = val;
+}
+
+struct ChainLds {
+    int8_t q_s[kCMaxK];
+    int part[kCMaxUnits * 16];
+    double part_d[kCQ];
+    float part_f[kCQ];
+    int qs_part[kCQ];
+    int qflag[kCQ];
+};
+
+// Stage s of layer l for the quantizer waves: input, codes, barrier, barrier,
+// outputs.  phantom: a layer past the end (odd layer counts), barriers only.
+__device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int l, int s, bool phantom, int qw, int ql,
+                                        ChainLds &sh, QState &qs) {
+    const Stage st = stage_of(A, geo, phantom ? A.L - 1 : l, s);
+    float *lay = A.stages + (size_t)l * A.Sw;
+    float *o_qkv = lay, *o_o = lay + (A.H + 2 * A.KV), *o_p = o_o + A.H, *o_y = o_p + A.I;
+    float v[kCPoll];
+    if (!phantom) {
+        if (s == 0) {
+            if (l == 0) load_x(A, ql, v);
+            else poll(A.stages + (size_t)(l - 1) * A.Sw + (A.H + 2 * A.KV) + A.H + A.I, A.H, ql, v, qs.live);
+        } else if (s == 1) {
+            poll(o_qkv, A.H, ql, v, qs.live);
+        } else if (s == 2) {
+            poll(o_o, A.H, ql, v, qs.live);
+        } else {
+            poll(o_p, A.I, ql, v, qs.live);
+        }
+        const ChainLayer &w = A.layers[l];
+        quantize(v, st.K, s == 2 ? w.g_sub : w.g_ffn, s >= 2, A.eps, qw, ql, sh.q_s, sh.part_d, sh.part_f, sh.qs_part,
+                 sh.qflag, qs);
+    }
+    lds_barrier();   // codes ready
+    // the code sums are read between the barriers: a wave rewrites its entry
+    // for the next stage only after the second one
+    const int qsum = ((sh.qs_part[0] + sh.qs_part[1]) + sh.qs_part[2]) + sh.qs_part[3];
+    lds_barrier();   // partial sums ready
+    if (!phantom) {
+        float *out = s == 0 ? o_qkv : (s == 1 ? o_o : (s == 2 ? o_p : o_y));
+        epilogue(A, st, s, l, ql, sh.part, qsum, qs.a, out, (s == 3 && l == A.L - 1) ? A.y : nullptr);
+    }
+}
+
+// The stream waves' registers: the units of two layers (ring slots 0, 1).
+struct Ring {
+    v4i q[kUq], o[kUo], g[kUg], d[kUd];
+};
+
+template <int S>
+__device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int l, int ws, int lane, Ring &rg,
+                                        const ChainLds &sh, int *part) {
+    const Stage st = stage_of(A, geo, l < A.L ? l : A.L - 1, S);
+    lds_barrier();   // codes ready
+    if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, part);
+    if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, part);
+    if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, part);
+    if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, part);
+    lds_barrier();   // partial sums ready
+    // refill this slot with the same stage two layers on (the last layer
+    // again past the end: the loads stay uniform, their data unused)
+    const int ln = l + 2 < A.L ? l + 2 : A.L - 1;
+    const Stage nx = stage_of(A, geo, ln, S);
+    if (S == 0) issue<kUq>(nx, ws, lane, rg.q);
+    if (S == 1) issue<kUo>(nx, ws, lane, rg.o);
+    if (S == 2) issue<kUg>(nx, ws, lane, rg.g);
+    if (S == 3) issue<kUd>(nx, ws, lane, rg.d);
+}
+
+__device__ __forceinline__ void s_issue_layer(const ChainArgs &A, const Geo &geo, int l, int ws, int lane, Ring &rg) {
+    const int lc = l < A.L ? l : A.L - 1;
+    issue<kUq>(stage_of(A, geo, lc, 0), ws, lane, rg.q);
+    issue<kUo>(stage_of(A, geo, lc, 1), ws, lane, rg.o);
+    issue<kUg>(stage_of(A, geo, lc, 2), ws, lane, rg.g);
+    issue<kUd>(stage_of(A, geo, lc, 3), ws, lane, rg.d);
+}
+
+__global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) {
+    (void)a_unused;
+    const ChainArgs &A = args();
+    __shared__ __attribute__((aligned(16))) ChainLds sh;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+    const Geo geo = make_geo(A);
+    if (wave < kCS) {
+        // stream waves: units of layers 0 and 1 first, then consume / refill
+        Ring r0, r1;
+        s_issue_layer(A, geo, 0, wave, lane, r0);
+        s_issue_layer(A, geo, 1, wave, lane, r1);
+        lds_barrier();   // pairs with the quantizer waves' flag set-up
+        for (int l = 0; l < A.L; l += 2) {
+            s_stage<0>(A, geo, l, wave, lane, r0, sh, sh.part);
+            s_stage<1>(A, geo, l, wave, lane, r0, sh, sh.part);
+            s_stage<2>(A, geo, l, wave, lane, r0, sh, sh.part);
+            s_stage<3>(A, geo, l, wave, lane, r0, sh, sh.part);
+            s_stage<0>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
+            s_stage<1>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
+            s_stage<2>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
+            s_stage<3>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
+        }
+    } else {
+        const int qw = wave - kCS, ql = threadIdx.x - kCS * 64;
+        if (lane == 0) sh.qflag[qw] = 0;
+        QState qs{1.0f, 0, true};
+        lds_barrier();   // every flag zeroed before any wave waits on one
+#pragma unroll 1
+        for (int i = 0; i < 4 * (A.L + (A.L & 1)); ++i) {
+            const int l = i >> 2, s = i & 3;
+            q_stage(A, geo, l, s, l >= A.L, qw, ql, sh, qs);
+        }
+    }
+}
+
+// Sets every word of the stage buffers to the fill pattern.
+__global__ __launch_bounds__(256) void k_chain_fill(unsigned *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = kFill;
+}
+
+} // namespace
+
+int chain_max_layers() { return kChainMaxLayers; }
+
+// Host check of the shapes against the kernel's fixed capacities (units per
+// stream wave and stage, LDS codes) for G workgroups.
+bool chain_fits(int H, int KV, int I, int G) {
+    if (H % kCUnit || I % kCUnit || KV % 16 || H > kCMaxK || I > kCMaxK || G < 1) return false;
+    auto units = [&](int R, int nt, int K) {
+        const int groups = R / 4;
+        const int per = (groups + G - 1) / G;
+        return nt * per * (K / kCUnit);
+    };
+    return units((H + 2 * KV) / 4, 1, H) <= kCS * kUq && units(H / 4, 1, H) <= kCS * kUo &&
+           units(I / 4, 2, H) <= kCS * kUg && units(H / 4, 1, I) <= kCS * kUd;
+}
+
+hipError_t launch_chain_decode(const ChainParams &p, hipStream_t s) {
+    ChainArgs a{};
+    a.x = p.x; a.x_dt = p.x_dt; a.L = p.L; a.H = p.H; a.KV = p.KV; a.I = p.I; a.eps = p.eps;
+    a.stages = p.stages; a.Sw = (p.H + 2 * p.KV) + p.H + p.I + p.H; a.y = p.y; a.G = p.G; a.seg_qkv = p.seg_qkv;
+    for (int l = 0; l < p.L; ++l) {
+        const ChainLayerPtrs &w = p.layers[l];
+        a.layers[l] = ChainLayer{w.P_qkv, w.w_qkv, w.P_o, w.w_o, w.P_gu, w.w_gu, w.P_dn, w.w_dn, w.g_sub, w.g_ffn};
+    }
+    const size_t words = (size_t)p.L * a.Sw;
+    hipLaunchKernelGGL(k_chain_fill, dim3(256), dim3(256), 0, s, reinterpret_cast<unsigned *>(p.stages), words);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_chain_decode, dim3(p.G), dim3(kCThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// Workgroups one launch may use: one per compute unit when the kernel fits
+// one per unit (all resident at once, as the polls require), else 0.
+int chain_workgroups() {
+    const int cus = device_cu_count();
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void *>(&k_chain_decode), kCThreads,
+                                                     0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return per >= 1 ? cus : 0;
+}
+
+hipError_t chain_wait_expired(unsigned int *count, bool reset) {
+    unsigned int v = 0;
+    if (hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_chain_expired), sizeof(v)); e != hipSuccess) return e;
+    if (reset && v) {
+        const unsigned int zero = 0;
+        if (hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_chain_expired), &zero, sizeof(zero)); e != hipSuccess)
+            return e;
+    }
+    *count = v;
+    return hipSuccess;
+}
+
+} // namespace bl

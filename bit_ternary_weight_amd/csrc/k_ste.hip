@@ -132,12 +132,23 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// C[i][j] = s * sum_l A[i][l] B[j][l] for i < Ir, j < Jr; A [I][L], B [J][L]
-// bf16 (zero-padded), C [Ir][Jr] fp32 with row stride Jr; I, J, L multiples
-// of 128, 128, 64; s read from device memory (1 if null).
-__global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __bf16 *B, float *C, int I, int J,
-                                                       int L, int Ir, int Jr, const float *s_ptr) {
-    const float s = s_ptr ? *s_ptr : 1.0f;
+// C[i][j] = epilogue(sum_l A[i][l] B[j][l]) for i < Ir, j < Jr; A [I][L],
+// B [J][L] bf16 (zero-padded), C [Ir][Jr] with row stride Jr; I, J, L
+// multiples of 128, 128, 64.  Epilogues:
+//   EPI_SCALE: fp32 C = s * sum, s read from device memory (1 if null);
+//   EPI_BITLINEAR: the BitLinear rescale of an exact integer sum (the
+//     operands are int8 activation codes and ternary codes, every partial sum
+//     an integer below 2^24, so the fp32 accumulator holds it exactly):
+//     C = float(sum) * (w_mean[seg(j)] / a[i]) in fp32, its bf16 rounding, or
+//     the int32 sum itself, per e.y_dt.
+constexpr int EPI_SCALE = 0;
+constexpr int EPI_BITLINEAR = 1;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __bf16 *B, void *Cv, int I, int J,
+                                                       int L, int Ir, int Jr, const float *s_ptr, GemmEpi e) {
+    float *C = static_cast<float *>(Cv);
+    const float s = (EPI == EPI_SCALE && s_ptr) ? *s_ptr : 1.0f;
     __shared__ __attribute__((aligned(16))) __bf16 as[kT * kL];
     __shared__ __attribute__((aligned(16))) __bf16 bs[kT * kL];
     const int nj = J / kT;
@@ -188,6 +199,56 @@ __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __b
         }
     }
     const bool whole = i0 + kT <= Ir && j0 + kT <= Jr && (Jr & 3) == 0;
+    if constexpr (EPI == EPI_BITLINEAR) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = i0 + wi + 16 * x + lr;
+            const float ai = i < Ir ? e.a[i] : 1.0f;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int j = j0 + wj + 4 * g + 16 * y;
+                float v[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    int sg = 0;
+#pragma unroll
+                    for (int t = 0; t < BL_MAX_SEGMENTS - 1; ++t)
+                        sg += (t + 1 < e.nseg && j + c >= e.cend[t]) ? 1 : 0;
+                    v[c] = acc[x][y][c] * (e.w_mean[sg] / ai);
+                }
+                const size_t o = (size_t)i * Jr + j;
+                if (e.y_dt == BL_I32) {
+                    int *Ci = static_cast<int *>(Cv);
+                    if (whole) {
+                        *reinterpret_cast<int4 *>(Ci + o) =
+                            int4{(int)acc[x][y][0], (int)acc[x][y][1], (int)acc[x][y][2], (int)acc[x][y][3]};
+                    } else if (i < Ir) {
+                        for (int c = 0; c < 4; ++c)
+                            if (j + c < Jr) Ci[o + c] = (int)acc[x][y][c];
+                    }
+                } else if (e.y_dt == BL_BF16) {
+                    uint16_t *Cb = static_cast<uint16_t *>(Cv);
+                    if (whole) {
+                        uint2 pk;
+                        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(Cb + o) = pk;
+                    } else if (i < Ir) {
+                        for (int c = 0; c < 4; ++c)
+                            if (j + c < Jr) Cb[o + c] = f32_to_bf16(v[c]);
+                    }
+                } else {
+                    if (whole) {
+                        *reinterpret_cast<float4 *>(C + o) = float4{v[0], v[1], v[2], v[3]};
+                    } else if (i < Ir) {
+                        for (int c = 0; c < 4; ++c)
+                            if (j + c < Jr) C[o + c] = v[c];
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int i = i0 + wi + 16 * x + lr;
@@ -257,7 +318,8 @@ hipError_t launch_ste_grad_input(const void *dY, bool dy_bf16, int M, int N, int
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         A = dyb;
     }
-    hipLaunchKernelGGL(k_gemm_nt_bf16, dim3((I / kT) * (J / kT)), dim3(256), 0, s, A, ct, dX, I, J, L, M, K, w_mean);
+    hipLaunchKernelGGL(k_gemm_nt_bf16<EPI_SCALE>, dim3((I / kT) * (J / kT)), dim3(256), 0, s, A, ct, (void *)dX, I, J, L,
+                       M, K, w_mean, GemmEpi{});
     return hipGetLastError();
 }
 
@@ -276,7 +338,29 @@ hipError_t launch_ste_grad_weight(const void *dY, bool dy_bf16, int M, int N, in
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((k_transpose<int8_t, false>), dim3(J / 64, L / 64), dim3(256), 0, s, q, M, K, nullptr, qt, L);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_nt_bf16, dim3((I / kT) * (J / kT)), dim3(256), 0, s, at, qt, dW, I, J, L, N, K, nullptr);
+    hipLaunchKernelGGL(k_gemm_nt_bf16<EPI_SCALE>, dim3((I / kT) * (J / kT)), dim3(256), 0, s, at, qt, (void *)dW, I, J,
+                       L, N, K, nullptr, GemmEpi{});
+    return hipGetLastError();
+}
+
+size_t unpacked_gemm_ws_bytes(int M, int K) { return (size_t)pad_to(M, kT) * K * sizeof(__bf16); }
+
+bool unpacked_gemm_fits(int M, int N, int K) {
+    return K % kL == 0 && N % kT == 0 && (size_t)pad_to(M, kT) * K < ((size_t)1 << 31) &&
+           (size_t)N * K < ((size_t)1 << 31) && (size_t)pad_to(M, kT) * N < ((size_t)1 << 31);
+}
+
+hipError_t launch_unpacked_gemm(const int8_t *q, const float *a, int M, int K, const __bf16 *W, int N,
+                                const GemmEpi &e, void *y, void *ws, hipStream_t s) {
+    const int I = pad_to(M, kT);
+    __bf16 *qb = static_cast<__bf16 *>(ws);   // [I][K] bf16 codes, zero rows below M
+    const size_t threads = (size_t)I * (K / 8);
+    hipLaunchKernelGGL(k_pad_bf16<int8_t>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, q, M, K, qb, I, K);
+    if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
+    GemmEpi ep = e;
+    ep.a = a;
+    hipLaunchKernelGGL(k_gemm_nt_bf16<EPI_BITLINEAR>, dim3((I / kT) * (N / kT)), dim3(256), 0, s, qb, W, y, I, N, K,
+                       M, N, nullptr, ep);
     return hipGetLastError();
 }
 

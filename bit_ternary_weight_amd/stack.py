@@ -146,6 +146,26 @@ def layer_forward(x: torch.Tensor, lw: LayerWeights, eps: float = 1e-5, out: tor
     return bl.ffn_chain(y_o, lw.packed_gu, lw.w_gu, lw.packed_down, lw.w_down, eps=eps, y=out)
 
 
+def stack_decode(x: torch.Tensor, layers, eps: float = 1e-5, out: torch.Tensor = None, stages: torch.Tensor = None):
+    """The same linear path as stack_forward at one token, every layer's
+    stages in one persistent launch per 32 layers (bl_stack_decode).
+    x [1,H] fp32 or bf16 -> [1,H] fp32; stages, when given, is
+    [len(layers), (H+2KV)+H+I+H] fp32 and receives each stage's output."""
+    if x.shape[0] != 1:
+        raise ValueError("stack_decode takes one token")
+    n = bl.STACK_DECODE_MAX_LAYERS
+    if out is None:
+        out = torch.empty((1, H), dtype=torch.float32, device=x.device)
+    cur = x
+    for i in range(0, len(layers), n):
+        part = layers[i:i + n]
+        st = None if stages is None else stages[i:i + len(part)]
+        y = out if i + n >= len(layers) else torch.empty((1, H), dtype=torch.float32, device=x.device)
+        bl.stack_decode(cur, part, H, KV, I, eps=eps, y=y, stages=st)
+        cur = y
+    return out
+
+
 def stack_forward(x: torch.Tensor, layers, eps: float = 1e-5, bufs: dict = None):
     """All layers in sequence; returns the last layer's output [M,H] fp32."""
     if bufs is None:

@@ -259,6 +259,92 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I,
                  const bl_ffn_debug *dbg, bl_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * bl_stack_decode -- the linear path of a stack of decoder layers for one
+ * token (M = 1) in one persistent launch.  Per layer, with attention left
+ * out (the stand-in wiring of the 30-layer stack: q's output feeds o, no
+ * residual additions):
+ *   x -> BitLinear q|k|v (segments H, KV, KV) -> BitLinear o on q's output
+ *     -> subln RMSNorm -> BitLinear gate|up -> ReLU^2(gate)*up
+ *     -> ffn_sub_norm RMSNorm -> BitLinear down -> the next layer's x.
+ * [T] "推理侧 BitLinear" (each BitLinear: per-token quantization, the packed
+ * ternary product, the rescale) and the subln paragraph; [M] "模型详情" and
+ * "BitNetConfig" (subln, ReLU squared, rms_norm_eps).  Every stage computes
+ * the same bits as bl_gemv_w2a8 / bl_ffn_chain (the RMSNorm's fp64 sum aside,
+ * whose order may differ in the last bit, as between those calls).
+ *   x        [H] fp32 or bf16 (x_dtype), the first layer's input;
+ *   layers   host array of n_layers weight sets (device pointers): packed
+ *            q|k|v [(H+2KV)/4, H] (q, k, v packed separately and stacked)
+ *            with w_qkv [3]; o [H/4, H], w_o [1]; gate|up [2I/4, H] (gate,
+ *            then up), w_gu [2]; down [H/4, I], w_down [1]; g_subln [H] and
+ *            g_ffn [I] RMSNorm gains or NULL (unit gain);
+ *   y        out [H] fp32, the last layer's output;
+ *   stages   optional out [n_layers][(H+2KV) + H + I + H] fp32: per layer the
+ *            q|k|v output, o's output, ReLU^2(gate)*up and down's output (the
+ *            buffers the workgroups exchange); NULL: they live in ws;
+ *   ws       bl_stack_decode_workspace_bytes(n_layers, H, KV, I) bytes when
+ *            stages is NULL, else unused (may be NULL).
+ * 1 <= n_layers <= 32; H and I multiples of 256 up to 8192, KV a multiple of
+ * 16, within the kernel's per-workgroup capacity (the BitNet-2B4T shape
+ * fits); the kernel needs one resident workgroup per compute unit.  Other
+ * shapes return BL_ERR_SHAPE (run the layers with the other calls).  The
+ * workgroups exchange stage outputs through device memory with bounded
+ * waits: a wait that expires is counted (bl_device_errors) and the launch
+ * still ends.  Calls sharing `stages` or ws must be ordered.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const uint8_t *packed_qkv;
+    const float *w_qkv;
+    const uint8_t *packed_o;
+    const float *w_o;
+    const uint8_t *packed_gu;
+    const float *w_gu;
+    const uint8_t *packed_down;
+    const float *w_down;
+    const float *g_subln;
+    const float *g_ffn;
+} bl_layer;
+
+size_t bl_stack_decode_workspace_bytes(int n_layers, int H, int KV, int I);
+int bl_stack_decode(const void *x, int x_dtype, int n_layers, const bl_layer *layers, int H, int KV, int I,
+                    float eps, float *y, float *stages, void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * bl_unpack_bf16 / bl_gemm_unpacked -- the offline-unpacked path: the packed
+ * ternary weight expanded once, at load time, to dense bf16 codes, and the
+ * BitLinear forward as a dense bf16 product against them.  [T]
+ * "BitNetQuantConfig" (AutoBitLinear with quantization_mode "offline": the
+ * packed weight is unpacked to the module's compute dtype when loaded, and
+ * the weight scale multiplies the output at inference) and "推理侧 BitLinear"
+ * (the unpack); [M] the efficiency note (the stock path is not faster than
+ * full precision), which this path lets one measure against the packed one.
+ * bl_unpack_bf16:
+ *   packed  [N/4,K] uint8 (plane order), n_seg segments stacked as for the
+ *           contractions (seg_n host widths; n_seg = 1, seg_n = NULL: one);
+ *   w_codes out [N,K] bf16, the codes -1, 0, +1 in output-column order (row
+ *           n of segment s: packed row n' mod R_s of the segment, field
+ *           n' div R_s, n' = n - the segment's first column, R_s = its
+ *           width / 4).
+ * bl_gemm_unpacked: the arguments of bl_gemm_w2a8 with w_codes [N,K] bf16 (as
+ *   bl_unpack_bf16 writes them) in place of the packed weight; int8 codes in
+ *   x must be contiguous rows.  The activation codes enter the product as
+ *   bf16 (exact); every partial sum is an integer below 2^24 and is exact in
+ *   the fp32 accumulators, so y is bit-identical to bl_gemm_w2a8's.  It
+ *   streams 2 bytes per weight instead of a quarter byte.
+ *   Shapes: N % 4 == 0; M <= 4 with K % 8 == 0, K <= 8192 runs the decode
+ *   kernel; larger M needs K % 64 == 0 and N % 128 == 0 (the bf16 MFMA GEMM),
+ *   else the decode kernel 4 rows at a time (K % 8 == 0, K <= 8192); other
+ *   shapes return BL_ERR_SHAPE.  w_codes, y 16-byte aligned.
+ *   ws: bl_gemm_unpacked_workspace_bytes(M, N, K) bytes.
+ * ------------------------------------------------------------------------ */
+int bl_unpack_bf16(const uint8_t *packed, int N, int K, int n_seg, const int *seg_n, void *w_codes,
+                   bl_stream stream);
+size_t bl_gemm_unpacked_workspace_bytes(int M, int N, int K);
+int bl_gemm_unpacked(const void *x, int x_dtype, int ldx, const float *a, int M, int K,
+                     const void *w_codes, int N, int n_seg, const int *seg_n,
+                     const float *w_mean, void *y, int y_dtype,
+                     void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
  * bl_ffn_chain_noalloc -- bl_ffn_chain for callers that cannot allocate
  * device memory or pass a workspace: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc.  Same arguments and results

@@ -291,3 +291,41 @@ def test_ste_validation(lib):
     assert gw(FAKE, BF, FAKE, FAKE, 128, 256, 384, FAKE_MIS, FAKE, nw, None) == lib.BL_ERR_ALIGN
     assert gw(FAKE, BF, FAKE, FAKE, 128, 256, 384, FAKE, FAKE, nw - 1, None) == lib.BL_ERR_WORKSPACE
     assert gw(FAKE, 3, FAKE, FAKE, 128, 256, 384, FAKE, FAKE, nw, None) == lib.BL_ERR_DTYPE
+
+
+def test_unpacked_validation(lib):
+    raw = lib.raw
+    assert raw.bl_unpack_bf16(None, 8, 8, 1, None, FAKE, None) == lib.BL_ERR_NULL
+    assert raw.bl_unpack_bf16(FAKE, 6, 8, 1, None, FAKE, None) == lib.BL_ERR_SHAPE
+    assert raw.bl_unpack_bf16(FAKE, 8, 8, 2, None, FAKE, None) == lib.BL_ERR_SEGMENTS
+    assert raw.bl_unpack_bf16(FAKE, 8, 8, 1, None, ctypes.c_void_p(0x10001), None) == lib.BL_ERR_ALIGN
+    need = raw.bl_gemm_unpacked_workspace_bytes(130, 256, 2560)
+    assert need >= 130 * 2560 + 256 * 2560 * 2
+    g = raw.bl_gemm_unpacked
+    ok = dict(x=FAKE, xdt=1, ldx=0, a=None, M=130, K=2560, w=FAKE, N=256, ns=1, seg=None, wm=FAKE, y=FAKE, ydt=0,
+              ws=FAKE, wsb=need)
+    call = lambda **kw: g(*{**ok, **kw}.values(), None)
+    assert call(x=None) == lib.BL_ERR_NULL
+    assert call(xdt=3) == lib.BL_ERR_DTYPE
+    assert call(xdt=2) == lib.BL_ERR_NULL          # int8 codes need their scales
+    assert call(N=254) == lib.BL_ERR_SHAPE
+    assert call(K=100, wsb=1 << 30) == lib.BL_ERR_SHAPE   # neither kernel takes K = 100 at M = 130
+    assert call(y=FAKE_MIS) == lib.BL_ERR_ALIGN
+    assert call(wsb=need - 1) == lib.BL_ERR_WORKSPACE
+
+
+def test_stack_decode_validation(lib):
+    raw = lib.raw
+    L = lib.Layer
+    ok = L(*[FAKE.value] * 8, None, None)
+    arr = (L * 2)(ok, ok)
+    H, KV, I = 2560, 640, 6912
+    need = raw.bl_stack_decode_workspace_bytes(2, H, KV, I)
+    assert need >= 2 * ((H + 2 * KV) + H + I + H) * 4
+    call = lambda **kw: raw.bl_stack_decode(*{**dict(x=FAKE, xdt=1, L=2, layers=arr, H=H, KV=KV, I=I, eps=1e-5, y=FAKE,
+                                                      st=None, ws=FAKE, wsb=need), **kw}.values(), None)
+    assert call(x=None) == lib.BL_ERR_NULL
+    assert call(xdt=2) == lib.BL_ERR_DTYPE
+    assert call(L=0) == lib.BL_ERR_SHAPE
+    assert call(L=33) == lib.BL_ERR_SHAPE
+    assert call(eps=-1.0) == lib.BL_ERR_SHAPE

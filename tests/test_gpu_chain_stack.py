@@ -172,3 +172,56 @@ def test_stack_prefill_30_layers_one_row_per_token_tile():
     M = 4096
     rows = sorted(set([32 * t + (13 * t) % 32 for t in range(M // 32)] + [M - 1]))
     _check_stack(M, 30, rows)
+
+
+# ----------------------------------------------------------------------------- the persistent decode step
+def _check_stack_decode(n_layers, x_kind="outliers", seed=0):
+    """bl_stack_decode over n_layers: every stage of every layer (q|k|v, o,
+    ReLU^2(gate)*up, down) against the oracle's layer on the GPU's own input
+    to that layer; all stage buffers and the output guarded."""
+    from bit_ternary_weight_amd import stack
+    H, KV, I = synth.HIDDEN, synth.KV_DIM, synth.INTERMEDIATE
+    layers = stack.build_layers(n_layers, dev())
+    bits = synth.act_outliers_bf16(seed, 1, H) if x_kind == "outliers" else synth.act_normal_bf16(seed, 1, H)
+    x = bf16_dev(bits)
+    Sw = (H + 2 * KV) + H + I + H
+    gst = guarded((n_layers, Sw))
+    gy = guarded((1, H))
+    stack.stack_decode(x, layers, out=gy.t, stages=gst.t)
+    gst.check("stages")
+    gy.check("y")
+    st = host(gst.t)
+    assert np.array_equal(host(gy.t)[0].view(np.uint32), st[-1, Sw - H:].view(np.uint32))
+    x_host = f32_of_bf16(bits)
+    offs = {"y_qkv": (0, H + 2 * KV), "y_o": (H + 2 * KV, H), "p": (2 * H + 2 * KV, I), "y": (2 * H + 2 * KV + I, H)}
+    for l in range(n_layers):
+        codes, wms = _oracle_layer_codes(l)
+        ref = oracle.layer(x_host, codes, wms)
+        for key, (o, n) in offs.items():
+            got = st[l:l + 1, o:o + n]
+            assert_exact(got.view(np.uint32), np.ascontiguousarray(ref[key]).view(np.uint32), f"layer {l} {key}")
+        x_host = st[l:l + 1, Sw - H:].copy()
+        print(f"[stack_decode] layer {l} stages bit-exact", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_stack_decode_persistent_30_layers():
+    _check_stack_decode(30)
+
+
+def test_stack_decode_persistent_odd_and_short():
+    """One layer (a phantom second layer in the pair loop) and three layers."""
+    _check_stack_decode(1, seed=3)
+    _check_stack_decode(3, x_kind="normal", seed=4)
+
+
+def test_stack_decode_persistent_matches_the_launch_chain():
+    """The persistent step and the separate launches give the same output."""
+    from bit_ternary_weight_amd import stack
+    layers = stack.build_layers(4, dev())
+    x = bf16_dev(synth.act_outliers_bf16(9, 1, synth.HIDDEN))
+    a = stack.stack_decode(x, layers).clone()
+    b = stack.stack_forward(x, layers, bufs={}).clone()
+    assert torch.equal(a, b)
+    # repeated calls on the same buffers stay identical
+    assert torch.equal(stack.stack_decode(x, layers), a)
