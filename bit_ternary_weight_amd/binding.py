@@ -425,13 +425,11 @@ def stack_decode(x, layers, H, KV, I, eps=1e-5, y=None, stages=None):
     _need(y, tuple(y.shape), (torch.float32,), "y")
     if y.numel() != H:
         raise ValueError(f"y must hold {H} elements")
-    ws = None
     if stages is not None:
         _need(stages, (L, (H + 2 * KV) + H + I + H), (torch.float32,), "stages")
-    else:
-        ws = workspace(dev, raw.bl_stack_decode_workspace_bytes(L, H, KV, I))
+    ws = workspace(dev, raw.bl_stack_decode_workspace_bytes(L, H, KV, I))
     _check(raw.bl_stack_decode(_ptr(x), _dt(x), L, arr, H, KV, I, float(eps), _ptr(y), _ptr(stages), _ptr(ws),
-                               0 if ws is None else ws.numel(), _stream(dev)))
+                               ws.numel(), _stream(dev)))
     return y
 
 

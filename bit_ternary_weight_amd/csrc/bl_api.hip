@@ -805,11 +805,8 @@ int bl_stack_decode(const void *x, int x_dtype, int n_layers, const bl_layer *la
     }
     if (!aligned(x, x_dtype == BL_F32 ? 4 : 2) || !aligned(y, 4) || (stages && !aligned(stages, 4)))
         return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
-    float *st = stages;
-    if (!st) {
-        if (int e = check_ws(fn, ws, ws_bytes, bl_stack_decode_workspace_bytes(n_layers, H, KV, I))) return e;
-        st = (float *)ws;
-    }
+    if (int e = check_ws(fn, ws, ws_bytes, bl_stack_decode_workspace_bytes(n_layers, H, KV, I))) return e;
+
     bl::ChainLayerPtrs lp[32];
     for (int l = 0; l < n_layers; ++l) {
         const bl_layer &w = layers[l];
@@ -817,7 +814,8 @@ int bl_stack_decode(const void *x, int x_dtype, int n_layers, const bl_layer *la
                                    w.w_down, w.g_subln, w.g_ffn};
     }
     bl::ChainParams p{};
-    p.x = x; p.x_dt = x_dtype; p.L = n_layers; p.H = H; p.KV = KV; p.I = I; p.eps = eps; p.stages = st; p.y = y;
+    p.x = x; p.x_dt = x_dtype; p.L = n_layers; p.H = H; p.KV = KV; p.I = I; p.eps = eps;
+    p.xch = (float *)ws; p.stages = stages; p.y = y;
     p.G = G; p.layers = lp;
     const int segs[3] = {H, KV, KV};
     if (int e = make_segtab(H + 2 * KV, 3, segs, p.seg_qkv)) return e;

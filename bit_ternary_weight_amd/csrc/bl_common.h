@@ -347,7 +347,8 @@ struct ChainParams {
     int x_dt;
     int L, H, KV, I;
     float eps;
-    float *stages;   // [L][(H + 2KV) + H + I + H] fp32, the exchange buffers
+    float *xch;      // [L][(H + 2KV) + H + I + H] fp32 exchange (packed-row order)
+    float *stages;   // the same in column order, or null
     float *y;        // [H]
     int G;           // workgroups (chain_workgroups())
     SegTab seg_qkv;

@@ -21,27 +21,34 @@
 //   * one workgroup per compute unit (all resident; the host checks the
 //     occupancy before launching), each owning a fixed set of 4-row groups of
 //     every stage's weight;
-//   * 12 stream waves hold the weight units (4 packed rows x 256 bytes) of two
-//     layers in registers: after a stage is consumed, the same registers are
-//     reloaded with that stage of the layer two ahead, so the HBM stream never
-//     waits for the chain of dependencies.  They issue no other global memory
-//     operation, so the compiler's waits on them stay exact;
+//   * 12 stream waves hold the weight units (4 packed rows x 256 bytes) of a
+//     stage in registers, loaded one stage ahead (issued as soon as the
+//     previous stage's outputs have been stored), so a stage's weights do
+//     not wait for its input.  They issue no other global memory operation,
+//     so the compiler's waits on them stay exact;
 //   * 4 quantizer waves poll the previous stage's output, normalize and
 //     quantize it into LDS, and after the stream waves' products store this
 //     workgroup's part of the stage's output.
 //
-// Cross-workgroup exchange without flags or fences: every stage output lives
-// in a buffer that a fill launch sets to an all-ones word (a NaN no stage
-// produces from finite input) right before the persistent launch.  Outputs
-// are written with agent-scope stores and read with agent-scope loads (the
-// coherent cache policy), and a consumer polls each word until it is no
-// longer the fill pattern.  Each word is written once, so per-location
-// coherence is all the exchange needs.  Polls are bounded: an expired poll is
-// counted (bl_device_errors) and the kernel runs to its end.
+// Cross-workgroup exchange without fences or counters: every stage output
+// goes to an exchange buffer that a fill launch sets to an all-ones word (a
+// NaN no stage produces from finite input) right before the persistent
+// launch.  The exchange holds a stage's outputs in packed-row order (output
+// of packed row r, field f at 4 r + f), so a workgroup's outputs are one
+// contiguous run of 64 or 128 bytes written by one store instruction, with
+// agent-scope stores (the coherent cache policy); the column-order copy the
+// caller may ask for is written with plain stores.  A consumer reads the
+// vector with agent-scope loads until no word holds the fill pattern: each
+// word is written once, so correctness rests on per-location coherence alone.
+// Waits are bounded: an expired one is counted (bl_device_errors) and the
+// kernel runs to its end.
 //
-// Within a workgroup the two roles meet at two barriers per stage (codes in
-// LDS; partial sums in LDS), both LDS-only so no wave waits for weight loads
-// in flight.
+// Within a workgroup the two roles meet at three barriers per stage (codes in
+// LDS; partial sums in LDS; outputs stored), all LDS-only so no wave waits
+// for weight loads in flight.  The next stage's weights are issued after the
+// third: a compute unit sends its memory requests in issue order, and stores
+// queued behind a stage's worth of weight loads reach the other workgroups
+// that much later.
 #include "bl_common.h"
 
 namespace bl {
@@ -60,7 +67,7 @@ constexpr int kCUnit = 256;             // k bytes of a unit
 constexpr int kUq = 1, kUo = 1, kUg = 4, kUd = 3;
 constexpr int kUMax = 4;
 constexpr int kCMaxUnits = kCS * kUMax;
-constexpr unsigned kFill = 0xFFFFFFFFu;  // stage words not yet written
+constexpr unsigned kFill = 0xFFFFFFFFu;  // exchange words not yet written
 constexpr int kPollMax = 1 << 17;       // polls per wait (each at least a memory round trip)
 
 __device__ unsigned int g_chain_expired = 0;
@@ -85,7 +92,8 @@ struct ChainArgs {
     int x_dt;
     int L, H, KV, I;
     float eps;
-    float *stages;   // [L][Sw]: q|k|v, o, p, y
+    float *xch;      // [L][Sw] exchange, packed-row order: q|k|v, o, p, y
+    float *stages;   // [L][Sw] the same in column order, or null
     int Sw;
     float *y;        // [H]
     int G;           // workgroups
@@ -158,6 +166,62 @@ __device__ __forceinline__ const uint8_t *unit_addr(const Stage &st, int mu, int
     return st.P + (size_t)row * st.K + (size_t)k * kCUnit + 16 * ch;
 }
 
+// Wave reductions by DPP row operations and lane reads (no LDS round trips);
+// the summation order is fixed.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int quad_sum(int v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    auto st = [](float x, int b) { return fmaxf(x, __int_as_float(b)); };
+    v = st(v, dpp<0xB1>(__float_as_int(v)));
+    v = st(v, dpp<0x4E>(__float_as_int(v)));
+    v = st(v, dpp<0x124>(__float_as_int(v)));   // row_ror:4
+    v = st(v, dpp<0x128>(__float_as_int(v)));   // row_ror:8
+    const int iv = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 32)), __int_as_float(__builtin_amdgcn_readlane(iv, 48))));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x128>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp<CTRL>((int)(b & 0xFFFFFFFF));
+    const int hi = dpp<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+    v += dpp_d<0xB1>(v);
+    v += dpp_d<0x4E>(v);
+    v += dpp_d<0x124>(v);
+    v += dpp_d<0x128>(v);
+    return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
+}
+
 template <int U>
 __device__ __forceinline__ void issue(const Stage &st, int ws, int lane, v4i (&r)[U]) {
 #pragma unroll
@@ -186,9 +250,7 @@ __device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) {
             const v4i d = mfma16(f[fi], b, v4i{0, 0, 0, 0});
-            int v = s == 0 ? d[0] : (s == 1 ? d[1] : (s == 2 ? d[2] : d[3]));
-            v += __shfl_xor(v, 1, 64);
-            v += __shfl_xor(v, 2, 64);
+            const int v = quad_sum(s == 0 ? d[0] : (s == 1 ? d[1] : (s == 2 ? d[2] : d[3])));
             tot[fi] = shift_field(v, fi);
         }
         if ((lane & 15) == 0) {
@@ -222,39 +284,27 @@ __device__ __forceinline__ void q_wait(const int *qflag, int step) {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-// Polls the K words of `in` this lane covers (element ql + 256 j) until none
-// holds the fill pattern; returns them in v.  `live` turns false after an
-// expired poll, after which later polls take what they find.
+// Polls the K exchange words this lane covers (position ql + 256 j) until
+// none holds the fill pattern; returns them in v.  `live` turns false after
+// an expired poll, after which later polls take what they find.
+// K is a multiple of 256, so j < K / 256 is the whole predicate (uniform);
+// every loop over j is unrolled and the loads of one poll are all in flight
+// together.
 __device__ __forceinline__ void poll(const float *in, int K, int ql, float (&v)[kCPoll], bool &live) {
-    const unsigned *p = reinterpret_cast<const unsigned *>(in);
+    const unsigned *p = reinterpret_cast<const unsigned *>(in) + ql;
+    const int nj = K >> 8;
     for (int it = 0;; ++it) {
+        unsigned u[kCPoll];
+#pragma unroll
+        for (int j = 0; j < kCPoll; ++j) {
+            u[j] = 0u;
+            if (j < nj) u[j] = __hip_atomic_load(p + kCQL * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         bool missing = false;
 #pragma unroll
         for (int j = 0; j < kCPoll; ++j) {
-            const int k = ql + kCQL * j;
-            if (j * kCQL >= K) break;
-            unsigned u = 0;
-            if (k < K) u = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            missing |= (k < K) && (u == kFill);
-            v[j] = __uint_as_float(u);
+            missing |= u[j] == kFill;
+            v[j] = __uint_as_float(u[j]);
         }
         if (!missing) return;
         if (!live || it >= kPollMax) {
@@ -266,18 +316,22 @@ __device__ __forceinline__ void poll(const float *in, int K, int ql, float (&v)[
     }
 }
 
-// The layer input x (the caller's fp32 or bf16 row, plain loads).
+// Column of exchange position p = ql + 256 j of a K-wide vector (one
+// segment, K / 4 packed rows): field p % 4 of packed row p / 4.
+__device__ __forceinline__ int col_at(int ql, int j, int K) { return (ql & 3) * (K >> 2) + (ql >> 2) + 64 * j; }
+
+// The layer input x (the caller's fp32 or bf16 row, plain loads), in the
+// exchange order of the polled stages.
 __device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float (&v)[kCPoll]) {
+    const int nj = A.H >> 8;
+    if (A.x_dt == BL_BF16) {
+        const uint16_t *xb = static_cast<const uint16_t *>(A.x);
 #pragma unroll
-    for (int j = 0; j < kCPoll; ++j) {
-        const int k = ql + kCQL * j;
-        if (j * kCQL >= A.H) break;
-        float t = 0.0f;
-        if (k < A.H) {
-            if (A.x_dt == BL_BF16) t = bf16_to_f32(static_cast<const uint16_t *>(A.x)[k]);
-            else t = static_cast<const float *>(A.x)[k];
-        }
-        v[j] = t;
+        for (int j = 0; j < kCPoll; ++j) v[j] = j < nj ? bf16_to_f32(xb[col_at(ql, j, A.H)]) : 0.0f;
+    } else {
+        const float *xf = static_cast<const float *>(A.x);
+#pragma unroll
+        for (int j = 0; j < kCPoll; ++j) v[j] = j < nj ? xf[col_at(ql, j, A.H)] : 0.0f;
     }
 }
 
@@ -287,21 +341,20 @@ struct QState {
     bool live;    // polls still wait
 };
 
-// Normalizes (optionally) and quantizes the K values in v: codes to q_s, the
-// scale to st.a, this wave's code sum to qs_part[qw] (summed after the first
-// barrier).  Same arithmetic as the row kernel: fp64 sum of squares,
+// Normalizes (optionally) and quantizes the K values in v (exchange order):
+// codes to q_s in column order, the scale to st.a, this wave's code sum to
+// qs_part[qw] (summed after the first barrier).  Same arithmetic as the row kernel: fp64 sum of squares,
 // r = float(1 / sqrt(ss / K + eps)), (h * r) * g, a = 127 / max(amax, 1e-5),
 // q = clamp(rint(x * a)).
 __device__ __forceinline__ void quantize(float (&v)[kCPoll], int K, const float *gain, bool norm, float eps, int qw,
                                          int ql, int8_t *q_s, double *part_d, float *part_f, int *qs_part,
                                          int *qflag, QState &qs) {
+    const int nj = K >> 8;
     if (norm) {
         double ss = 0.0;
 #pragma unroll
-        for (int j = 0; j < kCPoll; ++j) {
-            if (j * kCQL >= K) break;
-            if (ql + kCQL * j < K) ss += (double)v[j] * (double)v[j];
-        }
+        for (int j = 0; j < kCPoll; ++j)
+            if (j < nj) ss += (double)v[j] * (double)v[j];
         ss = wave_sum_d(ss);
         if ((threadIdx.x & 63) == 0) part_d[qw] = ss;
         q_publish(qflag, qw, ++qs.step);
@@ -311,30 +364,18 @@ __device__ __forceinline__ void quantize(float (&v)[kCPoll], int K, const float 
         if (gain) {
             float gv[kCPoll];
 #pragma unroll
-            for (int j = 0; j < kCPoll; ++j) {
-                const int k = ql + kCQL * j;
-                if (j * kCQL >= K) break;
-                gv[j] = k < K ? gain[k] : 1.0f;
-            }
+            for (int j = 0; j < kCPoll; ++j) gv[j] = j < nj ? gain[col_at(ql, j, K)] : 1.0f;
 #pragma unroll
-            for (int j = 0; j < kCPoll; ++j) {
-                if (j * kCQL >= K) break;
-                v[j] = (v[j] * r) * gv[j];
-            }
+            for (int j = 0; j < kCPoll; ++j) v[j] = (v[j] * r) * gv[j];
         } else {
 #pragma unroll
-            for (int j = 0; j < kCPoll; ++j) {
-                if (j * kCQL >= K) break;
-                v[j] = v[j] * r;
-            }
+            for (int j = 0; j < kCPoll; ++j) v[j] = v[j] * r;
         }
     }
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kCPoll; ++j) {
-        if (j * kCQL >= K) break;
-        if (ql + kCQL * j < K) am = fmaxf(am, fabsf(v[j]));
-    }
+    for (int j = 0; j < kCPoll; ++j)
+        if (j < nj) am = fmaxf(am, fabsf(v[j]));
     am = wave_max(am);
     if ((threadIdx.x & 63) == 0) part_f[qw] = am;
     q_publish(qflag, qw, ++qs.step);
@@ -345,12 +386,10 @@ __device__ __forceinline__ void quantize(float (&v)[kCPoll], int K, const float 
     int cs = 0;
 #pragma unroll
     for (int j = 0; j < kCPoll; ++j) {
-        const int k = ql + kCQL * j;
-        if (j * kCQL >= K) break;
-        if (k < K) {
+        if (j < nj) {
             const float q = __builtin_amdgcn_fmed3f(rintf(v[j] * a), -128.0f, 127.0f);
             const int qi = (int)q;
-            q_s[k] = (int8_t)qi;
+            q_s[col_at(ql, j, K)] = (int8_t)qi;
             cs += qi;
         }
     }
@@ -361,12 +400,14 @@ __device__ __forceinline__ void quantize(float (&v)[kCPoll], int K, const float 
 // This workgroup's outputs of a stage: quantizer lane ql < 16 ng takes group
 // ql / 16, row (ql / 4) % 4, field ql % 4; the unit partials of its row are
 // summed over K, the code sum subtracted, then the rescale (and ReLU^2 for
-// the pair).  Stores are agent-scope (the next stage polls them).
-__device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, int s, int l, int ql, const int *part,
-                                         int qsum, float a, float *out, float *y_last) {
+// the pair).  Exchange position 4 rr + f = 16 g0 + ql: the lanes store one
+// contiguous run, agent-scope (the next stage polls it); the column-order
+// copies are plain stores.
+__device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, int s, int ql, const int *part,
+                                         int qsum, float a, const float (&wm)[3], float *xout, float *out,
+                                         float *y_last) {
     if (ql >= 16 * st.ng) return;
     const int grl = ql >> 4, row = (ql >> 2) & 3, f = ql & 3;
-    const ChainLayer &w = A.layers[l];
     int acc[2] = {0, 0};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -380,21 +421,28 @@ __device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, in
     float val;
     int col;
     if (s == 2) {
-        const float gv = (float)acc[0] * (w.w_gu[0] / a);
-        const float uv = (float)acc[1] * (w.w_gu[1] / a);
+        const float gv = (float)acc[0] * (wm[0] / a);
+        const float uv = (float)acc[1] * (wm[1] / a);
         val = relu2_mul(gv, uv);
         col = f * st.R + rr;
     } else if (s == 0) {
         const ColOf c = col_of(A.seg_qkv, rr, f);
-        val = (float)acc[0] * (w.w_qkv[c.seg] / a);
+        val = (float)acc[0] * ((c.seg == 0 ? wm[0] : (c.seg == 1 ? wm[1] : wm[2])) / a);
         col = c.col;
     } else {
-        val = (float)acc[0] * ((s == 1 ? w.w_o[0] : w.w_dn[0]) / a);
+        val = (float)acc[0] * (wm[0] / a);
         col = f * st.R + rr;
     }
-    __hip_atomic_store(reinterpret_cast<unsigned *>(out) + col, __float_as_uint(val), __ATOMIC_RELAXED,
+    __hip_atomic_store(reinterpret_cast<unsigned *>(xout) + 16 * st.g0 + ql, __float_as_uint(val), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+    if (out) out[col] = val;
     if (y_last) y_last[col] = val;
+}
+
+// Offset of stage s's output (q|k|v, o, p, y) within a layer's row of the
+// exchange and stage buffers.
+__device__ __forceinline__ int stage_off(const ChainArgs &A, int s) {
+    return s == 0 ? 0 : (s == 1 ? A.H + 2 * A.KV : (s == 2 ? 2 * A.H + 2 * A.KV : 2 * A.H + 2 * A.KV + A.I));
 }
 
 struct ChainLds {
@@ -407,25 +455,29 @@ struct ChainLds {
 };
 
 // Stage s of layer l for the quantizer waves: input, codes, barrier, barrier,
-// outputs.  phantom: a layer past the end (odd layer counts), barriers only.
-__device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int l, int s, bool phantom, int qw, int ql,
-                                        ChainLds &sh, QState &qs) {
-    const Stage st = stage_of(A, geo, phantom ? A.L - 1 : l, s);
-    float *lay = A.stages + (size_t)l * A.Sw;
-    float *o_qkv = lay, *o_o = lay + (A.H + 2 * A.KV), *o_p = o_o + A.H, *o_y = o_p + A.I;
+// outputs, barrier.
+__device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int l, int s, int qw, int ql, ChainLds &sh,
+                                        QState &qs) {
+    const Stage st = stage_of(A, geo, l, s);
+    float *xl = A.xch + (size_t)l * A.Sw;
     float v[kCPoll];
-    if (!phantom) {
-        if (s == 0) {
-            if (l == 0) load_x(A, ql, v);
-            else poll(A.stages + (size_t)(l - 1) * A.Sw + (A.H + 2 * A.KV) + A.H + A.I, A.H, ql, v, qs.live);
-        } else if (s == 1) {
-            poll(o_qkv, A.H, ql, v, qs.live);
-        } else if (s == 2) {
-            poll(o_o, A.H, ql, v, qs.live);
-        } else {
-            poll(o_p, A.I, ql, v, qs.live);
-        }
+    float wm[3] = {1.0f, 1.0f, 1.0f};
+    {
+        // the epilogue's weight scales, fetched ahead of the wait
         const ChainLayer &w = A.layers[l];
+        if (s == 0) { wm[0] = w.w_qkv[0]; wm[1] = w.w_qkv[1]; wm[2] = w.w_qkv[2]; }
+        else if (s == 1) wm[0] = w.w_o[0];
+        else if (s == 2) { wm[0] = w.w_gu[0]; wm[1] = w.w_gu[1]; }
+        else wm[0] = w.w_dn[0];
+        const float *in;
+        int K;
+        if (s == 0 && l == 0) {
+            load_x(A, ql, v);
+        } else {
+            if (s == 0) { in = xl - A.Sw + stage_off(A, 3); K = A.H; }
+            else { in = xl + stage_off(A, s - 1); K = s == 3 ? A.I : A.H; }
+            poll(in, K, ql, v, qs.live);
+        }
         quantize(v, st.K, s == 2 ? w.g_sub : w.g_ffn, s >= 2, A.eps, qw, ql, sh.q_s, sh.part_d, sh.part_f, sh.qs_part,
                  sh.qflag, qs);
     }
@@ -434,43 +486,40 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
     // for the next stage only after the second one
     const int qsum = ((sh.qs_part[0] + sh.qs_part[1]) + sh.qs_part[2]) + sh.qs_part[3];
     lds_barrier();   // partial sums ready
-    if (!phantom) {
-        float *out = s == 0 ? o_qkv : (s == 1 ? o_o : (s == 2 ? o_p : o_y));
-        epilogue(A, st, s, l, ql, sh.part, qsum, qs.a, out, (s == 3 && l == A.L - 1) ? A.y : nullptr);
-    }
+    const int so = stage_off(A, s);
+    float *out = A.stages ? A.stages + (size_t)l * A.Sw + so : nullptr;
+    epilogue(A, st, s, ql, sh.part, qsum, qs.a, wm, xl + so, out, (s == 3 && l == A.L - 1) ? A.y : nullptr);
+    lds_barrier();   // outputs stored: the next stage's weights may queue behind them
 }
 
-// The stream waves' registers: the units of two layers (ring slots 0, 1).
+// The stream waves' registers: one set of unit slots per stage kind.
 struct Ring {
     v4i q[kUq], o[kUo], g[kUg], d[kUd];
 };
 
+// Stage S of layer l for the stream waves.  The next stage's units are
+// issued after the third barrier, i.e. after this stage's outputs have been
+// stored (requests leave a compute unit in issue order: stores queued behind
+// a stage of weight loads would reach the consumers that much later).  They
+// land during the next stage's poll and quantization.
 template <int S>
 __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int l, int ws, int lane, Ring &rg,
                                         const ChainLds &sh, int *part) {
-    const Stage st = stage_of(A, geo, l < A.L ? l : A.L - 1, S);
+    const Stage st = stage_of(A, geo, l, S);
+    constexpr int NS = (S + 1) & 3;
     lds_barrier();   // codes ready
     if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, part);
     if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, part);
     if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, part);
     if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, part);
     lds_barrier();   // partial sums ready
-    // refill this slot with the same stage two layers on (the last layer
-    // again past the end: the loads stay uniform, their data unused)
-    const int ln = l + 2 < A.L ? l + 2 : A.L - 1;
-    const Stage nx = stage_of(A, geo, ln, S);
-    if (S == 0) issue<kUq>(nx, ws, lane, rg.q);
-    if (S == 1) issue<kUo>(nx, ws, lane, rg.o);
-    if (S == 2) issue<kUg>(nx, ws, lane, rg.g);
-    if (S == 3) issue<kUd>(nx, ws, lane, rg.d);
-}
-
-__device__ __forceinline__ void s_issue_layer(const ChainArgs &A, const Geo &geo, int l, int ws, int lane, Ring &rg) {
-    const int lc = l < A.L ? l : A.L - 1;
-    issue<kUq>(stage_of(A, geo, lc, 0), ws, lane, rg.q);
-    issue<kUo>(stage_of(A, geo, lc, 1), ws, lane, rg.o);
-    issue<kUg>(stage_of(A, geo, lc, 2), ws, lane, rg.g);
-    issue<kUd>(stage_of(A, geo, lc, 3), ws, lane, rg.d);
+    lds_barrier();   // outputs stored
+    if (S == 3 && l + 1 >= A.L) return;   // no stage follows the last one
+    const Stage nx = stage_of(A, geo, S == 3 ? l + 1 : l, NS);
+    if (NS == 0) issue<kUq>(nx, ws, lane, rg.q);
+    if (NS == 1) issue<kUo>(nx, ws, lane, rg.o);
+    if (NS == 2) issue<kUg>(nx, ws, lane, rg.g);
+    if (NS == 3) issue<kUd>(nx, ws, lane, rg.d);
 }
 
 __global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) {
@@ -480,20 +529,14 @@ __global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) 
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
     const Geo geo = make_geo(A);
     if (wave < kCS) {
-        // stream waves: units of layers 0 and 1 first, then consume / refill
-        Ring r0, r1;
-        s_issue_layer(A, geo, 0, wave, lane, r0);
-        s_issue_layer(A, geo, 1, wave, lane, r1);
+        Ring rg;
+        issue<kUq>(stage_of(A, geo, 0, 0), wave, lane, rg.q);
         lds_barrier();   // pairs with the quantizer waves' flag set-up
-        for (int l = 0; l < A.L; l += 2) {
-            s_stage<0>(A, geo, l, wave, lane, r0, sh, sh.part);
-            s_stage<1>(A, geo, l, wave, lane, r0, sh, sh.part);
-            s_stage<2>(A, geo, l, wave, lane, r0, sh, sh.part);
-            s_stage<3>(A, geo, l, wave, lane, r0, sh, sh.part);
-            s_stage<0>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
-            s_stage<1>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
-            s_stage<2>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
-            s_stage<3>(A, geo, l + 1, wave, lane, r1, sh, sh.part);
+        for (int l = 0; l < A.L; ++l) {
+            s_stage<0>(A, geo, l, wave, lane, rg, sh, sh.part);
+            s_stage<1>(A, geo, l, wave, lane, rg, sh, sh.part);
+            s_stage<2>(A, geo, l, wave, lane, rg, sh, sh.part);
+            s_stage<3>(A, geo, l, wave, lane, rg, sh, sh.part);
         }
     } else {
         const int qw = wave - kCS, ql = threadIdx.x - kCS * 64;
@@ -501,14 +544,11 @@ __global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) 
         QState qs{1.0f, 0, true};
         lds_barrier();   // every flag zeroed before any wave waits on one
 #pragma unroll 1
-        for (int i = 0; i < 4 * (A.L + (A.L & 1)); ++i) {
-            const int l = i >> 2, s = i & 3;
-            q_stage(A, geo, l, s, l >= A.L, qw, ql, sh, qs);
-        }
+        for (int i = 0; i < 4 * A.L; ++i) q_stage(A, geo, i >> 2, i & 3, qw, ql, sh, qs);
     }
 }
 
-// Sets every word of the stage buffers to the fill pattern.
+// Sets every word of the exchange buffers to the fill pattern.
 __global__ __launch_bounds__(256) void k_chain_fill(unsigned *p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = kFill;
 }
@@ -533,13 +573,14 @@ bool chain_fits(int H, int KV, int I, int G) {
 hipError_t launch_chain_decode(const ChainParams &p, hipStream_t s) {
     ChainArgs a{};
     a.x = p.x; a.x_dt = p.x_dt; a.L = p.L; a.H = p.H; a.KV = p.KV; a.I = p.I; a.eps = p.eps;
-    a.stages = p.stages; a.Sw = (p.H + 2 * p.KV) + p.H + p.I + p.H; a.y = p.y; a.G = p.G; a.seg_qkv = p.seg_qkv;
+    a.xch = p.xch; a.stages = p.stages; a.Sw = (p.H + 2 * p.KV) + p.H + p.I + p.H; a.y = p.y; a.G = p.G;
+    a.seg_qkv = p.seg_qkv;
     for (int l = 0; l < p.L; ++l) {
         const ChainLayerPtrs &w = p.layers[l];
         a.layers[l] = ChainLayer{w.P_qkv, w.w_qkv, w.P_o, w.w_o, w.P_gu, w.w_gu, w.P_dn, w.w_dn, w.g_sub, w.g_ffn};
     }
     const size_t words = (size_t)p.L * a.Sw;
-    hipLaunchKernelGGL(k_chain_fill, dim3(256), dim3(256), 0, s, reinterpret_cast<unsigned *>(p.stages), words);
+    hipLaunchKernelGGL(k_chain_fill, dim3(256), dim3(256), 0, s, reinterpret_cast<unsigned *>(p.xch), words);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL(k_chain_decode, dim3(p.G), dim3(kCThreads), 0, s, a);
     return hipGetLastError();

@@ -279,10 +279,9 @@ int bl_ffn_chain(const void *h, int h_dtype, int M, int H, int I,
  *            g_ffn [I] RMSNorm gains or NULL (unit gain);
  *   y        out [H] fp32, the last layer's output;
  *   stages   optional out [n_layers][(H+2KV) + H + I + H] fp32: per layer the
- *            q|k|v output, o's output, ReLU^2(gate)*up and down's output (the
- *            buffers the workgroups exchange); NULL: they live in ws;
- *   ws       bl_stack_decode_workspace_bytes(n_layers, H, KV, I) bytes when
- *            stages is NULL, else unused (may be NULL).
+ *            q|k|v output, o's output, ReLU^2(gate)*up and down's output;
+ *   ws       bl_stack_decode_workspace_bytes(n_layers, H, KV, I) bytes: the
+ *            same stage outputs in the order the workgroups exchange them.
  * 1 <= n_layers <= 32; H and I multiples of 256 up to 8192, KV a multiple of
  * 16, within the kernel's per-workgroup capacity (the BitNet-2B4T shape
  * fits); the kernel needs one resident workgroup per compute unit.  Other
