@@ -58,9 +58,9 @@ namespace {
 constexpr int kCS = 12;                 // stream waves
 constexpr int kCQ = 4;                  // quantizer / epilogue waves
 constexpr int kCQL = kCQ * 64;
-constexpr int kCThreads = (kCS + kCQ) * 64;
+constexpr int kCWaves = kCS + kCQ;
+constexpr int kCThreads = kCWaves * 64;
 constexpr int kCMaxK = 8192;            // largest K: codes in LDS, polled words per lane
-constexpr int kCPoll = kCMaxK / kCQL;   // 32 polled words per quantizer lane, at most
 constexpr int kCUnit = 256;             // k bytes of a unit
 // Weight units per stream wave and stage (q|k|v, o, gate|up, down): a
 // workgroup owns at most 12 * kU units of a stage.
@@ -260,141 +260,170 @@ __device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const
     }
 }
 
+struct ChainLds {
+    float xs[kCMaxK];            // the stage input, exchange order
+    float xg[kCMaxK];            // its RMSNorm gains, exchange order
+    int8_t q_s[kCMaxK];          // its codes, column order
+    int part[kCMaxUnits * 16];   // unit partial sums
+    double red_d[kCWaves];       // per-wave sums of squares
+    float red_f[kCWaves];        // per-wave absolute maxima
+    int red_i[kCWaves];          // per-wave code sums
+};
+
 // ---------------------------------------------------------------------------
-// Quantizer-wave helpers.  Flags in LDS order the four quantizer waves among
-// themselves (the barriers would also stop the stream waves).
+// A stage's input, its normalization and its quantization.
+//
+// The quantizer waves poll the input vector (exchange order) as 16-byte
+// chunks, chunk c = ql + 256 i holding positions 4c .. 4c+3 (packed row c,
+// fields 0..3, i.e. columns f K/4 + c), and copy it to LDS; then all 16 waves
+// normalize and quantize it, thread t taking chunks t and t + 1024, so that
+// no single wave runs a long sequence of dependent instructions.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void q_publish(int *qflag, int qw, int step) {
-    asm volatile("" ::: "memory");
-    if ((threadIdx.x & 63) == 0) qflag[qw] = step;
-    asm volatile("" ::: "memory");
+constexpr int kCChunks = kCMaxK / 4 / kCQL;        // polled chunks per quantizer lane, at most
+constexpr int kCNormChunks = kCMaxK / 4 / kCThreads;   // chunks per thread in the quantization
+constexpr int kSc1 = 16;   // cache-policy operand of a buffer load: agent scope (the sc1 bit)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *p, int bytes) {
+    // raw buffer: base p, bytes in range (loads past it read zero), the data
+    // format word of gfx9-family buffer resources
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void q_wait(const int *qflag, int step) {
-    int lo = 0;
-    for (int it = 0; it < (1 << 22); ++it) {
-        asm volatile("" ::: "memory");
-        const v4i f = *reinterpret_cast<const v4i *>(qflag);
-        lo = min(min(__builtin_amdgcn_readfirstlane(f[0]), __builtin_amdgcn_readfirstlane(f[1])),
-                 min(__builtin_amdgcn_readfirstlane(f[2]), __builtin_amdgcn_readfirstlane(f[3])));
-        if (lo >= step) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    if (lo < step && (threadIdx.x & 63) == 0) atomicAdd(&g_chain_expired, 1u);
-    asm volatile("" ::: "memory");
-}
-
-// Polls the K exchange words this lane covers (position ql + 256 j) until
-// none holds the fill pattern; returns them in v.  `live` turns false after
-// an expired poll, after which later polls take what they find.
-// K is a multiple of 256, so j < K / 256 is the whole predicate (uniform);
-// every loop over j is unrolled and the loads of one poll are all in flight
-// together.
-__device__ __forceinline__ void poll(const float *in, int K, int ql, float (&v)[kCPoll], bool &live) {
-    const unsigned *p = reinterpret_cast<const unsigned *>(in) + ql;
-    const int nj = K >> 8;
-    for (int it = 0;; ++it) {
-        unsigned u[kCPoll];
+// Polls the K-word input `in` until no word of this lane's chunks holds the
+// fill pattern, then stores the chunks to xs (and the matching gains, or
+// ones, to xg).  Agent-scope loads of one poll are all in flight together.
+// `live` turns false after an expired poll; later polls take what they find.
+__device__ __forceinline__ void poll_to_lds(const float *in, int K, const float *gain, int ql, float *xs, float *xg,
+                                            bool &live) {
+    const int nc = K >> 2;
+    const int ni = (nc + kCQL - 1) / kCQL;
+    if (gain) {
+        // the gains of this lane's chunks, fetched ahead of the poll
+        float g[kCChunks][4];
 #pragma unroll
-        for (int j = 0; j < kCPoll; ++j) {
-            u[j] = 0u;
-            if (j < nj) u[j] = __hip_atomic_load(p + kCQL * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < kCChunks; ++i) {
+            const int c = ql + kCQL * i;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) g[i][f] = (i < ni && c < nc) ? gain[f * nc + c] : 1.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kCChunks; ++i) {
+            const int c = ql + kCQL * i;
+            if (i < ni && c < nc) *reinterpret_cast<float4 *>(xg + 4 * c) = float4{g[i][0], g[i][1], g[i][2], g[i][3]};
+        }
+    }
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(in, K * 4);
+    v4i u[kCChunks];
+    for (int it = 0;; ++it) {
+#pragma unroll
+        for (int i = 0; i < kCChunks; ++i) {
+            u[i] = v4i{0, 0, 0, 0};
+            if (i < ni) u[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (ql + kCQL * i) * 16, 0, kSc1);
         }
         bool missing = false;
 #pragma unroll
-        for (int j = 0; j < kCPoll; ++j) {
-            missing |= u[j] == kFill;
-            v[j] = __uint_as_float(u[j]);
+        for (int i = 0; i < kCChunks; ++i) {
+            const bool fill = (unsigned)u[i][0] == kFill || (unsigned)u[i][1] == kFill ||
+                              (unsigned)u[i][2] == kFill || (unsigned)u[i][3] == kFill;
+            missing |= (ql + kCQL * i < nc) && fill;
         }
-        if (!missing) return;
+        if (!missing) break;
         if (!live || it >= kPollMax) {
             if (live) atomicAdd(&g_chain_expired, 1u);
             live = false;
-            return;
+            break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
-}
-
-// Column of exchange position p = ql + 256 j of a K-wide vector (one
-// segment, K / 4 packed rows): field p % 4 of packed row p / 4.
-__device__ __forceinline__ int col_at(int ql, int j, int K) { return (ql & 3) * (K >> 2) + (ql >> 2) + 64 * j; }
-
-// The layer input x (the caller's fp32 or bf16 row, plain loads), in the
-// exchange order of the polled stages.
-__device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float (&v)[kCPoll]) {
-    const int nj = A.H >> 8;
-    if (A.x_dt == BL_BF16) {
-        const uint16_t *xb = static_cast<const uint16_t *>(A.x);
 #pragma unroll
-        for (int j = 0; j < kCPoll; ++j) v[j] = j < nj ? bf16_to_f32(xb[col_at(ql, j, A.H)]) : 0.0f;
-    } else {
-        const float *xf = static_cast<const float *>(A.x);
-#pragma unroll
-        for (int j = 0; j < kCPoll; ++j) v[j] = j < nj ? xf[col_at(ql, j, A.H)] : 0.0f;
+    for (int i = 0; i < kCChunks; ++i) {
+        const int c = ql + kCQL * i;
+        if (i < ni && c < nc) *reinterpret_cast<v4i *>(xs + 4 * c) = u[i];
     }
 }
 
-struct QState {
-    float a;      // this stage's activation scale
-    int step;     // quantizer-wave flag steps published so far
-    bool live;    // polls still wait
-};
+// The first layer's input x (the caller's fp32 or bf16 row, column order),
+// stored to xs in exchange order; xg is unused (stage 0 has no norm).
+__device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float *xs) {
+    const int nc = A.H >> 2;
+    for (int c = ql; c < nc; c += kCQL) {
+        float t[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int k = f * nc + c;
+            t[f] = A.x_dt == BL_BF16 ? bf16_to_f32(static_cast<const uint16_t *>(A.x)[k])
+                                     : static_cast<const float *>(A.x)[k];
+        }
+        *reinterpret_cast<float4 *>(xs + 4 * c) = float4{t[0], t[1], t[2], t[3]};
+    }
+}
 
-// Normalizes (optionally) and quantizes the K values in v (exchange order):
-// codes to q_s in column order, the scale to st.a, this wave's code sum to
-// qs_part[qw] (summed after the first barrier).  Same arithmetic as the row kernel: fp64 sum of squares,
-// r = float(1 / sqrt(ss / K + eps)), (h * r) * g, a = 127 / max(amax, 1e-5),
-// q = clamp(rint(x * a)).
-__device__ __forceinline__ void quantize(float (&v)[kCPoll], int K, const float *gain, bool norm, float eps, int qw,
-                                         int ql, int8_t *q_s, double *part_d, float *part_f, int *qs_part,
-                                         int *qflag, QState &qs) {
-    const int nj = K >> 8;
+// All 16 waves: normalizes (optionally) and quantizes the K values in xs:
+// codes to q_s in column order, this wave's code sum to red_i[wave]; returns
+// the activation scale.  Same arithmetic as the row kernel: fp64 sum of
+// squares, r = float(1 / sqrt(ss / K + eps)), (h * r) * g (g = 1 without a
+// gain), a = 127 / max(amax, 1e-5), q = clamp(rint(x * a)).  The sums run in
+// a fixed order (per thread, the wave, then the 16 waves in order).
+__device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, float eps, ChainLds &sh) {
+    const int t = threadIdx.x, wave = t >> 6;
+    const int nc = K >> 2;
+    float v[kCNormChunks][4];
+#pragma unroll
+    for (int i = 0; i < kCNormChunks; ++i) {
+        const int c = t + kCThreads * i;
+        const float4 x = c < nc ? *reinterpret_cast<const float4 *>(sh.xs + 4 * c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+        v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
+    }
     if (norm) {
         double ss = 0.0;
 #pragma unroll
-        for (int j = 0; j < kCPoll; ++j)
-            if (j < nj) ss += (double)v[j] * (double)v[j];
+        for (int i = 0; i < kCNormChunks; ++i)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) ss += (double)v[i][f] * (double)v[i][f];
         ss = wave_sum_d(ss);
-        if ((threadIdx.x & 63) == 0) part_d[qw] = ss;
-        q_publish(qflag, qw, ++qs.step);
-        q_wait(qflag, qs.step);
-        const double t = ((part_d[0] + part_d[1]) + part_d[2]) + part_d[3];
-        const float r = (float)(1.0 / sqrt(t / (double)K + (double)eps));
-        if (gain) {
-            float gv[kCPoll];
+        if ((t & 63) == 0) sh.red_d[wave] = ss;
+        lds_barrier();
+        double tot = 0.0;
 #pragma unroll
-            for (int j = 0; j < kCPoll; ++j) gv[j] = j < nj ? gain[col_at(ql, j, K)] : 1.0f;
+        for (int w = 0; w < kCWaves; ++w) tot += sh.red_d[w];
+        const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
 #pragma unroll
-            for (int j = 0; j < kCPoll; ++j) v[j] = (v[j] * r) * gv[j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < kCPoll; ++j) v[j] = v[j] * r;
+        for (int i = 0; i < kCNormChunks; ++i) {
+            const int c = t + kCThreads * i;
+            float4 g{1.0f, 1.0f, 1.0f, 1.0f};
+            if (has_gain && c < nc) g = *reinterpret_cast<const float4 *>(sh.xg + 4 * c);
+            v[i][0] = (v[i][0] * r) * g.x; v[i][1] = (v[i][1] * r) * g.y;
+            v[i][2] = (v[i][2] * r) * g.z; v[i][3] = (v[i][3] * r) * g.w;
         }
     }
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kCPoll; ++j)
-        if (j < nj) am = fmaxf(am, fabsf(v[j]));
+    for (int i = 0; i < kCNormChunks; ++i)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) am = fmaxf(am, fabsf(v[i][f]));
     am = wave_max(am);
-    if ((threadIdx.x & 63) == 0) part_f[qw] = am;
-    q_publish(qflag, qw, ++qs.step);
-    q_wait(qflag, qs.step);
-    const float mx = fmaxf(fmaxf(part_f[0], part_f[1]), fmaxf(part_f[2], part_f[3]));
+    if ((t & 63) == 0) sh.red_f[wave] = am;
+    lds_barrier();
+    float mx = sh.red_f[0];
+#pragma unroll
+    for (int w = 1; w < kCWaves; ++w) mx = fmaxf(mx, sh.red_f[w]);
     const float a = 127.0f / fmaxf(mx, 1e-5f);
-    qs.a = a;
     int cs = 0;
 #pragma unroll
-    for (int j = 0; j < kCPoll; ++j) {
-        if (j < nj) {
-            const float q = __builtin_amdgcn_fmed3f(rintf(v[j] * a), -128.0f, 127.0f);
-            const int qi = (int)q;
-            q_s[col_at(ql, j, K)] = (int8_t)qi;
-            cs += qi;
+    for (int i = 0; i < kCNormChunks; ++i) {
+        const int c = t + kCThreads * i;
+        if (c < nc) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int qi = (int)__builtin_amdgcn_fmed3f(rintf(v[i][f] * a), -128.0f, 127.0f);
+                sh.q_s[f * nc + c] = (int8_t)qi;
+                cs += qi;
+            }
         }
     }
     cs = wave_sum_i(cs);
-    if ((threadIdx.x & 63) == 0) qs_part[qw] = cs;
+    if ((t & 63) == 0) sh.red_i[wave] = cs;
+    return a;
 }
 
 // This workgroup's outputs of a stage: quantizer lane ql < 16 ng takes group
@@ -445,22 +474,21 @@ __device__ __forceinline__ int stage_off(const ChainArgs &A, int s) {
     return s == 0 ? 0 : (s == 1 ? A.H + 2 * A.KV : (s == 2 ? 2 * A.H + 2 * A.KV : 2 * A.H + 2 * A.KV + A.I));
 }
 
-struct ChainLds {
-    int8_t q_s[kCMaxK];
-    int part[kCMaxUnits * 16];
-    double part_d[kCQ];
-    float part_f[kCQ];
-    int qs_part[kCQ];
-    int qflag[kCQ];
-};
+__device__ __forceinline__ int stage_k(const ChainArgs &A, int s) { return s == 3 ? A.I : A.H; }
 
-// Stage s of layer l for the quantizer waves: input, codes, barrier, barrier,
-// outputs, barrier.
-__device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int l, int s, int qw, int ql, ChainLds &sh,
-                                        QState &qs) {
+__device__ __forceinline__ const float *stage_gain(const ChainArgs &A, int l, int s) {
+    return s == 2 ? A.layers[l].g_sub : (s == 3 ? A.layers[l].g_ffn : nullptr);
+}
+
+// Stage s of layer l for the quantizer waves: input to LDS, barrier, the
+// shared quantization, barrier (codes), barrier (partial sums), outputs,
+// barrier (outputs stored).
+__device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int l, int s, int ql, ChainLds &sh,
+                                        bool &live) {
     const Stage st = stage_of(A, geo, l, s);
     float *xl = A.xch + (size_t)l * A.Sw;
-    float v[kCPoll];
+    const int K = stage_k(A, s);
+    const float *gain = stage_gain(A, l, s);
     float wm[3] = {1.0f, 1.0f, 1.0f};
     {
         // the epilogue's weight scales, fetched ahead of the wait
@@ -469,26 +497,23 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
         else if (s == 1) wm[0] = w.w_o[0];
         else if (s == 2) { wm[0] = w.w_gu[0]; wm[1] = w.w_gu[1]; }
         else wm[0] = w.w_dn[0];
-        const float *in;
-        int K;
-        if (s == 0 && l == 0) {
-            load_x(A, ql, v);
-        } else {
-            if (s == 0) { in = xl - A.Sw + stage_off(A, 3); K = A.H; }
-            else { in = xl + stage_off(A, s - 1); K = s == 3 ? A.I : A.H; }
-            poll(in, K, ql, v, qs.live);
-        }
-        quantize(v, st.K, s == 2 ? w.g_sub : w.g_ffn, s >= 2, A.eps, qw, ql, sh.q_s, sh.part_d, sh.part_f, sh.qs_part,
-                 sh.qflag, qs);
     }
+    if (s == 0 && l == 0) {
+        load_x(A, ql, sh.xs);
+    } else {
+        const float *in = s == 0 ? xl - A.Sw + stage_off(A, 3) : xl + stage_off(A, s - 1);
+        poll_to_lds(in, K, gain, ql, sh.xs, sh.xg, live);
+    }
+    lds_barrier();   // input in LDS
+    const float a = quantize_all(K, s >= 2, gain != nullptr, A.eps, sh);
     lds_barrier();   // codes ready
-    // the code sums are read between the barriers: a wave rewrites its entry
-    // for the next stage only after the second one
-    const int qsum = ((sh.qs_part[0] + sh.qs_part[1]) + sh.qs_part[2]) + sh.qs_part[3];
     lds_barrier();   // partial sums ready
+    int qsum = 0;
+#pragma unroll
+    for (int w = 0; w < kCWaves; ++w) qsum += sh.red_i[w];
     const int so = stage_off(A, s);
     float *out = A.stages ? A.stages + (size_t)l * A.Sw + so : nullptr;
-    epilogue(A, st, s, ql, sh.part, qsum, qs.a, wm, xl + so, out, (s == 3 && l == A.L - 1) ? A.y : nullptr);
+    epilogue(A, st, s, ql, sh.part, qsum, a, wm, xl + so, out, (s == 3 && l == A.L - 1) ? A.y : nullptr);
     lds_barrier();   // outputs stored: the next stage's weights may queue behind them
 }
 
@@ -497,21 +522,23 @@ struct Ring {
     v4i q[kUq], o[kUo], g[kUg], d[kUd];
 };
 
-// Stage S of layer l for the stream waves.  The next stage's units are
-// issued after the third barrier, i.e. after this stage's outputs have been
-// stored (requests leave a compute unit in issue order: stores queued behind
-// a stage of weight loads would reach the consumers that much later).  They
-// land during the next stage's poll and quantization.
+// Stage S of layer l for the stream waves: the shared quantization, the
+// products, and then the next stage's weights, issued after the outputs have
+// been stored (requests leave a compute unit in issue order: stores queued
+// behind a stage of weight loads would reach the consumers that much later).
+// The weights land during the next stage's poll and quantization.
 template <int S>
 __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int l, int ws, int lane, Ring &rg,
-                                        const ChainLds &sh, int *part) {
+                                        ChainLds &sh) {
     const Stage st = stage_of(A, geo, l, S);
     constexpr int NS = (S + 1) & 3;
+    lds_barrier();   // input in LDS
+    (void)quantize_all(stage_k(A, S), S >= 2, stage_gain(A, l, S) != nullptr, A.eps, sh);
     lds_barrier();   // codes ready
-    if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, part);
-    if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, part);
-    if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, part);
-    if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, part);
+    if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, sh.part);
+    if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, sh.part);
+    if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, sh.part);
+    if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, sh.part);
     lds_barrier();   // partial sums ready
     lds_barrier();   // outputs stored
     if (S == 3 && l + 1 >= A.L) return;   // no stage follows the last one
@@ -531,20 +558,17 @@ __global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) 
     if (wave < kCS) {
         Ring rg;
         issue<kUq>(stage_of(A, geo, 0, 0), wave, lane, rg.q);
-        lds_barrier();   // pairs with the quantizer waves' flag set-up
         for (int l = 0; l < A.L; ++l) {
-            s_stage<0>(A, geo, l, wave, lane, rg, sh, sh.part);
-            s_stage<1>(A, geo, l, wave, lane, rg, sh, sh.part);
-            s_stage<2>(A, geo, l, wave, lane, rg, sh, sh.part);
-            s_stage<3>(A, geo, l, wave, lane, rg, sh, sh.part);
+            s_stage<0>(A, geo, l, wave, lane, rg, sh);
+            s_stage<1>(A, geo, l, wave, lane, rg, sh);
+            s_stage<2>(A, geo, l, wave, lane, rg, sh);
+            s_stage<3>(A, geo, l, wave, lane, rg, sh);
         }
     } else {
-        const int qw = wave - kCS, ql = threadIdx.x - kCS * 64;
-        if (lane == 0) sh.qflag[qw] = 0;
-        QState qs{1.0f, 0, true};
-        lds_barrier();   // every flag zeroed before any wave waits on one
+        const int ql = threadIdx.x - kCS * 64;
+        bool live = true;
 #pragma unroll 1
-        for (int i = 0; i < 4 * A.L; ++i) q_stage(A, geo, i >> 2, i & 3, qw, ql, sh, qs);
+        for (int i = 0; i < 4 * A.L; ++i) q_stage(A, geo, i >> 2, i & 3, ql, sh, live);
     }
 }
 
