@@ -79,6 +79,11 @@ def _load():
         "ora_attn_prefill_f64": (None, [P, P, P, I, I, I, I, ctypes.c_double, P, I, P]),
         "ora_ste_grad_input_rows": (None, [P, I, I, P, I, F, P, I, P]),
         "ora_ste_grad_weight_rows": (None, [P, I, I, P, P, I, P, I, P]),
+        "ora_binarize": (None, [P, L, P]),
+        "ora_pack_bits": (None, [P, I, I, P]),
+        "ora_unpack_bits": (None, [P, I, I, P]),
+        "ora_layernorm": (None, [P, I, I, P, P, F, P]),
+        "ora_bitlinear_w1": (None, [P, I, I, P, P, F, P, I, F, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -413,3 +418,63 @@ def ste_grad_weight(dy, q, a, rows=None) -> np.ndarray:
     out = np.empty((r.size, K), np.float64)
     _load().ora_ste_grad_weight_rows(_p(dy), M, N, _p(q), _p(a), K, _p(r), r.size, _p(out))
     return out
+
+
+# ---------------------------------------------------------------------------
+# The 1-bit BitLinear (binarized weights): layer norm, signs with one scale
+# per tensor, absmax int8 activations.
+# ---------------------------------------------------------------------------
+def binarize_pack(W):
+    """(packed [N/8,K] uint8, w_scale float32, signs [N,K] int8) for one tensor."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    assert N % 8 == 0
+    signs = np.empty((N, K), np.int8)
+    _load().ora_binarize(_p(W), W.size, _p(signs))
+    packed = np.empty((N // 8, K), np.uint8)
+    _load().ora_pack_bits(_p(signs), N, K, _p(packed))
+    return packed, weight_mean(W), signs
+
+
+def unpack_bits(packed, N=None):
+    packed = _c(packed, np.uint8)
+    R, K = packed.shape
+    N = 8 * R if N is None else N
+    signs = np.empty((N, K), np.int8)
+    _load().ora_unpack_bits(_p(packed), N, K, _p(signs))
+    return signs
+
+
+def layernorm(x, gamma=None, beta=None, eps=1e-5) -> np.ndarray:
+    x = _c(x, np.float32)
+    M, K = x.shape
+    gamma = None if gamma is None else _c(gamma, np.float32)
+    beta = None if beta is None else _c(beta, np.float32)
+    out = np.empty((M, K), np.float32)
+    _load().ora_layernorm(_p(x), M, K, _p(gamma), _p(beta), float(np.float32(eps)), _p(out))
+    return out
+
+
+def bitlinear_w1(x, signs, w_scale, gamma=None, beta=None, eps=1e-5):
+    """(q, a, A, y) of one 1-bit BitLinear forward on fp32 x [M,K], signs [N,K]."""
+    x = _c(x, np.float32)
+    signs = _c(signs, np.int8)
+    M, K = x.shape
+    N = signs.shape[0]
+    gamma = None if gamma is None else _c(gamma, np.float32)
+    beta = None if beta is None else _c(beta, np.float32)
+    q = np.empty((M, K), np.int8)
+    a = np.empty(M, np.float32)
+    A = np.empty((M, N), np.int32)
+    y = np.empty((M, N), np.float32)
+    _load().ora_bitlinear_w1(_p(x), M, K, _p(gamma), _p(beta), float(np.float32(eps)), _p(signs), N,
+                             float(np.float32(w_scale)), _p(q), _p(a), _p(A), _p(y))
+    return q, a, A, y
+
+
+def bitlinear_w1_f64gemm(x, signs, w_scale, gamma=None, beta=None, eps=1e-5):
+    """``bitlinear_w1`` with the contraction taken by ``contract_f64`` (exact:
+    |q| <= 128, |sign| = 1, integer partial sums below 2^53)."""
+    q, a = quant_act(layernorm(x, gamma, beta, eps))
+    A = contract_f64(q, signs)
+    return q, a, A, rescale(A, a, [signs.shape[0]], w_scale)

@@ -508,3 +508,101 @@ void ora_ste_grad_weight_rows(const float *dy, int M, int N, const int8_t *q, co
         }
     }
 }
+
+/* ===========================================================================
+ * The 1-bit BitLinear (binarized weights).
+ *  [S] project summary of a PyTorch "BitNet" implementation of 1-bit
+ *      Transformers, section "How It Works": the BitLinear that replaces a
+ *      linear layer quantizes its weights to one bit by binarization, and
+ *      its input through layer normalization followed by absolute-maximum
+ *      quantization.
+ * The page prints no formula.  Readings (also in the design notes):
+ *  - weight: sign(W), negative -> -1, anything else (zero included) -> +1;
+ *    one scale per tensor, the mean of |W| as for the ternary scale
+ *    (ora_weight_mean: fp64 sum in index order, fp32, floor 1e-5);
+ *  - packing: one bit per weight, plane order: bit i of packed row r holds
+ *    weight row i*N/8 + r (1 for +1, 0 for -1); N % 8 == 0;
+ *  - layer normalization per token over K, with optional gain and bias:
+ *      mu  = sum_k x / K                    (fp64, index order)
+ *      var = sum_k (x - mu)^2 / K           (fp64, index order)
+ *      r   = float(1 / sqrt(var + eps))     (fp64, then fp32)
+ *      out = (float(x - mu) * r) * gamma + beta   (fp32, no FMA)
+ *  - activations: the per-token absmax int8 quantization of the ternary
+ *    path (ora_quant_act);
+ *  - output: y = float(A) * (w_scale / a), A = sum_k q * sign (ora_rescale).
+ * ------------------------------------------------------------------------ */
+
+/* Binarization ([S] "How It Works"): -1 where W < 0, else +1. */
+void ora_binarize(const float *W, int64_t count, int8_t *signs)
+{
+    for (int64_t i = 0; i < count; ++i)
+        signs[i] = W[i] < 0.0f ? (int8_t)-1 : (int8_t)1;
+}
+
+/* One bit per weight, plane order (reading above).  signs: [N,K] in {-1,+1};
+ * packed: [N/8,K]. */
+void ora_pack_bits(const int8_t *signs, int N, int K, uint8_t *packed)
+{
+    int R = N / 8;
+    for (int r = 0; r < R; ++r)
+        for (int k = 0; k < K; ++k) {
+            unsigned byte = 0;
+            for (int i = 0; i < 8; ++i)
+                if (signs[(int64_t)(i * R + r) * K + k] > 0)
+                    byte |= 1u << i;
+            packed[(int64_t)r * K + k] = (uint8_t)byte;
+        }
+}
+
+/* Inverse of ora_pack_bits. */
+void ora_unpack_bits(const uint8_t *packed, int N, int K, int8_t *signs)
+{
+    int R = N / 8;
+    for (int r = 0; r < R; ++r)
+        for (int k = 0; k < K; ++k) {
+            unsigned byte = packed[(int64_t)r * K + k];
+            for (int i = 0; i < 8; ++i)
+                signs[(int64_t)(i * R + r) * K + k] = ((byte >> i) & 1u) ? (int8_t)1 : (int8_t)-1;
+        }
+}
+
+/* Layer normalization ([S] "How It Works"; formula as read above).
+ * gamma / beta may be NULL (1 and 0). */
+void ora_layernorm(const float *x, int M, int K, const float *gamma, const float *beta, float eps, float *out)
+{
+    for (int m = 0; m < M; ++m) {
+        const float *row = x + (int64_t)m * K;
+        double s = 0.0;
+        for (int k = 0; k < K; ++k)
+            s += (double)row[k];
+        double mu = s / (double)K;
+        double ss = 0.0;
+        for (int k = 0; k < K; ++k) {
+            double d = (double)row[k] - mu;
+            ss += d * d;
+        }
+        float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+        for (int k = 0; k < K; ++k) {
+            float v = (float)((double)row[k] - mu) * r;
+            if (gamma) v = v * gamma[k];
+            if (beta) v = v + beta[k];
+            out[(int64_t)m * K + k] = v;
+        }
+    }
+}
+
+/* One 1-bit BitLinear forward ([S] "How It Works", steps in the order the
+ * page names them): layer norm -> absmax int8 -> product with the signs ->
+ * rescale by the weight scale and the activation scale.
+ * Outputs q [M,K], a [M], A [M,N], y [M,N]. */
+void ora_bitlinear_w1(const float *x, int M, int K, const float *gamma, const float *beta, float eps,
+                      const int8_t *signs, int N, float w_scale, int8_t *q, float *a, int32_t *A, float *y)
+{
+    float *xn = (float *)malloc(sizeof(float) * (size_t)M * K);
+    int seg[1] = {N};
+    ora_layernorm(x, M, K, gamma, beta, eps, xn);
+    ora_quant_act(xn, M, K, q, a);
+    ora_contract(q, M, K, signs, N, A);
+    ora_rescale(A, M, N, a, 1, seg, &w_scale, y);
+    free(xn);
+}
