@@ -53,6 +53,11 @@ class GemvProblem(ctypes.Structure):
                 ("y", _P), ("y_dtype", _I)]
 
 
+class W1Problem(ctypes.Structure):
+    _fields_ = [("x", _P), ("x_dtype", _I), ("M", _I), ("K", _I), ("gamma", _P), ("beta", _P),
+                ("packed", _P), ("N", _I), ("w_scale", _P), ("y", _P)]
+
+
 MAX_PROBLEMS = 8
 
 
@@ -93,6 +98,12 @@ _SIGS = {
     "bl_rope_table": (_I, [_I, _I, ctypes.c_double, _P, _P]),
     "bl_attn_decode_workspace_bytes": (_S, [_I, _I]),
     "bl_attn_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _S, _P]),
+    "bl_binarize_workspace_bytes": (_S, [_L, _L]),
+    "bl_binarize_pack": (_I, [_P, _I, _I, _P, _P, _P, _S, _P]),
+    "bl_layernorm_quant": (_I, [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P]),
+    "bl_gemm_w1a8": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P]),
+    "bl_bitlinear_w1_workspace_bytes": (_S, [ctypes.POINTER(W1Problem), _I]),
+    "bl_bitlinear_w1": (_I, [ctypes.POINTER(W1Problem), _I, _F, _P, _S, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(raw, _name)
@@ -598,3 +609,92 @@ def ste_grad_weight(dy, q, a, dw=None):
     _check(raw.bl_ste_grad_weight(_ptr(dy), _dt(dy), _ptr(q), _ptr(a), M, N, K, _ptr(dw), _ptr(ws), ws.numel(),
                                   _stream(dev)))
     return dw
+
+
+# ---------------------------------------------------------------------------
+# The 1-bit BitLinear.
+# ---------------------------------------------------------------------------
+def binarize_pack(W: torch.Tensor, packed: torch.Tensor = None, w_scale: torch.Tensor = None):
+    """W fp32 [N,K] -> (packed uint8 [N/8,K], w_scale fp32 [1])."""
+    dev = _dev(W)
+    N, K = W.shape
+    _need(W, (N, K), (torch.float32,), "W")
+    if packed is None:
+        packed = torch.empty((N // 8, K), dtype=torch.uint8, device=dev)
+    if w_scale is None:
+        w_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    _need(packed, (N // 8, K), (torch.uint8,), "packed")
+    _need(w_scale, (1,), (torch.float32,), "w_scale")
+    ws = workspace(dev, raw.bl_binarize_workspace_bytes(N, K))
+    _check(raw.bl_binarize_pack(_ptr(W), N, K, _ptr(packed), _ptr(w_scale), _ptr(ws), ws.numel(), _stream(dev)))
+    return packed, w_scale
+
+
+def layernorm_quant(x: torch.Tensor, gamma=None, beta=None, eps: float = 1e-5, q=None, a=None):
+    """x [M,K] fp32/bf16 (row stride may exceed K) -> (q int8 [M,K], a fp32 [M])."""
+    dev = _dev(x)
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    if a is None:
+        a = torch.empty(M, dtype=torch.float32, device=dev)
+    _need(q, (M, K), (torch.int8,), "q")
+    _need(a, (M,), (torch.float32,), "a")
+    for t, nm in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _need(t, (K,), (torch.float32,), nm)
+    _check(raw.bl_layernorm_quant(_ptr(x), _dt(x), M, K, x.stride(0), _ptr(gamma), _ptr(beta), float(eps),
+                                  _ptr(q), _ptr(a), _stream(dev)))
+    return q, a
+
+
+def gemm_w1a8(q: torch.Tensor, a: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor, N: int = None,
+              y: torch.Tensor = None):
+    """Codes q int8 [M,K] with scales a [M] times packed signs [N/8,K] -> y fp32 [M,N]."""
+    dev = _dev(q, a, packed, w_scale)
+    M, K = q.shape
+    N = 8 * packed.shape[0] if N is None else N
+    _need(q, (M, K), (torch.int8,), "q")
+    _need(a, (M,), (torch.float32,), "a")
+    _need(packed, (N // 8, K), (torch.uint8,), "packed")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(y, (M, N), (torch.float32,), "y")
+    _check(raw.bl_gemm_w1a8(_ptr(q), _ptr(a), M, K, _ptr(packed), N, _ptr(w_scale), _ptr(y), _stream(dev)))
+    return y
+
+
+def bitlinear_w1_batched(problems, eps: float = 1e-5):
+    """Up to 8 forwards in two launches; each problem a dict with x [M,K]
+    (fp32/bf16, contiguous), packed [N/8,K], w_scale [1], y fp32 [M,N] and
+    optional gamma / beta [K]."""
+    if not 1 <= len(problems) <= MAX_PROBLEMS:
+        raise ValueError(f"1..{MAX_PROBLEMS} problems per call")
+    arr = (W1Problem * len(problems))()
+    dev = None
+    for i, pr in enumerate(problems):
+        x, packed, y = pr["x"], pr["packed"], pr["y"]
+        dev = _dev(x, packed, y, pr["w_scale"])
+        M, K = x.shape
+        N = y.shape[1]
+        _need(x, (M, K), (torch.float32, torch.bfloat16), "x")
+        _need(packed, (N // 8, K), (torch.uint8,), "packed")
+        _need(y, (M, N), (torch.float32,), "y")
+        arr[i] = W1Problem(x.data_ptr(), _dt(x), M, K, _ptr(pr.get("gamma")), _ptr(pr.get("beta")),
+                           packed.data_ptr(), N, pr["w_scale"].data_ptr(), y.data_ptr())
+    ws = workspace(dev, raw.bl_bitlinear_w1_workspace_bytes(arr, len(problems)))
+    _check(raw.bl_bitlinear_w1(arr, len(problems), float(eps), _ptr(ws), ws.numel(), _stream(dev)))
+    return [pr["y"] for pr in problems]
+
+
+def bitlinear_w1(x: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor, gamma=None, beta=None,
+                 eps: float = 1e-5, y: torch.Tensor = None):
+    """One 1-bit BitLinear forward: x [M,K] -> y fp32 [M, 8 * packed rows]."""
+    M = x.shape[0]
+    N = 8 * packed.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    bitlinear_w1_batched([dict(x=x, packed=packed, w_scale=w_scale, y=y, gamma=gamma, beta=beta)], eps)
+    return y

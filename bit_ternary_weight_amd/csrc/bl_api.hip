@@ -938,4 +938,124 @@ int bl_ste_grad_weight(const void *dy, int dy_dtype, const int8_t *q, const floa
                      fn);
 }
 
+// ---------------------------------------------------------------------------
+// The 1-bit BitLinear.
+// ---------------------------------------------------------------------------
+size_t bl_binarize_workspace_bytes(int64_t N, int64_t K) { return bl_ternarize_workspace_bytes(N, K); }
+
+int bl_binarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_scale, void *ws, size_t ws_bytes,
+                     bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_binarize_pack";
+    if (!W || !packed || !w_scale || !ws) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (N < 8 || N % 8 != 0 || K < 4 || K % 4 != 0)
+        return fail(BL_ERR_SHAPE, "%s: N=%d (a positive multiple of 8), K=%d (a positive multiple of 4)", fn, N, K);
+    if ((int64_t)N * K >= ((int64_t)1 << 40)) return fail(BL_ERR_SHAPE, "%s: N*K too large", fn);
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(ws, 16) || !aligned(w_scale, 4))
+        return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (int e = check_ws(fn, ws, ws_bytes, bl_binarize_workspace_bytes(N, K))) return e;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t count = (int64_t)N * K;
+    if (int st = check_hip(bl::launch_absmean(W, count, (double *)ws, bl::absmean_parts(count), w_scale, s), fn))
+        return st;
+    return check_hip(bl::launch_binarize_pack(W, N, K, packed, s), fn);
+}
+
+// Shape and pointer checks of one 1-bit problem; `norm`: x is read (else q).
+static int w1_check(const char *fn, int i, const void *x, int x_dtype, int M, int K, int ldx, const float *gamma,
+                    const float *beta, const uint8_t *packed, int N, const float *w_scale, const float *y,
+                    bool norm, bool gemm) {
+    if (M < 1 || K < 4 || K % 4 != 0) return fail(BL_ERR_SHAPE, "%s: problem %d: M=%d K=%d", fn, i, M, K);
+    if (norm) {
+        if (!x) return fail(BL_ERR_NULL, "%s: problem %d: NULL x", fn, i);
+        if (x_dtype != BL_F32 && x_dtype != BL_BF16)
+            return fail(BL_ERR_DTYPE, "%s: problem %d: x dtype %d not allowed", fn, i, x_dtype);
+        if (K > bl::w1_ln_max_k()) return fail(BL_ERR_SHAPE, "%s: problem %d: K=%d above %d", fn, i, K, bl::w1_ln_max_k());
+        if (ldx < K || ldx % 4 != 0) return fail(BL_ERR_SHAPE, "%s: problem %d: ldx=%d", fn, i, ldx);
+        if (!aligned(x, 16) || (gamma && !aligned(gamma, 16)) || (beta && !aligned(beta, 16)))
+            return fail(BL_ERR_ALIGN, "%s: problem %d: misaligned x, gamma or beta", fn, i);
+    }
+    if (gemm) {
+        if (!packed || !w_scale || !y) return fail(BL_ERR_NULL, "%s: problem %d: NULL pointer", fn, i);
+        if (K % 16 != 0 || K < 16 || K > 16384 || N < 8 || N % 8 != 0)
+            return fail(BL_ERR_SHAPE, "%s: problem %d: K=%d (16..16384, a multiple of 16), N=%d (a multiple of 8)",
+                        fn, i, K, N);
+        if ((int64_t)M * N >= ((int64_t)1 << 40)) return fail(BL_ERR_SHAPE, "%s: problem %d: M*N too large", fn, i);
+        if (!aligned(packed, 16) || !aligned(w_scale, 4) || !aligned(y, 4))
+            return fail(BL_ERR_ALIGN, "%s: problem %d: misaligned packed, w_scale or y", fn, i);
+    }
+    return 0;
+}
+
+int bl_layernorm_quant(const void *x, int x_dtype, int M, int K, int ldx, const float *gamma, const float *beta,
+                       float eps, int8_t *q, float *a, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_layernorm_quant";
+    if (!q || !a) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (ldx == 0) ldx = K;
+    if (int e = w1_check(fn, 0, x, x_dtype, M, K, ldx, gamma, beta, nullptr, 0, nullptr, nullptr, true, false))
+        return e;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return fail(BL_ERR_SHAPE, "%s: eps=%g", fn, (double)eps);
+    if (!aligned(q, 16) || !aligned(a, 4)) return fail(BL_ERR_ALIGN, "%s: misaligned q or a", fn);
+    bl::W1Args w{x, x_dtype, ldx, gamma, beta, M, K, q, a, nullptr, 0, nullptr, nullptr};
+    return check_hip(bl::launch_w1_norm(&w, 1, eps, (hipStream_t)stream), fn);
+}
+
+int bl_gemm_w1a8(const int8_t *q, const float *a, int M, int K, const uint8_t *packed, int N, const float *w_scale,
+                 float *y, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_gemm_w1a8";
+    if (!q || !a) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
+    if (int e = w1_check(fn, 0, nullptr, 0, M, K, K, nullptr, nullptr, packed, N, w_scale, y, false, true)) return e;
+    if (!aligned(q, 16) || !aligned(a, 4)) return fail(BL_ERR_ALIGN, "%s: misaligned q or a", fn);
+    bl::W1Args w{nullptr, 0, K, nullptr, nullptr, M, K, const_cast<int8_t *>(q), const_cast<float *>(a), packed, N,
+                 w_scale, y};
+    return check_hip(bl::launch_w1_gemm(&w, 1, (hipStream_t)stream), fn);
+}
+
+// Workspace of bl_bitlinear_w1: per problem the codes (M*K bytes) and the
+// scales (M floats), each 256-byte aligned.
+static size_t w1_ws_layout(const bl_w1_problem *probs, int n, size_t *q_off, size_t *a_off) {
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+        const size_t M = probs[i].M > 0 ? (size_t)probs[i].M : 0, K = probs[i].K > 0 ? (size_t)probs[i].K : 0;
+        if (q_off) q_off[i] = off;
+        off += align256(M * K);
+        if (a_off) a_off[i] = off;
+        off += align256(M * sizeof(float));
+    }
+    return off;
+}
+
+size_t bl_bitlinear_w1_workspace_bytes(const bl_w1_problem *probs, int n) {
+    if (!probs || n < 1 || n > bl::kMaxProblems) return 0;
+    return w1_ws_layout(probs, n, nullptr, nullptr);
+}
+
+int bl_bitlinear_w1(const bl_w1_problem *probs, int n, float eps, void *ws, size_t ws_bytes, bl_stream stream) {
+    g_err[0] = 0;
+    const char *fn = "bl_bitlinear_w1";
+    if (!probs) return fail(BL_ERR_NULL, "%s: NULL problem table", fn);
+    if (n < 1 || n > bl::kMaxProblems) return fail(BL_ERR_SHAPE, "%s: n=%d (1..%d)", fn, n, bl::kMaxProblems);
+    if (!(eps >= 0.0f) || !isfinite(eps)) return fail(BL_ERR_SHAPE, "%s: eps=%g", fn, (double)eps);
+    for (int i = 0; i < n; ++i) {
+        const bl_w1_problem &p = probs[i];
+        if (int e = w1_check(fn, i, p.x, p.x_dtype, p.M, p.K, p.K, p.gamma, p.beta, p.packed, p.N, p.w_scale, p.y,
+                             true, true))
+            return e;
+    }
+    if (int e = check_ws(fn, ws, ws_bytes, bl_bitlinear_w1_workspace_bytes(probs, n))) return e;
+    size_t q_off[bl::kMaxProblems], a_off[bl::kMaxProblems];
+    w1_ws_layout(probs, n, q_off, a_off);
+    bl::W1Args w[bl::kMaxProblems];
+    for (int i = 0; i < n; ++i) {
+        const bl_w1_problem &p = probs[i];
+        w[i] = bl::W1Args{p.x, p.x_dtype, p.K, p.gamma, p.beta, p.M, p.K, (int8_t *)((char *)ws + q_off[i]),
+                          (float *)((char *)ws + a_off[i]), p.packed, p.N, p.w_scale, p.y};
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (int e = check_hip(bl::launch_w1_norm(w, n, eps, s), fn)) return e;
+    return check_hip(bl::launch_w1_gemm(w, n, s), fn);
+}
+
 } // extern "C"

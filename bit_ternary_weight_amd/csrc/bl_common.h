@@ -354,6 +354,25 @@ struct ChainParams {
     SegTab seg_qkv;
     const ChainLayerPtrs *layers;   // host array of L
 };
+// The 1-bit BitLinear (k_binary.hip): one entry of a problem table.
+struct W1Args {
+    const void *x;        // raw activations [M, ldx] (fp32 or bf16), for the norm launch
+    int x_dt, ldx;
+    const float *gamma;   // [K] or null
+    const float *beta;    // [K] or null
+    int M, K;
+    int8_t *q;            // [M, K] codes
+    float *a;             // [M] activation scales
+    const uint8_t *P;     // packed signs [N/8, K], for the contraction
+    int N;
+    const float *w_scale; // [1]
+    float *y;             // [M, N] fp32
+};
+int w1_ln_max_k();
+hipError_t launch_binarize_pack(const float *W, int N, int K, uint8_t *packed, hipStream_t s);
+hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s);
+hipError_t launch_w1_gemm(const W1Args *probs, int n, hipStream_t s);
+
 int chain_max_layers();
 bool chain_fits(int H, int KV, int I, int G);
 int chain_workgroups();

@@ -1,0 +1,366 @@
+// k_binary.hip -- the 1-bit BitLinear: layer normalization, sign-binarized
+// weights (one bit each, one scale per tensor), absmax int8 activations and
+// the int8 x 1-bit contraction on the matrix cores.
+//
+// The PyTorch 1-bit BitNet project summary, section "How It Works": the
+// BitLinear that replaces a linear layer binarizes its weights and feeds it
+// activations that went through layer normalization and absolute-maximum
+// quantization.  The page prints no formula; the readings (shared with the
+// oracle, written independently there):
+//   * sign: -1 where W < 0, else +1; scale: the mean of |W| (the ternary
+//     path's absmean kernels: fp64 sum, fp32, floor 1e-5);
+//   * bit i of packed row r (plane order, N/8 packed rows) is weight row
+//     i*N/8 + r, set for +1;
+//   * mu and the variance in fp64, r = float(1/sqrt(var + eps)),
+//     x' = (float(x - mu) * r) * gamma + beta, then the ternary path's
+//     absmax int8 quantization, y = float(A) * (w_scale / a).
+//
+// The contraction: for a packed dword b (four k's of one packed row), the
+// int8x4 operand b & (0x01010101 << i) holds bit_i * 2^i for i = 0..6, and
+// (b >> 1) & 0x40404040 holds bit_7 * 64; the matrix core sums q * that, an
+// exact shift removes the power of two, and A = 2 sum_k q*bit - sum_k q
+// turns {0,1} into {-1,+1}.  |A| <= 64 * 128 * K stays inside int32 for
+// K <= 16384.
+#include "bl_common.h"
+
+namespace bl {
+
+namespace {
+
+constexpr int kT = 256;
+constexpr int kLnMaxChunks = 16;   // float4 chunks per thread in the norm: K <= 16384
+
+struct W1Problem {
+    const void *x;        // raw activations [M, ldx] (layer-norm launch), or null
+    int x_dt, ldx;
+    const float *gamma;   // [K] or null
+    const float *beta;    // [K] or null
+    int M, K;
+    int8_t *q;            // [M, K] codes
+    float *a;             // [M] activation scales
+    const uint8_t *P;     // packed signs [N/8, K]
+    int N;
+    const float *w_scale; // [1]
+    float *y;             // [M, N]
+};
+
+struct W1Batch {
+    W1Problem p[kMaxProblems];
+    int n;
+    int start[kMaxProblems + 1];   // first workgroup of each problem
+    float eps;
+};
+
+// The launch's single argument, read through the kernel-argument pointer so
+// that a run-time problem index is a scalar load, not a copy of the table.
+__device__ __forceinline__ const W1Batch &batch() {
+    return *(const W1Batch *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// Problem of this workgroup and the workgroup's index within it.
+__device__ __forceinline__ int problem_of(const W1Batch &b, int &local) {
+    const int blk = blockIdx.x;
+    int p = 0;
+    for (int i = 1; i < b.n; ++i)
+        if (blk >= b.start[i]) p = i;
+    local = blk - b.start[p];
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// Packing: one lane per 4 consecutive k of one packed row (K % 4 == 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_binarize_pack4(const float *__restrict__ W, int N, int K,
+                                                       uint8_t *__restrict__ P) {
+    const int R = N / 8, K4 = K / 4;
+    const int64_t idx = (int64_t)blockIdx.x * kT + threadIdx.x;
+    if (idx >= (int64_t)R * K4) return;
+    const int r = (int)(idx / K4);
+    const int k = (int)(idx % K4) * 4;
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = *reinterpret_cast<const float4 *>(W + (int64_t)(i * R + r) * K + k);
+        out |= (uint32_t)!(v.x < 0.0f) << i;
+        out |= (uint32_t)!(v.y < 0.0f) << (8 + i);
+        out |= (uint32_t)!(v.z < 0.0f) << (16 + i);
+        out |= (uint32_t)!(v.w < 0.0f) << (24 + i);
+    }
+    *reinterpret_cast<uint32_t *>(P + (int64_t)r * K + k) = out;
+}
+
+// ---------------------------------------------------------------------------
+// Layer normalization + absmax int8, one workgroup per row.  Thread t holds
+// the float4 chunks t + 256 j.  Sums in fixed order: per thread, the wave's
+// butterfly, then the four waves pairwise.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double block_sum(double v, double *red) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const double r = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
+    (void)unused;
+    __shared__ double red_d[4];
+    __shared__ float red_f[4];
+    const W1Batch &b = batch();
+    int m = 0;
+    const int p = problem_of(b, m);
+    const W1Problem &pr = b.p[p];
+    const int K = pr.K, nc = K >> 2, t = threadIdx.x;
+    float v[kLnMaxChunks][4];
+    if (pr.x_dt == BL_BF16) {
+        const uint16_t *row = static_cast<const uint16_t *>(pr.x) + (size_t)m * pr.ldx;
+#pragma unroll
+        for (int j = 0; j < kLnMaxChunks; ++j) {
+            const int c = t + kT * j;
+            uint2 u = make_uint2(0u, 0u);
+            if (c < nc) u = *reinterpret_cast<const uint2 *>(row + 4 * c);
+            v[j][0] = __uint_as_float(u.x << 16); v[j][1] = __uint_as_float(u.x & 0xFFFF0000u);
+            v[j][2] = __uint_as_float(u.y << 16); v[j][3] = __uint_as_float(u.y & 0xFFFF0000u);
+        }
+    } else {
+        const float *row = static_cast<const float *>(pr.x) + (size_t)m * pr.ldx;
+#pragma unroll
+        for (int j = 0; j < kLnMaxChunks; ++j) {
+            const int c = t + kT * j;
+            float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (c < nc) u = *reinterpret_cast<const float4 *>(row + 4 * c);
+            v[j][0] = u.x; v[j][1] = u.y; v[j][2] = u.z; v[j][3] = u.w;
+        }
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < kLnMaxChunks; ++j)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) s += (double)v[j][f];   // chunks past K hold zeros
+    const double mu = block_sum(s, red_d) / (double)K;
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kLnMaxChunks; ++j)
+        if (t + kT * j < nc)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const double d = (double)v[j][f] - mu;
+                ss += d * d;
+            }
+    const double var = block_sum(ss, red_d) / (double)K;
+    const float r = (float)(1.0 / sqrt(var + (double)b.eps));
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kLnMaxChunks; ++j) {
+        const int c = t + kT * j;
+        if (c < nc) {
+            float4 g = make_float4(1.0f, 1.0f, 1.0f, 1.0f), be = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (pr.gamma) g = *reinterpret_cast<const float4 *>(pr.gamma + 4 * c);
+            if (pr.beta) be = *reinterpret_cast<const float4 *>(pr.beta + 4 * c);
+            const float gg[4] = {g.x, g.y, g.z, g.w}, bb[4] = {be.x, be.y, be.z, be.w};
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                float o = (float)((double)v[j][f] - mu) * r;
+                if (pr.gamma) o = o * gg[f];
+                if (pr.beta) o = o + bb[f];
+                v[j][f] = o;
+                am = fmaxf(am, fabsf(o));
+            }
+        }
+    }
+    const float a = 127.0f / fmaxf(block_max(am, red_f), 1e-5f);
+    int8_t *qrow = pr.q + (size_t)m * K;
+#pragma unroll
+    for (int j = 0; j < kLnMaxChunks; ++j) {
+        const int c = t + kT * j;
+        if (c < nc) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int qi = (int)__builtin_amdgcn_fmed3f(rintf(v[j][f] * a), -128.0f, 127.0f);
+                w |= ((uint32_t)qi & 0xFFu) << (8 * f);
+            }
+            *reinterpret_cast<uint32_t *>(qrow + 4 * c) = w;
+        }
+    }
+    if (t == 0) pr.a[m] = a;
+}
+
+// ---------------------------------------------------------------------------
+// Contraction.  Workgroup tile: 16 packed rows (128 output columns, 8 bit
+// planes) x 16 NT tokens; the four waves split K step by step (wave w takes
+// the 64-k steps w, w + 4, ...), issuing U steps' loads before consuming
+// them, and meet through LDS integer adds at the end.  Loads read clamped,
+// always valid addresses; operands outside M, R or K are zeroed in the
+// consume phase.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void planes(v4i b, v4i f[8]) {
+#pragma unroll
+    for (int i = 0; i < 7; ++i) f[i] = b & (0x01010101 << i);
+    f[7] = (b >> 1) & 0x40404040;
+}
+
+template <int NT, int U>
+__global__ __launch_bounds__(kT) void k_w1_gemm(W1Batch unused) {
+    (void)unused;
+    __shared__ int red[NT][8][64][4];
+    __shared__ int qsm[NT * 16];
+    const W1Batch &b = batch();
+    int local = 0;
+    const int p = problem_of(b, local);
+    const W1Problem &pr = b.p[p];
+    const int K = pr.K, M = pr.M, R = pr.N >> 3;
+    const int nrg = (R + 15) >> 4;
+    const int r0 = (local % nrg) * 16, m0 = (local / nrg) * 16 * NT;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+
+    for (int i = tid; i < NT * 8 * 64 * 4; i += kT) (&red[0][0][0][0])[i] = 0;
+    if (tid < NT * 16) qsm[tid] = 0;
+
+    const bool row_ok = r0 + lr < R;
+    const uint8_t *pb = pr.P + (size_t)(row_ok ? r0 + lr : 0) * K;
+    const int8_t *pa[NT];
+    bool tok_ok[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int m = m0 + 16 * t + lr;
+        tok_ok[t] = m < M;
+        pa[t] = pr.q + (size_t)(tok_ok[t] ? m : 0) * K;
+    }
+    const int nst = (K + 63) >> 6;
+    v4i acc[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[t][i] = v4i{0, 0, 0, 0};
+    int qs[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qs[t] = 0;
+
+    for (int s0 = wave; s0 < nst; s0 += 4 * U) {
+        v4i bw[U], av[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int st = s0 + 4 * u;
+            int kk = (st < nst ? st : nst - 1) * 64 + 16 * g;
+            kk = kk < K ? kk : K - 16;
+            bw[u] = ld16(pb + kk);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) av[u][t] = ld16(pa[t] + kk);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int st = s0 + 4 * u;
+            const bool k_ok = st < nst && st * 64 + 16 * g < K;
+            const v4i z = v4i{0, 0, 0, 0};
+            v4i f[8];
+            planes((k_ok && row_ok) ? bw[u] : z, f);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const v4i a = (k_ok && tok_ok[t]) ? av[u][t] : z;
+                qs[t] += rowsum16(a);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[t][i] = mfma16(a, f[i], acc[t][i]);
+            }
+        }
+    }
+    __syncthreads();   // LDS cleared
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) atomicAdd(&red[t][i][lane][j], acc[t][i][j]);
+        int s = qs[t];
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (g == 0) atomicAdd(&qsm[16 * t + lr], s);
+    }
+    __syncthreads();
+    // epilogue: wave w writes bit planes 2w and 2w + 1
+    if (!row_ok) return;
+    const float wsc = pr.w_scale[0];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tl = 16 * t + 4 * g + j;
+            const int m = m0 + tl;
+            if (m >= M) continue;
+            const float sc = wsc / pr.a[m];
+            const int qsum = qsm[tl];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * wave + h;
+                const int d = red[t][i][lane][j] >> (i < 7 ? i : 6);
+                const int A = 2 * d - qsum;
+                pr.y[(size_t)m * pr.N + (size_t)i * R + r0 + lr] = (float)A * sc;
+            }
+        }
+}
+
+} // namespace
+
+// Workspace and shape rules for the host side (bl_api.hip).
+int w1_ln_max_k() { return kLnMaxChunks * kT * 4; }
+
+hipError_t launch_binarize_pack(const float *W, int N, int K, uint8_t *packed, hipStream_t s) {
+    const int64_t n = (int64_t)(N / 8) * (K / 4);
+    hipLaunchKernelGGL(k_binarize_pack4, dim3((unsigned)((n + kT - 1) / kT)), dim3(kT), 0, s, W, N, K, packed);
+    return hipGetLastError();
+}
+
+static W1Problem to_problem(const W1Args &a) {
+    return W1Problem{a.x, a.x_dt, a.ldx, a.gamma, a.beta, a.M, a.K, a.q, a.a, a.P, a.N, a.w_scale, a.y};
+}
+
+// The norm and quantization of every row of the problems (x, gamma, beta in;
+// q, a out), one launch.
+hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s) {
+    W1Batch b{};
+    b.n = n;
+    b.eps = eps;
+    int start = 0;
+    for (int i = 0; i < n; ++i) {
+        b.p[i] = to_problem(probs[i]);
+        b.start[i] = start;
+        start += probs[i].M;
+    }
+    b.start[n] = start;
+    hipLaunchKernelGGL(k_ln_quant, dim3(start), dim3(kT), 0, s, b);
+    return hipGetLastError();
+}
+
+// The contraction of every problem (q, a, P, w_scale in; y out), one launch.
+hipError_t launch_w1_gemm(const W1Args *probs, int n, hipStream_t s) {
+    W1Batch b{};
+    b.n = n;
+    int max_m = 0;
+    for (int i = 0; i < n; ++i) max_m = probs[i].M > max_m ? probs[i].M : max_m;
+    const int nt = max_m > 16 ? 2 : 1;
+    int start = 0;
+    for (int i = 0; i < n; ++i) {
+        b.p[i] = to_problem(probs[i]);
+        b.start[i] = start;
+        const int R = probs[i].N / 8;
+        start += ((R + 15) / 16) * ((probs[i].M + 16 * nt - 1) / (16 * nt));
+    }
+    b.start[n] = start;
+    if (nt == 1)
+        hipLaunchKernelGGL((k_w1_gemm<1, 8>), dim3(start), dim3(kT), 0, s, b);
+    else
+        hipLaunchKernelGGL((k_w1_gemm<2, 4>), dim3(start), dim3(kT), 0, s, b);
+    return hipGetLastError();
+}
+
+} // namespace bl

@@ -12,6 +12,9 @@
  *  [M] "BitNet" model documentation (Chinese and Portuguese editions):
  *      "模型详情" / "Detalhes do Modelo" (W1.58A8, ReLU squared, subln, no
  *      bias) and "BitNetConfig" (rms_norm_eps 1e-5, layer shapes).
+ *  [S] project summary of a PyTorch "BitNet" implementation of 1-bit
+ *      Transformers: "How It Works" (the 1-bit BitLinear: layer
+ *      normalization, binarization, absolute-maximum quantization).
  *
  * Numerics (what every call computes, bit for bit):
  *  - weight scale  w_mean = max(float(sum|W| / count), 1e-5), sum in fp64;
@@ -457,6 +460,60 @@ int bl_ste_grad_input(const void *dy, int dy_dtype, int M, int N, int K, const u
                       const float *w_mean, float *dx, void *ws, size_t ws_bytes, bl_stream stream);
 int bl_ste_grad_weight(const void *dy, int dy_dtype, const int8_t *q, const float *a, int M, int N, int K,
                        float *dw, void *ws, size_t ws_bytes, bl_stream stream);
+
+/* ---------------------------------------------------------------------------
+ * The 1-bit BitLinear.  [S] "How It Works": weights binarized to one bit,
+ * activations layer-normalized and absmax-quantized.  The page prints no
+ * formula; these calls compute (the readings stated with the oracle):
+ *  - weight sign   s = -1 where W < 0, else +1 (zeros +1);
+ *  - weight scale  w_scale = max(float(sum|W| / count), 1e-5), sum in fp64
+ *                  (the ternary path's absmean);
+ *  - packed        P[r,k] bit i = (s[i*N/8 + r, k] == +1)  (plane order,
+ *                  N/8 packed rows, one bit per weight);
+ *  - layer norm    mu = sum x / K and var = sum (x - mu)^2 / K in fp64,
+ *                  r = float(1/sqrt(var + eps)),
+ *                  x' = (float(x - mu) * r) * gamma + beta (fp32; gamma and
+ *                  beta optional);
+ *  - act codes     bl_quant_act's per-token absmax int8 of x';
+ *  - output        A = sum_k q * s (exact int32), y = float(A) * (w_scale / a).
+ *
+ * bl_binarize_pack: W [N,K] fp32 -> packed [N/8,K] uint8 and w_scale [1];
+ *   ws of bl_binarize_workspace_bytes(N, K) bytes.  N >= 8, N % 8 == 0,
+ *   K % 4 == 0, N*K < 2^40.
+ * bl_layernorm_quant: x [M,K] (row stride ldx elements, 0 = K; BL_F32 or
+ *   BL_BF16) -> q [M,K] int8, a [M] fp32; gamma, beta [K] or NULL.
+ *   K % 4 == 0, 4 <= K <= 16384, ldx % 4 == 0.
+ * bl_gemm_w1a8: q [M,K] int8 and a [M] -> y [M,N] fp32 with packed [N/8,K]
+ *   and w_scale [1].  K % 16 == 0, 16 <= K <= 16384, N % 8 == 0.
+ * bl_bitlinear_w1: up to 8 independent forwards (x -> y) in two launches
+ *   (all the norms, then all the contractions); each problem as in
+ *   bl_layernorm_quant + bl_gemm_w1a8; ws of
+ *   bl_bitlinear_w1_workspace_bytes(probs, n) bytes holds the codes and
+ *   scales.
+ * Every pointer 16-byte aligned (y: 4).  Errors: BL_ERR_NULL, BL_ERR_SHAPE,
+ * BL_ERR_DTYPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE before any launch.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const void *x;          /* [M, K] fp32 or bf16 activations       */
+    int x_dtype;
+    int M, K;
+    const float *gamma;     /* [K] layer-norm gain or NULL             */
+    const float *beta;      /* [K] layer-norm bias or NULL             */
+    const uint8_t *packed;  /* [N/8, K] bl_binarize_pack output        */
+    int N;
+    const float *w_scale;   /* [1]                                      */
+    float *y;               /* out [M, N] fp32                          */
+} bl_w1_problem;
+
+size_t bl_binarize_workspace_bytes(int64_t N, int64_t K);
+int bl_binarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_scale, void *ws, size_t ws_bytes,
+                     bl_stream stream);
+int bl_layernorm_quant(const void *x, int x_dtype, int M, int K, int ldx, const float *gamma, const float *beta,
+                       float eps, int8_t *q, float *a, bl_stream stream);
+int bl_gemm_w1a8(const int8_t *q, const float *a, int M, int K, const uint8_t *packed, int N,
+                 const float *w_scale, float *y, bl_stream stream);
+size_t bl_bitlinear_w1_workspace_bytes(const bl_w1_problem *probs, int n);
+int bl_bitlinear_w1(const bl_w1_problem *probs, int n, float eps, void *ws, size_t ws_bytes, bl_stream stream);
 
 #ifdef __cplusplus
 }

@@ -329,3 +329,47 @@ def test_stack_decode_validation(lib):
     assert call(L=0) == lib.BL_ERR_SHAPE
     assert call(L=33) == lib.BL_ERR_SHAPE
     assert call(eps=-1.0) == lib.BL_ERR_SHAPE
+
+
+def test_w1_validation(lib):
+    raw = lib.raw
+    assert raw.bl_binarize_workspace_bytes(2560, 2560) == raw.bl_ternarize_workspace_bytes(2560, 2560)
+    need = raw.bl_binarize_workspace_bytes(64, 32)
+    bp = lambda **kw: raw.bl_binarize_pack(*{**dict(W=FAKE, N=64, K=32, P=FAKE, s=FAKE, ws=FAKE, wsb=need),
+                                            **kw}.values(), None)
+    assert bp(W=None) == lib.BL_ERR_NULL
+    assert bp(N=60) == lib.BL_ERR_SHAPE
+    assert bp(K=30) == lib.BL_ERR_SHAPE
+    assert bp(P=FAKE_MIS) == lib.BL_ERR_ALIGN
+    assert bp(wsb=need - 1) == lib.BL_ERR_WORKSPACE
+    ln = lambda **kw: raw.bl_layernorm_quant(*{**dict(x=FAKE, xdt=0, M=4, K=2560, ldx=0, g=None, b=None, eps=1e-5,
+                                                      q=FAKE, a=FAKE), **kw}.values(), None)
+    assert ln(x=None) == lib.BL_ERR_NULL
+    assert ln(xdt=2) == lib.BL_ERR_DTYPE
+    assert ln(K=2562) == lib.BL_ERR_SHAPE
+    assert ln(K=16388) == lib.BL_ERR_SHAPE         # above the norm's 16384
+    assert ln(ldx=2561) == lib.BL_ERR_SHAPE
+    assert ln(eps=-1.0) == lib.BL_ERR_SHAPE
+    assert ln(g=FAKE_MIS) == lib.BL_ERR_ALIGN
+    gm = lambda **kw: raw.bl_gemm_w1a8(*{**dict(q=FAKE, a=FAKE, M=3, K=2560, P=FAKE, N=2560, s=FAKE, y=FAKE),
+                                         **kw}.values(), None)
+    assert gm(q=None) == lib.BL_ERR_NULL
+    assert gm(P=None) == lib.BL_ERR_NULL
+    assert gm(K=2568) == lib.BL_ERR_SHAPE          # K a multiple of 16
+    assert gm(N=2564) == lib.BL_ERR_SHAPE          # N a multiple of 8
+    assert gm(M=0) == lib.BL_ERR_SHAPE
+    assert gm(P=FAKE_MIS) == lib.BL_ERR_ALIGN
+    W1 = lib.W1Problem
+    ok = W1(FAKE.value, 1, 1, 2560, None, None, FAKE.value, 3840, FAKE.value, FAKE.value)
+    arr = (W1 * 2)(ok, ok)
+    need = raw.bl_bitlinear_w1_workspace_bytes(arr, 2)
+    assert need >= 2 * (2560 + 4)
+    assert raw.bl_bitlinear_w1_workspace_bytes(arr, 9) == 0
+    bw = lambda arr=arr, n=2, eps=1e-5, ws=FAKE, wsb=need: raw.bl_bitlinear_w1(arr, n, eps, ws, wsb, None)
+    assert bw(n=0) == lib.BL_ERR_SHAPE
+    assert bw(n=9) == lib.BL_ERR_SHAPE
+    assert bw(wsb=need - 1) == lib.BL_ERR_WORKSPACE
+    bad = (W1 * 2)(ok, W1(FAKE.value, 3, 1, 2560, None, None, FAKE.value, 3840, FAKE.value, FAKE.value))
+    assert bw(arr=bad) == lib.BL_ERR_DTYPE
+    bad = (W1 * 2)(ok, W1(FAKE.value, 1, 1, 2560, None, None, FAKE.value, 3844, FAKE.value, FAKE.value))
+    assert bw(arr=bad) == lib.BL_ERR_SHAPE
