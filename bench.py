@@ -346,6 +346,68 @@ def ste_timing(torch, dev, timer, H, I, M=2048):
     return out
 
 
+def w1_build(torch, bl, synth, dev, n_layers):
+    """Binarized weights of n_layers layers of the 2B4T shape: seeded N(0, 0.02)
+    masters drawn on the device (one projection at a time), sign-packed."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    out = []
+    for _ in range(n_layers):
+        lay = []
+        for name, N, K in synth.PROJECTIONS:
+            W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            lay.append(bl.binarize_pack(W))
+            del W
+        out.append(lay)
+    torch.cuda.synchronize()
+    return out
+
+
+def w1_timing(torch, bl, synth, timer, dev, n_layers, steps=None):
+    """The 1-bit BitLinear: decode M=1 over a layer's 7 projections (one call:
+    the norm launch, then the contraction launch) stepping through n_layers
+    layers, and the prefill of the FFN shapes at M=2048 (gate, up and down
+    as three problems of one call; and the contraction alone)."""
+    import numpy as np
+    res = {}
+    wl = w1_build(torch, bl, synth, dev, n_layers)
+    xs = [torch.from_numpy(synth.act_outliers_bf16(300 + j, 1, K).view(np.int16)).to(dev).view(torch.bfloat16)
+          for j, (_, N, K) in enumerate(synth.PROJECTIONS)]
+    ys = [torch.empty((1, N), dtype=torch.float32, device=dev) for _, N, K in synth.PROJECTIONS]
+    probs = [[dict(x=xs[j], packed=lay[j][0], w_scale=lay[j][1], y=ys[j]) for j in range(len(ys))] for lay in wl]
+    g = capture(torch, lambda: [bl.bitlinear_w1_batched(pl) for pl in probs])
+    t = timer.run(g.replay, steps or 10, 2) / n_layers
+    by = sum(N * K // 8 + K * 2 + N * 4 for _, N, K in synth.PROJECTIONS)
+    res["w1_decode_m1_7proj_us_per_layer"] = round(t * 1e3, 2)
+    res["w1_decode_m1_7proj_gbs"] = round(by / (t * 1e-3) / 1e9, 1)
+    res["w1_decode_m1_7proj_bytes"] = by
+    del g
+    H, I = synth.HIDDEN, synth.INTERMEDIATE
+    M = 2048
+    lay = wl[0]
+    names = [n for n, _, _ in synth.PROJECTIONS]
+    gi, ui, di = names.index("gate"), names.index("up"), names.index("down")
+    xh = torch.from_numpy(synth.act_normal_bf16(0, M, H).view(np.int16)).to(dev).view(torch.bfloat16)
+    xi = torch.from_numpy(synth.act_normal_bf16(1, M, I).view(np.int16)).to(dev).view(torch.bfloat16)
+    yg = torch.empty((M, I), dtype=torch.float32, device=dev)
+    yu = torch.empty((M, I), dtype=torch.float32, device=dev)
+    yd = torch.empty((M, H), dtype=torch.float32, device=dev)
+    pf = [dict(x=xh, packed=lay[gi][0], w_scale=lay[gi][1], y=yg), dict(x=xh, packed=lay[ui][0], w_scale=lay[ui][1], y=yu),
+          dict(x=xi, packed=lay[di][0], w_scale=lay[di][1], y=yd)]
+    ops = 2 * M * (2 * I * H + H * I)
+    t = timer.run(lambda: bl.bitlinear_w1_batched(pf), 20, 3)
+    res["w1_prefill_m2048_ffn_us"] = round(t * 1e3, 1)
+    res["w1_prefill_m2048_ffn_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
+    qh, ah = bl.layernorm_quant(xh)
+    qi, ai = bl.layernorm_quant(xi)
+    f = lambda: (bl.gemm_w1a8(qh, ah, lay[gi][0], lay[gi][1], y=yg), bl.gemm_w1a8(qh, ah, lay[ui][0], lay[ui][1], y=yu),
+                 bl.gemm_w1a8(qi, ai, lay[di][0], lay[di][1], y=yd))
+    t = timer.run(f, 20, 3)
+    res["w1_prefill_m2048_ffn_gemm_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
+    res["w1_prefill_m2048_ffn_gemm_frac_of_int8_peak"] = round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+    return res
+
+
 def unpacked_timing(torch, bl, stack, synth, timer, dev, layers, probs1, H, I):
     """The offline-unpacked baseline: the 30 layers' weights unpacked to bf16
     codes (about 4.2 GB), decode M=1 over each layer's 7 projections (the
@@ -417,6 +479,8 @@ def main():
                     help="only the persistent 30-layer decode step (for profiler runs)")
     ap.add_argument("--mt-only", type=int, default=0, metavar="M",
                     help="only the batched decode at M rows, 7 projections per launch over 30 layers (for profiler runs)")
+    ap.add_argument("--w1-only", action="store_true",
+                    help="only the 1-bit BitLinear decode (7 projections x 30 layers) and prefill (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 5 times (calibrates profiler byte counters)")
     args = ap.parse_args()
@@ -430,7 +494,8 @@ def main():
     # the oracle's CPU baseline first, before anything touches the GPU (its
     # core is pinned and nothing else runs meanwhile)
     run_cpu = not (args.no_cpu or args.copy_probe or args.kernel_only or args.attn_only or args.ste_only
-                   or args.attn_prefill_only or args.prefill_only or args.mt_only or args.chain_only)
+                   or args.attn_prefill_only or args.prefill_only or args.mt_only or args.chain_only
+                   or args.w1_only)
     cpu = cpu_baseline() if run_cpu else None
     if cpu is not None:
         log(f"cpu baseline (oracle, 1 core): {cpu['value']} GB/s decode; {cpu['per_config']}")
@@ -464,6 +529,10 @@ def main():
     if args.attn_prefill_only:
         t, tf = attn_prefill_timing(torch, bl, stack, timer, dev, H, KV)
         print(json.dumps({"attn_prefill_m4096_us": round(t * 1e3, 1), "attn_prefill_m4096_tflops": tf}), flush=True)
+        return
+    if args.w1_only:
+        print(json.dumps(w1_timing(torch, bl, synth, timer, dev, args.layers, steps=max(1, args.steps // args.layers))),
+              flush=True)
         return
     if args.prefill_only:
         lw = stack.build_layers(1, dev)[0]
@@ -704,6 +773,12 @@ def main():
         log(f"offline-unpacked: decode M=1 {extra['unpacked_decode_m1_us_per_layer']} us/layer "
             f"({extra['unpacked_decode_m1_weight_gbs']} GB/s of bf16 codes), prefill M=2048 "
             f"{extra['unpacked_prefill_m2048_ffn_tops']} TOPS")
+        # the 1-bit BitLinear (binarized weights, layer norm): decode over the
+        # 7 projections of 30 layers and the FFN prefill at M=2048
+        extra.update(w1_timing(torch, bl, synth, timer, dev, len(layers)))
+        log(f"1-bit BitLinear: decode M=1 {extra['w1_decode_m1_7proj_us_per_layer']} us/layer "
+            f"({extra['w1_decode_m1_7proj_gbs']} GB/s), prefill FFN M=2048 {extra['w1_prefill_m2048_ffn_tops']} TOPS "
+            f"(contraction alone {extra['w1_prefill_m2048_ffn_gemm_tops']} TOPS)")
         # offline ternarization (absmean + pack) of one 6912 x 2560 master
         W = torch.from_numpy(synth.layer_weight(0, "gate")).to(dev)
         pk = torch.empty((I // 4, H), dtype=torch.uint8, device=dev)

@@ -316,10 +316,11 @@ int bl_device_errors(unsigned int *expired_waits, int reset) {
     g_err[0] = 0;
     if (!expired_waits) return fail(BL_ERR_NULL, "bl_device_errors: NULL pointer argument");
     if (hipError_t e = hipDeviceSynchronize(); e != hipSuccess) return check_hip(e, "bl_device_errors");
-    unsigned int a = 0, b = 0;
+    unsigned int a = 0, b = 0, c = 0;
     if (int st = check_hip(bl::gemv_wait_expired(&a, reset != 0), "bl_device_errors")) return st;
     if (int st = check_hip(bl::chain_wait_expired(&b, reset != 0), "bl_device_errors")) return st;
-    *expired_waits = a + b;
+    if (int st = check_hip(bl::w1_wait_expired(&c, reset != 0), "bl_device_errors")) return st;
+    *expired_waits = a + b + c;
     return BL_OK;
 }
 
@@ -1054,6 +1055,7 @@ int bl_bitlinear_w1(const bl_w1_problem *probs, int n, float eps, void *ws, size
                           (float *)((char *)ws + a_off[i]), p.packed, p.N, p.w_scale, p.y};
     }
     hipStream_t s = (hipStream_t)stream;
+    if (bl::w1_decode_fits(w, n)) return check_hip(bl::launch_w1_decode(w, n, eps, s), fn);
     if (int e = check_hip(bl::launch_w1_norm(w, n, eps, s), fn)) return e;
     return check_hip(bl::launch_w1_gemm(w, n, s), fn);
 }

@@ -372,6 +372,9 @@ int w1_ln_max_k();
 hipError_t launch_binarize_pack(const float *W, int N, int K, uint8_t *packed, hipStream_t s);
 hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s);
 hipError_t launch_w1_gemm(const W1Args *probs, int n, hipStream_t s);
+bool w1_decode_fits(const W1Args *probs, int n);
+hipError_t w1_wait_expired(unsigned int *count, bool reset);
+hipError_t launch_w1_decode(const W1Args *probs, int n, float eps, hipStream_t s);
 
 int chain_max_layers();
 bool chain_fits(int H, int KV, int I, int G);

@@ -23,6 +23,8 @@
 // K <= 16384.
 #include "bl_common.h"
 
+#include <utility>
+
 namespace bl {
 
 namespace {
@@ -309,6 +311,285 @@ __global__ __launch_bounds__(kT) void k_w1_gemm(W1Batch unused) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// Decode (M = 1, K a multiple of 256 up to 8192): norm, quantization and
+// contraction in one launch.  One 16-wave workgroup per 16 packed rows over
+// all of K, cut into units of 4 packed rows x 256 bytes (lane (g, l) loads
+// row l / 4, 16-byte chunk l % 4 + 4 g: every row arrives as two whole
+// 128-byte lines).  Two roles:
+//   * 8 quantizer waves load the input row (and gains), normalize and
+//     quantize it into LDS; they issue no weight load, and they meet each
+//     other through LDS flags, not workgroup barriers;
+//   * 8 stream waves issue all their units at once (two waves per row quad,
+//     alternate k-units; a fixed count, past-the-end units reading a valid
+//     address), once every quantizer wave has issued its loads (requests
+//     leave a compute unit in issue order: row loads issued behind the weight
+//     stream would arrive after it), and then wait for the codes.  A wave that issues many loads stalls in the
+//     issue itself while the compute unit drains them, so a barrier shared
+//     with the quantization would wait for the stream.
+// A unit goes through the matrix cores once per bit plane, weights first:
+// product row 4 r + s is (unit row r, k-slice s), and column j of the codes
+// operand carries k-slice j % 4 of the same chunks, so entry (4 r + s, s) is
+// row r's sum over slice s; the four slices of a row sit in one lane quad
+// and are added there, once per wave after all its units (the products of a
+// wave's units accumulate in the matrix cores).  The row sums meet in LDS
+// (integer adds).
+// ---------------------------------------------------------------------------
+constexpr int kDQW = 8;                      // quantizer waves
+constexpr int kDSW = 8;                      // stream waves
+constexpr int kDT = (kDQW + kDSW) * 64;
+constexpr int kDQT = kDQW * 64;
+constexpr int kDU = 16;                      // k-units per stream wave: two waves per row quad, K / 256 <= 32
+constexpr int kDChunks = 8192 / 4 / kDQT;         // float4 input chunks per quantizer thread
+
+__device__ __forceinline__ void d_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int CTRL>
+__device__ __forceinline__ int d_dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double d_dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = d_dpp<CTRL>((int)(b & 0xFFFFFFFF));
+    const int hi = d_dpp<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double d_readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Wave sums by DPP row operations and lane reads (no LDS round trips), in a
+// fixed order.
+__device__ __forceinline__ double d_wave_sum(double v) {
+    v += d_dpp_d<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += d_dpp_d<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += d_dpp_d<0x124>(v);   // row_ror:4
+    v += d_dpp_d<0x128>(v);   // row_ror:8
+    return ((d_readlane_d(v, 0) + d_readlane_d(v, 16)) + d_readlane_d(v, 32)) + d_readlane_d(v, 48);
+}
+
+__device__ __forceinline__ float d_wave_max(float v) {
+    v = fmaxf(v, __int_as_float(d_dpp<0xB1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(d_dpp<0x4E>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(d_dpp<0x124>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(d_dpp<0x128>(__float_as_int(v))));
+    const int iv = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 32)), __int_as_float(__builtin_amdgcn_readlane(iv, 48))));
+}
+
+__device__ __forceinline__ int d_wave_sum_i(int v) {
+    v += d_dpp<0xB1>(v);
+    v += d_dpp<0x4E>(v);
+    v += d_dpp<0x124>(v);
+    v += d_dpp<0x128>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ __forceinline__ int d_quad_sum(int v) {
+    v += d_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += d_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    return v;
+}
+
+// The quantizer waves' rendezvous: each publishes `step` in its LDS flag and
+// waits until every flag reaches it (bounded; an expired wait is counted and
+// the wave goes on).
+__device__ unsigned int g_w1_expired = 0;
+
+__device__ __forceinline__ void q_sync(volatile int *flag, int qw, int step) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if ((threadIdx.x & 63) == 0) flag[qw] = step;
+    int lo = 0;
+    for (int it = 0; it < (1 << 22); ++it) {
+        lo = flag[0];
+#pragma unroll
+        for (int w = 1; w < kDQW; ++w) lo = min(lo, flag[w]);
+        lo = __builtin_amdgcn_readfirstlane(lo);
+        if (lo >= step) break;
+    }
+    if (lo < step && (threadIdx.x & 63) == 0) atomicAdd(&g_w1_expired, 1u);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
+    (void)unused;
+    __shared__ __attribute__((aligned(16))) int8_t qd[8192];
+    __shared__ int red[8][16];
+    __shared__ double rd[kDQW];
+    __shared__ float rf[kDQW];
+    __shared__ int ri[kDQW];
+    __shared__ int flag[kDQW];
+    const W1Batch &b = batch();
+    int local = 0;
+    const int p = problem_of(b, local);
+    const W1Problem &pr = b.p[p];
+    const int K = pr.K, R = pr.N >> 3, nku = K >> 8, nu = 4 * nku;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4;
+    const int r0 = local * 16;
+    float a = 1.0f;
+
+    if (wave < kDQW) {
+        // ---- quantizer waves: the row, its norm and its codes
+        const int nc = K >> 2;
+        if (lane == 0) flag[wave] = 0;
+        if (tid < 8 * 16) (&red[0][0])[tid] = 0;
+        float xv[kDChunks][4];
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i) {
+            const int c = tid + kDQT * i;
+            if (BF16) {
+                uint2 u = make_uint2(0u, 0u);
+                if (c < nc) u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(pr.x) + 4 * c);
+                xv[i][0] = __uint_as_float(u.x << 16); xv[i][1] = __uint_as_float(u.x & 0xFFFF0000u);
+                xv[i][2] = __uint_as_float(u.y << 16); xv[i][3] = __uint_as_float(u.y & 0xFFFF0000u);
+            } else {
+                float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (c < nc) u = *reinterpret_cast<const float4 *>(static_cast<const float *>(pr.x) + 4 * c);
+                xv[i][0] = u.x; xv[i][1] = u.y; xv[i][2] = u.z; xv[i][3] = u.w;
+            }
+        }
+        float4 gq[kDChunks], bq[kDChunks];
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i) {
+            const int c = tid + kDQT * i;
+            gq[i] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            bq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (pr.gamma && c < nc) gq[i] = *reinterpret_cast<const float4 *>(pr.gamma + 4 * c);
+            if (pr.beta && c < nc) bq[i] = *reinterpret_cast<const float4 *>(pr.beta + 4 * c);
+        }
+        d_barrier();   // every row and gain load issued: the weight stream may start
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) s += (double)xv[i][f];   // chunks past K hold zeros
+        s = d_wave_sum(s);
+        if (lane == 0) rd[wave] = s;
+        q_sync(flag, wave, 1);
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kDQW; ++w) tot += rd[w];
+        const double mu = tot / (double)K;
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i)
+            if (tid + kDQT * i < nc)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const double d = (double)xv[i][f] - mu;
+                    ss += d * d;
+                }
+        ss = d_wave_sum(ss);
+        q_sync(flag, wave, 2);   // every quantizer wave has read rd
+        if (lane == 0) rd[wave] = ss;
+        q_sync(flag, wave, 3);
+        tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kDQW; ++w) tot += rd[w];
+        const float r = (float)(1.0 / sqrt(tot / (double)K + (double)b.eps));
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i) {
+            const int c = tid + kDQT * i;
+            const float gg[4] = {gq[i].x, gq[i].y, gq[i].z, gq[i].w}, bb[4] = {bq[i].x, bq[i].y, bq[i].z, bq[i].w};
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                float o = (float)((double)xv[i][f] - mu) * r;
+                if (pr.gamma) o = o * gg[f];
+                if (pr.beta) o = o + bb[f];
+                xv[i][f] = c < nc ? o : 0.0f;
+                am = fmaxf(am, fabsf(xv[i][f]));
+            }
+        }
+        am = d_wave_max(am);
+        if (lane == 0) rf[wave] = am;
+        q_sync(flag, wave, 4);
+        float mx = rf[0];
+#pragma unroll
+        for (int w = 1; w < kDQW; ++w) mx = fmaxf(mx, rf[w]);
+        a = 127.0f / fmaxf(mx, 1e-5f);
+        int cs = 0;
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i) {
+            const int c = tid + kDQT * i;
+            if (c < nc) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const int qi = (int)__builtin_amdgcn_fmed3f(rintf(xv[i][f] * a), -128.0f, 127.0f);
+                    w |= ((uint32_t)qi & 0xFFu) << (8 * f);
+                    cs += qi;
+                }
+                *reinterpret_cast<uint32_t *>(qd + 4 * c) = w;
+            }
+        }
+        cs = d_wave_sum_i(cs);
+        if (lane == 0) ri[wave] = cs;
+        d_barrier();   // codes in LDS
+        d_barrier();   // row sums in LDS
+        if (lane < 16 && r0 + lane < R) {   // wave w writes bit plane w
+            int qsum = 0;
+#pragma unroll
+            for (int w = 0; w < kDQW; ++w) qsum += ri[w];
+            const int i = wave;
+            const int A = 2 * (red[i][lane] >> (i < 7 ? i : 6)) - qsum;
+            pr.y[(size_t)i * R + r0 + lane] = (float)A * (pr.w_scale[0] / a);
+        }
+    } else {
+        // ---- stream waves: every unit issued, then the products.  Wave w
+        // takes row quad w % 4 and every other 256-byte k-unit from w / 4,
+        // so its products accumulate in the matrix cores' accumulators
+        const int sw = wave - kDQW, q = sw & 3;
+        const int urow = (lane & 15) >> 2, ch = (lane & 3) + 4 * g;
+        int row = r0 + 4 * q + urow;
+        const bool row_ok = row < R;
+        row = row_ok ? row : R - 1;
+        const uint8_t *pw = pr.P + (size_t)row * K + 16 * ch;
+        d_barrier();   // the quantizer waves' loads go out first
+        v4i bw[kDU];
+#pragma unroll
+        for (int j = 0; j < kDU; ++j) {
+            int ku = (sw >> 2) + 2 * j;
+            ku = ku < nku ? ku : nku - 1;
+            bw[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(pw + ku * 256));
+        }
+        d_barrier();   // codes in LDS
+        v4i acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < kDU; ++j) {
+            const int ku = (sw >> 2) + 2 * j;
+            if (ku >= nku) break;   // uniform; the loads above were issued for every j
+            const v4i cw = *reinterpret_cast<const v4i *>(qd + ku * 256 + 16 * ch);
+            v4i f[8];
+            planes(row_ok ? bw[j] : v4i{0, 0, 0, 0}, f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = mfma16(f[i], cw, acc[i]);
+        }
+        const int sl = lane & 3;
+        int t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t[i] = d_quad_sum(sl == 0 ? acc[i][0] : (sl == 1 ? acc[i][1] : (sl == 2 ? acc[i][2] : acc[i][3])));
+        if ((lane & 15) == 0)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) atomicAdd(&red[i][4 * q + g], t[i]);
+        d_barrier();   // row sums in LDS
+    }
+}
+
 } // namespace
 
 // Workspace and shape rules for the host side (bl_api.hip).
@@ -338,6 +619,53 @@ hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s) 
     }
     b.start[n] = start;
     hipLaunchKernelGGL(k_ln_quant, dim3(start), dim3(kT), 0, s, b);
+    return hipGetLastError();
+}
+
+hipError_t w1_wait_expired(unsigned int *count, bool reset) {
+    unsigned int v = 0;
+    if (hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_w1_expired), sizeof(v)); e != hipSuccess) return e;
+    if (reset && v) {
+        const unsigned int zero = 0;
+        if (hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_w1_expired), &zero, sizeof(zero)); e != hipSuccess) return e;
+    }
+    *count = v;
+    return hipSuccess;
+}
+
+bool w1_decode_fits(const W1Args *probs, int n) {
+    for (int i = 0; i < n; ++i)
+        if (probs[i].M != 1 || probs[i].K % 256 != 0 || probs[i].K > 8192 || !probs[i].x ||
+            probs[i].x_dt != probs[0].x_dt)
+            return false;
+    return true;
+}
+
+// Decode: every problem at M = 1 (one input type, K a multiple of 256 up to
+// 8192) in one launch (norm, quantization and contraction; q and a are not
+// written).
+hipError_t launch_w1_decode(const W1Args *probs, int n, float eps, hipStream_t s) {
+    W1Batch b{};
+    b.n = n;
+    b.eps = eps;
+    // the problems with the longest tiles (largest K) first: the device
+    // starts the lowest workgroup numbers first
+    int order[kMaxProblems];
+    for (int i = 0; i < n; ++i) order[i] = i;
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && probs[order[j]].K > probs[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
+    int start = 0;
+    for (int i = 0; i < n; ++i) {
+        const W1Args &a = probs[order[i]];
+        b.p[i] = to_problem(a);
+        b.start[i] = start;
+        start += (a.N / 8 + 15) / 16;
+    }
+    b.start[n] = start;
+    if (probs[0].x_dt == BL_BF16)
+        hipLaunchKernelGGL(k_w1_decode<true>, dim3(start), dim3(kDT), 0, s, b);
+    else
+        hipLaunchKernelGGL(k_w1_decode<false>, dim3(start), dim3(kDT), 0, s, b);
     return hipGetLastError();
 }
 

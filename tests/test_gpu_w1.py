@@ -140,8 +140,8 @@ def test_gemm_w1a8_extreme_accumulators():
 
 def test_bitlinear_w1_seven_projections_decode():
     """A layer's seven projection shapes (q, k, v, o, gate, up, down of the
-    2B4T configuration) at one token, each with its own input: one call, two
-    launches, every output bit against the oracle."""
+    2B4T configuration) at one token, each with its own input: one call (the
+    fused single-token launch), every output bit against the oracle."""
     bl = _bl()
     probs, refs = [], []
     for j, (name, N, K) in enumerate(synth.PROJECTIONS):
@@ -174,3 +174,45 @@ def test_bitlinear_w1_prefill_all_rows(M, N, K):
     y.check("y")
     ref = oracle.bitlinear_w1_f64gemm(f32_of_bf16(bits), signs, ws, gamma, beta)[3]
     assert_exact(host(y.t).view(np.uint32), ref.view(np.uint32), "y")
+
+
+@pytest.mark.parametrize("N,K,kind,affine", [(8, 16, "f32", True), (136, 48, "bf16", False), (2560, 8192, "f32", True),
+                                             (640, 2560, "bf16", True), (2560, 8208, "bf16", False),
+                                             (24, 4112, "f32", False)])
+def test_bitlinear_w1_single_token(N, K, kind, affine):
+    """One token: the fused decode launch (K <= 8192), or the two-launch path
+    beyond it (K = 8208)."""
+    bl = _bl()
+    r = np.random.default_rng(N * 3 + K)
+    W = synth.master_weight(N + 5 * K, N, K)
+    packed, ws, signs = oracle.binarize_pack(W)
+    raw, x32 = _ln_case(1, K, kind, N + K)
+    gamma = beta = None
+    if affine:
+        gamma = (1.0 + 0.25 * r.standard_normal(K)).astype(np.float32)
+        beta = (0.1 * r.standard_normal(K)).astype(np.float32)
+    y = guarded((1, N), torch.float32)
+    bl.bitlinear_w1(bf16_dev(raw) if kind == "bf16" else to_dev(raw), to_dev(packed), to_dev(np.array([ws], np.float32)),
+                    None if gamma is None else to_dev(gamma), None if beta is None else to_dev(beta), y=y.t)
+    y.check("y")
+    ref = oracle.bitlinear_w1_f64gemm(x32, signs, ws, gamma, beta)[3]
+    assert_exact(host(y.t).view(np.uint32), ref.view(np.uint32), "y")
+
+
+def test_bitlinear_w1_mixed_batch():
+    """A batch mixing input types and a two-row problem takes the two-launch
+    path; the same outputs as the oracle."""
+    bl = _bl()
+    probs, refs = [], []
+    for j, (M, N, K, kind) in enumerate([(1, 256, 512, "bf16"), (1, 128, 256, "f32"), (2, 64, 1024, "bf16")]):
+        W = synth.master_weight(77 + j, N, K)
+        packed, ws, signs = oracle.binarize_pack(W)
+        raw, x32 = _ln_case(M, K, kind, 40 + j)
+        y = guarded((M, N), torch.float32)
+        probs.append((dict(x=bf16_dev(raw) if kind == "bf16" else to_dev(raw), packed=to_dev(packed),
+                           w_scale=to_dev(np.array([ws], np.float32)), y=y.t), y))
+        refs.append(oracle.bitlinear_w1_f64gemm(x32, signs, ws)[3])
+    bl.bitlinear_w1_batched([p for p, _ in probs])
+    for j, ((p, g), ref) in enumerate(zip(probs, refs)):
+        g.check(f"y {j}")
+        assert_exact(host(p["y"]).view(np.uint32), ref.view(np.uint32), f"problem {j}")
