@@ -335,16 +335,21 @@ __global__ __launch_bounds__(kT) void k_w1_gemm(W1Batch unused) {
 // wave's units accumulate in the matrix cores).  The row sums meet in LDS
 // (integer adds).
 // ---------------------------------------------------------------------------
-constexpr int kDQW = 8;                      // quantizer waves
+constexpr int kDQW = 8;                      // quantizer waves (sum8 / max8 read eight partials)
 constexpr int kDSW = 8;                      // stream waves
 constexpr int kDT = (kDQW + kDSW) * 64;
 constexpr int kDQT = kDQW * 64;
 constexpr int kDU = 16;                      // k-units per stream wave: two waves per row quad, K / 256 <= 32
 constexpr int kDChunks = 8192 / 4 / kDQT;         // float4 input chunks per quantizer thread
 
+// Workgroup barrier waiting for LDS operations only; the scheduling fences
+// keep the compiler from moving arithmetic (and the waits for its loaded
+// operands) across it.
 __device__ __forceinline__ void d_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
     asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int CTRL>
@@ -402,6 +407,19 @@ __device__ __forceinline__ int d_quad_sum(int v) {
     return v;
 }
 
+// The eight per-wave partials of an exchange, read as 16-byte vectors:
+// their sum in wave order, their maximum.
+__device__ __forceinline__ double sum8(const double *p) {
+    const double2 a = reinterpret_cast<const double2 *>(p)[0], b = reinterpret_cast<const double2 *>(p)[1];
+    const double2 c = reinterpret_cast<const double2 *>(p)[2], d = reinterpret_cast<const double2 *>(p)[3];
+    return ((((((a.x + a.y) + b.x) + b.y) + c.x) + c.y) + d.x) + d.y;
+}
+
+__device__ __forceinline__ float max8(const float *p) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+    return fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w)));
+}
+
 // The quantizer waves' rendezvous: each publishes `step` in its LDS flag and
 // waits until every flag reaches it (bounded; an expired wait is counted and
 // the wave goes on).
@@ -426,8 +444,10 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
     (void)unused;
     __shared__ __attribute__((aligned(16))) int8_t qd[8192];
     __shared__ int red[8][16];
-    __shared__ double rd[kDQW];
-    __shared__ float rf[kDQW];
+    __shared__ __attribute__((aligned(16))) double rd1[kDQW];   // per-wave sums of x
+    __shared__ __attribute__((aligned(16))) double rd2[kDQW];   // per-wave sums of (x - mu)^2
+    __shared__ __attribute__((aligned(16))) float rm[kDQW];     // per-wave max |float(x - mu)|
+    __shared__ __attribute__((aligned(16))) float rf[kDQW];     // per-wave max |x'| (with gain or bias)
     __shared__ int ri[kDQW];
     __shared__ int flag[kDQW];
     const W1Batch &b = batch();
@@ -444,44 +464,53 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         const int nc = K >> 2;
         if (lane == 0) flag[wave] = 0;
         if (tid < 8 * 16) (&red[0][0])[tid] = 0;
+        // every load unconditional, at a clamped valid address (chunks past K
+        // read chunk 0, absent gains read the row's first 16 bytes), zeroed or
+        // replaced afterwards: a branch around a load would make the compiler
+        // wait for the loads before it
         float xv[kDChunks][4];
+        uint2 xb[kDChunks];
+        float4 xf[kDChunks], gq[kDChunks], bq[kDChunks];
+        const float *gsrc = pr.gamma ? pr.gamma : static_cast<const float *>(pr.x);
+        const float *bsrc = pr.beta ? pr.beta : static_cast<const float *>(pr.x);
 #pragma unroll
         for (int i = 0; i < kDChunks; ++i) {
             const int c = tid + kDQT * i;
+            const int cc = c < nc ? c : 0;
+            if (BF16) xb[i] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(pr.x) + 4 * cc);
+            else xf[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(pr.x) + 4 * cc);
+            gq[i] = *reinterpret_cast<const float4 *>(gsrc + (pr.gamma ? 4 * cc : 0));
+            bq[i] = *reinterpret_cast<const float4 *>(bsrc + (pr.beta ? 4 * cc : 0));
+        }
+        d_barrier();   // every row and gain load issued: the weight stream may start
+#pragma unroll
+        for (int i = 0; i < kDChunks; ++i) {
+            const bool ok = tid + kDQT * i < nc;
             if (BF16) {
-                uint2 u = make_uint2(0u, 0u);
-                if (c < nc) u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(pr.x) + 4 * c);
+                const uint2 u = ok ? xb[i] : make_uint2(0u, 0u);
                 xv[i][0] = __uint_as_float(u.x << 16); xv[i][1] = __uint_as_float(u.x & 0xFFFF0000u);
                 xv[i][2] = __uint_as_float(u.y << 16); xv[i][3] = __uint_as_float(u.y & 0xFFFF0000u);
             } else {
-                float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (c < nc) u = *reinterpret_cast<const float4 *>(static_cast<const float *>(pr.x) + 4 * c);
+                const float4 u = ok ? xf[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 xv[i][0] = u.x; xv[i][1] = u.y; xv[i][2] = u.z; xv[i][3] = u.w;
             }
+            if (!pr.gamma) gq[i] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (!pr.beta) bq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
-        float4 gq[kDChunks], bq[kDChunks];
-#pragma unroll
-        for (int i = 0; i < kDChunks; ++i) {
-            const int c = tid + kDQT * i;
-            gq[i] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            bq[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (pr.gamma && c < nc) gq[i] = *reinterpret_cast<const float4 *>(pr.gamma + 4 * c);
-            if (pr.beta && c < nc) bq[i] = *reinterpret_cast<const float4 *>(pr.beta + 4 * c);
-        }
-        d_barrier();   // every row and gain load issued: the weight stream may start
         double s = 0.0;
 #pragma unroll
         for (int i = 0; i < kDChunks; ++i)
 #pragma unroll
             for (int f = 0; f < 4; ++f) s += (double)xv[i][f];   // chunks past K hold zeros
         s = d_wave_sum(s);
-        if (lane == 0) rd[wave] = s;
+        if (lane == 0) rd1[wave] = s;
         q_sync(flag, wave, 1);
-        double tot = 0.0;
-#pragma unroll
-        for (int w = 0; w < kDQW; ++w) tot += rd[w];
-        const double mu = tot / (double)K;
+        // each exchange has its own slots, so no wave waits for the others'
+        // reads before writing the next one; the partials are read as
+        // 16-byte vectors and added in wave order
+        const double mu = sum8(rd1) / (double)K;
         double ss = 0.0;
+        float md = 0.0f;
 #pragma unroll
         for (int i = 0; i < kDChunks; ++i)
             if (tid + kDQT * i < nc)
@@ -489,16 +518,24 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
                 for (int f = 0; f < 4; ++f) {
                     const double d = (double)xv[i][f] - mu;
                     ss += d * d;
+                    md = fmaxf(md, fabsf((float)d));
                 }
         ss = d_wave_sum(ss);
-        q_sync(flag, wave, 2);   // every quantizer wave has read rd
-        if (lane == 0) rd[wave] = ss;
-        q_sync(flag, wave, 3);
-        tot = 0.0;
-#pragma unroll
-        for (int w = 0; w < kDQW; ++w) tot += rd[w];
-        const float r = (float)(1.0 / sqrt(tot / (double)K + (double)b.eps));
-        float am = 0.0f;
+        md = d_wave_max(md);
+        if (lane == 0) {
+            rd2[wave] = ss;
+            rm[wave] = md;
+        }
+        q_sync(flag, wave, 2);
+        const float r = (float)(1.0 / sqrt(sum8(rd2) / (double)K + (double)b.eps));
+        const bool affine = pr.gamma || pr.beta;
+        float mx = 0.0f;
+        if (!affine) {
+            // without gain or bias the largest |float(x - mu) * r| is
+            // float(max |float(x - mu)| * r): the rounded product is monotone
+            // in the first factor and odd, so the maximum commutes with it
+            mx = max8(rm) * r;
+        }
 #pragma unroll
         for (int i = 0; i < kDChunks; ++i) {
             const int c = tid + kDQT * i;
@@ -509,15 +546,19 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
                 if (pr.gamma) o = o * gg[f];
                 if (pr.beta) o = o + bb[f];
                 xv[i][f] = c < nc ? o : 0.0f;
-                am = fmaxf(am, fabsf(xv[i][f]));
             }
         }
-        am = d_wave_max(am);
-        if (lane == 0) rf[wave] = am;
-        q_sync(flag, wave, 4);
-        float mx = rf[0];
+        if (affine) {
+            float am = 0.0f;
 #pragma unroll
-        for (int w = 1; w < kDQW; ++w) mx = fmaxf(mx, rf[w]);
+            for (int i = 0; i < kDChunks; ++i)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) am = fmaxf(am, fabsf(xv[i][f]));
+            am = d_wave_max(am);
+            if (lane == 0) rf[wave] = am;
+            q_sync(flag, wave, 3);
+            mx = max8(rf);
+        }
         a = 127.0f / fmaxf(mx, 1e-5f);
         int cs = 0;
 #pragma unroll
