@@ -267,6 +267,7 @@ struct ChainLds {
     int part[kCMaxUnits * 16];   // unit partial sums
     double red_d[kCWaves];       // per-wave sums of squares
     float red_f[kCWaves];        // per-wave absolute maxima
+    float red_m[kCWaves];        // per-wave max |h| (norm without gain)
     int red_i[kCWaves];          // per-wave code sums
 };
 
@@ -358,6 +359,30 @@ __device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float *xs) {
     }
 }
 
+// The sixteen per-wave partials of an exchange, read as 16-byte vectors:
+// their sum in wave order, their maximum.
+__device__ __forceinline__ double sum16(const double *p) {
+    const double2 *q = reinterpret_cast<const double2 *>(p);
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < kCWaves / 2; ++i) {
+        const double2 x = q[i];
+        s = (s + x.x) + x.y;
+    }
+    return s;
+}
+
+__device__ __forceinline__ float max16(const float *p) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCWaves / 4; ++i) {
+        const float4 x = q[i];
+        m = fmaxf(m, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+    }
+    return m;
+}
+
 // All 16 waves: normalizes (optionally) and quantizes the K values in xs:
 // codes to q_s in column order, this wave's code sum to red_i[wave]; returns
 // the activation scale.  Same arithmetic as the row kernel: fp64 sum of
@@ -374,19 +399,33 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
         const float4 x = c < nc ? *reinterpret_cast<const float4 *>(sh.xs + 4 * c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
         v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
     }
+    float mx = 0.0f;
+    bool have_max = false;
     if (norm) {
         double ss = 0.0;
+        float hm = 0.0f;
 #pragma unroll
         for (int i = 0; i < kCNormChunks; ++i)
 #pragma unroll
-            for (int f = 0; f < 4; ++f) ss += (double)v[i][f] * (double)v[i][f];
+            for (int f = 0; f < 4; ++f) {
+                ss += (double)v[i][f] * (double)v[i][f];
+                hm = fmaxf(hm, fabsf(v[i][f]));
+            }
         ss = wave_sum_d(ss);
-        if ((t & 63) == 0) sh.red_d[wave] = ss;
+        hm = wave_max(hm);
+        if ((t & 63) == 0) {
+            sh.red_d[wave] = ss;
+            sh.red_m[wave] = hm;
+        }
         lds_barrier();
-        double tot = 0.0;
-#pragma unroll
-        for (int w = 0; w < kCWaves; ++w) tot += sh.red_d[w];
-        const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
+        const float r = (float)(1.0 / sqrt(sum16(sh.red_d) / (double)K + (double)eps));
+        if (!has_gain) {
+            // without a gain the largest |h * r| is float(max |h| * r): the
+            // rounded product is monotone in the first factor and odd, so the
+            // maximum commutes with it (one exchange saved)
+            mx = max16(sh.red_m) * r;
+            have_max = true;
+        }
 #pragma unroll
         for (int i = 0; i < kCNormChunks; ++i) {
             const int c = t + kCThreads * i;
@@ -396,17 +435,17 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
             v[i][2] = (v[i][2] * r) * g.z; v[i][3] = (v[i][3] * r) * g.w;
         }
     }
-    float am = 0.0f;
+    if (!have_max) {
+        float am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kCNormChunks; ++i)
+        for (int i = 0; i < kCNormChunks; ++i)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) am = fmaxf(am, fabsf(v[i][f]));
-    am = wave_max(am);
-    if ((t & 63) == 0) sh.red_f[wave] = am;
-    lds_barrier();
-    float mx = sh.red_f[0];
-#pragma unroll
-    for (int w = 1; w < kCWaves; ++w) mx = fmaxf(mx, sh.red_f[w]);
+            for (int f = 0; f < 4; ++f) am = fmaxf(am, fabsf(v[i][f]));
+        am = wave_max(am);
+        if ((t & 63) == 0) sh.red_f[wave] = am;
+        lds_barrier();
+        mx = max16(sh.red_f);
+    }
     const float a = 127.0f / fmaxf(mx, 1e-5f);
     int cs = 0;
 #pragma unroll

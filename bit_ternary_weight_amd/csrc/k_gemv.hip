@@ -564,8 +564,14 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
     };
     int step = 0;
     float r[kFuseMaxM] = {1.0f, 1.0f, 1.0f, 1.0f};
+    // Without a gain the norm's largest |h * r| is float(max |h| * r) (the
+    // rounded product is monotone in the first factor and odd): the maximum
+    // travels with the sum of squares and one rendezvous is saved.
+    const bool fold = NORM && p.gain == nullptr;
+    float amax[kFuseMaxM] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (NORM) {
         double ss[kFuseMaxM] = {0.0, 0.0, 0.0, 0.0};
+        float hm = 0.0f;
 #pragma unroll
         for (int j = 0; j < kXRegs; ++j) {
             if (j >= nreg) break;
@@ -573,7 +579,10 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
             chunk_f32<PER>(reg(j), v);
             double t = 0.0;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) t += (double)v[i] * (double)v[i];
+            for (int i = 0; i < PER; ++i) {
+                t += (double)v[i] * (double)v[i];
+                hm = fmaxf(hm, fabsf(v[i]));
+            }
             row_update(ss, row_of(j), t, [](double a, double b) { return a + b; });
         }
 #pragma unroll
@@ -581,6 +590,11 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
             if (m >= M) break;
             const double w = wave_sum_dpp(ss[m]);
             if ((threadIdx.x & 63) == 0) part_d[m * kQuantWaves + qw] = w;
+        }
+        if (fold) {
+            // NORM: one row
+            const float w = wave_max_dpp(hm);
+            if ((threadIdx.x & 63) == 0) part_f[qw] = w;
         }
         publish(qflag, qw, ++step);
         wait_published<1>(qflag, step);
@@ -592,36 +606,48 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
             for (int w = 1; w < kQuantWaves; ++w) t += part_d[m * kQuantWaves + w];
             r[m] = (float)(1.0 / sqrt(t / (double)K + (double)p.eps));
         }
-    }
-    float amax[kFuseMaxM] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (fold) {
+            float t = part_f[0];
 #pragma unroll
-    for (int j = 0; j < kXRegs; ++j) {
-        if (j >= nreg) break;
-        float v[PER];
-        chunk_f32<PER>(reg(j), v);
-        const int m = row_of(j);
-        if (NORM) norm(v, j, r[0]);
-        float t = 0.0f;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) t = fmaxf(t, fabsf(v[i]));
-        row_update(amax, m, t, [](float a, float b) { return fmaxf(a, b); });
+            for (int w = 1; w < kQuantWaves; ++w) t = fmaxf(t, part_f[w]);
+            amax[0] = t * r[0];
+        }
     }
+    if (!fold) {
 #pragma unroll
-    for (int m = 0; m < kFuseMaxM; ++m) {
-        if (m >= M) break;
-        const float w = wave_max_dpp(amax[m]);
-        if ((threadIdx.x & 63) == 0) part_f[m * kQuantWaves + qw] = w;
+        for (int j = 0; j < kXRegs; ++j) {
+            if (j >= nreg) break;
+            float v[PER];
+            chunk_f32<PER>(reg(j), v);
+            const int m = row_of(j);
+            if (NORM) norm(v, j, r[0]);
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) t = fmaxf(t, fabsf(v[i]));
+            row_update(amax, m, t, [](float a, float b) { return fmaxf(a, b); });
+        }
+#pragma unroll
+        for (int m = 0; m < kFuseMaxM; ++m) {
+            if (m >= M) break;
+            const float w = wave_max_dpp(amax[m]);
+            if ((threadIdx.x & 63) == 0) part_f[m * kQuantWaves + qw] = w;
+        }
+        publish(qflag, qw, ++step);
+        wait_published<1>(qflag, step);
+#pragma unroll
+        for (int m = 0; m < kFuseMaxM; ++m) {
+            if (m >= M) break;
+            float t = part_f[m * kQuantWaves];
+#pragma unroll
+            for (int w = 1; w < kQuantWaves; ++w) t = fmaxf(t, part_f[m * kQuantWaves + w]);
+            amax[m] = t;
+        }
     }
-    publish(qflag, qw, ++step);
-    wait_published<1>(qflag, step);
     float s[kFuseMaxM] = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
     for (int m = 0; m < kFuseMaxM; ++m) {
         if (m >= M) break;
-        float t = part_f[m * kQuantWaves];
-#pragma unroll
-        for (int w = 1; w < kQuantWaves; ++w) t = fmaxf(t, part_f[m * kQuantWaves + w]);
-        s[m] = 127.0f / fmaxf(t, kFloor);   // IEEE fp32 division
+        s[m] = 127.0f / fmaxf(amax[m], kFloor);   // IEEE fp32 division
         if (threadIdx.x == (unsigned)(kStreamWaves * 64)) a_s[m] = s[m];
     }
     int qsum[kFuseMaxM] = {0, 0, 0, 0};
@@ -878,8 +904,9 @@ void k_gemv_lds(GemvBatch b) {
                 // this k-range's units have landed (loads complete in order)
                 wait_vm_upto11((nb - 1 - t) << lupk);
                 // the activation codes (once; the quantizer waves publish once per
-                // reduction -- the norm's sum of squares, the absmax -- and once when done)
-                if (b0 == 0 && t == 0) wait_published<4>(qflag, NORM ? 3 : 2);
+                // reduction -- the norm's sum of squares, the absmax unless it
+                // travels with the sum -- and once when done)
+                if (b0 == 0 && t == 0) wait_published<4>(qflag, NORM && p.gain != nullptr ? 3 : 2);
                 const int kr = kr0 + kstep * (b0 + t);
                 const unsigned char *slot = ring + (t * UPK + (rr >> 2)) * 1024 + 256 * (rr & 3);
                 // all operand reads of the k-range first: one LDS round trip
@@ -1251,8 +1278,9 @@ void k_gemv_v1(GemvBatch b) {
 #pragma clang loop unroll(full)
         for (int t = 1; t < NS; ++t) load_unit(t);
         // the activation codes (the quantizer waves publish once per
-        // reduction -- the norm's sum of squares, the absmax -- and once when done)
-        wait_published<4>(qflag, NORM ? 3 : 2);
+        // reduction -- the norm's sum of squares, the absmax unless it travels
+        // with the sum -- and once when done)
+        wait_published<4>(qflag, NORM && p.gain != nullptr ? 3 : 2);
         if (tid < 4 * CS * 4) {
             const int f = tid & 3;
             const int vr = r0 + (tid >> 2);
