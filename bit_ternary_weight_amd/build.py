@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbitlinear.so")
 
-SOURCES = ["bl_api.hip", "k_quant.hip", "k_ternarize.hip", "k_gemv.hip", "k_gemm.hip", "k_attn.hip", "k_attn_prefill.hip", "k_ste.hip", "k_unpacked.hip", "k_chain.hip", "k_binary.hip"]
+SOURCES = ["bl_api.hip", "k_quant.hip", "k_ternarize.hip", "k_gemv.hip", "k_gemv_mt.hip", "k_gemm.hip", "k_attn.hip", "k_attn_prefill.hip", "k_ste.hip", "k_unpacked.hip", "k_chain.hip", "k_binary.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -308,6 +308,15 @@ hipError_t launch_gemv_batch(GemvBatch &b, hipStream_t s);
 // Host check: decode problems with these M and K can go to the batched
 // streaming kernel (k_gemv_mt), whose codes the quantizer then writes tiled.
 bool gemv_mt_plan_ok(int n, const int *Ms, const int *Ks);
+// Batched decode with tiled codes (k_gemv_mt.hip): every problem fits the
+// kernel (tiled codes with their row sums, no gate|up pairing, K a multiple
+// of 256, aligned operands), and its launch (hipErrorNotSupported when some
+// problem's K needs more blocks per wave than the kernel holds).
+bool gemv_mt_ok(const GemvBatch &b);
+hipError_t launch_gemv_mt(GemvBatch &b, hipStream_t s);
+// The batch's weight bytes (nb tensors per problem) divided evenly over cus
+// workgroups: the per-workgroup budget the decode launchers size tiles by.
+size_t even_share(const GemvBatch &b, int nb, int cus);
 // Decode attention (k_attn.hip): workspace bytes (the per-chunk partial
 // results for n_heads query heads over max_seq positions), the largest
 // max_seq it serves, and the launches.
