@@ -114,6 +114,9 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     return r;
 }
 
+// NCH: float4 chunks per thread, the smallest count that covers the
+// launch's largest K (the unrolled loops do no work past it).
+template <int NCH>
 __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
     (void)unused;
     __shared__ double red_d[4];
@@ -123,11 +126,11 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
     const int p = problem_of(b, m);
     const W1Problem &pr = b.p[p];
     const int K = pr.K, nc = K >> 2, t = threadIdx.x;
-    float v[kLnMaxChunks][4];
+    float v[NCH][4];
     if (pr.x_dt == BL_BF16) {
         const uint16_t *row = static_cast<const uint16_t *>(pr.x) + (size_t)m * pr.ldx;
 #pragma unroll
-        for (int j = 0; j < kLnMaxChunks; ++j) {
+        for (int j = 0; j < NCH; ++j) {
             const int c = t + kT * j;
             uint2 u = make_uint2(0u, 0u);
             if (c < nc) u = *reinterpret_cast<const uint2 *>(row + 4 * c);
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
     } else {
         const float *row = static_cast<const float *>(pr.x) + (size_t)m * pr.ldx;
 #pragma unroll
-        for (int j = 0; j < kLnMaxChunks; ++j) {
+        for (int j = 0; j < NCH; ++j) {
             const int c = t + kT * j;
             float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (c < nc) u = *reinterpret_cast<const float4 *>(row + 4 * c);
@@ -146,13 +149,13 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
     }
     double s = 0.0;
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j)
+    for (int j = 0; j < NCH; ++j)
 #pragma unroll
         for (int f = 0; f < 4; ++f) s += (double)v[j][f];   // chunks past K hold zeros
     const double mu = block_sum(s, red_d) / (double)K;
     double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j)
+    for (int j = 0; j < NCH; ++j)
         if (t + kT * j < nc)
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
     const float r = (float)(1.0 / sqrt(var + (double)b.eps));
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         const int c = t + kT * j;
         if (c < nc) {
             float4 g = make_float4(1.0f, 1.0f, 1.0f, 1.0f), be = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
     const float a = 127.0f / fmaxf(block_max(am, red_f), 1e-5f);
     int8_t *qrow = pr.q + (size_t)m * K;
 #pragma unroll
-    for (int j = 0; j < kLnMaxChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         const int c = t + kT * j;
         if (c < nc) {
             uint32_t w = 0;
@@ -659,7 +662,18 @@ hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s) 
         start += probs[i].M;
     }
     b.start[n] = start;
-    hipLaunchKernelGGL(k_ln_quant, dim3(start), dim3(kT), 0, s, b);
+    int maxk = 4;
+    for (int i = 0; i < n; ++i) maxk = probs[i].K > maxk ? probs[i].K : maxk;
+    const int nch = (maxk / 4 + kT - 1) / kT;   // <= kLnMaxChunks (host-checked)
+    switch (nch) {
+#define BL_LN_CASE(c) \
+    case c: hipLaunchKernelGGL(k_ln_quant<c>, dim3(start), dim3(kT), 0, s, b); break;
+        BL_LN_CASE(1) BL_LN_CASE(2) BL_LN_CASE(3) BL_LN_CASE(4) BL_LN_CASE(5) BL_LN_CASE(6) BL_LN_CASE(7) BL_LN_CASE(8)
+        BL_LN_CASE(9) BL_LN_CASE(10) BL_LN_CASE(11) BL_LN_CASE(12) BL_LN_CASE(13) BL_LN_CASE(14) BL_LN_CASE(15)
+        BL_LN_CASE(16)
+#undef BL_LN_CASE
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
