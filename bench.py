@@ -280,6 +280,27 @@ def cpu_baseline():
             "flags": " ".join(oracle.CFLAGS)}
 
 
+def q1_disagreement_count(W, m) -> int:
+    """Weights whose ternary code differs between the two readings of the
+    weight quantization ("Transformers 实战 BitNet 1.58 位量化", section
+    "BitLinear 的三步量化"): W / m rounded half to even, against W * fl(1/m),
+    both in fp32 and clamped to [-1, 1].  They differ only where |W| / m lies
+    within about an ulp of 0.5 (m = 0.023221396, W one ulp above m / 2: the
+    quotient rounds to 0.50000006, code 1; the product to 0.5, code 0)."""
+    import numpy as np
+    W = np.asarray(W, np.float32)
+    m = np.float32(m)
+    a = np.clip(np.rint(W / m), -1, 1)
+    b = np.clip(np.rint(W * (np.float32(1.0) / m)), -1, 1)
+    return int(np.count_nonzero(a != b))
+
+
+def absmean_f32(W) -> "np.float32":
+    """mean |W| with an fp64 sum, floored at 1e-5, rounded to fp32."""
+    import numpy as np
+    return np.float32(max(float(np.abs(W).astype(np.float64).sum()) / W.size, 1e-5))
+
+
 ATTN_CTX = 4096
 
 
@@ -786,6 +807,15 @@ def main():
         t = timer.run(lambda: bl.ternarize_pack(W, packed=pk, w_mean=wm), 20, 3)
         extra["ternarize_pack_gbs"] = round((W.numel() * 4 + pk.numel()) / (t * 1e-3) / 1e9, 1)
         del W
+        # the two readings of the weight quantization (divide by the mean,
+        # multiply by its reciprocal) over one layer's 7 masters, on the host
+        nq, nw = 0, 0
+        for p, _, _ in synth.PROJECTIONS:
+            Wh = synth.layer_weight(0, p)
+            nq += q1_disagreement_count(Wh, absmean_f32(Wh))
+            nw += Wh.size
+        extra["divide_vs_reciprocal_code_disagreements"] = {"weights": nw, "disagree": nq}
+        log(f"weight codes that differ between W / mean and W * (1 / mean): {nq} of {nw}")
 
     line = {
         "metric": "W1.58A8 BitLinear decode GEMV HBM GB/s (M=1, 7 projections of a 2B4T layer per step)",

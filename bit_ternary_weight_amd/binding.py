@@ -18,7 +18,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+# BL_LIBRARY names another build of the same library (for example one whose
+# host code carries sanitizers); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("BL_LIBRARY") or os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_SEGMENTS, BL_ERR_WORKSPACE, BL_ERR_HIP = range(8)
 BL_F32, BL_BF16, BL_I8, BL_I32 = range(4)

@@ -11,7 +11,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
-LIB = os.path.join(ROOT, "bit_ternary_weight_amd", "libbitlinear.so")
+LIB = os.environ.get("BL_LIBRARY") or os.path.join(ROOT, "bit_ternary_weight_amd", "libbitlinear.so")
 
 
 def declared_functions():
@@ -373,3 +373,9 @@ def test_w1_validation(lib):
     assert bw(arr=bad) == lib.BL_ERR_DTYPE
     bad = (W1 * 2)(ok, W1(FAKE.value, 1, 1, 2560, None, None, FAKE.value, 3844, FAKE.value, FAKE.value))
     assert bw(arr=bad) == lib.BL_ERR_SHAPE
+
+
+def test_loaded_library_is_the_requested_build(lib):
+    """BL_LIBRARY, when set, names the build the binding loads (the sanitizer
+    run relies on it); otherwise the in-tree library."""
+    assert os.path.abspath(lib.LIB_PATH) == os.path.abspath(LIB)
