@@ -315,6 +315,173 @@ __global__ __launch_bounds__(kT) void k_w1_gemm(W1Batch unused) {
 }
 
 // ---------------------------------------------------------------------------
+// Contraction, large tiles (K a multiple of 128): 128 tokens x 32 packed rows
+// (256 output columns over the 8 bit planes) per 4-wave workgroup, waves in
+// a 2 x 2 grid (64 tokens x 16 packed rows each), two workgroups per CU.
+// K advances in stages of 128 bytes per row through a 3-stage LDS ring fed
+// by direct global->LDS loads (1 KB = 8 whole rows per load); one workgroup
+// barrier per stage publishes stage s and certifies that every wave is done
+// with stage s - 1, whose slot the loads of stage s + 2 reuse.  The 16-byte
+// chunk c of tile row r sits at c ^ ((r >> 1) & 7), so a fragment read (16
+// rows, one chunk each) spreads over all banks.  Each packed fragment is
+// split into its 8 bit planes in registers and goes through the matrix cores
+// once per plane with the weights as the first operand: lane (g, l) ends
+// with packed rows 4 g .. 4 g + 3 of token l, four consecutive output
+// columns of plane p (column p * N/8 + packed row).  The tokens' code sums
+// come from the same operand reads.  Rows past M or N/8 read row 0 and are
+// never stored.
+// ---------------------------------------------------------------------------
+constexpr int kWBK = 128;                        // k bytes per stage
+constexpr int kWBStages = 3;
+constexpr int kWBTM = 128;                       // tokens per tile
+constexpr int kWBTR = 32;                        // packed rows per tile
+constexpr int kWBA = kWBTM * kWBK;               // A bytes per stage
+constexpr int kWBStage = kWBA + kWBTR * kWBK;    // 20 KB
+constexpr int kWBDA = kWBA / (4 * 1024);         // 1 KB loads of A per wave per stage
+constexpr int kWBDB = kWBTR * kWBK / (4 * 1024); // of B
+constexpr int kWBDW = kWBDA + kWBDB;
+
+template <int VM>
+__device__ __forceinline__ void wb_wait_vm() {
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | (0x7 << 4) | (0xF << 8) | ((VM >> 4) << 14));
+}
+
+__device__ __forceinline__ void wb_dma16(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wb_lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Tiles of problem p: ceil(M / 128) token tiles x ceil(N/8 / 32) row tiles.
+__host__ __device__ inline int wb_tiles(int M, int N) {
+    return ((M + kWBTM - 1) / kWBTM) * ((N / 8 + kWBTR - 1) / kWBTR);
+}
+
+template <bool VOUT>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_w1_gemm_big(W1Batch unused) {
+    (void)unused;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kWBStages * kWBStage];
+    const W1Batch &b = batch();
+    int local = 0;
+    const int p = problem_of(b, local);
+    const W1Problem &pr = b.p[p];
+    const int K = pr.K, M = pr.M, N = pr.N, R = N >> 3;
+    const int ntm = (M + kWBTM - 1) / kWBTM;
+    const int m0 = (local % ntm) * kWBTM, r0 = (local / ntm) * kWBTR;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int nst = K / kWBK;
+    auto swz = [](int r) { return (r >> 1) & 7; };
+
+    // this lane's part of each 1 KB load: row lane / 8 of the load's 8, chunk slot lane % 8
+    const int lrow = lane >> 3, lpos = lane & 7;
+    const int8_t *a_src[kWBDA];
+#pragma unroll
+    for (int i = 0; i < kWBDA; ++i) {
+        const int row = (wave * kWBDA + i) * 8 + lrow;
+        const int m = m0 + row < M ? m0 + row : 0;
+        a_src[i] = pr.q + (size_t)m * K + 16 * (lpos ^ swz(row));
+    }
+    const uint8_t *b_src[kWBDB];
+#pragma unroll
+    for (int i = 0; i < kWBDB; ++i) {
+        const int row = (wave * kWBDB + i) * 8 + lrow;
+        const int r = r0 + row < R ? r0 + row : 0;
+        b_src[i] = pr.P + (size_t)r * K + 16 * (lpos ^ swz(row));
+    }
+    auto issue = [&](int st) {
+        unsigned char *base = lds + (st % kWBStages) * kWBStage;
+        const size_t k0 = (size_t)st * kWBK;
+#pragma unroll
+        for (int i = 0; i < kWBDA; ++i) wb_dma16(a_src[i] + k0, base + (wave * kWBDA + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < kWBDB; ++i) wb_dma16(b_src[i] + k0, base + kWBA + (wave * kWBDB + i) * 1024);
+    };
+
+    v4i acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[i][q] = v4i{0, 0, 0, 0};
+    int qs[4] = {0, 0, 0, 0};
+    int aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[i] = (wm * 64 + i * 16 + lr) * kWBK;
+    const int boff = kWBA + (wn * 16 + lr) * kWBK;
+    const int lsw = swz(lr);   // fragment rows start at multiples of 16
+    auto chunk = [&](int ch) { return 16 * (ch ^ lsw); };
+
+    wb_lds_barrier();
+    issue(0);
+    if (nst > 1) issue(1);
+    for (int st = 0; st < nst; ++st) {
+        if (st + 1 < nst) wb_wait_vm<kWBDW>();
+        else wb_wait_vm<0>();
+        wb_lds_barrier();
+        if (st + 2 < nst) issue(st + 2);
+        const unsigned char *base = lds + (st % kWBStages) * kWBStage;
+        v4i af[4], bw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i *>(base + aoff[i] + chunk(g));
+        bw = *reinterpret_cast<const v4i *>(base + boff + chunk(g));
+#pragma unroll
+        for (int ks = 0; ks < kWBK / 64; ++ks) {
+            v4i an[4], bn;
+            if (ks + 1 < kWBK / 64) {
+                const int ch = 4 * (ks + 1) + g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) an[i] = *reinterpret_cast<const v4i *>(base + aoff[i] + chunk(ch));
+                bn = *reinterpret_cast<const v4i *>(base + boff + chunk(ch));
+            }
+            v4i f[8];
+            planes(bw, f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qs[i] += rowsum16(af[i]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[i][q] = mfma16(f[q], af[i], acc[i][q]);
+            }
+            if (ks + 1 < kWBK / 64) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) af[i] = an[i];
+                bw = bn;
+            }
+        }
+    }
+
+    // Epilogue: A = 2 (S >> plane shift) - (token code sum); y = float(A) * (w_scale / a).
+    const float wsc = pr.w_scale[0];
+    const int vr0 = r0 + wn * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int s = qs[i];
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        const int m = m0 + wm * 64 + i * 16 + lr;
+        if (m >= M || vr0 >= R) continue;
+        const float sc = wsc / pr.a[m];
+        float *yrow = pr.y + (size_t)m * N;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int sh = q < 7 ? q : 6;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (float)(2 * (acc[i][q][j] >> sh) - s) * sc;
+            if (VOUT) {
+                *reinterpret_cast<float4 *>(yrow + (size_t)q * R + vr0) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (vr0 + j < R) yrow[(size_t)q * R + vr0 + j] = v[j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode (M = 1, K a multiple of 256 up to 8192): norm, quantization and
 // contraction in one launch.  One 16-wave workgroup per 16 packed rows over
 // all of K, cut into units of 4 packed rows x 256 bytes (lane (g, l) loads
@@ -728,6 +895,30 @@ hipError_t launch_w1_decode(const W1Args *probs, int n, float eps, hipStream_t s
 hipError_t launch_w1_gemm(const W1Args *probs, int n, hipStream_t s) {
     W1Batch b{};
     b.n = n;
+    // Large tiles when every K is whole 128-byte stages, the operands are
+    // 16-byte aligned and the launch holds at least one tile per CU.
+    bool big = true, vout = true;
+    int big_tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        const W1Args &a = probs[i];
+        big = big && a.K % kWBK == 0 && (uintptr_t)a.q % 16 == 0 && (uintptr_t)a.P % 16 == 0;
+        vout = vout && a.N % 32 == 0 && (uintptr_t)a.y % 16 == 0;
+        big_tiles += wb_tiles(a.M, a.N);
+    }
+    if (big && big_tiles >= device_cu_count()) {
+        int start = 0;
+        for (int i = 0; i < n; ++i) {
+            b.p[i] = to_problem(probs[i]);
+            b.start[i] = start;
+            start += wb_tiles(probs[i].M, probs[i].N);
+        }
+        b.start[n] = start;
+        if (vout)
+            hipLaunchKernelGGL(k_w1_gemm_big<true>, dim3(start), dim3(kT), 0, s, b);
+        else
+            hipLaunchKernelGGL(k_w1_gemm_big<false>, dim3(start), dim3(kT), 0, s, b);
+        return hipGetLastError();
+    }
     int max_m = 0;
     for (int i = 0; i < n; ++i) max_m = probs[i].M > max_m ? probs[i].M : max_m;
     const int nt = max_m > 16 ? 2 : 1;

@@ -108,7 +108,10 @@ def _codes(rng, M, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 16), (1, 136, 48), (5, 2560, 2560), (16, 128, 64), (17, 264, 80),
                                    (33, 2560, 2560), (64, 6912, 2560), (1, 2560, 6912), (300, 1024, 2560),
-                                   (2, 8, 16384)])
+                                   (2, 8, 16384),
+                                   # at least one 128 x 32 tile per CU: the LDS-staged kernel (ragged token
+                                   # and row tiles; N/8 not a multiple of 4: scalar stores)
+                                   (1200, 8008, 256), (1000, 8000, 384), (2048, 6912, 2560)])
 def test_gemm_w1a8_matches_the_oracle(M, N, K):
     bl = _bl()
     rng = np.random.default_rng(M * 7 + N + K)
@@ -158,7 +161,7 @@ def test_bitlinear_w1_seven_projections_decode():
         assert_exact(host(p["y"]).view(np.uint32), ref.view(np.uint32), f"projection {j}")
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 2560, 2560), (64, 6912, 2560), (200, 2560, 6912)])
+@pytest.mark.parametrize("M,N,K", [(2048, 2560, 2560), (64, 6912, 2560), (200, 2560, 6912), (2048, 6912, 2560)])
 def test_bitlinear_w1_prefill_all_rows(M, N, K):
     """Prefill sizes, every output row, with gain and bias."""
     bl = _bl()
