@@ -50,6 +50,7 @@ struct W1Batch {
     W1Problem p[kMaxProblems];
     int n;
     int start[kMaxProblems + 1];   // first workgroup of each problem
+    int quads[kMaxProblems];       // single-token launch: row quads (4 packed rows) per workgroup, 1, 2 or 4
     float eps;
 };
 
@@ -509,7 +510,8 @@ constexpr int kDQW = 8;                      // quantizer waves (sum8 / max8 rea
 constexpr int kDSW = 8;                      // stream waves
 constexpr int kDT = (kDQW + kDSW) * 64;
 constexpr int kDQT = kDQW * 64;
-constexpr int kDU = 16;                      // k-units per stream wave: two waves per row quad, K / 256 <= 32
+constexpr int kDU = 16;                      // k-units per stream wave: at least two waves per row quad, K / 256 <= 32
+constexpr int kDUnitsCap = 5;                // k-units per stream wave above which tiles shrink
 constexpr int kDChunks = 8192 / 4 / kDQT;         // float4 input chunks per quantizer thread
 
 // Workgroup barrier waiting for LDS operations only; the scheduling fences
@@ -595,18 +597,28 @@ __device__ __forceinline__ float max8(const float *p) {
 // the wave goes on).
 __device__ unsigned int g_w1_expired = 0;
 
-__device__ __forceinline__ void q_sync(volatile int *flag, int qw, int step) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+// A poll is two 16-byte LDS reads (one wait) and scalar compares: read one
+// flag at a time, each behind its own wait, a poll took about 0.4 us and a
+// rendezvous up to two of them.  The compiler memory clobbers make every poll
+// read LDS again and keep the flag store and the partials' reads in place.
+__device__ __forceinline__ void q_sync(int *flag, int qw, int step) {
+    static_assert(kDQW == 8, "two 16-byte reads cover the flags");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's partials are in LDS
+    asm volatile("" ::: "memory");
     if ((threadIdx.x & 63) == 0) flag[qw] = step;
     int lo = 0;
     for (int it = 0; it < (1 << 22); ++it) {
-        lo = flag[0];
+        asm volatile("" ::: "memory");
+        const v4i f = *reinterpret_cast<const v4i *>(flag);
+        const v4i h = *reinterpret_cast<const v4i *>(flag + 4);
+        lo = step;
 #pragma unroll
-        for (int w = 1; w < kDQW; ++w) lo = min(lo, flag[w]);
-        lo = __builtin_amdgcn_readfirstlane(lo);
+        for (int i = 0; i < 4; ++i)
+            lo = min(lo, min(__builtin_amdgcn_readfirstlane(f[i]), __builtin_amdgcn_readfirstlane(h[i])));
         if (lo >= step) break;
     }
     if (lo < step && (threadIdx.x & 63) == 0) atomicAdd(&g_w1_expired, 1u);
+    asm volatile("" ::: "memory");
 }
 
 template <bool BF16>
@@ -619,14 +631,15 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
     __shared__ __attribute__((aligned(16))) float rm[kDQW];     // per-wave max |float(x - mu)|
     __shared__ __attribute__((aligned(16))) float rf[kDQW];     // per-wave max |x'| (with gain or bias)
     __shared__ int ri[kDQW];
-    __shared__ int flag[kDQW];
+    __shared__ __attribute__((aligned(16))) int flag[kDQW];
     const W1Batch &b = batch();
     int local = 0;
     const int p = problem_of(b, local);
     const W1Problem &pr = b.p[p];
     const int K = pr.K, R = pr.N >> 3, nku = K >> 8, nu = 4 * nku;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4;
-    const int r0 = local * 16;
+    const int lq = b.quads[p] == 4 ? 2 : (b.quads[p] == 2 ? 1 : 0);   // log2 of the row quads
+    const int r0 = local * (4 << lq);
     float a = 1.0f;
 
     if (wave < kDQW) {
@@ -635,23 +648,29 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         if (lane == 0) flag[wave] = 0;
         if (tid < 8 * 16) (&red[0][0])[tid] = 0;
         // every load unconditional, at a clamped valid address (chunks past K
-        // read chunk 0, absent gains read the row's first 16 bytes), zeroed or
-        // replaced afterwards: a branch around a load would make the compiler
-        // wait for the loads before it
+        // read chunk 0; absent gains read 16 bytes of the row itself, at an
+        // offset of their own per lane: one address shared by every lane of
+        // the launch would queue on one L2 channel), zeroed or replaced
+        // afterwards: a branch around a load would make the compiler wait for
+        // the loads before it
         float xv[kDChunks][4];
         uint2 xb[kDChunks];
         float4 xf[kDChunks], gq[kDChunks], bq[kDChunks];
-        const float *gsrc = pr.gamma ? pr.gamma : static_cast<const float *>(pr.x);
-        const float *bsrc = pr.beta ? pr.beta : static_cast<const float *>(pr.x);
+        const float *xrow = static_cast<const float *>(pr.x);
+        const int xfl = BF16 ? K / 2 : K;   // the row's length in floats
 #pragma unroll
         for (int i = 0; i < kDChunks; ++i) {
             const int c = tid + kDQT * i;
             const int cc = c < nc ? c : 0;
             if (BF16) xb[i] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(pr.x) + 4 * cc);
             else xf[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(pr.x) + 4 * cc);
-            gq[i] = *reinterpret_cast<const float4 *>(gsrc + (pr.gamma ? 4 * cc : 0));
-            bq[i] = *reinterpret_cast<const float4 *>(bsrc + (pr.beta ? 4 * cc : 0));
+            const int xo = 4 * cc < xfl ? 4 * cc : 4 * cc - xfl;   // < xfl - 3: in the row
+            gq[i] = *reinterpret_cast<const float4 *>(pr.gamma ? pr.gamma + 4 * cc : xrow + xo);
+            bq[i] = *reinterpret_cast<const float4 *>(pr.beta ? pr.beta + 4 * cc : xrow + xo);
         }
+        // the weight scale for the epilogue, fetched with the row (read at
+        // the end it would be a memory round trip behind the weight stream)
+        const float wsc = pr.w_scale[0];
         d_barrier();   // every row and gain load issued: the weight stream may start
 #pragma unroll
         for (int i = 0; i < kDChunks; ++i) {
@@ -688,7 +707,8 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
                 for (int f = 0; f < 4; ++f) {
                     const double d = (double)xv[i][f] - mu;
                     ss += d * d;
-                    md = fmaxf(md, fabsf((float)d));
+                    xv[i][f] = (float)d;   // the normalization below needs only float(x - mu)
+                    md = fmaxf(md, fabsf(xv[i][f]));
                 }
         ss = d_wave_sum(ss);
         md = d_wave_max(md);
@@ -712,7 +732,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
             const float gg[4] = {gq[i].x, gq[i].y, gq[i].z, gq[i].w}, bb[4] = {bq[i].x, bq[i].y, bq[i].z, bq[i].w};
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                float o = (float)((double)xv[i][f] - mu) * r;
+                float o = xv[i][f] * r;   // float(x - mu) * r
                 if (pr.gamma) o = o * gg[f];
                 if (pr.beta) o = o + bb[f];
                 xv[i][f] = c < nc ? o : 0.0f;
@@ -749,19 +769,20 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         if (lane == 0) ri[wave] = cs;
         d_barrier();   // codes in LDS
         d_barrier();   // row sums in LDS
-        if (lane < 16 && r0 + lane < R) {   // wave w writes bit plane w
+        if (lane < (4 << lq) && r0 + lane < R) {   // wave w writes bit plane w
             int qsum = 0;
 #pragma unroll
             for (int w = 0; w < kDQW; ++w) qsum += ri[w];
             const int i = wave;
             const int A = 2 * (red[i][lane] >> (i < 7 ? i : 6)) - qsum;
-            pr.y[(size_t)i * R + r0 + lane] = (float)A * (pr.w_scale[0] / a);
+            pr.y[(size_t)i * R + r0 + lane] = (float)A * (wsc / a);
         }
     } else {
-        // ---- stream waves: every unit issued, then the products.  Wave w
-        // takes row quad w % 4 and every other 256-byte k-unit from w / 4,
-        // so its products accumulate in the matrix cores' accumulators
-        const int sw = wave - kDQW, q = sw & 3;
+        // ---- stream waves: every unit issued, then the products.  With Q
+        // row quads, wave w takes quad w % Q and every (8 / Q)-th 256-byte
+        // k-unit from w / Q, so its products accumulate in the matrix cores'
+        // accumulators
+        const int sw = wave - kDQW, q = sw & ((1 << lq) - 1), k0 = sw >> lq, kst = kDSW >> lq;
         const int urow = (lane & 15) >> 2, ch = (lane & 3) + 4 * g;
         int row = r0 + 4 * q + urow;
         const bool row_ok = row < R;
@@ -771,7 +792,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         v4i bw[kDU];
 #pragma unroll
         for (int j = 0; j < kDU; ++j) {
-            int ku = (sw >> 2) + 2 * j;
+            int ku = k0 + kst * j;
             ku = ku < nku ? ku : nku - 1;
             bw[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(pw + ku * 256));
         }
@@ -781,7 +802,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         for (int i = 0; i < 8; ++i) acc[i] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < kDU; ++j) {
-            const int ku = (sw >> 2) + 2 * j;
+            const int ku = k0 + kst * j;
             if (ku >= nku) break;   // uniform; the loads above were issued for every j
             const v4i cw = *reinterpret_cast<const v4i *>(qd + ku * 256 + 16 * ch);
             v4i f[8];
@@ -876,12 +897,19 @@ hipError_t launch_w1_decode(const W1Args *probs, int n, float eps, hipStream_t s
     for (int i = 0; i < n; ++i) order[i] = i;
     for (int i = 1; i < n; ++i)
         for (int j = i; j > 0 && probs[order[j]].K > probs[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
+    // Row quads per workgroup: 4 (16 packed rows) unless that gives a
+    // stream wave more than kDUnitsCap k-units (8 stream waves share the
+    // workgroup's quads x K/256 units): the longest rows get smaller tiles,
+    // so that no compute unit's matrix cores hold up the launch.
     int start = 0;
     for (int i = 0; i < n; ++i) {
         const W1Args &a = probs[order[i]];
         b.p[i] = to_problem(a);
         b.start[i] = start;
-        start += (a.N / 8 + 15) / 16;
+        int qd = 4;
+        while (qd > 1 && qd * (a.K / 256) > kDUnitsCap * kDSW) qd >>= 1;
+        b.quads[i] = qd;
+        start += (a.N / 8 + 4 * qd - 1) / (4 * qd);
     }
     b.start[n] = start;
     if (probs[0].x_dt == BL_BF16)
