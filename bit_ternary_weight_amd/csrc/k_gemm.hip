@@ -325,6 +325,10 @@ __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const
         g_lds_barrier();
         if (st + 2 < nst) issue(st + 2);
         const unsigned char *base = g_lds + (st % kGStages) * S::STAGE;
+        // Raised wave priority from the stage's operand reads to its last
+        // product: of the two workgroups sharing a CU, the one with operands in
+        // LDS issues first, the other's wait and barrier overlap it (3 %).
+        __builtin_amdgcn_s_setprio(1);
         // operands of k-step 0
 #pragma unroll
         for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const v4i *>(base + aoff[i] + chunk(g));
@@ -367,6 +371,7 @@ __device__ __forceinline__ void gemm_tile(const Contract &c, const int m0, const
                 for (int b = 0; b < NBW; ++b) bw[b] = bn[b];
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // Epilogue.  Lane (g, lr) holds, per token fragment i, weight fragment b
