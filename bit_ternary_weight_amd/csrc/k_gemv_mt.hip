@@ -200,6 +200,9 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
         const int sl = t & 1;
         const int cs = CB == 2 ? sl : 0;
         if (t < ks) {
+            // raised priority over the block's products: the other wave of
+            // the SIMD issues its loads meanwhile (64 tokens: 22.95 -> 22.45 us)
+            __builtin_amdgcn_s_setprio(1);
             // this wave's LDS operations run in order: the reads below see
             // these writes, and the next block's writes come after them
 #pragma unroll
@@ -224,6 +227,7 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
                     acc[u][3] = mfma16(f3, cv[cs][k][u], acc[u][3]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         if (CB == 2) {
             if (t + 2 < NB) {
