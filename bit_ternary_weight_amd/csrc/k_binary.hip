@@ -162,6 +162,7 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
             for (int f = 0; f < 4; ++f) {
                 const double d = (double)v[j][f] - mu;
                 ss += d * d;
+                v[j][f] = (float)d;   // the normalization needs only float(x - mu)
             }
     const double var = block_sum(ss, red_d) / (double)K;
     const float r = (float)(1.0 / sqrt(var + (double)b.eps));
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kT) void k_ln_quant(W1Batch unused) {
             const float gg[4] = {g.x, g.y, g.z, g.w}, bb[4] = {be.x, be.y, be.z, be.w};
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                float o = (float)((double)v[j][f] - mu) * r;
+                float o = v[j][f] * r;   // float(x - mu) * r
                 if (pr.gamma) o = o * gg[f];
                 if (pr.beta) o = o + bb[f];
                 v[j][f] = o;
@@ -837,32 +838,37 @@ static W1Problem to_problem(const W1Args &a) {
     return W1Problem{a.x, a.x_dt, a.ldx, a.gamma, a.beta, a.M, a.K, a.q, a.a, a.P, a.N, a.w_scale, a.y};
 }
 
-// The norm and quantization of every row of the problems (x, gamma, beta in;
-// q, a out), one launch.
-hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s) {
-    W1Batch b{};
-    b.n = n;
-    b.eps = eps;
-    int start = 0;
-    for (int i = 0; i < n; ++i) {
-        b.p[i] = to_problem(probs[i]);
-        b.start[i] = start;
-        start += probs[i].M;
-    }
-    b.start[n] = start;
-    int maxk = 4;
-    for (int i = 0; i < n; ++i) maxk = probs[i].K > maxk ? probs[i].K : maxk;
-    const int nch = (maxk / 4 + kT - 1) / kT;   // <= kLnMaxChunks (host-checked)
+// One launch of the norm over the rows of b, with NCH = nch.
+static hipError_t launch_ln(int nch, const W1Batch &b, int rows, hipStream_t s) {
     switch (nch) {
 #define BL_LN_CASE(c) \
-    case c: hipLaunchKernelGGL(k_ln_quant<c>, dim3(start), dim3(kT), 0, s, b); break;
+    case c: hipLaunchKernelGGL(k_ln_quant<c>, dim3(rows), dim3(kT), 0, s, b); break;
         BL_LN_CASE(1) BL_LN_CASE(2) BL_LN_CASE(3) BL_LN_CASE(4) BL_LN_CASE(5) BL_LN_CASE(6) BL_LN_CASE(7) BL_LN_CASE(8)
         BL_LN_CASE(9) BL_LN_CASE(10) BL_LN_CASE(11) BL_LN_CASE(12) BL_LN_CASE(13) BL_LN_CASE(14) BL_LN_CASE(15)
         BL_LN_CASE(16)
 #undef BL_LN_CASE
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;   // K above kLnMaxChunks * kT * 4 (host-checked)
     }
     return hipGetLastError();
+}
+
+// The norm and quantization of every row of the problems (x, gamma, beta in;
+// q, a out), one launch.  (One launch per chunk count measured the same:
+// the kernel is bound by each row's chain of loads and reductions, not by
+// the unrolled arithmetic.)
+hipError_t launch_w1_norm(const W1Args *probs, int n, float eps, hipStream_t s) {
+    W1Batch b{};
+    b.n = n;
+    b.eps = eps;
+    int rows = 0, maxk = 4;
+    for (int i = 0; i < n; ++i) {
+        b.p[i] = to_problem(probs[i]);
+        b.start[i] = rows;
+        rows += probs[i].M;
+        maxk = probs[i].K > maxk ? probs[i].K : maxk;
+    }
+    b.start[n] = rows;
+    return launch_ln((maxk / 4 + kT - 1) / kT, b, rows, s);
 }
 
 hipError_t w1_wait_expired(unsigned int *count, bool reset) {
