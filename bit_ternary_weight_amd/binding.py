@@ -75,7 +75,7 @@ _SIGS = {
     "bl_attn_prefill_workspace_bytes": (_S, [_I, _I, _I]),
     "bl_ste_grad_input_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "bl_ste_grad_weight_workspace_bytes": (_S, [_I, _I, _I]),
-    "bl_ste_grad_input": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
+    "bl_ste_grad_input": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_ste_grad_weight": (_I, [_P, _I, _P, _P, _I, _I, _I, _P, _P, _S, _P]),
     "bl_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _S, _P]),
     "bl_subln_gemv_workspace_bytes": (_S, [_I, _I]),
@@ -575,10 +575,11 @@ def attn_prefill(q, k, v, k_cache, v_cache, rope_cos, rope_sin, n_heads, n_kv_he
     return out
 
 
-def ste_grad_input(dy, packed, w_mean, dx=None):
+def ste_grad_input(dy, packed, w_mean, dx=None, dx_dtype=torch.float32):
     """dX = dY . (codes * w_mean) for dy [M,N] bf16 or fp32 (rounded to bf16
     on the device) and one packed weight segment [N/4,K] (see
-    bl_ste_grad_input); returns dx [M,K] fp32."""
+    bl_ste_grad_input); returns dx [M,K] in dx_dtype (fp32, or bf16 rounded
+    on the device), or in dx's dtype when dx is given."""
     dev = _dev(dy, packed, w_mean)
     M, N = dy.shape
     K = packed.shape[1]
@@ -586,11 +587,11 @@ def ste_grad_input(dy, packed, w_mean, dx=None):
     _need(packed, (N // 4, K), (torch.uint8,), "packed")
     _need(w_mean, (1,), (torch.float32,), "w_mean")
     if dx is None:
-        dx = torch.empty((M, K), dtype=torch.float32, device=dev)
-    _need(dx, (M, K), (torch.float32,), "dx")
+        dx = torch.empty((M, K), dtype=dx_dtype, device=dev)
+    _need(dx, (M, K), (torch.float32, torch.bfloat16), "dx")
     ws = workspace(dev, raw.bl_ste_grad_input_workspace_bytes(M, N, K, _dt(dy)))
-    _check(raw.bl_ste_grad_input(_ptr(dy), _dt(dy), M, N, K, _ptr(packed), _ptr(w_mean), _ptr(dx), _ptr(ws),
-                                 ws.numel(), _stream(dev)))
+    _check(raw.bl_ste_grad_input(_ptr(dy), _dt(dy), M, N, K, _ptr(packed), _ptr(w_mean), _ptr(dx), _dt(dx),
+                                 _ptr(ws), ws.numel(), _stream(dev)))
     return dx
 
 

@@ -912,17 +912,18 @@ static int ste_shape(const char *fn, int M, int N, int K, int dy_dtype) {
 }
 
 int bl_ste_grad_input(const void *dy, int dy_dtype, int M, int N, int K, const uint8_t *packed, const float *w_mean,
-                      float *dx, void *ws, size_t ws_bytes, bl_stream stream) {
+                      void *dx, int dx_dtype, void *ws, size_t ws_bytes, bl_stream stream) {
     g_err[0] = 0;
     const char *fn = "bl_ste_grad_input";
     if (!dy || !packed || !w_mean || !dx) return fail(BL_ERR_NULL, "%s: NULL pointer argument", fn);
     if (int st = ste_shape(fn, M, N, K, dy_dtype)) return st;
     if (N % 4) return fail(BL_ERR_SHAPE, "%s: N=%d is not a multiple of 4", fn, N);
-    if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(w_mean, 4))
+    if (dx_dtype != BL_F32 && dx_dtype != BL_BF16) return fail(BL_ERR_DTYPE, "%s: dx_dtype %d", fn, dx_dtype);
+    if (!aligned(dy, 16) || !aligned(dx, dx_dtype == BL_BF16 ? 8 : 16) || !aligned(w_mean, 4))
         return fail(BL_ERR_ALIGN, "%s: misaligned pointer", fn);
     if (int st = check_ws(fn, ws, ws_bytes, bl_ste_grad_input_workspace_bytes(M, N, K, dy_dtype))) return st;
-    return check_hip(bl::launch_ste_grad_input(dy, dy_dtype == BL_BF16, M, N, K, packed, w_mean, dx, ws,
-                                               (hipStream_t)stream),
+    return check_hip(bl::launch_ste_grad_input(dy, dy_dtype == BL_BF16, M, N, K, packed, w_mean, dx,
+                                               dx_dtype == BL_BF16, ws, (hipStream_t)stream),
                      fn);
 }
 

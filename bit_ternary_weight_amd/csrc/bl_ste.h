@@ -30,7 +30,7 @@ bool ste_dims_fit(int M, int N, int K);
 // dX [M][K] = (dY [M][N] . codes [N][K]) * w_mean[0] (device); dY bf16 or fp32
 // (rounded to bf16); N a multiple of 4.
 hipError_t launch_ste_grad_input(const void *dY, bool dy_bf16, int M, int N, int K, const uint8_t *packed,
-                                 const float *w_mean, float *dX, void *ws, hipStream_t s);
+                                 const float *w_mean, void *dX, bool dx_bf16, void *ws, hipStream_t s);
 // dW [N][K] = sum_m bf16(fp32(dY[m][n] / a[m])) * q[m][k]; dY bf16 or fp32.
 hipError_t launch_ste_grad_weight(const void *dY, bool dy_bf16, int M, int N, int K, const int8_t *q, const float *a,
                                   float *dW, void *ws, hipStream_t s);

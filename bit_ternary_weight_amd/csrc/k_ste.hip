@@ -135,7 +135,8 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 // C[i][j] = epilogue(sum_l A[i][l] B[j][l]) for i < Ir, j < Jr; A [I][L],
 // B [J][L] bf16 (zero-padded), C [Ir][Jr] with row stride Jr; I, J, L
 // multiples of 128, 128, 64.  Epilogues:
-//   EPI_SCALE: fp32 C = s * sum, s read from device memory (1 if null);
+//   EPI_SCALE: C = s * sum, s read from device memory (1 if null), fp32 or
+//     (e.y_dt = BL_BF16) rounded to bf16;
 //   EPI_BITLINEAR: the BitLinear rescale of an exact integer sum (the
 //     operands are int8 activation codes and ternary codes, every partial sum
 //     an integer below 2^24, so the fp32 accumulator holds it exactly):
@@ -254,6 +255,32 @@ __global__ __launch_bounds__(256) void k_gemm_nt_bf16(const __bf16 *A, const __b
         }
         return;
     }
+    if (e.y_dt == BL_BF16) {
+        // the scaled sums rounded to bf16 (round to nearest even), the
+        // caller's compute type
+        uint16_t *Cb = static_cast<uint16_t *>(Cv);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = i0 + wi + 16 * x + lr;
+            uint16_t *crow = Cb + (size_t)i * Jr + j0 + wj + 4 * g;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                uint16_t h[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) h[c] = f32_to_bf16(acc[x][y][c] * s);
+                if (whole) {
+                    *reinterpret_cast<uint2 *>(crow + 16 * y) =
+                        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                } else if (i < Ir) {
+                    const int j = j0 + wj + 4 * g + 16 * y;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (j + c < Jr) crow[16 * y + c] = h[c];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int i = i0 + wi + 16 * x + lr;
@@ -303,7 +330,7 @@ bool ste_dims_fit(int M, int N, int K) {
 }
 
 hipError_t launch_ste_grad_input(const void *dY, bool dy_bf16, int M, int N, int K, const uint8_t *packed,
-                                 const float *w_mean, float *dX, void *ws, hipStream_t s) {
+                                 const float *w_mean, void *dX, bool dx_bf16, void *ws, hipStream_t s) {
     const int L = pad_to(N, kL), I = pad_to(M, kT), J = pad_to(K, kT), R = N / 4;
     __bf16 *ct = static_cast<__bf16 *>(ws);
     hipLaunchKernelGGL(k_codes_t, dim3((R + 31) / 32, J / 64), dim3(256), 0, s, packed, R, K, L, ct);
@@ -323,8 +350,10 @@ hipError_t launch_ste_grad_input(const void *dY, bool dy_bf16, int M, int N, int
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
         A = dyb;
     }
-    hipLaunchKernelGGL(k_gemm_nt_bf16<EPI_SCALE>, dim3((I / kT) * (J / kT)), dim3(256), 0, s, A, ct, (void *)dX, I, J, L,
-                       M, K, w_mean, GemmEpi{});
+    GemmEpi e{};
+    e.y_dt = dx_bf16 ? BL_BF16 : BL_F32;
+    hipLaunchKernelGGL(k_gemm_nt_bf16<EPI_SCALE>, dim3((I / kT) * (J / kT)), dim3(256), 0, s, A, ct, dX, I, J, L, M,
+                       K, w_mean, e);
     return hipGetLastError();
 }
 

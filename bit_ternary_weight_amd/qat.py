@@ -34,12 +34,13 @@ def forward(x: torch.Tensor, W: torch.Tensor):
     return y, (packed, w_mean, q, a)
 
 
-def backward(dy: torch.Tensor, saved):
-    """dy [M,N] bf16 or fp32 -> (dx [M,K], dW [N,K]) fp32."""
+def backward(dy: torch.Tensor, saved, dx_dtype=torch.float32):
+    """dy [M,N] bf16 or fp32 -> (dx [M,K] in dx_dtype (fp32 or bf16, rounded on
+    the device), dW [N,K] fp32)."""
     packed, w_mean, q, a = saved
     if not dy.is_contiguous():
         raise ValueError("dy must be contiguous")
-    return bl.ste_grad_input(dy, packed, w_mean), bl.ste_grad_weight(dy, q, a)
+    return bl.ste_grad_input(dy, packed, w_mean, dx_dtype=dx_dtype), bl.ste_grad_weight(dy, q, a)
 
 
 class BitLinearFunction(torch.autograd.Function):
@@ -54,6 +55,6 @@ class BitLinearFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dy):
-        dx, dW = backward(dy, ctx.saved)
+        dx, dW = backward(dy, ctx.saved, dx_dtype=ctx.x_dtype)
         ctx.saved = None
-        return dx.to(ctx.x_dtype), dW
+        return dx, dW

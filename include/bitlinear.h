@@ -443,7 +443,9 @@ int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int
  *   packed  [N/4][K] uint8 device, one weight segment; w_mean [1] fp32 device;
  *   q, a    [M][K] int8 and [M] fp32 device: the forward's activation codes
  *           and scales (bl_quant_act);
- *   dx      out [M][K] fp32 device = (sum_n bf16(dy[m][n]) code[n][k]) * w_mean;
+ *   dx      out [M][K] device = (sum_n bf16(dy[m][n]) code[n][k]) * w_mean, in
+ *           dx_dtype BL_F32, or BL_BF16 (that fp32 value rounded to nearest
+ *           even: the input dtype of a bf16 layer, so no cast follows);
  *   dw      out [N][K] fp32 device = sum_m bf16(fp32(dy[m][n] / a[m])) q[m][k];
  *   ws      scratch of bl_ste_grad_input_workspace_bytes(M, N, K, dy_dtype) /
  *           bl_ste_grad_weight_workspace_bytes(M, N, K) bytes (the operands
@@ -452,12 +454,13 @@ int bl_attn_prefill(const float *q, const float *k, const float *v, int ldx, int
  * plain fp64 definitions differ by at most the bf16 rounding of the gradient
  * (relative 2^-8 per term) plus the fp32 sums.  Any M, N, K >= 1 (N a
  * multiple of 4 for dx), each product of two of them, rounded up to 128,
- * below 2^31; dx, dw 16-byte aligned; dy 16-byte aligned for dx.
+ * below 2^31; dw and an fp32 dx 16-byte aligned, a bf16 dx 8-byte aligned;
+ * dy 16-byte aligned for dx.  An unknown dx_dtype is BL_ERR_DTYPE.
  * ------------------------------------------------------------------------ */
 size_t bl_ste_grad_input_workspace_bytes(int M, int N, int K, int dy_dtype);
 size_t bl_ste_grad_weight_workspace_bytes(int M, int N, int K);
 int bl_ste_grad_input(const void *dy, int dy_dtype, int M, int N, int K, const uint8_t *packed,
-                      const float *w_mean, float *dx, void *ws, size_t ws_bytes, bl_stream stream);
+                      const float *w_mean, void *dx, int dx_dtype, void *ws, size_t ws_bytes, bl_stream stream);
 int bl_ste_grad_weight(const void *dy, int dy_dtype, const int8_t *q, const float *a, int M, int N, int K,
                        float *dw, void *ws, size_t ws_bytes, bl_stream stream);
 

@@ -279,13 +279,15 @@ def test_ste_validation(lib):
     assert raw.bl_ste_grad_input_workspace_bytes(100, 256, 384, BF) >= ni + 128 * 256 * 2
     assert raw.bl_ste_grad_input_workspace_bytes(128, 256, 384, 2) == 0
     ni100 = raw.bl_ste_grad_input_workspace_bytes(100, 200, 300, F)
-    assert gi(None, BF, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_NULL
-    assert gi(FAKE, BF, 0, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_SHAPE
-    assert gi(FAKE, F, 100, 202, 300, FAKE, FAKE, FAKE, FAKE, ni100, None) == lib.BL_ERR_SHAPE   # N % 4
-    assert gi(FAKE, 2, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_DTYPE
-    assert gi(FAKE_MIS, BF, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni, None) == lib.BL_ERR_ALIGN
-    assert gi(FAKE, BF, 128, 256, 384, FAKE, FAKE, FAKE, FAKE, ni - 1, None) == lib.BL_ERR_WORKSPACE
-    assert gi(FAKE, BF, 1 << 16, 1 << 16, 128, FAKE, FAKE, FAKE, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    assert gi(None, BF, 128, 256, 384, FAKE, FAKE, FAKE, F, FAKE, ni, None) == lib.BL_ERR_NULL
+    assert gi(FAKE, BF, 0, 256, 384, FAKE, FAKE, FAKE, F, FAKE, ni, None) == lib.BL_ERR_SHAPE
+    assert gi(FAKE, F, 100, 202, 300, FAKE, FAKE, FAKE, F, FAKE, ni100, None) == lib.BL_ERR_SHAPE   # N % 4
+    assert gi(FAKE, 2, 128, 256, 384, FAKE, FAKE, FAKE, F, FAKE, ni, None) == lib.BL_ERR_DTYPE
+    assert gi(FAKE_MIS, BF, 128, 256, 384, FAKE, FAKE, FAKE, F, FAKE, ni, None) == lib.BL_ERR_ALIGN
+    assert gi(FAKE, BF, 128, 256, 384, FAKE, FAKE, FAKE, F, FAKE, ni - 1, None) == lib.BL_ERR_WORKSPACE
+    assert gi(FAKE, BF, 1 << 16, 1 << 16, 128, FAKE, FAKE, FAKE, F, FAKE, BIG, None) == lib.BL_ERR_SHAPE
+    assert gi(FAKE, BF, 128, 256, 384, FAKE, FAKE, FAKE, 2, FAKE, ni, None) == lib.BL_ERR_DTYPE   # dx int8
+    assert gi(FAKE, BF, 128, 256, 384, FAKE, FAKE, FAKE_MIS, BF, FAKE, ni, None) == lib.BL_ERR_ALIGN
     assert gw(FAKE, BF, None, FAKE, 128, 256, 384, FAKE, FAKE, nw, None) == lib.BL_ERR_NULL
     assert gw(FAKE, BF, FAKE, FAKE, 128, 256, -1, FAKE, FAKE, nw, None) == lib.BL_ERR_SHAPE
     assert gw(FAKE, BF, FAKE, FAKE, 128, 256, 384, FAKE_MIS, FAKE, nw, None) == lib.BL_ERR_ALIGN

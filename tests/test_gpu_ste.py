@@ -26,7 +26,7 @@ import torch
 
 import oracle
 from bit_ternary_weight_amd import synth
-from gpu_helpers import bf16_dev, dev, f32_of_bf16, guarded, host, requires_gpu, to_dev
+from gpu_helpers import assert_exact, bf16_dev, dev, f32_of_bf16, guarded, host, requires_gpu, to_dev
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -84,6 +84,24 @@ def test_ste_grad_input(M, N, K, dy_kind):
     abs_t = np.abs(dy[rows]).astype(np.float64) @ c
     sq_t = (dy[rows].astype(np.float64) ** 2) @ (c ** 2)
     _check_bounds(got, ref, abs_t, sq_t, u_in, 0.0, "dx")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (100, 200, 300), (257, 132, 129), (1, 4, 1)])
+def test_ste_grad_input_bf16_output(M, N, K):
+    """dx requested in bf16 is the fp32 result rounded to nearest even
+    (oracle.to_bf16), element by element: the same products and sums, only
+    the store differs.  Whole and ragged tiles."""
+    bl = _bl()
+    packed, wm, codes = oracle.ternarize_pack(synth.master_weight(70 + K, N, K))
+    dyd = bf16_dev(synth.act_normal_bf16(71 + M, M, N))
+    P, W = to_dev(packed), to_dev(np.array([wm], np.float32))
+    f32 = guarded((M, K))
+    b16 = guarded((M, K), torch.bfloat16)
+    bl.ste_grad_input(dyd, P, W, dx=f32.t)
+    bl.ste_grad_input(dyd, P, W, dx=b16.t)
+    f32.check("dx fp32")
+    b16.check("dx bf16")
+    assert_exact(host(b16.t), oracle.to_bf16(host(f32.t)), "bf16 dx")
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES[:-1] + [(2048, 6912, 2560)])
@@ -147,3 +165,20 @@ def test_qat_forward_backward_autograd():
     qa = q.astype(np.float64)
     _check_bounds(host(Wd.grad).astype(np.float64), rw, np.abs(s).T @ np.abs(qa), (s ** 2).T @ (qa ** 2),
                   U + 2.0 ** -23, 0.0, "dw")
+
+
+def test_qat_backward_bf16_input():
+    """A bf16 input gets its gradient in bf16 from the library (no cast
+    after it): the fp32 input gradient of the same call, rounded to nearest
+    even."""
+    from bit_ternary_weight_amd import qat
+    M, N, K = 128, 256, 384
+    W = to_dev(synth.master_weight(98, N, K)).requires_grad_(True)
+    xb = bf16_dev(synth.act_normal_bf16(99, M, K)).requires_grad_(True)
+    y = qat.BitLinearFunction.apply(xb, W)
+    dy = to_dev(synth.act_normal_f32(100, M, N))
+    y.backward(dy)
+    assert xb.grad.dtype == torch.bfloat16
+    _, saved = qat.forward(xb.detach(), W.detach())
+    dx32, _ = qat.backward(dy, saved)
+    assert_exact(host(xb.grad), oracle.to_bf16(host(dx32)), "bf16 input gradient")
