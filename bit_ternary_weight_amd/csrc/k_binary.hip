@@ -423,7 +423,6 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         if (st + 1 < nst) wb_wait_vm<kWBDW>();
         else wb_wait_vm<0>();
         wb_lds_barrier();
-        if (st + 2 < nst) issue(st + 2);
         const unsigned char *base = lds + (st % kWBStages) * kWBStage;
         v4i af[4], bw;
 #pragma unroll
@@ -446,6 +445,9 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[i][q] = mfma16(f[q], af[i], acc[i][q]);
             }
+            // stage st + 2's loads after the first k-step's products (its
+            // slot was freed at this stage's barrier)
+            if (ks == 0 && st + 2 < nst) issue(st + 2);
             if (ks + 1 < kWBK / 64) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) af[i] = an[i];
