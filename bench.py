@@ -177,7 +177,7 @@ def cpu_baseline():
     core, on bounded samples of each workload; tokens are independent after
     ternarization, so a row sample's rate is the workload's rate.  Returns the
     cpu_baseline object: the headline (M=1, 7 projections of a layer) in
-    GB/s, the other workloads under per_config."""
+    GB/s, the other workloads under per_workload."""
     import numpy as np
 
     import oracle
@@ -214,20 +214,20 @@ def cpu_baseline():
             return nbytes / dt / 1e9, dt
 
         out = {}
-        W1, x1 = synth.config1()
+        W1, x1 = synth.bitlinear_m4_k256_n256()
         t0 = time.perf_counter()
         for _ in range(20):
             _, wm1, c1 = oracle.ternarize_pack(W1)
             oracle.bitlinear(x1, c1, None, wm1)
         t1 = (time.perf_counter() - t0) / 20
-        out["config1_us_per_forward"] = round(t1 * 1e6, 1)
+        out["bitlinear_m4_k256_n256_us_per_forward"] = round(t1 * 1e6, 1)
         g2, t2 = seven(1, "outliers", 40)
-        out["config2_decode_m1_gbs"] = round(g2, 4)
+        out["decode_m1_7proj_gbs"] = round(g2, 4)
         g16, t16 = seven(16, "heavy", 2)
-        out["config3_decode_m16_gbs"] = round(g16, 4)
+        out["decode_m16_7proj_gbs"] = round(g16, 4)
         g64, t64 = seven(64, "heavy", 1)
-        out["config3_decode_m64_gbs"] = round(g64, 4)
-        # config 4 on 16 of its 2048 rows (gate|up then down)
+        out["decode_m64_7proj_gbs"] = round(g64, 4)
+        # the M=2048 FFN prefill (gate|up then down) on 16 of its 2048 rows
         rows4 = 16
         codes, wms = layers[0]
         cgu = np.concatenate([codes["gate"], codes["up"]])
@@ -238,8 +238,8 @@ def cpu_baseline():
         oracle.bitlinear(xg, cgu, [I, I], wgu)
         oracle.bitlinear(xd, codes["down"], None, wms["down"])
         t4 = time.perf_counter() - t0
-        out["config4_prefill_tops"] = round(2 * rows4 * (2 * I * H + H * I) / t4 / 1e12, 6)
-        # config 5: the chained decode through 30 layers (two layers' codes
+        out["prefill_m2048_ffn_tops"] = round(2 * rows4 * (2 * I * H + H * I) / t4 / 1e12, 6)
+        # the 30-layer stack: the chained decode (two layers' codes
         # alternating) and the prefill on 4 of 4096 rows through 30 layers
         x = synth.bf16_to_f32(synth.act_outliers_bf16(0, 1, H))
         t0 = time.perf_counter()
@@ -247,7 +247,7 @@ def cpu_baseline():
             codes, wms = layers[l % 2]
             x = oracle.layer(x, codes, wms)["y"]
         t5d = time.perf_counter() - t0
-        out["config5_decode_m1_gbs"] = round((layer_bytes(1, 2, H, I, KV) + 29 * layer_bytes(1, 4, H, I, KV))
+        out["chained_decode_30layers_m1_gbs"] = round((layer_bytes(1, 2, H, I, KV) + 29 * layer_bytes(1, 4, H, I, KV))
                                              / t5d / 1e9, 4)
         rows5 = 4
         x = synth.bf16_to_f32(synth.act_normal_bf16(0, rows5, H))
@@ -256,7 +256,7 @@ def cpu_baseline():
             codes, wms = layers[l % 2]
             x = oracle.layer(x, codes, wms)["y"]
         t5p = time.perf_counter() - t0
-        out["config5_prefill_tops"] = round(30 * layer_ops(rows5, H, I, KV) / t5p / 1e12, 6)
+        out["prefill_m4096_30layers_tops"] = round(30 * layer_ops(rows5, H, I, KV) / t5p / 1e12, 6)
         total = t2 + t16 + t64 + t4 + t5d + t5p
     finally:
         if allowed is not None:
@@ -269,14 +269,14 @@ def cpu_baseline():
                 break
     except OSError:
         pass
-    return {"value": out["config2_decode_m1_gbs"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": out["decode_m1_7proj_gbs"], "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": (f"oracle (gcc {' '.join(oracle.CFLAGS[:4])}), one thread pinned to core {core}: "
-                       f"config 1 in full (ternarize + forward, 20 times), config 2 in full (40 single-token passes over the 7 projections, two seeded layers' "
-                       f"codes alternating), config 3 in full (M=16 twice, M=64 once), config 4 on 16 of "
-                       f"2048 rows, config 5 decode in full (30 chained layers), config 5 prefill on 4 of 4096 "
+                       f"the M=4, K=256, N=256 BitLinear in full (ternarize + forward, 20 times), the M=1 decode of a layer's 7 projections in full (40 single-token passes, two seeded layers' "
+                       f"codes alternating), the batched decode in full (M=16 twice, M=64 once), the M=2048 FFN prefill on 16 of "
+                       f"2048 rows, the 30-layer chained decode in full, the 30-layer M=4096 prefill on 4 of 4096 "
                        f"rows through 30 layers; rates scale with the rows (tokens are independent); "
                        f"{total:.1f} s of CPU work"),
-            "per_config": out, "cpu_model": model, "host_cpus": os.cpu_count(),
+            "per_workload": out, "cpu_model": model, "host_cpus": os.cpu_count(),
             "flags": " ".join(oracle.CFLAGS)}
 
 
@@ -433,7 +433,7 @@ def unpacked_timing(torch, bl, stack, synth, timer, dev, layers, probs1, H, I):
     """The offline-unpacked baseline: the 30 layers' weights unpacked to bf16
     codes (about 4.2 GB), decode M=1 over each layer's 7 projections (the
     headline's inputs, one launch per projection, graph replay), and the
-    config-4 prefill (gate|up then down at M=2048, quantization included)."""
+    M=2048 FFN prefill (gate|up then down, quantization included)."""
     import numpy as np
     out = {}
     unp = []
@@ -495,7 +495,7 @@ def main():
     ap.add_argument("--ste-only", action="store_true",
                     help="only the straight-through backward at M=2048 (for profiler runs)")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="only the config-4 prefill GEMMs (gate|up, then down, int8 codes given) (for profiler runs)")
+                    help="only the M=2048 FFN prefill GEMMs (gate|up, then down, int8 codes given) (for profiler runs)")
     ap.add_argument("--chain-only", action="store_true",
                     help="only the persistent 30-layer decode step (for profiler runs)")
     ap.add_argument("--mt-only", type=int, default=0, metavar="M",
@@ -519,7 +519,7 @@ def main():
                    or args.w1_only)
     cpu = cpu_baseline() if run_cpu else None
     if cpu is not None:
-        log(f"cpu baseline (oracle, 1 core): {cpu['value']} GB/s decode; {cpu['per_config']}")
+        log(f"cpu baseline (oracle, 1 core): {cpu['value']} GB/s decode; {cpu['per_workload']}")
 
     import torch
 
@@ -789,7 +789,7 @@ def main():
         # the offline-unpacked path (weights expanded once to bf16 codes, dense
         # bf16 products; the same output bits): decode M=1 over the 7
         # projections of each of the 30 layers (one launch per projection),
-        # and the config-4 prefill
+        # and the M=2048 FFN prefill
         extra.update(unpacked_timing(torch, bl, stack, synth, timer, dev, layers, probs1, H, I))
         log(f"offline-unpacked: decode M=1 {extra['unpacked_decode_m1_us_per_layer']} us/layer "
             f"({extra['unpacked_decode_m1_weight_gbs']} GB/s of bf16 codes), prefill M=2048 "

@@ -148,7 +148,7 @@ CONFIGS = (
 )
 
 
-def config1():
+def bitlinear_m4_k256_n256():
     """The small parity case's inputs: (W fp32 [256,256], x fp32 [4,256])."""
     W = master_weight(0, 256, 256)
     x = act_normal_f32(0, 4, 256)

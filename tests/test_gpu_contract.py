@@ -219,7 +219,7 @@ def test_extreme_accumulators():
 
 # ----------------------------------------------------------------------------- full-size shapes
 @pytest.mark.parametrize("proj", [p for p, _, _ in synth.PROJECTIONS])
-def test_config2_decode_projection(proj):
+def test_decode_m1_projection(proj):
     """M=1 decode over each projection of one 2B4T layer, oracle-packed weights."""
     _, N, K = synth.PROJECTIONS[synth.PROJ_INDEX[proj]]
     packed, wm, codes = oracle.ternarize_pack(synth.layer_weight(0, proj))
@@ -231,7 +231,7 @@ def test_config2_decode_projection(proj):
 
 
 @pytest.mark.parametrize("M", [16, 64])
-def test_config3_batched_decode(M):
+def test_batched_decode_seven_projections(M):
     """M=16/64 with Student-t rows over the fused q|k|v and gate|up shapes and down."""
     bits = synth.act_heavy_tail_bf16(0, M, 2560)
     for projs in (("q", "k", "v"), ("gate", "up")):
@@ -249,7 +249,7 @@ def test_config3_batched_decode(M):
 
 
 @pytest.mark.timeout(600)
-def test_config4_prefill_all_rows():
+def test_prefill_m2048_ffn_all_rows():
     """M=2048 prefill: fused gate|up (K=2560 -> 2x6912) and down (6912 -> 2560),
     every row and column: the int32 accumulators bit-exact against the exact
     integer product, the fp32 outputs bit-identical to the oracle's rescale."""

@@ -30,8 +30,8 @@ def _check_quant_bf16(bits: np.ndarray):
     assert_exact(host(a).view(np.uint32), ar.view(np.uint32), "a bits")
 
 
-def test_quant_config1_fp32():
-    _, x = synth.config1()
+def test_quant_m4_k256_fp32():
+    _, x = synth.bitlinear_m4_k256_n256()
     _check_quant_f32(x)
 
 
@@ -101,8 +101,8 @@ def _check_ternarize(W: np.ndarray):
     return host(packed), host(wm)
 
 
-def test_ternarize_config1():
-    W, _ = synth.config1()
+def test_ternarize_m4_k256_n256():
+    W, _ = synth.bitlinear_m4_k256_n256()
     _check_ternarize(W)
 
 

@@ -97,7 +97,7 @@ def test_gemm_unpacked_equals_the_oracle(M, K, seg_n, kind):
 
 
 @pytest.mark.timeout(600)
-def test_gemm_unpacked_config4_all_rows():
+def test_gemm_unpacked_prefill_m2048_all_rows():
     """M=2048 gate|up (K=2560 -> 2x6912) on the bf16 MFMA GEMM, every row."""
     bl = _bl()
     M = 2048
