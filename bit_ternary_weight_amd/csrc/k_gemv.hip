@@ -648,7 +648,7 @@ __device__ __forceinline__ void quant_rows(const GemvProblem &p, const v4i *xr, 
     for (int m = 0; m < kFuseMaxM; ++m) {
         if (m >= M) break;
         s[m] = 127.0f / fmaxf(amax[m], kFloor);   // IEEE fp32 division
-        if (threadIdx.x == (unsigned)(kStreamWaves * 64)) a_s[m] = s[m];
+        if (ql == 0) a_s[m] = s[m];
     }
     int qsum[kFuseMaxM] = {0, 0, 0, 0};
 #pragma unroll
@@ -1094,13 +1094,16 @@ int xkind_of(const GemvProblem &p) {
 // One-row streaming kernel (M == 1): the fused decode path for a single
 // activation row.  One 16-wave workgroup per CU, with the two roles of
 // k_gemv_lds:
-//   * 8 quantizer waves load the row and quantize it into LDS (quant_rows:
-//     RMSNorm sum of squares, absmax, codes, synchronised among themselves
-//     through LDS flags).  They issue no weight load, so nothing holds them
-//     up: a wave that issues weight loads is stalled in the issue for
-//     microseconds while the CU's requests drain at its share of HBM.
-//   * 8 stream waves issue their weight units once the activation loads are
-//     out: a unit is 4 packed rows x 256 bytes of one tensor (two whole
+//   * 8 quantizer waves (waves 0-7: a workgroup's waves are launched in
+//     order, so their row loads leave the CU before any weight load; as
+//     waves 8-15 the step took 6.47 instead of 6.21 us) load the row and
+//     quantize it into LDS (quant_rows: RMSNorm sum of squares, absmax,
+//     codes, synchronised among themselves through LDS flags).  They issue
+//     no weight load, so nothing holds them up: a wave that issues weight
+//     loads is stalled in the issue for microseconds while the CU's requests
+//     drain at its share of HBM.
+//   * 8 stream waves (8-15) issue their weight units once the activation
+//     loads are out: a unit is 4 packed rows x 256 bytes of one tensor (two whole
 //     128-byte lines per row), 16 bytes per lane, loaded into registers with
 //     the non-temporal hint.  Once the codes are published they consume the
 //     units in order, each as soon as it has landed.  Lane (g, l) = (L >> 4,
@@ -1161,7 +1164,10 @@ void k_gemv_v1(GemvBatch b) {
     const GemvProblem &p = b.p[pi];
 
     const int tid = threadIdx.x;
+    // waves 0 .. kQuantWaves - 1 quantize, the rest stream: the quantizer
+    // waves are launched first, so the activation loads leave the CU first
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+    const int sid = tid - kQuantWaves * 64;                      // stream-wave thread index
     const int lane = tid & 63;
     const int K = p.K;
     const int R = p.R;
@@ -1187,12 +1193,12 @@ void k_gemv_v1(GemvBatch b) {
     int ep_col = 0, ep_qsum = 0;
     float ep_s0 = 0.0f, ep_s1 = 0.0f;
 
-    if (wave >= SW) {
+    if (wave < kQuantWaves) {
         // ---------------- quantizer waves ----------------
         constexpr int per = BF ? 8 : 4;
         constexpr int esz = BF ? 2 : 4;
-        const int qw = wave - SW;
-        const int ql = tid - SW * 64;
+        const int qw = wave;
+        const int ql = tid;
         const int E = x_chunks(K, BF ? BL_BF16 : BL_F32, kQuantLanes);
         v4i xr[kXRegs];
         v4i gr[kXRegs];
@@ -1230,6 +1236,7 @@ void k_gemv_v1(GemvBatch b) {
         // ---------------- stream waves ----------------
         // tensor tsel, row group rg (4 packed rows), k-ranges kr0, kr0 +
         // kstep, ... (all counts powers of two)
+        const int wave = __builtin_amdgcn_readfirstlane(sid >> 6);   // stream wave 0 .. SW - 1
         const int groups = NB * CS;
         const int lwpg = __builtin_ctz(SW / groups);   // log2 stream waves per row group
         const int grp = wave >> lwpg;
@@ -1281,9 +1288,9 @@ void k_gemv_v1(GemvBatch b) {
         // reduction -- the norm's sum of squares, the absmax unless it travels
         // with the sum -- and once when done)
         wait_published<4>(qflag, NORM && p.gain != nullptr ? 3 : 2);
-        if (tid < 4 * CS * 4) {
-            const int f = tid & 3;
-            const int vr = r0 + (tid >> 2);
+        if (sid < 4 * CS * 4) {
+            const int f = sid & 3;
+            const int vr = r0 + (sid >> 2);
 #pragma unroll
             for (int w = 0; w < kQuantWaves; ++w) ep_qsum += sq_s[w];
             const float av = a_s[0];
@@ -1344,9 +1351,9 @@ void k_gemv_v1(GemvBatch b) {
     // owns output e = (packed row, field); the codes were taken as c + 1, so
     // the row's code sum comes off once
     const float a = a_s[0];
-    if (tid < 4 * CS * 4 && r0 + (tid >> 2) < R) {
-        const int f = tid & 3;
-        const int prow = tid >> 2;
+    if (sid >= 0 && sid < 4 * CS * 4 && r0 + (sid >> 2) < R) {
+        const int f = sid & 3;
+        const int prow = sid >> 2;
         const int A = red[(0 * kV1MaxRows + prow) * 4 + f] - ep_qsum;
         if (PAIR) {
             const int U = red[(1 * kV1MaxRows + prow) * 4 + f] - ep_qsum;
