@@ -49,6 +49,7 @@
 // third: a compute unit sends its memory requests in issue order, and stores
 // queued behind a stage's worth of weight loads reach the other workgroups
 // that much later.
+#include "bl_buffer.h"
 #include "bl_common.h"
 
 namespace bl {
@@ -284,12 +285,6 @@ constexpr int kCChunks = kCMaxK / 4 / kCQL;        // polled chunks per quantize
 constexpr int kCNormChunks = kCMaxK / 4 / kCThreads;   // chunks per thread in the quantization
 constexpr int kSc1 = 16;   // cache-policy operand of a buffer load: agent scope (the sc1 bit)
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *p, int bytes) {
-    // raw buffer: base p, bytes in range (loads past it read zero), the data
-    // format word of gfx9-family buffer resources
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
-}
-
 // Polls the K-word input `in` until no word of this lane's chunks holds the
 // fill pattern, then stores the chunks to xs (and the matching gains, or
 // ones, to xg).  Agent-scope loads of one poll are all in flight together.
@@ -313,7 +308,7 @@ __device__ __forceinline__ void poll_to_lds(const float *in, int K, const float 
             if (i < ni && c < nc) *reinterpret_cast<float4 *>(xg + 4 * c) = float4{g[i][0], g[i][1], g[i][2], g[i][3]};
         }
     }
-    const __amdgpu_buffer_rsrc_t rs = rsrc_of(in, K * 4);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(in, K * 4);
     v4i u[kCChunks];
     for (int it = 0;; ++it) {
 #pragma unroll

@@ -7,6 +7,7 @@
 // the inference forward multiplies the per-token int8 activations with the
 // unpacked ternary weight and rescales by both scales; the 2-bit fields are
 // expanded in registers, never written back.
+#include "bl_buffer.h"
 #include "bl_common.h"
 
 namespace bl {
@@ -35,7 +36,8 @@ namespace bl {
 //     token c: four consecutive output columns.
 // Blocks go two in flight (with 64 tokens the codes one block ahead), every
 // wave issuing the same number of loads on every path (the compiler's waits
-// stay exact; past its blocks a wave re-reads its last one).  The waves of a row group add their partial sums
+// stay exact; past its blocks a wave's loads fall outside their buffer
+// range and move no data).  The waves of a row group add their partial sums
 // through LDS at the end.
 // ===========================================================================
 constexpr int kMtWaves = 8;
@@ -104,23 +106,23 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
         return kr0 + kstep * (j >= ks ? j - ks : j);
     };
     const int r0 = ((int)blockIdx.x - p.tile0) * 16 * p.cs;
-    // this lane's rows of the four loads of a block (rows past R read row 0:
-    // in bounds, never stored)
-    const uint8_t *wsrc[4];
+    // Weights and codes go through buffer resources (gemv_mt_ok bounds both
+    // ranges below 2^31 bytes).  The padding loads -- blocks past the wave's
+    // own, and rows past R -- fall outside the range: they return zeros and
+    // move no data.  (Token tiles past the problem's codes re-read its last
+    // tile.)  A load's offset is this lane's in-range offset plus a uniform
+    // block offset, kBufOob for a padding block.
+    const int rb = r0 + 16 * grp;   // the wave's row group
+    const int vrows = p.R - rb <= 0 ? 0 : (p.R - rb < 16 ? p.R - rb : 16);
+    const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(p.P + (size_t)(vrows > 0 ? rb : 0) * K, vrows * K);
+    unsigned wo[4];   // this lane's offsets of the four loads of block 0
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = r0 + 16 * grp + 4 * j + (lane >> 4);
-        wsrc[j] = p.P + (size_t)(row < p.R ? row : 0) * K + 16 * lr;
-    }
-    // token tiles past this problem's codes re-read its last tile
-    const int8_t *q = reinterpret_cast<const int8_t *>(p.x);
+    for (int j = 0; j < 4; ++j) wo[j] = (unsigned)((4 * j + (lane >> 4)) * K + 16 * lr);
     const int qt = p.qtile;
-    const int8_t *qrow[T];
+    const __amdgpu_buffer_rsrc_t crs = buf_rsrc(p.x, qt * K);
+    unsigned co[T];   // this lane's offsets of token tile u in piece 0
 #pragma unroll
-    for (int u = 0; u < T; ++u) {
-        const int uu = 16 * u < qt ? u : qt / 16 - 1;
-        qrow[u] = q + (size_t)(16 * uu + lr) * 64 + 16 * g;
-    }
+    for (int u = 0; u < T; ++u) co[u] = (unsigned)((16 * (16 * u < qt ? u : qt / 16 - 1) + lr) * 64 + 16 * g);
     // The epilogue's inputs (token code sums and scales, segment weight
     // scales) are loaded right after the first block, so that their latency
     // is hidden; every lane loads the same number (clamped indices), so the
@@ -153,23 +155,19 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
     constexpr int CB = kOwn ? 2 : 1;
     v4i wv[2][4];
     v4i cv[CB][4][T];
-    auto block_of = [&](int t) {
-        const int tt = t < ks ? t : ks - 1;
-        return tt >= 0 ? kb_of(tt) : 0;
-    };
     auto issue_w = [&](int t, int sl) {
-        const int kb = block_of(t);
+        const unsigned bo = __builtin_amdgcn_readfirstlane(t < ks ? 256u * (unsigned)kb_of(t) : kBufOob);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wv[sl][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wsrc[j] + 256 * (size_t)kb));
+        for (int j = 0; j < 4; ++j) wv[sl][j] = buf_ld16<kBufNt>(wrs, wo[j] + bo);
     };
     auto issue_c = [&](int t, int sl) {
-        const int kb = block_of(t);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 4; ++k) {
+            const unsigned po = __builtin_amdgcn_readfirstlane(
+                t < ks ? (4u * (unsigned)kb_of(t) + k) * (unsigned)qt * 64u : kBufOob);
 #pragma unroll
-            for (int u = 0; u < T; ++u)
-                cv[sl][k][u] = *reinterpret_cast<const v4i *>(qrow[u] + (size_t)(4 * kb + k) * qt * 64);
+            for (int u = 0; u < T; ++u) cv[sl][k][u] = buf_ld16<0>(crs, co[u] + po);
+        }
     };
     v4i acc[T][4];
 #pragma unroll
@@ -322,6 +320,7 @@ bool gemv_mt_ok(const GemvBatch &b) {
         const GemvProblem &p = b.p[i];
         if (p.mode != 0 || p.pair != 0 || p.qsum == nullptr || p.a == nullptr || p.M < 1 || p.M > 64 ||
             p.qtile < 16 || p.qtile % 16 != 0 || p.qtile < p.M || p.K < 256 || p.K % 256 != 0 ||
+            (size_t)p.qtile * p.K >= ((size_t)1 << 31) || (size_t)16 * p.K >= ((size_t)1 << 31) ||
             ((uintptr_t)p.x % 16) != 0 || ((uintptr_t)p.P % 16) != 0)
             return false;
     }
