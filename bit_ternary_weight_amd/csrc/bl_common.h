@@ -98,6 +98,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     return (uint16_t)(u >> 16);
 }
 
+// Workgroup barrier ordering LDS only: wait for this wave's LDS operations
+// (lgkmcnt 0), then s_barrier.  __syncthreads() (and the compiler's own
+// barrier lowering) would also wait for every outstanding global load of the
+// wave, i.e. for a whole weight stream in flight.  The barrier is written as
+// an asm statement with a memory clobber so no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

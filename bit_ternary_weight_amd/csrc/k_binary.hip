@@ -352,11 +352,6 @@ __device__ __forceinline__ void wb_dma16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
-__device__ __forceinline__ void wb_lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
-    asm volatile("s_barrier" ::: "memory");
-}
-
 // Tiles of problem p: ceil(M / 128) token tiles x ceil(N/8 / 32) row tiles.
 __host__ __device__ inline int wb_tiles(int M, int N) {
     return ((M + kWBTM - 1) / kWBTM) * ((N / 8 + kWBTR - 1) / kWBTR);
@@ -416,13 +411,13 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int lsw = swz(lr);   // fragment rows start at multiples of 16
     auto chunk = [&](int ch) { return 16 * (ch ^ lsw); };
 
-    wb_lds_barrier();
+    lds_barrier();
     issue(0);
     if (nst > 1) issue(1);
     for (int st = 0; st < nst; ++st) {
         if (st + 1 < nst) wb_wait_vm<kWBDW>();
         else wb_wait_vm<0>();
-        wb_lds_barrier();
+        lds_barrier();
         const unsigned char *base = lds + (st % kWBStages) * kWBStage;
         v4i af[4], bw;
 #pragma unroll

@@ -108,11 +108,6 @@ __device__ __forceinline__ const ChainArgs &args() {
     return *(const ChainArgs *)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
-    asm volatile("s_barrier" ::: "memory");
-}
-
 // Stage geometry of this workgroup, the same for every layer: computed once.
 struct Stage {
     const uint8_t *P;  // packed weight (pair: gate rows, then up rows)

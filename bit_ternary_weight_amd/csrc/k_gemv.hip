@@ -385,16 +385,6 @@ __host__ __device__ inline int x_chunks(int K, int dt, int lanes) {
     return (K + per - 1) / per;
 }
 
-// Workgroup barrier ordering LDS only: wait for this wave's LDS operations
-// (lgkmcnt 0), then s_barrier.  __syncthreads() (and the compiler's own
-// barrier lowering) would also wait for every outstanding global load of the
-// wave, i.e. for the whole weight stream in flight.  The barrier is written
-// as an asm statement with a memory clobber so no LDS access moves across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
-    asm volatile("s_barrier" ::: "memory");
-}
-
 // Wave-wide reductions without LDS round trips: DPP within each 16-lane row
 // (xor 1, xor 2, rotate 4, rotate 8 leave every lane of a row holding the
 // row's result), then the four rows combined in order through readlane.  The

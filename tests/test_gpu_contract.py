@@ -109,6 +109,53 @@ def test_gemv_batched_input_kinds(M, x_kind):
     _check("gemv_w2a8", M, 2560, (640, 160), x_kind=x_kind, seed=10 + M)
 
 
+# 5 to 17 token rows through the row quantizer and the batched streaming
+# kernel: one 256-byte block, fused q|k|v, K = 6912, 7168 and 7424, fp32
+# rows, one token tile and a second one; 36 output rows leave a partial row
+# group of 9 packed rows.
+@pytest.mark.parametrize("M,K,seg_n,x_kind", [
+    (5, 256, (16,), "bf16"), (8, 2560, (2560, 640, 640), "bf16"), (13, 6912, (2560,), "bf16"),
+    (16, 7168, (68,), "bf16"), (16, 6912, (36,), "bf16"), (16, 7424, (68,), "bf16"),
+    (16, 2560, (640, 160), "f32"), (17, 2560, (640, 160), "bf16")])
+def test_gemv_batched_rows(M, K, seg_n, x_kind):
+    _check("gemv_w2a8", M, K, seg_n, x_kind=x_kind, seed=20 + M + K % 7)
+
+
+def test_gemv_batched_strided_rows():
+    """16 bf16 rows read with a row stride larger than K (a column slice of a
+    wider activation tensor): every output bit-identical to the oracle."""
+    M, K, seg_n = 16, 2560, (640, 160)
+    packed, wms, codes = _weights(77, seg_n, K)
+    bits = synth.act_heavy_tail_bf16(77, M, K + 64)
+    wide = bf16_dev(bits)
+    x = wide[:, 32:32 + K]
+    assert x.stride(0) == K + 64
+    _, _, A, y = oracle.bitlinear(f32_of_bf16(bits[:, 32:32 + K]), codes, seg_n, wms)
+    Ag = _run("gemv_w2a8", x, packed, wms, seg_n, torch.int32)
+    assert_exact(host(Ag), A, "int32 accumulators")
+    yg = host(_run("gemv_w2a8", x, packed, wms, seg_n, torch.float32))
+    assert max_ulp_diff(yg, y) == 0
+
+
+def test_batched_mixed_rows():
+    """Problems of 3, 9 and 16 bf16 rows (K 6912, 2560 with three segments,
+    256) in one call: the 16-row problem keeps the batch off the one-row and
+    LDS kernels, so every problem goes through the row quantizer and the
+    batched streaming kernel, the 3-row one included."""
+    specs = [(3, 6912, (2560,)), (9, 2560, (640, 160, 160)), (16, 256, (64,))]
+    probs, refs = [], []
+    for i, (M, K, seg_n) in enumerate(specs):
+        packed, wms, codes = _weights(400 + i, seg_n, K)
+        bits = synth.act_outliers_bf16(90 + i, M, K)
+        _, _, _, y = oracle.bitlinear(f32_of_bf16(bits), codes, seg_n, wms)
+        probs.append(dict(x=bf16_dev(bits), packed=to_dev(packed), w_mean=to_dev(wms),
+                          seg_n=list(seg_n) if len(seg_n) > 1 else None))
+        refs.append(y)
+    outs = _bl().gemv_w2a8_batched(probs)
+    for y, yr in zip(outs, refs):
+        assert max_ulp_diff(host(y), yr) == 0
+
+
 # The one-row decode kernel stages the row's codes in a 12288-byte LDS buffer:
 # K at that limit takes it, one k-range more takes the register kernel; fp32
 # rows carry half as many elements per load.
