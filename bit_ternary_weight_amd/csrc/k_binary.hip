@@ -522,61 +522,6 @@ __device__ __forceinline__ void d_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int CTRL>
-__device__ __forceinline__ int d_dpp(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ double d_dpp_d(double v) {
-    const long long b = __double_as_longlong(v);
-    const int lo = d_dpp<CTRL>((int)(b & 0xFFFFFFFF));
-    const int hi = d_dpp<CTRL>((int)(b >> 32));
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ double d_readlane_d(double v, int l) {
-    const long long b = __double_as_longlong(v);
-    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
-    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-// Wave sums by DPP row operations and lane reads (no LDS round trips), in a
-// fixed order.
-__device__ __forceinline__ double d_wave_sum(double v) {
-    v += d_dpp_d<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += d_dpp_d<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += d_dpp_d<0x124>(v);   // row_ror:4
-    v += d_dpp_d<0x128>(v);   // row_ror:8
-    return ((d_readlane_d(v, 0) + d_readlane_d(v, 16)) + d_readlane_d(v, 32)) + d_readlane_d(v, 48);
-}
-
-__device__ __forceinline__ float d_wave_max(float v) {
-    v = fmaxf(v, __int_as_float(d_dpp<0xB1>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(d_dpp<0x4E>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(d_dpp<0x124>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(d_dpp<0x128>(__float_as_int(v))));
-    const int iv = __float_as_int(v);
-    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 16))),
-                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 32)), __int_as_float(__builtin_amdgcn_readlane(iv, 48))));
-}
-
-__device__ __forceinline__ int d_wave_sum_i(int v) {
-    v += d_dpp<0xB1>(v);
-    v += d_dpp<0x4E>(v);
-    v += d_dpp<0x124>(v);
-    v += d_dpp<0x128>(v);
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
-           __builtin_amdgcn_readlane(v, 48);
-}
-
-__device__ __forceinline__ int d_quad_sum(int v) {
-    v += d_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += d_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    return v;
-}
-
 // The eight per-wave partials of an exchange, read as 16-byte vectors:
 // their sum in wave order, their maximum.
 __device__ __forceinline__ double sum8(const double *p) {
@@ -689,7 +634,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         for (int i = 0; i < kDChunks; ++i)
 #pragma unroll
             for (int f = 0; f < 4; ++f) s += (double)xv[i][f];   // chunks past K hold zeros
-        s = d_wave_sum(s);
+        s = wave_sum_dpp(s);
         if (lane == 0) rd1[wave] = s;
         q_sync(flag, wave, 1);
         // each exchange has its own slots, so no wave waits for the others'
@@ -708,8 +653,8 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
                     xv[i][f] = (float)d;   // the normalization below needs only float(x - mu)
                     md = fmaxf(md, fabsf(xv[i][f]));
                 }
-        ss = d_wave_sum(ss);
-        md = d_wave_max(md);
+        ss = wave_sum_dpp(ss);
+        md = wave_max_dpp(md);
         if (lane == 0) {
             rd2[wave] = ss;
             rm[wave] = md;
@@ -742,7 +687,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
             for (int i = 0; i < kDChunks; ++i)
 #pragma unroll
                 for (int f = 0; f < 4; ++f) am = fmaxf(am, fabsf(xv[i][f]));
-            am = d_wave_max(am);
+            am = wave_max_dpp(am);
             if (lane == 0) rf[wave] = am;
             q_sync(flag, wave, 3);
             mx = max8(rf);
@@ -763,7 +708,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
                 *reinterpret_cast<uint32_t *>(qd + 4 * c) = w;
             }
         }
-        cs = d_wave_sum_i(cs);
+        cs = wave_sum_dpp(cs);
         if (lane == 0) ri[wave] = cs;
         d_barrier();   // codes in LDS
         d_barrier();   // row sums in LDS
@@ -812,7 +757,7 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         int t[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            t[i] = d_quad_sum(sl == 0 ? acc[i][0] : (sl == 1 ? acc[i][1] : (sl == 2 ? acc[i][2] : acc[i][3])));
+            t[i] = quad_sum(sl == 0 ? acc[i][0] : (sl == 1 ? acc[i][1] : (sl == 2 ? acc[i][2] : acc[i][3])));
         if ((lane & 15) == 0)
 #pragma unroll
             for (int i = 0; i < 8; ++i) atomicAdd(&red[i][4 * q + g], t[i]);

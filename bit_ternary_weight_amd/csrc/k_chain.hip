@@ -162,62 +162,6 @@ __device__ __forceinline__ const uint8_t *unit_addr(const Stage &st, int mu, int
     return st.P + (size_t)row * st.K + (size_t)k * kCUnit + 16 * ch;
 }
 
-// Wave reductions by DPP row operations and lane reads (no LDS round trips);
-// the summation order is fixed.
-template <int CTRL>
-__device__ __forceinline__ int dpp(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
-__device__ __forceinline__ int quad_sum(int v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-    auto st = [](float x, int b) { return fmaxf(x, __int_as_float(b)); };
-    v = st(v, dpp<0xB1>(__float_as_int(v)));
-    v = st(v, dpp<0x4E>(__float_as_int(v)));
-    v = st(v, dpp<0x124>(__float_as_int(v)));   // row_ror:4
-    v = st(v, dpp<0x128>(__float_as_int(v)));   // row_ror:8
-    const int iv = __float_as_int(v);
-    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 16))),
-                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 32)), __int_as_float(__builtin_amdgcn_readlane(iv, 48))));
-}
-
-__device__ __forceinline__ int wave_sum_i(int v) {
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
-    v += dpp<0x124>(v);
-    v += dpp<0x128>(v);
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
-           __builtin_amdgcn_readlane(v, 48);
-}
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double v) {
-    const long long b = __double_as_longlong(v);
-    const int lo = dpp<CTRL>((int)(b & 0xFFFFFFFF));
-    const int hi = dpp<CTRL>((int)(b >> 32));
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ double readlane_d(double v, int l) {
-    const long long b = __double_as_longlong(v);
-    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
-    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-    v += dpp_d<0xB1>(v);
-    v += dpp_d<0x4E>(v);
-    v += dpp_d<0x124>(v);
-    v += dpp_d<0x128>(v);
-    return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
-}
-
 template <int U>
 __device__ __forceinline__ void issue(const Stage &st, int ws, int lane, v4i (&r)[U]) {
 #pragma unroll
@@ -401,8 +345,8 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
                 ss += (double)v[i][f] * (double)v[i][f];
                 hm = fmaxf(hm, fabsf(v[i][f]));
             }
-        ss = wave_sum_d(ss);
-        hm = wave_max(hm);
+        ss = wave_sum_dpp(ss);
+        hm = wave_max_dpp(hm);
         if ((t & 63) == 0) {
             sh.red_d[wave] = ss;
             sh.red_m[wave] = hm;
@@ -431,7 +375,7 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
         for (int i = 0; i < kCNormChunks; ++i)
 #pragma unroll
             for (int f = 0; f < 4; ++f) am = fmaxf(am, fabsf(v[i][f]));
-        am = wave_max(am);
+        am = wave_max_dpp(am);
         if ((t & 63) == 0) sh.red_f[wave] = am;
         lds_barrier();
         mx = max16(sh.red_f);
@@ -450,7 +394,7 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
             }
         }
     }
-    cs = wave_sum_i(cs);
+    cs = wave_sum_dpp(cs);
     if ((t & 63) == 0) sh.red_i[wave] = cs;
     return a;
 }

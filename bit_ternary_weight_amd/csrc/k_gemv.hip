@@ -385,59 +385,6 @@ __host__ __device__ inline int x_chunks(int K, int dt, int lanes) {
     return (K + per - 1) / per;
 }
 
-// Wave-wide reductions without LDS round trips: DPP within each 16-lane row
-// (xor 1, xor 2, rotate 4, rotate 8 leave every lane of a row holding the
-// row's result), then the four rows combined in order through readlane.  The
-// result is uniform and its summation order fixed.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
-__device__ __forceinline__ int wave_sum_dpp(int v) {
-    v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_i<0x124>(v);   // row_ror:4
-    v += dpp_i<0x128>(v);   // row_ror:8
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
-__device__ __forceinline__ float fmax_dpp_step(float v, int b) { return fmaxf(v, __int_as_float(b)); }
-
-__device__ __forceinline__ float wave_max_dpp(float v) {
-    v = fmax_dpp_step(v, dpp_i<0xB1>(__float_as_int(v)));
-    v = fmax_dpp_step(v, dpp_i<0x4E>(__float_as_int(v)));
-    v = fmax_dpp_step(v, dpp_i<0x124>(__float_as_int(v)));
-    v = fmax_dpp_step(v, dpp_i<0x128>(__float_as_int(v)));
-    const int iv = __float_as_int(v);
-    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 16))),
-                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(iv, 32)), __int_as_float(__builtin_amdgcn_readlane(iv, 48))));
-}
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double v) {
-    const long long b = __double_as_longlong(v);
-    const int lo = dpp_i<CTRL>((int)(b & 0xFFFFFFFF));
-    const int hi = dpp_i<CTRL>((int)(b >> 32));
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ double readlane_d(double v, int l) {
-    const long long b = __double_as_longlong(v);
-    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
-    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
-    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ double wave_sum_dpp(double v) {
-    v += dpp_d<0xB1>(v);
-    v += dpp_d<0x4E>(v);
-    v += dpp_d<0x124>(v);
-    v += dpp_d<0x128>(v);
-    return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
-}
-
 // The PER activation values of a 16-byte chunk as fp32 (bf16: 8, fp32: 4).
 template <int PER>
 __device__ __forceinline__ void chunk_f32(const v4i &c, float *v) {
@@ -687,7 +634,6 @@ struct kWaitVm {
     static_assert(VM >= 0 && VM < 64, "vmcnt is 6 bits");
     static constexpr int value = (VM & 0xF) | (0x7 << 4) | (0xF << 8) | ((VM >> 4) << 14);
 };
-
 
 // The weight stream is read once per launch: its loads carry the
 // non-temporal hint (cache policy bit nt), so that it does not evict the
@@ -1115,13 +1061,6 @@ constexpr int kV1MaxRows = 32;    // packed rows per tensor per workgroup (4 * C
 
 __device__ __forceinline__ v4i ld16_nt(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-}
-
-// Sum over each quad of lanes (every lane of the quad gets the sum).
-__device__ __forceinline__ int quad_sum(int v) {
-    v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
-    return v;
 }
 
 // Entry m (0 .. 3, per lane) of a 4-vector, with selects.

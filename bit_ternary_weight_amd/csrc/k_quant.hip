@@ -63,14 +63,15 @@ __device__ __forceinline__ uint32_t pack4(int c0, int c1, int c2, int c3) {
            ((uint32_t)(c3 & 0xFF) << 24);
 }
 
+// Block maximum and integer sum: DPP within each wave, then one LDS-only
+// barrier (no global store or load of the block need wait for it); each
+// reduction uses its own LDS slots once, so no second barrier guards them.
 __device__ __forceinline__ float block_max(float v, float *red) {
-    v = wave_max(v);
+    v = wave_max_dpp(v);
     int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    return r;
+    lds_barrier();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 __device__ __forceinline__ double block_sum(double v, double *red) {
@@ -96,11 +97,10 @@ __device__ __forceinline__ float elem(const T *row, int64_t k, float r, const fl
 }
 
 __device__ __forceinline__ int block_isum(int v, int *red) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v = wave_sum_dpp(v);
     int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
+    lds_barrier();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
