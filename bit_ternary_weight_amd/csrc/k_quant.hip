@@ -222,12 +222,13 @@ __global__ __launch_bounds__(kThreads) void k_rowq(QuantBatch qb) {
     __shared__ float redf[4];
     __shared__ double redd[4];
     __shared__ int redi[4];
-    // the problem whose [row0, row0 + M) holds this block (compile-time
-    // indices only, so the kernel-argument array is never indexed at run time)
-    QuantProblem p = qb.p[0];
+    // the problem whose [row0, row0 + M) holds this block: its index from
+    // the row starts (all loaded at once), then its fields by that index
+    int pi = 0;
 #pragma unroll
     for (int i = 1; i < kMaxProblems; ++i)
-        if (i < qb.n && (int)blockIdx.x >= qb.p[i].row0) p = qb.p[i];
+        if (i < qb.n && (int)blockIdx.x >= qb.p[i].row0) pi = i;
+    const QuantProblem &p = qb.p[pi];
     const int m = (int)blockIdx.x - p.row0;
     const int K = p.K;
     const T *row = reinterpret_cast<const T *>(p.x) + (int64_t)m * p.ldx;
