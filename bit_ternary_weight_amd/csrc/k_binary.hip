@@ -60,13 +60,23 @@ __device__ __forceinline__ const W1Batch &batch() {
     return *(const W1Batch *)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
-// Problem of this workgroup and the workgroup's index within it.
-__device__ __forceinline__ int problem_of(const W1Batch &b, int &local) {
+// Problem of this workgroup and the workgroup's index within it (and, when
+// asked, the problem's row quads per workgroup).  The loop has a fixed trip
+// count and carries the selected values along, so all its kernel-argument
+// loads go out together: a loop bounded by b.n, with b.start[p] read after
+// it, compiled to one dependent round trip per problem.
+__device__ __forceinline__ int problem_of(const W1Batch &b, int &local, int *quads = nullptr) {
     const int blk = blockIdx.x;
-    int p = 0;
-    for (int i = 1; i < b.n; ++i)
-        if (blk >= b.start[i]) p = i;
-    local = blk - b.start[p];
+    int p = 0, st = b.start[0], qd = b.quads[0];
+#pragma unroll
+    for (int i = 1; i < kMaxProblems; ++i) {
+        const bool in = i < b.n && blk >= b.start[i];   // selects, no branch around the loads
+        p = in ? i : p;
+        st = in ? b.start[i] : st;
+        qd = in ? b.quads[i] : qd;
+    }
+    local = blk - st;
+    if (quads) *quads = qd;
     return p;
 }
 
@@ -576,12 +586,15 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
     __shared__ int ri[kDQW];
     __shared__ __attribute__((aligned(16))) int flag[kDQW];
     const W1Batch &b = batch();
-    int local = 0;
-    const int p = problem_of(b, local);
+    int local = 0, quads = 1;
+    const int p = problem_of(b, local, &quads);
     const W1Problem &pr = b.p[p];
     const int K = pr.K, R = pr.N >> 3, nku = K >> 8, nu = 4 * nku;
+    // every field of the problem read here together (the compiler would
+    // issue each load next to its first use, one round trip after another)
+    asm volatile("" ::"s"(K), "s"(R), "s"(pr.x), "s"(pr.gamma), "s"(pr.beta), "s"(pr.w_scale), "s"(pr.P), "s"(pr.y));
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4;
-    const int lq = b.quads[p] == 4 ? 2 : (b.quads[p] == 2 ? 1 : 0);   // log2 of the row quads
+    const int lq = quads == 4 ? 2 : (quads == 2 ? 1 : 0);   // log2 of the row quads
     const int r0 = local * (4 << lq);
     float a = 1.0f;
 

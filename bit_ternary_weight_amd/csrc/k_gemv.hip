@@ -1104,6 +1104,17 @@ void k_gemv_v1(GemvBatch b) {
     const int r0 = ((int)blockIdx.x - p.tile0) * 4 * CS;
     const int nkr = (K + kUnitK - 1) / kUnitK;
     const int Kp = nkr * kUnitK;         // row pitch of q_s
+    // The fields both roles need before their first global load, read here
+    // together: left to itself the compiler issues each kernel-argument load
+    // next to its first use, which put three dependent round trips ahead of
+    // the first weight load.  (Later reads of these fields reuse the values.)
+    {
+        const uint8_t *P = p.P;
+        const void *X = p.x;
+        const float *WM = p.w_mean;
+        const int nseg = p.seg.n;
+        asm volatile("" ::"s"(K), "s"(R), "s"(CS), "s"(r0), "s"(P), "s"(X), "s"(WM), "s"(nseg));
+    }
 
     // LDS that is accumulated into or polled, and the zero code tail (k in
     // [K, Kp): weight bytes there are placeholders or past K and must meet

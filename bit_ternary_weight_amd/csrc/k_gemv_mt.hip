@@ -86,6 +86,11 @@ __global__ __launch_bounds__(kMtWaves * 64) void k_gemv_mt(GemvBatch b) {
     for (int i = 1; i < kMaxProblems; ++i)
         if (i < b.n && (int)blockIdx.x >= b.p[i].tile0) pi = i;
     const GemvProblem &p = b.p[pi];
+    // the problem's fields read here together (the compiler would issue each
+    // kernel-argument load next to its first use, one round trip after
+    // another ahead of the first weight load)
+    asm volatile("" ::"s"(p.K), "s"(p.cs), "s"(p.tile0), "s"(p.R), "s"(p.M), "s"(p.qtile), "s"(p.P), "s"(p.x),
+                 "s"(p.qsum), "s"(p.a), "s"(p.w_mean), "s"(p.seg.n));
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
