@@ -205,9 +205,9 @@ struct ChainLds {
     float xg[kCMaxK];            // its RMSNorm gains, exchange order
     int8_t q_s[kCMaxK];          // its codes, column order
     int part[kCMaxUnits * 16];   // unit partial sums
-    double red_d[kCWaves];       // per-wave sums of squares
-    float red_f[kCWaves];        // per-wave absolute maxima
-    float red_m[kCWaves];        // per-wave max |h| (norm without gain)
+    alignas(16) double qp_d[kCQ];  // per quantizer wave: sum of squares of its chunks (norm stages)
+    alignas(16) float qp_m[kCQ];   // per quantizer wave: max |value| of its chunks
+    float red_f[kCWaves];        // per-wave absolute maxima (norm with a gain)
     int red_i[kCWaves];          // per-wave code sums
 };
 
@@ -224,12 +224,27 @@ constexpr int kCChunks = kCMaxK / 4 / kCQL;        // polled chunks per quantize
 constexpr int kCNormChunks = kCMaxK / 4 / kCThreads;   // chunks per thread in the quantization
 constexpr int kSc1 = 16;   // cache-policy operand of a buffer load: agent scope (the sc1 bit)
 
+// The quantizer waves' share of the input's reductions, taken from the
+// values they already hold in registers: this wave's max |value| and (norm
+// stages) its fp64 sum of squares, to qp_m / qp_d of quantizer wave ql / 64.
+// Each lane sums its chunks in order, then the wave (DPP): a fixed order.
+__device__ __forceinline__ void publish_partials(float hm, double ss, bool norm, int ql, ChainLds &sh) {
+    hm = wave_max_dpp(hm);
+    if (norm) ss = wave_sum_dpp(ss);
+    if ((ql & 63) == 0) {
+        sh.qp_m[ql >> 6] = hm;
+        sh.qp_d[ql >> 6] = ss;
+    }
+}
+
 // Polls the K-word input `in` until no word of this lane's chunks holds the
 // fill pattern, then stores the chunks to xs (and the matching gains, or
-// ones, to xg).  Agent-scope loads of one poll are all in flight together.
-// `live` turns false after an expired poll; later polls take what they find.
-__device__ __forceinline__ void poll_to_lds(const float *in, int K, const float *gain, int ql, float *xs, float *xg,
-                                            bool &live) {
+// ones, to xg) and publishes the wave's partial reductions.  Agent-scope
+// loads of one poll are all in flight together.  `live` turns false after an
+// expired poll; later polls take what they find.
+__device__ __forceinline__ void poll_to_lds(const float *in, int K, const float *gain, bool norm, int ql,
+                                            ChainLds &sh, bool &live) {
+    float *xs = sh.xs, *xg = sh.xg;
     const int nc = K >> 2;
     const int ni = (nc + kCQL - 1) / kCQL;
     if (gain) {
@@ -270,17 +285,30 @@ __device__ __forceinline__ void poll_to_lds(const float *in, int K, const float 
         }
         __builtin_amdgcn_s_sleep(1);
     }
+    float hm = 0.0f;
+    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < kCChunks; ++i) {
         const int c = ql + kCQL * i;
-        if (i < ni && c < nc) *reinterpret_cast<v4i *>(xs + 4 * c) = u[i];
+        if (i < ni && c < nc) {
+            *reinterpret_cast<v4i *>(xs + 4 * c) = u[i];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const float v = __int_as_float(u[i][f]);
+                hm = fmaxf(hm, fabsf(v));
+                if (norm) ss += (double)v * (double)v;
+            }
+        }
     }
+    publish_partials(hm, ss, norm, ql, sh);
 }
 
 // The first layer's input x (the caller's fp32 or bf16 row, column order),
-// stored to xs in exchange order; xg is unused (stage 0 has no norm).
-__device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float *xs) {
+// stored to xs in exchange order, with the wave's max |x|; xg is unused
+// (stage 0 has no norm).
+__device__ __forceinline__ void load_x(const ChainArgs &A, int ql, ChainLds &sh) {
     const int nc = A.H >> 2;
+    float hm = 0.0f;
     for (int c = ql; c < nc; c += kCQL) {
         float t[4];
 #pragma unroll
@@ -288,22 +316,23 @@ __device__ __forceinline__ void load_x(const ChainArgs &A, int ql, float *xs) {
             const int k = f * nc + c;
             t[f] = A.x_dt == BL_BF16 ? bf16_to_f32(static_cast<const uint16_t *>(A.x)[k])
                                      : static_cast<const float *>(A.x)[k];
+            hm = fmaxf(hm, fabsf(t[f]));
         }
-        *reinterpret_cast<float4 *>(xs + 4 * c) = float4{t[0], t[1], t[2], t[3]};
+        *reinterpret_cast<float4 *>(sh.xs + 4 * c) = float4{t[0], t[1], t[2], t[3]};
     }
+    publish_partials(hm, 0.0, false, ql, sh);
 }
 
-// The sixteen per-wave partials of an exchange, read as 16-byte vectors:
-// their sum in wave order, their maximum.
-__device__ __forceinline__ double sum16(const double *p) {
+// The four quantizer waves' partial sums, added in wave order.
+__device__ __forceinline__ double sum4(const double *p) {
     const double2 *q = reinterpret_cast<const double2 *>(p);
-    double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < kCWaves / 2; ++i) {
-        const double2 x = q[i];
-        s = (s + x.x) + x.y;
-    }
-    return s;
+    const double2 a = q[0], b = q[1];
+    return ((a.x + a.y) + b.x) + b.y;
+}
+
+__device__ __forceinline__ float max4(const float *p) {
+    const float4 x = *reinterpret_cast<const float4 *>(p);
+    return fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
 }
 
 __device__ __forceinline__ float max16(const float *p) {
@@ -321,8 +350,10 @@ __device__ __forceinline__ float max16(const float *p) {
 // codes to q_s in column order, this wave's code sum to red_i[wave]; returns
 // the activation scale.  Same arithmetic as the row kernel: fp64 sum of
 // squares, r = float(1 / sqrt(ss / K + eps)), (h * r) * g (g = 1 without a
-// gain), a = 127 / max(amax, 1e-5), q = clamp(rint(x * a)).  The sums run in
-// a fixed order (per thread, the wave, then the 16 waves in order).
+// gain), a = 127 / max(amax, 1e-5), q = clamp(rint(x * a)).  The sum of
+// squares and max |h| come from the quantizer waves' partials (published
+// before the barrier that put xs in LDS); the sums run in a fixed order (per
+// lane over its chunks, the wave, then the four waves in order).
 __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, float eps, ChainLds &sh) {
     const int t = threadIdx.x, wave = t >> 6;
     const int nc = K >> 2;
@@ -336,28 +367,12 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
     float mx = 0.0f;
     bool have_max = false;
     if (norm) {
-        double ss = 0.0;
-        float hm = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kCNormChunks; ++i)
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                ss += (double)v[i][f] * (double)v[i][f];
-                hm = fmaxf(hm, fabsf(v[i][f]));
-            }
-        ss = wave_sum_dpp(ss);
-        hm = wave_max_dpp(hm);
-        if ((t & 63) == 0) {
-            sh.red_d[wave] = ss;
-            sh.red_m[wave] = hm;
-        }
-        lds_barrier();
-        const float r = (float)(1.0 / sqrt(sum16(sh.red_d) / (double)K + (double)eps));
+        const float r = (float)(1.0 / sqrt(sum4(sh.qp_d) / (double)K + (double)eps));
         if (!has_gain) {
             // without a gain the largest |h * r| is float(max |h| * r): the
             // rounded product is monotone in the first factor and odd, so the
             // maximum commutes with it (one exchange saved)
-            mx = max16(sh.red_m) * r;
+            mx = max4(sh.qp_m) * r;
             have_max = true;
         }
 #pragma unroll
@@ -368,6 +383,10 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
             v[i][0] = (v[i][0] * r) * g.x; v[i][1] = (v[i][1] * r) * g.y;
             v[i][2] = (v[i][2] * r) * g.z; v[i][3] = (v[i][3] * r) * g.w;
         }
+    }
+    if (!norm) {
+        mx = max4(sh.qp_m);
+        have_max = true;
     }
     if (!have_max) {
         float am = 0.0f;
@@ -472,10 +491,10 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
         else wm[0] = w.w_dn[0];
     }
     if (s == 0 && l == 0) {
-        load_x(A, ql, sh.xs);
+        load_x(A, ql, sh);
     } else {
         const float *in = s == 0 ? xl - A.Sw + stage_off(A, 3) : xl + stage_off(A, s - 1);
-        poll_to_lds(in, K, gain, ql, sh.xs, sh.xg, live);
+        poll_to_lds(in, K, gain, s >= 2, ql, sh, live);
     }
     lds_barrier();   // input in LDS
     const float a = quantize_all(K, s >= 2, gain != nullptr, A.eps, sh);

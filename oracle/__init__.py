@@ -309,10 +309,11 @@ def layer_f64gemm(x, codes, w_means, eps=1e-5):
     return dict(q_in=q0, a_in=a0, y_qkv=y_qkv, q_o=q_o, a_o=a_o, y_o=y_o, **ch)
 
 
-def layer(x, codes, w_means, eps=1e-5):
+def layer(x, codes, w_means, eps=1e-5, g_subln=None, g_ffn=None):
     """One decoder layer's linear path (attention excluded), fp32 x [M,2560].
 
-    codes: dict proj -> [N,K] int8; w_means: dict proj -> float32.
+    codes: dict proj -> [N,K] int8; w_means: dict proj -> float32; g_subln,
+    g_ffn: the FFN chain's RMSNorm gains, or None (unit gain).
     Wiring (a convention, parity unpinned by the pages): quantize x -> fused
     q|k|v -> q's output is re-quantized and fed to o -> FFN chain on o's
     output.  No residual additions.  Returns dict of stage outputs.
@@ -325,7 +326,7 @@ def layer(x, codes, w_means, eps=1e-5):
     q_o, a_o, A_o, y_o = bitlinear(y_q, codes["o"], None, w_means["o"])
     gu = np.concatenate([codes["gate"], codes["up"]], axis=0)
     ch = ffn_chain(y_o, gu, np.array([w_means["gate"], w_means["up"]], np.float32),
-                   codes["down"], w_means["down"], eps=eps)
+                   codes["down"], w_means["down"], g_subln=g_subln, g_ffn=g_ffn, eps=eps)
     return dict(q_in=q0, a_in=a0, y_qkv=y_qkv, q_o=q_o, a_o=a_o, y_o=y_o, **ch)
 
 

@@ -175,13 +175,21 @@ def test_stack_prefill_30_layers_one_row_per_token_tile():
 
 
 # ----------------------------------------------------------------------------- the persistent decode step
-def _check_stack_decode(n_layers, x_kind="outliers", seed=0):
+def _check_stack_decode(n_layers, x_kind="outliers", seed=0, gains=False):
     """bl_stack_decode over n_layers: every stage of every layer (q|k|v, o,
     ReLU^2(gate)*up, down) against the oracle's layer on the GPU's own input
-    to that layer; all stage buffers and the output guarded."""
+    to that layer; all stage buffers and the output guarded.  gains: every
+    layer gets seeded RMSNorm gains U(0.5, 1.5) for both sub-norms."""
     from bit_ternary_weight_amd import stack
     H, KV, I = synth.HIDDEN, synth.KV_DIM, synth.INTERMEDIATE
     layers = stack.build_layers(n_layers, dev())
+    host_gains = [(None, None)] * n_layers
+    if gains:
+        rng = np.random.default_rng(1000 + seed)
+        host_gains = [(rng.uniform(0.5, 1.5, size=H).astype(np.float32),
+                       rng.uniform(0.5, 1.5, size=I).astype(np.float32)) for _ in range(n_layers)]
+        for lw, (gs, gf) in zip(layers, host_gains):
+            lw.g_subln, lw.g_ffn = to_dev(gs), to_dev(gf)
     bits = synth.act_outliers_bf16(seed, 1, H) if x_kind == "outliers" else synth.act_normal_bf16(seed, 1, H)
     x = bf16_dev(bits)
     Sw = (H + 2 * KV) + H + I + H
@@ -196,7 +204,7 @@ def _check_stack_decode(n_layers, x_kind="outliers", seed=0):
     offs = {"y_qkv": (0, H + 2 * KV), "y_o": (H + 2 * KV, H), "p": (2 * H + 2 * KV, I), "y": (2 * H + 2 * KV + I, H)}
     for l in range(n_layers):
         codes, wms = _oracle_layer_codes(l)
-        ref = oracle.layer(x_host, codes, wms)
+        ref = oracle.layer(x_host, codes, wms, g_subln=host_gains[l][0], g_ffn=host_gains[l][1])
         for key, (o, n) in offs.items():
             got = st[l:l + 1, o:o + n]
             assert_exact(got.view(np.uint32), np.ascontiguousarray(ref[key]).view(np.uint32), f"layer {l} {key}")
@@ -213,6 +221,12 @@ def test_stack_decode_persistent_odd_and_short():
     """One layer (a phantom second layer in the pair loop) and three layers."""
     _check_stack_decode(1, seed=3)
     _check_stack_decode(3, x_kind="normal", seed=4)
+
+
+def test_stack_decode_persistent_with_gains():
+    """Both sub-norms with gains: the absmax is taken after the gain, so the
+    kernel's gain path (a separate max pass) runs in every FFN stage."""
+    _check_stack_decode(3, seed=5, gains=True)
 
 
 def test_stack_decode_persistent_matches_the_launch_chain():
