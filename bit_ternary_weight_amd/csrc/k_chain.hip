@@ -119,24 +119,44 @@ struct Stage {
     int nunits;        // nt * ng * ku
 };
 
-// The geometry is recomputed at each use from the kernel arguments (scalar
-// loads and scalar arithmetic on uniform values) rather than kept: a table
-// of it would be placed in scratch memory.
-struct Geo {};
+// The launch-wide fields, read from the kernel arguments once, all together,
+// at the start: left to itself the compiler issues each kernel-argument load
+// next to its first use, so every stage's epilogue and next-stage issue
+// waited on one dependent round trip after another.  The stage geometry is
+// recomputed at each use from these (scalar arithmetic on uniform values)
+// rather than kept: a table of it would be placed in scratch memory.
+struct Geo {
+    int L, H, KV, I, Sw, G, x_dt;
+    float eps;
+    float *xch, *stages, *y;
+    const void *x;
+    SegTab seg;
+};
 
-__device__ __forceinline__ Geo make_geo(const ChainArgs &) { return Geo{}; }
+__device__ __forceinline__ Geo make_geo(const ChainArgs &A) {
+    Geo g;
+    g.L = A.L; g.H = A.H; g.KV = A.KV; g.I = A.I; g.Sw = A.Sw; g.G = A.G; g.x_dt = A.x_dt;
+    g.eps = A.eps; g.xch = A.xch; g.stages = A.stages; g.y = A.y; g.x = A.x;
+    g.seg = A.seg_qkv;
+    asm volatile("" ::"s"(g.L), "s"(g.H), "s"(g.KV), "s"(g.I), "s"(g.Sw), "s"(g.G), "s"(g.x_dt), "s"(g.eps),
+                 "s"(g.xch), "s"(g.stages), "s"(g.y), "s"(g.x));
+#pragma unroll
+    for (int i = 0; i <= BL_MAX_SEGMENTS; ++i) asm volatile("" ::"s"(g.seg.roff[i]));
+    asm volatile("" ::"s"(g.seg.n));
+    return g;
+}
 
-__device__ __forceinline__ Stage stage_of(const ChainArgs &A, const Geo &, int l, int s) {
+__device__ __forceinline__ Stage stage_of(const ChainArgs &A, const Geo &g, int l, int s) {
     const ChainLayer &w = A.layers[l];
     Stage st;
-    if (s == 0) { st.P = w.P_qkv; st.K = A.H; st.R = (A.H + 2 * A.KV) / 4; st.nt = 1; }
-    else if (s == 1) { st.P = w.P_o; st.K = A.H; st.R = A.H / 4; st.nt = 1; }
-    else if (s == 2) { st.P = w.P_gu; st.K = A.H; st.R = A.I / 4; st.nt = 2; }
-    else { st.P = w.P_dn; st.K = A.I; st.R = A.H / 4; st.nt = 1; }
+    if (s == 0) { st.P = w.P_qkv; st.K = g.H; st.R = (g.H + 2 * g.KV) / 4; st.nt = 1; }
+    else if (s == 1) { st.P = w.P_o; st.K = g.H; st.R = g.H / 4; st.nt = 1; }
+    else if (s == 2) { st.P = w.P_gu; st.K = g.H; st.R = g.I / 4; st.nt = 2; }
+    else { st.P = w.P_dn; st.K = g.I; st.R = g.H / 4; st.nt = 1; }
     const int groups = st.R / 4;
     const int b = blockIdx.x;
-    st.g0 = b * groups / A.G;
-    st.ng = (b + 1) * groups / A.G - st.g0;
+    st.g0 = b * groups / g.G;
+    st.ng = (b + 1) * groups / g.G - st.g0;
     st.ku = st.K / kCUnit;
     st.nunits = st.nt * st.ng * st.ku;
     return st;
@@ -306,7 +326,7 @@ __device__ __forceinline__ void poll_to_lds(const float *in, int K, const float 
 // The first layer's input x (the caller's fp32 or bf16 row, column order),
 // stored to xs in exchange order, with the wave's max |x|; xg is unused
 // (stage 0 has no norm).
-__device__ __forceinline__ void load_x(const ChainArgs &A, int ql, ChainLds &sh) {
+__device__ __forceinline__ void load_x(const Geo &A, int ql, ChainLds &sh) {
     const int nc = A.H >> 2;
     float hm = 0.0f;
     for (int c = ql; c < nc; c += kCQL) {
@@ -424,7 +444,7 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
 // the pair).  Exchange position 4 rr + f = 16 g0 + ql: the lanes store one
 // contiguous run, agent-scope (the next stage polls it); the column-order
 // copies are plain stores.
-__device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, int s, int ql, const int *part,
+__device__ __forceinline__ void epilogue(const Geo &A, const Stage &st, int s, int ql, const int *part,
                                          int qsum, float a, const float (&wm)[3], float *xout, float *out,
                                          float *y_last) {
     if (ql >= 16 * st.ng) return;
@@ -447,7 +467,7 @@ __device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, in
         val = relu2_mul(gv, uv);
         col = f * st.R + rr;
     } else if (s == 0) {
-        const ColOf c = col_of(A.seg_qkv, rr, f);
+        const ColOf c = col_of(A.seg, rr, f);
         val = (float)acc[0] * ((c.seg == 0 ? wm[0] : (c.seg == 1 ? wm[1] : wm[2])) / a);
         col = c.col;
     } else {
@@ -462,11 +482,11 @@ __device__ __forceinline__ void epilogue(const ChainArgs &A, const Stage &st, in
 
 // Offset of stage s's output (q|k|v, o, p, y) within a layer's row of the
 // exchange and stage buffers.
-__device__ __forceinline__ int stage_off(const ChainArgs &A, int s) {
+__device__ __forceinline__ int stage_off(const Geo &A, int s) {
     return s == 0 ? 0 : (s == 1 ? A.H + 2 * A.KV : (s == 2 ? 2 * A.H + 2 * A.KV : 2 * A.H + 2 * A.KV + A.I));
 }
 
-__device__ __forceinline__ int stage_k(const ChainArgs &A, int s) { return s == 3 ? A.I : A.H; }
+__device__ __forceinline__ int stage_k(const Geo &A, int s) { return s == 3 ? A.I : A.H; }
 
 __device__ __forceinline__ const float *stage_gain(const ChainArgs &A, int l, int s) {
     return s == 2 ? A.layers[l].g_sub : (s == 3 ? A.layers[l].g_ffn : nullptr);
@@ -478,8 +498,8 @@ __device__ __forceinline__ const float *stage_gain(const ChainArgs &A, int l, in
 __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int l, int s, int ql, ChainLds &sh,
                                         bool &live) {
     const Stage st = stage_of(A, geo, l, s);
-    float *xl = A.xch + (size_t)l * A.Sw;
-    const int K = stage_k(A, s);
+    float *xl = geo.xch + (size_t)l * geo.Sw;
+    const int K = stage_k(geo, s);
     const float *gain = stage_gain(A, l, s);
     float wm[3] = {1.0f, 1.0f, 1.0f};
     {
@@ -490,22 +510,23 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
         else if (s == 2) { wm[0] = w.w_gu[0]; wm[1] = w.w_gu[1]; }
         else wm[0] = w.w_dn[0];
     }
+    asm volatile("" ::"s"(gain));
     if (s == 0 && l == 0) {
-        load_x(A, ql, sh);
+        load_x(geo, ql, sh);
     } else {
-        const float *in = s == 0 ? xl - A.Sw + stage_off(A, 3) : xl + stage_off(A, s - 1);
+        const float *in = s == 0 ? xl - geo.Sw + stage_off(geo, 3) : xl + stage_off(geo, s - 1);
         poll_to_lds(in, K, gain, s >= 2, ql, sh, live);
     }
     lds_barrier();   // input in LDS
-    const float a = quantize_all(K, s >= 2, gain != nullptr, A.eps, sh);
+    const float a = quantize_all(K, s >= 2, gain != nullptr, geo.eps, sh);
     lds_barrier();   // codes ready
     lds_barrier();   // partial sums ready
     int qsum = 0;
 #pragma unroll
     for (int w = 0; w < kCWaves; ++w) qsum += sh.red_i[w];
-    const int so = stage_off(A, s);
-    float *out = A.stages ? A.stages + (size_t)l * A.Sw + so : nullptr;
-    epilogue(A, st, s, ql, sh.part, qsum, a, wm, xl + so, out, (s == 3 && l == A.L - 1) ? A.y : nullptr);
+    const int so = stage_off(geo, s);
+    float *out = geo.stages ? geo.stages + (size_t)l * geo.Sw + so : nullptr;
+    epilogue(geo, st, s, ql, sh.part, qsum, a, wm, xl + so, out, (s == 3 && l == geo.L - 1) ? geo.y : nullptr);
     lds_barrier();   // outputs stored: the next stage's weights may queue behind them
 }
 
@@ -524,8 +545,19 @@ __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int 
                                         ChainLds &sh) {
     const Stage st = stage_of(A, geo, l, S);
     constexpr int NS = (S + 1) & 3;
+    // the next stage's weight pointer and this stage's gain pointer read
+    // before the first barrier, not where they are used
+    const bool more = !(S == 3 && l + 1 >= geo.L);
+    const uint8_t *nP = nullptr;
+    if (more) {
+        const ChainLayer &wn = A.layers[S == 3 ? l + 1 : l];
+        nP = NS == 0 ? wn.P_qkv : (NS == 1 ? wn.P_o : (NS == 2 ? wn.P_gu : wn.P_dn));
+    }
+    const float *gp = stage_gain(A, l, S);
+    asm volatile("" ::"s"(nP), "s"(gp));
+    const bool has_gain = gp != nullptr;
     lds_barrier();   // input in LDS
-    (void)quantize_all(stage_k(A, S), S >= 2, stage_gain(A, l, S) != nullptr, A.eps, sh);
+    (void)quantize_all(stage_k(geo, S), S >= 2, has_gain, geo.eps, sh);
     lds_barrier();   // codes ready
     if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, sh.part);
     if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, sh.part);
@@ -533,8 +565,9 @@ __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int 
     if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, sh.part);
     lds_barrier();   // partial sums ready
     lds_barrier();   // outputs stored
-    if (S == 3 && l + 1 >= A.L) return;   // no stage follows the last one
-    const Stage nx = stage_of(A, geo, S == 3 ? l + 1 : l, NS);
+    if (!more) return;   // no stage follows the last one
+    Stage nx = stage_of(A, geo, S == 3 ? l + 1 : l, NS);
+    nx.P = nP;
     if (NS == 0) issue<kUq>(nx, ws, lane, rg.q);
     if (NS == 1) issue<kUo>(nx, ws, lane, rg.o);
     if (NS == 2) issue<kUg>(nx, ws, lane, rg.g);
@@ -550,7 +583,7 @@ __global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) 
     if (wave < kCS) {
         Ring rg;
         issue<kUq>(stage_of(A, geo, 0, 0), wave, lane, rg.q);
-        for (int l = 0; l < A.L; ++l) {
+        for (int l = 0; l < geo.L; ++l) {
             s_stage<0>(A, geo, l, wave, lane, rg, sh);
             s_stage<1>(A, geo, l, wave, lane, rg, sh);
             s_stage<2>(A, geo, l, wave, lane, rg, sh);
@@ -560,7 +593,7 @@ __global__ __launch_bounds__(kCThreads) void k_chain_decode(ChainArgs a_unused) 
         const int ql = threadIdx.x - kCS * 64;
         bool live = true;
 #pragma unroll 1
-        for (int i = 0; i < 4 * A.L; ++i) q_stage(A, geo, i >> 2, i & 3, ql, sh, live);
+        for (int i = 0; i < 4 * geo.L; ++i) q_stage(A, geo, i >> 2, i & 3, ql, sh, live);
     }
 }
 
