@@ -68,6 +68,7 @@ constexpr int kCUnit = 256;             // k bytes of a unit
 constexpr int kUq = 1, kUo = 1, kUg = 4, kUd = 3;
 constexpr int kUMax = 4;
 constexpr int kCMaxUnits = kCS * kUMax;
+constexpr int kCMaxAcc = 2 * 4 * 16;    // outputs of a workgroup: 2 tensors x 4 groups x 16 (the host bounds ng)
 constexpr unsigned kFill = 0xFFFFFFFFu;  // exchange words not yet written
 constexpr int kPollMax = 1 << 17;       // polls per wait (each at least a memory round trip)
 
@@ -192,10 +193,12 @@ __device__ __forceinline__ void issue(const Stage &st, int ws, int lane, v4i (&r
 // Consumes this wave's units of a stage: per unit, each field through one
 // v_mfma_i32_16x16x64_i8 (weights first, the codes of the same chunks
 // second), the k-slice sums of each row gathered from the quad that holds
-// them; lane 16r writes the unit's 4 fields of unit row r to part[mu].
+// them; lane 16r adds the unit's 4 fields of unit row r into the row's
+// accumulators acc[((tensor, group) * 4 + r) * 4 + field] (LDS integer
+// atomics: exact and order-free), which the quantizer waves cleared.
 template <int U>
 __device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const v4i (&r)[U], const int8_t *q_s,
-                                        int *part) {
+                                        int *acc) {
     const int ch = (lane & 3) + 4 * (lane >> 4);
     const int s = lane & 3;
 #pragma unroll
@@ -214,8 +217,9 @@ __device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const
             tot[fi] = shift_field(v, fi);
         }
         if ((lane & 15) == 0) {
-            const int row = lane >> 4;
-            *reinterpret_cast<int4 *>(part + (mu * 4 + row) * 4) = int4{tot[0], tot[1], tot[2], tot[3]};
+            int *dst = acc + ((mu / st.ku) * 4 + (lane >> 4)) * 4;
+#pragma unroll
+            for (int fi = 0; fi < 4; ++fi) atomicAdd(dst + fi, tot[fi]);
         }
     }
 }
@@ -224,7 +228,7 @@ struct ChainLds {
     float xs[kCMaxK];            // the stage input, exchange order
     float xg[kCMaxK];            // its RMSNorm gains, exchange order
     int8_t q_s[kCMaxK];          // its codes, column order
-    int part[kCMaxUnits * 16];   // unit partial sums
+    int acc[kCMaxAcc];           // output accumulators: [tensor, group][unit row][field]
     alignas(16) double qp_d[kCQ];  // per quantizer wave: sum of squares of its chunks (norm stages)
     alignas(16) float qp_m[kCQ];   // per quantizer wave: max |value| of its chunks
     float red_f[kCWaves];        // per-wave absolute maxima (norm with a gain)
@@ -444,7 +448,7 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
 // the pair).  Exchange position 4 rr + f = 16 g0 + ql: the lanes store one
 // contiguous run, agent-scope (the next stage polls it); the column-order
 // copies are plain stores.
-__device__ __forceinline__ void epilogue(const Geo &A, const Stage &st, int s, int ql, const int *part,
+__device__ __forceinline__ void epilogue(const Geo &A, const Stage &st, int s, int ql, const int *accs,
                                          int qsum, float a, const float (&wm)[3], float *xout, float *out,
                                          float *y_last) {
     if (ql >= 16 * st.ng) return;
@@ -453,10 +457,7 @@ __device__ __forceinline__ void epilogue(const Geo &A, const Stage &st, int s, i
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (t >= st.nt) break;
-        int sum = 0;
-        const int base = (t * st.ng + grl) * st.ku;
-        for (int k = 0; k < st.ku; ++k) sum += part[((base + k) * 4 + row) * 4 + f];
-        acc[t] = sum - qsum;
+        acc[t] = accs[((t * st.ng + grl) * 4 + row) * 4 + f] - qsum;
     }
     const int rr = 4 * (st.g0 + grl) + row;   // packed row within its tensor
     float val;
@@ -511,6 +512,9 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
         else wm[0] = w.w_dn[0];
     }
     asm volatile("" ::"s"(gain));
+    // the output accumulators start at zero (the previous stage's epilogue
+    // read them before its last barrier)
+    for (int i = ql; i < kCMaxAcc; i += kCQL) sh.acc[i] = 0;
     if (s == 0 && l == 0) {
         load_x(geo, ql, sh);
     } else {
@@ -526,7 +530,7 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
     for (int w = 0; w < kCWaves; ++w) qsum += sh.red_i[w];
     const int so = stage_off(geo, s);
     float *out = geo.stages ? geo.stages + (size_t)l * geo.Sw + so : nullptr;
-    epilogue(geo, st, s, ql, sh.part, qsum, a, wm, xl + so, out, (s == 3 && l == geo.L - 1) ? geo.y : nullptr);
+    epilogue(geo, st, s, ql, sh.acc, qsum, a, wm, xl + so, out, (s == 3 && l == geo.L - 1) ? geo.y : nullptr);
     lds_barrier();   // outputs stored: the next stage's weights may queue behind them
 }
 
@@ -559,10 +563,10 @@ __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int 
     lds_barrier();   // input in LDS
     (void)quantize_all(stage_k(geo, S), S >= 2, has_gain, geo.eps, sh);
     lds_barrier();   // codes ready
-    if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, sh.part);
-    if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, sh.part);
-    if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, sh.part);
-    if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, sh.part);
+    if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, sh.acc);
+    if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, sh.acc);
+    if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, sh.acc);
+    if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, sh.acc);
     lds_barrier();   // partial sums ready
     lds_barrier();   // outputs stored
     if (!more) return;   // no stage follows the last one
@@ -607,16 +611,19 @@ __global__ __launch_bounds__(256) void k_chain_fill(unsigned *p, size_t n) {
 int chain_max_layers() { return kChainMaxLayers; }
 
 // Host check of the shapes against the kernel's fixed capacities (units per
-// stream wave and stage, LDS codes) for G workgroups.
+// stream wave and stage, output accumulators, LDS codes) for G workgroups.
 bool chain_fits(int H, int KV, int I, int G) {
     if (H % kCUnit || I % kCUnit || KV % 16 || H > kCMaxK || I > kCMaxK || G < 1) return false;
+    bool ok = true;
     auto units = [&](int R, int nt, int K) {
         const int groups = R / 4;
         const int per = (groups + G - 1) / G;
+        if (nt * per * 16 > kCMaxAcc) ok = false;
         return nt * per * (K / kCUnit);
     };
-    return units((H + 2 * KV) / 4, 1, H) <= kCS * kUq && units(H / 4, 1, H) <= kCS * kUo &&
-           units(I / 4, 2, H) <= kCS * kUg && units(H / 4, 1, I) <= kCS * kUd;
+    const bool fit = units((H + 2 * KV) / 4, 1, H) <= kCS * kUq && units(H / 4, 1, H) <= kCS * kUo &&
+                     units(I / 4, 2, H) <= kCS * kUg && units(H / 4, 1, I) <= kCS * kUd;
+    return fit && ok;
 }
 
 hipError_t launch_chain_decode(const ChainParams &p, hipStream_t s) {
