@@ -443,42 +443,66 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
 }
 
 // This workgroup's outputs of a stage: quantizer lane ql < 16 ng takes group
-// ql / 16, row (ql / 4) % 4, field ql % 4; the unit partials of its row are
-// summed over K, the code sum subtracted, then the rescale (and ReLU^2 for
-// the pair).  Exchange position 4 rr + f = 16 g0 + ql: the lanes store one
-// contiguous run, agent-scope (the next stage polls it); the column-order
-// copies are plain stores.
-__device__ __forceinline__ void epilogue(const Geo &A, const Stage &st, int s, int ql, const int *accs,
-                                         int qsum, float a, const float (&wm)[3], float *xout, float *out,
-                                         float *y_last) {
-    if (ql >= 16 * st.ng) return;
+// ql / 16, row (ql / 4) % 4, field ql % 4: its row's accumulated sum less the
+// code sum, then the rescale (and ReLU^2 for the pair).  Exchange position
+// 4 rr + f = 16 g0 + ql: the lanes store one contiguous run, agent-scope (the
+// next stage polls it); the column-order copies are plain stores.
+//
+// Everything but the sums is formed by ep_prepare while the stream waves
+// multiply (the scale and code sums are known once the codes are): after the
+// last barrier only a subtraction, a conversion, a multiply and the stores
+// remain.  The rescale is float(A) * (w_mean / a), with IEEE fp32 division.
+struct EpPrep {
+    bool on;       // this lane stores an output
+    int acc0;      // its accumulator (first tensor); acc1 the second (pair)
+    int acc1;
+    int qsum;      // the stage's code sum
+    float s0, s1;  // w_mean / a of its segment (pair: gate, up)
+    int col;       // column-order index
+    int xo;        // exchange index
+};
+
+__device__ __forceinline__ EpPrep ep_prepare(const Geo &A, const Stage &st, int s, int ql, int qsum, float a,
+                                             const float (&wm)[3]) {
+    EpPrep e;
+    e.on = ql < 16 * st.ng;
     const int grl = ql >> 4, row = (ql >> 2) & 3, f = ql & 3;
-    int acc[2] = {0, 0};
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        if (t >= st.nt) break;
-        acc[t] = accs[((t * st.ng + grl) * 4 + row) * 4 + f] - qsum;
-    }
+    e.acc0 = ((0 * st.ng + grl) * 4 + row) * 4 + f;
+    e.acc1 = ((1 * st.ng + grl) * 4 + row) * 4 + f;
+    e.qsum = qsum;
     const int rr = 4 * (st.g0 + grl) + row;   // packed row within its tensor
-    float val;
-    int col;
+    e.s1 = 0.0f;
     if (s == 2) {
-        const float gv = (float)acc[0] * (wm[0] / a);
-        const float uv = (float)acc[1] * (wm[1] / a);
-        val = relu2_mul(gv, uv);
-        col = f * st.R + rr;
+        e.s0 = wm[0] / a;
+        e.s1 = wm[1] / a;
+        e.col = f * st.R + rr;
     } else if (s == 0) {
         const ColOf c = col_of(A.seg, rr, f);
-        val = (float)acc[0] * ((c.seg == 0 ? wm[0] : (c.seg == 1 ? wm[1] : wm[2])) / a);
-        col = c.col;
+        e.s0 = (c.seg == 0 ? wm[0] : (c.seg == 1 ? wm[1] : wm[2])) / a;
+        e.col = c.col;
     } else {
-        val = (float)acc[0] * (wm[0] / a);
-        col = f * st.R + rr;
+        e.s0 = wm[0] / a;
+        e.col = f * st.R + rr;
     }
-    __hip_atomic_store(reinterpret_cast<unsigned *>(xout) + 16 * st.g0 + ql, __float_as_uint(val), __ATOMIC_RELAXED,
+    e.xo = 16 * st.g0 + ql;
+    return e;
+}
+
+__device__ __forceinline__ void ep_store(const EpPrep &e, int s, const int *accs, float *xout, float *out,
+                                         float *y_last) {
+    if (!e.on) return;
+    const int A0 = accs[e.acc0] - e.qsum;
+    float val;
+    if (s == 2) {
+        const int A1 = accs[e.acc1] - e.qsum;
+        val = relu2_mul((float)A0 * e.s0, (float)A1 * e.s1);
+    } else {
+        val = (float)A0 * e.s0;
+    }
+    __hip_atomic_store(reinterpret_cast<unsigned *>(xout) + e.xo, __float_as_uint(val), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    if (out) out[col] = val;
-    if (y_last) y_last[col] = val;
+    if (out) out[e.col] = val;
+    if (y_last) y_last[e.col] = val;
 }
 
 // Offset of stage s's output (q|k|v, o, p, y) within a layer's row of the
@@ -524,13 +548,16 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
     lds_barrier();   // input in LDS
     const float a = quantize_all(K, s >= 2, gain != nullptr, geo.eps, sh);
     lds_barrier();   // codes ready
-    lds_barrier();   // partial sums ready
+    // while the stream waves multiply: the epilogue's constants
     int qsum = 0;
 #pragma unroll
     for (int w = 0; w < kCWaves; ++w) qsum += sh.red_i[w];
+    const EpPrep ep = ep_prepare(geo, st, s, ql, qsum, a, wm);
     const int so = stage_off(geo, s);
     float *out = geo.stages ? geo.stages + (size_t)l * geo.Sw + so : nullptr;
-    epilogue(geo, st, s, ql, sh.acc, qsum, a, wm, xl + so, out, (s == 3 && l == geo.L - 1) ? geo.y : nullptr);
+    float *y_last = (s == 3 && l == geo.L - 1) ? geo.y : nullptr;
+    lds_barrier();   // partial sums ready
+    ep_store(ep, s, sh.acc, xl + so, out, y_last);
     lds_barrier();   // outputs stored: the next stage's weights may queue behind them
 }
 
