@@ -724,14 +724,18 @@ __global__ __launch_bounds__(kDT) void k_w1_decode(W1Batch unused) {
         cs = wave_sum_dpp(cs);
         if (lane == 0) ri[wave] = cs;
         d_barrier();   // codes in LDS
+        // while the stream waves multiply: the code sum and w_scale / a (IEEE
+        // fp32 division), so that only the row sum's read, a subtraction, a
+        // conversion, a multiply and the store follow the last barrier
+        int qsum = 0;
+#pragma unroll
+        for (int w = 0; w < kDQW; ++w) qsum += ri[w];
+        const float sc = wsc / a;
         d_barrier();   // row sums in LDS
         if (lane < (4 << lq) && r0 + lane < R) {   // wave w writes bit plane w
-            int qsum = 0;
-#pragma unroll
-            for (int w = 0; w < kDQW; ++w) qsum += ri[w];
             const int i = wave;
             const int A = 2 * (red[i][lane] >> (i < 7 ? i : 6)) - qsum;
-            pr.y[(size_t)i * R + r0 + lane] = (float)A * (wsc / a);
+            pr.y[(size_t)i * R + r0 + lane] = (float)A * sc;
         }
     } else {
         // ---- stream waves: every unit issued, then the products.  With Q
