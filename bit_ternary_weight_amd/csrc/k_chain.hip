@@ -196,11 +196,17 @@ __device__ __forceinline__ void issue(const Stage &st, int ws, int lane, v4i (&r
 // them; lane 16r adds the unit's 4 fields of unit row r into the row's
 // accumulators acc[((tensor, group) * 4 + r) * 4 + field] (LDS integer
 // atomics: exact and order-free), which the quantizer waves cleared.
+// Row r's sum over its four k-slices, at lane 16 r of a quad: entry s of the
+// product held by lane 16 r + s (quad broadcasts of lanes 1, 2, 3 of the quad;
+// the other lanes' results are not used).
+__device__ __forceinline__ int quad_diag(const v4i &d) {
+    return d[0] + dpp_i<0x55>(d[1]) + dpp_i<0xAA>(d[2]) + dpp_i<0xFF>(d[3]);   // quad_perm [1,1,1,1] ...
+}
+
 template <int U>
 __device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const v4i (&r)[U], const int8_t *q_s,
                                         int *acc) {
     const int ch = (lane & 3) + 4 * (lane >> 4);
-    const int s = lane & 3;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int mu = ws + kCS * u;
@@ -213,8 +219,7 @@ __device__ __forceinline__ void consume(const Stage &st, int ws, int lane, const
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) {
             const v4i d = mfma16(f[fi], b, v4i{0, 0, 0, 0});
-            const int v = quad_sum(s == 0 ? d[0] : (s == 1 ? d[1] : (s == 2 ? d[2] : d[3])));
-            tot[fi] = shift_field(v, fi);
+            tot[fi] = shift_field(quad_diag(d), fi);
         }
         if ((lane & 15) == 0) {
             int *dst = acc + ((mu / st.ku) * 4 + (lane >> 4)) * 4;
