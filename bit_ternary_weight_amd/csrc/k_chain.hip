@@ -26,9 +26,12 @@
 //     previous stage's outputs have been stored), so a stage's weights do
 //     not wait for its input.  They issue no other global memory operation,
 //     so the compiler's waits on them stay exact;
-//   * 4 quantizer waves poll the previous stage's output, normalize and
-//     quantize it into LDS, and after the stream waves' products store this
-//     workgroup's part of the stage's output.
+//   * 4 quantizer waves poll the previous stage's output into LDS and reduce
+//     its max |h| (and the norm's fp64 sum of squares) from the chunks they
+//     hold; all 16 waves then normalize and quantize it; the stream waves add
+//     each unit's products into one LDS accumulator per output, and the
+//     quantizer waves, which formed the epilogue's constants meanwhile,
+//     store this workgroup's part of the stage's output.
 //
 // Cross-workgroup exchange without fences or counters: every stage output
 // goes to an exchange buffer that a fill launch sets to an all-ones word (a
@@ -43,12 +46,12 @@
 // Waits are bounded: an expired one is counted (bl_device_errors) and the
 // kernel runs to its end.
 //
-// Within a workgroup the two roles meet at three barriers per stage (codes in
-// LDS; partial sums in LDS; outputs stored), all LDS-only so no wave waits
-// for weight loads in flight.  The next stage's weights are issued after the
-// third: a compute unit sends its memory requests in issue order, and stores
-// queued behind a stage's worth of weight loads reach the other workgroups
-// that much later.
+// Within a workgroup the two roles meet at four barriers per stage (input in
+// LDS; codes in LDS; products accumulated; outputs stored), all LDS-only so
+// no wave waits for weight loads in flight.  The next stage's weights are
+// issued after the last: a compute unit sends its memory requests in issue
+// order, and stores queued behind a stage's worth of weight loads reach the
+// other workgroups that much later.
 #include "bl_buffer.h"
 #include "bl_common.h"
 
@@ -561,7 +564,7 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
     const int so = stage_off(geo, s);
     float *out = geo.stages ? geo.stages + (size_t)l * geo.Sw + so : nullptr;
     float *y_last = (s == 3 && l == geo.L - 1) ? geo.y : nullptr;
-    lds_barrier();   // partial sums ready
+    lds_barrier();   // products accumulated
     ep_store(ep, s, sh.acc, xl + so, out, y_last);
     lds_barrier();   // outputs stored: the next stage's weights may queue behind them
 }
@@ -599,7 +602,7 @@ __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int 
     if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, sh.acc);
     if (S == 2) consume<kUg>(st, ws, lane, rg.g, sh.q_s, sh.acc);
     if (S == 3) consume<kUd>(st, ws, lane, rg.d, sh.q_s, sh.acc);
-    lds_barrier();   // partial sums ready
+    lds_barrier();   // products accumulated
     lds_barrier();   // outputs stored
     if (!more) return;   // no stage follows the last one
     Stage nx = stage_of(A, geo, S == 3 ? l + 1 : l, NS);
