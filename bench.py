@@ -227,8 +227,8 @@ def cpu_baseline():
         out["decode_m16_7proj_gbs"] = round(g16, 4)
         g64, t64 = seven(64, "heavy", 1)
         out["decode_m64_7proj_gbs"] = round(g64, 4)
-        # the M=2048 FFN prefill (gate|up then down) on 16 of its 2048 rows
-        rows4 = 16
+        # the M=2048 FFN prefill (gate|up then down) on 128 of its 2048 rows
+        rows4 = 128
         codes, wms = layers[0]
         cgu = np.concatenate([codes["gate"], codes["up"]])
         wgu = np.array([wms["gate"], wms["up"]], np.float32)
@@ -240,7 +240,7 @@ def cpu_baseline():
         t4 = time.perf_counter() - t0
         out["prefill_m2048_ffn_tops"] = round(2 * rows4 * (2 * I * H + H * I) / t4 / 1e12, 6)
         # the 30-layer stack: the chained decode (two layers' codes
-        # alternating) and the prefill on 4 of 4096 rows through 30 layers
+        # alternating) and the prefill on 12 of 4096 rows through 30 layers
         x = synth.bf16_to_f32(synth.act_outliers_bf16(0, 1, H))
         t0 = time.perf_counter()
         for l in range(30):
@@ -249,7 +249,7 @@ def cpu_baseline():
         t5d = time.perf_counter() - t0
         out["chained_decode_30layers_m1_gbs"] = round((layer_bytes(1, 2, H, I, KV) + 29 * layer_bytes(1, 4, H, I, KV))
                                              / t5d / 1e9, 4)
-        rows5 = 4
+        rows5 = 12
         x = synth.bf16_to_f32(synth.act_normal_bf16(0, rows5, H))
         t0 = time.perf_counter()
         for l in range(30):
@@ -272,8 +272,8 @@ def cpu_baseline():
     return {"value": out["decode_m1_7proj_gbs"], "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": (f"oracle (gcc {' '.join(oracle.CFLAGS[:4])}), one thread pinned to core {core}: "
                        f"the M=4, K=256, N=256 BitLinear in full (ternarize + forward, 20 times), the M=1 decode of a layer's 7 projections in full (40 single-token passes, two seeded layers' "
-                       f"codes alternating), the batched decode in full (M=16 twice, M=64 once), the M=2048 FFN prefill on 16 of "
-                       f"2048 rows, the 30-layer chained decode in full, the 30-layer M=4096 prefill on 4 of 4096 "
+                       f"codes alternating), the batched decode in full (M=16 twice, M=64 once), the M=2048 FFN prefill on {rows4} of "
+                       f"2048 rows, the 30-layer chained decode in full, the 30-layer M=4096 prefill on {rows5} of 4096 "
                        f"rows through 30 layers; rates scale with the rows (tokens are independent); "
                        f"{total:.1f} s of CPU work"),
             "per_workload": out, "cpu_model": model, "host_cpus": os.cpu_count(),
