@@ -239,6 +239,7 @@ struct ChainLds {
     int acc[kCMaxAcc];           // output accumulators: [tensor, group][unit row][field]
     alignas(16) double qp_d[kCQ];  // per quantizer wave: sum of squares of its chunks (norm stages)
     alignas(16) float qp_m[kCQ];   // per quantizer wave: max |value| of its chunks
+    float q_r, q_mx;             // the norm's r and the input's absmax (norm stages)
     float red_f[kCWaves];        // per-wave absolute maxima (norm with a gain)
     int red_i[kCWaves];          // per-wave code sums
 };
@@ -386,7 +387,7 @@ __device__ __forceinline__ float max16(const float *p) {
 // squares and max |h| come from the quantizer waves' partials (published
 // before the barrier that put xs in LDS); the sums run in a fixed order (per
 // lane over its chunks, the wave, then the four waves in order).
-__device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, float eps, ChainLds &sh) {
+__device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, float eps, ChainLds &sh, bool qwave) {
     const int t = threadIdx.x, wave = t >> 6;
     const int nc = K >> 2;
     float v[kCNormChunks][4];
@@ -399,12 +400,23 @@ __device__ __forceinline__ float quantize_all(int K, bool norm, bool has_gain, f
     float mx = 0.0f;
     bool have_max = false;
     if (norm) {
-        const float r = (float)(1.0 / sqrt(sum4(sh.qp_d) / (double)K + (double)eps));
-        if (!has_gain) {
+        // r's fp64 chain (two divisions and a square root) runs in the
+        // quantizer waves only, one per SIMD, and reaches the others through
+        // LDS: sixteen waves repeating it would queue on the fp64 units
+        if (qwave) {
+            const float rq = (float)(1.0 / sqrt(sum4(sh.qp_d) / (double)K + (double)eps));
             // without a gain the largest |h * r| is float(max |h| * r): the
             // rounded product is monotone in the first factor and odd, so the
             // maximum commutes with it (one exchange saved)
-            mx = max4(sh.qp_m) * r;
+            if (t == kCS * 64) {
+                sh.q_r = rq;
+                sh.q_mx = max4(sh.qp_m) * rq;
+            }
+        }
+        lds_barrier();   // r in LDS
+        const float r = sh.q_r;
+        if (!has_gain) {
+            mx = sh.q_mx;
             have_max = true;
         }
 #pragma unroll
@@ -554,7 +566,7 @@ __device__ __forceinline__ void q_stage(const ChainArgs &A, const Geo &geo, int 
         poll_to_lds(in, K, gain, s >= 2, ql, sh, live);
     }
     lds_barrier();   // input in LDS
-    const float a = quantize_all(K, s >= 2, gain != nullptr, geo.eps, sh);
+    const float a = quantize_all(K, s >= 2, gain != nullptr, geo.eps, sh, true);
     lds_barrier();   // codes ready
     // while the stream waves multiply: the epilogue's constants
     int qsum = 0;
@@ -596,7 +608,7 @@ __device__ __forceinline__ void s_stage(const ChainArgs &A, const Geo &geo, int 
     asm volatile("" ::"s"(nP), "s"(gp));
     const bool has_gain = gp != nullptr;
     lds_barrier();   // input in LDS
-    (void)quantize_all(stage_k(geo, S), S >= 2, has_gain, geo.eps, sh);
+    (void)quantize_all(stage_k(geo, S), S >= 2, has_gain, geo.eps, sh, false);
     lds_barrier();   // codes ready
     if (S == 0) consume<kUq>(st, ws, lane, rg.q, sh.q_s, sh.acc);
     if (S == 1) consume<kUo>(st, ws, lane, rg.o, sh.q_s, sh.acc);
